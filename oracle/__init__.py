@@ -1,0 +1,177 @@
+"""sp24 CPU oracle -- TEST INFRASTRUCTURE ONLY.
+
+numpy-facing wrapper around ``sp24_oracle.c``: a plain, slow, obviously correct CPU statement of the
+2:4 structured-sparse path (column norms, prune + compress, decompress, sparse GEMM in bf16 and int8).
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.py`` may import it;
+the product package never does, and this wrapper shares no code with the HIP path.
+
+Pages (cited by title and section): the Orin NN design book, Chapter 7 "2:4 structured sparsity",
+sections 2.1 (prune, values + 2-bit metadata, metadata mux), 5 (exercise Q1) and 6.1 (every 1x4 block
+must hold 2 zeros); the zyxy.net Wanda lecture, section 2.1 (score = |w| * ||X_j||_2); the NVIDIA
+technical blog on Ampere structured sparsity, Figure 1 (only non-zeros plus index metadata are stored).
+
+Every function here is pinned by the ``-m "not gpu"`` tests against what the pages and arithmetic fix
+(worked examples, brute force, closed forms, library routines); see tests/test_oracle_pins.py.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "sp24_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libsp24_oracle.so")
+
+BF16, FP16, FP32, I8, I32 = 0, 1, 2, 3, 4
+MAGNITUDE, WANDA = 0, 1
+_DT_NP = {BF16: np.uint16, FP16: np.uint16, FP32: np.float32, I8: np.int8}
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (plain C11, OpenMP, no contraction, no fast-math)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-fPIC", "-shared",
+               "-Wall", "-Wextra", _SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build(force=False)
+        lib = ctypes.CDLL(_LIB_PATH)
+        P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        lib.oracle_col_norms.argtypes = [P, I64, I64, I64, P]
+        lib.oracle_prune_compress.argtypes = [P, I, I64, I64, I64, I, P, P, I, P]
+        lib.oracle_meta_check.argtypes = [P, I64, I64]
+        lib.oracle_meta_check.restype = I64
+        lib.oracle_decompress.argtypes = [P, P, I, I64, I64, P, I64]
+        lib.oracle_gemm_bf16.argtypes = [P, P, I64, I64, P, I64, I64, P, I64, P]
+        lib.oracle_gemm_i8.argtypes = [P, P, I64, I64, P, I64, I64, P, P, I64, P, P]
+        lib.oracle_fp32_to_bf16.argtypes = [ctypes.c_float]
+        lib.oracle_fp32_to_bf16.restype = ctypes.c_uint16
+        lib.oracle_fp16_value.argtypes = [ctypes.c_uint16]
+        lib.oracle_fp16_value.restype = ctypes.c_double
+        _lib = lib
+    return _lib
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _check(rc):
+    if rc != 0:
+        raise OracleError(f"oracle returned {rc}")
+
+
+def _c(a, dtype):
+    a = np.asarray(a)
+    if a.dtype != np.dtype(dtype):
+        raise TypeError(f"expected {np.dtype(dtype)}, got {a.dtype}")
+    return a
+
+
+def col_norms(X_bf16: np.ndarray) -> np.ndarray:
+    """norms[j] = ||X[j, :]||_2 (X: K x N bf16 bits as uint16, row pitch = stride)."""
+    X = _c(X_bf16, np.uint16)
+    K, N = X.shape
+    ldx = X.strides[0] // 2 if K > 0 else N
+    if X.strides[1] != 2:
+        X = np.ascontiguousarray(X)
+        ldx = N
+    out = np.empty(K, np.float32)
+    _check(_load().oracle_col_norms(_ptr(X), K, N, ldx, _ptr(out)))
+    return out
+
+
+def prune_compress(W: np.ndarray, dtype: int, score: int = MAGNITUDE, norms: np.ndarray | None = None,
+                   val_dtype: int | None = None):
+    """Prune each group of 4 along K to its top-2 and compress. Returns (values, meta)."""
+    val_dtype = dtype if val_dtype is None else val_dtype
+    W = np.ascontiguousarray(_c(W, _DT_NP[dtype]))
+    M, K = W.shape
+    values = np.zeros((M, K // 2), _DT_NP[val_dtype])
+    meta = np.zeros((M, K // 8), np.uint8)
+    if norms is not None:
+        norms = np.ascontiguousarray(_c(norms, np.float32))
+    _check(_load().oracle_prune_compress(_ptr(W), dtype, M, K, K, score, _ptr(norms), _ptr(values), val_dtype,
+                                         _ptr(meta)))
+    return values, meta
+
+
+def meta_bad_nibbles(meta: np.ndarray, K: int) -> int:
+    meta = np.ascontiguousarray(_c(meta, np.uint8))
+    return int(_load().oracle_meta_check(_ptr(meta), meta.shape[0], K))
+
+
+def decompress(values: np.ndarray, meta: np.ndarray, dtype: int) -> np.ndarray:
+    values = np.ascontiguousarray(_c(values, _DT_NP[dtype]))
+    meta = np.ascontiguousarray(_c(meta, np.uint8))
+    M, K = values.shape[0], values.shape[1] * 2
+    out = np.empty((M, K), _DT_NP[dtype])
+    _check(_load().oracle_decompress(_ptr(values), _ptr(meta), dtype, M, K, _ptr(out), K))
+    return out
+
+
+def _rows_arg(rows, M):
+    if rows is None:
+        rows = np.arange(M, dtype=np.int64)
+    return np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+
+
+def gemm_bf16(values: np.ndarray, meta: np.ndarray, X: np.ndarray, rows=None) -> np.ndarray:
+    """Y[r, :] = (pruned W)[rows[r], :] . X in float64 (values/X: bf16 bits as uint16)."""
+    values = np.ascontiguousarray(_c(values, np.uint16))
+    meta = np.ascontiguousarray(_c(meta, np.uint8))
+    X = np.ascontiguousarray(_c(X, np.uint16))
+    M, K = values.shape[0], values.shape[1] * 2
+    N = X.shape[1]
+    if X.shape[0] != K:
+        raise ValueError("X must be K x N")
+    r = _rows_arg(rows, M)
+    Y = np.empty((len(r), N), np.float64)
+    _check(_load().oracle_gemm_bf16(_ptr(values), _ptr(meta), M, K, _ptr(X), N, N, _ptr(r), len(r), _ptr(Y)))
+    return Y
+
+
+def gemm_i8(values: np.ndarray, meta: np.ndarray, X: np.ndarray, scale: np.ndarray | None = None, rows=None):
+    """Exact int64 accumulators (checked to fit int32) and, with ``scale``, fl32(fl32(acc) * scale[m])."""
+    values = np.ascontiguousarray(_c(values, np.int8))
+    meta = np.ascontiguousarray(_c(meta, np.uint8))
+    X = np.ascontiguousarray(_c(X, np.int8))
+    M, K = values.shape[0], values.shape[1] * 2
+    N = X.shape[1]
+    if X.shape[0] != K:
+        raise ValueError("X must be K x N")
+    r = _rows_arg(rows, M)
+    acc = np.empty((len(r), N), np.int64)
+    Y = None
+    if scale is not None:
+        scale = np.ascontiguousarray(_c(scale, np.float32))
+        Y = np.empty((len(r), N), np.float32)
+    _check(_load().oracle_gemm_i8(_ptr(values), _ptr(meta), M, K, _ptr(X), N, N, _ptr(scale), _ptr(r), len(r),
+                                  _ptr(acc), _ptr(Y)))
+    return acc, Y
+
+
+def fp32_to_bf16(x: float) -> int:
+    return int(_load().oracle_fp32_to_bf16(float(x)))
+
+
+def fp16_value(h: int) -> float:
+    return float(_load().oracle_fp16_value(int(h)))

@@ -1,0 +1,344 @@
+/*
+ * sp24 CPU oracle -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, obviously correct CPU statement of what the 2:4 structured-sparse path computes.
+ * Only the tests, the smoke check and the benchmark's CPU-baseline leg may load it. The product
+ * library never links or calls it, and this file shares no code, header, table or helper with
+ * the HIP kernels.
+ *
+ * Sources (the pages are cited by title and section; they are the authority on what is computed):
+ *  [ORIN7]  "Chapter 7: 2:4 structured sparsity: benefit conditions and network constraints" (Orin NN
+ *           design book), section 2.1 hardware execution flow (Step 1 prune, Step 2 compressed storage
+ *           of values plus 2-bit metadata, Step 3 metadata mux feeding the ALU), section 2.3 alignment,
+ *           section 5 exercise Q1, section 6.1 ("ghost sparsity" check that every 1x4 block has 2 zeros).
+ *  [NVBLOG] NVIDIA technical blog (zhidx mirror) on Ampere fine-grained structured sparsity with
+ *           Tencent case studies: Figure 1 (2:4 pattern; only non-zeros and index metadata stored),
+ *           the quantization section (scale chosen to cover 99.99 % of values).
+ *  [WANDA]  zyxy.net lecture "Wanda: 2:4 sparse inference without retraining", section 2.1 (score =
+ *           |w| times the L2 norm of the input activation channel).
+ *  [FORUM]  oeforum post on sparse acceleration: exactly 2 of every 4 consecutive weights are zero;
+ *           2-bit metadata per kept value; the multiply only takes the matching activations.
+ *
+ * Readings where the pages are silent (each is listed in the design notes):
+ *  - groups are 4 consecutive weights along K inside one row of the M x K weight [ORIN7 2.1];
+ *  - exactly two slots are kept per group; between equal scores the lower index wins;
+ *  - kept values are stored in ascending position order [ORIN7 2.1 Step 2 shows [-0.5, 0.2] for
+ *    positions 1 and 3];
+ *  - metadata nibble of group g = i0 | (i1 << 2) with i0 < i1, group g of a row in byte g/2 of that
+ *    row's K/8 metadata bytes, even g in the low nibble;
+ *  - the Wanda score is the single-precision product fl32(|w|) * norms[j]; norms are an input;
+ *  - the pruned slots decompress to +0.
+ *
+ * Precision: scores are compared in double (|w| of bf16/fp16/fp32 is exact in double); norms and
+ * the bf16 GEMM accumulate in double; the int8 GEMM accumulates exactly in int64 and applies the
+ * dequant as fl32(fl32(acc) * scale[m]). Build with -ffp-contract=off and no fast-math.
+ * OpenMP over independent rows is only for timing; results do not depend on the thread count.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stddef.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { OR_BF16 = 0, OR_FP16 = 1, OR_FP32 = 2, OR_I8 = 3, OR_I32 = 4 };
+enum { OR_MAGNITUDE = 0, OR_WANDA = 1 };
+enum { OR_OK = 0, OR_EARG = -1, OR_EMETA = -2, OR_EOVERFLOW = -3 };
+
+/* ---------------------------------------------------------------- number formats (definitions) */
+
+/* bf16 is the upper half of an IEEE binary32 word, so its value is that word's value. */
+static double bf16_value(uint16_t h) {
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
+/* IEEE binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits. */
+static double fp16_value(uint16_t h) {
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1F;
+    int m = h & 0x3FF;
+    double v;
+    if (e == 0)
+        v = ldexp((double)m, -24); /* subnormal: m * 2^-10 * 2^-14 */
+    else if (e == 31)
+        v = m ? NAN : INFINITY;
+    else
+        v = ldexp(1.0 + (double)m / 1024.0, e - 15);
+    return sign ? -v : v;
+}
+
+static double fp32_value(uint32_t u) {
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
+/* Value of a bf16 pattern for rounding purposes: the pattern just above the largest finite one
+ * stands for 2^128, the value the next step would have with an unbounded exponent (IEEE 754
+ * rounds as if the exponent range were unbounded, then overflows to infinity). */
+static double bf16_value_unbounded(uint32_t h) {
+    if ((h & 0x7FFF) == 0x7F80) return (h & 0x8000) ? -ldexp(1.0, 128) : ldexp(1.0, 128);
+    return bf16_value((uint16_t)h);
+}
+
+/* fp32 -> bf16, round to nearest, ties to even, written from the definition: the two bf16
+ * neighbours of x are the truncation t (toward zero) and the next pattern t+1 (away from zero);
+ * pick the nearer; on a tie pick the one with an even last bit. Finite input, or infinity. */
+static uint16_t fp32_to_bf16_rne(uint32_t u) {
+    uint32_t t = u >> 16;
+    if ((u & 0xFFFF) == 0) return (uint16_t)t; /* exactly representable (also +-0, +-inf) */
+    double x = fp32_value(u);
+    double lo = bf16_value((uint16_t)t);
+    double hi = bf16_value_unbounded(t + 1);
+    double dlo = fabs(x - lo), dhi = fabs(hi - x);
+    if (dlo < dhi) return (uint16_t)t;
+    if (dhi < dlo) return (uint16_t)(t + 1);
+    return (t & 1) ? (uint16_t)(t + 1) : (uint16_t)t;
+}
+
+static size_t dtype_size(int dt) {
+    switch (dt) {
+    case OR_BF16: case OR_FP16: return 2;
+    case OR_FP32: case OR_I32: return 4;
+    case OR_I8: return 1;
+    }
+    return 0;
+}
+
+/* Exact value of element idx of a buffer of the given dtype. */
+static double elem_value(const void* p, int dt, size_t idx) {
+    switch (dt) {
+    case OR_BF16: return bf16_value(((const uint16_t*)p)[idx]);
+    case OR_FP16: return fp16_value(((const uint16_t*)p)[idx]);
+    case OR_FP32: return fp32_value(((const uint32_t*)p)[idx]);
+    case OR_I8: return (double)((const int8_t*)p)[idx];
+    }
+    return NAN;
+}
+
+/* ---------------------------------------------------------------- sp24 column norms [WANDA 2.1] */
+
+/* norms[j] = sqrt(sum_n X[j, n]^2) over the N calibration tokens of input channel j. X is bf16,
+ * K x N row-major with row pitch ldx. Squares and the sum are taken in double, in index order,
+ * then the square root is rounded once to fp32. */
+int oracle_col_norms(const uint16_t* X, int64_t K, int64_t N, int64_t ldx, float* norms) {
+    if (!X || !norms || K < 0 || N < 0 || ldx < N) return OR_EARG;
+#pragma omp parallel for schedule(static)
+    for (int64_t j = 0; j < K; j++) {
+        double s = 0.0;
+        for (int64_t n = 0; n < N; n++) {
+            double x = bf16_value(X[j * ldx + n]);
+            s += x * x;
+        }
+        norms[j] = (float)sqrt(s);
+    }
+    return OR_OK;
+}
+
+/* ---------------------------------------------------------------- prune + compress [ORIN7 2.1] */
+
+/* Scores of one group of four: magnitude |w| [ORIN7 2.1 Step 1] or Wanda fl32(|w|) * norm_j
+ * [WANDA 2.1]. */
+static void group_scores(const void* W, int dtype, size_t base, int score, const float* norms, int64_t k0,
+                         double s[4]) {
+    for (int t = 0; t < 4; t++) {
+        double a = fabs(elem_value(W, dtype, base + (size_t)t));
+        if (score == OR_WANDA) {
+            float af = (float)a;            /* exact: |w| of bf16/fp16/fp32 is an fp32 value */
+            float prod = af * norms[k0 + t]; /* one IEEE single-precision multiply */
+            s[t] = (double)prod;
+        } else {
+            s[t] = a;
+        }
+    }
+}
+
+/* The two kept positions of a group: element t is kept when at most one other element beats it,
+ * where u beats t if its score is larger, or equal with a lower index. Returns i0 < i1. */
+static void keep_two(const double s[4], int* i0, int* i1) {
+    int kept[2], nk = 0;
+    for (int t = 0; t < 4; t++) {
+        int beaten_by = 0;
+        for (int u = 0; u < 4; u++) {
+            if (u == t) continue;
+            if (s[u] > s[t] || (s[u] == s[t] && u < t)) beaten_by++;
+        }
+        if (beaten_by <= 1) kept[nk++] = t;
+    }
+    /* a strict total order always leaves exactly two elements beaten by at most one other */
+    *i0 = kept[0];
+    *i1 = kept[1];
+}
+
+/* W: M x K row-major (pitch ldw elements) of dtype in {BF16, FP16, FP32, I8}. Writes values
+ * (M x K/2 of val_dtype, packed) and meta (M x K/8 bytes, packed). val_dtype equals dtype, or is
+ * BF16 when dtype is FP32 (round to nearest even). score WANDA needs norms[K] and a float dtype. */
+int oracle_prune_compress(const void* W, int dtype, int64_t M, int64_t K, int64_t ldw, int score,
+                          const float* norms, void* values, int val_dtype, uint8_t* meta) {
+    if (!W || !values || !meta || M < 0 || K < 0 || K % 8 != 0 || ldw < K) return OR_EARG;
+    if (dtype != OR_BF16 && dtype != OR_FP16 && dtype != OR_FP32 && dtype != OR_I8) return OR_EARG;
+    if (!(val_dtype == dtype || (dtype == OR_FP32 && val_dtype == OR_BF16))) return OR_EARG;
+    if (score == OR_WANDA && (!norms || dtype == OR_I8)) return OR_EARG;
+    if (score != OR_WANDA && score != OR_MAGNITUDE) return OR_EARG;
+    const size_t isz = dtype_size(dtype), vsz = dtype_size(val_dtype);
+    const int64_t G = K / 4;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < M; i++) {
+        uint8_t* mrow = meta + (size_t)i * (size_t)(K / 8);
+        memset(mrow, 0, (size_t)(K / 8));
+        for (int64_t g = 0; g < G; g++) {
+            size_t base = (size_t)i * (size_t)ldw + (size_t)(4 * g);
+            double s[4];
+            int i0, i1;
+            group_scores(W, dtype, base, score, norms, 4 * g, s);
+            keep_two(s, &i0, &i1);
+            int pos[2] = {i0, i1};
+            for (int t = 0; t < 2; t++) {
+                size_t src = base + (size_t)pos[t];
+                size_t dst = (size_t)i * (size_t)(K / 2) + (size_t)(2 * g + t);
+                if (val_dtype == dtype) {
+                    memcpy((char*)values + dst * vsz, (const char*)W + src * isz, isz); /* bit copy */
+                } else {
+                    uint32_t u;
+                    memcpy(&u, (const char*)W + src * 4, 4);
+                    uint16_t h = fp32_to_bf16_rne(u);
+                    memcpy((char*)values + dst * 2, &h, 2);
+                }
+            }
+            uint8_t nib = (uint8_t)(i0 | (i1 << 2));
+            mrow[g / 2] |= (uint8_t)(nib << (4 * (g % 2)));
+        }
+    }
+    return OR_OK;
+}
+
+/* ---------------------------------------------------------------- metadata check [ORIN7 6.1] */
+
+/* Every nibble must name two distinct positions in ascending order. Returns the number of bad
+ * nibbles (0 when the stream is canonical). */
+int64_t oracle_meta_check(const uint8_t* meta, int64_t M, int64_t K) {
+    int64_t bad = 0;
+    for (int64_t i = 0; i < M; i++)
+        for (int64_t g = 0; g < K / 4; g++) {
+            int nib = (meta[(size_t)i * (size_t)(K / 8) + (size_t)(g / 2)] >> (4 * (g % 2))) & 0xF;
+            int i0 = nib & 3, i1 = (nib >> 2) & 3;
+            if (!(i0 < i1)) bad++;
+        }
+    return bad;
+}
+
+/* ---------------------------------------------------------------- decompress */
+
+/* Inverse of the compression: values[i, 2g + t] goes back to column 4g + i_t of row i; the other
+ * two columns of the group get +0 (all-zero bits). W_out: M x K row-major, pitch ldw. */
+int oracle_decompress(const void* values, const uint8_t* meta, int dtype, int64_t M, int64_t K, void* W_out,
+                      int64_t ldw) {
+    if (!values || !meta || !W_out || M < 0 || K < 0 || K % 8 != 0 || ldw < K) return OR_EARG;
+    const size_t sz = dtype_size(dtype);
+    if (sz == 0 || dtype == OR_I32) return OR_EARG;
+    if (oracle_meta_check(meta, M, K) != 0) return OR_EMETA;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < M; i++) {
+        char* orow = (char*)W_out + (size_t)i * (size_t)ldw * sz;
+        memset(orow, 0, (size_t)K * sz);
+        for (int64_t g = 0; g < K / 4; g++) {
+            int nib = (meta[(size_t)i * (size_t)(K / 8) + (size_t)(g / 2)] >> (4 * (g % 2))) & 0xF;
+            int pos[2] = {nib & 3, (nib >> 2) & 3};
+            for (int t = 0; t < 2; t++) {
+                size_t src = (size_t)i * (size_t)(K / 2) + (size_t)(2 * g + t);
+                memcpy(orow + (size_t)(4 * g + pos[t]) * sz, (const char*)values + src * sz, sz);
+            }
+        }
+    }
+    return OR_OK;
+}
+
+/* ---------------------------------------------------------------- sparse x dense GEMM */
+
+/* Dense row i of the pruned weight, as exact doubles (zeros at pruned slots). */
+static void dense_row(const void* values, const uint8_t* meta, int dtype, int64_t i, int64_t K, double* w) {
+    for (int64_t k = 0; k < K; k++) w[k] = 0.0;
+    for (int64_t g = 0; g < K / 4; g++) {
+        int nib = (meta[(size_t)i * (size_t)(K / 8) + (size_t)(g / 2)] >> (4 * (g % 2))) & 0xF;
+        w[4 * g + (nib & 3)] = elem_value(values, dtype, (size_t)i * (size_t)(K / 2) + (size_t)(2 * g));
+        w[4 * g + ((nib >> 2) & 3)] = elem_value(values, dtype, (size_t)i * (size_t)(K / 2) + (size_t)(2 * g + 1));
+    }
+}
+
+/* Y = W_2:4 . X for a list of output rows, in double [ORIN7 2.1 Step 3; NVBLOG Figure 1].
+ * values: bf16 M x K/2, meta M x K/8, X: bf16 K x N row-major (pitch ldx).
+ * rows[r] (r < nrows) names the output row; Y is nrows x N (row pitch N), double.
+ * The row is rebuilt densely and each Y[r, n] sums W[m, k] * X[k, n] over k in ascending order;
+ * every product of two bf16 numbers is exact in double. */
+int oracle_gemm_bf16(const uint16_t* values, const uint8_t* meta, int64_t M, int64_t K, const uint16_t* X,
+                     int64_t N, int64_t ldx, const int64_t* rows, int64_t nrows, double* Y) {
+    if (!values || !meta || !X || !rows || !Y || M < 0 || K < 0 || K % 8 != 0 || N < 0 || ldx < N) return OR_EARG;
+    for (int64_t r = 0; r < nrows; r++)
+        if (rows[r] < 0 || rows[r] >= M) return OR_EARG;
+    if (oracle_meta_check(meta, M, K) != 0) return OR_EMETA;
+#pragma omp parallel
+    {
+        double* w = (double*)malloc(sizeof(double) * (size_t)(K > 0 ? K : 1));
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t r = 0; r < nrows; r++) {
+            dense_row(values, meta, OR_BF16, rows[r], K, w);
+            double* y = Y + (size_t)r * (size_t)N;
+            for (int64_t n = 0; n < N; n++) y[n] = 0.0;
+            for (int64_t k = 0; k < K; k++) {
+                const uint16_t* xr = X + (size_t)k * (size_t)ldx;
+                for (int64_t n = 0; n < N; n++) y[n] += w[k] * bf16_value(xr[n]);
+            }
+        }
+        free(w);
+    }
+    return OR_OK;
+}
+
+/* int8 sparse GEMM with int32 accumulation and per-output-channel dequant [FORUM; ORIN7 3.1 Step 4].
+ * acc[r, n] = sum_k W[m, k] * X[k, n] exactly (int64; it must fit int32, else OR_EOVERFLOW).
+ * If Y is not NULL, Y[r, n] = fl32( fl32(acc) * scale[m] ), one single-precision multiply. */
+int oracle_gemm_i8(const int8_t* values, const uint8_t* meta, int64_t M, int64_t K, const int8_t* X, int64_t N,
+                   int64_t ldx, const float* scale, const int64_t* rows, int64_t nrows, int64_t* acc_out, float* Y) {
+    if (!values || !meta || !X || !rows || !acc_out || M < 0 || K < 0 || K % 8 != 0 || N < 0 || ldx < N)
+        return OR_EARG;
+    if (Y && !scale) return OR_EARG;
+    for (int64_t r = 0; r < nrows; r++)
+        if (rows[r] < 0 || rows[r] >= M) return OR_EARG;
+    if (oracle_meta_check(meta, M, K) != 0) return OR_EMETA;
+    int overflow = 0;
+#pragma omp parallel reduction(| : overflow)
+    {
+        double* w = (double*)malloc(sizeof(double) * (size_t)(K > 0 ? K : 1));
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t r = 0; r < nrows; r++) {
+            dense_row(values, meta, OR_I8, rows[r], K, w);
+            int64_t* a = acc_out + (size_t)r * (size_t)N;
+            for (int64_t n = 0; n < N; n++) a[n] = 0;
+            for (int64_t k = 0; k < K; k++) {
+                int64_t wk = (int64_t)w[k];
+                const int8_t* xr = X + (size_t)k * (size_t)ldx;
+                for (int64_t n = 0; n < N; n++) a[n] += wk * (int64_t)xr[n];
+            }
+            for (int64_t n = 0; n < N; n++) {
+                if (a[n] > INT32_MAX || a[n] < INT32_MIN) overflow = 1;
+                if (Y) {
+                    float accf = (float)(int32_t)a[n];
+                    float prod = accf * scale[rows[r]];
+                    Y[(size_t)r * (size_t)N + (size_t)n] = prod;
+                }
+            }
+        }
+        free(w);
+    }
+    return overflow ? OR_EOVERFLOW : OR_OK;
+}
+
+/* Exposed for the tests that pin the format conversions against independent references. */
+uint16_t oracle_fp32_to_bf16(float f) {
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    return fp32_to_bf16_rne(u);
+}
+double oracle_fp16_value(uint16_t h) { return fp16_value(h); }

@@ -1,0 +1,391 @@
+"""Pins for the CPU oracle: each test ties it to something other than itself -- the pages' worked
+examples (tests/golden), brute force over every small case, closed forms, and library routines
+(numpy/torch conversions and matmuls). These run without a GPU.
+
+Where a test needs a second statement of the selection rule, it uses a different algorithm from the
+oracle's (the oracle counts how many elements beat each one; the tests sort, or enumerate pairs).
+"""
+import itertools
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from structured_sparse_gemm_sp24_amd import synth
+from tests.conftest import read_golden
+
+# ----------------------------------------------------------------- independent helpers
+
+
+def top2_by_sort(scores: np.ndarray) -> np.ndarray:
+    """Kept positions (ascending) of each group of 4 along the last axis: stable sort by descending
+    score, so equal scores keep their index order and the lower index wins."""
+    s = scores.reshape(-1, 4)
+    order = np.argsort(-s, axis=1, kind="stable")[:, :2]
+    return np.sort(order, axis=1)
+
+
+def top2_by_pairs(scores4) -> tuple:
+    """Of the six pairs, the one whose sorted score pair is largest; among equal ones the
+    lexicographically smallest index pair."""
+    best = None
+    for a, b in itertools.combinations(range(4), 2):
+        key = tuple(sorted((scores4[a], scores4[b]), reverse=True))
+        if best is None or key > best[0]:
+            best = (key, (a, b))
+    return best[1]
+
+
+def meta_nibbles(meta: np.ndarray, K: int) -> np.ndarray:
+    m = np.asarray(meta, np.uint8)
+    lo, hi = m & 0xF, m >> 4
+    return np.stack([lo, hi], axis=-1).reshape(m.shape[0], K // 4)
+
+
+def dense_from_positions(Wd: np.ndarray, pos: np.ndarray) -> np.ndarray:
+    M, K = Wd.shape
+    out = np.zeros_like(Wd)
+    g = np.arange(K // 4)
+    for t in range(2):
+        cols = 4 * g[None, :] + pos.reshape(M, K // 4, 2)[:, :, t]
+        np.put_along_axis(out, cols, np.take_along_axis(Wd, cols, axis=1), axis=1)
+    return out
+
+
+def f16_bits(vals):
+    return np.asarray(vals, dtype=np.float16).view(np.uint16)
+
+
+# ----------------------------------------------------------------- worked examples from the pages
+
+
+def test_orin7_q1_exercise_fp16():
+    g = read_golden("orin7_q1_exercise.txt")
+    w = np.array([float(x) for x in g["weights"].split()])
+    W = f16_bits(w).reshape(1, 8)
+    vals, meta = oracle.prune_compress(W, oracle.FP16)
+    assert [f"{v:04X}" for v in vals[0]] == g["values_fp16_hex"].split()
+    assert meta.tolist() == [[int(g["meta_hex"], 16)]]
+    pruned = np.array([float(x) for x in g["pruned"].split()])
+    assert np.array_equal(oracle.decompress(vals, meta, oracle.FP16), f16_bits(pruned).reshape(1, 8))
+    # storage: every kept value is 16 bits, every group 4 bits of metadata
+    stored = vals.size * 16 + meta.size * 8
+    assert stored == int(g["stored_bits"]) and W.size * 16 == int(g["dense_bits"])
+    pos = [tuple(int(c) for c in p.split(",")) for p in g["kept_positions"].split()]
+    nib = meta_nibbles(meta, 8)[0]
+    assert [(n & 3, n >> 2) for n in nib] == pos
+
+
+@pytest.mark.parametrize("dt", [oracle.BF16, oracle.FP32])
+def test_orin7_q1_exercise_other_dtypes(dt):
+    g = read_golden("orin7_q1_exercise.txt")
+    w = np.array([float(x) for x in g["weights"].split()], dtype=np.float32)
+    W = synth.f32_to_bf16_bits(w).reshape(1, 8) if dt == oracle.BF16 else w.reshape(1, 8)
+    _, meta = oracle.prune_compress(W, dt)
+    assert meta.tolist() == [[int(g["meta_hex"], 16)]]
+
+
+def test_orin7_hw_flow_encoding_and_gather():
+    g = read_golden("orin7_hw_flow.txt")
+    pre = np.array([float(x) for x in g["prepruned"].split()] + [0, 0, 0, 0], dtype=np.float32)
+    W = synth.f32_to_bf16_bits(pre).reshape(1, 8)
+    vals, meta = oracle.prune_compress(W, oracle.BF16)
+    page_vals = np.array([float(x) for x in g["values"].split()], dtype=np.float32)
+    assert np.array_equal(vals[0, :2], synth.f32_to_bf16_bits(page_vals))  # the page's values, in bf16
+    bits = g["meta_bits"].split()
+    nib = meta_nibbles(meta, 8)[0, 0]
+    assert (f"{nib & 3:02b}", f"{nib >> 2:02b}") == tuple(bits)
+    assert nib == int(g["nibble_hex"], 16)
+    # gather semantics: result = -0.5 * x1 + 0.2 * x3 for activations x0..x3
+    x = np.array([float(v) for v in g["activations"].split()] + [1, 1, 1, 1], dtype=np.float32)
+    X = synth.f32_to_bf16_bits(x).reshape(8, 1)
+    Y = oracle.gemm_bf16(vals, meta, X)
+    v = synth.bf16_bits_to_f32(vals[0, :2]).astype(np.float64)
+    xs = synth.bf16_bits_to_f32(X[:, 0]).astype(np.float64)
+    assert Y[0, 0] == v[0] * xs[1] + v[1] * xs[3]
+    assert Y[0, 0] == pytest.approx(float(g["result"]), abs=11 * 2.0 ** -11)  # 0.2 rounded to bf16, times 11
+
+
+def test_orin7_rule_beats_illustration():
+    g = read_golden("orin7_hw_flow.txt")
+    w = np.array([float(x) for x in g["rule_example"].split()] + [0, 0, 0, 0], dtype=np.float32)
+    vals, meta = oracle.prune_compress(w.reshape(1, 8), oracle.FP32)
+    nib = meta_nibbles(meta, 8)[0, 0]
+    assert (nib & 3, nib >> 2) == tuple(int(c) for c in g["rule_kept_positions"].split(","))
+    assert vals[0, :2].tolist() == [np.float32(float(x)) for x in g["rule_values"].split()]
+
+
+# ----------------------------------------------------------------- brute force over small cases
+
+
+def test_bruteforce_every_group_over_small_alphabet():
+    """All 6^4 groups over {-2, -1, -0, +0, 1, 2}: the oracle's choice equals pair enumeration, kept
+    values are bit copies (signed zero included) and pruned slots decompress to +0."""
+    alphabet = np.array([-2.0, -1.0, -0.0, 0.0, 1.0, 2.0], dtype=np.float32)
+    groups = np.array(list(itertools.product(range(6), repeat=4)))
+    W = alphabet[groups].reshape(1, -1)
+    K = W.shape[1]
+    vals, meta = oracle.prune_compress(W, oracle.FP32)
+    nib = meta_nibbles(meta, K)[0]
+    for gi, gidx in enumerate(groups):
+        a, b = top2_by_pairs(np.abs(alphabet[gidx]).tolist())
+        assert (nib[gi] & 3, nib[gi] >> 2) == (a, b), (gi, alphabet[gidx])
+        assert vals[0, 2 * gi].view(np.uint32) == alphabet[gidx[a]].view(np.uint32)
+        assert vals[0, 2 * gi + 1].view(np.uint32) == alphabet[gidx[b]].view(np.uint32)
+    dense = oracle.decompress(vals, meta, oracle.FP32)
+    pos = np.array([[n & 3, n >> 2] for n in nib])
+    ref = dense_from_positions(W, pos)
+    assert np.array_equal(dense.view(np.uint32), ref.view(np.uint32))
+
+
+def test_bruteforce_int8_heavy_ties():
+    rng = np.random.default_rng(7)
+    alphabet = np.array([-128, -127, -3, -1, 0, 1, 3, 127], dtype=np.int8)
+    W = alphabet[rng.integers(0, len(alphabet), size=(64, 256))]
+    vals, meta = oracle.prune_compress(W, oracle.I8)
+    key = np.abs(W.astype(np.int32))  # |-128| = 128
+    pos = top2_by_sort(key.reshape(64, -1))
+    nib = meta_nibbles(meta, 256).reshape(-1)
+    assert np.array_equal(nib & 3, pos[:, 0]) and np.array_equal(nib >> 2, pos[:, 1])
+    assert np.array_equal(oracle.decompress(vals, meta, oracle.I8), dense_from_positions(W, pos))
+
+
+# ----------------------------------------------------------------- invariants on random data
+
+
+@pytest.mark.parametrize("dt", [oracle.BF16, oracle.FP16, oracle.FP32])
+def test_invariants_random(dt):
+    rng = np.random.default_rng(100 + dt)
+    M, K = 48, 320
+    Wf = (rng.standard_normal((M, K)) * 0.02).astype(np.float32)
+    if dt == oracle.BF16:
+        W, Wd = synth.f32_to_bf16_bits(Wf), synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(Wf))
+    elif dt == oracle.FP16:
+        W = Wf.astype(np.float16).view(np.uint16)
+        Wd = W.view(np.float16).astype(np.float32)
+    else:
+        W, Wd = Wf, Wf
+    vals, meta = oracle.prune_compress(W, dt)
+    assert oracle.meta_bad_nibbles(meta, K) == 0
+    pos = top2_by_sort(np.abs(Wd))
+    nib = meta_nibbles(meta, K).reshape(-1)
+    assert np.array_equal(nib & 3, pos[:, 0]) and np.array_equal(nib >> 2, pos[:, 1])
+    dense = oracle.decompress(vals, meta, dt)
+    ref = dense_from_positions(W, pos)
+    assert np.array_equal(dense, ref)  # decompress(compress(W)) == prune(W), bit-exact
+    # min kept magnitude >= max dropped magnitude in every group; exactly two non-zeros per group
+    a = np.abs(Wd).reshape(-1, 4)
+    keep = np.zeros_like(a, bool)
+    np.put_along_axis(keep, pos, True, axis=1)
+    assert np.all(np.where(keep, a, np.inf).min(1) >= np.where(keep, -np.inf, a).max(1))
+    dd = (dense.view(np.uint16) if dt != oracle.FP32 else dense.view(np.uint32)).reshape(-1, 4)
+    assert np.all(np.count_nonzero(dd, axis=1) == 2)
+    # idempotent: pruning the pruned matrix changes nothing
+    v2, m2 = oracle.prune_compress(dense, dt)
+    assert np.array_equal(oracle.decompress(v2, m2, dt), dense)
+
+
+def test_fp32_input_bf16_values_round_to_nearest_even():
+    rng = np.random.default_rng(5)
+    W = rng.standard_normal((16, 64)).astype(np.float32)
+    vals32, meta32 = oracle.prune_compress(W, oracle.FP32)
+    vals16, meta16 = oracle.prune_compress(W, oracle.FP32, val_dtype=oracle.BF16)
+    assert np.array_equal(meta32, meta16)
+    assert np.array_equal(vals16, synth.f32_to_bf16_bits(vals32))
+
+
+def test_fp32_to_bf16_definition_vs_torch():
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal(20000).astype(np.float32) * np.float32(1e3)
+    # exact ties: low 16 bits 0x8000 with both parities of the kept bit
+    ties = (rng.integers(0x3F800000, 0x47000000, size=2000, dtype=np.uint32) & 0xFFFF0000) | 0x8000
+    edge = np.array([0x7F7F8000, 0x7F7F7FFF, 0xFF7F8000, 0x00008000, 0x00018000, 0x3F808000, 0x3F818000,
+                     0x80000000, 0x7F800000], dtype=np.uint32)
+    allx = np.concatenate([x, ties.view(np.float32), edge.view(np.float32)])
+    ours = np.array([oracle.fp32_to_bf16(v) for v in allx], dtype=np.uint16)
+    assert np.array_equal(ours, synth.f32_to_bf16_bits(allx))
+    assert oracle.fp32_to_bf16(np.float32(1 + 2 ** -8)) == 0x3F80  # tie -> even (1.0)
+    assert oracle.fp32_to_bf16(np.float32(1 + 3 * 2 ** -8)) == 0x3F82  # tie -> even (1 + 2^-6)
+
+
+def test_fp16_decoding_every_pattern_vs_numpy():
+    h = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = h.view(np.float16).astype(np.float64)
+    ours = np.array([oracle.fp16_value(int(v)) for v in h])
+    finite = ~np.isnan(ref)
+    assert np.array_equal(ours[finite], ref[finite])
+    assert np.all(np.isnan(ours[~finite]))
+
+
+# ----------------------------------------------------------------- Wanda scoring
+
+
+def test_wanda_hand_example():
+    # |w| = 1 2 3 4 with input-channel norms 10 1 1 1 -> scores 10 2 3 4 -> keep positions 0 and 3;
+    # magnitude alone would keep 2 and 3.
+    w = np.array([1, 2, 3, 4, -4, 3, 2, 1], dtype=np.float32)
+    norms = np.array([10, 1, 1, 1, 0.25, 1, 8, 1], dtype=np.float32)  # group 1 scores 1 3 16 1 -> keep 1, 2
+    _, meta = oracle.prune_compress(w.reshape(1, 8), oracle.FP32, oracle.WANDA, norms)
+    nib = meta_nibbles(meta, 8)[0]
+    assert [(n & 3, n >> 2) for n in nib] == [(0, 3), (1, 2)]
+    _, meta_m = oracle.prune_compress(w.reshape(1, 8), oracle.FP32)
+    assert [(n & 3, n >> 2) for n in meta_nibbles(meta_m, 8)[0]] == [(2, 3), (0, 1)]
+
+
+@pytest.mark.parametrize("p", [0, 3, -5])
+def test_wanda_with_uniform_power_of_two_norms_equals_magnitude(p):
+    rng = np.random.default_rng(11)
+    W = synth.f32_to_bf16_bits((rng.standard_normal((32, 128)) * 0.02).astype(np.float32))
+    norms = np.full(128, 2.0 ** p, dtype=np.float32)
+    a = oracle.prune_compress(W, oracle.BF16, oracle.WANDA, norms)
+    b = oracle.prune_compress(W, oracle.BF16)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_wanda_vs_sorted_float32_scores():
+    rng = np.random.default_rng(12)
+    M, K = 40, 256
+    W = synth.f32_to_bf16_bits((rng.standard_normal((M, K)) * 0.02).astype(np.float32))
+    norms = (np.exp(rng.standard_normal(K)) * 30).astype(np.float32)
+    norms[::7] = norms[1::7][: len(norms[::7])]  # some repeated norms -> more ties
+    vals, meta = oracle.prune_compress(W, oracle.BF16, oracle.WANDA, norms)
+    s = np.abs(synth.bf16_bits_to_f32(W)) * norms[None, :]  # float32 * float32 in numpy: one rounding
+    assert s.dtype == np.float32
+    pos = top2_by_sort(s)
+    nib = meta_nibbles(meta, K).reshape(-1)
+    assert np.array_equal(nib & 3, pos[:, 0]) and np.array_equal(nib >> 2, pos[:, 1])
+
+
+def test_wanda_rejects_int8_and_missing_norms():
+    with pytest.raises(oracle.OracleError):
+        oracle.prune_compress(np.zeros((1, 8), np.int8), oracle.I8, oracle.WANDA, np.ones(8, np.float32))
+    with pytest.raises(oracle.OracleError):
+        oracle.prune_compress(np.zeros((1, 8), np.float32), oracle.FP32, oracle.WANDA, None)
+
+
+# ----------------------------------------------------------------- column norms
+
+
+@pytest.mark.parametrize("p,k", [(0, 0), (3, 1), (-4, 5), (7, 3)])
+def test_col_norms_closed_form(p, k):
+    N = 4 ** k
+    a = np.float32(2.0 ** p)
+    X = synth.f32_to_bf16_bits(np.full((3, N), a, dtype=np.float32))
+    X[1] = synth.f32_to_bf16_bits(np.full(N, -a, dtype=np.float32))
+    out = oracle.col_norms(X)
+    assert np.all(out == np.float32(abs(a) * 2.0 ** k))
+
+
+def test_col_norms_vs_numpy_norm():
+    X = synth.heavy_tailed_bf16(9, 64, 2048)
+    out = oracle.col_norms(X)
+    ref = np.linalg.norm(synth.bf16_bits_to_f32(X).astype(np.float64), axis=1)
+    np.testing.assert_allclose(out, ref, rtol=1.2e-7)  # one fp32 rounding of an fp64 result
+    # strided view: only the first N columns of each row count
+    wide = np.concatenate([X, np.full((64, 8), 0x7F80, np.uint16)], axis=1)  # +inf padding, ignored
+    assert np.array_equal(oracle.col_norms(wide[:, :2048]), out)
+
+
+# ----------------------------------------------------------------- sparse GEMM
+
+
+def _rand_pruned(seed, M, K, dt=oracle.BF16):
+    rng = np.random.default_rng(seed)
+    W = synth.f32_to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    vals, meta = oracle.prune_compress(W, dt)
+    return W, vals, meta
+
+
+@pytest.mark.parametrize("M,K,N", [(16, 16, 1), (37, 64, 29), (64, 48, 64), (5, 128, 3)])
+def test_gemm_bf16_vs_numpy_matmul(M, K, N):
+    W, vals, meta = _rand_pruned(M * 1000 + K + N, M, K)
+    X = synth.normal_bf16(N + 17, (K, N))
+    pos = top2_by_sort(np.abs(synth.bf16_bits_to_f32(W)))
+    Wp = synth.bf16_bits_to_f32(dense_from_positions(W, pos)).astype(np.float64)
+    ref = Wp @ synth.bf16_bits_to_f32(X).astype(np.float64)
+    Y = oracle.gemm_bf16(vals, meta, X)
+    np.testing.assert_allclose(Y, ref, rtol=1e-12, atol=1e-12)
+    rows = np.array([M - 1, 0, M // 2])
+    assert np.array_equal(oracle.gemm_bf16(vals, meta, X, rows=rows), Y[rows])
+
+
+def test_gemm_bf16_identity_equals_decompress():
+    M, K = 24, 64
+    W, vals, meta = _rand_pruned(4, M, K)
+    eye = synth.f32_to_bf16_bits(np.eye(K, dtype=np.float32))
+    Y = oracle.gemm_bf16(vals, meta, eye)
+    dense = synth.bf16_bits_to_f32(oracle.decompress(vals, meta, oracle.BF16)).astype(np.float64)
+    assert np.array_equal(Y, dense)
+
+
+def test_gemm_bf16_one_hot_columns_select_columns():
+    M, K = 16, 32
+    W, vals, meta = _rand_pruned(6, M, K)
+    cols = [3, 0, 31, 17]
+    X = np.zeros((K, len(cols)), np.float32)
+    for j, c in enumerate(cols):
+        X[c, j] = 1.0
+    Y = oracle.gemm_bf16(vals, meta, synth.f32_to_bf16_bits(X))
+    dense = synth.bf16_bits_to_f32(oracle.decompress(vals, meta, oracle.BF16)).astype(np.float64)
+    assert np.array_equal(Y, dense[:, cols])
+
+
+def test_gemm_i8_vs_numpy_integer_matmul_and_dequant():
+    rng = np.random.default_rng(8)
+    M, K, N = 33, 96, 40
+    W = rng.integers(-127, 128, size=(M, K), dtype=np.int8)
+    X = rng.integers(-128, 128, size=(K, N), dtype=np.int8)
+    vals, meta = oracle.prune_compress(W, oracle.I8)
+    pos = top2_by_sort(np.abs(W.astype(np.int32)))
+    Wp = dense_from_positions(W, pos).astype(np.int64)
+    ref = Wp @ X.astype(np.int64)
+    scale = (rng.random(M) * 1e-3).astype(np.float32)
+    acc, Y = oracle.gemm_i8(vals, meta, X, scale)
+    assert np.array_equal(acc, ref)
+    assert np.array_equal(Y, ref.astype(np.int32).astype(np.float32) * scale[:, None])
+    acc2, Y2 = oracle.gemm_i8(vals, meta, X)
+    assert Y2 is None and np.array_equal(acc2, ref)
+
+
+def test_gemm_i8_overflow_is_reported():
+    K = 270000 - 270000 % 16
+    W = np.full((1, K), -128, np.int8)
+    X = np.full((K, 1), -128, np.int8)
+    vals, meta = oracle.prune_compress(W, oracle.I8)
+    with pytest.raises(oracle.OracleError):
+        oracle.gemm_i8(vals, meta, X)
+
+
+def test_noncanonical_metadata_is_rejected():
+    vals = np.zeros((1, 4), np.uint16)
+    for bad in (0x00, 0x5, 0x1, 0x6, 0xF):  # i0 == i1 or i0 > i1
+        meta = np.array([[bad | (0x4 << 4)]], np.uint8)
+        assert oracle.meta_bad_nibbles(meta, 8) == 1
+        with pytest.raises(oracle.OracleError):
+            oracle.decompress(vals, meta, oracle.BF16)
+
+
+# ----------------------------------------------------------------- int8 preparation (caller side)
+
+
+def test_int8_row_scale_covers_9999_and_pruned_equals_unpruned():
+    W = synth.normal_f32(21, (64, 768), 0.02)
+    vals, meta = oracle.prune_compress(W, oracle.FP32)
+    Wp = oracle.decompress(vals, meta, oracle.FP32)
+    q, s = synth.quantize_rows(Wp)
+    q0, s0 = synth.quantize_rows(W)
+    assert np.array_equal(s, s0)  # the 0.9999 quantile of 768 values sits between the top two
+    assert q.min() >= -127 and q.max() <= 127
+    # s is the 0.9999 quantile over 127, rounded once to fp32; only the values above that quantile
+    # (at most K - 1 - floor(0.9999 (K - 1)) of them per row, 1 for K = 768) get clipped
+    K = W.shape[1]
+    qtl = np.quantile(np.abs(Wp).astype(np.float64), 0.9999, axis=1)
+    np.testing.assert_allclose(s.astype(np.float64), qtl / 127, rtol=2.0 ** -24)
+    above = np.sum(np.abs(Wp) > qtl[:, None], axis=1)
+    assert np.all(above <= K - 1 - np.floor(0.9999 * (K - 1)))
+    # round half to even on exact ties
+    assert synth.quantize_sym(np.array([0.5, 1.5, 2.5, -0.5]), np.float32(1.0)).tolist() == [0, 2, 2, 0]
+    # quantizing the pruned matrix and re-pruning by |q| keeps the dense int8 matrix unchanged
+    v8, m8 = oracle.prune_compress(q, oracle.I8)
+    assert np.array_equal(oracle.decompress(v8, m8, oracle.I8), q)
