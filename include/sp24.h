@@ -1,0 +1,125 @@
+/*
+ * sp24 -- 2:4 fine-grained structured sparsity for Linear and 1x1-conv layers on AMD MI355X (gfx950).
+ *
+ * The operations follow these pages (cited by title and section):
+ *  - Orin NN design book, Chapter 7 "2:4 structured sparsity: benefit conditions and network constraints":
+ *    section 2.1 (in every 4 consecutive weights along the input channel K, keep the 2 largest
+ *    magnitudes; store only the kept values plus 2-bit positions; at run time the positions select
+ *    which activations meet each kept value), section 2.3 and 6.2 (dimensions in multiples of 16,
+ *    padding penalties), section 6.1 (a single non-2:4 block silently disables the sparse path on
+ *    other stacks -- this library never falls back silently).
+ *  - zyxy.net lecture on Wanda 2:4 pruning, section 2.1: score(w_ij) = |w_ij| * ||X_j||_2, the L2 norm
+ *    of input channel j's activations over the calibration tokens.
+ *  - NVIDIA technical blog on Ampere structured sparsity (Tencent case studies), Figure 1: the
+ *    compressed format holds the non-zeros and index metadata; the sparse product does half the
+ *    multiplies of the dense one. Its cuSPARSELt section keeps dimensions in multiples of 16 and
+ *    picks a plan per input size (here: an internal per-shape kernel choice).
+ *  - oeforum post on sparse acceleration: exactly 2 of every 4 are zero, 2-bit metadata per kept
+ *    value; int8 and 2:4 combine.
+ *
+ * Data formats (all matrices row-major):
+ *  W       M x K weight (output channels x input channels), row pitch ldw elements.
+ *  values  M x K/2, packed (row pitch K/2): for group g = 4 consecutive columns 4g..4g+3 of row i, the
+ *          two kept elements in ascending column order at values[i, 2g] and values[i, 2g+1].
+ *  meta    M x K/8 bytes, packed (row pitch K/8): group g of row i is the nibble i0 | (i1 << 2),
+ *          0 <= i0 < i1 <= 3 the kept positions, stored in byte g/2 of the row, even g in the low
+ *          nibble. This is the per-lane index format of gfx950's v_smfmac, so a 16-column slice of a
+ *          row's metadata (2 bytes) is one smfmac index operand.
+ *  X       K x N activations (input channels x tokens; one NCHW image of a 1x1 conv is Cin x H*W),
+ *          row pitch ldx elements.
+ *  Y       M x N output, row pitch ldy elements.
+ *
+ * Selection: element t of a group beats element u when its score is larger, or equal with t < u
+ * (lower index wins ties); the two elements beaten by at most one other are kept. Scores are |w|
+ * (|q| for int8, |-128| = 128) or, for Wanda, the single-precision product fl32(|w|) * norms[j].
+ * Inputs must be finite (NaN is outside the contract); norms must be finite and non-negative.
+ *
+ * Conventions for every entry point:
+ *  - All pointers are device pointers owned by the caller; the library allocates nothing and keeps no
+ *    per-call state. Every call is asynchronous on `stream` (a hipStream_t; NULL = default stream).
+ *  - Arguments are validated on the host before any HIP call; on error nothing is launched and an
+ *    sp24_status below is returned. SP24_ERR_HIP reports a launch error (hipGetLastError after the
+ *    launch); errors inside a kernel surface at the caller's next synchronisation.
+ *  - K must be a positive multiple of 16 (the alignment rule of the pages); M, N >= 1; row pitches
+ *    must be at least the row length. M and N need no padding: tails are handled in the kernels.
+ *  - Base pointers must be 16-byte aligned, and where stated a row pitch must keep rows 16-byte
+ *    aligned (true for any contiguous tensor whose rows are multiples of 16 bytes).
+ *  - values/meta passed to sp24_decompress and the GEMMs must be canonical (i0 < i1 in every nibble),
+ *    which sp24_prune_compress always produces; other metadata is outside the contract.
+ *  - The device must be gfx950 (MI355X / MI350X), else SP24_ERR_DEVICE.
+ *  - Reentrant; concurrent calls on different streams are independent.
+ */
+#ifndef SP24_H
+#define SP24_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SP24_OK = 0,
+    SP24_ERR_NULL = -1,   /* a required pointer is NULL */
+    SP24_ERR_SHAPE = -2,  /* M, N < 1; K < 16 or K % 16 != 0; a row pitch shorter than the row */
+    SP24_ERR_ALIGN = -3,  /* a base pointer or row pitch breaks the stated 16-byte alignment */
+    SP24_ERR_DTYPE = -4,  /* unsupported dtype or dtype combination */
+    SP24_ERR_ARG = -5,    /* other invalid argument (score mode, norms with magnitude, ...) */
+    SP24_ERR_DEVICE = -6, /* no usable device, or the current device is not gfx950 */
+    SP24_ERR_HIP = -7     /* the HIP runtime reported an error at launch */
+} sp24_status;
+
+typedef enum { SP24_BF16 = 0, SP24_FP16 = 1, SP24_FP32 = 2, SP24_I8 = 3, SP24_I32 = 4 } sp24_dtype;
+
+typedef enum { SP24_SCORE_MAGNITUDE = 0, SP24_SCORE_WANDA = 1 } sp24_score;
+
+/* Per-input-channel activation norms for Wanda scoring (zyxy.net Wanda lecture, section 2.1).
+ *   norms[j] = sqrt( sum_{n<N} X[j*ldx + n]^2 ),  j < K.
+ * X: bf16, K x N, any row pitch ldx >= N (16-byte aligned base). norms: fp32[K].
+ * The sum of squares is accumulated in double precision, the square root taken in double and
+ * rounded once to fp32. K need not be a multiple of 16 here (K >= 1). */
+int sp24_col_norms(const void* X, int64_t K, int64_t N, int64_t ldx, float* norms, void* stream);
+
+/* 2:4 prune and compress (Orin NN design, Chapter 7, section 2.1, Steps 1-2).
+ *   W: M x K of dtype in {BF16, FP16, FP32, I8}, pitch ldw with ldw*sizeof(dtype) % 16 == 0.
+ *   score: MAGNITUDE (norms must be NULL) or WANDA (norms: fp32[K] device array, dtype not I8).
+ *   values: M x K/2 of val_dtype, where val_dtype == dtype, or BF16 when dtype == FP32 (the kept fp32
+ *           values rounded to nearest even). Otherwise kept values are bit-exact copies (-0 stays -0).
+ *   meta: M x K/8 bytes. */
+int sp24_prune_compress(const void* W, int dtype, int64_t M, int64_t K, int64_t ldw, int score,
+                        const float* norms, void* values, int val_dtype, uint8_t* meta, void* stream);
+
+/* Inverse of the compression: W_out (M x K of dtype in {BF16, FP16, FP32, I8}, pitch ldw with
+ * ldw*sizeof(dtype) % 16 == 0) gets every kept value at its original column and +0 (all-zero bits)
+ * at the two pruned columns of every group. */
+int sp24_decompress(const void* values, const uint8_t* meta, int dtype, int64_t M, int64_t K, void* W_out,
+                    int64_t ldw, void* stream);
+
+/* Sparse x dense GEMM in bf16 with fp32 accumulation (NVIDIA blog Figure 1; Orin NN design,
+ * Chapter 7, section 2.1 Step 3):
+ *   Y[m, n] = sum_g sum_{t=0,1} values[m, 2g+t] * X[4g + i_t(m, g), n].
+ *   values: bf16 M x K/2, meta M x K/8, X: bf16 K x N (pitch ldx >= N, any value), Y: M x N (pitch
+ *   ldy >= N) of out_dtype FP32, or BF16 (the fp32 result rounded to nearest even).
+ *   The kernel is chosen from (M, N, K) and the operand alignment; results never depend on it beyond
+ *   fp32 summation order. */
+int sp24_gemm_bf16(const void* values, const uint8_t* meta, int64_t M, int64_t K, const void* X, int64_t N,
+                   int64_t ldx, void* Y, int out_dtype, int64_t ldy, void* stream);
+
+/* Sparse x dense GEMM in int8 with int32 accumulation and per-output-channel dequantization (oeforum
+ * post: int8 and 2:4 combine; Orin NN design, Chapter 7, section 3.1 Step 4):
+ *   acc[m, n] = sum over kept k of values * X[k, n] (exact int32; |acc| stays below 2^31 for
+ *               K <= 262142),
+ *   scale != NULL: Y fp32, Y[m, n] = fl32( fl32(acc[m, n]) * scale[m] )  (one multiply, no fusing)
+ *   scale == NULL: Y int32, Y[m, n] = acc[m, n].
+ *   values: int8 M x K/2, meta M x K/8, X: int8 K x N (pitch ldx >= N), Y pitch ldy >= N. */
+int sp24_gemm_i8(const int8_t* values, const uint8_t* meta, int64_t M, int64_t K, const int8_t* X, int64_t N,
+                 int64_t ldx, const float* scale, void* Y, int64_t ldy, void* stream);
+
+/* Static description of a status code. */
+const char* sp24_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SP24_H */

@@ -1,1 +1,160 @@
-"""sp24: 2:4 structured-sparse prune/compress and sparse GEMM for AMD MI355X (gfx950)."""
+"""sp24: 2:4 structured-sparse prune/compress and sparse GEMM for AMD MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``libsp24.so`` (declared in include/sp24.h): the functions
+below have the C entry points' names and only marshal arguments -- torch tensors supply device
+memory and the current HIP stream; every step runs in the library's HIP kernels. If the library is
+not built, or the device is not gfx950, the calls raise; there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libsp24.so")
+
+SP24_OK, SP24_ERR_NULL, SP24_ERR_SHAPE, SP24_ERR_ALIGN = 0, -1, -2, -3
+SP24_ERR_DTYPE, SP24_ERR_ARG, SP24_ERR_DEVICE, SP24_ERR_HIP = -4, -5, -6, -7
+SP24_BF16, SP24_FP16, SP24_FP32, SP24_I8, SP24_I32 = 0, 1, 2, 3, 4
+SP24_SCORE_MAGNITUDE, SP24_SCORE_WANDA = 0, 1
+
+# every symbol include/sp24.h declares
+EXPORTS = ("sp24_col_norms", "sp24_prune_compress", "sp24_decompress", "sp24_gemm_bf16", "sp24_gemm_i8",
+           "sp24_status_string")
+
+_TORCH_TO_SP24 = {torch.bfloat16: SP24_BF16, torch.float16: SP24_FP16, torch.float32: SP24_FP32,
+                  torch.int8: SP24_I8, torch.int32: SP24_I32}
+_SP24_TO_TORCH = {v: k for k, v in _TORCH_TO_SP24.items()}
+
+
+class Sp24Error(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {status_string(status)} (status {status})")
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libsp24.so (built by ``structured_sparse_gemm_sp24_amd.build``). Raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -m structured_sparse_gemm_sp24_amd.build` "
+                           "(there is no fallback path)")
+    lib = ctypes.CDLL(path)
+    P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.sp24_col_norms.argtypes = [P, I64, I64, I64, P, P]
+    lib.sp24_prune_compress.argtypes = [P, I, I64, I64, I64, I, P, P, I, P, P]
+    lib.sp24_decompress.argtypes = [P, P, I, I64, I64, P, I64, P]
+    lib.sp24_gemm_bf16.argtypes = [P, P, I64, I64, P, I64, I64, P, I, I64, P]
+    lib.sp24_gemm_i8.argtypes = [P, P, I64, I64, P, I64, I64, P, P, I64, P]
+    for fn in EXPORTS[:-1]:
+        getattr(lib, fn).restype = I
+    lib.sp24_status_string.argtypes = [I]
+    lib.sp24_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().sp24_status_string(int(status)).decode()
+
+
+def _check(fn: str, st: int):
+    if st != SP24_OK:
+        raise Sp24Error(fn, st)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _rows(t: torch.Tensor, name: str) -> int:
+    """Row pitch of a 2-D tensor with unit column stride."""
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D")
+    if t.stride(1) != 1 and t.shape[1] > 1:
+        raise ValueError(f"{name} must have unit column stride")
+    return t.stride(0) if t.shape[0] > 1 else max(t.stride(0), t.shape[1])
+
+
+def _dev_check(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("sp24 operates on device tensors only")
+
+
+def sp24_col_norms(X: torch.Tensor, norms: torch.Tensor | None = None) -> torch.Tensor:
+    """norms[j] = ||X[j, :]||_2 for bf16 X (K x N, row pitch = X.stride(0)); returns fp32[K]."""
+    _dev_check(X)
+    K, N = X.shape
+    if norms is None:
+        norms = torch.empty(K, dtype=torch.float32, device=X.device)
+    _check("sp24_col_norms", load_library().sp24_col_norms(_ptr(X), K, N, _rows(X, "X"), _ptr(norms), _stream(X)))
+    return norms
+
+
+def sp24_prune_compress(W: torch.Tensor, score: int = SP24_SCORE_MAGNITUDE, norms: torch.Tensor | None = None,
+                        val_dtype: torch.dtype | None = None, values: torch.Tensor | None = None,
+                        meta: torch.Tensor | None = None):
+    """2:4 prune + compress of W (M x K); returns (values M x K/2, meta M x K/8 uint8)."""
+    _dev_check(W, norms, values, meta)
+    M, K = W.shape
+    vdt = W.dtype if val_dtype is None else val_dtype
+    if values is None:
+        values = torch.empty((M, K // 2), dtype=vdt, device=W.device)
+    if meta is None:
+        meta = torch.empty((M, K // 8), dtype=torch.uint8, device=W.device)
+    st = load_library().sp24_prune_compress(_ptr(W), _TORCH_TO_SP24[W.dtype], M, K, _rows(W, "W"), int(score),
+                                            _ptr(norms), _ptr(values), _TORCH_TO_SP24[vdt], _ptr(meta), _stream(W))
+    _check("sp24_prune_compress", st)
+    return values, meta
+
+
+def sp24_decompress(values: torch.Tensor, meta: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Dense M x K pruned weight from (values, meta); +0 at pruned slots."""
+    _dev_check(values, meta, out)
+    M, K = values.shape[0], values.shape[1] * 2
+    if out is None:
+        out = torch.empty((M, K), dtype=values.dtype, device=values.device)
+    st = load_library().sp24_decompress(_ptr(values), _ptr(meta), _TORCH_TO_SP24[values.dtype], M, K, _ptr(out),
+                                        _rows(out, "out"), _stream(values))
+    _check("sp24_decompress", st)
+    return out
+
+
+def sp24_gemm_bf16(values: torch.Tensor, meta: torch.Tensor, X: torch.Tensor, out_dtype: torch.dtype = torch.float32,
+                   out: torch.Tensor | None = None) -> torch.Tensor:
+    """Y = W_2:4 . X with bf16 operands and fp32 accumulation; Y is fp32 or bf16 (M x N)."""
+    _dev_check(values, meta, X, out)
+    M, K = values.shape[0], values.shape[1] * 2
+    N = X.shape[1]
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=X.device)
+    st = load_library().sp24_gemm_bf16(_ptr(values), _ptr(meta), M, K, _ptr(X), N, _rows(X, "X"), _ptr(out),
+                                       _TORCH_TO_SP24[out.dtype], _rows(out, "out"), _stream(X))
+    _check("sp24_gemm_bf16", st)
+    return out
+
+
+def sp24_gemm_i8(values: torch.Tensor, meta: torch.Tensor, X: torch.Tensor, scale: torch.Tensor | None = None,
+                 out: torch.Tensor | None = None) -> torch.Tensor:
+    """int8 sparse GEMM: int32 accumulators, or fp32 fl32(acc) * scale[m] when ``scale`` is given."""
+    _dev_check(values, meta, X, scale, out)
+    M, K = values.shape[0], values.shape[1] * 2
+    N = X.shape[1]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32 if scale is not None else torch.int32, device=X.device)
+    st = load_library().sp24_gemm_i8(_ptr(values), _ptr(meta), M, K, _ptr(X), N, _rows(X, "X"), _ptr(scale),
+                                     _ptr(out), _rows(out, "out"), _stream(X))
+    _check("sp24_gemm_i8", st)
+    return out

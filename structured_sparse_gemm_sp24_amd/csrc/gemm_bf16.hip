@@ -1,0 +1,104 @@
+// Sparse x dense GEMM, bf16 in, fp32 accumulate: Y = W_2:4 . X (NVIDIA blog on Ampere structured
+// sparsity, Figure 1; Orin NN design, Chapter 7, section 2.1 Step 3 -- the kept values meet only
+// the activations their 2-bit positions select).
+//
+// On gfx950 that selection is done by v_smfmac_f32_16x16x64_bf16. Operand layout of one instruction
+// (wave of 64 lanes, lane l = 16*q + r):
+//   A (sparse, 16 x 64 dense): lane holds 8 kept values of row r covering dense columns
+//       [16q, 16q+16) -- exactly 16 contiguous bytes of a row of `values`;
+//   index: 16 bits per lane, 2 bits per kept value -- exactly 2 contiguous bytes of a row of `meta`;
+//   B (dense, 64 x 16): lane holds column n = r, element e at row k = 8q + (e & 7) + 32 (e >> 3);
+//   C/D (16 x 16 fp32): lane holds column r, rows 4q .. 4q+3.
+// So the stored values + metadata feed the instruction with no repacking.
+//
+// This file holds the direct kernel: each wave owns a 16-row x (16*NF)-column tile, takes A and the
+// index straight from global memory and gathers B element by element with bounds checks, so it works
+// for every shape and row pitch. The tiled LDS kernels (gemm_bf16_tiled.hip) take over where their
+// alignment and size conditions hold.
+#include "sp24_device.h"
+#include "sp24_launch.h"
+
+namespace sp24 {
+
+template <int NF>
+__global__ __launch_bounds__(256) void gemm_bf16_direct(const uint16_t* __restrict__ vals,
+                                                        const uint8_t* __restrict__ meta, int64_t M, int64_t K,
+                                                        const uint16_t* __restrict__ X, int64_t N, int64_t ldx,
+                                                        void* __restrict__ Y, int out_fp32, int64_t ldy) {
+    const int lane = threadIdx.x & 63;
+    const int r = lane & 15, q = lane >> 4;
+    const int64_t m0 = ((int64_t)blockIdx.y * 4 + (threadIdx.x >> 6)) * 16;
+    const int64_t n0 = (int64_t)blockIdx.x * 16 * NF;
+    if (m0 >= M) return;  // whole wave
+    const int64_t row = m0 + r;
+    const bool row_ok = row < M;
+    f32x4 acc[NF];
+#pragma unroll
+    for (int f = 0; f < NF; f++) acc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    for (int64_t k0 = 0; k0 < K; k0 += 64) {
+        const int64_t kd = k0 + 16 * q;  // first dense column of this lane's A slice
+        u32x4 a = {0u, 0u, 0u, 0u};
+        uint32_t idx = 0x4444u;  // (0,1) in every group: harmless with zero values
+        if (row_ok && kd < K) {  // K % 16 == 0, so the whole 16-column slice is inside the row
+            a = *reinterpret_cast<const u32x4*>(vals + row * (K / 2) + kd / 2);
+            idx = *reinterpret_cast<const uint16_t*>(meta + row * (K / 8) + kd / 8);
+        }
+#pragma unroll
+        for (int f = 0; f < NF; f++) {
+            const int64_t n = n0 + 16 * f + r;
+            uint32_t b[8];
+#pragma unroll
+            for (int h = 0; h < 8; h++) {
+                uint32_t v2 = 0;
+#pragma unroll
+                for (int s = 0; s < 2; s++) {
+                    const int e = 2 * h + s;
+                    const int64_t k = k0 + 8 * q + (e & 7) + 32 * (e >> 3);
+                    uint32_t v = 0;
+                    if (n < N && k < K) v = X[k * ldx + n];
+                    v2 |= v << (16 * s);
+                }
+                b[h] = v2;
+            }
+            const u32x8 bv = {b[0], b[1], b[2], b[3], b[4], b[5], b[6], b[7]};
+            acc[f] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, a),
+                                                               __builtin_bit_cast(bf16x16, bv), acc[f], (int)idx, 0, 0);
+        }
+    }
+#pragma unroll
+    for (int f = 0; f < NF; f++) {
+        const int64_t n = n0 + 16 * f + r;
+        if (n >= N) continue;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int64_t m = m0 + 4 * q + i;
+            if (m >= M) continue;
+            if (out_fp32)
+                reinterpret_cast<float*>(Y)[m * ldy + n] = acc[f][i];
+            else
+                reinterpret_cast<uint16_t*>(Y)[m * ldy + n] = f32_to_bf16_rne(acc[f][i]);
+        }
+    }
+}
+
+hipError_t launch_gemm_bf16_direct(const uint16_t* values, const uint8_t* meta, int64_t M, int64_t K,
+                                   const uint16_t* X, int64_t N, int64_t ldx, void* Y, bool out_fp32, int64_t ldy,
+                                   hipStream_t s) {
+    const unsigned gy = (unsigned)((M + 63) / 64);
+    if (N <= 16) {
+        hipLaunchKernelGGL(gemm_bf16_direct<1>, dim3((unsigned)((N + 15) / 16), gy), dim3(256), 0, s, values, meta, M,
+                           K, X, N, ldx, Y, (int)out_fp32, ldy);
+    } else {
+        hipLaunchKernelGGL(gemm_bf16_direct<4>, dim3((unsigned)((N + 63) / 64), gy), dim3(256), 0, s, values, meta, M,
+                           K, X, N, ldx, Y, (int)out_fp32, ldy);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_bf16(const uint16_t* values, const uint8_t* meta, int64_t M, int64_t K, const uint16_t* X,
+                            int64_t N, int64_t ldx, void* Y, bool out_fp32, int64_t ldy, hipStream_t s) {
+    return launch_gemm_bf16_direct(values, meta, M, K, X, N, ldx, Y, out_fp32, ldy, s);
+}
+
+}  // namespace sp24

@@ -1,0 +1,104 @@
+// Sparse x dense GEMM in int8 with exact int32 accumulation and a per-output-channel dequant
+// epilogue (oeforum post on sparse acceleration: int8 and 2:4 combine; Orin NN design, Chapter 7,
+// section 3.1 Step 4, sparse + INT8).
+//
+// gfx950's v_smfmac_i32_16x16x128_i8 operand layout (lane l = 16*q + r):
+//   A (sparse, 16 x 128 dense): lane holds 16 kept int8 of row r covering dense columns
+//       [32q, 32q+32) -- 16 contiguous bytes of a row of `values`;
+//   index: 32 bits per lane (8 groups) -- 4 contiguous bytes of a row of `meta`;
+//   B (dense, 128 x 16): lane holds column r, element e at row k = 16q + (e & 15) + 64 (e >> 4);
+//   C/D (16 x 16 int32): lane holds column r, rows 4q .. 4q+3.
+// Epilogue: y = fl32( fl32(acc) * scale[m] ), a single rounding multiply.
+//
+// Direct kernel: each wave owns a 16 x (16*NF) tile, reads A and the index from global memory and
+// gathers B element by element with bounds checks (any shape and row pitch).
+#include "sp24_device.h"
+#include "sp24_launch.h"
+
+namespace sp24 {
+
+template <int NF>
+__global__ __launch_bounds__(256) void gemm_i8_direct(const int8_t* __restrict__ vals, const uint8_t* __restrict__ meta,
+                                                      int64_t M, int64_t K, const int8_t* __restrict__ X, int64_t N,
+                                                      int64_t ldx, const float* __restrict__ scale,
+                                                      void* __restrict__ Y, int64_t ldy) {
+    const int lane = threadIdx.x & 63;
+    const int r = lane & 15, q = lane >> 4;
+    const int64_t m0 = ((int64_t)blockIdx.y * 4 + (threadIdx.x >> 6)) * 16;
+    const int64_t n0 = (int64_t)blockIdx.x * 16 * NF;
+    if (m0 >= M) return;  // whole wave
+    const int64_t row = m0 + r;
+    const bool row_ok = row < M;
+    i32x4 acc[NF];
+#pragma unroll
+    for (int f = 0; f < NF; f++) acc[f] = i32x4{0, 0, 0, 0};
+
+    for (int64_t k0 = 0; k0 < K; k0 += 128) {
+        const int64_t kd = k0 + 32 * q;  // first dense column of this lane's A slice
+        uint32_t a[4] = {0u, 0u, 0u, 0u};
+        uint32_t idx = 0x44444444u;
+        if (row_ok && kd < K) {
+            // the row's value bytes start 8-byte aligned and its metadata 2-byte aligned
+            const uint8_t* vp = reinterpret_cast<const uint8_t*>(vals) + row * (K / 2) + kd / 2;
+            const uint8_t* mp = meta + row * (K / 8) + kd / 8;
+            const uint2 lo = *reinterpret_cast<const uint2*>(vp);
+            a[0] = lo.x; a[1] = lo.y;
+            idx = (idx & 0xFFFF0000u) | *reinterpret_cast<const uint16_t*>(mp);
+            if (kd + 16 < K) {  // second half of the 32-column slice
+                const uint2 hi = *reinterpret_cast<const uint2*>(vp + 8);
+                a[2] = hi.x; a[3] = hi.y;
+                idx = (idx & 0x0000FFFFu) | ((uint32_t)*reinterpret_cast<const uint16_t*>(mp + 2) << 16);
+            }
+        }
+        const i32x4 av = {(int)a[0], (int)a[1], (int)a[2], (int)a[3]};
+#pragma unroll
+        for (int f = 0; f < NF; f++) {
+            const int64_t n = n0 + 16 * f + r;
+            uint32_t b[8];
+#pragma unroll
+            for (int w = 0; w < 8; w++) {
+                uint32_t v4 = 0;
+#pragma unroll
+                for (int s = 0; s < 4; s++) {
+                    const int e = 4 * w + s;
+                    const int64_t k = k0 + 16 * q + (e & 15) + 64 * (e >> 4);
+                    uint32_t v = 0;
+                    if (n < N && k < K) v = (uint8_t)X[k * ldx + n];
+                    v4 |= v << (8 * s);
+                }
+                b[w] = v4;
+            }
+            const i32x8 bv = {(int)b[0], (int)b[1], (int)b[2], (int)b[3], (int)b[4], (int)b[5], (int)b[6], (int)b[7]};
+            acc[f] = __builtin_amdgcn_smfmac_i32_16x16x128_i8(av, bv, acc[f], (int)idx, 0, 0);
+        }
+    }
+#pragma unroll
+    for (int f = 0; f < NF; f++) {
+        const int64_t n = n0 + 16 * f + r;
+        if (n >= N) continue;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int64_t m = m0 + 4 * q + i;
+            if (m >= M) continue;
+            if (scale)
+                reinterpret_cast<float*>(Y)[m * ldy + n] = __fmul_rn((float)acc[f][i], scale[m]);
+            else
+                reinterpret_cast<int32_t*>(Y)[m * ldy + n] = acc[f][i];
+        }
+    }
+}
+
+hipError_t launch_gemm_i8(const int8_t* values, const uint8_t* meta, int64_t M, int64_t K, const int8_t* X, int64_t N,
+                          int64_t ldx, const float* scale, void* Y, int64_t ldy, hipStream_t s) {
+    const unsigned gy = (unsigned)((M + 63) / 64);
+    if (N <= 16) {
+        hipLaunchKernelGGL(gemm_i8_direct<1>, dim3((unsigned)((N + 15) / 16), gy), dim3(256), 0, s, values, meta, M, K,
+                           X, N, ldx, scale, Y, ldy);
+    } else {
+        hipLaunchKernelGGL(gemm_i8_direct<4>, dim3((unsigned)((N + 63) / 64), gy), dim3(256), 0, s, values, meta, M, K,
+                           X, N, ldx, scale, Y, ldy);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace sp24

@@ -1,0 +1,166 @@
+// C ABI of the sp24 library: argument validation (host only, before any HIP call), the device check,
+// and dispatch to the kernels. Declarations and the contract live in include/sp24.h.
+#include "../../include/sp24.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "sp24_launch.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+// 0 = unknown, 1 = gfx950, -1 = other
+std::atomic<int> g_dev_ok[kMaxDevices];
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+int elem_size(int dt) {
+    switch (dt) {
+    case SP24_BF16: case SP24_FP16: return 2;
+    case SP24_FP32: case SP24_I32: return 4;
+    case SP24_I8: return 1;
+    }
+    return 0;
+}
+
+int check_k(int64_t K) { return (K >= 16 && K % 16 == 0) ? SP24_OK : SP24_ERR_SHAPE; }
+
+// The current device must be gfx950. Cached per device; the first call asks the runtime.
+int check_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+        (void)hipGetLastError();
+        return SP24_ERR_DEVICE;
+    }
+    if (dev < kMaxDevices) {
+        int c = g_dev_ok[dev].load(std::memory_order_relaxed);
+        if (c != 0) return c > 0 ? SP24_OK : SP24_ERR_DEVICE;
+    }
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return SP24_ERR_DEVICE;
+    }
+    const bool ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    if (dev < kMaxDevices) g_dev_ok[dev].store(ok ? 1 : -1, std::memory_order_relaxed);
+    return ok ? SP24_OK : SP24_ERR_DEVICE;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? SP24_OK : SP24_ERR_HIP; }
+
+// Launch-size limits of the kernels (one thread per 16-column chunk, 32-bit chunk counter; the
+// direct GEMMs put 64 rows per workgroup in grid.y).
+constexpr int64_t kMaxChunks = (int64_t)1 << 32;
+constexpr int64_t kMaxRowsDirect = (int64_t)65535 * 64;
+
+}  // namespace
+
+extern "C" {
+
+const char* sp24_status_string(int status) {
+    switch (status) {
+    case SP24_OK: return "ok";
+    case SP24_ERR_NULL: return "a required pointer is NULL";
+    case SP24_ERR_SHAPE: return "invalid shape (M, N >= 1; K a positive multiple of 16; pitch >= row length)";
+    case SP24_ERR_ALIGN: return "a pointer or row pitch breaks the 16-byte alignment rule";
+    case SP24_ERR_DTYPE: return "unsupported dtype or dtype combination";
+    case SP24_ERR_ARG: return "invalid argument";
+    case SP24_ERR_DEVICE: return "no gfx950 device is current";
+    case SP24_ERR_HIP: return "HIP runtime error at launch";
+    }
+    return "unknown sp24 status";
+}
+
+int sp24_col_norms(const void* X, int64_t K, int64_t N, int64_t ldx, float* norms, void* stream) {
+    if (!X || !norms) return SP24_ERR_NULL;
+    if (K < 1 || N < 1 || ldx < N) return SP24_ERR_SHAPE;
+    if (!aligned16(X)) return SP24_ERR_ALIGN;
+    if ((K + 3) / 4 > 0x7FFFFFFF) return SP24_ERR_SHAPE;
+    int st = check_device();
+    if (st != SP24_OK) return st;
+    return hip_status(sp24::launch_col_norms(static_cast<const uint16_t*>(X), K, N, ldx, norms,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+int sp24_prune_compress(const void* W, int dtype, int64_t M, int64_t K, int64_t ldw, int score, const float* norms,
+                        void* values, int val_dtype, uint8_t* meta, void* stream) {
+    if (!W || !values || !meta) return SP24_ERR_NULL;
+    if (dtype != SP24_BF16 && dtype != SP24_FP16 && dtype != SP24_FP32 && dtype != SP24_I8) return SP24_ERR_DTYPE;
+    if (!(val_dtype == dtype || (dtype == SP24_FP32 && val_dtype == SP24_BF16))) return SP24_ERR_DTYPE;
+    if (score != SP24_SCORE_MAGNITUDE && score != SP24_SCORE_WANDA) return SP24_ERR_ARG;
+    if (score == SP24_SCORE_WANDA) {
+        if (dtype == SP24_I8) return SP24_ERR_DTYPE;
+        if (!norms) return SP24_ERR_NULL;
+    } else if (norms) {
+        return SP24_ERR_ARG;
+    }
+    if (M < 1) return SP24_ERR_SHAPE;
+    int st = check_k(K);
+    if (st != SP24_OK) return st;
+    if (ldw < K) return SP24_ERR_SHAPE;
+    if (M * (K / 16) >= kMaxChunks) return SP24_ERR_SHAPE;
+    const int isz = elem_size(dtype);
+    if (!aligned16(W) || !aligned16(values) || !aligned16(meta) || (ldw * isz) % 16 != 0) return SP24_ERR_ALIGN;
+    if (norms && !aligned16(norms)) return SP24_ERR_ALIGN;
+    st = check_device();
+    if (st != SP24_OK) return st;
+    return hip_status(sp24::launch_prune_compress(W, dtype, M, K, ldw, score, norms, values, val_dtype, meta,
+                                                  static_cast<hipStream_t>(stream)));
+}
+
+int sp24_decompress(const void* values, const uint8_t* meta, int dtype, int64_t M, int64_t K, void* W_out, int64_t ldw,
+                    void* stream) {
+    if (!values || !meta || !W_out) return SP24_ERR_NULL;
+    if (dtype != SP24_BF16 && dtype != SP24_FP16 && dtype != SP24_FP32 && dtype != SP24_I8) return SP24_ERR_DTYPE;
+    if (M < 1) return SP24_ERR_SHAPE;
+    int st = check_k(K);
+    if (st != SP24_OK) return st;
+    if (ldw < K) return SP24_ERR_SHAPE;
+    if (M * (K / 16) >= kMaxChunks) return SP24_ERR_SHAPE;
+    const int isz = elem_size(dtype);
+    if (!aligned16(values) || !aligned16(meta) || !aligned16(W_out) || (ldw * isz) % 16 != 0) return SP24_ERR_ALIGN;
+    st = check_device();
+    if (st != SP24_OK) return st;
+    return hip_status(
+        sp24::launch_decompress(values, meta, dtype, M, K, W_out, ldw, static_cast<hipStream_t>(stream)));
+}
+
+int sp24_gemm_bf16(const void* values, const uint8_t* meta, int64_t M, int64_t K, const void* X, int64_t N,
+                   int64_t ldx, void* Y, int out_dtype, int64_t ldy, void* stream) {
+    if (!values || !meta || !X || !Y) return SP24_ERR_NULL;
+    if (out_dtype != SP24_FP32 && out_dtype != SP24_BF16) return SP24_ERR_DTYPE;
+    if (M < 1 || N < 1) return SP24_ERR_SHAPE;
+    int st = check_k(K);
+    if (st != SP24_OK) return st;
+    if (ldx < N || ldy < N) return SP24_ERR_SHAPE;
+    if (M > kMaxRowsDirect || N > ((int64_t)1 << 31)) return SP24_ERR_SHAPE;
+    if (!aligned16(values) || !aligned16(meta) || !aligned16(X) || !aligned16(Y)) return SP24_ERR_ALIGN;
+    st = check_device();
+    if (st != SP24_OK) return st;
+    return hip_status(sp24::launch_gemm_bf16(static_cast<const uint16_t*>(values), meta, M, K,
+                                             static_cast<const uint16_t*>(X), N, ldx, Y, out_dtype == SP24_FP32, ldy,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+int sp24_gemm_i8(const int8_t* values, const uint8_t* meta, int64_t M, int64_t K, const int8_t* X, int64_t N,
+                 int64_t ldx, const float* scale, void* Y, int64_t ldy, void* stream) {
+    if (!values || !meta || !X || !Y) return SP24_ERR_NULL;
+    if (M < 1 || N < 1) return SP24_ERR_SHAPE;
+    int st = check_k(K);
+    if (st != SP24_OK) return st;
+    if (K > 262142) return SP24_ERR_SHAPE;  // keeps |acc| < 2^31 for any int8 inputs
+    if (ldx < N || ldy < N) return SP24_ERR_SHAPE;
+    if (M > kMaxRowsDirect || N > ((int64_t)1 << 31)) return SP24_ERR_SHAPE;
+    if (!aligned16(values) || !aligned16(meta) || !aligned16(X) || !aligned16(Y)) return SP24_ERR_ALIGN;
+    if (scale && (reinterpret_cast<uintptr_t>(scale) & 3) != 0) return SP24_ERR_ALIGN;
+    st = check_device();
+    if (st != SP24_OK) return st;
+    return hip_status(
+        sp24::launch_gemm_i8(values, meta, M, K, X, N, ldx, scale, Y, ldy, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,140 @@
+"""Host-side checks of the C-ABI library (no GPU needed, no kernel launched):
+the library loads, exports every symbol include/sp24.h declares, and rejects invalid arguments on
+the host before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import structured_sparse_gemm_sp24_amd as sp
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    txt = open(os.path.join(ROOT, "include", "sp24.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(sp24_[a-z0-9_]+)\s*\(", txt)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(sp.LIB_PATH):
+        from structured_sparse_gemm_sp24_amd import build
+        build.build()
+    return sp.load_library()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    decl = _declared_functions()
+    assert set(decl) == set(sp.EXPORTS)
+    for name in decl:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for st in (0, -1, -2, -3, -4, -5, -6, -7):
+        assert sp.status_string(st) and "unknown" not in sp.status_string(st)
+    assert "unknown" in sp.status_string(12345)
+
+
+# Fake 16-byte-aligned addresses: every call below must be rejected before anything touches them.
+A = ctypes.c_void_p(0x10000)
+B = ctypes.c_void_p(0x20000)
+C = ctypes.c_void_p(0x30000)
+MIS = ctypes.c_void_p(0x10008)  # 8-byte aligned only
+NULL = None
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((NULL, 16, 8, 8, A, NULL), sp.SP24_ERR_NULL),
+    ((A, 16, 8, 8, NULL, NULL), sp.SP24_ERR_NULL),
+    ((A, 0, 8, 8, B, NULL), sp.SP24_ERR_SHAPE),
+    ((A, 16, 0, 8, B, NULL), sp.SP24_ERR_SHAPE),
+    ((A, 16, 8, 7, B, NULL), sp.SP24_ERR_SHAPE),
+    ((MIS, 16, 8, 8, B, NULL), sp.SP24_ERR_ALIGN),
+])
+def test_col_norms_validation(lib, args, expect):
+    assert lib.sp24_col_norms(*args) == expect
+
+
+BF16, FP16, FP32, I8, I32 = sp.SP24_BF16, sp.SP24_FP16, sp.SP24_FP32, sp.SP24_I8, sp.SP24_I32
+MAG, WANDA = sp.SP24_SCORE_MAGNITUDE, sp.SP24_SCORE_WANDA
+
+
+@pytest.mark.parametrize("args,expect", [
+    # W, dtype, M, K, ldw, score, norms, values, val_dtype, meta, stream
+    ((NULL, BF16, 4, 16, 16, MAG, NULL, B, BF16, C, NULL), sp.SP24_ERR_NULL),
+    ((A, BF16, 4, 16, 16, MAG, NULL, NULL, BF16, C, NULL), sp.SP24_ERR_NULL),
+    ((A, BF16, 4, 16, 16, MAG, NULL, B, BF16, NULL, NULL), sp.SP24_ERR_NULL),
+    ((A, I32, 4, 16, 16, MAG, NULL, B, I32, C, NULL), sp.SP24_ERR_DTYPE),
+    ((A, BF16, 4, 16, 16, MAG, NULL, B, FP32, C, NULL), sp.SP24_ERR_DTYPE),
+    ((A, FP16, 4, 16, 16, MAG, NULL, B, BF16, C, NULL), sp.SP24_ERR_DTYPE),
+    ((A, I8, 4, 16, 16, WANDA, A, B, I8, C, NULL), sp.SP24_ERR_DTYPE),
+    ((A, BF16, 4, 16, 16, WANDA, NULL, B, BF16, C, NULL), sp.SP24_ERR_NULL),
+    ((A, BF16, 4, 16, 16, MAG, A, B, BF16, C, NULL), sp.SP24_ERR_ARG),
+    ((A, BF16, 4, 16, 16, 7, NULL, B, BF16, C, NULL), sp.SP24_ERR_ARG),
+    ((A, BF16, 0, 16, 16, MAG, NULL, B, BF16, C, NULL), sp.SP24_ERR_SHAPE),
+    ((A, BF16, 4, 8, 8, MAG, NULL, B, BF16, C, NULL), sp.SP24_ERR_SHAPE),
+    ((A, BF16, 4, 24, 24, MAG, NULL, B, BF16, C, NULL), sp.SP24_ERR_SHAPE),
+    ((A, BF16, 4, 32, 16, MAG, NULL, B, BF16, C, NULL), sp.SP24_ERR_SHAPE),
+    ((A, BF16, 4, 16, 20, MAG, NULL, B, BF16, C, NULL), sp.SP24_ERR_ALIGN),  # 40-byte rows
+    ((MIS, BF16, 4, 16, 16, MAG, NULL, B, BF16, C, NULL), sp.SP24_ERR_ALIGN),
+    ((A, FP32, 4, 16, 16, WANDA, MIS, B, BF16, C, NULL), sp.SP24_ERR_ALIGN),
+    ((A, I8, 4, 16, 24, MAG, NULL, B, I8, C, NULL), sp.SP24_ERR_ALIGN),
+])
+def test_prune_compress_validation(lib, args, expect):
+    assert lib.sp24_prune_compress(*args) == expect
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((NULL, B, BF16, 4, 16, C, 16, NULL), sp.SP24_ERR_NULL),
+    ((A, B, I32, 4, 16, C, 16, NULL), sp.SP24_ERR_DTYPE),
+    ((A, B, BF16, 4, 40, C, 40, NULL), sp.SP24_ERR_SHAPE),
+    ((A, B, BF16, 4, 16, C, 8, NULL), sp.SP24_ERR_SHAPE),
+    ((A, B, FP32, 4, 16, C, 18, NULL), sp.SP24_ERR_ALIGN),
+    ((A, MIS, BF16, 4, 16, C, 16, NULL), sp.SP24_ERR_ALIGN),
+])
+def test_decompress_validation(lib, args, expect):
+    assert lib.sp24_decompress(*args) == expect
+
+
+@pytest.mark.parametrize("args,expect", [
+    # values, meta, M, K, X, N, ldx, Y, out_dtype, ldy, stream
+    ((NULL, B, 16, 16, C, 4, 4, A, FP32, 4, NULL), sp.SP24_ERR_NULL),
+    ((A, B, 16, 16, C, 4, 4, NULL, FP32, 4, NULL), sp.SP24_ERR_NULL),
+    ((A, B, 16, 16, C, 4, 4, A, I8, 4, NULL), sp.SP24_ERR_DTYPE),
+    ((A, B, 0, 16, C, 4, 4, A, FP32, 4, NULL), sp.SP24_ERR_SHAPE),
+    ((A, B, 16, 16, C, 0, 4, A, FP32, 4, NULL), sp.SP24_ERR_SHAPE),
+    ((A, B, 16, 20, C, 4, 4, A, FP32, 4, NULL), sp.SP24_ERR_SHAPE),
+    ((A, B, 16, 16, C, 4, 3, A, FP32, 4, NULL), sp.SP24_ERR_SHAPE),
+    ((A, B, 16, 16, C, 4, 4, A, FP32, 3, NULL), sp.SP24_ERR_SHAPE),
+    ((A, B, 16, 16, MIS, 4, 4, A, FP32, 4, NULL), sp.SP24_ERR_ALIGN),
+])
+def test_gemm_bf16_validation(lib, args, expect):
+    assert lib.sp24_gemm_bf16(*args) == expect
+
+
+@pytest.mark.parametrize("args,expect", [
+    # values, meta, M, K, X, N, ldx, scale, Y, ldy, stream
+    ((NULL, B, 16, 16, C, 4, 4, NULL, A, 4, NULL), sp.SP24_ERR_NULL),
+    ((A, B, 16, 262144, C, 4, 4, NULL, A, 4, NULL), sp.SP24_ERR_SHAPE),
+    ((A, B, 16, 16, C, 4, 4, ctypes.c_void_p(0x10002), A, 4, NULL), sp.SP24_ERR_ALIGN),
+    ((A, B, 16, 16, C, 5, 4, NULL, A, 5, NULL), sp.SP24_ERR_SHAPE),
+])
+def test_gemm_i8_validation(lib, args, expect):
+    assert lib.sp24_gemm_i8(*args) == expect
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="only meaningful where no GPU is visible")
+def test_valid_arguments_without_a_device_report_device_error(lib):
+    # all host checks pass, then the device check fails: nothing is launched
+    assert lib.sp24_gemm_bf16(A, B, 16, 16, C, 4, 4, A, FP32, 4, NULL) == sp.SP24_ERR_DEVICE
+    assert lib.sp24_col_norms(A, 16, 8, 8, B, NULL) == sp.SP24_ERR_DEVICE
+
+
+def test_binding_refuses_host_tensors(lib):
+    with pytest.raises(ValueError):
+        sp.sp24_col_norms(torch.zeros((4, 4), dtype=torch.bfloat16))
