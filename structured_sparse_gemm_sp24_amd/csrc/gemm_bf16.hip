@@ -98,6 +98,8 @@ hipError_t launch_gemm_bf16_direct(const uint16_t* values, const uint8_t* meta, 
 
 hipError_t launch_gemm_bf16(const uint16_t* values, const uint8_t* meta, int64_t M, int64_t K, const uint16_t* X,
                             int64_t N, int64_t ldx, void* Y, bool out_fp32, int64_t ldy, hipStream_t s) {
+    if (gemm_bf16_tiled_ok(M, K, N, ldx, X))
+        return launch_gemm_bf16_tiled(values, meta, M, K, X, N, ldx, Y, out_fp32, ldy, s);
     return launch_gemm_bf16_direct(values, meta, M, K, X, N, ldx, Y, out_fp32, ldy, s);
 }
 

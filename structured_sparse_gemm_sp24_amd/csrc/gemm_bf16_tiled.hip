@@ -1,0 +1,258 @@
+// Tiled sparse x dense GEMM for large N, bf16 in, fp32 accumulate (NVIDIA blog on Ampere structured
+// sparsity, Figure 1; Orin NN design, Chapter 7, section 2.1 Step 3).
+//
+// Workgroup tile 256 (M) x 256 (N), 4 waves in a 2 x 2 grid, each wave 128 x 128 = 8 x 8
+// v_smfmac_f32_16x16x64_bf16 fragments (256 fp32 accumulators per lane, one wave per SIMD).
+// K advances 64 dense columns per stage; three stages are in flight through LDS (3 x 50 KB).
+//
+// Global -> LDS uses buffer loads with LDS destination (no VGPR staging); the buffer descriptors'
+// record counts return zeros for rows past M and past the end of X, so M/N tails need no branches
+// in the main loop (columns past N only feed output columns that are never stored).
+//   A tile (compressed values, 256 rows x 64 B): stored fragment-major, [16-row block][q][r] x 16 B,
+//     so each lane's ds_read_b128 of its A operand is conflict-free.
+//   metadata (256 rows x 8 B): row-major; a lane reads its 16-bit index with ds_read_u16.
+//   B tile (X, 64 rows x 256 bf16 = 512 B per row): row-major with the 16-byte chunks of row k
+//     XOR-swizzled by swz(k), so the transposing reads below hit distinct banks.
+// The B operand (lane = column, 16 k values in two halves of 8) comes from four ds_read_b64_tr_b16:
+// in each 16-lane group, lane s points at row k0 + s/4, columns c0 + 4(s%4); the instruction hands
+// lane i the four consecutive k of column c0 + i.
+//
+// Tiles are ordered XCD-first: workgroup p runs on XCD p % 8, so logical tiles are numbered such
+// that each XCD gets a contiguous range, walked in groups of 8 tile-rows (A tiles and B tiles are
+// re-read from that XCD's L2).
+#include "sp24_device.h"
+#include "sp24_launch.h"
+
+namespace sp24 {
+namespace tiled_bf16 {
+
+constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int WM = 128, WN = 128;
+constexpr int FM = WM / 16, FN = WN / 16;
+constexpr int A_BYTES = BM * BK;          // BK/2 bf16 values per row = BK bytes
+constexpr int META_BYTES = BM * BK / 8;   // 4 bits per group of 4
+constexpr int B_BYTES = BK * BN * 2;
+constexpr int B_ROW = BN * 2;             // 512 bytes
+constexpr int STAGE_BYTES = A_BYTES + META_BYTES + B_BYTES;
+constexpr int LOADS_PER_STAGE = 4 + 2 + 8;  // per wave: A, metadata, B
+constexpr int GROUP_M = 8;
+constexpr uint32_t RSRC_FLAGS = 0x00020000u;
+
+typedef __attribute__((address_space(3))) void* lds_vptr;
+
+__device__ __forceinline__ int swz(int k) { return 2 * ((k & 3) | ((k >> 1) & 4)); }
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+    const int64_t n = bytes < 0 ? 0 : (bytes > 0xFFFFFFFFll ? 0xFFFFFFFFll : bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)(uint32_t)n, RSRC_FLAGS);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+struct Args {
+    const uint16_t* vals;
+    const uint8_t* meta;
+    const uint16_t* X;
+    void* Y;
+    int64_t M, K, N, ldx, ldy;
+    int tilesM, tilesN;
+    int out_fp32;
+};
+
+// Issue this wave's share of the loads of stage `s` into `smem`.
+__device__ __forceinline__ void load_stage(char* smem, const Args& a, __amdgpu_buffer_rsrc_t rA,
+                                           __amdgpu_buffer_rsrc_t rM, int64_t n0, int s, int wave, int lane) {
+    const int64_t k0 = (int64_t)s * BK;
+    const int r = lane & 15, q = lane >> 4;
+    // A: 16 blocks of 16 rows x 64 B; this wave loads blocks 4*wave .. 4*wave+3
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        const int b = 4 * wave + j;
+        const uint32_t voff = (uint32_t)((16 * b + r) * a.K + k0 + 16 * q);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_vptr)(smem + b * 1024), 16, voff, 0, 0, 0);
+    }
+    // metadata: 256 rows x 8 B, row-major; this wave loads rows 64*wave .. +63 as dwords
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+        const int row0 = 64 * wave + 32 * h;
+        const uint32_t voff = (uint32_t)((row0 + (lane >> 1)) * (a.K / 8) + k0 / 8 + 4 * (lane & 1));
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rM, (lds_vptr)(smem + A_BYTES + row0 * 8), 4, voff, 0, 0, 0);
+    }
+    // B: 64 rows x 512 B; this wave loads rows 16*wave .. +15, two rows per instruction
+    const __amdgpu_buffer_rsrc_t rB =
+        make_rsrc(a.X + k0 * a.ldx + n0, (a.K * a.ldx - k0 * a.ldx - n0) * 2);
+#pragma unroll
+    for (int h = 0; h < 8; h++) {
+        const int row = 16 * wave + 2 * h + (lane >> 5);
+        const int c = (lane & 31) ^ swz(row);
+        const uint32_t voff = (uint32_t)(row * a.ldx * 2 + 16 * c);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_vptr)(smem + A_BYTES + META_BYTES + (16 * wave + 2 * h) * B_ROW),
+                                                 16, voff, 0, 0, 0);
+    }
+}
+
+// Lane-dependent LDS byte offsets used by compute_stage (computed once per kernel).
+struct LaneOffsets {
+    int a;        // A fragment: (q * 16 + r) * 16
+    int m;        // metadata: r * 8 + 2 q (plus the wave's row offset)
+    int b[FN];    // B fragment j, first read (t = 0): row part + swizzled column part
+};
+
+__device__ __forceinline__ LaneOffsets lane_offsets(int wm0, int wn0, int lane) {
+    const int r = lane & 15, q = lane >> 4;
+    LaneOffsets o;
+    o.a = (wm0 >> 4) * 1024 + (q * 16 + r) * 16;
+    o.m = A_BYTES + (wm0 + r) * 8 + 2 * q;
+    // rows read by read t of group q: 8q + 4t' + r/4 (+32 for t >= 2); bits 0-1 and 3 of the row fix
+    // swz(row), so the XOR term depends on the lane only and t/h enter as immediates.
+    const int row0 = 8 * q + (r >> 2);
+    const int sw = swz(row0);
+#pragma unroll
+    for (int j = 0; j < FN; j++) {
+        const int col = wn0 + 16 * j + 4 * (r & 3);
+        o.b[j] = A_BYTES + META_BYTES + row0 * B_ROW + (((col >> 3) ^ sw) << 4) + 8 * (r & 1);
+    }
+    return o;
+}
+
+__device__ __forceinline__ void compute_stage(const char* smem, f32x4 (&acc)[FM][FN], const LaneOffsets& o) {
+    bf16x8 a[FM];
+    uint32_t idx[FM];
+#pragma unroll
+    for (int i = 0; i < FM; i++) {
+        a[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(smem + o.a + i * 1024));
+        idx[i] = *reinterpret_cast<const uint16_t*>(smem + o.m + i * 128);
+    }
+#pragma unroll
+    for (int j = 0; j < FN; j++) {
+        u32x8 b;
+#pragma unroll
+        for (int t = 0; t < 4; t++) {
+            // t = 0, 1: rows 8q + 4t + r/4; t = 2, 3: the same + 32
+            const int imm = (t & 1) * 4 * B_ROW + (t >> 1) * 32 * B_ROW;
+            const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) i16x4*)(smem + o.b[j] + imm));
+            b[2 * t] = (uint16_t)v[0] | ((uint32_t)(uint16_t)v[1] << 16);
+            b[2 * t + 1] = (uint16_t)v[2] | ((uint32_t)(uint16_t)v[3] << 16);
+        }
+        const bf16x16 bb = __builtin_bit_cast(bf16x16, b);
+#pragma unroll
+        for (int i = 0; i < FM; i++)
+            acc[i][j] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(a[i], bb, acc[i][j], (int)idx[i], 0, 0);
+    }
+}
+
+template <int CUR, int STAGES>
+__device__ __forceinline__ void step(char* cur, char* nxt, const Args& a, __amdgpu_buffer_rsrc_t rA,
+                                     __amdgpu_buffer_rsrc_t rM, int64_t n0, int s, int S, f32x4 (&acc)[FM][FN],
+                                     const LaneOffsets& o, int wave, int lane) {
+    if (s + 2 < S) {
+        load_stage(nxt, a, rA, rM, n0, s + 2, wave, lane);
+        wait_vmcnt<2 * LOADS_PER_STAGE>();
+    } else if (s + 1 < S) {
+        wait_vmcnt<LOADS_PER_STAGE>();
+    } else {
+        wait_vmcnt<0>();
+    }
+    __builtin_amdgcn_s_barrier();
+    compute_stage(cur, acc, o);
+    __builtin_amdgcn_s_barrier();
+}
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_bf16_tiled_kernel(Args a) {
+    __shared__ __attribute__((aligned(16))) char s0[STAGE_BYTES];
+    __shared__ __attribute__((aligned(16))) char s1[STAGE_BYTES];
+    __shared__ __attribute__((aligned(16))) char s2[STAGE_BYTES];
+
+    // XCD-first, then grouped tile order
+    const int T = a.tilesM * a.tilesN;
+    const int pid = blockIdx.x;
+    const int xcd = pid & 7, slot = pid >> 3;
+    const int per = T >> 3, rem = T & 7;
+    const int logical = xcd * per + (xcd < rem ? xcd : rem) + slot;
+    const int gsize = GROUP_M * a.tilesN;
+    const int g = logical / gsize;
+    const int first_m = g * GROUP_M;
+    const int gm = (a.tilesM - first_m) < GROUP_M ? (a.tilesM - first_m) : GROUP_M;
+    const int in_g = logical - g * gsize;
+    const int tm = first_m + in_g % gm, tn = in_g / gm;
+    const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wm0 = (wave >> 1) * WM, wn0 = (wave & 1) * WN;
+    const __amdgpu_buffer_rsrc_t rA = make_rsrc(a.vals + m0 * (a.K / 2), (a.M - m0) * a.K);
+    const __amdgpu_buffer_rsrc_t rM = make_rsrc(a.meta + m0 * (a.K / 8), (a.M - m0) * (a.K / 8));
+
+    f32x4 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; i++)
+#pragma unroll
+        for (int j = 0; j < FN; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const LaneOffsets o = lane_offsets(wm0, wn0, lane);
+    const int S = (int)(a.K / BK);
+    load_stage(s0, a, rA, rM, n0, 0, wave, lane);
+    if (S > 1) load_stage(s1, a, rA, rM, n0, 1, wave, lane);
+    // main loop in groups of three stages (one per LDS buffer), then the 0-2 remaining stages;
+    // keeping the loop body free of early exits keeps the accumulators in registers
+    int s = 0;
+    for (; s + 3 <= S; s += 3) {
+        step<0, 3>(s0, s2, a, rA, rM, n0, s, S, acc, o, wave, lane);
+        step<1, 3>(s1, s0, a, rA, rM, n0, s + 1, S, acc, o, wave, lane);
+        step<2, 3>(s2, s1, a, rA, rM, n0, s + 2, S, acc, o, wave, lane);
+    }
+    if (s < S) step<0, 3>(s0, s2, a, rA, rM, n0, s, S, acc, o, wave, lane);
+    if (s + 1 < S) step<1, 3>(s1, s0, a, rA, rM, n0, s + 1, S, acc, o, wave, lane);
+
+    // epilogue: lane holds column n0 + wn0 + 16 j + r, rows m0 + wm0 + 16 i + 4 q + t
+    const int r = lane & 15, q = lane >> 4;
+    const int64_t mrow = m0 + wm0 + 4 * q, ncol = n0 + wn0 + r;
+    const bool full = (m0 + BM <= a.M) && (n0 + BN <= a.N);
+    if (a.out_fp32) {
+        float* y = reinterpret_cast<float*>(a.Y) + mrow * a.ldy + ncol;
+#pragma unroll
+        for (int i = 0; i < FM; i++)
+#pragma unroll
+            for (int t = 0; t < 4; t++)
+#pragma unroll
+                for (int j = 0; j < FN; j++)
+                    if (full || (mrow + 16 * i + t < a.M && ncol + 16 * j < a.N))
+                        y[(16 * i + t) * a.ldy + 16 * j] = acc[i][j][t];
+    } else {
+        uint16_t* y = reinterpret_cast<uint16_t*>(a.Y) + mrow * a.ldy + ncol;
+#pragma unroll
+        for (int i = 0; i < FM; i++)
+#pragma unroll
+            for (int t = 0; t < 4; t++)
+#pragma unroll
+                for (int j = 0; j < FN; j++)
+                    if (full || (mrow + 16 * i + t < a.M && ncol + 16 * j < a.N))
+                        y[(16 * i + t) * a.ldy + 16 * j] = f32_to_bf16_rne(acc[i][j][t]);
+    }
+}
+
+}  // namespace tiled_bf16
+
+bool gemm_bf16_tiled_ok(int64_t M, int64_t K, int64_t N, int64_t ldx, const void* X) {
+    return K % tiled_bf16::BK == 0 && ldx % 8 == 0 && (reinterpret_cast<uintptr_t>(X) & 15) == 0 && N > 64 &&
+           ldx < ((int64_t)1 << 24) && K < ((int64_t)1 << 24) && ((M + 255) / 256) * ((N + 255) / 256) < (1 << 30);
+}
+
+hipError_t launch_gemm_bf16_tiled(const uint16_t* values, const uint8_t* meta, int64_t M, int64_t K, const uint16_t* X,
+                                  int64_t N, int64_t ldx, void* Y, bool out_fp32, int64_t ldy, hipStream_t s) {
+    tiled_bf16::Args a;
+    a.vals = values; a.meta = meta; a.X = X; a.Y = Y;
+    a.M = M; a.K = K; a.N = N; a.ldx = ldx; a.ldy = ldy;
+    a.tilesM = (int)((M + tiled_bf16::BM - 1) / tiled_bf16::BM);
+    a.tilesN = (int)((N + tiled_bf16::BN - 1) / tiled_bf16::BN);
+    a.out_fp32 = out_fp32 ? 1 : 0;
+    const unsigned grid = (unsigned)(a.tilesM * a.tilesN);
+    hipLaunchKernelGGL(tiled_bf16::gemm_bf16_tiled_kernel, dim3(grid), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace sp24

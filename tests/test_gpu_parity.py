@@ -162,6 +162,12 @@ GEMM_SHAPES = [
     (70, 512, 8, 8, 8),
     (256, 256, 64, 64, 64),
     (512, 768, 520, 520, 520),
+    # tiled kernel (K % 64 == 0, N > 64): ragged M and N, several tiles, padded pitches
+    (1000, 512, 777, 784, 777),
+    (64, 64, 65, 72, 65),
+    (257, 128, 513, 520, 516),
+    (768, 1024, 1024, 1024, 1024),
+    (40, 192, 300, 304, 300),
 ]
 
 
