@@ -58,16 +58,17 @@ def workload_vit(args):
     copies = []
     for _ in range(n_copies(step_bytes)):
         W = to_dev(d["W_bf16"], "bf16")
+        vb, mb = sp.sp24_compressed_bytes(M, K, torch.bfloat16)
         copies.append(dict(W=W, X=to_dev(d["X_bf16"], "bf16"),
-                           vals=torch.empty((M, K // 2), dtype=torch.bfloat16, device="cuda"),
-                           meta=torch.empty((M, K // 8), dtype=torch.uint8, device="cuda"),
+                           vals=torch.empty(vb // 2, dtype=torch.bfloat16, device="cuda"),
+                           meta=torch.empty(mb, dtype=torch.uint8, device="cuda"),
                            Y=torch.empty((M, N), dtype=torch.bfloat16, device="cuda")))
 
     def prune(c):
         sp.sp24_prune_compress(c["W"], values=c["vals"], meta=c["meta"])
 
     def gemm(c):
-        sp.sp24_gemm_bf16(c["vals"], c["meta"], c["X"], out=c["Y"])
+        sp.sp24_gemm_bf16(c["vals"], c["meta"], M, c["X"], out=c["Y"])
 
     def cpu_sample(budget_s):
         import oracle
@@ -76,11 +77,11 @@ def workload_vit(args):
         t_prune = time.perf_counter() - t0
         rows = 8
         t0 = time.perf_counter()
-        oracle.gemm_bf16(v, m, d["X_bf16"], rows=np.arange(rows))
+        oracle.gemm_bf16(v, m, d["X_bf16"], M, rows=np.arange(rows))
         t_small = time.perf_counter() - t0
         rows = int(min(M, max(8, rows * (budget_s - t_prune) / max(t_small, 1e-6))))
         t0 = time.perf_counter()
-        oracle.gemm_bf16(v, m, d["X_bf16"], rows=np.arange(rows))
+        oracle.gemm_bf16(v, m, d["X_bf16"], M, rows=np.arange(rows))
         t_rows = time.perf_counter() - t0
         t_step = t_prune + t_rows * M / rows
         return t_step, f"prune/compress of the full {M}x{K} W + GEMM on {rows} of {M} rows, scaled to all rows"

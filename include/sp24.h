@@ -17,17 +17,31 @@
  *  - oeforum post on sparse acceleration: exactly 2 of every 4 are zero, 2-bit metadata per kept
  *    value; int8 and 2:4 combine.
  *
- * Data formats (all matrices row-major):
- *  W       M x K weight (output channels x input channels), row pitch ldw elements.
- *  values  M x K/2, packed (row pitch K/2): for group g = 4 consecutive columns 4g..4g+3 of row i, the
- *          two kept elements in ascending column order at values[i, 2g] and values[i, 2g+1].
- *  meta    M x K/8 bytes, packed (row pitch K/8): group g of row i is the nibble i0 | (i1 << 2),
- *          0 <= i0 < i1 <= 3 the kept positions, stored in byte g/2 of the row, even g in the low
- *          nibble. This is the per-lane index format of gfx950's v_smfmac, so a 16-column slice of a
- *          row's metadata (2 bytes) is one smfmac index operand.
+ * Data formats:
+ *  W       M x K weight (output channels x input channels), row-major, row pitch ldw elements.
  *  X       K x N activations (input channels x tokens; one NCHW image of a 1x1 conv is Cin x H*W),
- *          row pitch ldx elements.
- *  Y       M x N output, row pitch ldy elements.
+ *          row-major, row pitch ldx elements.
+ *  Y       M x N output, row-major, row pitch ldy elements.
+ *  values, meta -- the compressed weight. Logically, compressed row i holds, for each group g of 4
+ *          consecutive columns 4g..4g+3, the two kept elements in ascending column order (kept value
+ *          j = 2g + t), and the nibble i0 | (i1 << 2) (0 <= i0 < i1 <= 3, the kept positions) in
+ *          metadata byte g/2 of the row, even g in the low nibble. That nibble is the per-value
+ *          2-bit index format of gfx950's v_smfmac.
+ *          Physically both streams are stored in the order one v_smfmac holds its sparse operand:
+ *           - rows are padded to Mp = M rounded up to 16, columns to Kp = K rounded up to
+ *             KT = 128 / e dense columns (e = value size in bytes: bf16/fp16 64, fp32 32, int8 128);
+ *           - a tile is 16 rows x 64 bytes of values (KT dense columns) and 16 rows x KT/8 bytes of
+ *             metadata; tiles are stored row block by row block, along K inside a row block;
+ *           - inside a tile each row is cut into 4 quarters (16 bytes of values; KT/32 bytes of
+ *             metadata) stored quarter-major: quarter 0 of rows 0..15, then quarter 1, ... -- so for
+ *             bf16, byte range [16 l, 16 l + 16) of a values tile and [2 l, 2 l + 2) of its metadata
+ *             tile are exactly the A operand and index operand of lane l of one
+ *             v_smfmac_f32_16x16x64_bf16 (int8: v_smfmac_i32_16x16x128_i8, 4 metadata bytes);
+ *           - byte b of compressed row i is at ((i/16 * Kp/KT + b/T) * 4 + (b%T)/(T/4)) * 4T
+ *             + (i%16) * T/4 + b % (T/4), with T = 64 for values and T = KT/8 for metadata;
+ *           - padded rows and columns hold value 0 and metadata nibble 0x4 (positions 0 and 1).
+ *          Buffer sizes: values Mp * Kp/2 * e bytes, metadata Mp * Kp/8 bytes
+ *          (sp24_compressed_bytes computes them).
  *
  * Selection: element t of a group beats element u when its score is larger, or equal with t < u
  * (lower index wins ties); the two elements beaten by at most one other are kept. Scores are |w|
@@ -44,8 +58,10 @@
  *    must be at least the row length. M and N need no padding: tails are handled in the kernels.
  *  - Base pointers must be 16-byte aligned, and where stated a row pitch must keep rows 16-byte
  *    aligned (true for any contiguous tensor whose rows are multiples of 16 bytes).
- *  - values/meta passed to sp24_decompress and the GEMMs must be canonical (i0 < i1 in every nibble),
- *    which sp24_prune_compress always produces; other metadata is outside the contract.
+ *  - values/meta passed to sp24_decompress and the GEMMs must be canonical (i0 < i1 in every nibble)
+ *    and laid out as above, which sp24_prune_compress always produces; other metadata is outside
+ *    the contract. The library cannot check buffer lengths: the caller provides buffers of the
+ *    sizes sp24_compressed_bytes reports.
  *  - The device must be gfx950 (MI355X / MI350X), else SP24_ERR_DEVICE.
  *  - Reentrant; concurrent calls on different streams are independent.
  */
@@ -80,26 +96,30 @@ typedef enum { SP24_SCORE_MAGNITUDE = 0, SP24_SCORE_WANDA = 1 } sp24_score;
  * rounded once to fp32. K need not be a multiple of 16 here (K >= 1). */
 int sp24_col_norms(const void* X, int64_t K, int64_t N, int64_t ldx, float* norms, void* stream);
 
+/* Sizes in bytes of the compressed values and metadata of an M x K weight whose kept values have
+ * dtype val_dtype (BF16, FP16, FP32 or I8). Host-only, no HIP call. */
+int sp24_compressed_bytes(int64_t M, int64_t K, int val_dtype, int64_t* values_bytes, int64_t* meta_bytes);
+
 /* 2:4 prune and compress (Orin NN design, Chapter 7, section 2.1, Steps 1-2).
  *   W: M x K of dtype in {BF16, FP16, FP32, I8}, pitch ldw with ldw*sizeof(dtype) % 16 == 0.
  *   score: MAGNITUDE (norms must be NULL) or WANDA (norms: fp32[K] device array, dtype not I8).
- *   values: M x K/2 of val_dtype, where val_dtype == dtype, or BF16 when dtype == FP32 (the kept fp32
- *           values rounded to nearest even). Otherwise kept values are bit-exact copies (-0 stays -0).
- *   meta: M x K/8 bytes. */
+ *   values: compressed values of val_dtype, where val_dtype == dtype, or BF16 when dtype == FP32 (the
+ *           kept fp32 values rounded to nearest even); otherwise kept values are bit-exact copies
+ *           (-0 stays -0). meta: the metadata. Both in the tiled layout above, padding included. */
 int sp24_prune_compress(const void* W, int dtype, int64_t M, int64_t K, int64_t ldw, int score,
                         const float* norms, void* values, int val_dtype, uint8_t* meta, void* stream);
 
 /* Inverse of the compression: W_out (M x K of dtype in {BF16, FP16, FP32, I8}, pitch ldw with
  * ldw*sizeof(dtype) % 16 == 0) gets every kept value at its original column and +0 (all-zero bits)
- * at the two pruned columns of every group. */
+ * at the two pruned columns of every group. dtype is the values' dtype. */
 int sp24_decompress(const void* values, const uint8_t* meta, int dtype, int64_t M, int64_t K, void* W_out,
                     int64_t ldw, void* stream);
 
 /* Sparse x dense GEMM in bf16 with fp32 accumulation (NVIDIA blog Figure 1; Orin NN design,
  * Chapter 7, section 2.1 Step 3):
  *   Y[m, n] = sum_g sum_{t=0,1} values[m, 2g+t] * X[4g + i_t(m, g), n].
- *   values: bf16 M x K/2, meta M x K/8, X: bf16 K x N (pitch ldx >= N, any value), Y: M x N (pitch
- *   ldy >= N) of out_dtype FP32, or BF16 (the fp32 result rounded to nearest even).
+ *   values (bf16) and meta: the compressed M x K weight; X: bf16 K x N (pitch ldx >= N, any value);
+ *   Y: M x N (pitch ldy >= N) of out_dtype FP32, or BF16 (the fp32 result rounded to nearest even).
  *   The kernel is chosen from (M, N, K) and the operand alignment; results never depend on it beyond
  *   fp32 summation order. */
 int sp24_gemm_bf16(const void* values, const uint8_t* meta, int64_t M, int64_t K, const void* X, int64_t N,
@@ -111,7 +131,8 @@ int sp24_gemm_bf16(const void* values, const uint8_t* meta, int64_t M, int64_t K
  *               K <= 262142),
  *   scale != NULL: Y fp32, Y[m, n] = fl32( fl32(acc[m, n]) * scale[m] )  (one multiply, no fusing)
  *   scale == NULL: Y int32, Y[m, n] = acc[m, n].
- *   values: int8 M x K/2, meta M x K/8, X: int8 K x N (pitch ldx >= N), Y pitch ldy >= N. */
+ *   values (int8) and meta: the compressed M x K weight; X: int8 K x N (pitch ldx >= N); Y pitch
+ *   ldy >= N. */
 int sp24_gemm_i8(const int8_t* values, const uint8_t* meta, int64_t M, int64_t K, const int8_t* X, int64_t N,
                  int64_t ldx, const float* scale, void* Y, int64_t ldy, void* stream);
 

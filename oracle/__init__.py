@@ -53,8 +53,13 @@ def _load():
         P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
         lib.oracle_col_norms.argtypes = [P, I64, I64, I64, P]
         lib.oracle_prune_compress.argtypes = [P, I, I64, I64, I64, I, P, P, I, P]
-        lib.oracle_meta_check.argtypes = [P, I64, I64]
+        lib.oracle_meta_check.argtypes = [P, I64, I64, I]
         lib.oracle_meta_check.restype = I64
+        lib.oracle_compressed_bytes.argtypes = [I64, I64, I, ctypes.POINTER(I64), ctypes.POINTER(I64)]
+        lib.oracle_values_offset.argtypes = [I64, I64, I64, I]
+        lib.oracle_values_offset.restype = I64
+        lib.oracle_meta_offset.argtypes = [I64, I64, I64, I]
+        lib.oracle_meta_offset.restype = I64
         lib.oracle_decompress.argtypes = [P, P, I, I64, I64, P, I64]
         lib.oracle_gemm_bf16.argtypes = [P, P, I64, I64, P, I64, I64, P, I64, P]
         lib.oracle_gemm_i8.argtypes = [P, P, I64, I64, P, I64, I64, P, P, I64, P, P]
@@ -99,14 +104,26 @@ def col_norms(X_bf16: np.ndarray) -> np.ndarray:
     return out
 
 
+_ESIZE = {BF16: 2, FP16: 2, FP32: 4, I8: 1}
+
+
+def compressed_bytes(M: int, K: int, val_dtype: int):
+    """(values bytes, metadata bytes) of the compressed form of an M x K weight."""
+    vb, mb = ctypes.c_int64(), ctypes.c_int64()
+    _check(_load().oracle_compressed_bytes(M, K, val_dtype, ctypes.byref(vb), ctypes.byref(mb)))
+    return vb.value, mb.value
+
+
 def prune_compress(W: np.ndarray, dtype: int, score: int = MAGNITUDE, norms: np.ndarray | None = None,
                    val_dtype: int | None = None):
-    """Prune each group of 4 along K to its top-2 and compress. Returns (values, meta)."""
+    """Prune each group of 4 along K to its top-2 and compress. Returns (values, meta) as flat
+    buffers in the tiled layout (values in val_dtype, meta uint8)."""
     val_dtype = dtype if val_dtype is None else val_dtype
     W = np.ascontiguousarray(_c(W, _DT_NP[dtype]))
     M, K = W.shape
-    values = np.zeros((M, K // 2), _DT_NP[val_dtype])
-    meta = np.zeros((M, K // 8), np.uint8)
+    vb, mb = compressed_bytes(M, K, val_dtype)
+    values = np.zeros(vb // _ESIZE[val_dtype], _DT_NP[val_dtype])
+    meta = np.zeros(mb, np.uint8)
     if norms is not None:
         norms = np.ascontiguousarray(_c(norms, np.float32))
     _check(_load().oracle_prune_compress(_ptr(W), dtype, M, K, K, score, _ptr(norms), _ptr(values), val_dtype,
@@ -114,15 +131,29 @@ def prune_compress(W: np.ndarray, dtype: int, score: int = MAGNITUDE, norms: np.
     return values, meta
 
 
-def meta_bad_nibbles(meta: np.ndarray, K: int) -> int:
+def meta_bad_nibbles(meta: np.ndarray, M: int, K: int, val_dtype: int) -> int:
     meta = np.ascontiguousarray(_c(meta, np.uint8))
-    return int(_load().oracle_meta_check(_ptr(meta), meta.shape[0], K))
+    return int(_load().oracle_meta_check(_ptr(meta), M, K, val_dtype))
 
 
-def decompress(values: np.ndarray, meta: np.ndarray, dtype: int) -> np.ndarray:
+def values_offset(i: int, b: int, K: int, val_dtype: int) -> int:
+    return int(_load().oracle_values_offset(i, b, K, _ESIZE[val_dtype]))
+
+
+def meta_offset(i: int, mb: int, K: int, val_dtype: int) -> int:
+    return int(_load().oracle_meta_offset(i, mb, K, _ESIZE[val_dtype]))
+
+
+def _check_sizes(values, meta, M, K, dtype):
+    vb, mb = compressed_bytes(M, K, dtype)
+    if values.nbytes != vb or meta.nbytes != mb:
+        raise ValueError(f"compressed buffers of {values.nbytes}/{meta.nbytes} bytes, expected {vb}/{mb}")
+
+
+def decompress(values: np.ndarray, meta: np.ndarray, dtype: int, M: int, K: int) -> np.ndarray:
     values = np.ascontiguousarray(_c(values, _DT_NP[dtype]))
     meta = np.ascontiguousarray(_c(meta, np.uint8))
-    M, K = values.shape[0], values.shape[1] * 2
+    _check_sizes(values, meta, M, K, dtype)
     out = np.empty((M, K), _DT_NP[dtype])
     _check(_load().oracle_decompress(_ptr(values), _ptr(meta), dtype, M, K, _ptr(out), K))
     return out
@@ -134,30 +165,27 @@ def _rows_arg(rows, M):
     return np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
 
 
-def gemm_bf16(values: np.ndarray, meta: np.ndarray, X: np.ndarray, rows=None) -> np.ndarray:
-    """Y[r, :] = (pruned W)[rows[r], :] . X in float64 (values/X: bf16 bits as uint16)."""
+def gemm_bf16(values: np.ndarray, meta: np.ndarray, X: np.ndarray, M: int, rows=None) -> np.ndarray:
+    """Y[r, :] = (pruned W)[rows[r], :] . X in float64 (values/X: bf16 bits as uint16; K = X rows)."""
     values = np.ascontiguousarray(_c(values, np.uint16))
     meta = np.ascontiguousarray(_c(meta, np.uint8))
     X = np.ascontiguousarray(_c(X, np.uint16))
-    M, K = values.shape[0], values.shape[1] * 2
-    N = X.shape[1]
-    if X.shape[0] != K:
-        raise ValueError("X must be K x N")
+    K, N = X.shape
+    _check_sizes(values, meta, M, K, BF16)
     r = _rows_arg(rows, M)
     Y = np.empty((len(r), N), np.float64)
     _check(_load().oracle_gemm_bf16(_ptr(values), _ptr(meta), M, K, _ptr(X), N, N, _ptr(r), len(r), _ptr(Y)))
     return Y
 
 
-def gemm_i8(values: np.ndarray, meta: np.ndarray, X: np.ndarray, scale: np.ndarray | None = None, rows=None):
+def gemm_i8(values: np.ndarray, meta: np.ndarray, X: np.ndarray, M: int, scale: np.ndarray | None = None,
+            rows=None):
     """Exact int64 accumulators (checked to fit int32) and, with ``scale``, fl32(fl32(acc) * scale[m])."""
     values = np.ascontiguousarray(_c(values, np.int8))
     meta = np.ascontiguousarray(_c(meta, np.uint8))
     X = np.ascontiguousarray(_c(X, np.int8))
-    M, K = values.shape[0], values.shape[1] * 2
-    N = X.shape[1]
-    if X.shape[0] != K:
-        raise ValueError("X must be K x N")
+    K, N = X.shape
+    _check_sizes(values, meta, M, K, I8)
     r = _rows_arg(rows, M)
     acc = np.empty((len(r), N), np.int64)
     Y = None

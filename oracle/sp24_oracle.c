@@ -25,7 +25,8 @@
  *  - kept values are stored in ascending position order [ORIN7 2.1 Step 2 shows [-0.5, 0.2] for
  *    positions 1 and 3];
  *  - metadata nibble of group g = i0 | (i1 << 2) with i0 < i1, group g of a row in byte g/2 of that
- *    row's K/8 metadata bytes, even g in the low nibble;
+ *    row's metadata bytes, even g in the low nibble; the bytes of both streams are placed in 16-row
+ *    tiles in the order of the sparse MFMA operand (see "compressed layout" below);
  *  - the Wanda score is the single-precision product fl32(|w|) * norms[j]; norms are an input;
  *  - the pruned slots decompress to +0.
  *
@@ -137,6 +138,64 @@ int oracle_col_norms(const uint16_t* X, int64_t K, int64_t N, int64_t ldx, float
     return OR_OK;
 }
 
+/* ---------------------------------------------------------------- compressed layout */
+
+/* Where the compressed stream lives in memory. The pages fix what is stored (the kept values in
+ * ascending position order plus 2 bits of position each [ORIN7 2.1 Step 2; NVBLOG Figure 1]) but
+ * not the placement; this library stores it in the order gfx950's sparse MFMA holds its sparse
+ * operand, so a tile can be copied straight into the instruction's registers:
+ *  - rows are padded to Mp = M rounded up to 16, columns to Kp = K rounded up to KT = 128 / e
+ *    dense columns (e = value size in bytes: bf16/fp16 64, fp32 32, int8 128);
+ *  - a tile is 16 rows x 64 bytes of values (= KT dense columns) and 16 rows x KT/8 bytes of
+ *    metadata; tiles go row-block by row-block, and along K inside a row block;
+ *  - inside a tile each row's bytes are cut into 4 quarters (16 bytes of values, KT/32 bytes of
+ *    metadata) and stored quarter-major: quarter 0 of rows 0..15, then quarter 1, ...;
+ *  - padding holds value 0 and metadata nibble 0x4 (positions 0 and 1).
+ * The offset functions below are that definition written out. */
+
+static int64_t dense_tile_width(int esize) { return 128 / esize; }
+
+static int64_t padded_k(int64_t K, int esize) {
+    int64_t kt = dense_tile_width(esize);
+    return (K + kt - 1) / kt * kt;
+}
+
+static int64_t padded_m(int64_t M) { return (M + 15) / 16 * 16; }
+
+/* Byte offset of byte b (0 <= b < Kp*e/2) of compressed row i in the values buffer. */
+static size_t values_offset(int64_t i, int64_t b, int64_t K, int esize) {
+    const int64_t tiles_per_row = padded_k(K, esize) / dense_tile_width(esize);
+    const int64_t rb = i / 16, r = i % 16;
+    const int64_t t = b / 64, c = (b % 64) / 16, o = b % 16;
+    return (size_t)(((rb * tiles_per_row + t) * 4 + c) * 256 + r * 16 + o);
+}
+
+/* Byte offset of metadata byte mb (0 <= mb < Kp/8) of row i in the metadata buffer. */
+static size_t meta_offset(int64_t i, int64_t mb, int64_t K, int esize) {
+    const int64_t tiles_per_row = padded_k(K, esize) / dense_tile_width(esize);
+    const int64_t tm = dense_tile_width(esize) / 8, qm = tm / 4;
+    const int64_t rb = i / 16, r = i % 16;
+    const int64_t t = mb / tm, c = (mb % tm) / qm, o = mb % qm;
+    return (size_t)(((rb * tiles_per_row + t) * 4 + c) * (16 * qm) + r * qm + o);
+}
+
+/* Sizes of the two buffers for an M x K weight of the given value dtype. */
+int oracle_compressed_bytes(int64_t M, int64_t K, int val_dtype, int64_t* values_bytes, int64_t* meta_bytes) {
+    const int esize = (int)dtype_size(val_dtype);
+    if (esize == 0 || val_dtype == OR_I32 || M < 0 || K < 0) return OR_EARG;
+    *values_bytes = padded_m(M) * padded_k(K, esize) / 2 * esize;
+    *meta_bytes = padded_m(M) * padded_k(K, esize) / 8;
+    return OR_OK;
+}
+
+int64_t oracle_values_offset(int64_t i, int64_t b, int64_t K, int esize) { return (int64_t)values_offset(i, b, K, esize); }
+int64_t oracle_meta_offset(int64_t i, int64_t mb, int64_t K, int esize) { return (int64_t)meta_offset(i, mb, K, esize); }
+
+/* Nibble (kept positions) of group g of row i. */
+static int get_nibble(const uint8_t* meta, int64_t i, int64_t g, int64_t K, int esize) {
+    return (meta[meta_offset(i, g / 2, K, esize)] >> (4 * (g % 2))) & 0xF;
+}
+
 /* ---------------------------------------------------------------- prune + compress [ORIN7 2.1] */
 
 /* Scores of one group of four: magnitude |w| [ORIN7 2.1 Step 1] or Wanda fl32(|w|) * norm_j
@@ -172,22 +231,26 @@ static void keep_two(const double s[4], int* i0, int* i1) {
     *i1 = kept[1];
 }
 
-/* W: M x K row-major (pitch ldw elements) of dtype in {BF16, FP16, FP32, I8}. Writes values
- * (M x K/2 of val_dtype, packed) and meta (M x K/8 bytes, packed). val_dtype equals dtype, or is
- * BF16 when dtype is FP32 (round to nearest even). score WANDA needs norms[K] and a float dtype. */
+/* W: M x K row-major (pitch ldw elements) of dtype in {BF16, FP16, FP32, I8}, K % 16 == 0.
+ * Writes the compressed values (val_dtype) and metadata in the layout above; the buffers must hold
+ * oracle_compressed_bytes(M, K, val_dtype) bytes. val_dtype equals dtype, or is BF16 when dtype is
+ * FP32 (round to nearest even). score WANDA needs norms[K] and a float dtype. */
 int oracle_prune_compress(const void* W, int dtype, int64_t M, int64_t K, int64_t ldw, int score,
                           const float* norms, void* values, int val_dtype, uint8_t* meta) {
-    if (!W || !values || !meta || M < 0 || K < 0 || K % 8 != 0 || ldw < K) return OR_EARG;
+    if (!W || !values || !meta || M < 0 || K < 0 || K % 16 != 0 || ldw < K) return OR_EARG;
     if (dtype != OR_BF16 && dtype != OR_FP16 && dtype != OR_FP32 && dtype != OR_I8) return OR_EARG;
     if (!(val_dtype == dtype || (dtype == OR_FP32 && val_dtype == OR_BF16))) return OR_EARG;
     if (score == OR_WANDA && (!norms || dtype == OR_I8)) return OR_EARG;
     if (score != OR_WANDA && score != OR_MAGNITUDE) return OR_EARG;
-    const size_t isz = dtype_size(dtype), vsz = dtype_size(val_dtype);
+    const size_t isz = dtype_size(dtype);
+    const int vsz = (int)dtype_size(val_dtype);
+    int64_t vbytes, mbytes;
+    oracle_compressed_bytes(M, K, val_dtype, &vbytes, &mbytes);
+    memset(values, 0, (size_t)vbytes);          /* padding: value 0 */
+    memset(meta, 0x44, (size_t)mbytes);          /* padding: positions 0 and 1 */
     const int64_t G = K / 4;
 #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < M; i++) {
-        uint8_t* mrow = meta + (size_t)i * (size_t)(K / 8);
-        memset(mrow, 0, (size_t)(K / 8));
         for (int64_t g = 0; g < G; g++) {
             size_t base = (size_t)i * (size_t)ldw + (size_t)(4 * g);
             double s[4];
@@ -197,18 +260,20 @@ int oracle_prune_compress(const void* W, int dtype, int64_t M, int64_t K, int64_
             int pos[2] = {i0, i1};
             for (int t = 0; t < 2; t++) {
                 size_t src = base + (size_t)pos[t];
-                size_t dst = (size_t)i * (size_t)(K / 2) + (size_t)(2 * g + t);
+                int64_t j = 2 * g + t; /* index of the kept value in the compressed row */
+                char* dst = (char*)values + values_offset(i, j * vsz, K, vsz);
                 if (val_dtype == dtype) {
-                    memcpy((char*)values + dst * vsz, (const char*)W + src * isz, isz); /* bit copy */
+                    memcpy(dst, (const char*)W + src * isz, isz); /* bit copy */
                 } else {
                     uint32_t u;
                     memcpy(&u, (const char*)W + src * 4, 4);
                     uint16_t h = fp32_to_bf16_rne(u);
-                    memcpy((char*)values + dst * 2, &h, 2);
+                    memcpy(dst, &h, 2);
                 }
             }
             uint8_t nib = (uint8_t)(i0 | (i1 << 2));
-            mrow[g / 2] |= (uint8_t)(nib << (4 * (g % 2)));
+            uint8_t* mb = meta + meta_offset(i, g / 2, K, vsz);
+            *mb = (uint8_t)((*mb & (0xF0 >> (4 * (g % 2)))) | (nib << (4 * (g % 2))));
         }
     }
     return OR_OK;
@@ -216,13 +281,14 @@ int oracle_prune_compress(const void* W, int dtype, int64_t M, int64_t K, int64_
 
 /* ---------------------------------------------------------------- metadata check [ORIN7 6.1] */
 
-/* Every nibble must name two distinct positions in ascending order. Returns the number of bad
- * nibbles (0 when the stream is canonical). */
-int64_t oracle_meta_check(const uint8_t* meta, int64_t M, int64_t K) {
+/* Every nibble of the M x K region must name two distinct positions in ascending order. Returns
+ * the number of bad nibbles (0 when the stream is canonical). val_dtype fixes the layout. */
+int64_t oracle_meta_check(const uint8_t* meta, int64_t M, int64_t K, int val_dtype) {
+    const int esize = (int)dtype_size(val_dtype);
     int64_t bad = 0;
     for (int64_t i = 0; i < M; i++)
         for (int64_t g = 0; g < K / 4; g++) {
-            int nib = (meta[(size_t)i * (size_t)(K / 8) + (size_t)(g / 2)] >> (4 * (g % 2))) & 0xF;
+            int nib = get_nibble(meta, i, g, K, esize);
             int i0 = nib & 3, i1 = (nib >> 2) & 3;
             if (!(i0 < i1)) bad++;
         }
@@ -231,24 +297,24 @@ int64_t oracle_meta_check(const uint8_t* meta, int64_t M, int64_t K) {
 
 /* ---------------------------------------------------------------- decompress */
 
-/* Inverse of the compression: values[i, 2g + t] goes back to column 4g + i_t of row i; the other
- * two columns of the group get +0 (all-zero bits). W_out: M x K row-major, pitch ldw. */
+/* Inverse of the compression: the kept value j = 2g + t of row i goes back to column 4g + i_t; the
+ * other two columns of the group get +0 (all-zero bits). W_out: M x K row-major, pitch ldw. */
 int oracle_decompress(const void* values, const uint8_t* meta, int dtype, int64_t M, int64_t K, void* W_out,
                       int64_t ldw) {
-    if (!values || !meta || !W_out || M < 0 || K < 0 || K % 8 != 0 || ldw < K) return OR_EARG;
+    if (!values || !meta || !W_out || M < 0 || K < 0 || K % 16 != 0 || ldw < K) return OR_EARG;
     const size_t sz = dtype_size(dtype);
     if (sz == 0 || dtype == OR_I32) return OR_EARG;
-    if (oracle_meta_check(meta, M, K) != 0) return OR_EMETA;
+    if (oracle_meta_check(meta, M, K, dtype) != 0) return OR_EMETA;
 #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < M; i++) {
         char* orow = (char*)W_out + (size_t)i * (size_t)ldw * sz;
         memset(orow, 0, (size_t)K * sz);
         for (int64_t g = 0; g < K / 4; g++) {
-            int nib = (meta[(size_t)i * (size_t)(K / 8) + (size_t)(g / 2)] >> (4 * (g % 2))) & 0xF;
+            int nib = get_nibble(meta, i, g, K, (int)sz);
             int pos[2] = {nib & 3, (nib >> 2) & 3};
             for (int t = 0; t < 2; t++) {
-                size_t src = (size_t)i * (size_t)(K / 2) + (size_t)(2 * g + t);
-                memcpy(orow + (size_t)(4 * g + pos[t]) * sz, (const char*)values + src * sz, sz);
+                const char* src = (const char*)values + values_offset(i, (2 * g + t) * (int64_t)sz, K, (int)sz);
+                memcpy(orow + (size_t)(4 * g + pos[t]) * sz, src, sz);
             }
         }
     }
@@ -257,27 +323,38 @@ int oracle_decompress(const void* values, const uint8_t* meta, int dtype, int64_
 
 /* ---------------------------------------------------------------- sparse x dense GEMM */
 
+/* Exact value of kept value j of row i. */
+static double kept_value(const void* values, int dtype, int64_t i, int64_t j, int64_t K) {
+    const int sz = (int)dtype_size(dtype);
+    const char* p = (const char*)values + values_offset(i, j * sz, K, sz);
+    switch (dtype) {
+    case OR_BF16: { uint16_t h; memcpy(&h, p, 2); return bf16_value(h); }
+    case OR_I8: return (double)*(const int8_t*)p;
+    }
+    return NAN;
+}
+
 /* Dense row i of the pruned weight, as exact doubles (zeros at pruned slots). */
 static void dense_row(const void* values, const uint8_t* meta, int dtype, int64_t i, int64_t K, double* w) {
     for (int64_t k = 0; k < K; k++) w[k] = 0.0;
     for (int64_t g = 0; g < K / 4; g++) {
-        int nib = (meta[(size_t)i * (size_t)(K / 8) + (size_t)(g / 2)] >> (4 * (g % 2))) & 0xF;
-        w[4 * g + (nib & 3)] = elem_value(values, dtype, (size_t)i * (size_t)(K / 2) + (size_t)(2 * g));
-        w[4 * g + ((nib >> 2) & 3)] = elem_value(values, dtype, (size_t)i * (size_t)(K / 2) + (size_t)(2 * g + 1));
+        int nib = get_nibble(meta, i, g, K, (int)dtype_size(dtype));
+        w[4 * g + (nib & 3)] = kept_value(values, dtype, i, 2 * g, K);
+        w[4 * g + ((nib >> 2) & 3)] = kept_value(values, dtype, i, 2 * g + 1, K);
     }
 }
 
 /* Y = W_2:4 . X for a list of output rows, in double [ORIN7 2.1 Step 3; NVBLOG Figure 1].
- * values: bf16 M x K/2, meta M x K/8, X: bf16 K x N row-major (pitch ldx).
+ * values: bf16, meta: as above; X: bf16 K x N row-major (pitch ldx).
  * rows[r] (r < nrows) names the output row; Y is nrows x N (row pitch N), double.
  * The row is rebuilt densely and each Y[r, n] sums W[m, k] * X[k, n] over k in ascending order;
  * every product of two bf16 numbers is exact in double. */
 int oracle_gemm_bf16(const uint16_t* values, const uint8_t* meta, int64_t M, int64_t K, const uint16_t* X,
                      int64_t N, int64_t ldx, const int64_t* rows, int64_t nrows, double* Y) {
-    if (!values || !meta || !X || !rows || !Y || M < 0 || K < 0 || K % 8 != 0 || N < 0 || ldx < N) return OR_EARG;
+    if (!values || !meta || !X || !rows || !Y || M < 0 || K < 0 || K % 16 != 0 || N < 0 || ldx < N) return OR_EARG;
     for (int64_t r = 0; r < nrows; r++)
         if (rows[r] < 0 || rows[r] >= M) return OR_EARG;
-    if (oracle_meta_check(meta, M, K) != 0) return OR_EMETA;
+    if (oracle_meta_check(meta, M, K, OR_BF16) != 0) return OR_EMETA;
 #pragma omp parallel
     {
         double* w = (double*)malloc(sizeof(double) * (size_t)(K > 0 ? K : 1));
@@ -301,12 +378,12 @@ int oracle_gemm_bf16(const uint16_t* values, const uint8_t* meta, int64_t M, int
  * If Y is not NULL, Y[r, n] = fl32( fl32(acc) * scale[m] ), one single-precision multiply. */
 int oracle_gemm_i8(const int8_t* values, const uint8_t* meta, int64_t M, int64_t K, const int8_t* X, int64_t N,
                    int64_t ldx, const float* scale, const int64_t* rows, int64_t nrows, int64_t* acc_out, float* Y) {
-    if (!values || !meta || !X || !rows || !acc_out || M < 0 || K < 0 || K % 8 != 0 || N < 0 || ldx < N)
+    if (!values || !meta || !X || !rows || !acc_out || M < 0 || K < 0 || K % 16 != 0 || N < 0 || ldx < N)
         return OR_EARG;
     if (Y && !scale) return OR_EARG;
     for (int64_t r = 0; r < nrows; r++)
         if (rows[r] < 0 || rows[r] >= M) return OR_EARG;
-    if (oracle_meta_check(meta, M, K) != 0) return OR_EMETA;
+    if (oracle_meta_check(meta, M, K, OR_I8) != 0) return OR_EMETA;
     int overflow = 0;
 #pragma omp parallel reduction(| : overflow)
     {

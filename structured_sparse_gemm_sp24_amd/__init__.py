@@ -21,8 +21,8 @@ SP24_BF16, SP24_FP16, SP24_FP32, SP24_I8, SP24_I32 = 0, 1, 2, 3, 4
 SP24_SCORE_MAGNITUDE, SP24_SCORE_WANDA = 0, 1
 
 # every symbol include/sp24.h declares
-EXPORTS = ("sp24_col_norms", "sp24_prune_compress", "sp24_decompress", "sp24_gemm_bf16", "sp24_gemm_i8",
-           "sp24_status_string")
+EXPORTS = ("sp24_col_norms", "sp24_compressed_bytes", "sp24_prune_compress", "sp24_decompress", "sp24_gemm_bf16",
+           "sp24_gemm_i8", "sp24_status_string")
 
 _TORCH_TO_SP24 = {torch.bfloat16: SP24_BF16, torch.float16: SP24_FP16, torch.float32: SP24_FP32,
                   torch.int8: SP24_I8, torch.int32: SP24_I32}
@@ -49,6 +49,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib = ctypes.CDLL(path)
     P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     lib.sp24_col_norms.argtypes = [P, I64, I64, I64, P, P]
+    lib.sp24_compressed_bytes.argtypes = [I64, I64, I, ctypes.POINTER(I64), ctypes.POINTER(I64)]
     lib.sp24_prune_compress.argtypes = [P, I, I64, I64, I64, I, P, P, I, P, P]
     lib.sp24_decompress.argtypes = [P, P, I, I64, I64, P, I64, P]
     lib.sp24_gemm_bf16.argtypes = [P, P, I64, I64, P, I64, I64, P, I, I64, P]
@@ -103,27 +104,51 @@ def sp24_col_norms(X: torch.Tensor, norms: torch.Tensor | None = None) -> torch.
     return norms
 
 
+_ESIZE = {torch.bfloat16: 2, torch.float16: 2, torch.float32: 4, torch.int8: 1}
+
+
+def sp24_compressed_bytes(M: int, K: int, val_dtype: torch.dtype):
+    """(values bytes, metadata bytes) of the compressed form of an M x K weight."""
+    vb, mb = ctypes.c_int64(), ctypes.c_int64()
+    _check("sp24_compressed_bytes", load_library().sp24_compressed_bytes(M, K, _TORCH_TO_SP24[val_dtype],
+                                                                           ctypes.byref(vb), ctypes.byref(mb)))
+    return vb.value, mb.value
+
+
+def _check_compressed(values: torch.Tensor, meta: torch.Tensor, M: int, K: int):
+    vb, mb = sp24_compressed_bytes(M, K, values.dtype)
+    if values.numel() * _ESIZE[values.dtype] != vb or meta.numel() != mb or meta.dtype != torch.uint8:
+        raise ValueError(f"compressed buffers hold {values.numel() * _ESIZE[values.dtype]} / {meta.numel()} bytes; "
+                         f"an {M} x {K} weight needs {vb} / {mb}")
+    if not (values.is_contiguous() and meta.is_contiguous()):
+        raise ValueError("compressed buffers must be contiguous")
+
+
 def sp24_prune_compress(W: torch.Tensor, score: int = SP24_SCORE_MAGNITUDE, norms: torch.Tensor | None = None,
                         val_dtype: torch.dtype | None = None, values: torch.Tensor | None = None,
                         meta: torch.Tensor | None = None):
-    """2:4 prune + compress of W (M x K); returns (values M x K/2, meta M x K/8 uint8)."""
+    """2:4 prune + compress of W (M x K). Returns (values, meta): 1-D buffers in the tiled layout of
+    include/sp24.h (values of val_dtype, meta uint8), sized by sp24_compressed_bytes."""
     _dev_check(W, norms, values, meta)
     M, K = W.shape
     vdt = W.dtype if val_dtype is None else val_dtype
+    vb, mb = sp24_compressed_bytes(M, K, vdt)
     if values is None:
-        values = torch.empty((M, K // 2), dtype=vdt, device=W.device)
+        values = torch.empty(vb // _ESIZE[vdt], dtype=vdt, device=W.device)
     if meta is None:
-        meta = torch.empty((M, K // 8), dtype=torch.uint8, device=W.device)
+        meta = torch.empty(mb, dtype=torch.uint8, device=W.device)
+    _check_compressed(values, meta, M, K)
     st = load_library().sp24_prune_compress(_ptr(W), _TORCH_TO_SP24[W.dtype], M, K, _rows(W, "W"), int(score),
                                             _ptr(norms), _ptr(values), _TORCH_TO_SP24[vdt], _ptr(meta), _stream(W))
     _check("sp24_prune_compress", st)
     return values, meta
 
 
-def sp24_decompress(values: torch.Tensor, meta: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+def sp24_decompress(values: torch.Tensor, meta: torch.Tensor, M: int, K: int,
+                    out: torch.Tensor | None = None) -> torch.Tensor:
     """Dense M x K pruned weight from (values, meta); +0 at pruned slots."""
     _dev_check(values, meta, out)
-    M, K = values.shape[0], values.shape[1] * 2
+    _check_compressed(values, meta, M, K)
     if out is None:
         out = torch.empty((M, K), dtype=values.dtype, device=values.device)
     st = load_library().sp24_decompress(_ptr(values), _ptr(meta), _TORCH_TO_SP24[values.dtype], M, K, _ptr(out),
@@ -132,12 +157,13 @@ def sp24_decompress(values: torch.Tensor, meta: torch.Tensor, out: torch.Tensor 
     return out
 
 
-def sp24_gemm_bf16(values: torch.Tensor, meta: torch.Tensor, X: torch.Tensor, out_dtype: torch.dtype = torch.float32,
-                   out: torch.Tensor | None = None) -> torch.Tensor:
-    """Y = W_2:4 . X with bf16 operands and fp32 accumulation; Y is fp32 or bf16 (M x N)."""
+def sp24_gemm_bf16(values: torch.Tensor, meta: torch.Tensor, M: int, X: torch.Tensor,
+                   out_dtype: torch.dtype = torch.float32, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Y = W_2:4 . X with bf16 operands and fp32 accumulation; W is M x K (K = X rows); Y is fp32 or
+    bf16 (M x N)."""
     _dev_check(values, meta, X, out)
-    M, K = values.shape[0], values.shape[1] * 2
-    N = X.shape[1]
+    K, N = X.shape
+    _check_compressed(values, meta, M, K)
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=X.device)
     st = load_library().sp24_gemm_bf16(_ptr(values), _ptr(meta), M, K, _ptr(X), N, _rows(X, "X"), _ptr(out),
@@ -146,12 +172,12 @@ def sp24_gemm_bf16(values: torch.Tensor, meta: torch.Tensor, X: torch.Tensor, ou
     return out
 
 
-def sp24_gemm_i8(values: torch.Tensor, meta: torch.Tensor, X: torch.Tensor, scale: torch.Tensor | None = None,
+def sp24_gemm_i8(values: torch.Tensor, meta: torch.Tensor, M: int, X: torch.Tensor, scale: torch.Tensor | None = None,
                  out: torch.Tensor | None = None) -> torch.Tensor:
     """int8 sparse GEMM: int32 accumulators, or fp32 fl32(acc) * scale[m] when ``scale`` is given."""
     _dev_check(values, meta, X, scale, out)
-    M, K = values.shape[0], values.shape[1] * 2
-    N = X.shape[1]
+    K, N = X.shape
+    _check_compressed(values, meta, M, K)
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32 if scale is not None else torch.int32, device=X.device)
     st = load_library().sp24_gemm_i8(_ptr(values), _ptr(meta), M, K, _ptr(X), N, _rows(X, "X"), _ptr(scale),

@@ -11,6 +11,9 @@
 //   C/D (16 x 16 fp32): lane holds column r, rows 4q .. 4q+3.
 // So the stored values + metadata feed the instruction with no repacking.
 //
+// The compressed weight is stored in that lane order (16-row x 64-column tiles, see include/sp24.h),
+// so a wave's A operand is one contiguous 1 KB load and its index operand one 128 B load.
+//
 // This file holds the direct kernel: each wave owns a 16-row x (16*NF)-column tile, takes A and the
 // index straight from global memory and gathers B element by element with bounds checks, so it works
 // for every shape and row pitch. The tiled LDS kernels (gemm_bf16_tiled.hip) take over where their
@@ -30,20 +33,19 @@ __global__ __launch_bounds__(256) void gemm_bf16_direct(const uint16_t* __restri
     const int64_t m0 = ((int64_t)blockIdx.y * 4 + (threadIdx.x >> 6)) * 16;
     const int64_t n0 = (int64_t)blockIdx.x * 16 * NF;
     if (m0 >= M) return;  // whole wave
-    const int64_t row = m0 + r;
-    const bool row_ok = row < M;
     f32x4 acc[NF];
 #pragma unroll
     for (int f = 0; f < NF; f++) acc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    for (int64_t k0 = 0; k0 < K; k0 += 64) {
-        const int64_t kd = k0 + 16 * q;  // first dense column of this lane's A slice
-        u32x4 a = {0u, 0u, 0u, 0u};
-        uint32_t idx = 0x4444u;  // (0,1) in every group: harmless with zero values
-        if (row_ok && kd < K) {  // K % 16 == 0, so the whole 16-column slice is inside the row
-            a = *reinterpret_cast<const u32x4*>(vals + row * (K / 2) + kd / 2);
-            idx = *reinterpret_cast<const uint16_t*>(meta + row * (K / 8) + kd / 8);
-        }
+    // compressed tiles of this 16-row block: one 1 KB values tile and one 128 B metadata tile per 64
+    // dense columns, already in lane order (rows and columns are padded, so every tile exists)
+    const int64_t tiles_per_row = (K + 63) / 64;
+    const u32x4* vt = reinterpret_cast<const u32x4*>(vals) + (m0 >> 4) * tiles_per_row * 64 + lane;
+    const uint16_t* mt = reinterpret_cast<const uint16_t*>(meta) + (m0 >> 4) * tiles_per_row * 64 + lane;
+    for (int64_t t = 0; t < tiles_per_row; t++) {
+        const int64_t k0 = 64 * t;
+        const u32x4 a = vt[64 * t];
+        const uint32_t idx = mt[64 * t];
 #pragma unroll
         for (int f = 0; f < NF; f++) {
             const int64_t n = n0 + 16 * f + r;

@@ -6,13 +6,15 @@
 // K advances 64 dense columns per stage; three stages are in flight through LDS (3 x 50 KB).
 //
 // Global -> LDS uses buffer loads with LDS destination (no VGPR staging); the buffer descriptors'
-// record counts return zeros for rows past M and past the end of X, so M/N tails need no branches
-// in the main loop (columns past N only feed output columns that are never stored).
-//   A tile (compressed values, 256 rows x 64 B): stored fragment-major, [16-row block][q][r] x 16 B,
-//     so each lane's ds_read_b128 of its A operand is conflict-free.
-//   metadata (256 rows x 8 B): row-major; a lane reads its 16-bit index with ds_read_u16.
-//   B tile (X, 64 rows x 256 bf16 = 512 B per row): row-major with the 16-byte chunks of row k
-//     XOR-swizzled by swz(k), so the transposing reads below hit distinct banks.
+// record counts return zeros past the padded rows and past the end of X, so M/N tails need no
+// branches in the main loop (columns past N only feed output columns that are never stored).
+//   A (compressed values): the weight is stored as 1 KB tiles in the lane order of the smfmac A
+//     operand (16 rows x 64 dense columns), so each tile is one contiguous 64-lane copy, and a
+//     lane's ds_read_b128 of its operand is conflict-free.
+//   metadata: 128 B tiles in lane order; a lane reads its 16-bit index with ds_read_u16.
+//   B tile (X, 64 rows x 256 bf16 = 512 B per row): row-major with the 64-byte blocks of row k
+//     stored at block ^ (k & 3), so the transposing reads below hit distinct banks while every
+//     global read stays a run of 64 contiguous bytes.
 // The B operand (lane = column, 16 k values in two halves of 8) comes from four ds_read_b64_tr_b16:
 // in each 16-lane group, lane s points at row k0 + s/4, columns c0 + 4(s%4); the instruction hands
 // lane i the four consecutive k of column c0 + i.
@@ -38,13 +40,34 @@ constexpr int LOADS_PER_STAGE = 4 + 2 + 8;  // per wave: A, metadata, B
 constexpr int GROUP_M = 8;
 constexpr uint32_t RSRC_FLAGS = 0x00020000u;
 
-typedef __attribute__((address_space(3))) void* lds_vptr;
-
-__device__ __forceinline__ int swz(int k) { return 2 * ((k & 3) | ((k >> 1) & 4)); }
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+// Raw buffer descriptor: base, stride 0, byte count (reads at or past it return 0), format word.
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, int64_t bytes) {
     const int64_t n = bytes < 0 ? 0 : (bytes > 0xFFFFFFFFll ? 0xFFFFFFFFll : bytes);
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)(uint32_t)n, RSRC_FLAGS);
+    const uint64_t b = reinterpret_cast<uint64_t>(base);
+    i32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+    r[1] = __builtin_amdgcn_readfirstlane((int)((b >> 32) & 0xFFFFu));
+    r[2] = __builtin_amdgcn_readfirstlane((int)(uint32_t)n);
+    r[3] = (int)RSRC_FLAGS;
+    return r;
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const char* p) {
+    return (uint32_t)(size_t)(__attribute__((address_space(3))) const char*)p;
+}
+
+// Buffer loads with LDS destination: lane i's bytes land at lds + i * width. Issued from inline asm
+// so the compiler adds no waits of its own for them; the kernel orders them with explicit
+// s_waitcnt vmcnt + s_barrier. They write no VGPRs.
+__device__ __forceinline__ void dma16(uint32_t lds, uint32_t voff, i32x4 rsrc) {
+    lds = __builtin_amdgcn_readfirstlane(lds);  // wave-uniform (it depends on the wave index only)
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :: "s"(lds), "v"(voff), "s"(rsrc) : "memory");
+}
+__device__ __forceinline__ void dma4(uint32_t lds, uint32_t voff, i32x4 rsrc) {
+    lds = __builtin_amdgcn_readfirstlane(lds);
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+                 :: "s"(lds), "v"(voff), "s"(rsrc) : "memory");
 }
 
 template <int N>
@@ -63,58 +86,59 @@ struct Args {
     int out_fp32;
 };
 
-// Issue this wave's share of the loads of stage `s` into `smem`.
-__device__ __forceinline__ void load_stage(char* smem, const Args& a, __amdgpu_buffer_rsrc_t rA,
-                                           __amdgpu_buffer_rsrc_t rM, int64_t n0, int s, int wave, int lane) {
+// Issue this wave's share of the loads of stage `s` into `smem`. rA / rM cover the compressed
+// tiles of this workgroup's 16 row blocks (tile (b, s) of block b at (b * tiles + s) * 1 KB of
+// values and * 128 B of metadata); loads past the padded rows return zeros.
+__device__ __forceinline__ void load_stage(char* smem, const Args& a, i32x4 rA, i32x4 rM, int64_t n0, int s,
+                                           int wave, int lane) {
     const int64_t k0 = (int64_t)s * BK;
-    const int r = lane & 15, q = lane >> 4;
-    // A: 16 blocks of 16 rows x 64 B; this wave loads blocks 4*wave .. 4*wave+3
+    const int tiles = (int)(a.K / BK);
+    // A: one 1 KB tile per 16-row block, copied as is (it is already in lane order)
 #pragma unroll
     for (int j = 0; j < 4; j++) {
         const int b = 4 * wave + j;
-        const uint32_t voff = (uint32_t)((16 * b + r) * a.K + k0 + 16 * q);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_vptr)(smem + b * 1024), 16, voff, 0, 0, 0);
+        dma16(lds_addr(smem + b * 1024), (uint32_t)((b * tiles + s) * 1024 + 16 * lane), rA);
     }
-    // metadata: 256 rows x 8 B, row-major; this wave loads rows 64*wave .. +63 as dwords
+    // metadata: one 128 B tile per block; 4 blocks per wave, two per dword instruction
 #pragma unroll
     for (int h = 0; h < 2; h++) {
-        const int row0 = 64 * wave + 32 * h;
-        const uint32_t voff = (uint32_t)((row0 + (lane >> 1)) * (a.K / 8) + k0 / 8 + 4 * (lane & 1));
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rM, (lds_vptr)(smem + A_BYTES + row0 * 8), 4, voff, 0, 0, 0);
+        const int b = 4 * wave + 2 * h + (lane >> 5);
+        dma4(lds_addr(smem + A_BYTES + (4 * wave + 2 * h) * 128), (uint32_t)((b * tiles + s) * 128 + 4 * (lane & 31)),
+             rM);
     }
-    // B: 64 rows x 512 B; this wave loads rows 16*wave .. +15, two rows per instruction
-    const __amdgpu_buffer_rsrc_t rB =
-        make_rsrc(a.X + k0 * a.ldx + n0, (a.K * a.ldx - k0 * a.ldx - n0) * 2);
+    // B: 64 rows x 512 B; this wave loads rows 16*wave .. +15, two rows per instruction. The 64-byte
+    // blocks of row k are stored at block ^ (k & 3); lanes keep 16-byte runs in order inside a block.
+    const i32x4 rB = make_rsrc(a.X + k0 * a.ldx + n0, (a.K * a.ldx - k0 * a.ldx - n0) * 2);
 #pragma unroll
     for (int h = 0; h < 8; h++) {
         const int row = 16 * wave + 2 * h + (lane >> 5);
-        const int c = (lane & 31) ^ swz(row);
-        const uint32_t voff = (uint32_t)(row * a.ldx * 2 + 16 * c);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_vptr)(smem + A_BYTES + META_BYTES + (16 * wave + 2 * h) * B_ROW),
-                                                 16, voff, 0, 0, 0);
+        const int pc = lane & 31;                                  // 16-byte slot in the LDS row
+        const int lc = ((((pc >> 2) ^ (row & 3))) << 2) | (pc & 3);  // 16-byte chunk of the X row
+        dma16(lds_addr(smem + A_BYTES + META_BYTES + (16 * wave + 2 * h) * B_ROW),
+              (uint32_t)(row * a.ldx * 2 + 16 * lc), rB);
     }
 }
 
 // Lane-dependent LDS byte offsets used by compute_stage (computed once per kernel).
 struct LaneOffsets {
-    int a;        // A fragment: (q * 16 + r) * 16
-    int m;        // metadata: r * 8 + 2 q (plus the wave's row offset)
+    int a;        // A fragment of block wm0/16: block * 1024 + lane * 16
+    int m;        // metadata of block wm0/16: A_BYTES + block * 128 + lane * 2
     int b[FN];    // B fragment j, first read (t = 0): row part + swizzled column part
 };
 
 __device__ __forceinline__ LaneOffsets lane_offsets(int wm0, int wn0, int lane) {
     const int r = lane & 15, q = lane >> 4;
     LaneOffsets o;
-    o.a = (wm0 >> 4) * 1024 + (q * 16 + r) * 16;
-    o.m = A_BYTES + (wm0 + r) * 8 + 2 * q;
-    // rows read by read t of group q: 8q + 4t' + r/4 (+32 for t >= 2); bits 0-1 and 3 of the row fix
-    // swz(row), so the XOR term depends on the lane only and t/h enter as immediates.
+    o.a = (wm0 >> 4) * 1024 + lane * 16;
+    o.m = A_BYTES + (wm0 >> 4) * 128 + lane * 2;
+    // read t of group q covers rows 8q + 4(t&1) + 32(t>>1) + r/4; row & 3 = (r >> 2) & 3 fixes the
+    // block swizzle for every t, so t only adds immediates
     const int row0 = 8 * q + (r >> 2);
-    const int sw = swz(row0);
+    const int sw = row0 & 3;
 #pragma unroll
     for (int j = 0; j < FN; j++) {
-        const int col = wn0 + 16 * j + 4 * (r & 3);
-        o.b[j] = A_BYTES + META_BYTES + row0 * B_ROW + (((col >> 3) ^ sw) << 4) + 8 * (r & 1);
+        const int col = wn0 + 16 * j + 4 * (r & 3);  // first of the 4 columns this lane points at
+        o.b[j] = A_BYTES + META_BYTES + row0 * B_ROW + (((col >> 5) ^ sw) << 6) + 2 * (col & 31);
     }
     return o;
 }
@@ -147,8 +171,8 @@ __device__ __forceinline__ void compute_stage(const char* smem, f32x4 (&acc)[FM]
 }
 
 template <int CUR, int STAGES>
-__device__ __forceinline__ void step(char* cur, char* nxt, const Args& a, __amdgpu_buffer_rsrc_t rA,
-                                     __amdgpu_buffer_rsrc_t rM, int64_t n0, int s, int S, f32x4 (&acc)[FM][FN],
+__device__ __forceinline__ void step(char* cur, char* nxt, const Args& a, i32x4 rA,
+                                     i32x4 rM, int64_t n0, int s, int S, f32x4 (&acc)[FM][FN],
                                      const LaneOffsets& o, int wave, int lane) {
     if (s + 2 < S) {
         load_stage(nxt, a, rA, rM, n0, s + 2, wave, lane);
@@ -184,8 +208,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int wm0 = (wave >> 1) * WM, wn0 = (wave & 1) * WN;
-    const __amdgpu_buffer_rsrc_t rA = make_rsrc(a.vals + m0 * (a.K / 2), (a.M - m0) * a.K);
-    const __amdgpu_buffer_rsrc_t rM = make_rsrc(a.meta + m0 * (a.K / 8), (a.M - m0) * (a.K / 8));
+    // compressed tiles of this workgroup's first row block onward (rows are padded to 16)
+    const int64_t tiles = a.K / BK, blocks_left = (a.M + 15) / 16 - m0 / 16;
+    const i32x4 rA = make_rsrc(reinterpret_cast<const char*>(a.vals) + (m0 / 16) * tiles * 1024,
+                               blocks_left * tiles * 1024);
+    const i32x4 rM = make_rsrc(a.meta + (m0 / 16) * tiles * 128, blocks_left * tiles * 128);
 
     f32x4 acc[FM][FN];
 #pragma unroll

@@ -10,8 +10,10 @@
 //   C/D (16 x 16 int32): lane holds column r, rows 4q .. 4q+3.
 // Epilogue: y = fl32( fl32(acc) * scale[m] ), a single rounding multiply.
 //
-// Direct kernel: each wave owns a 16 x (16*NF) tile, reads A and the index from global memory and
-// gathers B element by element with bounds checks (any shape and row pitch).
+// The compressed weight is stored in that lane order (16-row x 128-column tiles, see include/sp24.h).
+// Direct kernel: each wave owns a 16 x (16*NF) tile, reads A (1 KB) and the index (256 B) of each
+// tile from global memory and gathers B element by element with bounds checks (any shape and row
+// pitch).
 #include "sp24_device.h"
 #include "sp24_launch.h"
 
@@ -27,29 +29,19 @@ __global__ __launch_bounds__(256) void gemm_i8_direct(const int8_t* __restrict__
     const int64_t m0 = ((int64_t)blockIdx.y * 4 + (threadIdx.x >> 6)) * 16;
     const int64_t n0 = (int64_t)blockIdx.x * 16 * NF;
     if (m0 >= M) return;  // whole wave
-    const int64_t row = m0 + r;
-    const bool row_ok = row < M;
     i32x4 acc[NF];
 #pragma unroll
     for (int f = 0; f < NF; f++) acc[f] = i32x4{0, 0, 0, 0};
 
-    for (int64_t k0 = 0; k0 < K; k0 += 128) {
-        const int64_t kd = k0 + 32 * q;  // first dense column of this lane's A slice
-        uint32_t a[4] = {0u, 0u, 0u, 0u};
-        uint32_t idx = 0x44444444u;
-        if (row_ok && kd < K) {
-            // the row's value bytes start 8-byte aligned and its metadata 2-byte aligned
-            const uint8_t* vp = reinterpret_cast<const uint8_t*>(vals) + row * (K / 2) + kd / 2;
-            const uint8_t* mp = meta + row * (K / 8) + kd / 8;
-            const uint2 lo = *reinterpret_cast<const uint2*>(vp);
-            a[0] = lo.x; a[1] = lo.y;
-            idx = (idx & 0xFFFF0000u) | *reinterpret_cast<const uint16_t*>(mp);
-            if (kd + 16 < K) {  // second half of the 32-column slice
-                const uint2 hi = *reinterpret_cast<const uint2*>(vp + 8);
-                a[2] = hi.x; a[3] = hi.y;
-                idx = (idx & 0x0000FFFFu) | ((uint32_t)*reinterpret_cast<const uint16_t*>(mp + 2) << 16);
-            }
-        }
+    // compressed tiles of this 16-row block: 1 KB of values and 256 B of metadata per 128 dense
+    // columns, in lane order (padded rows/columns hold zeros and canonical metadata)
+    const int64_t tiles_per_row = (K + 127) / 128;
+    const u32x4* vt = reinterpret_cast<const u32x4*>(vals) + (m0 >> 4) * tiles_per_row * 64 + lane;
+    const uint32_t* mt = reinterpret_cast<const uint32_t*>(meta) + (m0 >> 4) * tiles_per_row * 64 + lane;
+    for (int64_t t = 0; t < tiles_per_row; t++) {
+        const int64_t k0 = 128 * t;
+        const u32x4 a = vt[64 * t];
+        const uint32_t idx = mt[64 * t];
         const i32x4 av = {(int)a[0], (int)a[1], (int)a[2], (int)a[3]};
 #pragma unroll
         for (int f = 0; f < NF; f++) {

@@ -3,8 +3,9 @@
 //
 // Both kernels are HBM streams. One thread owns one 16-column chunk of a row (4 groups): it reads
 // the chunk with 16-byte loads, scores and selects in registers, and writes 8 values (one 16-byte
-// store for 16-bit types) plus the chunk's 16 metadata bits (2 bytes). Consecutive threads own
-// consecutive chunks, so a wave reads and writes contiguous runs.
+// store for 16-bit types) plus the chunk's 16 metadata bits (2 bytes) into the tiled compressed
+// layout (16-row tiles in the order of the sparse MFMA operand). Consecutive threads own consecutive
+// chunks of a row, so loads are contiguous runs; each store lands in a 16-byte quarter of a tile.
 //
 // Selection is a knockout over the group: (0 vs 1) and (2 vs 3), then the two winners; the
 // runner-up is the better of the two elements that lost directly to the champion. "a beats b" for
@@ -85,56 +86,68 @@ __device__ __forceinline__ void knockout_top2(const uint32_t k[4], int& lo, int&
     hi = champ < second ? second : champ;
 }
 
+template <int DT> constexpr int esize() { return DT == DT_FP32 ? 4 : (DT == DT_I8 ? 1 : 2); }
+
+// One thread per 16-column chunk c of padded row i (Mp x Kp/16 chunks, Kp/KT tiles per row). Chunks
+// outside the M x K weight write the padding (values 0, metadata nibbles 0x4).
 template <int DT, int VOUT, bool WANDA>
-__global__ __launch_bounds__(256) void prune_compress_kernel(const void* __restrict__ W, int64_t ldw,
-                                                             uint32_t chunks_per_row, uint32_t total_chunks,
-                                                             int64_t K, const float* __restrict__ norms,
+__global__ __launch_bounds__(256) void prune_compress_kernel(const void* __restrict__ W, int64_t ldw, int64_t M,
+                                                             int64_t K, uint32_t chunks_per_row, uint32_t total_chunks,
+                                                             int64_t tiles_per_row, const float* __restrict__ norms,
                                                              void* __restrict__ values, uint8_t* __restrict__ meta) {
     const uint32_t t = blockIdx.x * 256u + threadIdx.x;
     if (t >= total_chunks) return;
     const uint32_t row = t / chunks_per_row, c = t - row * chunks_per_row;
-    constexpr int isz = DT == DT_FP32 ? 4 : (DT == DT_I8 ? 1 : 2);
-    Chunk<DT> x;
-    x.load(reinterpret_cast<const char*>(W) + ((int64_t)row * ldw + 16 * (int64_t)c) * isz);
-
-    float nrm[16];
-    if (WANDA) {
-        const float4* np = reinterpret_cast<const float4*>(norms + 16 * (int64_t)c);
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            float4 v = np[i];
-            nrm[4 * i] = v.x; nrm[4 * i + 1] = v.y; nrm[4 * i + 2] = v.z; nrm[4 * i + 3] = v.w;
-        }
-    }
-    uint32_t mbits = 0;
+    constexpr int isz = esize<DT>(), vsz = esize<VOUT>();
     typename Chunk<DT>::T kept[8];
+    uint32_t mbits = 0x4444u;
+    if (row < M && 16 * (int64_t)c < K) {
+        Chunk<DT> x;
+        x.load(reinterpret_cast<const char*>(W) + ((int64_t)row * ldw + 16 * (int64_t)c) * isz);
+        float nrm[16];
+        if (WANDA) {
+            const float4* np = reinterpret_cast<const float4*>(norms + 16 * (int64_t)c);
 #pragma unroll
-    for (int g = 0; g < 4; g++) {
-        uint32_t key[4];
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            if (WANDA)
-                key[i] = __float_as_uint(__fmul_rn(x.abs_f32(4 * g + i), nrm[4 * g + i])) & 0x7FFFFFFFu;
-            else
-                key[i] = x.mag_key(4 * g + i);
+            for (int i = 0; i < 4; i++) {
+                float4 v = np[i];
+                nrm[4 * i] = v.x; nrm[4 * i + 1] = v.y; nrm[4 * i + 2] = v.z; nrm[4 * i + 3] = v.w;
+            }
         }
-        int lo, hi;
-        knockout_top2(key, lo, hi);
-        mbits |= (uint32_t)(lo | (hi << 2)) << (4 * g);
-        kept[2 * g] = x.e[4 * g + lo];
-        kept[2 * g + 1] = x.e[4 * g + hi];
+        mbits = 0;
+#pragma unroll
+        for (int g = 0; g < 4; g++) {
+            uint32_t key[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                if (WANDA)
+                    key[i] = __float_as_uint(__fmul_rn(x.abs_f32(4 * g + i), nrm[4 * g + i])) & 0x7FFFFFFFu;
+                else
+                    key[i] = x.mag_key(4 * g + i);
+            }
+            int lo, hi;
+            knockout_top2(key, lo, hi);
+            mbits |= (uint32_t)(lo | (hi << 2)) << (4 * g);
+            kept[2 * g] = x.e[4 * g + lo];
+            kept[2 * g + 1] = x.e[4 * g + hi];
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; i++) kept[i] = 0;
     }
-    const int64_t vbase = (int64_t)row * (K / 2) + 8 * (int64_t)c;  // element index in values
-    if (VOUT == DT_FP32) {
-        uint4* o = reinterpret_cast<uint4*>(reinterpret_cast<uint32_t*>(values) + vbase);
-        o[0] = make_uint4(kept[0], kept[1], kept[2], kept[3]);
-        o[1] = make_uint4(kept[4], kept[5], kept[6], kept[7]);
-    } else if (VOUT == DT_I8) {
+    // values: 8 kept values = 8 * vsz bytes at byte 8 * vsz * c of the compressed row
+    char* vbase = reinterpret_cast<char*>(values);
+    const int64_t vb = 8 * vsz * (int64_t)c;
+    if (VOUT == DT_FP32) {  // two whole 16-byte quarters
+        *reinterpret_cast<uint4*>(vbase + tiled_offset<64>(row, vb, tiles_per_row)) =
+            make_uint4(kept[0], kept[1], kept[2], kept[3]);
+        *reinterpret_cast<uint4*>(vbase + tiled_offset<64>(row, vb + 16, tiles_per_row)) =
+            make_uint4(kept[4], kept[5], kept[6], kept[7]);
+    } else if (VOUT == DT_I8) {  // half of a quarter
         uint2 v;
         v.x = (uint32_t)kept[0] | ((uint32_t)kept[1] << 8) | ((uint32_t)kept[2] << 16) | ((uint32_t)kept[3] << 24);
         v.y = (uint32_t)kept[4] | ((uint32_t)kept[5] << 8) | ((uint32_t)kept[6] << 16) | ((uint32_t)kept[7] << 24);
-        *reinterpret_cast<uint2*>(reinterpret_cast<uint8_t*>(values) + vbase) = v;
-    } else {  // 16-bit values: bf16/fp16 bit copies, or fp32 rounded to bf16
+        *reinterpret_cast<uint2*>(vbase + tiled_offset<64>(row, vb, tiles_per_row)) = v;
+    } else {  // 16-bit values: one quarter; bf16/fp16 bit copies, or fp32 rounded to bf16
         uint32_t h[8];
 #pragma unroll
         for (int i = 0; i < 8; i++) {
@@ -143,34 +156,51 @@ __global__ __launch_bounds__(256) void prune_compress_kernel(const void* __restr
             else
                 h[i] = (uint32_t)kept[i];
         }
-        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(values) + vbase) =
+        *reinterpret_cast<uint4*>(vbase + tiled_offset<64>(row, vb, tiles_per_row)) =
             make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
     }
-    *reinterpret_cast<uint16_t*>(meta + (int64_t)row * (K / 8) + 2 * (int64_t)c) = (uint16_t)mbits;
+    // metadata: 2 bytes at byte 2c of the row's metadata; tiles of KT/8 = 16/vsz bytes per row
+    constexpr int TM = 16 / vsz;
+    if (TM >= 8) {  // bf16 (quarter 2 bytes) and int8 (quarter 4 bytes): one 16-bit store
+        *reinterpret_cast<uint16_t*>(meta + tiled_offset<TM>(row, 2 * (int64_t)c, tiles_per_row)) = (uint16_t)mbits;
+    } else {  // fp32: 1-byte quarters
+        meta[tiled_offset<TM>(row, 2 * (int64_t)c, tiles_per_row)] = (uint8_t)(mbits & 0xFF);
+        meta[tiled_offset<TM>(row, 2 * (int64_t)c + 1, tiles_per_row)] = (uint8_t)(mbits >> 8);
+    }
 }
 
+// One thread per 16-column chunk of the M x K weight.
 template <int DT>
 __global__ __launch_bounds__(256) void decompress_kernel(const void* __restrict__ values,
                                                          const uint8_t* __restrict__ meta, uint32_t chunks_per_row,
-                                                         uint32_t total_chunks, int64_t K, void* __restrict__ W,
-                                                         int64_t ldw) {
+                                                         uint32_t total_chunks, int64_t tiles_per_row,
+                                                         void* __restrict__ W, int64_t ldw) {
     const uint32_t t = blockIdx.x * 256u + threadIdx.x;
     if (t >= total_chunks) return;
     const uint32_t row = t / chunks_per_row, c = t - row * chunks_per_row;
-    constexpr int isz = DT == DT_FP32 ? 4 : (DT == DT_I8 ? 1 : 2);
-    const uint32_t mbits = *reinterpret_cast<const uint16_t*>(meta + (int64_t)row * (K / 8) + 2 * (int64_t)c);
-    const char* vp = reinterpret_cast<const char*>(values) + ((int64_t)row * (K / 2) + 8 * (int64_t)c) * isz;
+    constexpr int isz = esize<DT>();
+    constexpr int TM = 16 / isz;
+    const char* vbase = reinterpret_cast<const char*>(values);
+    const int64_t vb = 8 * isz * (int64_t)c;
+    uint32_t mbits;
+    if (TM >= 8) {
+        mbits = *reinterpret_cast<const uint16_t*>(meta + tiled_offset<TM>(row, 2 * (int64_t)c, tiles_per_row));
+    } else {
+        mbits = meta[tiled_offset<TM>(row, 2 * (int64_t)c, tiles_per_row)] |
+                ((uint32_t)meta[tiled_offset<TM>(row, 2 * (int64_t)c + 1, tiles_per_row)] << 8);
+    }
     uint32_t v[8];
     if (isz == 2) {
-        uint4 a = *reinterpret_cast<const uint4*>(vp);
+        uint4 a = *reinterpret_cast<const uint4*>(vbase + tiled_offset<64>(row, vb, tiles_per_row));
         const uint32_t w[4] = {a.x, a.y, a.z, a.w};
 #pragma unroll
         for (int i = 0; i < 8; i++) v[i] = (w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
     } else if (isz == 4) {
-        uint4 a = reinterpret_cast<const uint4*>(vp)[0], b = reinterpret_cast<const uint4*>(vp)[1];
+        uint4 a = *reinterpret_cast<const uint4*>(vbase + tiled_offset<64>(row, vb, tiles_per_row));
+        uint4 b = *reinterpret_cast<const uint4*>(vbase + tiled_offset<64>(row, vb + 16, tiles_per_row));
         v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
     } else {
-        uint2 a = *reinterpret_cast<const uint2*>(vp);
+        uint2 a = *reinterpret_cast<const uint2*>(vbase + tiled_offset<64>(row, vb, tiles_per_row));
 #pragma unroll
         for (int i = 0; i < 8; i++) v[i] = ((i < 4 ? a.x : a.y) >> (8 * (i & 3))) & 0xFFu;
     }
@@ -202,14 +232,24 @@ __global__ __launch_bounds__(256) void decompress_kernel(const void* __restrict_
     }
 }
 
+// Padded sizes of the compressed form (values of `vsz` bytes): Mp, Kp, tiles per row.
+static inline void padded_dims(int64_t M, int64_t K, int vsz, int64_t& Mp, int64_t& Kp, int64_t& tiles) {
+    const int64_t kt = 128 / vsz;
+    Mp = (M + 15) / 16 * 16;
+    Kp = (K + kt - 1) / kt * kt;
+    tiles = Kp / kt;
+}
+
 template <int DT, int VOUT, bool WANDA>
 static hipError_t launch_pc(const void* W, int64_t M, int64_t K, int64_t ldw, const float* norms, void* values,
                             uint8_t* meta, hipStream_t s) {
-    const uint32_t cpr = (uint32_t)(K / 16);
-    const uint32_t total = (uint32_t)(M * (K / 16));
+    int64_t Mp, Kp, tiles;
+    padded_dims(M, K, esize<VOUT>(), Mp, Kp, tiles);
+    const uint32_t cpr = (uint32_t)(Kp / 16);
+    const uint32_t total = (uint32_t)(Mp * (Kp / 16));
     const uint32_t blocks = (total + 255) / 256;
-    hipLaunchKernelGGL((prune_compress_kernel<DT, VOUT, WANDA>), dim3(blocks), dim3(256), 0, s, W, ldw, cpr, total, K,
-                       norms, values, meta);
+    hipLaunchKernelGGL((prune_compress_kernel<DT, VOUT, WANDA>), dim3(blocks), dim3(256), 0, s, W, ldw, M, K, cpr, total,
+                       tiles, norms, values, meta);
     return hipGetLastError();
 }
 
@@ -235,29 +275,27 @@ hipError_t launch_prune_compress(const void* W, int dtype, int64_t M, int64_t K,
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_decompress(const void* values, const uint8_t* meta, int dtype, int64_t M, int64_t K, void* W_out,
-                             int64_t ldw, hipStream_t s) {
+template <int DT>
+static hipError_t launch_dc(const void* values, const uint8_t* meta, int64_t M, int64_t K, void* W_out, int64_t ldw,
+                            hipStream_t s) {
+    int64_t Mp, Kp, tiles;
+    padded_dims(M, K, esize<DT>(), Mp, Kp, tiles);
     const uint32_t cpr = (uint32_t)(K / 16);
     const uint32_t total = (uint32_t)(M * (K / 16));
     const uint32_t blocks = (total + 255) / 256;
+    hipLaunchKernelGGL(decompress_kernel<DT>, dim3(blocks), dim3(256), 0, s, values, meta, cpr, total, tiles, W_out, ldw);
+    return hipGetLastError();
+}
+
+hipError_t launch_decompress(const void* values, const uint8_t* meta, int dtype, int64_t M, int64_t K, void* W_out,
+                             int64_t ldw, hipStream_t s) {
     switch (dtype) {
     case DT_BF16:
-    case DT_FP16:
-        hipLaunchKernelGGL(decompress_kernel<DT_BF16>, dim3(blocks), dim3(256), 0, s, values, meta, cpr, total, K, W_out,
-                           ldw);
-        break;
-    case DT_FP32:
-        hipLaunchKernelGGL(decompress_kernel<DT_FP32>, dim3(blocks), dim3(256), 0, s, values, meta, cpr, total, K, W_out,
-                           ldw);
-        break;
-    case DT_I8:
-        hipLaunchKernelGGL(decompress_kernel<DT_I8>, dim3(blocks), dim3(256), 0, s, values, meta, cpr, total, K, W_out,
-                           ldw);
-        break;
-    default:
-        return hipErrorInvalidValue;
+    case DT_FP16: return launch_dc<DT_BF16>(values, meta, M, K, W_out, ldw, s);
+    case DT_FP32: return launch_dc<DT_FP32>(values, meta, M, K, W_out, ldw, s);
+    case DT_I8: return launch_dc<DT_I8>(values, meta, M, K, W_out, ldw, s);
     }
-    return hipGetLastError();
+    return hipErrorInvalidValue;
 }
 
 }  // namespace sp24

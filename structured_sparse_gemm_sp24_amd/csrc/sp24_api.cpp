@@ -29,6 +29,13 @@ int elem_size(int dt) {
 
 int check_k(int64_t K) { return (K >= 16 && K % 16 == 0) ? SP24_OK : SP24_ERR_SHAPE; }
 
+// Padded dimensions of the compressed form: rows to 16, columns to 128 / value size.
+int64_t padded_m(int64_t M) { return (M + 15) / 16 * 16; }
+int64_t padded_k(int64_t K, int vsz) {
+    const int64_t kt = 128 / vsz;
+    return (K + kt - 1) / kt * kt;
+}
+
 // The current device must be gfx950. Cached per device; the first call asks the runtime.
 int check_device() {
     int dev = -1;
@@ -75,6 +82,20 @@ const char* sp24_status_string(int status) {
     return "unknown sp24 status";
 }
 
+int sp24_compressed_bytes(int64_t M, int64_t K, int val_dtype, int64_t* values_bytes, int64_t* meta_bytes) {
+    if (!values_bytes || !meta_bytes) return SP24_ERR_NULL;
+    if (val_dtype != SP24_BF16 && val_dtype != SP24_FP16 && val_dtype != SP24_FP32 && val_dtype != SP24_I8)
+        return SP24_ERR_DTYPE;
+    if (M < 1) return SP24_ERR_SHAPE;
+    int st = check_k(K);
+    if (st != SP24_OK) return st;
+    const int vsz = elem_size(val_dtype);
+    const int64_t Mp = padded_m(M), Kp = padded_k(K, vsz);
+    *values_bytes = Mp * (Kp / 2) * vsz;
+    *meta_bytes = Mp * (Kp / 8);
+    return SP24_OK;
+}
+
 int sp24_col_norms(const void* X, int64_t K, int64_t N, int64_t ldx, float* norms, void* stream) {
     if (!X || !norms) return SP24_ERR_NULL;
     if (K < 1 || N < 1 || ldx < N) return SP24_ERR_SHAPE;
@@ -102,7 +123,7 @@ int sp24_prune_compress(const void* W, int dtype, int64_t M, int64_t K, int64_t 
     int st = check_k(K);
     if (st != SP24_OK) return st;
     if (ldw < K) return SP24_ERR_SHAPE;
-    if (M * (K / 16) >= kMaxChunks) return SP24_ERR_SHAPE;
+    if (padded_m(M) * (padded_k(K, elem_size(val_dtype)) / 16) >= kMaxChunks) return SP24_ERR_SHAPE;
     const int isz = elem_size(dtype);
     if (!aligned16(W) || !aligned16(values) || !aligned16(meta) || (ldw * isz) % 16 != 0) return SP24_ERR_ALIGN;
     if (norms && !aligned16(norms)) return SP24_ERR_ALIGN;

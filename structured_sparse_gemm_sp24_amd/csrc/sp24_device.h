@@ -31,6 +31,17 @@ __device__ __forceinline__ float f16_to_f32(uint32_t h) {
     return (float)v;
 }
 
+// Compressed layout: byte b of compressed row i, for tiles of T bytes per row (T = 64 for values,
+// KT/8 for metadata, KT = 128 / value size), 16-row tiles stored row block by row block and along K
+// inside a block, each row's tile bytes cut into 4 quarters stored quarter-major.
+template <int T>
+__device__ __forceinline__ int64_t tiled_offset(int64_t i, int64_t b, int64_t tiles_per_row) {
+    constexpr int Q = T / 4;
+    const int64_t t = b / T;
+    const int rem = (int)(b - t * T);
+    return (((i >> 4) * tiles_per_row + t) * 4 + rem / Q) * (16 * Q) + (i & 15) * Q + rem % Q;
+}
+
 // Wave-level sum of a double (64 lanes) by butterfly shuffles.
 __device__ __forceinline__ double wave_sum_f64(double v) {
 #pragma unroll

@@ -128,6 +128,26 @@ def test_gemm_i8_validation(lib, args, expect):
     assert lib.sp24_gemm_i8(*args) == expect
 
 
+def test_compressed_bytes(lib):
+    vb, mb = ctypes.c_int64(), ctypes.c_int64()
+    # rows padded to 16, columns to 128 / value size
+    for M, K, dt, want in [(3072, 768, BF16, (3072 * 384 * 2, 3072 * 96)), (1, 16, BF16, (16 * 32 * 2, 16 * 8)),
+                           (17, 48, I8, (32 * 64, 32 * 16)), (5, 16, FP32, (16 * 16 * 4, 16 * 4))]:
+        assert lib.sp24_compressed_bytes(M, K, dt, ctypes.byref(vb), ctypes.byref(mb)) == sp.SP24_OK
+        assert (vb.value, mb.value) == want
+    assert lib.sp24_compressed_bytes(4, 20, BF16, ctypes.byref(vb), ctypes.byref(mb)) == sp.SP24_ERR_SHAPE
+    assert lib.sp24_compressed_bytes(4, 16, I32, ctypes.byref(vb), ctypes.byref(mb)) == sp.SP24_ERR_DTYPE
+    assert lib.sp24_compressed_bytes(4, 16, BF16, None, ctypes.byref(mb)) == sp.SP24_ERR_NULL
+
+
+def test_compressed_bytes_matches_oracle(lib):
+    import oracle
+    for M, K in [(1, 16), (37, 208), (3072, 768)]:
+        for dt in (BF16, FP32, I8):
+            assert sp.sp24_compressed_bytes(M, K, {BF16: torch.bfloat16, FP32: torch.float32, I8: torch.int8}[dt]) == \
+                oracle.compressed_bytes(M, K, dt)
+
+
 @pytest.mark.skipif(torch.cuda.device_count() > 0, reason="only meaningful where no GPU is visible")
 def test_valid_arguments_without_a_device_report_device_error(lib):
     # all host checks pass, then the device check fails: nothing is launched

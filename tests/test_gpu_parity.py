@@ -91,6 +91,7 @@ def test_prune_compress_bit_exact(dt, score, M, K, ld):
     vals, meta = sp.sp24_prune_compress(Wd, score=osc, norms=dev(norms) if norms is not None else None,
                                         val_dtype=val_dtype)
     torch.cuda.synchronize()
+    # whole buffers, padding included, in the tiled layout
     assert np.array_equal(host_bits(meta), ref_m)
     assert np.array_equal(host_bits(vals).view(ref_v.dtype), ref_v)
 
@@ -105,19 +106,19 @@ def test_decompress_bit_exact_with_row_pitch(dt):
     Wf = weights_f32(99, M, K)
     W, odt, kind = as_dtype(Wf, dt)
     v, m = oracle.prune_compress(W, odt)
-    ref = oracle.decompress(v, m, odt)
+    ref = oracle.decompress(v, m, odt, M, K)
     say(f"decompress dt={dt}")
     vd = dev(v, kind)
     raw = torch.full((M * ld * _SIZE[dt],), 0xFF, dtype=torch.uint8, device="cuda")
     out_buf = raw.view(_TORCH_DT[dt]).view(M, ld)
-    sp.sp24_decompress(vd, dev(m), out=out_buf[:, :K])
+    sp.sp24_decompress(vd, dev(m), M, K, out=out_buf[:, :K])
     torch.cuda.synchronize()
     got = host_bits(out_buf)
     assert np.array_equal(got[:, :K].view(ref.dtype), ref)
     assert np.all(host_bits(out_buf[:, K:].contiguous()).view(np.uint8) == 0xFF)  # padding untouched
     # the GPU pair round-trips: decompress(compress(W)) == prune(W)
     vals, meta = sp.sp24_prune_compress(dev(W, kind))
-    assert np.array_equal(host_bits(sp.sp24_decompress(vals, meta)).view(ref.dtype), ref)
+    assert np.array_equal(host_bits(sp.sp24_decompress(vals, meta, M, K)).view(ref.dtype), ref)
 
 
 # ----------------------------------------------------------------------------- column norms
@@ -178,9 +179,9 @@ def _gemm_inputs(M, K, N, seed):
     return W, X, v, m
 
 
-def _check_bf16_gemm(v, m, X, Yf32, Ybf16, rows=None):
-    Y64 = oracle.gemm_bf16(v, m, X, rows=rows)
-    dense = bf16_to_f64(oracle.decompress(v, m, oracle.BF16))
+def _check_bf16_gemm(v, m, M, X, Yf32, Ybf16, rows=None):
+    Y64 = oracle.gemm_bf16(v, m, X, M, rows=rows)
+    dense = bf16_to_f64(oracle.decompress(v, m, oracle.BF16, M, X.shape[0]))
     if rows is not None:
         dense = dense[rows]
     K = dense.shape[1]
@@ -205,12 +206,12 @@ def test_gemm_bf16_parity(M, K, N, ldx, ldy):
     vd, md = dev(v, "bf16"), dev(m)
     Yf = torch.full((M, ldy), 12345.0, dtype=torch.float32, device="cuda")
     Yb = torch.full((M, ldy), 12345.0, dtype=torch.bfloat16, device="cuda")
-    sp.sp24_gemm_bf16(vd, md, Xd, out=Yf[:, :N])
-    sp.sp24_gemm_bf16(vd, md, Xd, out=Yb[:, :N])
+    sp.sp24_gemm_bf16(vd, md, M, Xd, out=Yf[:, :N])
+    sp.sp24_gemm_bf16(vd, md, M, Xd, out=Yb[:, :N])
     torch.cuda.synchronize()
     yf, yb = host_bits(Yf), host_bits(Yb)
     assert np.all(yf[:, N:] == 12345.0)  # nothing written past N (X's padding there is NaN)
-    _check_bf16_gemm(v, m, X, yf[:, :N], yb[:, :N])
+    _check_bf16_gemm(v, m, M, X, yf[:, :N], yb[:, :N])
 
 
 def test_gemm_bf16_identity_equals_decompress():
@@ -219,8 +220,8 @@ def test_gemm_bf16_identity_equals_decompress():
     v, m = oracle.prune_compress(W, oracle.BF16)
     eye = synth.f32_to_bf16_bits(np.eye(K, dtype=np.float32))
     say("gemm_bf16 identity")
-    Y = host_bits(sp.sp24_gemm_bf16(dev(v, "bf16"), dev(m), dev(eye, "bf16")))
-    dense = bf16_to_f64(oracle.decompress(v, m, oracle.BF16)).astype(np.float32)
+    Y = host_bits(sp.sp24_gemm_bf16(dev(v, "bf16"), dev(m), M, dev(eye, "bf16")))
+    dense = bf16_to_f64(oracle.decompress(v, m, oracle.BF16, M, K)).astype(np.float32)
     assert np.array_equal(Y, dense)
 
 
@@ -230,12 +231,12 @@ def test_gemm_bf16_orin7_gather_example():
     W[0, 1], W[0, 3] = -0.5, 0.2
     Wb = synth.f32_to_bf16_bits(W)
     v, m = oracle.prune_compress(Wb, oracle.BF16)
-    assert m[0, 0] & 0xF == 0xD
+    assert m[0] & 0xF == 0xD  # row 0, group 0 sits at byte 0 of the metadata
     X = synth.f32_to_bf16_bits(np.arange(1, 17, dtype=np.float32).reshape(16, 1))
     say("gemm_bf16 gather example")
-    Y = host_bits(sp.sp24_gemm_bf16(dev(v, "bf16"), dev(m), dev(X, "bf16")))
+    Y = host_bits(sp.sp24_gemm_bf16(dev(v, "bf16"), dev(m), 1, dev(X, "bf16")))
     x = bf16_to_f64(X[:, 0])
-    assert Y[0, 0] == np.float32(bf16_to_f64(v[0, 0]) * x[1] + bf16_to_f64(v[0, 1]) * x[3])
+    assert Y[0, 0] == np.float32(bf16_to_f64(v[0]) * x[1] + bf16_to_f64(v[1]) * x[3])
 
 
 # ----------------------------------------------------------------------------- sparse GEMM, int8
@@ -251,10 +252,10 @@ def test_gemm_i8_bit_exact(M, K, N, ldx):
     X = rng.integers(-128, 128, size=(K, N), dtype=np.int8)
     scale = (rng.random(M) * 1e-3 + 1e-5).astype(np.float32)
     v, m = oracle.prune_compress(W, oracle.I8)
-    acc, Y = oracle.gemm_i8(v, m, X, scale)
+    acc, Y = oracle.gemm_i8(v, m, X, M, scale)
     say(f"gemm_i8 M={M} K={K} N={N} ldx={ldx}")
     vd, md, Xd = dev(v), dev(m), dev(padded(X, ldx))[:, :N]
-    got_acc = host_bits(sp.sp24_gemm_i8(vd, md, Xd))
-    got_y = host_bits(sp.sp24_gemm_i8(vd, md, Xd, scale=dev(scale)))
+    got_acc = host_bits(sp.sp24_gemm_i8(vd, md, M, Xd))
+    got_y = host_bits(sp.sp24_gemm_i8(vd, md, M, Xd, scale=dev(scale)))
     assert np.array_equal(got_acc.astype(np.int64), acc)
     assert np.array_equal(got_y.view(np.uint32), Y.view(np.uint32))

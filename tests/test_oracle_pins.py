@@ -14,6 +14,19 @@ import torch
 import oracle
 from structured_sparse_gemm_sp24_amd import synth
 from tests.conftest import read_golden
+from tests.layout_ref import padding_ok, to_row_major
+
+ESIZE = {oracle.BF16: 2, oracle.FP16: 2, oracle.FP32: 4, oracle.I8: 1}
+
+
+def compress_rm(W, dt, score=oracle.MAGNITUDE, norms=None, val_dtype=None):
+    """Oracle compression viewed row-major: (values M x K/2, meta M x K/8, flat values, flat meta)."""
+    vdt = dt if val_dtype is None else val_dtype
+    v, m = oracle.prune_compress(W, dt, score, norms, val_dtype)
+    M, K = W.shape
+    assert padding_ok(v, m, M, K, ESIZE[vdt])
+    vr, mr = to_row_major(v, m, M, K, ESIZE[vdt])
+    return vr, mr, v, m
 
 # ----------------------------------------------------------------- independent helpers
 
@@ -63,44 +76,47 @@ def f16_bits(vals):
 def test_orin7_q1_exercise_fp16():
     g = read_golden("orin7_q1_exercise.txt")
     w = np.array([float(x) for x in g["weights"].split()])
-    W = f16_bits(w).reshape(1, 8)
-    vals, meta = oracle.prune_compress(W, oracle.FP16)
-    assert [f"{v:04X}" for v in vals[0]] == g["values_fp16_hex"].split()
-    assert meta.tolist() == [[int(g["meta_hex"], 16)]]
+    # the page's slice is 8 weights; the library works on rows of a multiple of 16, so the slice is
+    # followed by 8 zero weights (their group picks positions 0 and 1, values +0)
+    W = np.concatenate([f16_bits(w), np.zeros(8, np.uint16)]).reshape(1, 16)
+    vals, meta, _, _ = compress_rm(W, oracle.FP16)
+    assert [f"{v:04X}" for v in vals[0, :4]] == g["values_fp16_hex"].split()
+    assert meta[0, 0] == int(g["meta_hex"], 16)
     pruned = np.array([float(x) for x in g["pruned"].split()])
-    assert np.array_equal(oracle.decompress(vals, meta, oracle.FP16), f16_bits(pruned).reshape(1, 8))
-    # storage: every kept value is 16 bits, every group 4 bits of metadata
-    stored = vals.size * 16 + meta.size * 8
-    assert stored == int(g["stored_bits"]) and W.size * 16 == int(g["dense_bits"])
+    dense = oracle.decompress(*oracle.prune_compress(W, oracle.FP16), oracle.FP16, 1, 16)
+    assert np.array_equal(dense[0, :8], f16_bits(pruned))
+    # storage of the slice: every kept value is 16 bits, every group 4 bits of metadata
+    stored = vals[0, :4].size * 16 + 1 * 8
+    assert stored == int(g["stored_bits"]) and w.size * 16 == int(g["dense_bits"])
     pos = [tuple(int(c) for c in p.split(",")) for p in g["kept_positions"].split()]
-    nib = meta_nibbles(meta, 8)[0]
+    nib = meta_nibbles(meta, 16)[0, :2]
     assert [(n & 3, n >> 2) for n in nib] == pos
 
 
 @pytest.mark.parametrize("dt", [oracle.BF16, oracle.FP32])
 def test_orin7_q1_exercise_other_dtypes(dt):
     g = read_golden("orin7_q1_exercise.txt")
-    w = np.array([float(x) for x in g["weights"].split()], dtype=np.float32)
-    W = synth.f32_to_bf16_bits(w).reshape(1, 8) if dt == oracle.BF16 else w.reshape(1, 8)
-    _, meta = oracle.prune_compress(W, dt)
-    assert meta.tolist() == [[int(g["meta_hex"], 16)]]
+    w = np.array([float(x) for x in g["weights"].split()] + [0] * 8, dtype=np.float32)
+    W = synth.f32_to_bf16_bits(w).reshape(1, 16) if dt == oracle.BF16 else w.reshape(1, 16)
+    _, meta, _, _ = compress_rm(W, dt)
+    assert meta[0, 0] == int(g["meta_hex"], 16)
 
 
 def test_orin7_hw_flow_encoding_and_gather():
     g = read_golden("orin7_hw_flow.txt")
-    pre = np.array([float(x) for x in g["prepruned"].split()] + [0, 0, 0, 0], dtype=np.float32)
-    W = synth.f32_to_bf16_bits(pre).reshape(1, 8)
-    vals, meta = oracle.prune_compress(W, oracle.BF16)
+    pre = np.array([float(x) for x in g["prepruned"].split()] + [0] * 12, dtype=np.float32)
+    W = synth.f32_to_bf16_bits(pre).reshape(1, 16)
+    vals, meta, vflat, mflat = compress_rm(W, oracle.BF16)
     page_vals = np.array([float(x) for x in g["values"].split()], dtype=np.float32)
     assert np.array_equal(vals[0, :2], synth.f32_to_bf16_bits(page_vals))  # the page's values, in bf16
     bits = g["meta_bits"].split()
-    nib = meta_nibbles(meta, 8)[0, 0]
+    nib = meta_nibbles(meta, 16)[0, 0]
     assert (f"{nib & 3:02b}", f"{nib >> 2:02b}") == tuple(bits)
     assert nib == int(g["nibble_hex"], 16)
     # gather semantics: result = -0.5 * x1 + 0.2 * x3 for activations x0..x3
-    x = np.array([float(v) for v in g["activations"].split()] + [1, 1, 1, 1], dtype=np.float32)
-    X = synth.f32_to_bf16_bits(x).reshape(8, 1)
-    Y = oracle.gemm_bf16(vals, meta, X)
+    x = np.array([float(v) for v in g["activations"].split()] + [1] * 12, dtype=np.float32)
+    X = synth.f32_to_bf16_bits(x).reshape(16, 1)
+    Y = oracle.gemm_bf16(vflat, mflat, X, 1)
     v = synth.bf16_bits_to_f32(vals[0, :2]).astype(np.float64)
     xs = synth.bf16_bits_to_f32(X[:, 0]).astype(np.float64)
     assert Y[0, 0] == v[0] * xs[1] + v[1] * xs[3]
@@ -109,9 +125,9 @@ def test_orin7_hw_flow_encoding_and_gather():
 
 def test_orin7_rule_beats_illustration():
     g = read_golden("orin7_hw_flow.txt")
-    w = np.array([float(x) for x in g["rule_example"].split()] + [0, 0, 0, 0], dtype=np.float32)
-    vals, meta = oracle.prune_compress(w.reshape(1, 8), oracle.FP32)
-    nib = meta_nibbles(meta, 8)[0, 0]
+    w = np.array([float(x) for x in g["rule_example"].split()] + [0] * 12, dtype=np.float32)
+    vals, meta, _, _ = compress_rm(w.reshape(1, 16), oracle.FP32)
+    nib = meta_nibbles(meta, 16)[0, 0]
     assert (nib & 3, nib >> 2) == tuple(int(c) for c in g["rule_kept_positions"].split(","))
     assert vals[0, :2].tolist() == [np.float32(float(x)) for x in g["rule_values"].split()]
 
@@ -126,14 +142,14 @@ def test_bruteforce_every_group_over_small_alphabet():
     groups = np.array(list(itertools.product(range(6), repeat=4)))
     W = alphabet[groups].reshape(1, -1)
     K = W.shape[1]
-    vals, meta = oracle.prune_compress(W, oracle.FP32)
+    vals, meta, vflat, mflat = compress_rm(W, oracle.FP32)
     nib = meta_nibbles(meta, K)[0]
     for gi, gidx in enumerate(groups):
         a, b = top2_by_pairs(np.abs(alphabet[gidx]).tolist())
         assert (nib[gi] & 3, nib[gi] >> 2) == (a, b), (gi, alphabet[gidx])
         assert vals[0, 2 * gi].view(np.uint32) == alphabet[gidx[a]].view(np.uint32)
         assert vals[0, 2 * gi + 1].view(np.uint32) == alphabet[gidx[b]].view(np.uint32)
-    dense = oracle.decompress(vals, meta, oracle.FP32)
+    dense = oracle.decompress(vflat, mflat, oracle.FP32, 1, K)
     pos = np.array([[n & 3, n >> 2] for n in nib])
     ref = dense_from_positions(W, pos)
     assert np.array_equal(dense.view(np.uint32), ref.view(np.uint32))
@@ -143,12 +159,12 @@ def test_bruteforce_int8_heavy_ties():
     rng = np.random.default_rng(7)
     alphabet = np.array([-128, -127, -3, -1, 0, 1, 3, 127], dtype=np.int8)
     W = alphabet[rng.integers(0, len(alphabet), size=(64, 256))]
-    vals, meta = oracle.prune_compress(W, oracle.I8)
+    vals, meta, vflat, mflat = compress_rm(W, oracle.I8)
     key = np.abs(W.astype(np.int32))  # |-128| = 128
     pos = top2_by_sort(key.reshape(64, -1))
     nib = meta_nibbles(meta, 256).reshape(-1)
     assert np.array_equal(nib & 3, pos[:, 0]) and np.array_equal(nib >> 2, pos[:, 1])
-    assert np.array_equal(oracle.decompress(vals, meta, oracle.I8), dense_from_positions(W, pos))
+    assert np.array_equal(oracle.decompress(vflat, mflat, oracle.I8, 64, 256), dense_from_positions(W, pos))
 
 
 # ----------------------------------------------------------------- invariants on random data
@@ -166,12 +182,12 @@ def test_invariants_random(dt):
         Wd = W.view(np.float16).astype(np.float32)
     else:
         W, Wd = Wf, Wf
-    vals, meta = oracle.prune_compress(W, dt)
-    assert oracle.meta_bad_nibbles(meta, K) == 0
+    vals, meta, vflat, mflat = compress_rm(W, dt)
+    assert oracle.meta_bad_nibbles(mflat, M, K, dt) == 0
     pos = top2_by_sort(np.abs(Wd))
     nib = meta_nibbles(meta, K).reshape(-1)
     assert np.array_equal(nib & 3, pos[:, 0]) and np.array_equal(nib >> 2, pos[:, 1])
-    dense = oracle.decompress(vals, meta, dt)
+    dense = oracle.decompress(vflat, mflat, dt, M, K)
     ref = dense_from_positions(W, pos)
     assert np.array_equal(dense, ref)  # decompress(compress(W)) == prune(W), bit-exact
     # min kept magnitude >= max dropped magnitude in every group; exactly two non-zeros per group
@@ -183,14 +199,14 @@ def test_invariants_random(dt):
     assert np.all(np.count_nonzero(dd, axis=1) == 2)
     # idempotent: pruning the pruned matrix changes nothing
     v2, m2 = oracle.prune_compress(dense, dt)
-    assert np.array_equal(oracle.decompress(v2, m2, dt), dense)
+    assert np.array_equal(oracle.decompress(v2, m2, dt, M, K), dense)
 
 
 def test_fp32_input_bf16_values_round_to_nearest_even():
     rng = np.random.default_rng(5)
     W = rng.standard_normal((16, 64)).astype(np.float32)
-    vals32, meta32 = oracle.prune_compress(W, oracle.FP32)
-    vals16, meta16 = oracle.prune_compress(W, oracle.FP32, val_dtype=oracle.BF16)
+    vals32, meta32, _, _ = compress_rm(W, oracle.FP32)
+    vals16, meta16, _, _ = compress_rm(W, oracle.FP32, val_dtype=oracle.BF16)
     assert np.array_equal(meta32, meta16)
     assert np.array_equal(vals16, synth.f32_to_bf16_bits(vals32))
 
@@ -224,13 +240,13 @@ def test_fp16_decoding_every_pattern_vs_numpy():
 def test_wanda_hand_example():
     # |w| = 1 2 3 4 with input-channel norms 10 1 1 1 -> scores 10 2 3 4 -> keep positions 0 and 3;
     # magnitude alone would keep 2 and 3.
-    w = np.array([1, 2, 3, 4, -4, 3, 2, 1], dtype=np.float32)
-    norms = np.array([10, 1, 1, 1, 0.25, 1, 8, 1], dtype=np.float32)  # group 1 scores 1 3 16 1 -> keep 1, 2
-    _, meta = oracle.prune_compress(w.reshape(1, 8), oracle.FP32, oracle.WANDA, norms)
-    nib = meta_nibbles(meta, 8)[0]
+    w = np.array([1, 2, 3, 4, -4, 3, 2, 1] + [0] * 8, dtype=np.float32)
+    norms = np.array([10, 1, 1, 1, 0.25, 1, 8, 1] + [1] * 8, dtype=np.float32)  # group 1: 1 3 16 1 -> 1, 2
+    _, meta, _, _ = compress_rm(w.reshape(1, 16), oracle.FP32, oracle.WANDA, norms)
+    nib = meta_nibbles(meta, 16)[0, :2]
     assert [(n & 3, n >> 2) for n in nib] == [(0, 3), (1, 2)]
-    _, meta_m = oracle.prune_compress(w.reshape(1, 8), oracle.FP32)
-    assert [(n & 3, n >> 2) for n in meta_nibbles(meta_m, 8)[0]] == [(2, 3), (0, 1)]
+    _, meta_m, _, _ = compress_rm(w.reshape(1, 16), oracle.FP32)
+    assert [(n & 3, n >> 2) for n in meta_nibbles(meta_m, 16)[0, :2]] == [(2, 3), (0, 1)]
 
 
 @pytest.mark.parametrize("p", [0, 3, -5])
@@ -249,7 +265,7 @@ def test_wanda_vs_sorted_float32_scores():
     W = synth.f32_to_bf16_bits((rng.standard_normal((M, K)) * 0.02).astype(np.float32))
     norms = (np.exp(rng.standard_normal(K)) * 30).astype(np.float32)
     norms[::7] = norms[1::7][: len(norms[::7])]  # some repeated norms -> more ties
-    vals, meta = oracle.prune_compress(W, oracle.BF16, oracle.WANDA, norms)
+    vals, meta, _, _ = compress_rm(W, oracle.BF16, oracle.WANDA, norms)
     s = np.abs(synth.bf16_bits_to_f32(W)) * norms[None, :]  # float32 * float32 in numpy: one rounding
     assert s.dtype == np.float32
     pos = top2_by_sort(s)
@@ -259,9 +275,11 @@ def test_wanda_vs_sorted_float32_scores():
 
 def test_wanda_rejects_int8_and_missing_norms():
     with pytest.raises(oracle.OracleError):
-        oracle.prune_compress(np.zeros((1, 8), np.int8), oracle.I8, oracle.WANDA, np.ones(8, np.float32))
+        oracle.prune_compress(np.zeros((1, 16), np.int8), oracle.I8, oracle.WANDA, np.ones(16, np.float32))
     with pytest.raises(oracle.OracleError):
-        oracle.prune_compress(np.zeros((1, 8), np.float32), oracle.FP32, oracle.WANDA, None)
+        oracle.prune_compress(np.zeros((1, 16), np.float32), oracle.FP32, oracle.WANDA, None)
+    with pytest.raises(oracle.OracleError):
+        oracle.prune_compress(np.zeros((1, 8), np.float32), oracle.FP32)  # K not a multiple of 16
 
 
 # ----------------------------------------------------------------- column norms
@@ -297,25 +315,25 @@ def _rand_pruned(seed, M, K, dt=oracle.BF16):
     return W, vals, meta
 
 
-@pytest.mark.parametrize("M,K,N", [(16, 16, 1), (37, 64, 29), (64, 48, 64), (5, 128, 3)])
+@pytest.mark.parametrize("M,K,N", [(16, 16, 1), (37, 64, 29), (64, 48, 64), (5, 128, 3), (40, 208, 7)])
 def test_gemm_bf16_vs_numpy_matmul(M, K, N):
     W, vals, meta = _rand_pruned(M * 1000 + K + N, M, K)
     X = synth.normal_bf16(N + 17, (K, N))
     pos = top2_by_sort(np.abs(synth.bf16_bits_to_f32(W)))
     Wp = synth.bf16_bits_to_f32(dense_from_positions(W, pos)).astype(np.float64)
     ref = Wp @ synth.bf16_bits_to_f32(X).astype(np.float64)
-    Y = oracle.gemm_bf16(vals, meta, X)
+    Y = oracle.gemm_bf16(vals, meta, X, M)
     np.testing.assert_allclose(Y, ref, rtol=1e-12, atol=1e-12)
     rows = np.array([M - 1, 0, M // 2])
-    assert np.array_equal(oracle.gemm_bf16(vals, meta, X, rows=rows), Y[rows])
+    assert np.array_equal(oracle.gemm_bf16(vals, meta, X, M, rows=rows), Y[rows])
 
 
 def test_gemm_bf16_identity_equals_decompress():
     M, K = 24, 64
     W, vals, meta = _rand_pruned(4, M, K)
     eye = synth.f32_to_bf16_bits(np.eye(K, dtype=np.float32))
-    Y = oracle.gemm_bf16(vals, meta, eye)
-    dense = synth.bf16_bits_to_f32(oracle.decompress(vals, meta, oracle.BF16)).astype(np.float64)
+    Y = oracle.gemm_bf16(vals, meta, eye, M)
+    dense = synth.bf16_bits_to_f32(oracle.decompress(vals, meta, oracle.BF16, M, K)).astype(np.float64)
     assert np.array_equal(Y, dense)
 
 
@@ -326,8 +344,8 @@ def test_gemm_bf16_one_hot_columns_select_columns():
     X = np.zeros((K, len(cols)), np.float32)
     for j, c in enumerate(cols):
         X[c, j] = 1.0
-    Y = oracle.gemm_bf16(vals, meta, synth.f32_to_bf16_bits(X))
-    dense = synth.bf16_bits_to_f32(oracle.decompress(vals, meta, oracle.BF16)).astype(np.float64)
+    Y = oracle.gemm_bf16(vals, meta, synth.f32_to_bf16_bits(X), M)
+    dense = synth.bf16_bits_to_f32(oracle.decompress(vals, meta, oracle.BF16, M, K)).astype(np.float64)
     assert np.array_equal(Y, dense[:, cols])
 
 
@@ -341,10 +359,10 @@ def test_gemm_i8_vs_numpy_integer_matmul_and_dequant():
     Wp = dense_from_positions(W, pos).astype(np.int64)
     ref = Wp @ X.astype(np.int64)
     scale = (rng.random(M) * 1e-3).astype(np.float32)
-    acc, Y = oracle.gemm_i8(vals, meta, X, scale)
+    acc, Y = oracle.gemm_i8(vals, meta, X, M, scale)
     assert np.array_equal(acc, ref)
     assert np.array_equal(Y, ref.astype(np.int32).astype(np.float32) * scale[:, None])
-    acc2, Y2 = oracle.gemm_i8(vals, meta, X)
+    acc2, Y2 = oracle.gemm_i8(vals, meta, X, M)
     assert Y2 is None and np.array_equal(acc2, ref)
 
 
@@ -354,16 +372,18 @@ def test_gemm_i8_overflow_is_reported():
     X = np.full((K, 1), -128, np.int8)
     vals, meta = oracle.prune_compress(W, oracle.I8)
     with pytest.raises(oracle.OracleError):
-        oracle.gemm_i8(vals, meta, X)
+        oracle.gemm_i8(vals, meta, X, 1)
 
 
 def test_noncanonical_metadata_is_rejected():
-    vals = np.zeros((1, 4), np.uint16)
+    vals, meta = oracle.prune_compress(np.ones((3, 16), np.uint16), oracle.BF16)
     for bad in (0x00, 0x5, 0x1, 0x6, 0xF):  # i0 == i1 or i0 > i1
-        meta = np.array([[bad | (0x4 << 4)]], np.uint8)
-        assert oracle.meta_bad_nibbles(meta, 8) == 1
+        m = meta.copy()
+        off = oracle.meta_offset(2, 1, 16, oracle.BF16)  # row 2, groups 2 and 3
+        m[off] = bad | (0x4 << 4)
+        assert oracle.meta_bad_nibbles(m, 3, 16, oracle.BF16) == 1
         with pytest.raises(oracle.OracleError):
-            oracle.decompress(vals, meta, oracle.BF16)
+            oracle.decompress(vals, m, oracle.BF16, 3, 16)
 
 
 # ----------------------------------------------------------------- int8 preparation (caller side)
@@ -372,7 +392,7 @@ def test_noncanonical_metadata_is_rejected():
 def test_int8_row_scale_covers_9999_and_pruned_equals_unpruned():
     W = synth.normal_f32(21, (64, 768), 0.02)
     vals, meta = oracle.prune_compress(W, oracle.FP32)
-    Wp = oracle.decompress(vals, meta, oracle.FP32)
+    Wp = oracle.decompress(vals, meta, oracle.FP32, *W.shape)
     q, s = synth.quantize_rows(Wp)
     q0, s0 = synth.quantize_rows(W)
     assert np.array_equal(s, s0)  # the 0.9999 quantile of 768 values sits between the top two
@@ -388,4 +408,37 @@ def test_int8_row_scale_covers_9999_and_pruned_equals_unpruned():
     assert synth.quantize_sym(np.array([0.5, 1.5, 2.5, -0.5]), np.float32(1.0)).tolist() == [0, 2, 2, 0]
     # quantizing the pruned matrix and re-pruning by |q| keeps the dense int8 matrix unchanged
     v8, m8 = oracle.prune_compress(q, oracle.I8)
-    assert np.array_equal(oracle.decompress(v8, m8, oracle.I8), q)
+    assert np.array_equal(oracle.decompress(v8, m8, oracle.I8, *q.shape), q)
+
+
+# ----------------------------------------------------------------- compressed layout
+
+
+@pytest.mark.parametrize("dt", [oracle.BF16, oracle.FP32, oracle.I8])
+@pytest.mark.parametrize("M,K", [(1, 16), (16, 64), (37, 208), (48, 384)])
+def test_layout_offsets_match_the_stated_layout(dt, M, K):
+    from tests.layout_ref import _perm, padded_shape
+    e = ESIZE[dt]
+    Mp, Kp = padded_shape(M, K, e)
+    vb, mb = oracle.compressed_bytes(M, K, dt)
+    assert (vb, mb) == (Mp * Kp // 2 * e, Mp * Kp // 8)
+    pv = _perm(Mp, Kp // 2 * e, 64)
+    pm = _perm(Mp, Kp // 8, 16 // e)
+    assert sorted(pv.ravel().tolist()) == list(range(vb))  # a permutation of the buffer
+    for i in sorted({0, M - 1, Mp - 1, min(17, Mp - 1)}):
+        for b in sorted({0, 15, 16, 63, 64, Kp // 2 * e - 1} & set(range(Kp // 2 * e))):
+            assert oracle.values_offset(i, b, K, dt) == pv[i, b]
+        for b in sorted({0, 1, 3, Kp // 8 - 1} & set(range(Kp // 8))):
+            assert oracle.meta_offset(i, b, K, dt) == pm[i, b]
+
+
+def test_layout_one_tile_is_the_smfmac_operand_order():
+    # a 16 x 64 bf16 weight is one tile: lane l = 16 q + r of v_smfmac_f32_16x16x64_bf16 holds the
+    # 8 kept values of row r, dense columns [16 q, 16 q + 16), at bytes [16 l, 16 l + 16)
+    W = synth.normal_bf16(3, (16, 64))
+    vflat, mflat = oracle.prune_compress(W, oracle.BF16)
+    vr, mr = to_row_major(vflat, mflat, 16, 64, 2)
+    for lane in range(64):
+        q, r = lane // 16, lane % 16
+        assert np.array_equal(vflat[8 * lane: 8 * lane + 8], vr[r, 8 * q: 8 * q + 8])
+        assert mflat[2 * lane: 2 * lane + 2].tolist() == mr[r, 2 * q: 2 * q + 2].tolist()
