@@ -52,22 +52,18 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, int64_t bytes) {
     return r;
 }
 
-__device__ __forceinline__ uint32_t lds_addr(const char* p) {
-    return (uint32_t)(size_t)(__attribute__((address_space(3))) const char*)p;
-}
 
 // Buffer loads with LDS destination: lane i's bytes land at lds + i * width. Issued from inline asm
 // so the compiler adds no waits of its own for them; the kernel orders them with explicit
 // s_waitcnt vmcnt + s_barrier. They write no VGPRs.
-__device__ __forceinline__ void dma16(uint32_t lds, uint32_t voff, i32x4 rsrc) {
-    lds = __builtin_amdgcn_readfirstlane(lds);  // wave-uniform (it depends on the wave index only)
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                 :: "s"(lds), "v"(voff), "s"(rsrc) : "memory");
+// `lds` and `soff` are wave-uniform (SGPRs); `voff` is the per-lane part of the byte offset.
+__device__ __forceinline__ void dma16(uint32_t lds, uint32_t voff, uint32_t soff, i32x4 rsrc) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
 }
-__device__ __forceinline__ void dma4(uint32_t lds, uint32_t voff, i32x4 rsrc) {
-    lds = __builtin_amdgcn_readfirstlane(lds);
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
-                 :: "s"(lds), "v"(voff), "s"(rsrc) : "memory");
+__device__ __forceinline__ void dma4(uint32_t lds, uint32_t voff, uint32_t soff, i32x4 rsrc) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+                 :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
 }
 
 template <int N>
@@ -84,38 +80,57 @@ struct Args {
     int64_t M, K, N, ldx, ldy;
     int tilesM, tilesN;
     int out_fp32;
+    int y_vec;  // Y base and row pitch allow 16-byte stores
 };
 
-// Issue this wave's share of the loads of stage `s` into `smem`. rA / rM cover the compressed
-// tiles of this workgroup's 16 row blocks (tile (b, s) of block b at (b * tiles + s) * 1 KB of
-// values and * 128 B of metadata); loads past the padded rows return zeros.
-__device__ __forceinline__ void load_stage(char* smem, const Args& a, i32x4 rA, i32x4 rM, int64_t n0, int s,
-                                           int wave, int lane) {
+// Per-lane parts of the load offsets (the uniform parts go into the SGPR offset operand).
+struct LoadOffsets {
+    uint32_t a;      // A tile: 16 * lane
+    uint32_t m;      // metadata: 4 * (lane & 31) + (lane >> 5) * tiles * 128 (second tile of the pair)
+    uint32_t b[2];   // B row pair: (lane >> 5) * row pitch + 16 * swizzled chunk, for even / odd pair index
+};
+
+__device__ __forceinline__ LoadOffsets load_offsets(const Args& a, int lane) {
+    LoadOffsets o;
+    const int tiles = (int)(a.K / BK);
+    o.a = 16 * lane;
+    o.m = 4 * (lane & 31) + (lane >> 5) * tiles * 128;
+    const int pc = lane & 31;  // 16-byte slot in the LDS row
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+        const int row = 2 * h + (lane >> 5);                       // row & 3 of the pair's rows
+        const int lc = (((pc >> 2) ^ (row & 3)) << 2) | (pc & 3);  // 16-byte chunk of the X row
+        o.b[h] = (uint32_t)((lane >> 5) * a.ldx * 2 + 16 * lc);
+    }
+    return o;
+}
+
+// Issue this wave's share of the loads of stage `s` into the stage buffer at LDS address `lds`.
+// rA / rM cover the compressed tiles of this workgroup's 16 row blocks (tile (b, s) of block b at
+// (b * tiles + s) * 1 KB of values and * 128 B of metadata); loads past the padded rows return 0.
+__device__ __forceinline__ void load_stage(uint32_t lds, const Args& a, i32x4 rA, i32x4 rM, int64_t n0, int s,
+                                           int wave, const LoadOffsets& lo) {
     const int64_t k0 = (int64_t)s * BK;
     const int tiles = (int)(a.K / BK);
     // A: one 1 KB tile per 16-row block, copied as is (it is already in lane order)
 #pragma unroll
     for (int j = 0; j < 4; j++) {
         const int b = 4 * wave + j;
-        dma16(lds_addr(smem + b * 1024), (uint32_t)((b * tiles + s) * 1024 + 16 * lane), rA);
+        dma16(lds + b * 1024, lo.a, (uint32_t)((b * tiles + s) * 1024), rA);
     }
     // metadata: one 128 B tile per block; 4 blocks per wave, two per dword instruction
 #pragma unroll
     for (int h = 0; h < 2; h++) {
-        const int b = 4 * wave + 2 * h + (lane >> 5);
-        dma4(lds_addr(smem + A_BYTES + (4 * wave + 2 * h) * 128), (uint32_t)((b * tiles + s) * 128 + 4 * (lane & 31)),
-             rM);
+        const int b = 4 * wave + 2 * h;
+        dma4(lds + A_BYTES + b * 128, lo.m, (uint32_t)((b * tiles + s) * 128), rM);
     }
     // B: 64 rows x 512 B; this wave loads rows 16*wave .. +15, two rows per instruction. The 64-byte
     // blocks of row k are stored at block ^ (k & 3); lanes keep 16-byte runs in order inside a block.
     const i32x4 rB = make_rsrc(a.X + k0 * a.ldx + n0, (a.K * a.ldx - k0 * a.ldx - n0) * 2);
 #pragma unroll
     for (int h = 0; h < 8; h++) {
-        const int row = 16 * wave + 2 * h + (lane >> 5);
-        const int pc = lane & 31;                                  // 16-byte slot in the LDS row
-        const int lc = ((((pc >> 2) ^ (row & 3))) << 2) | (pc & 3);  // 16-byte chunk of the X row
-        dma16(lds_addr(smem + A_BYTES + META_BYTES + (16 * wave + 2 * h) * B_ROW),
-              (uint32_t)(row * a.ldx * 2 + 16 * lc), rB);
+        const int row = 16 * wave + 2 * h;
+        dma16(lds + A_BYTES + META_BYTES + row * B_ROW, lo.b[h & 1], (uint32_t)(row * a.ldx * 2), rB);
     }
 }
 
@@ -143,54 +158,182 @@ __device__ __forceinline__ LaneOffsets lane_offsets(int wm0, int wn0, int lane) 
     return o;
 }
 
-__device__ __forceinline__ void compute_stage(const char* smem, f32x4 (&acc)[FM][FN], const LaneOffsets& o) {
+// Operands of one stage held in registers: the 8 A fragments and their indices.
+struct AFrags {
     bf16x8 a[FM];
     uint32_t idx[FM];
+};
+
+__device__ __forceinline__ void read_a(const char* buf, const LaneOffsets& o, AFrags& f) {
 #pragma unroll
     for (int i = 0; i < FM; i++) {
-        a[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(smem + o.a + i * 1024));
-        idx[i] = *reinterpret_cast<const uint16_t*>(smem + o.m + i * 128);
-    }
-#pragma unroll
-    for (int j = 0; j < FN; j++) {
-        u32x8 b;
-#pragma unroll
-        for (int t = 0; t < 4; t++) {
-            // t = 0, 1: rows 8q + 4t + r/4; t = 2, 3: the same + 32
-            const int imm = (t & 1) * 4 * B_ROW + (t >> 1) * 32 * B_ROW;
-            const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) i16x4*)(smem + o.b[j] + imm));
-            b[2 * t] = (uint16_t)v[0] | ((uint32_t)(uint16_t)v[1] << 16);
-            b[2 * t + 1] = (uint16_t)v[2] | ((uint32_t)(uint16_t)v[3] << 16);
-        }
-        const bf16x16 bb = __builtin_bit_cast(bf16x16, b);
-#pragma unroll
-        for (int i = 0; i < FM; i++)
-            acc[i][j] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(a[i], bb, acc[i][j], (int)idx[i], 0, 0);
+        f.a[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(buf + o.a + i * 1024));
+        f.idx[i] = *reinterpret_cast<const uint16_t*>(buf + o.m + i * 128);
     }
 }
 
-template <int CUR, int STAGES>
-__device__ __forceinline__ void step(char* cur, char* nxt, const Args& a, i32x4 rA,
-                                     i32x4 rM, int64_t n0, int s, int S, f32x4 (&acc)[FM][FN],
-                                     const LaneOffsets& o, int wave, int lane) {
-    if (s + 2 < S) {
-        load_stage(nxt, a, rA, rM, n0, s + 2, wave, lane);
-        wait_vmcnt<2 * LOADS_PER_STAGE>();
-    } else if (s + 1 < S) {
-        wait_vmcnt<LOADS_PER_STAGE>();
-    } else {
-        wait_vmcnt<0>();
+// B fragment j (16 columns x 64 k) of the stage in `buf`: four transposing reads.
+__device__ __forceinline__ bf16x16 read_b(const char* buf, const LaneOffsets& o, int j) {
+    u32x8 b;
+#pragma unroll
+    for (int t = 0; t < 4; t++) {
+        // t = 0, 1: rows 8q + 4t + r/4; t = 2, 3: the same + 32
+        const int imm = (t & 1) * 4 * B_ROW + (t >> 1) * 32 * B_ROW;
+        const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(buf + o.b[j] + imm));
+        b[2 * t] = (uint16_t)v[0] | ((uint32_t)(uint16_t)v[1] << 16);
+        b[2 * t + 1] = (uint16_t)v[2] | ((uint32_t)(uint16_t)v[3] << 16);
     }
-    __builtin_amdgcn_s_barrier();
-    compute_stage(cur, acc, o);
-    __builtin_amdgcn_s_barrier();
+    return __builtin_bit_cast(bf16x16, b);
+}
+
+__device__ __forceinline__ void mfma_block(f32x4 (&acc)[FM][FN], const AFrags& f, const bf16x16& b, int j) {
+#pragma unroll
+    for (int i = 0; i < FM; i++)
+        acc[i][j] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(f.a[i], b, acc[i][j], (int)f.idx[i], 0, 0);
+}
+
+// One K stage (see the pipeline description in the kernel). U selects the A register set.
+template <int U>
+__device__ __forceinline__ void stage(char* smem, uint32_t l0, const Args& a, i32x4 rA, i32x4 rM, int64_t n0, int s,
+                                      int S, f32x4 (&acc)[FM][FN], AFrags (&fa)[2], bf16x16 (&rb)[4],
+                                      const LaneOffsets& o, int wave, const LoadOffsets& lo) {
+    const int cb = s % 3;
+    const char* cur = smem + cb * STAGE_BYTES;
+    const uint32_t lcur = l0 + cb * STAGE_BYTES;
+    const char* nxt = smem + (cb == 2 ? 0 : cb + 1) * STAGE_BYTES;
+    const AFrags& f = fa[U];
+#pragma unroll
+    for (int j = 0; j < 6; j++) {
+        rb[(j + 2) & 3] = read_b(cur, o, j + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_block(acc, f, rb[j & 3], j);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    if (s + 1 < S) {
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of stage s are done
+        if (s + 2 < S)
+            wait_vmcnt<LOADS_PER_STAGE>();   // stage s+1 has landed (s+2 may still be in flight)
+        else
+            wait_vmcnt<0>();
+        __builtin_amdgcn_s_barrier();
+        if (s + 3 < S) load_stage(lcur, a, rA, rM, n0, s + 3, wave, lo);
+        read_a(nxt, o, fa[U ^ 1]);
+        rb[0] = read_b(nxt, o, 0);
+        rb[1] = read_b(nxt, o, 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_block(acc, f, rb[2], 6);
+    mfma_block(acc, f, rb[3], 7);
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// ---------------------------------------------------------------- epilogues
+// The accumulators hold, per lane, 4 consecutive rows of one column; Y wants runs along a row. Each
+// wave stages its 128 x 128 tile through LDS (reusing the pipeline buffers) so global stores are
+// 16 bytes per lane with 64 contiguous bytes per row segment.
+
+// bf16: the tile is written column-major (one column = 128 rows, pitch EPI_COL bytes, padded so
+// both the 8-byte writes and the transposing reads below are free of bank conflicts), then read back
+// with ds_read_b64_tr_b16, which hands each lane 4 consecutive columns of one row.
+constexpr int EPI_COL = 128 * 2 + 40;
+static_assert(4 * 128 * EPI_COL <= 3 * STAGE_BYTES, "epilogue staging fits in the stage buffers");
+
+__device__ __forceinline__ void store_bf16(char* smem, const f32x4 (&acc)[FM][FN], const Args& a, int64_t mw, int64_t nw,
+                                           int wave, int lane) {
+    const int r = lane & 15, q = lane >> 4;
+    char* tile = smem + wave * 128 * EPI_COL;
+#pragma unroll
+    for (int i = 0; i < FM; i++)
+#pragma unroll
+        for (int j = 0; j < FN; j++) {
+            const uint32_t lo = f32_to_bf16_rne(acc[i][j][0]) | ((uint32_t)f32_to_bf16_rne(acc[i][j][1]) << 16);
+            const uint32_t hi = f32_to_bf16_rne(acc[i][j][2]) | ((uint32_t)f32_to_bf16_rne(acc[i][j][3]) << 16);
+            *reinterpret_cast<uint2*>(tile + (16 * j + r) * EPI_COL + (16 * i + 4 * q) * 2) = make_uint2(lo, hi);
+        }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes are done
+    __builtin_amdgcn_wave_barrier();
+    // 32 steps of 16 rows x 32 columns: group q takes columns cb + 8q .. +7 of rows rb .. rb+15
+    const bool full = (mw + 128 <= a.M) && (nw + 128 <= a.N);
+#pragma unroll
+    for (int rb = 0; rb < 128; rb += 16)
+#pragma unroll
+        for (int cb = 0; cb < 128; cb += 32) {
+            const int c0 = cb + 8 * q;
+            // lane s of the group points at column c0 + s/4 (+4), rows rb + 4(s%4) .. +3
+            const char* p0 = tile + (c0 + (r >> 2)) * EPI_COL + (rb + 4 * (r & 3)) * 2;
+            const i16x4 u = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p0);
+            const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) i16x4*)(p0 + 4 * EPI_COL));
+            const int64_t m = mw + rb + r, n = nw + c0;
+            const uint4 val = make_uint4((uint16_t)u[0] | ((uint32_t)(uint16_t)u[1] << 16),
+                                         (uint16_t)u[2] | ((uint32_t)(uint16_t)u[3] << 16),
+                                         (uint16_t)v[0] | ((uint32_t)(uint16_t)v[1] << 16),
+                                         (uint16_t)v[2] | ((uint32_t)(uint16_t)v[3] << 16));
+            uint16_t* y = reinterpret_cast<uint16_t*>(a.Y) + m * a.ldy + n;
+            if (full && a.y_vec) {
+                *reinterpret_cast<uint4*>(y) = val;
+            } else if (m < a.M) {
+                const uint16_t e[8] = {(uint16_t)val.x, (uint16_t)(val.x >> 16), (uint16_t)val.y, (uint16_t)(val.y >> 16),
+                                       (uint16_t)val.z, (uint16_t)(val.z >> 16), (uint16_t)val.w, (uint16_t)(val.w >> 16)};
+#pragma unroll
+                for (int k = 0; k < 8; k++)
+                    if (n + k < a.N) y[k] = e[k];
+            }
+        }
+}
+
+// fp32: two passes of 64 rows; the half-tile is written row-major (pitch EPI_ROW32 bytes, padded)
+// with one 4-byte write per value and read back 16 bytes (4 columns) per lane.
+constexpr int EPI_ROW32 = 128 * 4 + 16;
+static_assert(4 * 64 * EPI_ROW32 <= 3 * STAGE_BYTES, "epilogue staging fits in the stage buffers");
+
+__device__ __forceinline__ void store_fp32(char* smem, const f32x4 (&acc)[FM][FN], const Args& a, int64_t mw, int64_t nw,
+                                           int wave, int lane) {
+    const int r = lane & 15, q = lane >> 4;
+    char* tile = smem + wave * 64 * EPI_ROW32;
+    const bool full = (mw + 128 <= a.M) && (nw + 128 <= a.N);
+#pragma unroll
+    for (int half = 0; half < 2; half++) {
+#pragma unroll
+        for (int i = 0; i < FM / 2; i++)
+#pragma unroll
+            for (int j = 0; j < FN; j++)
+#pragma unroll
+                for (int t = 0; t < 4; t++)
+                    *reinterpret_cast<float*>(tile + (16 * i + 4 * q + t) * EPI_ROW32 + (16 * j + r) * 4) =
+                        acc[half * (FM / 2) + i][j][t];
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        __builtin_amdgcn_wave_barrier();
+        // 64 rows x 128 columns: each step covers 2 rows (32 lanes x 4 columns per row)
+#pragma unroll
+        for (int rr = 0; rr < 64; rr += 2) {
+            const int row = rr + (lane >> 5), col = 4 * (lane & 31);
+            const float4 v = *reinterpret_cast<const float4*>(tile + row * EPI_ROW32 + col * 4);
+            const int64_t m = mw + 64 * half + row, n = nw + col;
+            float* y = reinterpret_cast<float*>(a.Y) + m * a.ldy + n;
+            if (full && a.y_vec) {
+                *reinterpret_cast<float4*>(y) = v;
+            } else if (m < a.M) {
+                const float e[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int k = 0; k < 4; k++)
+                    if (n + k < a.N) y[k] = e[k];
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        __builtin_amdgcn_wave_barrier();
+    }
 }
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_bf16_tiled_kernel(Args a) {
-    __shared__ __attribute__((aligned(16))) char s0[STAGE_BYTES];
-    __shared__ __attribute__((aligned(16))) char s1[STAGE_BYTES];
-    __shared__ __attribute__((aligned(16))) char s2[STAGE_BYTES];
+    __shared__ __attribute__((aligned(16))) char smem[3 * STAGE_BYTES];
+    char* const s0 = smem;
+    char* const s1 = smem + STAGE_BYTES;
+    char* const s2 = smem + 2 * STAGE_BYTES;
+    // LDS byte addresses of the three stage buffers (for the LDS-destination loads)
+    const uint32_t l0 = (uint32_t)(size_t)(__attribute__((address_space(3))) char*)smem;
+    const uint32_t l1 = l0 + STAGE_BYTES, l2 = l0 + 2 * STAGE_BYTES;
 
     // XCD-first, then grouped tile order
     const int T = a.tilesM * a.tilesN;
@@ -206,7 +349,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int tm = first_m + in_g % gm, tn = in_g / gm;
     const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
 
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int wm0 = (wave >> 1) * WM, wn0 = (wave & 1) * WN;
     // compressed tiles of this workgroup's first row block onward (rows are padded to 16)
     const int64_t tiles = a.K / BK, blocks_left = (a.M + 15) / 16 - m0 / 16;
@@ -221,45 +364,47 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         for (int j = 0; j < FN; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const LaneOffsets o = lane_offsets(wm0, wn0, lane);
+    const LoadOffsets lo = load_offsets(a, lane);
     const int S = (int)(a.K / BK);
-    load_stage(s0, a, rA, rM, n0, 0, wave, lane);
-    if (S > 1) load_stage(s1, a, rA, rM, n0, 1, wave, lane);
-    // main loop in groups of three stages (one per LDS buffer), then the 0-2 remaining stages;
-    // keeping the loop body free of early exits keeps the accumulators in registers
+
+    // Software pipeline over K stages of 64 columns, three LDS buffers (stage s in buffer s % 3):
+    //  - the loads of stage s+3 go out once every wave has finished reading stage s, i.e. at the
+    //    barrier placed before the last two fragment blocks of stage s, so each stage's loads have
+    //    about two stages of compute to land;
+    //  - that barrier also publishes stage s+1 (each wave first waits for its own loads of it), so
+    //    stage s+1's A fragments, indices and first B fragments are read while the last 16
+    //    smfmacs of stage s run;
+    //  - inside a stage, B fragment j+2 is read while fragment j is multiplied (ring of 4).
+    load_stage(l0, a, rA, rM, n0, 0, wave, lo);
+    if (S > 1) load_stage(l1, a, rA, rM, n0, 1, wave, lo);
+    if (S > 1)
+        wait_vmcnt<LOADS_PER_STAGE>();
+    else
+        wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    if (S > 2) load_stage(l2, a, rA, rM, n0, 2, wave, lo);
+
+    AFrags fa[2];
+    bf16x16 rb[4];
+    read_a(s0, o, fa[0]);
+    rb[0] = read_b(s0, o, 0);
+    rb[1] = read_b(s0, o, 1);
+
+    // two stages per loop iteration so the A register sets alternate statically; the loop body
+    // has no early exit (that keeps the accumulators in registers), the last odd stage follows
     int s = 0;
-    for (; s + 3 <= S; s += 3) {
-        step<0, 3>(s0, s2, a, rA, rM, n0, s, S, acc, o, wave, lane);
-        step<1, 3>(s1, s0, a, rA, rM, n0, s + 1, S, acc, o, wave, lane);
-        step<2, 3>(s2, s1, a, rA, rM, n0, s + 2, S, acc, o, wave, lane);
+    for (; s + 2 <= S; s += 2) {
+        stage<0>(smem, l0, a, rA, rM, n0, s, S, acc, fa, rb, o, wave, lo);
+        stage<1>(smem, l0, a, rA, rM, n0, s + 1, S, acc, fa, rb, o, wave, lo);
     }
-    if (s < S) step<0, 3>(s0, s2, a, rA, rM, n0, s, S, acc, o, wave, lane);
-    if (s + 1 < S) step<1, 3>(s1, s0, a, rA, rM, n0, s + 1, S, acc, o, wave, lane);
+    if (s < S) stage<0>(smem, l0, a, rA, rM, n0, s, S, acc, fa, rb, o, wave, lo);
 
     // epilogue: lane holds column n0 + wn0 + 16 j + r, rows m0 + wm0 + 16 i + 4 q + t
-    const int r = lane & 15, q = lane >> 4;
-    const int64_t mrow = m0 + wm0 + 4 * q, ncol = n0 + wn0 + r;
-    const bool full = (m0 + BM <= a.M) && (n0 + BN <= a.N);
-    if (a.out_fp32) {
-        float* y = reinterpret_cast<float*>(a.Y) + mrow * a.ldy + ncol;
-#pragma unroll
-        for (int i = 0; i < FM; i++)
-#pragma unroll
-            for (int t = 0; t < 4; t++)
-#pragma unroll
-                for (int j = 0; j < FN; j++)
-                    if (full || (mrow + 16 * i + t < a.M && ncol + 16 * j < a.N))
-                        y[(16 * i + t) * a.ldy + 16 * j] = acc[i][j][t];
-    } else {
-        uint16_t* y = reinterpret_cast<uint16_t*>(a.Y) + mrow * a.ldy + ncol;
-#pragma unroll
-        for (int i = 0; i < FM; i++)
-#pragma unroll
-            for (int t = 0; t < 4; t++)
-#pragma unroll
-                for (int j = 0; j < FN; j++)
-                    if (full || (mrow + 16 * i + t < a.M && ncol + 16 * j < a.N))
-                        y[(16 * i + t) * a.ldy + 16 * j] = f32_to_bf16_rne(acc[i][j][t]);
-    }
+    __builtin_amdgcn_s_barrier();  // every wave is done reading the stage buffers
+    if (a.out_fp32)
+        store_fp32(s0, acc, a, m0 + wm0, n0 + wn0, wave, lane);
+    else
+        store_bf16(s0, acc, a, m0 + wm0, n0 + wn0, wave, lane);
 }
 
 }  // namespace tiled_bf16
@@ -277,6 +422,7 @@ hipError_t launch_gemm_bf16_tiled(const uint16_t* values, const uint8_t* meta, i
     a.tilesM = (int)((M + tiled_bf16::BM - 1) / tiled_bf16::BM);
     a.tilesN = (int)((N + tiled_bf16::BN - 1) / tiled_bf16::BN);
     a.out_fp32 = out_fp32 ? 1 : 0;
+    a.y_vec = ((reinterpret_cast<uintptr_t>(Y) & 15) == 0) && ((ldy * (out_fp32 ? 4 : 2)) % 16 == 0);
     const unsigned grid = (unsigned)(a.tilesM * a.tilesN);
     hipLaunchKernelGGL(tiled_bf16::gemm_bf16_tiled_kernel, dim3(grid), dim3(256), 0, s, a);
     return hipGetLastError();
