@@ -13,6 +13,7 @@ or flops per launch), and the CPU oracle timed on a bounded sample of the same w
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -32,6 +33,8 @@ SPARSE_BF16_PEAK_TF = 5033.2   # dense-equivalent, 2:4 sparse MFMA
 SPARSE_I8_PEAK_TOPS = 10066.4
 DENSE_BF16_PEAK_TF = 2516.6
 CACHE_BYTES = 256 << 20        # MI355X Infinity Cache
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "structured_sparse_gemm_sp24_amd", "csrc")
 
 
 def to_dev(a, kind=None):
@@ -70,6 +73,13 @@ def workload_vit(args):
     def gemm(c):
         sp.sp24_gemm_bf16(c["vals"], c["meta"], M, c["X"], out=c["Y"])
 
+    def dense_ref():
+        # dense bf16 GEMM of the same shape (torch.matmul -> hipBLASLt) on the decompressed pruned weight
+        c0 = copies[0]
+        sp.sp24_prune_compress(c0["W"], values=c0["vals"], meta=c0["meta"])
+        Wd = sp.sp24_decompress(c0["vals"], c0["meta"], M, K)
+        return [(lambda c, Wd=Wd: torch.matmul(Wd, c["X"], out=c["Y"]))]
+
     def cpu_sample(budget_s):
         import oracle
         t0 = time.perf_counter()
@@ -91,14 +101,70 @@ def workload_vit(args):
                             activations="bf16 N(0,1) seed 12, N = 32 images x 197 tokens", score="magnitude",
                             out="bf16", step="prune_compress + gemm_bf16"),
                 flops=2.0 * M * N * K, copies=copies, kernels=dict(prune_compress=prune, gemm_bf16=gemm),
-                dominant="gemm_bf16", gemm_bytes=M * K * 9 // 8 + K * N * 2 + M * N * 2, gemm_flops=2.0 * M * N * K,
+                dominant="gemm_bf16", sources=("gemm_bf16_tiled.hip", "sp24_device.h"),
+                dense_ref=dense_ref, gemm_bytes=M * K * 9 // 8 + K * N * 2 + M * N * 2, gemm_flops=2.0 * M * N * K,
                 prune_bytes=M * K * 2 + M * K * 9 // 8, cpu_sample=cpu_sample, unit="TFLOP/s")
 
 
 WORKLOADS = {"vit_b16_fc1": workload_vit}
 
 
+# ----------------------------------------------------------------------------- HBM traffic
+
+def source_digest(files) -> str:
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(w):
+    """HBM bytes per launch of the dominant kernel from the committed counter summary (FETCH_SIZE +
+    WRITE_SIZE, scaled by a plain copy's reading), or None when there is none or the kernel's source
+    has changed since the counters were taken."""
+    path = os.path.join(PROFILES, f"{w['dominant']}_{w['name']}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_digest") != source_digest(w["sources"]):
+        return None
+    return int(float(kv["traffic_bytes_per_launch"]))
+
+
+def copy_calibration(mib: int, reps: int):
+    """A plain device-to-device copy of a known size, for scaling FETCH_SIZE / WRITE_SIZE readings."""
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps(dict(copy_bytes_read=n, copy_bytes_written=n, reps=reps)), flush=True)
+
+
 # ----------------------------------------------------------------------------- timing
+
+def kernel_time_ms(fn, copies, steps, warmup):
+    """Average duration of fn(copy) from HIP events recorded on the launch stream, rotating copies."""
+    nc = len(copies)
+    for i in range(warmup):
+        fn(copies[i % nc])
+    ev = []
+    for i in range(steps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn(copies[i % nc])
+        e1.record()
+        ev.append((e0, e1))
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
 
 def timed_steps(w, steps, warmup):
     copies, kernels = w["copies"], w["kernels"]
@@ -142,6 +208,9 @@ def main():
     ap.add_argument("--workload", default="vit_b16_fc1", choices=sorted(WORKLOADS))
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense-ref", action="store_true", help="skip timing the dense bf16 GEMM of the same shape")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain copy of MIB MiB (to scale FETCH_SIZE / WRITE_SIZE counter readings)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path shards with no "
@@ -150,6 +219,9 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, max(args.steps, 1))
+        return
     sp.load_library()
     w = WORKLOADS[args.workload](args)
     t_total, per_kernel_ms = timed_steps(w, args.steps, args.warmup)
@@ -165,11 +237,12 @@ def main():
     ideal_mfma = w["gemm_flops"] / (peak_tf * 1e12)
     if ideal_hbm >= ideal_mfma:
         roof = dict(bound="hbm", achieved=round(achieved_gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(achieved_gbs / HBM_PEAK_GBS, 4), traffic=None)
+                    frac=round(achieved_gbs / HBM_PEAK_GBS, 4), traffic=measured_traffic(w))
     else:
         roof = dict(bound="mfma", achieved=round(achieved_tf, 1), peak=peak_tf,
                     unit="TOP/s" if w["dtype"] == "i8" else "TFLOP/s", frac=round(achieved_tf / peak_tf, 4),
-                    traffic=None)
+                    traffic=measured_traffic(w))
+    roof["algorithmic_bytes"] = w["gemm_bytes"]
     roof["kernel"] = dom
     roof["mfma_frac"] = round(achieved_tf / peak_tf, 4)
     roof["hbm_frac"] = round(achieved_gbs / HBM_PEAK_GBS, 4)
@@ -182,6 +255,12 @@ def main():
     if "prune_compress" in per_kernel_ms:
         kernels["prune_compress"]["gbs_algorithmic"] = round(w["prune_bytes"] / (per_kernel_ms["prune_compress"] * 1e-3)
                                                             / 1e9, 1)
+
+    if not args.no_dense_ref and w.get("dense_ref"):
+        fns = w["dense_ref"]()
+        t_dense = sum(kernel_time_ms(f, w["copies"], args.steps, args.warmup) for f in fns)
+        kernels["dense_bf16_matmul_same_shape"] = dict(avg_us=round(t_dense * 1e3, 2))
+        kernels[dom]["speedup_vs_dense"] = round(t_dense / per_kernel_ms[dom], 3)
 
     cpu = None
     if not args.no_cpu_baseline:
