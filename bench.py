@@ -1,14 +1,21 @@
 """Benchmark of the 2:4 sparse hot path on one MI355X.
 
-One step = one pass of the workload's whole path over its synthetic batch, e.g. for the default
-ViT-B/16 MLP fc1 workload: 2:4 magnitude prune + compress of W (3072 x 768 bf16), then the sparse
-GEMM Y = W_2:4 . X (X 768 x 6304 bf16, Y bf16). Inputs are resident in HBM before timing; steps
-rotate over enough copies of every buffer (> 2x the 256 MB Infinity Cache) that each step reads its
-operands from HBM, not from cache.
+One step = one pass of a workload's whole path over its synthetic batch. The default workload is the
+ViT-B/16 MLP fc1 layer: 2:4 magnitude prune + compress of W (3072 x 768 bf16), then the sparse GEMM
+Y = W_2:4 . X (X 768 x 6304 bf16, Y bf16). Other workloads (--workload, --n) cover the single 256 x 256
+Linear, the BERT-base int8 FFN pair, the LLM projections with Wanda scoring and the 28672 x 8192 FFN
+sweep. Inputs are resident in HBM before timing; steps rotate over enough copies of every buffer
+(> 2x the 256 MB Infinity Cache, when they fit) that each step reads its operands from HBM.
 
-Prints ONE JSON line: dense-equivalent TFLOP/s of the step (2*M*N*K per step), the dominant
-kernel's roofline (its own average duration from HIP events on the launch stream, algorithmic bytes
-or flops per launch), and the CPU oracle timed on a bounded sample of the same workload.
+Prints ONE JSON line: the step's dense-equivalent throughput (2*M*N*K per GEMM), the dominant
+kernel's roofline (its average duration from HIP events on the launch stream; algorithmic bytes or
+flops per launch; HBM traffic from the committed counter summary when the kernel source matches),
+and the CPU oracle timed on a bounded sample of the same workload.
+
+Roofline conventions: a 2:4 GEMM executes M*N*K/2 multiply-adds, i.e. M*N*K algorithmic flops, which
+are priced against the dense MFMA peak of the dtype (bf16 2516.6 TFLOP/s, int8 5033.2 TOP/s); this
+fraction equals the dense-equivalent rate 2*M*N*K/t over the sparse-MFMA peak. HBM-bound kernels are
+priced as algorithmic bytes / t against 8 TB/s.
 """
 from __future__ import annotations
 
@@ -29,12 +36,11 @@ import structured_sparse_gemm_sp24_amd as sp  # noqa: E402
 from structured_sparse_gemm_sp24_amd import synth  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
-SPARSE_BF16_PEAK_TF = 5033.2   # dense-equivalent, 2:4 sparse MFMA
-SPARSE_I8_PEAK_TOPS = 10066.4
-DENSE_BF16_PEAK_TF = 2516.6
-CACHE_BYTES = 256 << 20        # MI355X Infinity Cache
+DENSE_PEAK = {"bf16": 2516.6, "i8": 5033.2}   # TFLOP/s (bf16) and TOP/s (int8), dense MFMA
+CACHE_BYTES = 256 << 20                      # MI355X Infinity Cache
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "structured_sparse_gemm_sp24_amd", "csrc")
+TILED_MIN_N = 65                             # sp24_gemm_bf16 uses the LDS-tiled kernel above N = 64
 
 
 def to_dev(a, kind=None):
@@ -44,69 +50,219 @@ def to_dev(a, kind=None):
     return torch.from_numpy(a).cuda()
 
 
-def n_copies(step_bytes: int) -> int:
-    return max(1, min(64, int(np.ceil(2 * CACHE_BYTES / max(step_bytes, 1)))))
+def n_copies(step_bytes: int, budget: int = 24 << 30) -> int:
+    n = int(np.ceil(2 * CACHE_BYTES / max(step_bytes, 1)))
+    return max(1, min(64, n, budget // max(step_bytes, 1)))
+
+
+class Kernel:
+    """One launch of the step: fn(copy), algorithmic bytes and flops per launch, the dtype of its
+    arithmetic, and the source files whose digest keys its counter-measured traffic."""
+
+    def __init__(self, name, fn, nbytes, flops=0.0, dtype="bf16", sources=()):
+        self.name, self.fn, self.nbytes, self.flops, self.dtype, self.sources = name, fn, nbytes, flops, dtype, sources
+
+
+def gemm_sources(N):
+    return ("gemm_bf16_tiled.hip", "sp24_device.h") if N >= TILED_MIN_N else ("gemm_bf16.hip", "sp24_device.h")
 
 
 # ----------------------------------------------------------------------------- workloads
-# Each builder returns a dict with: name, config, flops (dense-equivalent per step), copies (list of
-# per-copy buffer dicts), step(c) (runs one pass on copy c), gemm(c) (the dominant kernel alone),
-# gemm_bytes / gemm_flops (algorithmic, per launch), bound, dtype, cpu_sample() (oracle timing).
+# Each builder returns: name, config, dtype, flops (dense-equivalent per step), copies, kernels (in
+# step order), dense_ref (optional: the dense GEMM of the same shape), cpu_sample(budget) -> (s, text).
+
+def _bf16_gemm_workload(name, W_host, X_host, score, Xcal_host, config, out=torch.bfloat16):
+    M, K = W_host.shape
+    N = X_host.shape[1]
+    vb, mb = sp.sp24_compressed_bytes(M, K, torch.bfloat16)
+    ob = 2 if out == torch.bfloat16 else 4
+    step_bytes = M * K * 2 + vb + mb + K * N * 2 + M * N * ob + (Xcal_host.size * 2 if Xcal_host is not None else 0)
+    copies = []
+    for _ in range(n_copies(step_bytes)):
+        c = dict(W=to_dev(W_host, "bf16"), X=to_dev(X_host, "bf16"),
+                 vals=torch.empty(vb // 2, dtype=torch.bfloat16, device="cuda"),
+                 meta=torch.empty(mb, dtype=torch.uint8, device="cuda"),
+                 Y=torch.empty((M, N), dtype=out, device="cuda"))
+        if Xcal_host is not None:
+            c["Xcal"] = to_dev(Xcal_host, "bf16")
+            c["norms"] = torch.empty(K, dtype=torch.float32, device="cuda")
+        copies.append(c)
+    kernels = []
+    if Xcal_host is not None:
+        Ncal = Xcal_host.shape[1]
+        kernels.append(Kernel("col_norms", lambda c: sp.sp24_col_norms(c["Xcal"], norms=c["norms"]),
+                              K * Ncal * 2 + K * 4, sources=("norms.hip", "sp24_device.h")))
+    wanda = score == sp.SP24_SCORE_WANDA
+    kernels.append(Kernel(
+        "prune_compress",
+        lambda c: sp.sp24_prune_compress(c["W"], score=score, norms=c["norms"] if wanda else None, values=c["vals"],
+                                         meta=c["meta"]),
+        M * K * 2 + (K * 4 if wanda else 0) + M * K * 9 // 8, sources=("prune.hip", "sp24_device.h")))
+    kernels.append(Kernel("gemm_bf16", lambda c: sp.sp24_gemm_bf16(c["vals"], c["meta"], M, c["X"], out=c["Y"]),
+                          M * K * 9 // 8 + K * N * 2 + M * N * ob, float(M) * N * K, "bf16", gemm_sources(N)))
+
+    def dense_ref():
+        c0 = copies[0]
+        for k in kernels:
+            k.fn(c0)
+        Wd = sp.sp24_decompress(c0["vals"], c0["meta"], M, K)
+        Yd = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        return lambda c: torch.matmul(Wd, c["X"], out=Yd)
+
+    def cpu_sample(budget_s):
+        import oracle
+        t0 = time.perf_counter()
+        norms = None
+        if Xcal_host is not None:
+            norms = oracle.col_norms(Xcal_host)
+        v, m = oracle.prune_compress(W_host, oracle.BF16, oracle.WANDA if wanda else oracle.MAGNITUDE, norms)
+        t_fixed = time.perf_counter() - t0
+        rows = min(M, 8)
+        t0 = time.perf_counter()
+        oracle.gemm_bf16(v, m, X_host, M, rows=np.arange(rows))
+        t_small = time.perf_counter() - t0
+        rows = int(min(M, max(8, rows * max(budget_s - t_fixed, 1.0) / max(t_small, 1e-6))))
+        t0 = time.perf_counter()
+        oracle.gemm_bf16(v, m, X_host, M, rows=np.arange(rows))
+        t_rows = time.perf_counter() - t0
+        what = ("column norms + " if norms is not None else "") + f"prune/compress of the full {M}x{K} W"
+        return t_fixed + t_rows * M / rows, f"{what} + GEMM on {rows} of {M} rows (N = {N}), scaled to all rows"
+
+    return dict(name=name, dtype="bf16", unit="TFLOP/s", config=config, flops=2.0 * M * N * K, copies=copies,
+                kernels=kernels, dense_ref=dense_ref, cpu_sample=cpu_sample)
+
 
 def workload_vit(args):
     d = synth.vit_b16_fc1()
     M, K = d["W_bf16"].shape
     N = d["X_bf16"].shape[1]
-    step_bytes = M * K * 2 + M * K * 9 // 8 + K * N * 2 + M * N * 2
-    copies = []
-    for _ in range(n_copies(step_bytes)):
-        W = to_dev(d["W_bf16"], "bf16")
-        vb, mb = sp.sp24_compressed_bytes(M, K, torch.bfloat16)
-        copies.append(dict(W=W, X=to_dev(d["X_bf16"], "bf16"),
-                           vals=torch.empty(vb // 2, dtype=torch.bfloat16, device="cuda"),
-                           meta=torch.empty(mb, dtype=torch.uint8, device="cuda"),
-                           Y=torch.empty((M, N), dtype=torch.bfloat16, device="cuda")))
+    cfg = dict(workload="vit_b16_fc1", M=M, K=K, N=N, weight="bf16 N(0,0.02^2) seed 11",
+               activations="bf16 N(0,1) seed 12, N = 32 images x 197 tokens", score="magnitude", out="bf16",
+               step="prune_compress + gemm_bf16")
+    return _bf16_gemm_workload("vit_b16_fc1", d["W_bf16"], d["X_bf16"], sp.SP24_SCORE_MAGNITUDE, None, cfg)
 
-    def prune(c):
-        sp.sp24_prune_compress(c["W"], values=c["vals"], meta=c["meta"])
 
-    def gemm(c):
-        sp.sp24_gemm_bf16(c["vals"], c["meta"], M, c["X"], out=c["Y"])
+def workload_llm(M):
+    def build(args):
+        N = args.n or 4096
+        d = synth.llm_proj(M)
+        X = np.ascontiguousarray(d["X_bf16"][:, :N])
+        cfg = dict(workload=f"llm_proj_{M}x4096", M=M, K=4096, N=N,
+                   weight=f"bf16 N(0,0.02^2) seed {31 if M == 11008 else 32}",
+                   calibration="4096 x 2048 bf16, lognormal(0,1) channel scale x Student-t(3), seed 33",
+                   activations="same law, seed 34, first N columns", score="wanda", out="bf16",
+                   step="col_norms + prune_compress (Wanda) + gemm_bf16")
+        return _bf16_gemm_workload(f"llm_proj_{M}x4096_n{N}", d["W_bf16"], X, sp.SP24_SCORE_WANDA, d["Xcal_bf16"], cfg)
+    return build
 
-    def dense_ref():
-        # dense bf16 GEMM of the same shape (torch.matmul -> hipBLASLt) on the decompressed pruned weight
-        c0 = copies[0]
-        sp.sp24_prune_compress(c0["W"], values=c0["vals"], meta=c0["meta"])
-        Wd = sp.sp24_decompress(c0["vals"], c0["meta"], M, K)
-        return [(lambda c, Wd=Wd: torch.matmul(Wd, c["X"], out=c["Y"]))]
+
+def workload_ffn(args):
+    N = args.n or 8192
+    d = synth.ffn_28672x8192(N)
+    cfg = dict(workload="ffn_28672x8192", M=28672, K=8192, N=N, weight="bf16 N(0,0.02^2) seed 41",
+               activations="bf16 N(0,1) seed 42, first N columns of an 8192-wide draw", score="magnitude",
+               out="bf16", step="prune_compress + gemm_bf16")
+    return _bf16_gemm_workload(f"ffn_28672x8192_n{N}", d["W_bf16"], d["X_bf16"], sp.SP24_SCORE_MAGNITUDE, None, cfg)
+
+
+def workload_single(args):
+    d = synth.single_linear_256()
+    W, X = d["W_f32"], d["X_bf16"]
+    M, K = W.shape
+    N = X.shape[1]
+    vb, mb = sp.sp24_compressed_bytes(M, K, torch.bfloat16)
+    copies = [dict(W=to_dev(W), X=to_dev(X, "bf16"), vals=torch.empty(vb // 2, dtype=torch.bfloat16, device="cuda"),
+                   meta=torch.empty(mb, dtype=torch.uint8, device="cuda"),
+                   Y=torch.empty((M, N), dtype=torch.float32, device="cuda")) for _ in range(8)]
+    kernels = [
+        Kernel("prune_compress", lambda c: sp.sp24_prune_compress(c["W"], val_dtype=torch.bfloat16, values=c["vals"],
+                                                                  meta=c["meta"]),
+               M * K * 4 + M * K * 9 // 8, sources=("prune.hip", "sp24_device.h")),
+        Kernel("gemm_bf16", lambda c: sp.sp24_gemm_bf16(c["vals"], c["meta"], M, c["X"], out=c["Y"]),
+               M * K * 9 // 8 + K * N * 2 + M * N * 4, float(M) * N * K, "bf16", gemm_sources(N))]
 
     def cpu_sample(budget_s):
         import oracle
         t0 = time.perf_counter()
-        v, m = oracle.prune_compress(d["W_bf16"], oracle.BF16)
-        t_prune = time.perf_counter() - t0
-        rows = 8
-        t0 = time.perf_counter()
-        oracle.gemm_bf16(v, m, d["X_bf16"], M, rows=np.arange(rows))
-        t_small = time.perf_counter() - t0
-        rows = int(min(M, max(8, rows * (budget_s - t_prune) / max(t_small, 1e-6))))
-        t0 = time.perf_counter()
-        oracle.gemm_bf16(v, m, d["X_bf16"], M, rows=np.arange(rows))
-        t_rows = time.perf_counter() - t0
-        t_step = t_prune + t_rows * M / rows
-        return t_step, f"prune/compress of the full {M}x{K} W + GEMM on {rows} of {M} rows, scaled to all rows"
+        v, m = oracle.prune_compress(W, oracle.FP32, val_dtype=oracle.BF16)
+        oracle.gemm_bf16(v, m, X, M)
+        return time.perf_counter() - t0, "the whole step (prune/compress fp32 -> bf16 values, GEMM) once"
 
-    return dict(name="vit_b16_fc1", dtype="bf16",
-                config=dict(workload="vit_b16_fc1", M=M, K=K, N=N, weight="bf16 N(0,0.02^2) seed 11",
-                            activations="bf16 N(0,1) seed 12, N = 32 images x 197 tokens", score="magnitude",
-                            out="bf16", step="prune_compress + gemm_bf16"),
-                flops=2.0 * M * N * K, copies=copies, kernels=dict(prune_compress=prune, gemm_bf16=gemm),
-                dominant="gemm_bf16", sources=("gemm_bf16_tiled.hip", "sp24_device.h"),
-                dense_ref=dense_ref, gemm_bytes=M * K * 9 // 8 + K * N * 2 + M * N * 2, gemm_flops=2.0 * M * N * K,
-                prune_bytes=M * K * 2 + M * K * 9 // 8, cpu_sample=cpu_sample, unit="TFLOP/s")
+    cfg = dict(workload="single_linear_256", M=M, K=K, N=N, weight="fp32 N(0,1) seed 1, kept values rounded to bf16",
+               activations="fp32 N(0,1) seed 2 rounded to bf16", score="magnitude", out="fp32",
+               step="prune_compress + gemm_bf16")
+    return dict(name="single_linear_256", dtype="bf16", unit="TFLOP/s", config=cfg, flops=2.0 * M * N * K,
+                copies=copies, kernels=kernels, dense_ref=None, cpu_sample=cpu_sample)
 
 
-WORKLOADS = {"vit_b16_fc1": workload_vit}
+def workload_bert_int8(args):
+    """BERT-base FFN pair in int8: W1 3072x768 and W2 768x3072 magnitude-pruned 2:4 in fp32, then per-row
+    symmetric int8 (99.99 % coverage); activations per-tensor int8. The step prunes/compresses both
+    int8 weights on the GPU and runs both int8 GEMMs (int32 accumulate, fp32 dequant epilogue)."""
+    d = synth.bert_ffn_int8_dense()
+    layers = []
+    for wk, xk in (("W1_f32", "X1_f32"), ("W2_f32", "X2_f32")):
+        Wf = d[wk]
+        M, K = Wf.shape
+        # host data prep (untimed): prune the fp32 weight with the library itself, then quantize
+        v, m = sp.sp24_prune_compress(to_dev(Wf))
+        Wp = sp.sp24_decompress(v, m, M, K).cpu().numpy()
+        q, s_w = synth.quantize_rows(Wp)
+        xq, s_x = synth.quantize_tensor(d[xk])
+        layers.append(dict(M=M, K=K, N=xq.shape[1], q=q, xq=xq, scale=synth.dequant_scales(s_w, s_x)))
+    step_bytes = sum(L["M"] * L["K"] * 2 + L["K"] * L["N"] + 4 * L["M"] * L["N"] for L in layers)
+    copies = []
+    for _ in range(n_copies(step_bytes)):
+        c = {}
+        for i, L in enumerate(layers):
+            vb, mb = sp.sp24_compressed_bytes(L["M"], L["K"], torch.int8)
+            c[i] = dict(W=to_dev(L["q"]), X=to_dev(L["xq"]), scale=to_dev(L["scale"]),
+                        vals=torch.empty(vb, dtype=torch.int8, device="cuda"),
+                        meta=torch.empty(mb, dtype=torch.uint8, device="cuda"),
+                        Y=torch.empty((L["M"], L["N"]), dtype=torch.float32, device="cuda"))
+        copies.append(c)
+    kernels = []
+    for i, L in enumerate(layers):
+        M, K, N = L["M"], L["K"], L["N"]
+        kernels.append(Kernel(f"prune_compress_i8_w{i + 1}",
+                              lambda c, i=i: sp.sp24_prune_compress(c[i]["W"], values=c[i]["vals"], meta=c[i]["meta"]),
+                              M * K + M * K * 5 // 8, sources=("prune.hip", "sp24_device.h")))
+        kernels.append(Kernel(f"gemm_i8_w{i + 1}",
+                              lambda c, i=i, M=M: sp.sp24_gemm_i8(c[i]["vals"], c[i]["meta"], M, c[i]["X"],
+                                                                  scale=c[i]["scale"], out=c[i]["Y"]),
+                              M * K * 5 // 8 + K * N + 4 * M * N + 4 * M, float(M) * N * K, "i8",
+                              ("gemm_i8.hip", "sp24_device.h")))
+
+    def cpu_sample(budget_s):
+        import oracle
+        total, parts = 0.0, []
+        for L in layers:
+            t0 = time.perf_counter()
+            v8, m8 = oracle.prune_compress(L["q"], oracle.I8)
+            t_fixed = time.perf_counter() - t0
+            rows = 16
+            t0 = time.perf_counter()
+            oracle.gemm_i8(v8, m8, L["xq"], L["M"], L["scale"], rows=np.arange(rows))
+            t_small = time.perf_counter() - t0
+            rows = int(min(L["M"], max(16, rows * max(budget_s / 2 - t_fixed, 0.5) / max(t_small, 1e-6))))
+            t0 = time.perf_counter()
+            oracle.gemm_i8(v8, m8, L["xq"], L["M"], L["scale"], rows=np.arange(rows))
+            total += t_fixed + (time.perf_counter() - t0) * L["M"] / rows
+            parts.append(f"{L['M']}x{L['K']}: GEMM on {rows} rows")
+        return total, "int8 prune/compress of both weights + " + ", ".join(parts) + ", scaled to all rows"
+
+    cfg = dict(workload="bert_ffn_int8", W1="3072x768", W2="768x3072", N=8192,
+               weights="fp32 N(0,0.02^2) seeds 21/22, 2:4 magnitude, per-row int8 at 99.99 % coverage",
+               activations="fp32 N(0,1) seeds 23/24, per-tensor int8 at 99.99 % coverage (64 x 128 tokens)",
+               out="fp32 (int32 accumulate, per-channel dequant)", step="2 x (prune_compress int8 + gemm_i8)")
+    flops = sum(2.0 * L["M"] * L["N"] * L["K"] for L in layers)
+    return dict(name="bert_ffn_int8", dtype="i8", unit="TOP/s", config=cfg, flops=flops, copies=copies,
+                kernels=kernels, dense_ref=None, cpu_sample=cpu_sample)
+
+
+WORKLOADS = {"vit_b16_fc1": workload_vit, "single_linear_256": workload_single, "bert_ffn_int8": workload_bert_int8,
+             "llm_proj_11008x4096": workload_llm(11008), "llm_proj_4096x4096": workload_llm(4096),
+             "ffn_28672x8192": workload_ffn}
 
 
 # ----------------------------------------------------------------------------- HBM traffic
@@ -119,19 +275,19 @@ def source_digest(files) -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(w):
-    """HBM bytes per launch of the dominant kernel from the committed counter summary (FETCH_SIZE +
-    WRITE_SIZE, scaled by a plain copy's reading), or None when there is none or the kernel's source
-    has changed since the counters were taken."""
-    path = os.path.join(PROFILES, f"{w['dominant']}_{w['name']}_traffic.txt")
+def measured_traffic(workload: str, k: Kernel):
+    """HBM bytes per launch of kernel k from the committed counter summary (FETCH_SIZE + WRITE_SIZE, each
+    scaled by a plain copy's reading), or None when there is none or the kernel's source has changed
+    since the counters were taken."""
+    path = os.path.join(PROFILES, f"{k.name}_{workload}_traffic.txt")
     if not os.path.exists(path):
         return None
     kv = {}
     for line in open(path):
         if ":" in line and not line.startswith("#"):
-            k, v = line.split(":", 1)
-            kv[k.strip()] = v.strip()
-    if kv.get("kernel_source_digest") != source_digest(w["sources"]):
+            key, v = line.split(":", 1)
+            kv[key.strip()] = v.strip()
+    if kv.get("kernel_source_digest") != source_digest(k.sources):
         return None
     return int(float(kv["traffic_bytes_per_launch"]))
 
@@ -168,36 +324,54 @@ def kernel_time_ms(fn, copies, steps, warmup):
 
 def timed_steps(w, steps, warmup):
     copies, kernels = w["copies"], w["kernels"]
-    names = list(kernels)
 
     def step(c):
-        for n in names:
-            kernels[n](c)
+        for k in kernels:
+            k.fn(c)
 
     nc = len(copies)
     for i in range(warmup):
         step(copies[i % nc])
     torch.cuda.synchronize()
-    # whole steps, host clock around K steps bracketed by synchronizations
+    # whole steps: host clock around K steps bracketed by synchronizations
     t0 = time.perf_counter()
     for i in range(steps):
         step(copies[i % nc])
     torch.cuda.synchronize()
     t_total = time.perf_counter() - t0
     # per-kernel durations: HIP events on the launch stream around each kernel, same rotation
-    ev = {n: [] for n in names}
+    ev = {k.name: [] for k in kernels}
     for i in range(steps):
         c = copies[i % nc]
-        for n in names:
+        for k in kernels:
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record()
-            kernels[n](c)
+            k.fn(c)
             e1.record()
-            ev[n].append((e0, e1))
+            ev[k.name].append((e0, e1))
     torch.cuda.synchronize()
-    per_kernel_ms = {n: float(np.mean([a.elapsed_time(b) for a, b in ev[n]])) for n in names}
+    per_kernel_ms = {n: float(np.mean([a.elapsed_time(b) for a, b in e])) for n, e in ev.items()}
     return t_total, per_kernel_ms
+
+
+def roofline(k: Kernel, t_s: float, workload: str):
+    gbs = k.nbytes / t_s / 1e9
+    peak_tf = DENSE_PEAK[k.dtype]
+    tf = k.flops / t_s / 1e12
+    if k.flops == 0 or k.nbytes / (HBM_PEAK_GBS * 1e9) >= k.flops / (peak_tf * 1e12):
+        r = dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s", frac=round(gbs / HBM_PEAK_GBS, 4))
+    else:
+        r = dict(bound="mfma", achieved=round(tf, 1), peak=peak_tf, unit="TOP/s" if k.dtype == "i8" else "TFLOP/s",
+                 frac=round(tf / peak_tf, 4))
+    r["traffic"] = measured_traffic(workload, k)
+    r["kernel"] = k.name
+    r["algorithmic_bytes"] = int(k.nbytes)
+    if k.flops:
+        r["algorithmic_flops"] = k.flops
+        r["mfma_frac"] = round(tf / peak_tf, 4)
+    r["hbm_frac"] = round(gbs / HBM_PEAK_GBS, 4)
+    return r
 
 
 def main():
@@ -206,6 +380,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="vit_b16_fc1", choices=sorted(WORKLOADS))
+    ap.add_argument("--n", type=int, default=0, help="tokens N for the llm_proj_* and ffn_* workloads")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense-ref", action="store_true", help="skip timing the dense bf16 GEMM of the same shape")
@@ -214,7 +389,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path shards with no "
-              "communication: by tokens or by output channels, see DESIGN.md)", file=sys.stderr)
+              "communication: by tokens or by output channels)", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
@@ -228,39 +403,22 @@ def main():
     ms_per_step = 1e3 * t_total / args.steps
     value = w["flops"] / (ms_per_step * 1e-3) / 1e12
 
-    dom = w["dominant"]
-    t_dom = per_kernel_ms[dom] * 1e-3
-    achieved_gbs = w["gemm_bytes"] / t_dom / 1e9
-    achieved_tf = w["gemm_flops"] / t_dom / 1e12
-    peak_tf = SPARSE_I8_PEAK_TOPS if w["dtype"] == "i8" else SPARSE_BF16_PEAK_TF
-    ideal_hbm = w["gemm_bytes"] / (HBM_PEAK_GBS * 1e9)
-    ideal_mfma = w["gemm_flops"] / (peak_tf * 1e12)
-    if ideal_hbm >= ideal_mfma:
-        roof = dict(bound="hbm", achieved=round(achieved_gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(achieved_gbs / HBM_PEAK_GBS, 4), traffic=measured_traffic(w))
-    else:
-        roof = dict(bound="mfma", achieved=round(achieved_tf, 1), peak=peak_tf,
-                    unit="TOP/s" if w["dtype"] == "i8" else "TFLOP/s", frac=round(achieved_tf / peak_tf, 4),
-                    traffic=measured_traffic(w))
-    roof["algorithmic_bytes"] = w["gemm_bytes"]
-    roof["kernel"] = dom
-    roof["mfma_frac"] = round(achieved_tf / peak_tf, 4)
-    roof["hbm_frac"] = round(achieved_gbs / HBM_PEAK_GBS, 4)
-
+    by_name = {k.name: k for k in w["kernels"]}
+    dom = max(per_kernel_ms, key=per_kernel_ms.get)
+    roof = roofline(by_name[dom], per_kernel_ms[dom] * 1e-3, w["name"])
     kernels = {}
-    for n, ms in per_kernel_ms.items():
-        kernels[n] = dict(avg_us=round(ms * 1e3, 2))
-    kernels[dom]["tflops_dense_equiv"] = round(achieved_tf, 1)
-    kernels[dom]["gbs_algorithmic"] = round(achieved_gbs, 1)
-    if "prune_compress" in per_kernel_ms:
-        kernels["prune_compress"]["gbs_algorithmic"] = round(w["prune_bytes"] / (per_kernel_ms["prune_compress"] * 1e-3)
-                                                            / 1e9, 1)
+    for k in w["kernels"]:
+        t = per_kernel_ms[k.name] * 1e-3
+        e = dict(avg_us=round(t * 1e6, 2), gbs_algorithmic=round(k.nbytes / t / 1e9, 1))
+        if k.flops:
+            e["tflops_dense_equiv"] = round(2 * k.flops / t / 1e12, 1)
+        kernels[k.name] = e
 
     if not args.no_dense_ref and w.get("dense_ref"):
-        fns = w["dense_ref"]()
-        t_dense = sum(kernel_time_ms(f, w["copies"], args.steps, args.warmup) for f in fns)
+        fn = w["dense_ref"]()
+        t_dense = kernel_time_ms(fn, w["copies"], args.steps, args.warmup)
         kernels["dense_bf16_matmul_same_shape"] = dict(avg_us=round(t_dense * 1e3, 2))
-        kernels[dom]["speedup_vs_dense"] = round(t_dense / per_kernel_ms[dom], 3)
+        kernels["gemm_bf16"]["speedup_vs_dense"] = round(t_dense / per_kernel_ms["gemm_bf16"], 3)
 
     cpu = None
     if not args.no_cpu_baseline:
