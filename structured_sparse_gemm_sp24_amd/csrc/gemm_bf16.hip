@@ -16,8 +16,9 @@
 //
 // This file holds the direct kernel: each wave owns a 16-row x (16*NF)-column tile, takes A and the
 // index straight from global memory and gathers B element by element with bounds checks, so it works
-// for every shape and row pitch. The tiled LDS kernels (gemm_bf16_tiled.hip) take over where their
-// alignment and size conditions hold.
+// for every shape and row pitch. It serves the shapes the others do not take: the few-token kernel
+// (gemm_bf16_skinny.hip, N <= 64) and the LDS-tiled kernel (gemm_bf16_tiled.hip, N > 64), each
+// within its alignment and size conditions.
 #include "sp24_device.h"
 #include "sp24_launch.h"
 
@@ -100,6 +101,7 @@ hipError_t launch_gemm_bf16_direct(const uint16_t* values, const uint8_t* meta, 
 
 hipError_t launch_gemm_bf16(const uint16_t* values, const uint8_t* meta, int64_t M, int64_t K, const uint16_t* X,
                             int64_t N, int64_t ldx, void* Y, bool out_fp32, int64_t ldy, hipStream_t s) {
+    if (gemm_bf16_skinny_ok(K, N, ldx)) return launch_gemm_bf16_skinny(values, meta, M, K, X, N, ldx, Y, out_fp32, ldy, s);
     if (gemm_bf16_tiled_ok(M, K, N, ldx, X))
         return launch_gemm_bf16_tiled(values, meta, M, K, X, N, ldx, Y, out_fp32, ldy, s);
     return launch_gemm_bf16_direct(values, meta, M, K, X, N, ldx, Y, out_fp32, ldy, s);

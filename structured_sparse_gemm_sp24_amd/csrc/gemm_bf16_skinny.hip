@@ -1,0 +1,210 @@
+// Sparse x dense GEMM for few tokens (N <= 64), bf16 in, fp32 accumulate (NVIDIA blog on Ampere
+// structured sparsity, Figure 1; Orin NN design, Chapter 7, section 2.1 Step 3).
+//
+// With N this small the product is bound by streaming the compressed weight (1.125 bytes per dense
+// weight) from HBM once; X is a few KB to a few MB and stays in L2. So the kernel is built to keep
+// many weight bytes in flight and to touch each weight byte once:
+//  - a workgroup owns R consecutive 16-row blocks of the weight and all N columns (NF fragments of
+//    16 columns); its S waves split the K tiles of those blocks into S contiguous ranges;
+//  - a wave walks its range U tiles at a time, double-buffered: the next round's compressed tiles
+//    (one 16-byte value load and one 2-byte index load per lane and block, in smfmac lane order) and
+//    X fragments are requested before the current round's smfmacs;
+//  - the X fragment of a tile (lane = column, 16 k values) is gathered straight from global memory
+//    once per tile and shared by the R blocks; for a unit-pitch vector (N = 1) it is two 16-byte loads;
+//  - at the end the S partial 16 x 16 accumulators of each block are summed through LDS in wave order
+//    (deterministic), rounded if the output is bf16, and stored with bounds checks.
+#include "sp24_device.h"
+#include "sp24_launch.h"
+
+namespace sp24 {
+namespace skinny {
+
+// X fragment for columns 16 f .. 16 f + 15 of tile k0 (smfmac B operand: lane n = r holds
+// k = k0 + 8q + (e & 7) + 32 (e >> 3)); zero past K and past N. The general case reads single
+// elements through a buffer descriptor covering exactly X's extent, so rows past K come back as 0.
+template <bool UNIT>
+__device__ __forceinline__ bf16x16 load_x(const uint16_t* __restrict__ X, __amdgpu_buffer_rsrc_t rx, int64_t ldx,
+                                          int64_t K, int64_t N, int64_t k0, int64_t n, int q) {
+    u32x8 b = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (n < N) {
+        if (UNIT) {
+            // N == 1 with unit pitch: the 16 values are two runs of 8 consecutive elements
+            const int64_t ka = k0 + 8 * q, kb = ka + 32;
+            if (kb + 8 <= K) {
+                const u32x4 lo = *reinterpret_cast<const u32x4*>(X + ka);
+                const u32x4 hi = *reinterpret_cast<const u32x4*>(X + kb);
+                b = u32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            } else {
+#pragma unroll
+                for (int e = 0; e < 16; e += 2) {
+                    const int64_t k = k0 + 8 * q + (e & 7) + 32 * (e >> 3);
+                    const uint32_t v0 = k < K ? X[k] : 0u;
+                    const uint32_t v1 = k + 1 < K ? X[k + 1] : 0u;
+                    b[e >> 1] = v0 | (v1 << 16);
+                }
+            }
+        } else {
+            const uint32_t ld2 = (uint32_t)ldx * 2;
+            const uint32_t o = (uint32_t)(((k0 + 8 * q) * ldx + n) * 2);
+#pragma unroll
+            for (int e = 0; e < 16; e += 2) {
+                const uint32_t oe = o + (uint32_t)((e & 7) + 32 * (e >> 3)) * ld2;
+                const uint32_t v0 = __builtin_amdgcn_raw_buffer_load_b16(rx, (int)oe, 0, 0);
+                const uint32_t v1 = __builtin_amdgcn_raw_buffer_load_b16(rx, (int)(oe + ld2), 0, 0);
+                b[e >> 1] = v0 | (v1 << 16);
+            }
+        }
+    }
+    return __builtin_bit_cast(bf16x16, b);
+}
+
+template <int NF, int R, int U>
+struct Round {
+    u32x4 a[U][R];
+    uint32_t idx[U][R];
+    bf16x16 b[U][NF];
+};
+
+template <int NF, int R, int S, int U, bool UNIT>
+__global__ __launch_bounds__(64 * S) void gemm_bf16_skinny(const uint16_t* __restrict__ vals,
+                                                           const uint8_t* __restrict__ meta, int64_t M, int64_t K,
+                                                           const uint16_t* __restrict__ X, int64_t N, int64_t ldx,
+                                                           void* __restrict__ Y, int out_fp32, int64_t ldy) {
+    __shared__ float red[S * R * NF * 256];
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int r = lane & 15, q = lane >> 4;
+    const int64_t nblocks = (M + 15) / 16;
+    const int64_t b0 = (int64_t)blockIdx.x * R;
+    const int64_t T = (K + 63) / 64;  // compressed tiles per row block
+    const int64_t t0 = T * wave / S, t1 = T * (wave + 1) / S;
+    int nb = (int)(nblocks - b0 < R ? nblocks - b0 : R);
+
+    // tile (b, t): values at ((b * T + t) * 64 + lane) * 16 bytes, index at ((b * T + t) * 64 + lane) * 2
+    const u32x4* vt = reinterpret_cast<const u32x4*>(vals) + b0 * T * 64 + lane;
+    const uint16_t* mt = reinterpret_cast<const uint16_t*>(meta) + b0 * T * 64 + lane;
+    // X's extent in bytes: (K - 1) rows of pitch ldx plus N elements (below 2^31, checked on the host)
+    const __amdgpu_buffer_rsrc_t rx =
+        __builtin_amdgcn_make_buffer_rsrc((void*)X, (short)0, (int)(((K - 1) * ldx + N) * 2), 0x00020000);
+
+    f32x4 acc[R][NF];
+#pragma unroll
+    for (int j = 0; j < R; j++)
+#pragma unroll
+        for (int f = 0; f < NF; f++) acc[j][f] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto issue = [&](Round<NF, R, U>& rd, int64_t t) {
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            const int64_t tt = t + u;
+            const bool ok = tt < t1;
+#pragma unroll
+            for (int j = 0; j < R; j++) {
+                if (ok && j < nb) {
+                    rd.a[u][j] = __builtin_nontemporal_load(vt + (j * T + tt) * 64);
+                    rd.idx[u][j] = __builtin_nontemporal_load(mt + (j * T + tt) * 64);
+                } else {
+                    rd.a[u][j] = u32x4{0, 0, 0, 0};
+                    rd.idx[u][j] = 0x4444u;
+                }
+            }
+#pragma unroll
+            for (int f = 0; f < NF; f++) {
+                if (ok)
+                    rd.b[u][f] = load_x<UNIT>(X, rx, ldx, K, N, 64 * tt, 16 * f + r, q);
+                else
+                    rd.b[u][f] = __builtin_bit_cast(bf16x16, u32x8{0, 0, 0, 0, 0, 0, 0, 0});
+            }
+        }
+    };
+    auto compute = [&](const Round<NF, R, U>& rd) {
+#pragma unroll
+        for (int u = 0; u < U; u++)
+#pragma unroll
+            for (int j = 0; j < R; j++)
+#pragma unroll
+                for (int f = 0; f < NF; f++)
+                    acc[j][f] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, rd.a[u][j]),
+                                                                          rd.b[u][f], acc[j][f], (int)rd.idx[u][j], 0,
+                                                                          0);
+    };
+
+    if (t0 < t1) {
+        Round<NF, R, U> cur, nxt;
+        issue(cur, t0);
+        int64_t t = t0;
+        for (; t + U < t1; t += U) {
+            issue(nxt, t + U);
+            compute(cur);
+            cur = nxt;
+        }
+        compute(cur);
+    }
+
+    // sum the S partial tiles of each block in wave order
+#pragma unroll
+    for (int j = 0; j < R; j++)
+#pragma unroll
+        for (int f = 0; f < NF; f++)
+#pragma unroll
+            for (int i = 0; i < 4; i++) red[((wave * R + j) * NF + f) * 256 + (4 * q + i) * 16 + r] = acc[j][f][i];
+    __syncthreads();
+    for (int e = threadIdx.x; e < R * NF * 256; e += 64 * S) {
+        const int j = e / (NF * 256), f = (e / 256) % NF, row = (e / 16) % 16, col = e % 16;
+        float s = 0.f;
+#pragma unroll 4
+        for (int w = 0; w < S; w++) s += red[((w * R + j) * NF + f) * 256 + row * 16 + col];
+        const int64_t m = (b0 + j) * 16 + row, n = 16 * f + col;
+        if (j < nb && m < M && n < N) {
+            if (out_fp32)
+                reinterpret_cast<float*>(Y)[m * ldy + n] = s;
+            else
+                reinterpret_cast<uint16_t*>(Y)[m * ldy + n] = f32_to_bf16_rne(s);
+        }
+    }
+}
+
+template <int NF, int R, int S, int U>
+hipError_t launch(const uint16_t* values, const uint8_t* meta, int64_t M, int64_t K, const uint16_t* X, int64_t N,
+                  int64_t ldx, void* Y, bool out_fp32, int64_t ldy, hipStream_t s) {
+    const unsigned grid = (unsigned)(((M + 15) / 16 + R - 1) / R);
+    if constexpr (NF == 1) {
+        if (N == 1 && ldx == 1) {
+            hipLaunchKernelGGL((gemm_bf16_skinny<NF, R, S, U, true>), dim3(grid), dim3(64 * S), 0, s, values, meta, M, K,
+                               X, N, ldx, Y, (int)out_fp32, ldy);
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((gemm_bf16_skinny<NF, R, S, U, false>), dim3(grid), dim3(64 * S), 0, s, values, meta, M, K, X,
+                       N, ldx, Y, (int)out_fp32, ldy);
+    return hipGetLastError();
+}
+
+}  // namespace skinny
+
+// Row blocks per workgroup: enough workgroups to cover the chip (about 256 or more), as many blocks
+// per workgroup as that allows (each X fragment is then shared by more weight tiles).
+bool gemm_bf16_skinny_ok(int64_t K, int64_t N, int64_t ldx) {
+    // 32-bit element offsets for every row the tiles touch (K padded to 64, plus one tile)
+    return N <= 64 && (K + 128) * ldx * 2 < ((int64_t)1 << 31);
+}
+
+hipError_t launch_gemm_bf16_skinny(const uint16_t* values, const uint8_t* meta, int64_t M, int64_t K, const uint16_t* X,
+                                   int64_t N, int64_t ldx, void* Y, bool out_fp32, int64_t ldy, hipStream_t s) {
+    const int64_t nblocks = (M + 15) / 16;
+    const int R = nblocks >= 1024 ? 4 : nblocks >= 512 ? 2 : 1;
+    if (N <= 16) {
+        if (R == 4) return skinny::launch<1, 4, 16, 1>(values, meta, M, K, X, N, ldx, Y, out_fp32, ldy, s);
+        if (R == 2) return skinny::launch<1, 2, 16, 2>(values, meta, M, K, X, N, ldx, Y, out_fp32, ldy, s);
+        return skinny::launch<1, 1, 16, 2>(values, meta, M, K, X, N, ldx, Y, out_fp32, ldy, s);
+    }
+    if (N <= 32) {
+        if (R == 4) return skinny::launch<2, 4, 8, 1>(values, meta, M, K, X, N, ldx, Y, out_fp32, ldy, s);
+        if (R == 2) return skinny::launch<2, 2, 16, 1>(values, meta, M, K, X, N, ldx, Y, out_fp32, ldy, s);
+        return skinny::launch<2, 1, 16, 1>(values, meta, M, K, X, N, ldx, Y, out_fp32, ldy, s);
+    }
+    if (R == 4) return skinny::launch<4, 4, 8, 1>(values, meta, M, K, X, N, ldx, Y, out_fp32, ldy, s);
+    if (R == 2) return skinny::launch<4, 2, 8, 1>(values, meta, M, K, X, N, ldx, Y, out_fp32, ldy, s);
+    return skinny::launch<4, 1, 8, 1>(values, meta, M, K, X, N, ldx, Y, out_fp32, ldy, s);
+}
+
+}  // namespace sp24

@@ -17,6 +17,10 @@ hipError_t launch_decompress(const void* values, const uint8_t* meta, int dtype,
 hipError_t launch_gemm_bf16(const uint16_t* values, const uint8_t* meta, int64_t M, int64_t K, const uint16_t* X,
                             int64_t N, int64_t ldx, void* Y, bool out_fp32, int64_t ldy, hipStream_t s);
 
+bool gemm_bf16_skinny_ok(int64_t K, int64_t N, int64_t ldx);
+hipError_t launch_gemm_bf16_skinny(const uint16_t* values, const uint8_t* meta, int64_t M, int64_t K, const uint16_t* X,
+                                   int64_t N, int64_t ldx, void* Y, bool out_fp32, int64_t ldy, hipStream_t s);
+
 bool gemm_bf16_tiled_ok(int64_t M, int64_t K, int64_t N, int64_t ldx, const void* X);
 hipError_t launch_gemm_bf16_tiled(const uint16_t* values, const uint8_t* meta, int64_t M, int64_t K, const uint16_t* X,
                                   int64_t N, int64_t ldx, void* Y, bool out_fp32, int64_t ldy, hipStream_t s);

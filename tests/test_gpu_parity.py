@@ -163,6 +163,15 @@ GEMM_SHAPES = [
     (70, 512, 8, 8, 8),
     (256, 256, 64, 64, 64),
     (512, 768, 520, 520, 520),
+    # few-token kernel (N <= 64): 1, 2 and 4 row blocks per workgroup (M >= 8192 and >= 16384 rows),
+    # one to four 16-column fragments, the unit-pitch vector, a strided vector, one tile of K, K tails
+    (9000, 80, 1, 1, 1),
+    (600, 4096, 1, 3, 1),
+    (8200, 256, 5, 5, 5),
+    (16400, 128, 24, 32, 24),
+    (16400, 192, 40, 40, 40),
+    (100, 16, 33, 40, 33),
+    (1040, 1088, 64, 64, 64),
     # tiled kernel (K % 64 == 0, N > 64): ragged M and N, several tiles, padded pitches
     (1000, 512, 777, 784, 777),
     (64, 64, 65, 72, 65),
