@@ -9,8 +9,10 @@
 //  - a wave walks its range U tiles at a time, double-buffered: the next round's compressed tiles
 //    (one 16-byte value load and one 2-byte index load per lane and block, in smfmac lane order) and
 //    X fragments are requested before the current round's smfmacs;
-//  - the X fragment of a tile (lane = column, 16 k values) is gathered straight from global memory
-//    once per tile and shared by the R blocks; for a unit-pitch vector (N = 1) it is two 16-byte loads;
+//  - the X fragments of a tile (lane = column, 16 k values) are built once per tile and shared by the
+//    R blocks: for a unit-pitch vector (N = 1) from two 16-byte loads; when rows of X are 16-byte
+//    aligned and N is a multiple of 8, by staging the 64 x 16 NF tile through a wave-private LDS slot
+//    (16-byte loads, ds_write_b128, then ds_read_b64_tr_b16); otherwise element by element;
 //  - at the end the S partial 16 x 16 accumulators of each block are summed through LDS in wave order
 //    (deterministic), rounded if the output is bf16, and stored with bounds checks.
 #include "sp24_device.h"
@@ -58,19 +60,39 @@ __device__ __forceinline__ bf16x16 load_x(const uint16_t* __restrict__ X, __amdg
     return __builtin_bit_cast(bf16x16, b);
 }
 
-template <int NF, int R, int U>
+enum { X_ELEMENTS = 0, X_UNIT_VECTOR = 1, X_STAGED = 2 };
+
+// Staged X tile (64 rows x 16 NF bf16) in a wave's LDS slot: row pitch P = 32 NF bytes plus a gap of
+// G bytes after every 8 rows. The gap puts the 16 rows x 32 bytes of each transposing read (rows
+// 8q + {0..3}, q = 0..3) into 8 distinct 32-byte bank groups, and every read of a fragment is then
+// one lane address plus immediates (+4 rows, +32 rows) -- checked by enumeration for NF = 1, 2, 4.
+template <int NF>
+struct XTile {
+    static constexpr int P = 32 * NF;
+    static constexpr int G = NF == 1 ? 64 : 32;
+    static constexpr int GROUP = 8 * P + G;
+    static constexpr int BYTES = 8 * GROUP;
+    static constexpr __device__ int row(int k) { return (k >> 3) * GROUP + (k & 7) * P; }
+};
+
+template <int NF, int R, int U, int XMODE>
 struct Round {
     u32x4 a[U][R];
     uint32_t idx[U][R];
     bf16x16 b[U][NF];
+    u32x4 xs[XMODE == X_STAGED ? U : 1][2 * NF];  // staged X chunks (16 bytes each) of every tile
 };
 
-template <int NF, int R, int S, int U, bool UNIT>
+template <int NF, int R, int S, int U, int XMODE>
 __global__ __launch_bounds__(64 * S) void gemm_bf16_skinny(const uint16_t* __restrict__ vals,
                                                            const uint8_t* __restrict__ meta, int64_t M, int64_t K,
                                                            const uint16_t* __restrict__ X, int64_t N, int64_t ldx,
                                                            void* __restrict__ Y, int out_fp32, int64_t ldy) {
-    __shared__ float red[S * R * NF * 256];
+    // the wave-private X slots during the K loop, the reduction buffer after it
+    constexpr int RED_BYTES = S * R * NF * 256 * 4;
+    constexpr int X_BYTES = XMODE == X_STAGED ? S * XTile<NF>::BYTES : 0;
+    __shared__ __attribute__((aligned(16))) char smem[RED_BYTES > X_BYTES ? RED_BYTES : X_BYTES];
+    float* const red = reinterpret_cast<float*>(smem);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int r = lane & 15, q = lane >> 4;
     const int64_t nblocks = (M + 15) / 16;
@@ -92,7 +114,11 @@ __global__ __launch_bounds__(64 * S) void gemm_bf16_skinny(const uint16_t* __res
 #pragma unroll
         for (int f = 0; f < NF; f++) acc[j][f] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    auto issue = [&](Round<NF, R, U>& rd, int64_t t) {
+    char* const xslot = smem + wave * XTile<NF>::BYTES;
+    // lane address of the transposing reads of fragment f (t = 0): row 8q + r/4, columns 16 f + 4 (r % 4)
+    const int xrd = XTile<NF>::row(8 * q + (r >> 2)) + 2 * (4 * (r & 3));
+
+    auto issue = [&](Round<NF, R, U, XMODE>& rd, int64_t t) {
 #pragma unroll
         for (int u = 0; u < U; u++) {
             const int64_t tt = t + u;
@@ -107,18 +133,54 @@ __global__ __launch_bounds__(64 * S) void gemm_bf16_skinny(const uint16_t* __res
                     rd.idx[u][j] = 0x4444u;
                 }
             }
+            if constexpr (XMODE == X_STAGED) {
+                // chunk c = lane + 64 i of the tile: row c / (2 NF), 8 columns at 8 (c % (2 NF)); chunks
+                // wholly past N (N is a multiple of 8 here) reread the row's first chunk, rows past K
+                // are out of the descriptor's range and read as zeros
 #pragma unroll
-            for (int f = 0; f < NF; f++) {
-                if (ok)
-                    rd.b[u][f] = load_x<UNIT>(X, rx, ldx, K, N, 64 * tt, 16 * f + r, q);
-                else
-                    rd.b[u][f] = __builtin_bit_cast(bf16x16, u32x8{0, 0, 0, 0, 0, 0, 0, 0});
+                for (int i = 0; i < 2 * NF; i++) {
+                    const int c = lane + 64 * i, row = c / (2 * NF), col = 8 * (c % (2 * NF));
+                    const int64_t k = 64 * tt + row;
+                    const uint32_t off = (uint32_t)((k * ldx + (col < N ? col : 0)) * 2);
+                    rd.xs[u][i] = ok ? __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, (int)off, 0, 0))
+                                     : u32x4{0, 0, 0, 0};
+                }
+            } else {
+#pragma unroll
+                for (int f = 0; f < NF; f++) {
+                    if (ok)
+                        rd.b[u][f] = load_x<XMODE == X_UNIT_VECTOR>(X, rx, ldx, K, N, 64 * tt, 16 * f + r, q);
+                    else
+                        rd.b[u][f] = __builtin_bit_cast(bf16x16, u32x8{0, 0, 0, 0, 0, 0, 0, 0});
+                }
             }
         }
     };
-    auto compute = [&](const Round<NF, R, U>& rd) {
+    auto compute = [&](Round<NF, R, U, XMODE>& rd) {
 #pragma unroll
-        for (int u = 0; u < U; u++)
+        for (int u = 0; u < U; u++) {
+            if constexpr (XMODE == X_STAGED) {
+                // write the tile into the slot (the previous tile's reads of it have completed: their
+                // results fed the previous smfmacs), then read the NF fragments back transposed
+#pragma unroll
+                for (int i = 0; i < 2 * NF; i++) {
+                    const int c = lane + 64 * i, row = c / (2 * NF), col = 8 * (c % (2 * NF));
+                    *reinterpret_cast<u32x4*>(xslot + XTile<NF>::row(row) + 2 * col) = rd.xs[u][i];
+                }
+#pragma unroll
+                for (int f = 0; f < NF; f++) {
+                    u32x8 b;
+#pragma unroll
+                    for (int t = 0; t < 4; t++) {
+                        const int imm = XTile<NF>::row(4 * (t & 1) + 32 * (t >> 1)) + 32 * f;
+                        const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (__attribute__((address_space(3))) i16x4*)(xslot + xrd + imm));
+                        b[2 * t] = (uint16_t)v[0] | ((uint32_t)(uint16_t)v[1] << 16);
+                        b[2 * t + 1] = (uint16_t)v[2] | ((uint32_t)(uint16_t)v[3] << 16);
+                    }
+                    rd.b[u][f] = __builtin_bit_cast(bf16x16, b);
+                }
+            }
 #pragma unroll
             for (int j = 0; j < R; j++)
 #pragma unroll
@@ -126,10 +188,11 @@ __global__ __launch_bounds__(64 * S) void gemm_bf16_skinny(const uint16_t* __res
                     acc[j][f] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, rd.a[u][j]),
                                                                           rd.b[u][f], acc[j][f], (int)rd.idx[u][j], 0,
                                                                           0);
+        }
     };
 
     if (t0 < t1) {
-        Round<NF, R, U> cur, nxt;
+        Round<NF, R, U, XMODE> cur, nxt;
         issue(cur, t0);
         int64_t t = t0;
         for (; t + U < t1; t += U) {
@@ -141,6 +204,7 @@ __global__ __launch_bounds__(64 * S) void gemm_bf16_skinny(const uint16_t* __res
     }
 
     // sum the S partial tiles of each block in wave order
+    if constexpr (XMODE == X_STAGED) __syncthreads();  // the X slots become the reduction buffer
 #pragma unroll
     for (int j = 0; j < R; j++)
 #pragma unroll
@@ -169,41 +233,50 @@ hipError_t launch(const uint16_t* values, const uint8_t* meta, int64_t M, int64_
     const unsigned grid = (unsigned)(((M + 15) / 16 + R - 1) / R);
     if constexpr (NF == 1) {
         if (N == 1 && ldx == 1) {
-            hipLaunchKernelGGL((gemm_bf16_skinny<NF, R, S, U, true>), dim3(grid), dim3(64 * S), 0, s, values, meta, M, K,
-                               X, N, ldx, Y, (int)out_fp32, ldy);
+            hipLaunchKernelGGL((gemm_bf16_skinny<NF, R, S, U, X_UNIT_VECTOR>), dim3(grid), dim3(64 * S), 0, s, values,
+                               meta, M, K, X, N, ldx, Y, (int)out_fp32, ldy);
             return hipGetLastError();
         }
     }
-    hipLaunchKernelGGL((gemm_bf16_skinny<NF, R, S, U, false>), dim3(grid), dim3(64 * S), 0, s, values, meta, M, K, X,
-                       N, ldx, Y, (int)out_fp32, ldy);
+    if (ldx % 8 == 0 && N % 8 == 0)
+        hipLaunchKernelGGL((gemm_bf16_skinny<NF, R, S, U, X_STAGED>), dim3(grid), dim3(64 * S), 0, s, values, meta, M,
+                           K, X, N, ldx, Y, (int)out_fp32, ldy);
+    else
+        hipLaunchKernelGGL((gemm_bf16_skinny<NF, R, S, U, X_ELEMENTS>), dim3(grid), dim3(64 * S), 0, s, values, meta, M,
+                           K, X, N, ldx, Y, (int)out_fp32, ldy);
     return hipGetLastError();
 }
 
 }  // namespace skinny
 
-// Row blocks per workgroup: enough workgroups to cover the chip (about 256 or more), as many blocks
-// per workgroup as that allows (each X fragment is then shared by more weight tiles).
 bool gemm_bf16_skinny_ok(int64_t K, int64_t N, int64_t ldx) {
     // 32-bit element offsets for every row the tiles touch (K padded to 64, plus one tile)
     return N <= 64 && (K + 128) * ldx * 2 < ((int64_t)1 << 31);
 }
 
+// Row blocks per workgroup (R), waves per workgroup (S) and tiles per round (U) by size: about 256 or
+// more workgroups, R as large as that allows (each X fragment is then shared by more weight tiles);
+// the unit-vector case reads its X fragment cheaply and prefers more, smaller workgroups. Chosen by
+// measurement on MI355X over R in {1, 2, 4}, S in {4, 8, 16}, U in {1, 2, 4}.
 hipError_t launch_gemm_bf16_skinny(const uint16_t* values, const uint8_t* meta, int64_t M, int64_t K, const uint16_t* X,
                                    int64_t N, int64_t ldx, void* Y, bool out_fp32, int64_t ldy, hipStream_t s) {
-    const int64_t nblocks = (M + 15) / 16;
-    const int R = nblocks >= 1024 ? 4 : nblocks >= 512 ? 2 : 1;
+    const int64_t nb = (M + 15) / 16;
+    if (N == 1 && ldx == 1) {
+        if (nb >= 1024) return skinny::launch<1, 4, 16, 1>(values, meta, M, K, X, N, ldx, Y, out_fp32, ldy, s);
+        if (nb >= 512) return skinny::launch<1, 2, 4, 2>(values, meta, M, K, X, N, ldx, Y, out_fp32, ldy, s);
+        return skinny::launch<1, 1, 8, 4>(values, meta, M, K, X, N, ldx, Y, out_fp32, ldy, s);
+    }
     if (N <= 16) {
-        if (R == 4) return skinny::launch<1, 4, 16, 1>(values, meta, M, K, X, N, ldx, Y, out_fp32, ldy, s);
-        if (R == 2) return skinny::launch<1, 2, 16, 2>(values, meta, M, K, X, N, ldx, Y, out_fp32, ldy, s);
+        if (nb >= 512) return skinny::launch<1, 4, 16, 1>(values, meta, M, K, X, N, ldx, Y, out_fp32, ldy, s);
         return skinny::launch<1, 1, 16, 2>(values, meta, M, K, X, N, ldx, Y, out_fp32, ldy, s);
     }
     if (N <= 32) {
-        if (R == 4) return skinny::launch<2, 4, 8, 1>(values, meta, M, K, X, N, ldx, Y, out_fp32, ldy, s);
-        if (R == 2) return skinny::launch<2, 2, 16, 1>(values, meta, M, K, X, N, ldx, Y, out_fp32, ldy, s);
+        if (nb >= 1024) return skinny::launch<2, 4, 8, 1>(values, meta, M, K, X, N, ldx, Y, out_fp32, ldy, s);
+        if (nb >= 512) return skinny::launch<2, 2, 16, 1>(values, meta, M, K, X, N, ldx, Y, out_fp32, ldy, s);
         return skinny::launch<2, 1, 16, 1>(values, meta, M, K, X, N, ldx, Y, out_fp32, ldy, s);
     }
-    if (R == 4) return skinny::launch<4, 4, 8, 1>(values, meta, M, K, X, N, ldx, Y, out_fp32, ldy, s);
-    if (R == 2) return skinny::launch<4, 2, 8, 1>(values, meta, M, K, X, N, ldx, Y, out_fp32, ldy, s);
+    if (nb >= 1024) return skinny::launch<4, 4, 8, 1>(values, meta, M, K, X, N, ldx, Y, out_fp32, ldy, s);
+    if (nb >= 512) return skinny::launch<4, 2, 8, 1>(values, meta, M, K, X, N, ldx, Y, out_fp32, ldy, s);
     return skinny::launch<4, 1, 8, 1>(values, meta, M, K, X, N, ldx, Y, out_fp32, ldy, s);
 }
 

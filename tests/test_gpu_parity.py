@@ -172,6 +172,9 @@ GEMM_SHAPES = [
     (16400, 192, 40, 40, 40),
     (100, 16, 33, 40, 33),
     (1040, 1088, 64, 64, 64),
+    (2000, 208, 16, 16, 16),
+    (300, 320, 8, 16, 8),
+    (12000, 4096, 1, 1, 1),
     # tiled kernel (K % 64 == 0, N > 64): ragged M and N, several tiles, padded pitches
     (1000, 512, 777, 784, 777),
     (64, 64, 65, 72, 65),
