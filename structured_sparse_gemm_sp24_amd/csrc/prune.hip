@@ -1,11 +1,13 @@
 // 2:4 prune + compress, and decompress (Orin NN design, Chapter 7, section 2.1 Steps 1-2; NVIDIA
 // blog on Ampere structured sparsity, Figure 1).
 //
-// Both kernels are HBM streams. One thread owns one 16-column chunk of a row (4 groups): it reads
-// the chunk with 16-byte loads, scores and selects in registers, and writes 8 values (one 16-byte
-// store for 16-bit types) plus the chunk's 16 metadata bits (2 bytes) into the tiled compressed
-// layout (16-row tiles in the order of the sparse MFMA operand). Consecutive threads own consecutive
-// chunks of a row, so loads are contiguous runs; each store lands in a 16-byte quarter of a tile.
+// Both kernels are HBM streams. Prune/compress is organized by compressed tile (16 rows x 64 bytes
+// of values, in the lane order of the sparse MFMA operand): lane l of a wave owns slot l of a tile,
+// i.e. row l % 16 and dense columns [KT/4 * (l / 16), +KT/4) of the tile (KT = 128 / value size).
+// It loads those columns (16-byte loads; several tiles per lane in flight), scores and selects in
+// registers, and writes its 16 value bytes and 4 / value-size metadata bytes, so every wave writes
+// whole 1 KB value tiles and whole metadata tiles with contiguous stores. Decompress keeps one thread
+// per 16-column chunk of a row.
 //
 // Selection is a knockout over the group: (0 vs 1) and (2 vs 3), then the two winners; the
 // runner-up is the better of the two elements that lost directly to the champion. "a beats b" for
@@ -19,53 +21,16 @@ namespace sp24 {
 
 enum { DT_BF16 = 0, DT_FP16 = 1, DT_FP32 = 2, DT_I8 = 3 };
 
-// Element storage for one 16-column chunk.
-template <int DT> struct Chunk;
-template <> struct Chunk<DT_BF16> {
-    typedef uint16_t T;
-    T e[16];
-    __device__ void load(const void* p) {
-        const u32x4* q = reinterpret_cast<const u32x4*>(p);
-        u32x4 a = __builtin_nontemporal_load(q), b = __builtin_nontemporal_load(q + 1);
-        const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-        for (int i = 0; i < 8; i++) { e[2 * i] = (T)(w[i] & 0xFFFF); e[2 * i + 1] = (T)(w[i] >> 16); }
-    }
-    __device__ uint32_t mag_key(int i) const { return e[i] & 0x7FFFu; }
-    __device__ float abs_f32(int i) const { return bf16_to_f32(e[i] & 0x7FFFu); }
-};
-template <> struct Chunk<DT_FP16> : Chunk<DT_BF16> {
-    __device__ float abs_f32(int i) const { return f16_to_f32(e[i] & 0x7FFFu); }
-};
-template <> struct Chunk<DT_FP32> {
-    typedef uint32_t T;
-    T e[16];
-    __device__ void load(const void* p) {
-        const u32x4* q = reinterpret_cast<const u32x4*>(p);
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            u32x4 a = __builtin_nontemporal_load(q + i);
-            e[4 * i] = a.x; e[4 * i + 1] = a.y; e[4 * i + 2] = a.z; e[4 * i + 3] = a.w;
-        }
-    }
-    __device__ uint32_t mag_key(int i) const { return e[i] & 0x7FFFFFFFu; }
-    __device__ float abs_f32(int i) const { return __uint_as_float(e[i] & 0x7FFFFFFFu); }
-};
-template <> struct Chunk<DT_I8> {
-    typedef uint8_t T;
-    T e[16];
-    __device__ void load(const void* p) {
-        u32x4 a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-        const uint32_t w[4] = {a.x, a.y, a.z, a.w};
-#pragma unroll
-        for (int i = 0; i < 16; i++) e[i] = (T)((w[i >> 2] >> (8 * (i & 3))) & 0xFF);
-    }
-    __device__ uint32_t mag_key(int i) const {
-        int v = (int)(int8_t)e[i];
-        return (uint32_t)(v < 0 ? -v : v);
-    }
-    __device__ float abs_f32(int) const { return 0.f; }  // Wanda is not offered for int8
-};
+// Storage type of one weight element (bit pattern).
+template <int DT> struct Elem { typedef uint16_t T; };
+template <> struct Elem<DT_FP32> { typedef uint32_t T; };
+template <> struct Elem<DT_I8> { typedef uint8_t T; };
+
+// v[i] for i in 0..3 by selects (a register array indexed at run time would go to scratch).
+template <typename T>
+__device__ __forceinline__ T pick4(T v0, T v1, T v2, T v3, int i) {
+    return i == 0 ? v0 : (i == 1 ? v1 : (i == 2 ? v2 : v3));
+}
 
 // Kept positions (lo < hi) of the group whose keys are k[0..3].
 __device__ __forceinline__ void knockout_top2(const uint32_t k[4], int& lo, int& hi) {
@@ -88,84 +53,109 @@ __device__ __forceinline__ void knockout_top2(const uint32_t k[4], int& lo, int&
 
 template <int DT> constexpr int esize() { return DT == DT_FP32 ? 4 : (DT == DT_I8 ? 1 : 2); }
 
-// One thread per 16-column chunk c of padded row i (Mp x Kp/16 chunks, Kp/KT tiles per row). Chunks
-// outside the M x K weight write the padding (values 0, metadata nibbles 0x4).
-template <int DT, int VOUT, bool WANDA>
+// Workgroup = 4 waves x TPW tiles of one 16-row block: wave w takes tiles t0 + w + 4 i, i < TPW.
+// Slots outside the M x K weight write the padding (values 0, metadata nibbles 0x4).
+template <int DT, int VOUT, bool WANDA, int TPW>
 __global__ __launch_bounds__(256) void prune_compress_kernel(const void* __restrict__ W, int64_t ldw, int64_t M,
-                                                             int64_t K, uint32_t chunks_per_row, uint32_t total_chunks,
-                                                             int64_t tiles_per_row, const float* __restrict__ norms,
-                                                             void* __restrict__ values, uint8_t* __restrict__ meta) {
-    const uint32_t t = blockIdx.x * 256u + threadIdx.x;
-    if (t >= total_chunks) return;
-    const uint32_t row = t / chunks_per_row, c = t - row * chunks_per_row;
+                                                             int64_t K, int64_t tiles, int64_t groups_x,
+                                                             const float* __restrict__ norms, void* __restrict__ values,
+                                                             uint8_t* __restrict__ meta) {
     constexpr int isz = esize<DT>(), vsz = esize<VOUT>();
-    typename Chunk<DT>::T kept[8];
-    uint32_t mbits = 0x4444u;
-    if (row < M && 16 * (int64_t)c < K) {
-        Chunk<DT> x;
-        x.load(reinterpret_cast<const char*>(W) + ((int64_t)row * ldw + 16 * (int64_t)c) * isz);
-        float nrm[16];
-        if (WANDA) {
-            const float4* np = reinterpret_cast<const float4*>(norms + 16 * (int64_t)c);
+    constexpr int KT = 128 / vsz;       // dense columns per tile
+    constexpr int SPAN = KT / 4;        // dense columns per lane: 16 (2-byte values), 32 (int8), 8 (fp32)
+    constexpr int NG = SPAN / 4;        // groups per lane
+    constexpr int MB = 4 / vsz;         // metadata bytes per lane
+    typedef typename Elem<DT>::T T;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r = lane & 15, qq = lane >> 4;
+    const int64_t b = blockIdx.x / groups_x;
+    const int64_t tx = blockIdx.x - b * groups_x;
+    const int64_t row = 16 * b + r;
+    const bool row_ok = row < M;
+    const char* wrow = reinterpret_cast<const char*>(W) + row * ldw * isz;
+
+    // load every tile first (TPW x SPAN elements per lane)
+    T x[TPW][SPAN];
 #pragma unroll
-            for (int i = 0; i < 4; i++) {
-                float4 v = np[i];
-                nrm[4 * i] = v.x; nrm[4 * i + 1] = v.y; nrm[4 * i + 2] = v.z; nrm[4 * i + 3] = v.w;
+    for (int i = 0; i < TPW; i++) {
+        const int64_t t = tx * 4 * TPW + wave + 4 * i;
+        const int64_t c0 = t * KT + SPAN * qq;
+#pragma unroll
+        for (int h = 0; h < (SPAN * isz) / 16; h++) {  // 16-byte pieces of the lane's span
+            constexpr int PER = 16 / isz;                // elements per piece
+            const int64_t c = c0 + PER * h;
+            u32x4 v = u32x4{0, 0, 0, 0};
+            if (row_ok && t < tiles && c < K) v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wrow + c * isz));
+#pragma unroll
+            for (int e = 0; e < PER; e++) {
+                if (isz == 4) x[i][PER * h + e] = (T)v[e];
+                if (isz == 2) x[i][PER * h + e] = (T)((v[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+                if (isz == 1) x[i][PER * h + e] = (T)((v[e >> 2] >> (8 * (e & 3))) & 0xFFu);
             }
         }
-        mbits = 0;
+    }
 #pragma unroll
-        for (int g = 0; g < 4; g++) {
-            uint32_t key[4];
+    for (int i = 0; i < TPW; i++) {
+        const int64_t t = tx * 4 * TPW + wave + 4 * i;
+        if (t >= tiles) break;
+        const int64_t c0 = t * KT + SPAN * qq;
+        T kept[2 * NG];
+        uint32_t mbits = 0;
 #pragma unroll
-            for (int i = 0; i < 4; i++) {
-                if (WANDA)
-                    key[i] = __float_as_uint(__fmul_rn(x.abs_f32(4 * g + i), nrm[4 * g + i])) & 0x7FFFFFFFu;
-                else
-                    key[i] = x.mag_key(4 * g + i);
+        for (int g = 0; g < NG; g++) {
+            const int64_t c = c0 + 4 * g;
+            if (row_ok && c < K) {
+                uint32_t key[4];
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const T v = x[i][4 * g + e];
+                    if (WANDA) {
+                        float a;
+                        if (DT == DT_FP32) a = __uint_as_float((uint32_t)v & 0x7FFFFFFFu);
+                        else if (DT == DT_FP16) a = f16_to_f32((uint16_t)(v & 0x7FFFu));
+                        else a = bf16_to_f32((uint16_t)(v & 0x7FFFu));
+                        key[e] = __float_as_uint(__fmul_rn(a, norms[c + e])) & 0x7FFFFFFFu;
+                    } else if (DT == DT_I8) {
+                        const int sv = (int)(int8_t)v;
+                        key[e] = (uint32_t)(sv < 0 ? -sv : sv);
+                    } else {
+                        key[e] = (uint32_t)v & (DT == DT_FP32 ? 0x7FFFFFFFu : 0x7FFFu);
+                    }
+                }
+                int lo, hi;
+                knockout_top2(key, lo, hi);
+                mbits |= (uint32_t)(lo | (hi << 2)) << (4 * g);
+                kept[2 * g] = pick4(x[i][4 * g], x[i][4 * g + 1], x[i][4 * g + 2], x[i][4 * g + 3], lo);
+                kept[2 * g + 1] = pick4(x[i][4 * g], x[i][4 * g + 1], x[i][4 * g + 2], x[i][4 * g + 3], hi);
+            } else {
+                mbits |= 0x4u << (4 * g);
+                kept[2 * g] = 0;
+                kept[2 * g + 1] = 0;
             }
-            int lo, hi;
-            knockout_top2(key, lo, hi);
-            mbits |= (uint32_t)(lo | (hi << 2)) << (4 * g);
-            kept[2 * g] = x.e[4 * g + lo];
-            kept[2 * g + 1] = x.e[4 * g + hi];
         }
-    } else {
+        // values: this lane's 16 bytes of tile (b, t); metadata: its MB bytes of the metadata tile
+        char* vt = reinterpret_cast<char*>(values) + (b * tiles + t) * 1024 + 16 * lane;
+        uint8_t* mt = meta + (b * tiles + t) * (64 * MB) + MB * lane;
+        if (VOUT == DT_FP32) {
+            *reinterpret_cast<uint4*>(vt) = make_uint4(kept[0], kept[1], kept[2], kept[3]);
+        } else if (VOUT == DT_I8) {
+            uint32_t w[4];
 #pragma unroll
-        for (int i = 0; i < 8; i++) kept[i] = 0;
-    }
-    // values: 8 kept values = 8 * vsz bytes at byte 8 * vsz * c of the compressed row
-    char* vbase = reinterpret_cast<char*>(values);
-    const int64_t vb = 8 * vsz * (int64_t)c;
-    if (VOUT == DT_FP32) {  // two whole 16-byte quarters
-        *reinterpret_cast<uint4*>(vbase + tiled_offset<64>(row, vb, tiles_per_row)) =
-            make_uint4(kept[0], kept[1], kept[2], kept[3]);
-        *reinterpret_cast<uint4*>(vbase + tiled_offset<64>(row, vb + 16, tiles_per_row)) =
-            make_uint4(kept[4], kept[5], kept[6], kept[7]);
-    } else if (VOUT == DT_I8) {  // half of a quarter
-        uint2 v;
-        v.x = (uint32_t)kept[0] | ((uint32_t)kept[1] << 8) | ((uint32_t)kept[2] << 16) | ((uint32_t)kept[3] << 24);
-        v.y = (uint32_t)kept[4] | ((uint32_t)kept[5] << 8) | ((uint32_t)kept[6] << 16) | ((uint32_t)kept[7] << 24);
-        *reinterpret_cast<uint2*>(vbase + tiled_offset<64>(row, vb, tiles_per_row)) = v;
-    } else {  // 16-bit values: one quarter; bf16/fp16 bit copies, or fp32 rounded to bf16
-        uint32_t h[8];
+            for (int k = 0; k < 4; k++)
+                w[k] = (uint32_t)(uint8_t)kept[4 * k] | ((uint32_t)(uint8_t)kept[4 * k + 1] << 8) |
+                       ((uint32_t)(uint8_t)kept[4 * k + 2] << 16) | ((uint32_t)(uint8_t)kept[4 * k + 3] << 24);
+            *reinterpret_cast<uint4*>(vt) = make_uint4(w[0], w[1], w[2], w[3]);
+        } else {  // 16-bit values: bf16/fp16 bit copies, or fp32 rounded to bf16
+            uint32_t h[8];
 #pragma unroll
-        for (int i = 0; i < 8; i++) {
-            if (DT == DT_FP32)
-                h[i] = f32_to_bf16_rne(__uint_as_float((uint32_t)kept[i]));
-            else
-                h[i] = (uint32_t)kept[i];
+            for (int k = 0; k < 8; k++)
+                h[k] = DT == DT_FP32 ? (uint32_t)f32_to_bf16_rne(__uint_as_float((uint32_t)kept[k])) : (uint32_t)kept[k];
+            *reinterpret_cast<uint4*>(vt) =
+                make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
         }
-        *reinterpret_cast<uint4*>(vbase + tiled_offset<64>(row, vb, tiles_per_row)) =
-            make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
-    }
-    // metadata: 2 bytes at byte 2c of the row's metadata; tiles of KT/8 = 16/vsz bytes per row
-    constexpr int TM = 16 / vsz;
-    if (TM >= 8) {  // bf16 (quarter 2 bytes) and int8 (quarter 4 bytes): one 16-bit store
-        *reinterpret_cast<uint16_t*>(meta + tiled_offset<TM>(row, 2 * (int64_t)c, tiles_per_row)) = (uint16_t)mbits;
-    } else {  // fp32: 1-byte quarters
-        meta[tiled_offset<TM>(row, 2 * (int64_t)c, tiles_per_row)] = (uint8_t)(mbits & 0xFF);
-        meta[tiled_offset<TM>(row, 2 * (int64_t)c + 1, tiles_per_row)] = (uint8_t)(mbits >> 8);
+        if (MB == 4) *reinterpret_cast<uint32_t*>(mt) = mbits;
+        else if (MB == 2) *reinterpret_cast<uint16_t*>(mt) = (uint16_t)mbits;
+        else *mt = (uint8_t)mbits;
     }
 }
 
@@ -240,17 +230,27 @@ static inline void padded_dims(int64_t M, int64_t K, int vsz, int64_t& Mp, int64
     tiles = Kp / kt;
 }
 
+template <int DT, int VOUT, bool WANDA, int TPW>
+static hipError_t launch_pc_tpw(const void* W, int64_t M, int64_t K, int64_t ldw, const float* norms, void* values,
+                                uint8_t* meta, int64_t Mp, int64_t tiles, hipStream_t s) {
+    const int64_t groups_x = (tiles + 4 * TPW - 1) / (4 * TPW);
+    const int64_t blocks = (Mp / 16) * groups_x;
+    if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((prune_compress_kernel<DT, VOUT, WANDA, TPW>), dim3((unsigned)blocks), dim3(256), 0, s, W, ldw, M,
+                       K, tiles, groups_x, norms, values, meta);
+    return hipGetLastError();
+}
+
+// Four tiles per wave (4 x 32-64 bytes of loads in flight per lane) when that still leaves a few
+// thousand workgroups; one otherwise, so small weights spread over the whole chip.
 template <int DT, int VOUT, bool WANDA>
 static hipError_t launch_pc(const void* W, int64_t M, int64_t K, int64_t ldw, const float* norms, void* values,
                             uint8_t* meta, hipStream_t s) {
     int64_t Mp, Kp, tiles;
     padded_dims(M, K, esize<VOUT>(), Mp, Kp, tiles);
-    const uint32_t cpr = (uint32_t)(Kp / 16);
-    const uint32_t total = (uint32_t)(Mp * (Kp / 16));
-    const uint32_t blocks = (total + 255) / 256;
-    hipLaunchKernelGGL((prune_compress_kernel<DT, VOUT, WANDA>), dim3(blocks), dim3(256), 0, s, W, ldw, M, K, cpr, total,
-                       tiles, norms, values, meta);
-    return hipGetLastError();
+    if ((Mp / 16) * ((tiles + 15) / 16) >= 2048)
+        return launch_pc_tpw<DT, VOUT, WANDA, 4>(W, M, K, ldw, norms, values, meta, Mp, tiles, s);
+    return launch_pc_tpw<DT, VOUT, WANDA, 1>(W, M, K, ldw, norms, values, meta, Mp, tiles, s);
 }
 
 hipError_t launch_prune_compress(const void* W, int dtype, int64_t M, int64_t K, int64_t ldw, int score,
