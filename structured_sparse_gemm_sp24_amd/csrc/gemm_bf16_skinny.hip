@@ -104,9 +104,11 @@ __global__ __launch_bounds__(64 * S) void gemm_bf16_skinny(const uint16_t* __res
     // tile (b, t): values at ((b * T + t) * 64 + lane) * 16 bytes, index at ((b * T + t) * 64 + lane) * 2
     const u32x4* vt = reinterpret_cast<const u32x4*>(vals) + b0 * T * 64 + lane;
     const uint16_t* mt = reinterpret_cast<const uint16_t*>(meta) + b0 * T * 64 + lane;
-    // X's extent in bytes: (K - 1) rows of pitch ldx plus N elements (below 2^31, checked on the host)
+    // X's extent in bytes: (K - 1) rows of pitch ldx plus N elements (below 2^31, checked on the host),
+    // rounded up to a whole dword (the range check passes a dword only if all of it is in range; the
+    // rounding stays inside the aligned dword that holds the last element)
     const __amdgpu_buffer_rsrc_t rx =
-        __builtin_amdgcn_make_buffer_rsrc((void*)X, (short)0, (int)(((K - 1) * ldx + N) * 2), 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc((void*)X, (short)0, (int)((((K - 1) * ldx + N) * 2 + 3) & ~3), 0x00020000);
 
     f32x4 acc[R][NF];
 #pragma unroll

@@ -45,9 +45,11 @@ constexpr int LOADS_PER_STAGE = 4 + 2 + 8;  // per wave: A, metadata, B
 constexpr int GROUP_M = 8;
 constexpr uint32_t RSRC_FLAGS = 0x00020000u;
 
-// Raw buffer descriptor: base, stride 0, byte count (reads at or past it return 0), format word.
+// Raw buffer descriptor: base, stride 0, byte count rounded up to whole dwords, format word. The range
+// check returns a dword only when all of it is below the record count; the rounding keeps the last
+// partial dword of the real data (that dword lies in the same page as the data it ends).
 __device__ __forceinline__ i32x4 make_rsrc(const void* base, int64_t bytes) {
-    const int64_t n = bytes < 0 ? 0 : (bytes > 0xFFFFFFFFll ? 0xFFFFFFFFll : bytes);
+    const int64_t n = bytes <= 0 ? 0 : (bytes > 0xFFFFFFFCll ? 0xFFFFFFFCll : (bytes + 3) & ~(int64_t)3);
     const uint64_t b = reinterpret_cast<uint64_t>(base);
     i32x4 r;
     r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)b);
@@ -135,7 +137,9 @@ __device__ __forceinline__ void load_stage(uint32_t lds, const Args& a, i32x4 rA
     }
     // B: 64 rows x 512 B; this wave loads rows 16*wave .. +15, two rows per instruction (rows
     // 16 wave + 2h + lane / 32: row & 3 = 2 (h & 1) + lane / 32, (row >> 3) & 1 = h >> 2).
-    const i32x4 rB = make_rsrc(a.X + k0 * a.ldx + n0, (a.K * a.ldx - k0 * a.ldx - n0) * 2);
+    // X's exact extent from this stage's corner ((K - 1) rows of pitch ldx plus N elements); make_rsrc
+    // rounds it up to whole dwords (the range check passes a dword only if all of it is in range)
+    const i32x4 rB = make_rsrc(a.X + k0 * a.ldx + n0, ((a.K - 1 - k0) * a.ldx + a.N - n0) * 2);
 #pragma unroll
     for (int h = 0; h < 8; h++) {
         const int row = 16 * wave + 2 * h;

@@ -13,7 +13,7 @@
 // The compressed weight is stored in that lane order (16-row x 128-column tiles, see include/sp24.h).
 // Direct kernel: each wave owns a 16 x (16*NF) tile, reads A (1 KB) and the index (256 B) of each
 // tile from global memory and gathers B element by element with bounds checks (any shape and row
-// pitch).
+// pitch). The LDS-tiled kernel (gemm_i8_tiled.hip) takes over for N > 64 with 16-byte X rows.
 #include "sp24_device.h"
 #include "sp24_launch.h"
 
@@ -82,6 +82,7 @@ __global__ __launch_bounds__(256) void gemm_i8_direct(const int8_t* __restrict__
 
 hipError_t launch_gemm_i8(const int8_t* values, const uint8_t* meta, int64_t M, int64_t K, const int8_t* X, int64_t N,
                           int64_t ldx, const float* scale, void* Y, int64_t ldy, hipStream_t s) {
+    if (gemm_i8_tiled_ok(M, K, N, ldx, X)) return launch_gemm_i8_tiled(values, meta, M, K, X, N, ldx, scale, Y, ldy, s);
     const unsigned gy = (unsigned)((M + 63) / 64);
     if (N <= 16) {
         hipLaunchKernelGGL(gemm_i8_direct<1>, dim3((unsigned)((N + 15) / 16), gy), dim3(256), 0, s, values, meta, M, K,

@@ -1,0 +1,370 @@
+// Tiled sparse x dense GEMM for large N, int8 in, exact int32 accumulation, per-output-channel fp32
+// dequant epilogue (oeforum post on sparse acceleration: int8 and 2:4 combine; Orin NN design,
+// Chapter 7, section 3.1 Step 4; NVIDIA blog on Ampere structured sparsity, Figure 1).
+//
+// Same organisation as the bf16 tiled kernel, with v_smfmac_i32_16x16x128_i8:
+// workgroup tile 256 (M) x 256 (N), 4 waves in a 2 x 2 grid, each wave 128 x 128 = 8 x 8 fragments
+// (256 int32 accumulators per lane, one wave per SIMD). K advances 128 dense columns per stage; three
+// stages are in flight through LDS (3 x 52 KB):
+//   A (compressed values): one 1 KB tile per 16-row block, already in the operand's lane order
+//     (lane l holds 16 kept int8 of row l % 16, dense columns [32 (l / 16), +32));
+//   metadata: one 256 B tile per block (lane l's 32-bit index at 4 l);
+//   B tile (X, 128 rows x 256 int8 = 256 B per row): row-major with the 16-byte units of row k
+//     stored at unit ^ f(k), f(k) = (k & 7) + 8 ((k >> 4) & 1). One ds_read_b64_tr_b8 takes 8 rows x
+//     16 bytes per 16-lane group, rows 16q + {0..7} (+8, +64) for q = 0..3; f puts those 32 rows in 16
+//     distinct 16-byte bank slots (two rows each, the minimum for 512 bytes), and stays the same for
+//     the +8 / +64 row offsets, so those are immediates. Every 4 consecutive lanes of a global load
+//     still read one aligned 64-byte run.
+// The B operand (lane = column, 32 k values: k = 16q + (e & 15) + 64 (e >> 4)) comes from four
+// ds_read_b64_tr_b8: in each 16-lane group, lane s points at row k0 + s/2, columns c0 + 8 (s % 2);
+// the instruction hands lane i the 8 consecutive k of column c0 + i.
+//
+// Loads are buffer loads with LDS destination whose whole byte offset is in the range-checked VGPR
+// operand: reads past this workgroup's row blocks, past K and past the end of X return zeros, and the
+// loads the pipeline issues past the last stage are pushed out of range on purpose. Tiles are ordered
+// XCD-first, then in groups of 8 tile-rows. The epilogue stages each wave's results through LDS (two
+// passes of 64 rows) so global stores are 16 bytes per lane.
+#include "sp24_device.h"
+#include "sp24_launch.h"
+
+namespace sp24 {
+namespace tiled_i8 {
+
+constexpr int BM = 256, BN = 256, BK = 128;
+constexpr int WM = 128, WN = 128;
+constexpr int FM = WM / 16, FN = WN / 16;
+constexpr int A_BYTES = BM * 64;          // 64 kept int8 per row per stage
+constexpr int META_BYTES = BM * 16;       // 64 kept values x 2 bits = 16 bytes per row
+constexpr int B_ROW = BN;                 // 256 bytes
+constexpr int B_BYTES = BK * B_ROW;
+constexpr int STAGE_BYTES = A_BYTES + META_BYTES + B_BYTES;
+constexpr int LOADS_PER_STAGE = 4 + 1 + 8;  // per wave: A, metadata, B
+constexpr int GROUP_M = 8;
+constexpr uint32_t RSRC_FLAGS = 0x00020000u;
+static_assert(3 * STAGE_BYTES <= 160 * 1024, "three stages fit in LDS");
+
+// Raw buffer descriptor over `bytes` bytes rounded up to whole dwords: the range check returns a
+// dword only when all of it is below the record count, and the rounding keeps the last partial dword
+// of the real data (that dword lies in the same page as the data it ends).
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, int64_t bytes) {
+    const int64_t n = bytes <= 0 ? 0 : (bytes > 0xFFFFFFFCll ? 0xFFFFFFFCll : (bytes + 3) & ~(int64_t)3);
+    const uint64_t b = reinterpret_cast<uint64_t>(base);
+    i32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+    r[1] = __builtin_amdgcn_readfirstlane((int)((b >> 32) & 0xFFFFu));
+    r[2] = __builtin_amdgcn_readfirstlane((int)(uint32_t)n);
+    r[3] = (int)RSRC_FLAGS;
+    return r;
+}
+
+// Buffer load with LDS destination (lane i's 16 bytes land at lds + 16 i), from inline asm so the
+// compiler adds no waits of its own; ordered by explicit s_waitcnt vmcnt + s_barrier. No VGPR is
+// written. `lds` is wave-uniform; `voff` is the lane's whole byte offset (range-checked).
+__device__ __forceinline__ void dma16(uint32_t lds, uint32_t voff, i32x4 rsrc) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :: "s"(lds), "v"(voff), "s"(rsrc) : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+struct Args {
+    const int8_t* vals;
+    const uint8_t* meta;
+    const int8_t* X;
+    const float* scale;
+    void* Y;
+    int64_t M, K, N, ldx, ldy;
+    int tilesM, tilesN;
+    int y_vec;  // Y base and row pitch allow 16-byte stores
+};
+
+// Swizzle of the 16-byte units of B row k (see the header).
+__device__ __forceinline__ int bswz(int k) { return (k & 7) | (((k >> 4) & 1) << 3); }
+
+// Per-lane parts of the load offsets.
+struct LoadOffsets {
+    uint32_t a;      // A tile: 16 * lane
+    uint32_t m;      // metadata: tile (lane / 16) of the wave's 4 blocks, 16 * (lane % 16) inside it
+    uint32_t b[8];   // B rows 4h + lane / 16 of the wave's 32 rows: row part + swizzled chunk
+};
+
+__device__ __forceinline__ LoadOffsets load_offsets(const Args& a, int lane, int wave) {
+    LoadOffsets o;
+    const int tiles = (int)((a.K + BK - 1) / BK);
+    o.a = 16 * lane;
+    o.m = (uint32_t)((lane >> 4) * tiles * 256 + 16 * (lane & 15));
+    const int p = lane & 15;  // 16-byte slot in the LDS row
+#pragma unroll
+    for (int h = 0; h < 8; h++) {
+        const int row = 32 * wave + 4 * h + (lane >> 4);
+        o.b[h] = (uint32_t)(row * a.ldx + 16 * (p ^ bswz(row)));
+    }
+    return o;
+}
+
+// This wave's share of the loads of stage s into the buffer at LDS address `lds`. For s >= S the
+// offsets get bit 31 set (beyond every record count): zeros, no memory traffic.
+__device__ __forceinline__ void load_stage(uint32_t lds, const Args& a, i32x4 rA, i32x4 rM, int64_t n0, int s, int S,
+                                           int wave, const LoadOffsets& lo) {
+    const int64_t k0 = (int64_t)s * BK;
+    const int tiles = (int)((a.K + BK - 1) / BK);
+    const uint32_t past = s < S ? 0u : 0x80000000u;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        const int b = 4 * wave + j;
+        dma16(lds + b * 1024, lo.a + (((uint32_t)(b * tiles + s) * 1024u) | past), rA);
+    }
+    // metadata of blocks 4 wave .. 4 wave + 3 (one 256 B tile each) in one instruction
+    dma16(lds + A_BYTES + 4 * wave * 256, lo.m + (((uint32_t)(4 * wave * tiles + s) * 256u) | past), rM);
+    // X's exact extent from this stage's corner, rounded up to whole dwords (see make_rsrc)
+    const i32x4 rB = make_rsrc(a.X + k0 * a.ldx + n0, (a.K - 1 - k0) * a.ldx + a.N - n0);
+#pragma unroll
+    for (int h = 0; h < 8; h++) dma16(lds + A_BYTES + META_BYTES + (32 * wave + 4 * h) * B_ROW, lo.b[h], rB);
+}
+
+struct LaneOffsets {
+    int a;       // A fragment of block wm0/16: block * 1024 + lane * 16
+    int m;       // metadata: A_BYTES + block * 256 + lane * 4
+    int b[FN];   // B fragment j, first read (t = 0)
+};
+
+__device__ __forceinline__ LaneOffsets lane_offsets(int wm0, int wn0, int lane) {
+    const int r = lane & 15, q = lane >> 4;
+    LaneOffsets o;
+    o.a = (wm0 >> 4) * 1024 + lane * 16;
+    o.m = A_BYTES + (wm0 >> 4) * 256 + lane * 4;
+    // read t of group q covers rows 16q + 8(t&1) + 64(t>>1) + r/2, which share row & 7 and
+    // (row >> 4) & 1 with row0, so the swizzle is fixed per lane and t only adds immediates
+    const int row0 = 16 * q + (r >> 1);
+    const int f = bswz(row0);
+#pragma unroll
+    for (int j = 0; j < FN; j++) {
+        const int unit = (wn0 >> 4) + j;  // 16 columns = one 16-byte unit
+        o.b[j] = A_BYTES + META_BYTES + row0 * B_ROW + ((unit ^ f) << 4) + 8 * (r & 1);
+    }
+    return o;
+}
+
+struct AFrags {
+    i32x4 a[FM];
+    uint32_t idx[FM];
+};
+
+typedef __attribute__((address_space(3))) char lds_char;
+
+// A lane's LDS address in this stage's buffer, opaque to the optimizer (keeps the immediates in the
+// reads instead of dozens of hoisted loop-invariant sums).
+__device__ __forceinline__ uint32_t stage_addr(uint32_t buf, int off) {
+    uint32_t v = buf + (uint32_t)off;
+    asm volatile("" : "+v"(v));
+    return v;
+}
+
+__device__ __forceinline__ void read_a(uint32_t buf, const LaneOffsets& o, AFrags& f) {
+    const lds_char* pa = (const lds_char*)(size_t)stage_addr(buf, o.a);
+    const lds_char* pm = (const lds_char*)(size_t)stage_addr(buf, o.m);
+#pragma unroll
+    for (int i = 0; i < FM; i++) {
+        f.a[i] = *reinterpret_cast<const __attribute__((address_space(3))) i32x4*>(pa + i * 1024);
+        f.idx[i] = *reinterpret_cast<const __attribute__((address_space(3))) uint32_t*>(pm + i * 256);
+    }
+}
+
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
+// B fragment j (16 columns x 128 k): four transposing reads of 8 k each.
+__device__ __forceinline__ i32x8 read_b(uint32_t buf, const LaneOffsets& o, int j) {
+    const lds_char* p = (const lds_char*)(size_t)stage_addr(buf, o.b[j]);
+    i32x8 b;
+#pragma unroll
+    for (int t = 0; t < 4; t++) {
+        const int imm = ((t & 1) * 8 + (t >> 1) * 64) * B_ROW;
+        const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)(p + imm));
+        b[2 * t] = v[0];
+        b[2 * t + 1] = v[1];
+    }
+    return b;
+}
+
+__device__ __forceinline__ void mfma_block(i32x4 (&acc)[FM][FN], const AFrags& f, const i32x8& b, int j) {
+#pragma unroll
+    for (int i = 0; i < FM; i++)
+        acc[i][j] = __builtin_amdgcn_smfmac_i32_16x16x128_i8(f.a[i], b, acc[i][j], (int)f.idx[i], 0, 0);
+}
+
+// One K stage: B fragments read two blocks ahead (ring of 4); before the last two blocks, the
+// barrier publishes stage s+1 and the loads of stage s+3 go into this stage's buffer; the next
+// stage's A fragments are reloaded one by one inside the last block. No branches.
+__device__ __forceinline__ void stage(uint32_t l0, const Args& a, i32x4 rA, i32x4 rM, int64_t n0, int s, int S,
+                                      i32x4 (&acc)[FM][FN], AFrags& f, i32x8 (&rb)[4], const LaneOffsets& o, int wave,
+                                      const LoadOffsets& lo) {
+    const int cb = s % 3;
+    const uint32_t cur = l0 + cb * STAGE_BYTES;
+    const uint32_t nxt = l0 + (cb == 2 ? 0 : cb + 1) * STAGE_BYTES;
+#pragma unroll
+    for (int j = 0; j < 6; j++) {
+        rb[(j + 2) & 3] = read_b(cur, o, j + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_block(acc, f, rb[j & 3], j);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of stage s are done
+    wait_vmcnt<LOADS_PER_STAGE>();       // stage s+1 has landed
+    __builtin_amdgcn_s_barrier();
+    load_stage(cur, a, rA, rM, n0, s + 3, S, wave, lo);
+    rb[0] = read_b(nxt, o, 0);
+    rb[1] = read_b(nxt, o, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_block(acc, f, rb[2], 6);
+    __builtin_amdgcn_sched_barrier(0);
+    const lds_char* pa = (const lds_char*)(size_t)stage_addr(nxt, o.a);
+    const lds_char* pm = (const lds_char*)(size_t)stage_addr(nxt, o.m);
+#pragma unroll
+    for (int i = 0; i < FM; i++) {
+        acc[i][7] = __builtin_amdgcn_smfmac_i32_16x16x128_i8(f.a[i], rb[3], acc[i][7], (int)f.idx[i], 0, 0);
+        f.a[i] = *reinterpret_cast<const __attribute__((address_space(3))) i32x4*>(pa + i * 1024);
+        f.idx[i] = *reinterpret_cast<const __attribute__((address_space(3))) uint32_t*>(pm + i * 256);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// Epilogue: two passes of 64 rows; the half-tile is written row-major (pitch EPI_ROW bytes, padded)
+// with one 4-byte write per value -- fl32(fl32(acc) * scale[m]) or the raw int32 -- and read back 16
+// bytes per lane.
+constexpr int EPI_ROW = 128 * 4 + 16;
+static_assert(4 * 64 * EPI_ROW <= 3 * STAGE_BYTES, "epilogue staging fits in the stage buffers");
+
+template <bool SCALE>
+__device__ __forceinline__ void store(char* smem, const i32x4 (&acc)[FM][FN], const Args& a, int64_t mw, int64_t nw,
+                                      int wave, int lane) {
+    const int r = lane & 15, q = lane >> 4;
+    char* tile = smem + wave * 64 * EPI_ROW;
+    const bool full = (mw + 128 <= a.M) && (nw + 128 <= a.N);
+#pragma unroll
+    for (int half = 0; half < 2; half++) {
+#pragma unroll
+        for (int i = 0; i < FM / 2; i++) {
+            float sc[4];
+#pragma unroll
+            for (int t = 0; t < 4; t++) {
+                const int64_t m = mw + 64 * half + 16 * i + 4 * q + t;
+                sc[t] = (SCALE && m < a.M) ? a.scale[m] : 0.f;
+            }
+#pragma unroll
+            for (int j = 0; j < FN; j++)
+#pragma unroll
+                for (int t = 0; t < 4; t++) {
+                    const int v = acc[half * (FM / 2) + i][j][t];
+                    const uint32_t bits = SCALE ? __float_as_uint(__fmul_rn((float)v, sc[t])) : (uint32_t)v;
+                    *reinterpret_cast<uint32_t*>(tile + (16 * i + 4 * q + t) * EPI_ROW + (16 * j + r) * 4) = bits;
+                }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int rr = 0; rr < 64; rr += 2) {
+            const int row = rr + (lane >> 5), col = 4 * (lane & 31);
+            const uint4 v = *reinterpret_cast<const uint4*>(tile + row * EPI_ROW + col * 4);
+            const int64_t m = mw + 64 * half + row, n = nw + col;
+            uint32_t* y = reinterpret_cast<uint32_t*>(a.Y) + m * a.ldy + n;
+            if (full && a.y_vec) {
+                *reinterpret_cast<uint4*>(y) = v;
+            } else if (m < a.M) {
+                const uint32_t e[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int k = 0; k < 4; k++)
+                    if (n + k < a.N) y[k] = e[k];
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+
+template <bool SCALE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_i8_tiled_kernel(Args a) {
+    __shared__ __attribute__((aligned(16))) char smem[3 * STAGE_BYTES];
+    const uint32_t l0 = (uint32_t)(size_t)(__attribute__((address_space(3))) char*)smem;
+    const uint32_t l1 = l0 + STAGE_BYTES, l2 = l0 + 2 * STAGE_BYTES;
+
+    // XCD-first, then grouped tile order
+    const int T = a.tilesM * a.tilesN;
+    const int pid = blockIdx.x;
+    const int xcd = pid & 7, slot = pid >> 3;
+    const int per = T >> 3, rem = T & 7;
+    const int logical = xcd * per + (xcd < rem ? xcd : rem) + slot;
+    const int gsize = GROUP_M * a.tilesN;
+    const int g = logical / gsize;
+    const int first_m = g * GROUP_M;
+    const int gm = (a.tilesM - first_m) < GROUP_M ? (a.tilesM - first_m) : GROUP_M;
+    const int in_g = logical - g * gsize;
+    const int tm = first_m + in_g % gm, tn = in_g / gm;
+    const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int wm0 = (wave >> 1) * WM, wn0 = (wave & 1) * WN;
+    const int64_t tiles = (a.K + BK - 1) / BK, blocks_left = (a.M + 15) / 16 - m0 / 16;
+    const int64_t blocks = blocks_left < BM / 16 ? blocks_left : BM / 16;
+    const i32x4 rA = make_rsrc(reinterpret_cast<const char*>(a.vals) + (m0 / 16) * tiles * 1024, blocks * tiles * 1024);
+    const i32x4 rM = make_rsrc(a.meta + (m0 / 16) * tiles * 256, blocks * tiles * 256);
+
+    i32x4 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; i++)
+#pragma unroll
+        for (int j = 0; j < FN; j++) acc[i][j] = i32x4{0, 0, 0, 0};
+
+    const LaneOffsets o = lane_offsets(wm0, wn0, lane);
+    const LoadOffsets lo = load_offsets(a, lane, wave);
+    const int S = (int)tiles;
+
+    load_stage(l0, a, rA, rM, n0, 0, S, wave, lo);
+    load_stage(l1, a, rA, rM, n0, 1, S, wave, lo);
+    wait_vmcnt<LOADS_PER_STAGE>();
+    __builtin_amdgcn_s_barrier();
+    load_stage(l2, a, rA, rM, n0, 2, S, wave, lo);
+
+    AFrags fa;
+    i32x8 rb[4];
+    read_a(l0, o, fa);
+    rb[0] = read_b(l0, o, 0);
+    rb[1] = read_b(l0, o, 1);
+    for (int s = 0; s < S; s++) stage(l0, a, rA, rM, n0, s, S, acc, fa, rb, o, wave, lo);
+
+    wait_vmcnt<0>();               // the zero-filling loads past the last stage have landed
+    __builtin_amdgcn_s_barrier();  // every wave is done reading (and loading) the stage buffers
+    store<SCALE>(smem, acc, a, m0 + wm0, n0 + wn0, wave, lane);
+}
+
+}  // namespace tiled_i8
+
+bool gemm_i8_tiled_ok(int64_t M, int64_t K, int64_t N, int64_t ldx, const void* X) {
+    // 16-byte X rows; 32-bit load offsets: 128 rows of X (128 * ldx < 2^31) and 16 row blocks of
+    // compressed tiles (16 * K / 128 * 1 KB < 2^31) stay below bit 31, which marks the loads past the
+    // last stage
+    return ldx % 16 == 0 && (reinterpret_cast<uintptr_t>(X) & 15) == 0 && N > 64 && ldx < ((int64_t)1 << 24) &&
+           K < ((int64_t)1 << 22) && ((M + 255) / 256) * ((N + 255) / 256) < (1 << 30);
+}
+
+hipError_t launch_gemm_i8_tiled(const int8_t* values, const uint8_t* meta, int64_t M, int64_t K, const int8_t* X,
+                                int64_t N, int64_t ldx, const float* scale, void* Y, int64_t ldy, hipStream_t s) {
+    tiled_i8::Args a;
+    a.vals = values; a.meta = meta; a.X = X; a.scale = scale; a.Y = Y;
+    a.M = M; a.K = K; a.N = N; a.ldx = ldx; a.ldy = ldy;
+    a.tilesM = (int)((M + tiled_i8::BM - 1) / tiled_i8::BM);
+    a.tilesN = (int)((N + tiled_i8::BN - 1) / tiled_i8::BN);
+    a.y_vec = ((reinterpret_cast<uintptr_t>(Y) & 15) == 0) && ((ldy * 4) % 16 == 0);
+    const unsigned grid = (unsigned)(a.tilesM * a.tilesN);
+    if (scale)
+        hipLaunchKernelGGL(tiled_i8::gemm_i8_tiled_kernel<true>, dim3(grid), dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL(tiled_i8::gemm_i8_tiled_kernel<false>, dim3(grid), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace sp24

@@ -25,6 +25,10 @@ bool gemm_bf16_tiled_ok(int64_t M, int64_t K, int64_t N, int64_t ldx, const void
 hipError_t launch_gemm_bf16_tiled(const uint16_t* values, const uint8_t* meta, int64_t M, int64_t K, const uint16_t* X,
                                   int64_t N, int64_t ldx, void* Y, bool out_fp32, int64_t ldy, hipStream_t s);
 
+bool gemm_i8_tiled_ok(int64_t M, int64_t K, int64_t N, int64_t ldx, const void* X);
+hipError_t launch_gemm_i8_tiled(const int8_t* values, const uint8_t* meta, int64_t M, int64_t K, const int8_t* X,
+                                int64_t N, int64_t ldx, const float* scale, void* Y, int64_t ldy, hipStream_t s);
+
 hipError_t launch_gemm_i8(const int8_t* values, const uint8_t* meta, int64_t M, int64_t K, const int8_t* X,
                           int64_t N, int64_t ldx, const float* scale, void* Y, int64_t ldy, hipStream_t s);
 

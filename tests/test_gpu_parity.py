@@ -254,7 +254,9 @@ def test_gemm_bf16_orin7_gather_example():
 # ----------------------------------------------------------------------------- sparse GEMM, int8
 
 I8_SHAPES = [(16, 16, 1, 1), (33, 48, 17, 20), (64, 128, 64, 64), (200, 336, 100, 112), (96, 1024, 300, 304),
-             (80, 512, 8, 8)]
+             (80, 512, 8, 8),
+             # tiled kernel (N > 64, 16-byte X rows): ragged M and N, K tails, several tiles both ways
+             (257, 512, 513, 528), (40, 128, 65, 80), (520, 1168, 1000, 1008), (300, 3072, 600, 608)]
 
 
 @pytest.mark.parametrize("M,K,N,ldx", I8_SHAPES)
