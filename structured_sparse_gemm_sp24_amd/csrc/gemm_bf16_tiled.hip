@@ -24,9 +24,12 @@
 // in each 16-lane group, lane s points at row k0 + s/4, columns c0 + 4(s%4); the instruction hands
 // lane i the four consecutive k of column c0 + i.
 //
-// Tiles are ordered XCD-first: workgroup p runs on XCD p % 8, so logical tiles are numbered such
-// that each XCD gets a contiguous range, walked in groups of 8 tile-rows (A tiles and B tiles are
-// re-read from that XCD's L2).
+// Persistent: one workgroup per CU walks its tiles (p, p + G, p + 2G, ... in a numbering where the
+// workgroups of one XCD -- workgroup p runs on XCD p % 8 -- hold neighbouring tiles at the same time,
+// walked in groups of 8 tile-rows, so A and B tiles are re-read from that XCD's L2). The three-stage
+// LDS pipeline runs across tile boundaries: the last stages of a tile load the first stages of the
+// next, and the epilogue works from registers only (4 x 4 transposes inside lane quads by DPP, then
+// 8- or 16-byte stores), so its stores drain while the next tile computes.
 #include "sp24_device.h"
 #include "sp24_launch.h"
 
@@ -86,8 +89,25 @@ struct Args {
     void* Y;
     int64_t M, K, N, ldx, ldy;
     int tilesM, tilesN;
-    int y_vec;  // Y base and row pitch allow 16-byte stores
+    int y_vec;  // Y base and row pitch allow 8-byte (bf16) / 16-byte (fp32) stores
 };
+
+// Where the loads of one tile come from: its corner and the buffer descriptors of its compressed
+// row blocks. `valid` is false past the workgroup's last tile (its loads are then pushed out of range).
+struct TileDesc {
+    int64_t m0, n0;
+    i32x4 rA, rM;
+    bool valid;
+};
+
+// Logical tile of workgroup p at its k-th turn, or -1. Within a turn the G workgroups hold tiles
+// [kG, kG + G); those of XCD x (p % 8 == x) hold a contiguous range of them.
+__device__ __forceinline__ int tile_of(const Args& a, int p, int k) {
+    const int G = gridDim.x, T = a.tilesM * a.tilesN;
+    const int pp = (G & 7) == 0 ? (p & 7) * (G >> 3) + (p >> 3) : p;
+    const int64_t L = (int64_t)k * G + pp;
+    return L < T ? (int)L : -1;
+}
 
 // Per-lane parts of the load offsets (the uniform parts go into the SGPR offset operand).
 struct LoadOffsets {
@@ -98,7 +118,7 @@ struct LoadOffsets {
 
 __device__ __forceinline__ LoadOffsets load_offsets(const Args& a, int lane) {
     LoadOffsets o;
-    const int tiles = (int)(a.K / BK);
+    const int tiles = (int)((a.K + BK - 1) / BK);
     o.a = 16 * lane;
     o.m = 4 * (lane & 31) + (lane >> 5) * tiles * 128;
     const int pc = lane & 31;  // 16-byte slot in the LDS row
@@ -113,39 +133,61 @@ __device__ __forceinline__ LoadOffsets load_offsets(const Args& a, int lane) {
     return o;
 }
 
-// Issue this wave's share of the loads of stage `s` into the stage buffer at LDS address `lds`.
-// rA / rM cover the compressed tiles of this workgroup's row blocks (at most 16; tile (b, s) of block
-// b at (b * tiles + s) * 1 KB of values and * 128 B of metadata). For s >= S (the pipeline runs three
-// stages ahead and issues these unconditionally) the offsets get bit 31 set, past every record
-// count, so the loads return zeros without memory traffic; rB's record count is 0 there anyway.
-__device__ __forceinline__ void load_stage(uint32_t lds, const Args& a, i32x4 rA, i32x4 rM, int64_t n0, int s, int S,
-                                           int wave, const LoadOffsets& lo) {
+// Issue this wave's share of the loads of stage `s` of tile `td` into the stage buffer at LDS address
+// `lds`. td.rA / td.rM cover the compressed tiles of the tile's row blocks (at most 16; tile (b, s) of
+// block b at (b * tiles + s) * 1 KB of values and * 128 B of metadata). When td is not valid (past the
+// workgroup's last tile) the offsets get bit 31 set, past every record count, so the loads return
+// zeros without memory traffic (and X's record count is 0).
+__device__ __forceinline__ void load_stage(uint32_t lds, const Args& a, const TileDesc& td, int s, int wave,
+                                           const LoadOffsets& lo) {
     const int64_t k0 = (int64_t)s * BK;
-    const int tiles = (int)(a.K / BK);
-    const uint32_t past = s < S ? 0u : 0x80000000u;
+    const int tiles = (int)((a.K + BK - 1) / BK);
+    const uint32_t past = td.valid ? 0u : 0x80000000u;
     // A: one 1 KB tile per 16-row block, copied as is (it is already in lane order)
 #pragma unroll
     for (int j = 0; j < 4; j++) {
         const int b = 4 * wave + j;
-        dma16(lds + b * 1024, lo.a + (((uint32_t)(b * tiles + s) * 1024u) | past), rA);
+        dma16(lds + b * 1024, lo.a + (((uint32_t)(b * tiles + s) * 1024u) | past), td.rA);
     }
     // metadata: one 128 B tile per block; 4 blocks per wave, two per dword instruction
 #pragma unroll
     for (int h = 0; h < 2; h++) {
         const int b = 4 * wave + 2 * h;
-        dma4(lds + A_BYTES + b * 128, lo.m + (((uint32_t)(b * tiles + s) * 128u) | past), rM);
+        dma4(lds + A_BYTES + b * 128, lo.m + (((uint32_t)(b * tiles + s) * 128u) | past), td.rM);
     }
     // B: 64 rows x 512 B; this wave loads rows 16*wave .. +15, two rows per instruction (rows
     // 16 wave + 2h + lane / 32: row & 3 = 2 (h & 1) + lane / 32, (row >> 3) & 1 = h >> 2).
     // X's exact extent from this stage's corner ((K - 1) rows of pitch ldx plus N elements); make_rsrc
     // rounds it up to whole dwords (the range check passes a dword only if all of it is in range)
-    const i32x4 rB = make_rsrc(a.X + k0 * a.ldx + n0, ((a.K - 1 - k0) * a.ldx + a.N - n0) * 2);
+    const i32x4 rB =
+        make_rsrc(a.X + k0 * a.ldx + td.n0, td.valid ? ((a.K - 1 - k0) * a.ldx + a.N - td.n0) * 2 : 0);
 #pragma unroll
     for (int h = 0; h < 8; h++) {
         const int row = 16 * wave + 2 * h;
         dma16(lds + A_BYTES + META_BYTES + row * B_ROW,
               lo.b[(h & 1) | ((h >> 2) << 1)] + (uint32_t)(row * a.ldx * 2), rB);
     }
+}
+
+// Tile descriptor of logical tile L (-1: none). Tiles are walked in groups of GROUP_M tile-rows,
+// column by column inside a group.
+__device__ __forceinline__ TileDesc tile_desc(const Args& a, int L) {
+    TileDesc td;
+    td.valid = L >= 0;
+    const int Lc = L >= 0 ? L : 0;
+    const int gsize = GROUP_M * a.tilesN;
+    const int g = Lc / gsize;
+    const int first_m = g * GROUP_M;
+    const int gm = (a.tilesM - first_m) < GROUP_M ? (a.tilesM - first_m) : GROUP_M;
+    const int in_g = Lc - g * gsize;
+    const int tm = first_m + in_g % gm, tn = in_g / gm;
+    td.m0 = (int64_t)tm * BM;
+    td.n0 = (int64_t)tn * BN;
+    const int64_t tiles = (a.K + BK - 1) / BK, blocks_left = (a.M + 15) / 16 - td.m0 / 16;
+    const int64_t blocks = blocks_left < BM / 16 ? blocks_left : BM / 16;
+    td.rA = make_rsrc(reinterpret_cast<const char*>(a.vals) + (td.m0 / 16) * tiles * 1024, blocks * tiles * 1024);
+    td.rM = make_rsrc(a.meta + (td.m0 / 16) * tiles * 128, blocks * tiles * 128);
+    return td;
 }
 
 // Lane-dependent LDS byte offsets used by compute_stage (computed once per kernel).
@@ -220,12 +262,13 @@ __device__ __forceinline__ void mfma_block(f32x4 (&acc)[FM][FN], const AFrags& f
         acc[i][j] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(f.a[i], b, acc[i][j], (int)f.idx[i], 0, 0);
 }
 
-// One K stage (see the pipeline description in the kernel). The body has no branches: past the
-// last stage the loads are out of range and the reads of the "next" buffer are never used.
-__device__ __forceinline__ void stage(uint32_t l0, const Args& a, i32x4 rA, i32x4 rM, int64_t n0, int s, int S,
-                                      f32x4 (&acc)[FM][FN], AFrags& f, bf16x16 (&rb)[4], const LaneOffsets& o,
-                                      int wave, const LoadOffsets& lo) {
-    const int cb = s % 3;
+// One K stage (see the pipeline description in the kernel): stage s of the current tile, g-th stage of
+// the workgroup overall (selects the buffer). The loads it issues are those of stage s + 3 of the
+// current tile or, past its end, stage s + 3 - S of the next one. No branches.
+__device__ __forceinline__ void stage(uint32_t l0, const Args& a, const TileDesc& cur_t, const TileDesc& next_t, int s,
+                                      int S, int g, f32x4 (&acc)[FM][FN], AFrags& f, bf16x16 (&rb)[4],
+                                      const LaneOffsets& o, int wave, const LoadOffsets& lo) {
+    const int cb = g % 3;
     const uint32_t cur = l0 + cb * STAGE_BYTES;
     const uint32_t nxt = l0 + (cb == 2 ? 0 : cb + 1) * STAGE_BYTES;
 #pragma unroll
@@ -235,10 +278,11 @@ __device__ __forceinline__ void stage(uint32_t l0, const Args& a, i32x4 rA, i32x
         mfma_block(acc, f, rb[j & 3], j);
         __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of stage s are done
-    wait_vmcnt<LOADS_PER_STAGE>();       // stage s+1 has landed (s+2 may still be in flight)
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of stage g are done
+    wait_vmcnt<LOADS_PER_STAGE>();       // stage g+1 has landed (g+2 may still be in flight)
     __builtin_amdgcn_s_barrier();
-    load_stage(cur, a, rA, rM, n0, s + 3, S, wave, lo);
+    const bool here = s + 3 < S;
+    load_stage(cur, a, here ? cur_t : next_t, here ? s + 3 : s + 3 - S, wave, lo);
     rb[0] = read_b(nxt, o, 0);
     rb[1] = read_b(nxt, o, 1);
     __builtin_amdgcn_sched_barrier(0);
@@ -258,135 +302,97 @@ __device__ __forceinline__ void stage(uint32_t l0, const Args& a, i32x4 rA, i32x
 }
 
 // ---------------------------------------------------------------- epilogues
-// The accumulators hold, per lane, 4 consecutive rows of one column; Y wants runs along a row. Each
-// wave stages its 128 x 128 tile through LDS (reusing the pipeline buffers) so global stores are
-// 16 bytes per lane with 64 contiguous bytes per row segment.
+// The accumulators hold, per lane l = 16q + 4a + b, rows 4q .. 4q+3 of column 4a + b of each 16 x 16
+// fragment; Y wants runs along a row. A 4 x 4 transpose inside each lane quad (b = 0..3) by two DPP
+// exchanges -- with lane b ^ 2 (off-diagonal 2 x 2 blocks), then with lane b ^ 1 -- leaves lane b with
+// row 4q + b, columns 4a .. 4a+3, which it stores as one 8-byte (bf16) or 16-byte (fp32) write. No LDS
+// is used, so the next tile's loads can land in the stage buffers meanwhile.
 
-// bf16: the tile is written column-major (one column = 128 rows, pitch EPI_COL bytes, padded so
-// both the 8-byte writes and the transposing reads below are free of bank conflicts), then read back
-// with ds_read_b64_tr_b16, which hands each lane 4 consecutive columns of one row.
-constexpr int EPI_COL = 128 * 2 + 40;
-static_assert(4 * 128 * EPI_COL <= 3 * STAGE_BYTES, "epilogue staging fits in the stage buffers");
-
-__device__ __forceinline__ void store_bf16(char* smem, const f32x4 (&acc)[FM][FN], const Args& a, int64_t mw, int64_t nw,
-                                           int wave, int lane) {
-    const int r = lane & 15, q = lane >> 4;
-    char* tile = smem + wave * 128 * EPI_COL;
-#pragma unroll
-    for (int i = 0; i < FM; i++) {
-#pragma unroll
-        for (int j = 0; j < FN; j++) {
-            const uint32_t lo = f32_to_bf16_rne(acc[i][j][0]) | ((uint32_t)f32_to_bf16_rne(acc[i][j][1]) << 16);
-            const uint32_t hi = f32_to_bf16_rne(acc[i][j][2]) | ((uint32_t)f32_to_bf16_rne(acc[i][j][3]) << 16);
-            *reinterpret_cast<uint2*>(tile + (16 * j + r) * EPI_COL + (16 * i + 4 * q) * 2) = make_uint2(lo, hi);
-        }
-        __builtin_amdgcn_sched_barrier(0);  // convert row block by row block (bounded live registers)
-    }
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes are done
-    __builtin_amdgcn_wave_barrier();
-    // 32 steps of 16 rows x 32 columns: group q takes columns cb + 8q .. +7 of rows rb .. rb+15
-    const bool full = (mw + 128 <= a.M) && (nw + 128 <= a.N);
-#pragma unroll
-    for (int rb = 0; rb < 128; rb += 16)
-#pragma unroll
-        for (int cb = 0; cb < 128; cb += 32) {
-            const int c0 = cb + 8 * q;
-            // lane s of the group points at column c0 + s/4 (+4), rows rb + 4(s%4) .. +3
-            const char* p0 = tile + (c0 + (r >> 2)) * EPI_COL + (rb + 4 * (r & 3)) * 2;
-            const i16x4 u = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p0);
-            const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) i16x4*)(p0 + 4 * EPI_COL));
-            const int64_t m = mw + rb + r, n = nw + c0;
-            const uint4 val = make_uint4((uint16_t)u[0] | ((uint32_t)(uint16_t)u[1] << 16),
-                                         (uint16_t)u[2] | ((uint32_t)(uint16_t)u[3] << 16),
-                                         (uint16_t)v[0] | ((uint32_t)(uint16_t)v[1] << 16),
-                                         (uint16_t)v[2] | ((uint32_t)(uint16_t)v[3] << 16));
-            uint16_t* y = reinterpret_cast<uint16_t*>(a.Y) + m * a.ldy + n;
-            if (full && a.y_vec) {
-                *reinterpret_cast<uint4*>(y) = val;
-            } else if (m < a.M) {
-                const uint16_t e[8] = {(uint16_t)val.x, (uint16_t)(val.x >> 16), (uint16_t)val.y, (uint16_t)(val.y >> 16),
-                                       (uint16_t)val.z, (uint16_t)(val.z >> 16), (uint16_t)val.w, (uint16_t)(val.w >> 16)};
-#pragma unroll
-                for (int k = 0; k < 8; k++)
-                    if (n + k < a.N) y[k] = e[k];
-            }
-        }
+__device__ __forceinline__ uint32_t dpp_xor2(uint32_t v) {  // value of lane b ^ 2 of the quad
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
+}
+__device__ __forceinline__ uint32_t dpp_xor1(uint32_t v) {  // value of lane b ^ 1 of the quad
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
 }
 
-// fp32: two passes of 64 rows; the half-tile is written row-major (pitch EPI_ROW32 bytes, padded)
-// with one 4-byte write per value and read back 16 bytes (4 columns) per lane.
-constexpr int EPI_ROW32 = 128 * 4 + 16;
-static_assert(4 * 64 * EPI_ROW32 <= 3 * STAGE_BYTES, "epilogue staging fits in the stage buffers");
+// bf16 out: pack rows (0,1) and (2,3), swap packed halves across b ^ 2, then 16-bit halves across b ^ 1.
+__device__ __forceinline__ uint2 quad_transpose_bf16(const f32x4& v, int b) {
+    const uint32_t p0 = pack_bf16x2_rne(v[0], v[1]);
+    const uint32_t p1 = pack_bf16x2_rne(v[2], v[3]);
+    const bool low = b < 2, even = (b & 1) == 0;
+    const uint32_t r = dpp_xor2(low ? p1 : p0);
+    const uint32_t x0 = low ? p0 : r, x1 = low ? r : p1;
+    const uint32_t r0 = dpp_xor1(x0), r1 = dpp_xor1(x1);
+    uint2 y;
+    y.x = even ? (x0 & 0xFFFFu) | (r0 << 16) : (r0 >> 16) | (x0 & 0xFFFF0000u);
+    y.y = even ? (x1 & 0xFFFFu) | (r1 << 16) : (r1 >> 16) | (x1 & 0xFFFF0000u);
+    return y;
+}
 
-__device__ __forceinline__ void store_fp32(char* smem, const f32x4 (&acc)[FM][FN], const Args& a, int64_t mw, int64_t nw,
-                                           int wave, int lane) {
-    const int r = lane & 15, q = lane >> 4;
-    char* tile = smem + wave * 64 * EPI_ROW32;
-    const bool full = (mw + 128 <= a.M) && (nw + 128 <= a.N);
+// fp32 out: the same two exchanges on single values.
+__device__ __forceinline__ uint4 quad_transpose_f32(const f32x4& v, int b) {
+    const uint32_t v0 = __float_as_uint(v[0]), v1 = __float_as_uint(v[1]);
+    const uint32_t v2 = __float_as_uint(v[2]), v3 = __float_as_uint(v[3]);
+    const bool low = b < 2, even = (b & 1) == 0;
+    const uint32_t r0 = dpp_xor2(low ? v2 : v0), r1 = dpp_xor2(low ? v3 : v1);
+    const uint32_t x0 = low ? v0 : r0, x1 = low ? v1 : r1, x2 = low ? r0 : v2, x3 = low ? r1 : v3;
+    const uint32_t s0 = dpp_xor1(even ? x1 : x0), s1 = dpp_xor1(even ? x3 : x2);
+    return even ? make_uint4(x0, s0, x2, s1) : make_uint4(s0, x1, s1, x3);
+}
+
+template <bool OUT_FP32>
+__device__ __forceinline__ void store_tile(const f32x4 (&acc)[FM][FN], const Args& a, int64_t mw, int64_t nw,
+                                           int lane) {
+    const int q = lane >> 4, r = lane & 15, b = r & 3, c4 = r & ~3;
+    const bool full = (mw + WM <= a.M) && (nw + WN <= a.N) && a.y_vec;
 #pragma unroll
-    for (int half = 0; half < 2; half++) {
+    for (int i = 0; i < FM; i++) {
+        const int64_t m = mw + 16 * i + 4 * q + b;
 #pragma unroll
-        for (int i = 0; i < FM / 2; i++) {
+        for (int j = 0; j < FN; j++) {
+            const int64_t n = nw + 16 * j + c4;
+            if (OUT_FP32) {
+                const uint4 y = quad_transpose_f32(acc[i][j], b);
+                uint32_t* p = reinterpret_cast<uint32_t*>(a.Y) + m * a.ldy + n;
+                if (full) {
+                    *reinterpret_cast<uint4*>(p) = y;
+                } else if (m < a.M) {
+                    const uint32_t e[4] = {y.x, y.y, y.z, y.w};
 #pragma unroll
-            for (int j = 0; j < FN; j++)
+                    for (int k = 0; k < 4; k++)
+                        if (n + k < a.N) p[k] = e[k];
+                }
+            } else {
+                const uint2 y = quad_transpose_bf16(acc[i][j], b);
+                uint16_t* p = reinterpret_cast<uint16_t*>(a.Y) + m * a.ldy + n;
+                if (full) {
+                    *reinterpret_cast<uint2*>(p) = y;
+                } else if (m < a.M) {
+                    const uint16_t e[4] = {(uint16_t)y.x, (uint16_t)(y.x >> 16), (uint16_t)y.y, (uint16_t)(y.y >> 16)};
 #pragma unroll
-                for (int t = 0; t < 4; t++)
-                    *reinterpret_cast<float*>(tile + (16 * i + 4 * q + t) * EPI_ROW32 + (16 * j + r) * 4) =
-                        acc[half * (FM / 2) + i][j][t];
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        __builtin_amdgcn_s_waitcnt(0xC07F);
-        __builtin_amdgcn_wave_barrier();
-        // 64 rows x 128 columns: each step covers 2 rows (32 lanes x 4 columns per row)
-#pragma unroll
-        for (int rr = 0; rr < 64; rr += 2) {
-            const int row = rr + (lane >> 5), col = 4 * (lane & 31);
-            const float4 v = *reinterpret_cast<const float4*>(tile + row * EPI_ROW32 + col * 4);
-            const int64_t m = mw + 64 * half + row, n = nw + col;
-            float* y = reinterpret_cast<float*>(a.Y) + m * a.ldy + n;
-            if (full && a.y_vec) {
-                *reinterpret_cast<float4*>(y) = v;
-            } else if (m < a.M) {
-                const float e[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-                for (int k = 0; k < 4; k++)
-                    if (n + k < a.N) y[k] = e[k];
+                    for (int k = 0; k < 4; k++)
+                        if (n + k < a.N) p[k] = e[k];
+                }
             }
         }
-        __builtin_amdgcn_s_waitcnt(0xC07F);
-        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_sched_barrier(0);  // one row block of fragments at a time (bounded live registers)
     }
 }
 
 template <bool OUT_FP32>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_bf16_tiled_kernel(Args a) {
     __shared__ __attribute__((aligned(16))) char smem[3 * STAGE_BYTES];
-    // LDS byte addresses of the three stage buffers (for the LDS-destination loads)
+    // LDS byte address of the first stage buffer (for the LDS-destination loads)
     const uint32_t l0 = (uint32_t)(size_t)(__attribute__((address_space(3))) char*)smem;
-    const uint32_t l1 = l0 + STAGE_BYTES, l2 = l0 + 2 * STAGE_BYTES;
 
-    // XCD-first, then grouped tile order
-    const int T = a.tilesM * a.tilesN;
-    const int pid = blockIdx.x;
-    const int xcd = pid & 7, slot = pid >> 3;
-    const int per = T >> 3, rem = T & 7;
-    const int logical = xcd * per + (xcd < rem ? xcd : rem) + slot;
-    const int gsize = GROUP_M * a.tilesN;
-    const int g = logical / gsize;
-    const int first_m = g * GROUP_M;
-    const int gm = (a.tilesM - first_m) < GROUP_M ? (a.tilesM - first_m) : GROUP_M;
-    const int in_g = logical - g * gsize;
-    const int tm = first_m + in_g % gm, tn = in_g / gm;
-    const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
-
+    const int p = blockIdx.x;
+    int L = tile_of(a, p, 0);
+    if (L < 0) return;  // whole workgroup
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int wm0 = (wave >> 1) * WM, wn0 = (wave & 1) * WN;
-    // compressed tiles of this workgroup's first row block onward (rows are padded to 16)
-    const int64_t tiles = a.K / BK, blocks_left = (a.M + 15) / 16 - m0 / 16;
-    const int64_t blocks = blocks_left < BM / 16 ? blocks_left : BM / 16;
-    const i32x4 rA = make_rsrc(reinterpret_cast<const char*>(a.vals) + (m0 / 16) * tiles * 1024, blocks * tiles * 1024);
-    const i32x4 rM = make_rsrc(a.meta + (m0 / 16) * tiles * 128, blocks * tiles * 128);
+    const LaneOffsets o = lane_offsets(wm0, wn0, lane);
+    const LoadOffsets lo = load_offsets(a, lane);
+    const int S = (int)((a.K + BK - 1) / BK);
 
     f32x4 acc[FM][FN];
 #pragma unroll
@@ -394,47 +400,65 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
         for (int j = 0; j < FN; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const LaneOffsets o = lane_offsets(wm0, wn0, lane);
-    const LoadOffsets lo = load_offsets(a, lane);
-    const int S = (int)(a.K / BK);
-
-    // Software pipeline over K stages of 64 columns, three LDS buffers (stage s in buffer s % 3):
-    //  - the loads of stage s+3 go out once every wave has finished reading stage s, i.e. at the
-    //    barrier placed before the last two fragment blocks of stage s, so each stage's loads have
+    // Software pipeline over K stages of 64 columns, three LDS buffers (the workgroup's g-th stage in
+    // buffer g % 3), continued across the workgroup's tiles:
+    //  - the loads of stage g+3 go out once every wave has finished reading stage g, i.e. at the
+    //    barrier placed before the last two fragment blocks of stage g, so each stage's loads have
     //    about two stages of compute to land;
-    //  - that barrier also publishes stage s+1 (each wave first waits for its own loads of it), so
-    //    stage s+1's A fragments, indices and first B fragments are read while the last 16
-    //    smfmacs of stage s run;
+    //  - that barrier also publishes stage g+1 (each wave first waits for its own loads of it), so
+    //    stage g+1's A fragments, indices and first B fragments are read while the last 16 smfmacs of
+    //    stage g run;
     //  - inside a stage, B fragment j+2 is read while fragment j is multiplied (ring of 4).
-    load_stage(l0, a, rA, rM, n0, 0, S, wave, lo);
-    load_stage(l1, a, rA, rM, n0, 1, S, wave, lo);
+    // With fewer than 3 stages per tile every workgroup has one tile (see the launcher).
+    TileDesc cur_t = tile_desc(a, L);
+    TileDesc next_t = tile_desc(a, tile_of(a, p, 1));
+    load_stage(l0, a, S > 0 ? cur_t : next_t, 0, wave, lo);
+    load_stage(l0 + STAGE_BYTES, a, S > 1 ? cur_t : next_t, S > 1 ? 1 : 0, wave, lo);
     wait_vmcnt<LOADS_PER_STAGE>();
     __builtin_amdgcn_s_barrier();
-    load_stage(l2, a, rA, rM, n0, 2, S, wave, lo);
+    load_stage(l0 + 2 * STAGE_BYTES, a, S > 2 ? cur_t : next_t, S > 2 ? 2 : 0, wave, lo);
 
     AFrags fa;
     bf16x16 rb[4];
     read_a(l0, o, fa);
     rb[0] = read_b(l0, o, 0);
     rb[1] = read_b(l0, o, 1);
-    for (int s = 0; s < S; s++) stage(l0, a, rA, rM, n0, s, S, acc, fa, rb, o, wave, lo);
-
-    // epilogue: lane holds column n0 + wn0 + 16 j + r, rows m0 + wm0 + 16 i + 4 q + t
-    wait_vmcnt<0>();               // the zero-filling loads past the last stage have landed
-    __builtin_amdgcn_s_barrier();  // every wave is done reading (and loading) the stage buffers
-    if (OUT_FP32)
-        store_fp32(smem, acc, a, m0 + wm0, n0 + wn0, wave, lane);
-    else
-        store_bf16(smem, acc, a, m0 + wm0, n0 + wn0, wave, lane);
+    int g = 0;
+    for (int k = 1;; k++) {
+        for (int s = 0; s < S; s++, g++) stage(l0, a, cur_t, next_t, s, S, g, acc, fa, rb, o, wave, lo);
+        // epilogue from registers; the next tile's first stages are in flight meanwhile
+        store_tile<OUT_FP32>(acc, a, cur_t.m0 + wm0, cur_t.n0 + wn0, lane);
+        if (!next_t.valid) break;
+#pragma unroll
+        for (int i = 0; i < FM; i++)
+#pragma unroll
+            for (int j = 0; j < FN; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        cur_t = next_t;
+        next_t = tile_desc(a, tile_of(a, p, k + 1));
+    }
+    wait_vmcnt<0>();  // the zero-filling loads past the last tile have landed before the workgroup ends
 }
 
 }  // namespace tiled_bf16
 
 bool gemm_bf16_tiled_ok(int64_t M, int64_t K, int64_t N, int64_t ldx, const void* X) {
     // 32-bit load offsets: 64 rows of X (64 * ldx * 2 < 2^31) and 16 row blocks of compressed tiles
-    // (16 * K / 64 * 1 KB < 2^31) stay below bit 31, which marks the loads past the last stage
-    return K % tiled_bf16::BK == 0 && ldx % 8 == 0 && (reinterpret_cast<uintptr_t>(X) & 15) == 0 && N > 64 &&
-           ldx < ((int64_t)1 << 24) && K < ((int64_t)1 << 22) && ((M + 255) / 256) * ((N + 255) / 256) < (1 << 30);
+    // (16 * K / 64 * 1 KB < 2^31) stay below bit 31, which marks the loads past the last tile
+    return ldx % 8 == 0 && (reinterpret_cast<uintptr_t>(X) & 15) == 0 && N > 64 && ldx < ((int64_t)1 << 24) &&
+           K < ((int64_t)1 << 22) && ((M + 255) / 256) * ((N + 255) / 256) < (1 << 30);
+}
+
+// Number of compute units of the current device (cached per device).
+static int device_cus() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
 }
 
 hipError_t launch_gemm_bf16_tiled(const uint16_t* values, const uint8_t* meta, int64_t M, int64_t K, const uint16_t* X,
@@ -445,7 +469,12 @@ hipError_t launch_gemm_bf16_tiled(const uint16_t* values, const uint8_t* meta, i
     a.tilesM = (int)((M + tiled_bf16::BM - 1) / tiled_bf16::BM);
     a.tilesN = (int)((N + tiled_bf16::BN - 1) / tiled_bf16::BN);
     a.y_vec = ((reinterpret_cast<uintptr_t>(Y) & 15) == 0) && ((ldy * (out_fp32 ? 4 : 2)) % 16 == 0);
-    const unsigned grid = (unsigned)(a.tilesM * a.tilesN);
+    const int T = a.tilesM * a.tilesN;
+    const int S = (int)((K + tiled_bf16::BK - 1) / tiled_bf16::BK);
+    // one workgroup per compute unit walking several tiles; one tile each when a tile has fewer than
+    // three stages (the cross-tile pipeline then has nothing to overlap)
+    const int cus = device_cus();
+    const unsigned grid = (unsigned)(S >= 3 && T > cus ? cus : T);
     if (out_fp32)
         hipLaunchKernelGGL(tiled_bf16::gemm_bf16_tiled_kernel<true>, dim3(grid), dim3(256), 0, s, a);
     else

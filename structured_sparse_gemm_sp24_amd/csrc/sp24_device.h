@@ -25,6 +25,14 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
+// Two fp32 -> packed bf16 (lo in bits 0..15), round to nearest even: one v_cvt_pk_bf16_f32. Same
+// result as f32_to_bf16_rne for every finite value and infinities (NaN payloads may differ).
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2_rne(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), bf16x2));
+}
+
 // IEEE half bits -> float (exact).
 __device__ __forceinline__ float f16_to_f32(uint32_t h) {
     _Float16 v = __builtin_bit_cast(_Float16, (uint16_t)h);
