@@ -1,0 +1,121 @@
+"""GPU parity at the full sizes of the benchmark workloads, through the same C-ABI calls (hence the same
+kernels and launch configurations) that bench.py times.
+
+Every selection-type result is compared whole: prune/compress values and metadata bit-exact (the full
+compressed buffers, padding included), column norms within 1e-5. GEMM outputs are compared on a
+seeded sample of rows that the oracle computes one by one (fp64 for bf16, exact int64 for int8), at
+every token count the workloads use: fp32 output within the fp32 summation bound element by element
+and 1e-3 Frobenius; bf16 output equal to the kernel's own fp32 result rounded to nearest even; int8
+output bit-exact.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import structured_sparse_gemm_sp24_amd as sp
+from structured_sparse_gemm_sp24_amd import synth
+from tests.gpu_util import bf16_to_f64, dev, fp32_sum_bound, frob_rel, host_bits, require_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+ROWS = 48  # sampled output rows per GEMM
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def _rows(M, seed):
+    rng = np.random.default_rng(seed)
+    r = np.sort(rng.choice(M, size=min(ROWS, M), replace=False))
+    return np.unique(np.concatenate([r, [0, M - 1]]))
+
+
+def _prune_bit_exact(W_host, dt, score=oracle.MAGNITUDE, norms=None, val_dtype=None):
+    """Prune on both sides; returns the oracle's (values, meta) after checking the GPU's bit for bit."""
+    kind = "bf16" if dt == oracle.BF16 else None
+    vdt = {oracle.BF16: torch.bfloat16, oracle.FP32: torch.float32, oracle.I8: torch.int8}[dt if val_dtype is None else val_dtype]
+    v, m = sp.sp24_prune_compress(dev(W_host, kind), score=score,
+                                  norms=None if norms is None else dev(norms), val_dtype=vdt)
+    rv, rm = oracle.prune_compress(W_host, dt, score, norms, val_dtype)
+    assert np.array_equal(host_bits(m), rm)
+    assert np.array_equal(host_bits(v).view(np.uint8), rv.view(np.uint8))  # bit patterns (-0, NaN-safe)
+    return v, m, rv, rm
+
+
+def _check_bf16(vd, md, rv, rm, M, X_host, rows):
+    K, N = X_host.shape
+    Xd = dev(X_host, "bf16")
+    r = torch.from_numpy(rows).cuda()
+    Yf = host_bits(sp.sp24_gemm_bf16(vd, md, M, Xd, out_dtype=torch.float32)[r])
+    Yb = host_bits(sp.sp24_gemm_bf16(vd, md, M, Xd, out_dtype=torch.bfloat16)[r])
+    Y64 = oracle.gemm_bf16(rv, rm, X_host, M, rows=rows)
+    dense = bf16_to_f64(oracle.decompress(rv, rm, oracle.BF16, M, K)[rows])
+    bound = fp32_sum_bound(np.abs(dense) @ np.abs(bf16_to_f64(X_host)), K)
+    assert np.all(np.abs(Yf.astype(np.float64) - Y64) <= bound)
+    assert frob_rel(Yf, Y64) <= 1e-3
+    assert np.array_equal(Yb, synth.f32_to_bf16_bits(Yf))
+
+
+def test_single_linear_256():
+    d = synth.single_linear_256()
+    say("full size: single linear 256 (fp32 prune, bf16 values, N = 64)")
+    _prune_bit_exact(d["W_f32"], oracle.FP32)  # fp32 values, bit copies
+    vd, md, rv, rm = _prune_bit_exact(d["W_f32"], oracle.FP32, val_dtype=oracle.BF16)
+    _check_bf16(vd, md, rv, rm, 256, d["X_bf16"], np.arange(256))
+
+
+def test_vit_b16_fc1():
+    d = synth.vit_b16_fc1()
+    say("full size: ViT-B/16 fc1 3072 x 768, N = 6304")
+    vd, md, rv, rm = _prune_bit_exact(d["W_bf16"], oracle.BF16)
+    _check_bf16(vd, md, rv, rm, 3072, d["X_bf16"], _rows(3072, 1))
+
+
+def test_bert_ffn_int8():
+    d = synth.bert_ffn_int8_dense()
+    for wk, xk, seed in (("W1_f32", "X1_f32", 2), ("W2_f32", "X2_f32", 3)):
+        W = d[wk]
+        M, K = W.shape
+        say(f"full size: BERT FFN int8 {M} x {K}, N = 8192")
+        # fp32 prune (GPU bit-exact with the oracle), then the host int8 preparation from the oracle's
+        # pruned weight, then the int8 prune/compress (bit-exact) and the int8 GEMM (bit-exact)
+        _, _, rv, rm = _prune_bit_exact(W, oracle.FP32)
+        Wp = oracle.decompress(rv, rm, oracle.FP32, M, K)
+        q, s_w = synth.quantize_rows(Wp)
+        xq, s_x = synth.quantize_tensor(d[xk])
+        scale = synth.dequant_scales(s_w, s_x)
+        v8, m8, rv8, rm8 = _prune_bit_exact(q, oracle.I8)
+        rows = _rows(M, seed)
+        r = torch.from_numpy(rows).cuda()
+        Xd = dev(xq)
+        got = host_bits(sp.sp24_gemm_i8(v8, m8, M, Xd, scale=dev(scale))[r])
+        got_acc = host_bits(sp.sp24_gemm_i8(v8, m8, M, Xd)[r])
+        acc, Y = oracle.gemm_i8(rv8, rm8, xq, M, scale, rows=rows)
+        assert np.array_equal(got_acc.astype(np.int64), acc)
+        assert np.array_equal(got.view(np.uint32), Y.view(np.uint32))
+
+
+@pytest.mark.parametrize("M", [11008, 4096])
+def test_llm_projection_wanda(M):
+    d = synth.llm_proj(M)
+    say(f"full size: LLM projection {M} x 4096 with Wanda, N in 1, 16, 4096")
+    norms = host_bits(sp.sp24_col_norms(dev(d["Xcal_bf16"], "bf16")))
+    ref_norms = oracle.col_norms(d["Xcal_bf16"])
+    assert np.max(np.abs(norms.astype(np.float64) - ref_norms) / ref_norms) <= 1e-5
+    # prune with the oracle's norms on both sides, so the selection compares bit for bit
+    vd, md, rv, rm = _prune_bit_exact(d["W_bf16"], oracle.BF16, oracle.WANDA, ref_norms)
+    rows = _rows(M, 4)
+    for N in (1, 16, 4096):
+        _check_bf16(vd, md, rv, rm, M, np.ascontiguousarray(d["X_bf16"][:, :N]), rows)
+
+
+def test_ffn_28672x8192():
+    d = synth.ffn_28672x8192(8192)
+    say("full size: FFN 28672 x 8192, N in 8, 64, 512, 8192")
+    vd, md, rv, rm = _prune_bit_exact(d["W_bf16"], oracle.BF16)
+    rows = _rows(28672, 5)[:24]
+    for N in (8, 64, 512, 8192):
+        _check_bf16(vd, md, rv, rm, 28672, np.ascontiguousarray(d["X_bf16"][:, :N]), rows)
