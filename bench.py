@@ -10,7 +10,9 @@ sweep. Inputs are resident in HBM before timing; steps rotate over enough copies
 Prints ONE JSON line: the step's dense-equivalent throughput (2*M*N*K per GEMM), the dominant
 kernel's roofline (its average duration from HIP events on the launch stream; algorithmic bytes or
 flops per launch; HBM traffic from the committed counter summary when the kernel source matches),
-and the CPU oracle timed on a bounded sample of the same workload.
+and the CPU oracle timed on a bounded sample of the same workload. The timed steps, and the repeated
+launches behind each kernel's average, are replayed from HIP graphs, so microsecond kernels are
+timed without the Python binding's per-call overhead between them.
 
 Roofline conventions: a 2:4 GEMM executes M*N*K/2 multiply-adds, i.e. M*N*K algorithmic flops, which
 are priced against the dense MFMA peak of the dtype (bf16 2516.6 TFLOP/s, int8 5033.2 TOP/s); this
@@ -64,7 +66,7 @@ class Kernel:
 
 
 def gemm_sources(N):
-    return ("gemm_bf16_tiled.hip", "sp24_device.h") if N >= TILED_MIN_N else ("gemm_bf16.hip", "sp24_device.h")
+    return ("gemm_bf16_tiled.hip", "sp24_device.h") if N >= TILED_MIN_N else ("gemm_bf16_skinny.hip", "sp24_device.h")
 
 
 # ----------------------------------------------------------------------------- workloads
@@ -305,24 +307,38 @@ def copy_calibration(mib: int, reps: int):
 
 # ----------------------------------------------------------------------------- timing
 
+def capture(calls):
+    """One HIP graph holding the given calls in order (captured on torch's capture stream, which the
+    library launches on), so the timed region runs them back to back without host gaps."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for c in calls:
+            c()
+    return g
+
+
 def kernel_time_ms(fn, copies, steps, warmup):
-    """Average duration of fn(copy) from HIP events recorded on the launch stream, rotating copies."""
+    """Average duration of fn(copy) over `steps` launches rotating the copies: the launches are replayed
+    from one HIP graph bracketed by HIP events on the stream they run on."""
     nc = len(copies)
     for i in range(warmup):
         fn(copies[i % nc])
-    ev = []
-    for i in range(steps):
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        fn(copies[i % nc])
-        e1.record()
-        ev.append((e0, e1))
     torch.cuda.synchronize()
-    return float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    g = capture([lambda i=i: fn(copies[i % nc]) for i in range(steps)])
+    g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
 
 
 def timed_steps(w, steps, warmup):
+    """Whole steps: W eager warmup steps, then exactly K steps replayed from one HIP graph, timed with the
+    host clock between two synchronizations. Per kernel: `kernel_time_ms` for each kernel of the step."""
     copies, kernels = w["copies"], w["kernels"]
 
     def step(c):
@@ -333,25 +349,13 @@ def timed_steps(w, steps, warmup):
     for i in range(warmup):
         step(copies[i % nc])
     torch.cuda.synchronize()
-    # whole steps: host clock around K steps bracketed by synchronizations
+    g = capture([lambda i=i: step(copies[i % nc]) for i in range(steps)])
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(steps):
-        step(copies[i % nc])
+    g.replay()
     torch.cuda.synchronize()
     t_total = time.perf_counter() - t0
-    # per-kernel durations: HIP events on the launch stream around each kernel, same rotation
-    ev = {k.name: [] for k in kernels}
-    for i in range(steps):
-        c = copies[i % nc]
-        for k in kernels:
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record()
-            k.fn(c)
-            e1.record()
-            ev[k.name].append((e0, e1))
-    torch.cuda.synchronize()
-    per_kernel_ms = {n: float(np.mean([a.elapsed_time(b) for a, b in e])) for n, e in ev.items()}
+    per_kernel_ms = {k.name: kernel_time_ms(k.fn, copies, steps, 1) for k in kernels}
     return t_total, per_kernel_ms
 
 

@@ -100,13 +100,18 @@ struct TileDesc {
     bool valid;
 };
 
-// Logical tile of workgroup p at its k-th turn, or -1. Within a turn the G workgroups hold tiles
-// [kG, kG + G); those of XCD x (p % 8 == x) hold a contiguous range of them.
+// Logical tile of workgroup p at its k-th turn, or -1. Turn k covers tiles [kG, kG + rem), rem =
+// min(G, T - kG), split evenly over the 8 XCDs (workgroup p runs on XCD p % 8): XCD x takes a
+// contiguous run of rem / 8 or rem / 8 + 1 of them, so a partial last turn still spreads its tiles,
+// and their output writes, over every XCD, and neighbouring tiles share an L2.
 __device__ __forceinline__ int tile_of(const Args& a, int p, int k) {
     const int G = gridDim.x, T = a.tilesM * a.tilesN;
-    const int pp = (G & 7) == 0 ? (p & 7) * (G >> 3) + (p >> 3) : p;
-    const int64_t L = (int64_t)k * G + pp;
-    return L < T ? (int)L : -1;
+    const int64_t base = (int64_t)k * G;
+    if (base >= T) return -1;
+    const int rem = (T - base) < G ? (int)(T - base) : G;
+    const int x = p & 7, i = p >> 3, q8 = rem >> 3, r8 = rem & 7;
+    if (i >= q8 + (x < r8 ? 1 : 0)) return -1;
+    return (int)base + x * q8 + (x < r8 ? x : r8) + i;
 }
 
 // Per-lane parts of the load offsets (the uniform parts go into the SGPR offset operand).

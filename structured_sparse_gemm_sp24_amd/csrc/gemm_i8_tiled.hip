@@ -21,9 +21,11 @@
 //
 // Loads are buffer loads with LDS destination whose whole byte offset is in the range-checked VGPR
 // operand: reads past this workgroup's row blocks, past K and past the end of X return zeros, and the
-// loads the pipeline issues past the last stage are pushed out of range on purpose. Tiles are ordered
-// XCD-first, then in groups of 8 tile-rows. The epilogue stages each wave's results through LDS (two
-// passes of 64 rows) so global stores are 16 bytes per lane.
+// loads the pipeline issues past the workgroup's last tile are pushed out of range on purpose.
+// Persistent like the bf16 kernel: one workgroup per CU walks its tiles (neighbouring tiles on the same
+// XCD at the same time, groups of 8 tile-rows) with the LDS pipeline continued across tiles; the
+// epilogue dequantizes in registers, transposes 4 x 4 blocks inside lane quads by DPP and stores 16
+// bytes per lane, so its stores drain while the next tile computes.
 #include "sp24_device.h"
 #include "sp24_launch.h"
 
@@ -82,6 +84,27 @@ struct Args {
     int y_vec;  // Y base and row pitch allow 16-byte stores
 };
 
+// Corner and compressed-tile descriptors of one tile; `valid` is false past the workgroup's last tile.
+struct TileDesc {
+    int64_t m0, n0;
+    i32x4 rA, rM;
+    bool valid;
+};
+
+// Logical tile of workgroup p at its k-th turn, or -1. Turn k covers tiles [kG, kG + rem), rem =
+// min(G, T - kG), split evenly over the 8 XCDs (workgroup p runs on XCD p % 8): XCD x takes a
+// contiguous run of rem / 8 or rem / 8 + 1 of them, so a partial last turn still spreads its tiles,
+// and their output writes, over every XCD, and neighbouring tiles share an L2.
+__device__ __forceinline__ int tile_of(const Args& a, int p, int k) {
+    const int G = gridDim.x, T = a.tilesM * a.tilesN;
+    const int64_t base = (int64_t)k * G;
+    if (base >= T) return -1;
+    const int rem = (T - base) < G ? (int)(T - base) : G;
+    const int x = p & 7, i = p >> 3, q8 = rem >> 3, r8 = rem & 7;
+    if (i >= q8 + (x < r8 ? 1 : 0)) return -1;
+    return (int)base + x * q8 + (x < r8 ? x : r8) + i;
+}
+
 // Swizzle of the 16-byte units of B row k (see the header).
 __device__ __forceinline__ int bswz(int k) { return (k & 7) | (((k >> 4) & 1) << 3); }
 
@@ -106,24 +129,44 @@ __device__ __forceinline__ LoadOffsets load_offsets(const Args& a, int lane, int
     return o;
 }
 
-// This wave's share of the loads of stage s into the buffer at LDS address `lds`. For s >= S the
-// offsets get bit 31 set (beyond every record count): zeros, no memory traffic.
-__device__ __forceinline__ void load_stage(uint32_t lds, const Args& a, i32x4 rA, i32x4 rM, int64_t n0, int s, int S,
-                                           int wave, const LoadOffsets& lo) {
+// This wave's share of the loads of stage s of tile td into the buffer at LDS address `lds`. When td
+// is not valid the offsets get bit 31 set (beyond every record count): zeros, no memory traffic.
+__device__ __forceinline__ void load_stage(uint32_t lds, const Args& a, const TileDesc& td, int s, int wave,
+                                           const LoadOffsets& lo) {
     const int64_t k0 = (int64_t)s * BK;
     const int tiles = (int)((a.K + BK - 1) / BK);
-    const uint32_t past = s < S ? 0u : 0x80000000u;
+    const uint32_t past = td.valid ? 0u : 0x80000000u;
 #pragma unroll
     for (int j = 0; j < 4; j++) {
         const int b = 4 * wave + j;
-        dma16(lds + b * 1024, lo.a + (((uint32_t)(b * tiles + s) * 1024u) | past), rA);
+        dma16(lds + b * 1024, lo.a + (((uint32_t)(b * tiles + s) * 1024u) | past), td.rA);
     }
     // metadata of blocks 4 wave .. 4 wave + 3 (one 256 B tile each) in one instruction
-    dma16(lds + A_BYTES + 4 * wave * 256, lo.m + (((uint32_t)(4 * wave * tiles + s) * 256u) | past), rM);
+    dma16(lds + A_BYTES + 4 * wave * 256, lo.m + (((uint32_t)(4 * wave * tiles + s) * 256u) | past), td.rM);
     // X's exact extent from this stage's corner, rounded up to whole dwords (see make_rsrc)
-    const i32x4 rB = make_rsrc(a.X + k0 * a.ldx + n0, (a.K - 1 - k0) * a.ldx + a.N - n0);
+    const i32x4 rB = make_rsrc(a.X + k0 * a.ldx + td.n0, td.valid ? (a.K - 1 - k0) * a.ldx + a.N - td.n0 : 0);
 #pragma unroll
     for (int h = 0; h < 8; h++) dma16(lds + A_BYTES + META_BYTES + (32 * wave + 4 * h) * B_ROW, lo.b[h], rB);
+}
+
+// Descriptor of logical tile L (-1: none); tiles walked in groups of GROUP_M tile-rows.
+__device__ __forceinline__ TileDesc tile_desc(const Args& a, int L) {
+    TileDesc td;
+    td.valid = L >= 0;
+    const int Lc = L >= 0 ? L : 0;
+    const int gsize = GROUP_M * a.tilesN;
+    const int g = Lc / gsize;
+    const int first_m = g * GROUP_M;
+    const int gm = (a.tilesM - first_m) < GROUP_M ? (a.tilesM - first_m) : GROUP_M;
+    const int in_g = Lc - g * gsize;
+    const int tm = first_m + in_g % gm, tn = in_g / gm;
+    td.m0 = (int64_t)tm * BM;
+    td.n0 = (int64_t)tn * BN;
+    const int64_t tiles = (a.K + BK - 1) / BK, blocks_left = (a.M + 15) / 16 - td.m0 / 16;
+    const int64_t blocks = blocks_left < BM / 16 ? blocks_left : BM / 16;
+    td.rA = make_rsrc(reinterpret_cast<const char*>(a.vals) + (td.m0 / 16) * tiles * 1024, blocks * tiles * 1024);
+    td.rM = make_rsrc(a.meta + (td.m0 / 16) * tiles * 256, blocks * tiles * 256);
+    return td;
 }
 
 struct LaneOffsets {
@@ -196,13 +239,14 @@ __device__ __forceinline__ void mfma_block(i32x4 (&acc)[FM][FN], const AFrags& f
         acc[i][j] = __builtin_amdgcn_smfmac_i32_16x16x128_i8(f.a[i], b, acc[i][j], (int)f.idx[i], 0, 0);
 }
 
-// One K stage: B fragments read two blocks ahead (ring of 4); before the last two blocks, the
-// barrier publishes stage s+1 and the loads of stage s+3 go into this stage's buffer; the next
+// One K stage: stage s of the current tile, the workgroup's g-th stage (selects the buffer). B
+// fragments are read two blocks ahead (ring of 4); before the last two blocks the barrier publishes
+// stage g+1 and the loads of stage s+3 of this tile (or s+3-S of the next) go into this buffer; the next
 // stage's A fragments are reloaded one by one inside the last block. No branches.
-__device__ __forceinline__ void stage(uint32_t l0, const Args& a, i32x4 rA, i32x4 rM, int64_t n0, int s, int S,
-                                      i32x4 (&acc)[FM][FN], AFrags& f, i32x8 (&rb)[4], const LaneOffsets& o, int wave,
-                                      const LoadOffsets& lo) {
-    const int cb = s % 3;
+__device__ __forceinline__ void stage(uint32_t l0, const Args& a, const TileDesc& cur_t, const TileDesc& next_t, int s,
+                                      int S, int g, i32x4 (&acc)[FM][FN], AFrags& f, i32x8 (&rb)[4],
+                                      const LaneOffsets& o, int wave, const LoadOffsets& lo) {
+    const int cb = g % 3;
     const uint32_t cur = l0 + cb * STAGE_BYTES;
     const uint32_t nxt = l0 + (cb == 2 ? 0 : cb + 1) * STAGE_BYTES;
 #pragma unroll
@@ -212,10 +256,11 @@ __device__ __forceinline__ void stage(uint32_t l0, const Args& a, i32x4 rA, i32x
         mfma_block(acc, f, rb[j & 3], j);
         __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of stage s are done
-    wait_vmcnt<LOADS_PER_STAGE>();       // stage s+1 has landed
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of stage g are done
+    wait_vmcnt<LOADS_PER_STAGE>();       // stage g+1 has landed
     __builtin_amdgcn_s_barrier();
-    load_stage(cur, a, rA, rM, n0, s + 3, S, wave, lo);
+    const bool here = s + 3 < S;
+    load_stage(cur, a, here ? cur_t : next_t, here ? s + 3 : s + 3 - S, wave, lo);
     rb[0] = read_b(nxt, o, 0);
     rb[1] = read_b(nxt, o, 1);
     __builtin_amdgcn_sched_barrier(0);
@@ -232,57 +277,54 @@ __device__ __forceinline__ void stage(uint32_t l0, const Args& a, i32x4 rA, i32x
     }
 }
 
-// Epilogue: two passes of 64 rows; the half-tile is written row-major (pitch EPI_ROW bytes, padded)
-// with one 4-byte write per value -- fl32(fl32(acc) * scale[m]) or the raw int32 -- and read back 16
-// bytes per lane.
-constexpr int EPI_ROW = 128 * 4 + 16;
-static_assert(4 * 64 * EPI_ROW <= 3 * STAGE_BYTES, "epilogue staging fits in the stage buffers");
+// Epilogue from registers: lane l = 16q + 4a + b holds rows 4q .. 4q+3 of column 4a + b of each
+// 16 x 16 fragment. The dequant -- fl32(fl32(acc) * scale[m]), one rounding multiply -- is applied per
+// row, then a 4 x 4 transpose inside each lane quad (DPP exchanges with lanes b ^ 2, then b ^ 1) leaves
+// lane b with row 4q + b, columns 4a .. 4a+3, stored as one 16-byte write. No LDS is used.
+__device__ __forceinline__ uint32_t dpp_xor2(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
+}
+__device__ __forceinline__ uint32_t dpp_xor1(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
+}
+__device__ __forceinline__ uint4 quad_transpose(uint32_t v0, uint32_t v1, uint32_t v2, uint32_t v3, int b) {
+    const bool low = b < 2, even = (b & 1) == 0;
+    const uint32_t r0 = dpp_xor2(low ? v2 : v0), r1 = dpp_xor2(low ? v3 : v1);
+    const uint32_t x0 = low ? v0 : r0, x1 = low ? v1 : r1, x2 = low ? r0 : v2, x3 = low ? r1 : v3;
+    const uint32_t s0 = dpp_xor1(even ? x1 : x0), s1 = dpp_xor1(even ? x3 : x2);
+    return even ? make_uint4(x0, s0, x2, s1) : make_uint4(s0, x1, s1, x3);
+}
 
 template <bool SCALE>
-__device__ __forceinline__ void store(char* smem, const i32x4 (&acc)[FM][FN], const Args& a, int64_t mw, int64_t nw,
-                                      int wave, int lane) {
-    const int r = lane & 15, q = lane >> 4;
-    char* tile = smem + wave * 64 * EPI_ROW;
-    const bool full = (mw + 128 <= a.M) && (nw + 128 <= a.N);
+__device__ __forceinline__ void store_tile(const i32x4 (&acc)[FM][FN], const Args& a, int64_t mw, int64_t nw, int lane) {
+    const int q = lane >> 4, r = lane & 15, b = r & 3, c4 = r & ~3;
+    const bool full = (mw + WM <= a.M) && (nw + WN <= a.N) && a.y_vec;
 #pragma unroll
-    for (int half = 0; half < 2; half++) {
+    for (int i = 0; i < FM; i++) {
+        const int64_t mq = mw + 16 * i + 4 * q;  // rows mq .. mq+3 before the transpose
+        float sc[4];
 #pragma unroll
-        for (int i = 0; i < FM / 2; i++) {
-            float sc[4];
+        for (int t = 0; t < 4; t++) sc[t] = (SCALE && mq + t < a.M) ? a.scale[mq + t] : 0.f;
+        const int64_t m = mq + b;  // this lane's row after the transpose
 #pragma unroll
-            for (int t = 0; t < 4; t++) {
-                const int64_t m = mw + 64 * half + 16 * i + 4 * q + t;
-                sc[t] = (SCALE && m < a.M) ? a.scale[m] : 0.f;
-            }
+        for (int j = 0; j < FN; j++) {
+            uint32_t v[4];
 #pragma unroll
-            for (int j = 0; j < FN; j++)
-#pragma unroll
-                for (int t = 0; t < 4; t++) {
-                    const int v = acc[half * (FM / 2) + i][j][t];
-                    const uint32_t bits = SCALE ? __float_as_uint(__fmul_rn((float)v, sc[t])) : (uint32_t)v;
-                    *reinterpret_cast<uint32_t*>(tile + (16 * i + 4 * q + t) * EPI_ROW + (16 * j + r) * 4) = bits;
-                }
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        __builtin_amdgcn_s_waitcnt(0xC07F);
-        __builtin_amdgcn_wave_barrier();
-#pragma unroll
-        for (int rr = 0; rr < 64; rr += 2) {
-            const int row = rr + (lane >> 5), col = 4 * (lane & 31);
-            const uint4 v = *reinterpret_cast<const uint4*>(tile + row * EPI_ROW + col * 4);
-            const int64_t m = mw + 64 * half + row, n = nw + col;
-            uint32_t* y = reinterpret_cast<uint32_t*>(a.Y) + m * a.ldy + n;
-            if (full && a.y_vec) {
-                *reinterpret_cast<uint4*>(y) = v;
+            for (int t = 0; t < 4; t++)
+                v[t] = SCALE ? __float_as_uint(__fmul_rn((float)acc[i][j][t], sc[t])) : (uint32_t)acc[i][j][t];
+            const uint4 y = quad_transpose(v[0], v[1], v[2], v[3], b);
+            const int64_t n = nw + 16 * j + c4;
+            uint32_t* p = reinterpret_cast<uint32_t*>(a.Y) + m * a.ldy + n;
+            if (full) {
+                *reinterpret_cast<uint4*>(p) = y;
             } else if (m < a.M) {
-                const uint32_t e[4] = {v.x, v.y, v.z, v.w};
+                const uint32_t e[4] = {y.x, y.y, y.z, y.w};
 #pragma unroll
                 for (int k = 0; k < 4; k++)
-                    if (n + k < a.N) y[k] = e[k];
+                    if (n + k < a.N) p[k] = e[k];
             }
         }
-        __builtin_amdgcn_s_waitcnt(0xC07F);
-        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_sched_barrier(0);  // one row block of fragments at a time
     }
 }
 
@@ -290,28 +332,15 @@ template <bool SCALE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_i8_tiled_kernel(Args a) {
     __shared__ __attribute__((aligned(16))) char smem[3 * STAGE_BYTES];
     const uint32_t l0 = (uint32_t)(size_t)(__attribute__((address_space(3))) char*)smem;
-    const uint32_t l1 = l0 + STAGE_BYTES, l2 = l0 + 2 * STAGE_BYTES;
 
-    // XCD-first, then grouped tile order
-    const int T = a.tilesM * a.tilesN;
-    const int pid = blockIdx.x;
-    const int xcd = pid & 7, slot = pid >> 3;
-    const int per = T >> 3, rem = T & 7;
-    const int logical = xcd * per + (xcd < rem ? xcd : rem) + slot;
-    const int gsize = GROUP_M * a.tilesN;
-    const int g = logical / gsize;
-    const int first_m = g * GROUP_M;
-    const int gm = (a.tilesM - first_m) < GROUP_M ? (a.tilesM - first_m) : GROUP_M;
-    const int in_g = logical - g * gsize;
-    const int tm = first_m + in_g % gm, tn = in_g / gm;
-    const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
-
+    const int p = blockIdx.x;
+    const int L = tile_of(a, p, 0);
+    if (L < 0) return;  // whole workgroup
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int wm0 = (wave >> 1) * WM, wn0 = (wave & 1) * WN;
-    const int64_t tiles = (a.K + BK - 1) / BK, blocks_left = (a.M + 15) / 16 - m0 / 16;
-    const int64_t blocks = blocks_left < BM / 16 ? blocks_left : BM / 16;
-    const i32x4 rA = make_rsrc(reinterpret_cast<const char*>(a.vals) + (m0 / 16) * tiles * 1024, blocks * tiles * 1024);
-    const i32x4 rM = make_rsrc(a.meta + (m0 / 16) * tiles * 256, blocks * tiles * 256);
+    const LaneOffsets o = lane_offsets(wm0, wn0, lane);
+    const LoadOffsets lo = load_offsets(a, lane, wave);
+    const int S = (int)((a.K + BK - 1) / BK);
 
     i32x4 acc[FM][FN];
 #pragma unroll
@@ -319,26 +348,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
         for (int j = 0; j < FN; j++) acc[i][j] = i32x4{0, 0, 0, 0};
 
-    const LaneOffsets o = lane_offsets(wm0, wn0, lane);
-    const LoadOffsets lo = load_offsets(a, lane, wave);
-    const int S = (int)tiles;
-
-    load_stage(l0, a, rA, rM, n0, 0, S, wave, lo);
-    load_stage(l1, a, rA, rM, n0, 1, S, wave, lo);
+    // three-stage pipeline continued across the workgroup's tiles (see stage()); with fewer than 3
+    // stages per tile every workgroup has one tile (see the launcher)
+    TileDesc cur_t = tile_desc(a, L);
+    TileDesc next_t = tile_desc(a, tile_of(a, p, 1));
+    load_stage(l0, a, S > 0 ? cur_t : next_t, 0, wave, lo);
+    load_stage(l0 + STAGE_BYTES, a, S > 1 ? cur_t : next_t, S > 1 ? 1 : 0, wave, lo);
     wait_vmcnt<LOADS_PER_STAGE>();
     __builtin_amdgcn_s_barrier();
-    load_stage(l2, a, rA, rM, n0, 2, S, wave, lo);
+    load_stage(l0 + 2 * STAGE_BYTES, a, S > 2 ? cur_t : next_t, S > 2 ? 2 : 0, wave, lo);
 
     AFrags fa;
     i32x8 rb[4];
     read_a(l0, o, fa);
     rb[0] = read_b(l0, o, 0);
     rb[1] = read_b(l0, o, 1);
-    for (int s = 0; s < S; s++) stage(l0, a, rA, rM, n0, s, S, acc, fa, rb, o, wave, lo);
-
-    wait_vmcnt<0>();               // the zero-filling loads past the last stage have landed
-    __builtin_amdgcn_s_barrier();  // every wave is done reading (and loading) the stage buffers
-    store<SCALE>(smem, acc, a, m0 + wm0, n0 + wn0, wave, lane);
+    int g = 0;
+    for (int k = 1;; k++) {
+        for (int s = 0; s < S; s++, g++) stage(l0, a, cur_t, next_t, s, S, g, acc, fa, rb, o, wave, lo);
+        store_tile<SCALE>(acc, a, cur_t.m0 + wm0, cur_t.n0 + wn0, lane);
+        if (!next_t.valid) break;
+#pragma unroll
+        for (int i = 0; i < FM; i++)
+#pragma unroll
+            for (int j = 0; j < FN; j++) acc[i][j] = i32x4{0, 0, 0, 0};
+        cur_t = next_t;
+        next_t = tile_desc(a, tile_of(a, p, k + 1));
+    }
+    wait_vmcnt<0>();  // the zero-filling loads past the last tile have landed before the workgroup ends
 }
 
 }  // namespace tiled_i8
@@ -359,7 +396,15 @@ hipError_t launch_gemm_i8_tiled(const int8_t* values, const uint8_t* meta, int64
     a.tilesM = (int)((M + tiled_i8::BM - 1) / tiled_i8::BM);
     a.tilesN = (int)((N + tiled_i8::BN - 1) / tiled_i8::BN);
     a.y_vec = ((reinterpret_cast<uintptr_t>(Y) & 15) == 0) && ((ldy * 4) % 16 == 0);
-    const unsigned grid = (unsigned)(a.tilesM * a.tilesN);
+    const int T = a.tilesM * a.tilesN;
+    const int S = (int)((K + tiled_i8::BK - 1) / tiled_i8::BK);
+    int cus = 0, dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                                 hipSuccess || cus <= 0)
+        cus = 256;
+    // one workgroup per compute unit walking several tiles; one tile each when a tile has fewer than
+    // three stages (the cross-tile pipeline then has nothing to overlap)
+    const unsigned grid = (unsigned)(S >= 3 && T > cus ? cus : T);
     if (scale)
         hipLaunchKernelGGL(tiled_i8::gemm_i8_tiled_kernel<true>, dim3(grid), dim3(256), 0, s, a);
     else
