@@ -306,77 +306,62 @@ __device__ __forceinline__ void stage(uint32_t l0, const Args& a, const TileDesc
     }
 }
 
-// ---------------------------------------------------------------- epilogues
-// The accumulators hold, per lane l = 16q + 4a + b, rows 4q .. 4q+3 of column 4a + b of each 16 x 16
-// fragment; Y wants runs along a row. A 4 x 4 transpose inside each lane quad (b = 0..3) by two DPP
-// exchanges -- with lane b ^ 2 (off-diagonal 2 x 2 blocks), then with lane b ^ 1 -- leaves lane b with
-// row 4q + b, columns 4a .. 4a+3, which it stores as one 8-byte (bf16) or 16-byte (fp32) write. No LDS
-// is used, so the next tile's loads can land in the stage buffers meanwhile.
-
-__device__ __forceinline__ uint32_t dpp_xor2(uint32_t v) {  // value of lane b ^ 2 of the quad
-    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
-}
-__device__ __forceinline__ uint32_t dpp_xor1(uint32_t v) {  // value of lane b ^ 1 of the quad
-    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
-}
-
-// bf16 out: pack rows (0,1) and (2,3), swap packed halves across b ^ 2, then 16-bit halves across b ^ 1.
-__device__ __forceinline__ uint2 quad_transpose_bf16(const f32x4& v, int b) {
-    const uint32_t p0 = pack_bf16x2_rne(v[0], v[1]);
-    const uint32_t p1 = pack_bf16x2_rne(v[2], v[3]);
-    const bool low = b < 2, even = (b & 1) == 0;
-    const uint32_t r = dpp_xor2(low ? p1 : p0);
-    const uint32_t x0 = low ? p0 : r, x1 = low ? r : p1;
-    const uint32_t r0 = dpp_xor1(x0), r1 = dpp_xor1(x1);
-    uint2 y;
-    y.x = even ? (x0 & 0xFFFFu) | (r0 << 16) : (r0 >> 16) | (x0 & 0xFFFF0000u);
-    y.y = even ? (x1 & 0xFFFFu) | (r1 << 16) : (r1 >> 16) | (x1 & 0xFFFF0000u);
-    return y;
-}
-
-// fp32 out: the same two exchanges on single values.
-__device__ __forceinline__ uint4 quad_transpose_f32(const f32x4& v, int b) {
-    const uint32_t v0 = __float_as_uint(v[0]), v1 = __float_as_uint(v[1]);
-    const uint32_t v2 = __float_as_uint(v[2]), v3 = __float_as_uint(v[3]);
-    const bool low = b < 2, even = (b & 1) == 0;
-    const uint32_t r0 = dpp_xor2(low ? v2 : v0), r1 = dpp_xor2(low ? v3 : v1);
-    const uint32_t x0 = low ? v0 : r0, x1 = low ? v1 : r1, x2 = low ? r0 : v2, x3 = low ? r1 : v3;
-    const uint32_t s0 = dpp_xor1(even ? x1 : x0), s1 = dpp_xor1(even ? x3 : x2);
-    return even ? make_uint4(x0, s0, x2, s1) : make_uint4(s0, x1, s1, x3);
-}
-
+// ---------------------------------------------------------------- epilogue
+// From registers, four fragments (64 columns) at a time: the quad transposes leave lane (q, 4a + b)
+// with row 4q + b, columns 4a .. 4a+3 of each fragment f; row_transpose4 then trades fragments for
+// row groups across the lane rows, so slot s holds row 4s + b, columns 4a .. 4a+3 of fragment q. Each
+// store instruction thus writes 4 rows x 64 consecutive columns -- whole 128-byte lines (bf16) or
+// pairs of them (fp32) -- so no line is ever cached half written (with power-of-two row pitches,
+// half-written lines were evicted and written back twice). No LDS is used, so the next tile's loads can
+// land in the stage buffers meanwhile.
 template <bool OUT_FP32>
 __device__ __forceinline__ void store_tile(const f32x4 (&acc)[FM][FN], const Args& a, int64_t mw, int64_t nw,
                                            int lane) {
     const int q = lane >> 4, r = lane & 15, b = r & 3, c4 = r & ~3;
     const bool full = (mw + WM <= a.M) && (nw + WN <= a.N) && a.y_vec;
+    constexpr int W = OUT_FP32 ? 4 : 2;
 #pragma unroll
     for (int i = 0; i < FM; i++) {
-        const int64_t m = mw + 16 * i + 4 * q + b;
 #pragma unroll
-        for (int j = 0; j < FN; j++) {
-            const int64_t n = nw + 16 * j + c4;
-            if (OUT_FP32) {
-                const uint4 y = quad_transpose_f32(acc[i][j], b);
-                uint32_t* p = reinterpret_cast<uint32_t*>(a.Y) + m * a.ldy + n;
-                if (full) {
-                    *reinterpret_cast<uint4*>(p) = y;
-                } else if (m < a.M) {
-                    const uint32_t e[4] = {y.x, y.y, y.z, y.w};
+        for (int jg = 0; jg < FN / 4; jg++) {
+            uint32_t v[4][W];
 #pragma unroll
-                    for (int k = 0; k < 4; k++)
-                        if (n + k < a.N) p[k] = e[k];
+            for (int f = 0; f < 4; f++) {
+                const f32x4 c = acc[i][4 * jg + f];
+                if constexpr (OUT_FP32) {
+#pragma unroll
+                    for (int t = 0; t < 4; t++) v[f][t] = __float_as_uint(c[t]);
+                    quad_transpose(v[f], b);
+                } else {
+                    const float e[4] = {c[0], c[1], c[2], c[3]};
+                    quad_transpose_bf16(e, v[f], b);
                 }
-            } else {
-                const uint2 y = quad_transpose_bf16(acc[i][j], b);
-                uint16_t* p = reinterpret_cast<uint16_t*>(a.Y) + m * a.ldy + n;
-                if (full) {
-                    *reinterpret_cast<uint2*>(p) = y;
-                } else if (m < a.M) {
-                    const uint16_t e[4] = {(uint16_t)y.x, (uint16_t)(y.x >> 16), (uint16_t)y.y, (uint16_t)(y.y >> 16)};
+            }
+            row_transpose4<W>(v);
+            const int64_t n = nw + 16 * (4 * jg + q) + c4;
 #pragma unroll
-                    for (int k = 0; k < 4; k++)
-                        if (n + k < a.N) p[k] = e[k];
+            for (int s = 0; s < 4; s++) {
+                const int64_t m = mw + 16 * i + 4 * s + b;
+                if constexpr (OUT_FP32) {
+                    uint32_t* p = reinterpret_cast<uint32_t*>(a.Y) + m * a.ldy + n;
+                    if (full) {
+                        *reinterpret_cast<uint4*>(p) = make_uint4(v[s][0], v[s][1], v[s][2], v[s][3]);
+                    } else if (m < a.M) {
+#pragma unroll
+                        for (int k = 0; k < 4; k++)
+                            if (n + k < a.N) p[k] = v[s][k];
+                    }
+                } else {
+                    uint16_t* p = reinterpret_cast<uint16_t*>(a.Y) + m * a.ldy + n;
+                    if (full) {
+                        *reinterpret_cast<uint2*>(p) = make_uint2(v[s][0], v[s][1]);
+                    } else if (m < a.M) {
+                        const uint16_t e[4] = {(uint16_t)v[s][0], (uint16_t)(v[s][0] >> 16), (uint16_t)v[s][1],
+                                               (uint16_t)(v[s][1] >> 16)};
+#pragma unroll
+                        for (int k = 0; k < 4; k++)
+                            if (n + k < a.N) p[k] = e[k];
+                    }
                 }
             }
         }

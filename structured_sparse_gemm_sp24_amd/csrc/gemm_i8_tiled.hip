@@ -277,51 +277,48 @@ __device__ __forceinline__ void stage(uint32_t l0, const Args& a, const TileDesc
     }
 }
 
-// Epilogue from registers: lane l = 16q + 4a + b holds rows 4q .. 4q+3 of column 4a + b of each
-// 16 x 16 fragment. The dequant -- fl32(fl32(acc) * scale[m]), one rounding multiply -- is applied per
-// row, then a 4 x 4 transpose inside each lane quad (DPP exchanges with lanes b ^ 2, then b ^ 1) leaves
-// lane b with row 4q + b, columns 4a .. 4a+3, stored as one 16-byte write. No LDS is used.
-__device__ __forceinline__ uint32_t dpp_xor2(uint32_t v) {
-    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
-}
-__device__ __forceinline__ uint32_t dpp_xor1(uint32_t v) {
-    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
-}
-__device__ __forceinline__ uint4 quad_transpose(uint32_t v0, uint32_t v1, uint32_t v2, uint32_t v3, int b) {
-    const bool low = b < 2, even = (b & 1) == 0;
-    const uint32_t r0 = dpp_xor2(low ? v2 : v0), r1 = dpp_xor2(low ? v3 : v1);
-    const uint32_t x0 = low ? v0 : r0, x1 = low ? v1 : r1, x2 = low ? r0 : v2, x3 = low ? r1 : v3;
-    const uint32_t s0 = dpp_xor1(even ? x1 : x0), s1 = dpp_xor1(even ? x3 : x2);
-    return even ? make_uint4(x0, s0, x2, s1) : make_uint4(s0, x1, s1, x3);
-}
-
+// Epilogue from registers, four fragments (64 columns) at a time. The dequant -- fl32(fl32(acc) *
+// scale[m]), one rounding multiply -- is applied per accumulator row; the quad transposes leave lane
+// (q, 4a + b) with row 4q + b, columns 4a .. 4a+3 of each fragment f, and row_transpose4 trades
+// fragments for row groups across the lane rows, so slot s holds row 4s + b, columns 4a .. 4a+3 of
+// fragment q. Each 16-byte store instruction thus writes 4 rows x 256 bytes -- whole 128-byte lines,
+// never a half-written line that the cache could evict and write back twice (as happened with
+// power-of-two row pitches). No LDS is used.
 template <bool SCALE>
 __device__ __forceinline__ void store_tile(const i32x4 (&acc)[FM][FN], const Args& a, int64_t mw, int64_t nw, int lane) {
     const int q = lane >> 4, r = lane & 15, b = r & 3, c4 = r & ~3;
     const bool full = (mw + WM <= a.M) && (nw + WN <= a.N) && a.y_vec;
 #pragma unroll
     for (int i = 0; i < FM; i++) {
-        const int64_t mq = mw + 16 * i + 4 * q;  // rows mq .. mq+3 before the transpose
+        const int64_t mq = mw + 16 * i + 4 * q;  // accumulator rows mq .. mq+3
         float sc[4];
 #pragma unroll
         for (int t = 0; t < 4; t++) sc[t] = (SCALE && mq + t < a.M) ? a.scale[mq + t] : 0.f;
-        const int64_t m = mq + b;  // this lane's row after the transpose
 #pragma unroll
-        for (int j = 0; j < FN; j++) {
-            uint32_t v[4];
+        for (int jg = 0; jg < FN / 4; jg++) {
+            uint32_t v[4][4];
 #pragma unroll
-            for (int t = 0; t < 4; t++)
-                v[t] = SCALE ? __float_as_uint(__fmul_rn((float)acc[i][j][t], sc[t])) : (uint32_t)acc[i][j][t];
-            const uint4 y = quad_transpose(v[0], v[1], v[2], v[3], b);
-            const int64_t n = nw + 16 * j + c4;
-            uint32_t* p = reinterpret_cast<uint32_t*>(a.Y) + m * a.ldy + n;
-            if (full) {
-                *reinterpret_cast<uint4*>(p) = y;
-            } else if (m < a.M) {
-                const uint32_t e[4] = {y.x, y.y, y.z, y.w};
+            for (int f = 0; f < 4; f++) {
 #pragma unroll
-                for (int k = 0; k < 4; k++)
-                    if (n + k < a.N) p[k] = e[k];
+                for (int t = 0; t < 4; t++) {
+                    const int x = acc[i][4 * jg + f][t];
+                    v[f][t] = SCALE ? __float_as_uint(__fmul_rn((float)x, sc[t])) : (uint32_t)x;
+                }
+                quad_transpose(v[f], b);
+            }
+            row_transpose4<4>(v);
+            const int64_t n = nw + 16 * (4 * jg + q) + c4;
+#pragma unroll
+            for (int s = 0; s < 4; s++) {
+                const int64_t m = mw + 16 * i + 4 * s + b;
+                uint32_t* p = reinterpret_cast<uint32_t*>(a.Y) + m * a.ldy + n;
+                if (full) {
+                    *reinterpret_cast<uint4*>(p) = make_uint4(v[s][0], v[s][1], v[s][2], v[s][3]);
+                } else if (m < a.M) {
+#pragma unroll
+                    for (int k = 0; k < 4; k++)
+                        if (n + k < a.N) p[k] = v[s][k];
+                }
             }
         }
         __builtin_amdgcn_sched_barrier(0);  // one row block of fragments at a time

@@ -50,6 +50,68 @@ __device__ __forceinline__ int64_t tiled_offset(int64_t i, int64_t b, int64_t ti
     return (((i >> 4) * tiles_per_row + t) * 4 + rem / Q) * (16 * Q) + (i & 15) * Q + rem % Q;
 }
 
+// ---------------------------------------------------------------- register-only epilogue helpers
+// An MFMA 16 x 16 accumulator fragment gives lane l = 16q + 4a + b rows 4q .. 4q+3 of column 4a + b;
+// row-major outputs want runs along a row. quad_transpose: a 4 x 4 transpose inside each lane quad
+// (b = 0..3) by two DPP exchanges -- with lane b ^ 2 (off-diagonal 2 x 2 blocks), then with lane b ^ 1
+// -- leaves lane b with row 4q + b, columns 4a .. 4a+3.
+__device__ __forceinline__ uint32_t dpp_xor2(uint32_t v) {  // value of lane b ^ 2 of the quad
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
+}
+__device__ __forceinline__ uint32_t dpp_xor1(uint32_t v) {  // value of lane b ^ 1 of the quad
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
+}
+// 32-bit elements: v[t] = row 4q + t of this lane's column on entry; on exit element t is column 4a + t
+// of row 4q + b.
+__device__ __forceinline__ void quad_transpose(uint32_t (&v)[4], int b) {
+    const bool low = b < 2, even = (b & 1) == 0;
+    const uint32_t r0 = dpp_xor2(low ? v[2] : v[0]), r1 = dpp_xor2(low ? v[3] : v[1]);
+    const uint32_t x0 = low ? v[0] : r0, x1 = low ? v[1] : r1, x2 = low ? r0 : v[2], x3 = low ? r1 : v[3];
+    const uint32_t s0 = dpp_xor1(even ? x1 : x0), s1 = dpp_xor1(even ? x3 : x2);
+    v[0] = even ? x0 : s0;
+    v[1] = even ? s0 : x1;
+    v[2] = even ? x2 : s1;
+    v[3] = even ? s1 : x3;
+}
+// fp32 rows -> bf16 (round to nearest even), then the same transpose on packed pairs: pack rows
+// (0,1) and (2,3), swap packed words across b ^ 2, then 16-bit halves across b ^ 1. v[0] holds columns
+// 4a, 4a+1 of row 4q + b on exit, v[1] columns 4a+2, 4a+3.
+__device__ __forceinline__ void quad_transpose_bf16(const float (&f)[4], uint32_t (&v)[2], int b) {
+    const uint32_t p0 = pack_bf16x2_rne(f[0], f[1]);
+    const uint32_t p1 = pack_bf16x2_rne(f[2], f[3]);
+    const bool low = b < 2, even = (b & 1) == 0;
+    const uint32_t r = dpp_xor2(low ? p1 : p0);
+    const uint32_t x0 = low ? p0 : r, x1 = low ? r : p1;
+    const uint32_t r0 = dpp_xor1(x0), r1 = dpp_xor1(x1);
+    v[0] = even ? (x0 & 0xFFFFu) | (r0 << 16) : (r0 >> 16) | (x0 & 0xFFFF0000u);
+    v[1] = even ? (x1 & 0xFFFFu) | (r1 << 16) : (r1 >> 16) | (x1 & 0xFFFF0000u);
+}
+// gfx950 lane-row swaps (a row is 16 lanes): swap32 trades lanes 32..63 of x for lanes 0..31 of y;
+// swap16 trades lanes 16..31 and 48..63 of x for lanes 0..15 and 32..47 of y.
+__device__ __forceinline__ void swap32(uint32_t& x, uint32_t& y) {
+    const auto r = __builtin_amdgcn_permlane32_swap(x, y, false, false);
+    x = r[0];
+    y = r[1];
+}
+__device__ __forceinline__ void swap16(uint32_t& x, uint32_t& y) {
+    const auto r = __builtin_amdgcn_permlane16_swap(x, y, false, false);
+    x = r[0];
+    y = r[1];
+}
+// Transpose of (lane row q = lane / 16, slot f) over four slots of W words: on entry lane row q holds
+// item (q, f) in slot f, on exit item (f, q). swap32 on slot pairs (0,2), (1,3) exchanges the 2 x 2
+// blocks across lane halves, swap16 on (0,1), (2,3) the elements inside them.
+template <int W>
+__device__ __forceinline__ void row_transpose4(uint32_t (&v)[4][W]) {
+#pragma unroll
+    for (int w = 0; w < W; w++) {
+        swap32(v[0][w], v[2][w]);
+        swap32(v[1][w], v[3][w]);
+        swap16(v[0][w], v[1][w]);
+        swap16(v[2][w], v[3][w]);
+    }
+}
+
 // Wave-level sum of a double (64 lanes) by butterfly shuffles.
 __device__ __forceinline__ double wave_sum_f64(double v) {
 #pragma unroll
