@@ -89,7 +89,7 @@ struct Args {
     void* Y;
     int64_t M, K, N, ldx, ldy;
     int tilesM, tilesN;
-    int y_vec;  // Y base and row pitch allow 8-byte (bf16) / 16-byte (fp32) stores
+    int y_vec;  // Y base and row pitch allow 8-byte (bf16) / 16-byte (fp32) stores, 4 rows < 2^31 bytes
 };
 
 // Where the loads of one tile come from: its corner and the buffer descriptors of its compressed
@@ -312,14 +312,20 @@ __device__ __forceinline__ void stage(uint32_t l0, const Args& a, const TileDesc
 // row groups across the lane rows, so slot s holds row 4s + b, columns 4a .. 4a+3 of fragment q. Each
 // store instruction thus writes 4 rows x 64 consecutive columns -- whole 128-byte lines (bf16) or
 // pairs of them (fp32) -- so no line is ever cached half written (with power-of-two row pitches,
-// half-written lines were evicted and written back twice). No LDS is used, so the next tile's loads can
-// land in the stage buffers meanwhile.
-template <bool OUT_FP32>
+// half-written lines were evicted and written back twice). The epilogue is bound by VALU issue (each
+// wave64 VALU instruction takes 4 cycles), so it keeps to cross-lane moves (DPP, permlane swaps) and
+// selects, without branches. No LDS is used, so the next tile's loads can land in the stage buffers
+// meanwhile.
+// FULL: the wave's whole 128 x 128 block lies inside Y and vector stores are allowed (then the row
+// offsets of a lane quad fit 32 bits); otherwise every element is bounds-checked.
+template <bool OUT_FP32, bool FULL>
 __device__ __forceinline__ void store_tile(const f32x4 (&acc)[FM][FN], const Args& a, int64_t mw, int64_t nw,
                                            int lane) {
+    constexpr int W = OUT_FP32 ? 4 : 2, ES = OUT_FP32 ? 4 : 2;
     const int q = lane >> 4, r = lane & 15, b = r & 3, c4 = r & ~3;
-    const bool full = (mw + WM <= a.M) && (nw + WN <= a.N) && a.y_vec;
-    constexpr int W = OUT_FP32 ? 4 : 2;
+    const uint32_t sel = half_sel(b);
+    char* const y0 = static_cast<char*>(a.Y) + (mw * a.ldy + nw) * ES;  // wave-uniform corner
+    const uint32_t lane_off = FULL ? (uint32_t)((b * a.ldy + 16 * q + c4) * ES) : 0u;
 #pragma unroll
     for (int i = 0; i < FM; i++) {
 #pragma unroll
@@ -334,33 +340,30 @@ __device__ __forceinline__ void store_tile(const f32x4 (&acc)[FM][FN], const Arg
                     quad_transpose(v[f], b);
                 } else {
                     const float e[4] = {c[0], c[1], c[2], c[3]};
-                    quad_transpose_bf16(e, v[f], b);
+                    quad_transpose_bf16(e, v[f], b, sel);
                 }
             }
             row_transpose4<W>(v);
-            const int64_t n = nw + 16 * (4 * jg + q) + c4;
 #pragma unroll
             for (int s = 0; s < 4; s++) {
-                const int64_t m = mw + 16 * i + 4 * s + b;
-                if constexpr (OUT_FP32) {
-                    uint32_t* p = reinterpret_cast<uint32_t*>(a.Y) + m * a.ldy + n;
-                    if (full) {
+                if constexpr (FULL) {
+                    char* const p = y0 + ((16 * i + 4 * s) * a.ldy + 64 * jg) * ES + lane_off;
+                    if constexpr (OUT_FP32)
                         *reinterpret_cast<uint4*>(p) = make_uint4(v[s][0], v[s][1], v[s][2], v[s][3]);
-                    } else if (m < a.M) {
-#pragma unroll
-                        for (int k = 0; k < 4; k++)
-                            if (n + k < a.N) p[k] = v[s][k];
-                    }
-                } else {
-                    uint16_t* p = reinterpret_cast<uint16_t*>(a.Y) + m * a.ldy + n;
-                    if (full) {
+                    else
                         *reinterpret_cast<uint2*>(p) = make_uint2(v[s][0], v[s][1]);
-                    } else if (m < a.M) {
-                        const uint16_t e[4] = {(uint16_t)v[s][0], (uint16_t)(v[s][0] >> 16), (uint16_t)v[s][1],
-                                               (uint16_t)(v[s][1] >> 16)};
+                } else {
+                    const int64_t m = mw + 16 * i + 4 * s + b, n = nw + 16 * (4 * jg + q) + c4;
+                    if (m < a.M) {
 #pragma unroll
-                        for (int k = 0; k < 4; k++)
-                            if (n + k < a.N) p[k] = e[k];
+                        for (int k = 0; k < 4; k++) {
+                            if (n + k >= a.N) continue;
+                            const uint32_t w = v[s][OUT_FP32 ? k : k >> 1];
+                            if constexpr (OUT_FP32)
+                                reinterpret_cast<uint32_t*>(a.Y)[m * a.ldy + n + k] = w;
+                            else
+                                reinterpret_cast<uint16_t*>(a.Y)[m * a.ldy + n + k] = (uint16_t)(k & 1 ? w >> 16 : w);
+                        }
                     }
                 }
             }
@@ -417,7 +420,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     for (int k = 1;; k++) {
         for (int s = 0; s < S; s++, g++) stage(l0, a, cur_t, next_t, s, S, g, acc, fa, rb, o, wave, lo);
         // epilogue from registers; the next tile's first stages are in flight meanwhile
-        store_tile<OUT_FP32>(acc, a, cur_t.m0 + wm0, cur_t.n0 + wn0, lane);
+        {
+            const int64_t mw = cur_t.m0 + wm0, nw = cur_t.n0 + wn0;
+            if ((mw + WM <= a.M) && (nw + WN <= a.N) && a.y_vec)
+                store_tile<OUT_FP32, true>(acc, a, mw, nw, lane);
+            else
+                store_tile<OUT_FP32, false>(acc, a, mw, nw, lane);
+        }
         if (!next_t.valid) break;
 #pragma unroll
         for (int i = 0; i < FM; i++)
@@ -458,7 +467,8 @@ hipError_t launch_gemm_bf16_tiled(const uint16_t* values, const uint8_t* meta, i
     a.M = M; a.K = K; a.N = N; a.ldx = ldx; a.ldy = ldy;
     a.tilesM = (int)((M + tiled_bf16::BM - 1) / tiled_bf16::BM);
     a.tilesN = (int)((N + tiled_bf16::BN - 1) / tiled_bf16::BN);
-    a.y_vec = ((reinterpret_cast<uintptr_t>(Y) & 15) == 0) && ((ldy * (out_fp32 ? 4 : 2)) % 16 == 0);
+    a.y_vec = ((reinterpret_cast<uintptr_t>(Y) & 15) == 0) && ((ldy * (out_fp32 ? 4 : 2)) % 16 == 0) &&
+              ldy * (out_fp32 ? 4 : 2) * 4 < ((int64_t)1 << 31);
     const int T = a.tilesM * a.tilesN;
     const int S = (int)((K + tiled_bf16::BK - 1) / tiled_bf16::BK);
     // one workgroup per compute unit walking several tiles; one tile each when a tile has fewer than

@@ -81,7 +81,7 @@ struct Args {
     void* Y;
     int64_t M, K, N, ldx, ldy;
     int tilesM, tilesN;
-    int y_vec;  // Y base and row pitch allow 16-byte stores
+    int y_vec;  // Y base and row pitch allow 16-byte stores, 4 rows < 2^31 bytes
 };
 
 // Corner and compressed-tile descriptors of one tile; `valid` is false past the workgroup's last tile.
@@ -284,16 +284,19 @@ __device__ __forceinline__ void stage(uint32_t l0, const Args& a, const TileDesc
 // fragment q. Each 16-byte store instruction thus writes 4 rows x 256 bytes -- whole 128-byte lines,
 // never a half-written line that the cache could evict and write back twice (as happened with
 // power-of-two row pitches). No LDS is used.
-template <bool SCALE>
+// FULL: the wave's whole 128 x 128 block lies inside Y and 16-byte stores are allowed (then the row
+// offsets of a lane quad fit 32 bits); otherwise every element is bounds-checked.
+template <bool SCALE, bool FULL>
 __device__ __forceinline__ void store_tile(const i32x4 (&acc)[FM][FN], const Args& a, int64_t mw, int64_t nw, int lane) {
     const int q = lane >> 4, r = lane & 15, b = r & 3, c4 = r & ~3;
-    const bool full = (mw + WM <= a.M) && (nw + WN <= a.N) && a.y_vec;
+    char* const y0 = reinterpret_cast<char*>(a.Y) + (mw * a.ldy + nw) * 4;  // wave-uniform corner
+    const uint32_t lane_off = FULL ? (uint32_t)((b * a.ldy + 16 * q + c4) * 4) : 0u;
 #pragma unroll
     for (int i = 0; i < FM; i++) {
         const int64_t mq = mw + 16 * i + 4 * q;  // accumulator rows mq .. mq+3
         float sc[4];
 #pragma unroll
-        for (int t = 0; t < 4; t++) sc[t] = (SCALE && mq + t < a.M) ? a.scale[mq + t] : 0.f;
+        for (int t = 0; t < 4; t++) sc[t] = (SCALE && (FULL || mq + t < a.M)) ? a.scale[mq + t] : 0.f;
 #pragma unroll
         for (int jg = 0; jg < FN / 4; jg++) {
             uint32_t v[4][4];
@@ -307,17 +310,19 @@ __device__ __forceinline__ void store_tile(const i32x4 (&acc)[FM][FN], const Arg
                 quad_transpose(v[f], b);
             }
             row_transpose4<4>(v);
-            const int64_t n = nw + 16 * (4 * jg + q) + c4;
 #pragma unroll
             for (int s = 0; s < 4; s++) {
-                const int64_t m = mw + 16 * i + 4 * s + b;
-                uint32_t* p = reinterpret_cast<uint32_t*>(a.Y) + m * a.ldy + n;
-                if (full) {
+                if constexpr (FULL) {
+                    char* const p = y0 + ((16 * i + 4 * s) * a.ldy + 64 * jg) * 4 + lane_off;
                     *reinterpret_cast<uint4*>(p) = make_uint4(v[s][0], v[s][1], v[s][2], v[s][3]);
-                } else if (m < a.M) {
+                } else {
+                    const int64_t m = mw + 16 * i + 4 * s + b, n = nw + 16 * (4 * jg + q) + c4;
+                    uint32_t* p = reinterpret_cast<uint32_t*>(a.Y) + m * a.ldy + n;
+                    if (m < a.M) {
 #pragma unroll
-                    for (int k = 0; k < 4; k++)
-                        if (n + k < a.N) p[k] = v[s][k];
+                        for (int k = 0; k < 4; k++)
+                            if (n + k < a.N) p[k] = v[s][k];
+                    }
                 }
             }
         }
@@ -363,7 +368,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     int g = 0;
     for (int k = 1;; k++) {
         for (int s = 0; s < S; s++, g++) stage(l0, a, cur_t, next_t, s, S, g, acc, fa, rb, o, wave, lo);
-        store_tile<SCALE>(acc, a, cur_t.m0 + wm0, cur_t.n0 + wn0, lane);
+        {
+            const int64_t mw = cur_t.m0 + wm0, nw = cur_t.n0 + wn0;
+            if ((mw + WM <= a.M) && (nw + WN <= a.N) && a.y_vec)
+                store_tile<SCALE, true>(acc, a, mw, nw, lane);
+            else
+                store_tile<SCALE, false>(acc, a, mw, nw, lane);
+        }
         if (!next_t.valid) break;
 #pragma unroll
         for (int i = 0; i < FM; i++)
@@ -392,7 +403,7 @@ hipError_t launch_gemm_i8_tiled(const int8_t* values, const uint8_t* meta, int64
     a.M = M; a.K = K; a.N = N; a.ldx = ldx; a.ldy = ldy;
     a.tilesM = (int)((M + tiled_i8::BM - 1) / tiled_i8::BM);
     a.tilesN = (int)((N + tiled_i8::BN - 1) / tiled_i8::BN);
-    a.y_vec = ((reinterpret_cast<uintptr_t>(Y) & 15) == 0) && ((ldy * 4) % 16 == 0);
+    a.y_vec = ((reinterpret_cast<uintptr_t>(Y) & 15) == 0) && ((ldy * 4) % 16 == 0) && ldy * 16 < ((int64_t)1 << 31);
     const int T = a.tilesM * a.tilesN;
     const int S = (int)((K + tiled_i8::BK - 1) / tiled_i8::BK);
     int cus = 0, dev = 0;

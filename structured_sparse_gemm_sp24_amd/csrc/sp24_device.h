@@ -74,17 +74,23 @@ __device__ __forceinline__ void quad_transpose(uint32_t (&v)[4], int b) {
     v[3] = even ? s1 : x3;
 }
 // fp32 rows -> bf16 (round to nearest even), then the same transpose on packed pairs: pack rows
-// (0,1) and (2,3), swap packed words across b ^ 2, then 16-bit halves across b ^ 1. v[0] holds columns
-// 4a, 4a+1 of row 4q + b on exit, v[1] columns 4a+2, 4a+3.
-__device__ __forceinline__ void quad_transpose_bf16(const float (&f)[4], uint32_t (&v)[2], int b) {
+// (0,1) and (2,3), swap packed words across b ^ 2, then 16-bit halves across b ^ 1 (one byte permute
+// per word; `sel` is half_sel(b)). v[0] holds columns 4a, 4a+1 of row 4q + b on exit, v[1] columns
+// 4a+2, 4a+3.
+__device__ __forceinline__ uint32_t half_sel(int b) {
+    // v_perm_b32 byte selectors over {hi = partner word, lo = own word}: even lanes keep their low half
+    // and take the partner's low half as high half; odd lanes take the partner's high half as low half
+    // and keep their high half
+    return (b & 1) == 0 ? 0x05040100u : 0x03020706u;
+}
+__device__ __forceinline__ void quad_transpose_bf16(const float (&f)[4], uint32_t (&v)[2], int b, uint32_t sel) {
     const uint32_t p0 = pack_bf16x2_rne(f[0], f[1]);
     const uint32_t p1 = pack_bf16x2_rne(f[2], f[3]);
-    const bool low = b < 2, even = (b & 1) == 0;
+    const bool low = b < 2;
     const uint32_t r = dpp_xor2(low ? p1 : p0);
     const uint32_t x0 = low ? p0 : r, x1 = low ? r : p1;
-    const uint32_t r0 = dpp_xor1(x0), r1 = dpp_xor1(x1);
-    v[0] = even ? (x0 & 0xFFFFu) | (r0 << 16) : (r0 >> 16) | (x0 & 0xFFFF0000u);
-    v[1] = even ? (x1 & 0xFFFFu) | (r1 << 16) : (r1 >> 16) | (x1 & 0xFFFF0000u);
+    v[0] = __builtin_amdgcn_perm(dpp_xor1(x0), x0, sel);
+    v[1] = __builtin_amdgcn_perm(dpp_xor1(x1), x1, sel);
 }
 // gfx950 lane-row swaps (a row is 16 lanes): swap32 trades lanes 32..63 of x for lanes 0..31 of y;
 // swap16 trades lanes 16..31 and 48..63 of x for lanes 0..15 and 32..47 of y.
