@@ -89,6 +89,13 @@ typedef enum { SP24_BF16 = 0, SP24_FP16 = 1, SP24_FP32 = 2, SP24_I8 = 3, SP24_I3
 
 typedef enum { SP24_SCORE_MAGNITUDE = 0, SP24_SCORE_WANDA = 1 } sp24_score;
 
+/* Operand layout of the *_ex GEMMs:
+ *  SP24_FEATURE_MAJOR: X is K x N (input channels x tokens; one NCHW image of a 1x1 conv is
+ *                      Cin x H*W), Y is M x N -- the layout of sp24_gemm_bf16 / sp24_gemm_i8.
+ *  SP24_TOKEN_MAJOR:   X is N x K (tokens x input channels, the layout of a Linear layer's input),
+ *                      Y is N x M; row pitches ldx >= K and ldy >= M. */
+typedef enum { SP24_FEATURE_MAJOR = 0, SP24_TOKEN_MAJOR = 1 } sp24_layout;
+
 /* Per-input-channel activation norms for Wanda scoring (zyxy.net Wanda lecture, section 2.1).
  *   norms[j] = sqrt( sum_{n<N} X[j*ldx + n]^2 ),  j < K.
  * X: bf16, K x N, any row pitch ldx >= N (16-byte aligned base). norms: fp32[K].
@@ -135,6 +142,29 @@ int sp24_gemm_bf16(const void* values, const uint8_t* meta, int64_t M, int64_t K
  *   ldy >= N. */
 int sp24_gemm_i8(const int8_t* values, const uint8_t* meta, int64_t M, int64_t K, const int8_t* X, int64_t N,
                  int64_t ldx, const float* scale, void* Y, int64_t ldy, void* stream);
+
+/* The bf16 GEMM for either operand layout and for a batch of products sharing one weight (Orin NN
+ * design, Chapter 7, section 2.1: 2:4 sparsity applies to Linear and 1x1-conv layers alike; a 1x1
+ * conv over B NCHW images is B feature-major products, a Linear layer's input is token-major):
+ *   for b < batch:  Y_b = W_2:4 * X_b  with  X_b = X + b * x_batch_stride,  Y_b = Y + b * y_batch_stride
+ *   (strides in elements). layout is an sp24_layout: feature-major X_b is K x N (pitch ldx >= N) and Y_b
+ *   M x N (pitch ldy >= N); token-major X_b is N x K (ldx >= K) and Y_b N x M (ldy >= M), i.e.
+ *   Y_b[n, m] = sum_g sum_t values[m, 2g+t] * X_b[n, 4g + i_t(m, g)].
+ *   batch >= 1. With batch > 1: x_batch_stride >= 0 (entries may overlap or repeat: X is only read),
+ *   y_batch_stride at least one Y entry's extent (entries of Y must not overlap), and both strides keep
+ *   every entry's base 16-byte aligned; with batch == 1 the strides are ignored. Everything else as
+ *   sp24_gemm_bf16, which is this call with batch 1 and SP24_FEATURE_MAJOR. */
+int sp24_gemm_bf16_ex(const void* values, const uint8_t* meta, int64_t M, int64_t K, const void* X, int64_t N,
+                      int64_t ldx, int64_t x_batch_stride, void* Y, int out_dtype, int64_t ldy, int64_t y_batch_stride,
+                      int64_t batch, int layout, void* stream);
+
+/* The int8 GEMM for either operand layout and a batch of products sharing one weight; operands,
+ * strides and rules as sp24_gemm_bf16_ex (X int8, Y fp32 with scale or int32 without; the dequant
+ * scale is per output channel m in both layouts). sp24_gemm_i8 is this call with batch 1 and
+ * SP24_FEATURE_MAJOR. */
+int sp24_gemm_i8_ex(const int8_t* values, const uint8_t* meta, int64_t M, int64_t K, const int8_t* X, int64_t N,
+                    int64_t ldx, int64_t x_batch_stride, const float* scale, void* Y, int64_t ldy,
+                    int64_t y_batch_stride, int64_t batch, int layout, void* stream);
 
 /* Static description of a status code. */
 const char* sp24_status_string(int status);

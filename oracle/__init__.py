@@ -165,8 +165,22 @@ def _rows_arg(rows, M):
     return np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
 
 
-def gemm_bf16(values: np.ndarray, meta: np.ndarray, X: np.ndarray, M: int, rows=None) -> np.ndarray:
-    """Y[r, :] = (pruned W)[rows[r], :] . X in float64 (values/X: bf16 bits as uint16; K = X rows)."""
+def _feature_major(X: np.ndarray, layout: str) -> np.ndarray:
+    """Token-major X (N x K, a Linear layer's input) holds the same numbers as feature-major X (K x N),
+    transposed: the product is the same sum, only the storage order of its operands and result differs."""
+    if layout == "feature":
+        return X
+    if layout == "token":
+        return X.T
+    raise ValueError(layout)
+
+
+def gemm_bf16(values: np.ndarray, meta: np.ndarray, X: np.ndarray, M: int, rows=None,
+              layout: str = "feature") -> np.ndarray:
+    """Y[r, :] = (pruned W)[rows[r], :] . X in float64 (values/X: bf16 bits as uint16; K = X rows).
+    layout "token": X is N x K and the result is returned N x len(rows) (Y[n, r])."""
+    if layout != "feature":
+        return gemm_bf16(values, meta, _feature_major(X, layout), M, rows).T
     values = np.ascontiguousarray(_c(values, np.uint16))
     meta = np.ascontiguousarray(_c(meta, np.uint8))
     X = np.ascontiguousarray(_c(X, np.uint16))
@@ -179,8 +193,12 @@ def gemm_bf16(values: np.ndarray, meta: np.ndarray, X: np.ndarray, M: int, rows=
 
 
 def gemm_i8(values: np.ndarray, meta: np.ndarray, X: np.ndarray, M: int, scale: np.ndarray | None = None,
-            rows=None):
-    """Exact int64 accumulators (checked to fit int32) and, with ``scale``, fl32(fl32(acc) * scale[m])."""
+            rows=None, layout: str = "feature"):
+    """Exact int64 accumulators (checked to fit int32) and, with ``scale``, fl32(fl32(acc) * scale[m]).
+    layout "token": X is N x K and both results are returned N x len(rows)."""
+    if layout != "feature":
+        acc, Y = gemm_i8(values, meta, _feature_major(X, layout), M, scale, rows)
+        return acc.T, (None if Y is None else Y.T)
     values = np.ascontiguousarray(_c(values, np.int8))
     meta = np.ascontiguousarray(_c(meta, np.uint8))
     X = np.ascontiguousarray(_c(X, np.int8))

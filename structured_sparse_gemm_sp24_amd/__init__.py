@@ -19,10 +19,11 @@ SP24_OK, SP24_ERR_NULL, SP24_ERR_SHAPE, SP24_ERR_ALIGN = 0, -1, -2, -3
 SP24_ERR_DTYPE, SP24_ERR_ARG, SP24_ERR_DEVICE, SP24_ERR_HIP = -4, -5, -6, -7
 SP24_BF16, SP24_FP16, SP24_FP32, SP24_I8, SP24_I32 = 0, 1, 2, 3, 4
 SP24_SCORE_MAGNITUDE, SP24_SCORE_WANDA = 0, 1
+SP24_FEATURE_MAJOR, SP24_TOKEN_MAJOR = 0, 1
 
 # every symbol include/sp24.h declares
 EXPORTS = ("sp24_col_norms", "sp24_compressed_bytes", "sp24_prune_compress", "sp24_decompress", "sp24_gemm_bf16",
-           "sp24_gemm_i8", "sp24_status_string")
+           "sp24_gemm_i8", "sp24_gemm_bf16_ex", "sp24_gemm_i8_ex", "sp24_status_string")
 
 _TORCH_TO_SP24 = {torch.bfloat16: SP24_BF16, torch.float16: SP24_FP16, torch.float32: SP24_FP32,
                   torch.int8: SP24_I8, torch.int32: SP24_I32}
@@ -54,6 +55,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sp24_decompress.argtypes = [P, P, I, I64, I64, P, I64, P]
     lib.sp24_gemm_bf16.argtypes = [P, P, I64, I64, P, I64, I64, P, I, I64, P]
     lib.sp24_gemm_i8.argtypes = [P, P, I64, I64, P, I64, I64, P, P, I64, P]
+    lib.sp24_gemm_bf16_ex.argtypes = [P, P, I64, I64, P, I64, I64, I64, P, I, I64, I64, I64, I, P]
+    lib.sp24_gemm_i8_ex.argtypes = [P, P, I64, I64, P, I64, I64, I64, P, P, I64, I64, I64, I, P]
     for fn in EXPORTS[:-1]:
         getattr(lib, fn).restype = I
     lib.sp24_status_string.argtypes = [I]
@@ -183,4 +186,64 @@ def sp24_gemm_i8(values: torch.Tensor, meta: torch.Tensor, M: int, X: torch.Tens
     st = load_library().sp24_gemm_i8(_ptr(values), _ptr(meta), M, K, _ptr(X), N, _rows(X, "X"), _ptr(scale),
                                      _ptr(out), _rows(out, "out"), _stream(X))
     _check("sp24_gemm_i8", st)
+    return out
+
+
+def _layout(layout) -> int:
+    if layout in ("feature", SP24_FEATURE_MAJOR):
+        return SP24_FEATURE_MAJOR
+    if layout in ("token", SP24_TOKEN_MAJOR):
+        return SP24_TOKEN_MAJOR
+    raise ValueError(f"layout must be 'feature' or 'token', not {layout!r}")
+
+
+def _gemm_operands(X: torch.Tensor, M: int, layout: int, out: torch.Tensor | None, out_dtype: torch.dtype):
+    """(K, N, ldx, x batch stride, batch, out, ldy, y batch stride) of a 2-D or batched 3-D X."""
+    if X.dim() not in (2, 3):
+        raise ValueError("X must be 2-D, or 3-D for a batch")
+    batch = X.shape[0] if X.dim() == 3 else 1
+    X2 = X[0] if X.dim() == 3 else X
+    if layout == SP24_TOKEN_MAJOR:
+        N, K = X2.shape
+        yshape = (N, M)
+    else:
+        K, N = X2.shape
+        yshape = (M, N)
+    if out is None:
+        out = torch.empty(((batch,) if X.dim() == 3 else ()) + yshape, dtype=out_dtype, device=X.device)
+    if out.dim() != X.dim() or tuple(out.shape[-2:]) != yshape or (X.dim() == 3 and out.shape[0] != batch):
+        raise ValueError(f"out must have shape {((batch,) if X.dim() == 3 else ()) + yshape}")
+    Y2 = out[0] if out.dim() == 3 else out
+    sx = X.stride(0) if X.dim() == 3 else 0
+    sy = out.stride(0) if out.dim() == 3 else 0
+    return K, N, _rows(X2, "X"), sx, batch, out, _rows(Y2, "out"), sy
+
+
+def sp24_gemm_bf16_ex(values: torch.Tensor, meta: torch.Tensor, M: int, X: torch.Tensor, layout="feature",
+                      out_dtype: torch.dtype = torch.float32, out: torch.Tensor | None = None) -> torch.Tensor:
+    """bf16 sparse GEMM in either layout, optionally batched. layout 'feature': X is K x N, Y M x N;
+    'token': X is N x K (a Linear layer's input), Y N x M. A 3-D X ([batch, ...]) runs one product per
+    entry with the shared weight (e.g. a 1x1 conv over NCHW images, feature-major)."""
+    _dev_check(values, meta, X, out)
+    lay = _layout(layout)
+    K, N, ldx, sx, batch, out, ldy, sy = _gemm_operands(X, M, lay, out, out_dtype)
+    _check_compressed(values, meta, M, K)
+    st = load_library().sp24_gemm_bf16_ex(_ptr(values), _ptr(meta), M, K, _ptr(X), N, ldx, sx, _ptr(out),
+                                          _TORCH_TO_SP24[out.dtype], ldy, sy, batch, lay, _stream(X))
+    _check("sp24_gemm_bf16_ex", st)
+    return out
+
+
+def sp24_gemm_i8_ex(values: torch.Tensor, meta: torch.Tensor, M: int, X: torch.Tensor, scale: torch.Tensor | None = None,
+                    layout="feature", out: torch.Tensor | None = None) -> torch.Tensor:
+    """int8 sparse GEMM in either layout, optionally batched (as sp24_gemm_bf16_ex); fp32 out with
+    ``scale`` (per output channel m), else int32 accumulators."""
+    _dev_check(values, meta, X, scale, out)
+    lay = _layout(layout)
+    K, N, ldx, sx, batch, out, ldy, sy = _gemm_operands(X, M, lay, out,
+                                                        torch.float32 if scale is not None else torch.int32)
+    _check_compressed(values, meta, M, K)
+    st = load_library().sp24_gemm_i8_ex(_ptr(values), _ptr(meta), M, K, _ptr(X), N, ldx, sx, _ptr(scale), _ptr(out),
+                                        ldy, sy, batch, lay, _stream(X))
+    _check("sp24_gemm_i8_ex", st)
     return out

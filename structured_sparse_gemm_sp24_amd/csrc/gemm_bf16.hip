@@ -15,34 +15,46 @@
 // so a wave's A operand is one contiguous 1 KB load and its index operand one 128 B load.
 //
 // This file holds the direct kernel: each wave owns a 16-row x (16*NF)-column tile, takes A and the
-// index straight from global memory and gathers B element by element with bounds checks, so it works
-// for every shape and row pitch. It serves the shapes the others do not take: the few-token kernel
-// (gemm_bf16_skinny.hip, N <= 64) and the LDS-tiled kernel (gemm_bf16_tiled.hip, N > 64), each
-// within its alignment and size conditions.
+// index straight from global memory and gathers B element by element with bounds checks, through
+// general element strides, so it works for every shape, layout (feature- or token-major), batch and
+// row pitch. It serves the cases the others do not take: the few-token kernel (gemm_bf16_skinny.hip,
+// N <= 64) and the LDS-tiled kernel (gemm_bf16_tiled.hip, N > 64), each within its alignment and
+// size conditions.
 #include "sp24_device.h"
 #include "sp24_launch.h"
 
 namespace sp24 {
 
+// Element strides: X[k, n] at k * sxk + n * sxn, Y[m, n] at m * sym + n * syn; batch blockIdx.z adds
+// z * sxb / z * syb.
+struct DirectArgs {
+    const uint16_t* vals;
+    const uint8_t* meta;
+    int64_t M, K, N;
+    const uint16_t* X;
+    int64_t sxk, sxn, sxb;
+    void* Y;
+    int64_t sym, syn, syb;
+    int out_fp32;
+};
+
 template <int NF>
-__global__ __launch_bounds__(256) void gemm_bf16_direct(const uint16_t* __restrict__ vals,
-                                                        const uint8_t* __restrict__ meta, int64_t M, int64_t K,
-                                                        const uint16_t* __restrict__ X, int64_t N, int64_t ldx,
-                                                        void* __restrict__ Y, int out_fp32, int64_t ldy) {
+__global__ __launch_bounds__(256) void gemm_bf16_direct(DirectArgs d) {
     const int lane = threadIdx.x & 63;
     const int r = lane & 15, q = lane >> 4;
     const int64_t m0 = ((int64_t)blockIdx.y * 4 + (threadIdx.x >> 6)) * 16;
     const int64_t n0 = (int64_t)blockIdx.x * 16 * NF;
-    if (m0 >= M) return;  // whole wave
+    if (m0 >= d.M) return;  // whole wave
+    const uint16_t* __restrict__ X = d.X + (int64_t)blockIdx.z * d.sxb;
     f32x4 acc[NF];
 #pragma unroll
     for (int f = 0; f < NF; f++) acc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // compressed tiles of this 16-row block: one 1 KB values tile and one 128 B metadata tile per 64
     // dense columns, already in lane order (rows and columns are padded, so every tile exists)
-    const int64_t tiles_per_row = (K + 63) / 64;
-    const u32x4* vt = reinterpret_cast<const u32x4*>(vals) + (m0 >> 4) * tiles_per_row * 64 + lane;
-    const uint16_t* mt = reinterpret_cast<const uint16_t*>(meta) + (m0 >> 4) * tiles_per_row * 64 + lane;
+    const int64_t tiles_per_row = (d.K + 63) / 64;
+    const u32x4* vt = reinterpret_cast<const u32x4*>(d.vals) + (m0 >> 4) * tiles_per_row * 64 + lane;
+    const uint16_t* mt = reinterpret_cast<const uint16_t*>(d.meta) + (m0 >> 4) * tiles_per_row * 64 + lane;
     for (int64_t t = 0; t < tiles_per_row; t++) {
         const int64_t k0 = 64 * t;
         const u32x4 a = vt[64 * t];
@@ -59,7 +71,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_direct(const uint16_t* __restri
                     const int e = 2 * h + s;
                     const int64_t k = k0 + 8 * q + (e & 7) + 32 * (e >> 3);
                     uint32_t v = 0;
-                    if (n < N && k < K) v = X[k * ldx + n];
+                    if (n < d.N && k < d.K) v = X[k * d.sxk + n * d.sxn];
                     v2 |= v << (16 * s);
                 }
                 b[h] = v2;
@@ -69,42 +81,59 @@ __global__ __launch_bounds__(256) void gemm_bf16_direct(const uint16_t* __restri
                                                                __builtin_bit_cast(bf16x16, bv), acc[f], (int)idx, 0, 0);
         }
     }
+    char* const Y = static_cast<char*>(d.Y) + (int64_t)blockIdx.z * d.syb * (d.out_fp32 ? 4 : 2);
 #pragma unroll
     for (int f = 0; f < NF; f++) {
         const int64_t n = n0 + 16 * f + r;
-        if (n >= N) continue;
+        if (n >= d.N) continue;
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             const int64_t m = m0 + 4 * q + i;
-            if (m >= M) continue;
-            if (out_fp32)
-                reinterpret_cast<float*>(Y)[m * ldy + n] = acc[f][i];
+            if (m >= d.M) continue;
+            const int64_t o = m * d.sym + n * d.syn;
+            if (d.out_fp32)
+                reinterpret_cast<float*>(Y)[o] = acc[f][i];
             else
-                reinterpret_cast<uint16_t*>(Y)[m * ldy + n] = f32_to_bf16_rne(acc[f][i]);
+                reinterpret_cast<uint16_t*>(Y)[o] = f32_to_bf16_rne(acc[f][i]);
         }
     }
 }
 
-hipError_t launch_gemm_bf16_direct(const uint16_t* values, const uint8_t* meta, int64_t M, int64_t K,
-                                   const uint16_t* X, int64_t N, int64_t ldx, void* Y, bool out_fp32, int64_t ldy,
-                                   hipStream_t s) {
-    const unsigned gy = (unsigned)((M + 63) / 64);
-    if (N <= 16) {
-        hipLaunchKernelGGL(gemm_bf16_direct<1>, dim3((unsigned)((N + 15) / 16), gy), dim3(256), 0, s, values, meta, M,
-                           K, X, N, ldx, Y, (int)out_fp32, ldy);
-    } else {
-        hipLaunchKernelGGL(gemm_bf16_direct<4>, dim3((unsigned)((N + 63) / 64), gy), dim3(256), 0, s, values, meta, M,
-                           K, X, N, ldx, Y, (int)out_fp32, ldy);
+static hipError_t launch_gemm_bf16_direct(const GemmArgs& g, hipStream_t s) {
+    DirectArgs d;
+    d.vals = static_cast<const uint16_t*>(g.values);
+    d.meta = g.meta;
+    d.M = g.M; d.K = g.K; d.N = g.N;
+    d.X = static_cast<const uint16_t*>(g.X);
+    d.sxk = g.tm ? 1 : g.ldx;
+    d.sxn = g.tm ? g.ldx : 1;
+    d.sxb = g.sx;
+    d.Y = g.Y;
+    d.sym = g.tm ? 1 : g.ldy;
+    d.syn = g.tm ? g.ldy : 1;
+    d.syb = g.sy;
+    d.out_fp32 = g.out_fp32;
+    const unsigned gy = (unsigned)((g.M + 63) / 64);
+    // grid z covers at most 65535 batch entries per launch
+    for (int64_t b0 = 0; b0 < g.batch; b0 += 65535) {
+        const unsigned gz = (unsigned)(g.batch - b0 < 65535 ? g.batch - b0 : 65535);
+        DirectArgs e = d;
+        e.X = d.X + b0 * d.sxb;
+        e.Y = static_cast<char*>(d.Y) + b0 * d.syb * (g.out_fp32 ? 4 : 2);
+        if (g.N <= 16)
+            hipLaunchKernelGGL(gemm_bf16_direct<1>, dim3((unsigned)((g.N + 15) / 16), gy, gz), dim3(256), 0, s, e);
+        else
+            hipLaunchKernelGGL(gemm_bf16_direct<4>, dim3((unsigned)((g.N + 63) / 64), gy, gz), dim3(256), 0, s, e);
+        const hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
     }
-    return hipGetLastError();
+    return hipSuccess;
 }
 
-hipError_t launch_gemm_bf16(const uint16_t* values, const uint8_t* meta, int64_t M, int64_t K, const uint16_t* X,
-                            int64_t N, int64_t ldx, void* Y, bool out_fp32, int64_t ldy, hipStream_t s) {
-    if (gemm_bf16_skinny_ok(K, N, ldx)) return launch_gemm_bf16_skinny(values, meta, M, K, X, N, ldx, Y, out_fp32, ldy, s);
-    if (gemm_bf16_tiled_ok(M, K, N, ldx, X))
-        return launch_gemm_bf16_tiled(values, meta, M, K, X, N, ldx, Y, out_fp32, ldy, s);
-    return launch_gemm_bf16_direct(values, meta, M, K, X, N, ldx, Y, out_fp32, ldy, s);
+hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s) {
+    if (gemm_bf16_skinny_ok(g)) return launch_gemm_bf16_skinny(g, s);
+    if (gemm_bf16_tiled_ok(g)) return launch_gemm_bf16_tiled(g, s);
+    return launch_gemm_bf16_direct(g, s);
 }
 
 }  // namespace sp24

@@ -10,16 +10,32 @@
 //    (one 16-byte value load and one 2-byte index load per lane and block, in smfmac lane order) and
 //    X fragments are requested before the current round's smfmacs;
 //  - the X fragments of a tile (lane = column, 16 k values) are built once per tile and shared by the
-//    R blocks: for a unit-pitch vector (N = 1) from two 16-byte loads; when rows of X are 16-byte
-//    aligned and N is a multiple of 8, by staging the 64 x 16 NF tile through a wave-private LDS slot
-//    (16-byte loads, ds_write_b128, then ds_read_b64_tr_b16); otherwise element by element;
+//    R blocks. Feature-major X (K x N): for a unit-pitch vector (N = 1) from two 16-byte loads; when
+//    rows of X are 16-byte aligned and N is a multiple of 8, by staging the 64 x 16 NF tile through a
+//    wave-private LDS slot (16-byte loads, ds_write_b128, then ds_read_b64_tr_b16); otherwise element
+//    by element. Token-major X (N x K): a lane's 16 k values are two runs of 8 consecutive elements of
+//    its token's row, so two 16-byte loads when rows are 16-byte aligned (element loads in the K tail
+//    tile and otherwise);
 //  - at the end the S partial 16 x 16 accumulators of each block are summed through LDS in wave order
-//    (deterministic), rounded if the output is bf16, and stored with bounds checks.
+//    (deterministic), rounded if the output is bf16, and stored with bounds checks (M x N or, token-
+//    major, N x M).
+// A batch of independent products sharing the weight (1x1 conv over B images) is grid dimension y.
 #include "sp24_device.h"
 #include "sp24_launch.h"
 
 namespace sp24 {
 namespace skinny {
+
+struct Args {
+    const uint16_t* vals;
+    const uint8_t* meta;
+    int64_t M, K, N;
+    const uint16_t* X;
+    int64_t ldx, sxb;
+    void* Y;
+    int64_t ldy, syb;
+    int out_fp32;
+};
 
 // X fragment for columns 16 f .. 16 f + 15 of tile k0 (smfmac B operand: lane n = r holds
 // k = k0 + 8q + (e & 7) + 32 (e >> 3)); zero past K and past N. The general case reads single
@@ -60,7 +76,34 @@ __device__ __forceinline__ bf16x16 load_x(const uint16_t* __restrict__ X, __amdg
     return __builtin_bit_cast(bf16x16, b);
 }
 
-enum { X_ELEMENTS = 0, X_UNIT_VECTOR = 1, X_STAGED = 2 };
+// Token-major X (row n holds token n's K values): lane n = r's fragment is the two runs
+// k0 + 8q .. +7 and k0 + 32 + 8q .. +7 of its row. VEC: 16-byte loads (rows 16-byte aligned) except in
+// the K tail tile, where elements at k >= K (the next row, or row padding) must read as zero.
+template <bool VEC>
+__device__ __forceinline__ bf16x16 load_x_tm(__amdgpu_buffer_rsrc_t rx, int64_t ldx, int64_t K, int64_t N, int64_t k0,
+                                             int64_t n, int q) {
+    u32x8 b = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (n < N) {
+        const uint32_t o = (uint32_t)((n * ldx + k0 + 8 * q) * 2);
+        if (VEC && k0 + 64 <= K) {
+            const u32x4 lo = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, (int)o, 0, 0));
+            const u32x4 hi = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(o + 64), 0, 0));
+            b = u32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        } else {
+#pragma unroll
+            for (int e = 0; e < 16; e += 2) {
+                const int d = (e & 7) + 32 * (e >> 3);
+                const int64_t k = k0 + 8 * q + d;
+                const uint32_t v0 = k < K ? __builtin_amdgcn_raw_buffer_load_b16(rx, (int)(o + 2 * d), 0, 0) : 0u;
+                const uint32_t v1 = k + 1 < K ? __builtin_amdgcn_raw_buffer_load_b16(rx, (int)(o + 2 * d + 2), 0, 0) : 0u;
+                b[e >> 1] = v0 | (v1 << 16);
+            }
+        }
+    }
+    return __builtin_bit_cast(bf16x16, b);
+}
+
+enum { X_ELEMENTS = 0, X_UNIT_VECTOR = 1, X_STAGED = 2, X_TOKEN = 3, X_TOKEN_ELEMENTS = 4 };
 
 // Staged X tile (64 rows x 16 NF bf16) in a wave's LDS slot: row pitch P = 32 NF bytes plus a gap of
 // G bytes after every 8 rows. The gap puts the 16 rows x 32 bytes of each transposing read (rows
@@ -84,10 +127,14 @@ struct Round {
 };
 
 template <int NF, int R, int S, int U, int XMODE>
-__global__ __launch_bounds__(64 * S) void gemm_bf16_skinny(const uint16_t* __restrict__ vals,
-                                                           const uint8_t* __restrict__ meta, int64_t M, int64_t K,
-                                                           const uint16_t* __restrict__ X, int64_t N, int64_t ldx,
-                                                           void* __restrict__ Y, int out_fp32, int64_t ldy) {
+__global__ __launch_bounds__(64 * S) void gemm_bf16_skinny(Args g) {
+    constexpr bool TM = XMODE == X_TOKEN || XMODE == X_TOKEN_ELEMENTS;
+    const uint8_t* __restrict__ meta = g.meta;
+    const uint16_t* __restrict__ vals = g.vals;
+    const int64_t M = g.M, K = g.K, N = g.N, ldx = g.ldx, ldy = g.ldy;
+    const int out_fp32 = g.out_fp32;
+    const uint16_t* __restrict__ X = g.X + (int64_t)blockIdx.y * g.sxb;
+    char* const Y = static_cast<char*>(g.Y) + (int64_t)blockIdx.y * g.syb * (out_fp32 ? 4 : 2);
     // the wave-private X slots during the K loop, the reduction buffer after it
     constexpr int RED_BYTES = S * R * NF * 256 * 4;
     constexpr int X_BYTES = XMODE == X_STAGED ? S * XTile<NF>::BYTES : 0;
@@ -104,11 +151,13 @@ __global__ __launch_bounds__(64 * S) void gemm_bf16_skinny(const uint16_t* __res
     // tile (b, t): values at ((b * T + t) * 64 + lane) * 16 bytes, index at ((b * T + t) * 64 + lane) * 2
     const u32x4* vt = reinterpret_cast<const u32x4*>(vals) + b0 * T * 64 + lane;
     const uint16_t* mt = reinterpret_cast<const uint16_t*>(meta) + b0 * T * 64 + lane;
-    // X's extent in bytes: (K - 1) rows of pitch ldx plus N elements (below 2^31, checked on the host),
-    // rounded up to a whole dword (the range check passes a dword only if all of it is in range; the
-    // rounding stays inside the aligned dword that holds the last element)
+    // X's extent in bytes: (K - 1) rows of pitch ldx plus N elements, token-major (N - 1) rows plus K
+    // (below 2^31, checked on the host), rounded up to a whole dword (the range check passes a dword
+    // only if all of it is in range; the rounding stays inside the aligned dword that holds the last
+    // element)
+    const int64_t x_elems = TM ? (N - 1) * ldx + K : (K - 1) * ldx + N;
     const __amdgpu_buffer_rsrc_t rx =
-        __builtin_amdgcn_make_buffer_rsrc((void*)X, (short)0, (int)((((K - 1) * ldx + N) * 2 + 3) & ~3), 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc((void*)X, (short)0, (int)((x_elems * 2 + 3) & ~3), 0x00020000);
 
     f32x4 acc[R][NF];
 #pragma unroll
@@ -150,7 +199,9 @@ __global__ __launch_bounds__(64 * S) void gemm_bf16_skinny(const uint16_t* __res
             } else {
 #pragma unroll
                 for (int f = 0; f < NF; f++) {
-                    if (ok)
+                    if (ok && TM)
+                        rd.b[u][f] = load_x_tm<XMODE == X_TOKEN>(rx, ldx, K, N, 64 * tt, 16 * f + r, q);
+                    else if (ok)
                         rd.b[u][f] = load_x<XMODE == X_UNIT_VECTOR>(X, rx, ldx, K, N, 64 * tt, 16 * f + r, q);
                     else
                         rd.b[u][f] = __builtin_bit_cast(bf16x16, u32x8{0, 0, 0, 0, 0, 0, 0, 0});
@@ -215,71 +266,93 @@ __global__ __launch_bounds__(64 * S) void gemm_bf16_skinny(const uint16_t* __res
             for (int i = 0; i < 4; i++) red[((wave * R + j) * NF + f) * 256 + (4 * q + i) * 16 + r] = acc[j][f][i];
     __syncthreads();
     for (int e = threadIdx.x; e < R * NF * 256; e += 64 * S) {
-        const int j = e / (NF * 256), f = (e / 256) % NF, row = (e / 16) % 16, col = e % 16;
+        // consecutive threads take consecutive elements of an output row: columns of Y (M x N), or rows
+        // of the block (token-major, N x M)
+        const int j = e / (NF * 256), f = (e / 256) % NF;
+        const int row = TM ? e % 16 : (e / 16) % 16, col = TM ? (e / 16) % 16 : e % 16;
         float s = 0.f;
 #pragma unroll 4
         for (int w = 0; w < S; w++) s += red[((w * R + j) * NF + f) * 256 + row * 16 + col];
         const int64_t m = (b0 + j) * 16 + row, n = 16 * f + col;
         if (j < nb && m < M && n < N) {
+            const int64_t o = TM ? n * ldy + m : m * ldy + n;
             if (out_fp32)
-                reinterpret_cast<float*>(Y)[m * ldy + n] = s;
+                reinterpret_cast<float*>(Y)[o] = s;
             else
-                reinterpret_cast<uint16_t*>(Y)[m * ldy + n] = f32_to_bf16_rne(s);
+                reinterpret_cast<uint16_t*>(Y)[o] = f32_to_bf16_rne(s);
         }
     }
 }
 
 template <int NF, int R, int S, int U>
-hipError_t launch(const uint16_t* values, const uint8_t* meta, int64_t M, int64_t K, const uint16_t* X, int64_t N,
-                  int64_t ldx, void* Y, bool out_fp32, int64_t ldy, hipStream_t s) {
-    const unsigned grid = (unsigned)(((M + 15) / 16 + R - 1) / R);
-    if constexpr (NF == 1) {
-        if (N == 1 && ldx == 1) {
-            hipLaunchKernelGGL((gemm_bf16_skinny<NF, R, S, U, X_UNIT_VECTOR>), dim3(grid), dim3(64 * S), 0, s, values,
-                               meta, M, K, X, N, ldx, Y, (int)out_fp32, ldy);
-            return hipGetLastError();
+hipError_t launch(const GemmArgs& g, hipStream_t s) {
+    Args a;
+    a.vals = static_cast<const uint16_t*>(g.values);
+    a.meta = g.meta;
+    a.M = g.M; a.K = g.K; a.N = g.N;
+    a.X = static_cast<const uint16_t*>(g.X);
+    a.ldx = g.ldx; a.sxb = g.sx;
+    a.Y = g.Y;
+    a.ldy = g.ldy; a.syb = g.sy;
+    a.out_fp32 = g.out_fp32;
+    const unsigned grid = (unsigned)(((g.M + 15) / 16 + R - 1) / R);
+    // grid y covers at most 65535 batch entries per launch
+    for (int64_t b0 = 0; b0 < g.batch; b0 += 65535) {
+        const unsigned gb = (unsigned)(g.batch - b0 < 65535 ? g.batch - b0 : 65535);
+        Args e = a;
+        e.X = a.X + b0 * a.sxb;
+        e.Y = static_cast<char*>(a.Y) + b0 * a.syb * (g.out_fp32 ? 4 : 2);
+        const dim3 grd(grid, gb), blk(64 * S);
+        if (g.tm) {
+            if (g.ldx % 8 == 0)
+                hipLaunchKernelGGL((gemm_bf16_skinny<NF, R, S, U, X_TOKEN>), grd, blk, 0, s, e);
+            else
+                hipLaunchKernelGGL((gemm_bf16_skinny<NF, R, S, U, X_TOKEN_ELEMENTS>), grd, blk, 0, s, e);
+        } else if (NF == 1 && g.N == 1 && g.ldx == 1) {
+            hipLaunchKernelGGL((gemm_bf16_skinny<NF, R, S, U, X_UNIT_VECTOR>), grd, blk, 0, s, e);
+        } else if (g.ldx % 8 == 0 && g.N % 8 == 0) {
+            hipLaunchKernelGGL((gemm_bf16_skinny<NF, R, S, U, X_STAGED>), grd, blk, 0, s, e);
+        } else {
+            hipLaunchKernelGGL((gemm_bf16_skinny<NF, R, S, U, X_ELEMENTS>), grd, blk, 0, s, e);
         }
+        const hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
     }
-    if (ldx % 8 == 0 && N % 8 == 0)
-        hipLaunchKernelGGL((gemm_bf16_skinny<NF, R, S, U, X_STAGED>), dim3(grid), dim3(64 * S), 0, s, values, meta, M,
-                           K, X, N, ldx, Y, (int)out_fp32, ldy);
-    else
-        hipLaunchKernelGGL((gemm_bf16_skinny<NF, R, S, U, X_ELEMENTS>), dim3(grid), dim3(64 * S), 0, s, values, meta, M,
-                           K, X, N, ldx, Y, (int)out_fp32, ldy);
-    return hipGetLastError();
+    return hipSuccess;
 }
 
 }  // namespace skinny
 
-bool gemm_bf16_skinny_ok(int64_t K, int64_t N, int64_t ldx) {
-    // 32-bit element offsets for every row the tiles touch (K padded to 64, plus one tile)
-    return N <= 64 && (K + 128) * ldx * 2 < ((int64_t)1 << 31);
+bool gemm_bf16_skinny_ok(const GemmArgs& g) {
+    // 32-bit byte offsets for every element the tiles touch (K padded to 64, plus one tile)
+    const int64_t extent = g.tm ? g.N * g.ldx + g.K + 128 : (g.K + 128) * g.ldx;
+    return g.N <= 64 && extent * 2 < ((int64_t)1 << 31);
 }
 
 // Row blocks per workgroup (R), waves per workgroup (S) and tiles per round (U) by size: about 256 or
 // more workgroups, R as large as that allows (each X fragment is then shared by more weight tiles);
 // the unit-vector case reads its X fragment cheaply and prefers more, smaller workgroups. Chosen by
 // measurement on MI355X over R in {1, 2, 4}, S in {4, 8, 16}, U in {1, 2, 4}.
-hipError_t launch_gemm_bf16_skinny(const uint16_t* values, const uint8_t* meta, int64_t M, int64_t K, const uint16_t* X,
-                                   int64_t N, int64_t ldx, void* Y, bool out_fp32, int64_t ldy, hipStream_t s) {
-    const int64_t nb = (M + 15) / 16;
-    if (N == 1 && ldx == 1) {
-        if (nb >= 1024) return skinny::launch<1, 4, 16, 1>(values, meta, M, K, X, N, ldx, Y, out_fp32, ldy, s);
-        if (nb >= 512) return skinny::launch<1, 2, 4, 2>(values, meta, M, K, X, N, ldx, Y, out_fp32, ldy, s);
-        return skinny::launch<1, 1, 8, 4>(values, meta, M, K, X, N, ldx, Y, out_fp32, ldy, s);
+hipError_t launch_gemm_bf16_skinny(const GemmArgs& g, hipStream_t s) {
+    const int64_t nb = (g.M + 15) / 16;
+    const bool vec1 = g.N == 1 && (g.tm || g.ldx == 1);  // one token: X is a contiguous K-vector
+    if (vec1) {
+        if (nb >= 1024) return skinny::launch<1, 4, 16, 1>(g, s);
+        if (nb >= 512) return skinny::launch<1, 2, 4, 2>(g, s);
+        return skinny::launch<1, 1, 8, 4>(g, s);
     }
-    if (N <= 16) {
-        if (nb >= 512) return skinny::launch<1, 4, 16, 1>(values, meta, M, K, X, N, ldx, Y, out_fp32, ldy, s);
-        return skinny::launch<1, 1, 16, 2>(values, meta, M, K, X, N, ldx, Y, out_fp32, ldy, s);
+    if (g.N <= 16) {
+        if (nb >= 512) return skinny::launch<1, 4, 16, 1>(g, s);
+        return skinny::launch<1, 1, 16, 2>(g, s);
     }
-    if (N <= 32) {
-        if (nb >= 1024) return skinny::launch<2, 4, 8, 1>(values, meta, M, K, X, N, ldx, Y, out_fp32, ldy, s);
-        if (nb >= 512) return skinny::launch<2, 2, 16, 1>(values, meta, M, K, X, N, ldx, Y, out_fp32, ldy, s);
-        return skinny::launch<2, 1, 16, 1>(values, meta, M, K, X, N, ldx, Y, out_fp32, ldy, s);
+    if (g.N <= 32) {
+        if (nb >= 1024) return skinny::launch<2, 4, 8, 1>(g, s);
+        if (nb >= 512) return skinny::launch<2, 2, 16, 1>(g, s);
+        return skinny::launch<2, 1, 16, 1>(g, s);
     }
-    if (nb >= 1024) return skinny::launch<4, 4, 8, 1>(values, meta, M, K, X, N, ldx, Y, out_fp32, ldy, s);
-    if (nb >= 512) return skinny::launch<4, 2, 8, 1>(values, meta, M, K, X, N, ldx, Y, out_fp32, ldy, s);
-    return skinny::launch<4, 1, 8, 1>(values, meta, M, K, X, N, ldx, Y, out_fp32, ldy, s);
+    if (nb >= 1024) return skinny::launch<4, 4, 8, 1>(g, s);
+    if (nb >= 512) return skinny::launch<4, 2, 8, 1>(g, s);
+    return skinny::launch<4, 1, 8, 1>(g, s);
 }
 
 }  // namespace sp24

@@ -24,6 +24,16 @@
 // in each 16-lane group, lane s points at row k0 + s/4, columns c0 + 4(s%4); the instruction hands
 // lane i the four consecutive k of column c0 + i.
 //
+// Token-major X (N x K, the nn.Linear layout) needs no transposing read: the B tile is 256 token rows
+// x 64 k (128 B per row), and a lane's operand is two 16-byte runs of its token's row (k = 8q .. +7
+// and 32 + 8q .. +7), two ds_read_b128. Row n's 16-byte units sit at unit ^ f(n), f(n) = ((n >> 1) & 7)
+// ^ 4 (n & 1): the 16 rows of one read group then use every 16-byte bank slot once per row parity (and
+// 8 consecutive rows 8 distinct slots). The output Y (N x M) takes each accumulator's 4 consecutive
+// rows of M as one 8- or 16-byte store, with no transposes. K must be a multiple of 64 there (inside a
+// row the range check cannot stop at K).
+//
+// A batch of products sharing the weight (1x1 conv over B images) adds the batch to the tile index.
+//
 // Persistent: one workgroup per CU walks its tiles (p, p + G, p + 2G, ... in a numbering where the
 // workgroups of one XCD -- workgroup p runs on XCD p % 8 -- hold neighbouring tiles at the same time,
 // walked in groups of 8 tile-rows, so A and B tiles are re-read from that XCD's L2). The three-stage
@@ -88,7 +98,8 @@ struct Args {
     const uint16_t* X;
     void* Y;
     int64_t M, K, N, ldx, ldy;
-    int tilesM, tilesN;
+    int64_t sxb, syb;  // batch strides (elements)
+    int tilesM, tilesN, batch;
     int y_vec;  // Y base and row pitch allow 8-byte (bf16) / 16-byte (fp32) stores, 4 rows < 2^31 bytes
 };
 
@@ -96,6 +107,8 @@ struct Args {
 // row blocks. `valid` is false past the workgroup's last tile (its loads are then pushed out of range).
 struct TileDesc {
     int64_t m0, n0;
+    const uint16_t* x;  // X and Y of the tile's batch entry
+    char* y;
     i32x4 rA, rM;
     bool valid;
 };
@@ -105,7 +118,7 @@ struct TileDesc {
 // contiguous run of rem / 8 or rem / 8 + 1 of them, so a partial last turn still spreads its tiles,
 // and their output writes, over every XCD, and neighbouring tiles share an L2.
 __device__ __forceinline__ int tile_of(const Args& a, int p, int k) {
-    const int G = gridDim.x, T = a.tilesM * a.tilesN;
+    const int G = gridDim.x, T = a.tilesM * a.tilesN * a.batch;
     const int64_t base = (int64_t)k * G;
     if (base >= T) return -1;
     const int rem = (T - base) < G ? (int)(T - base) : G;
@@ -114,26 +127,43 @@ __device__ __forceinline__ int tile_of(const Args& a, int p, int k) {
     return (int)base + x * q8 + (x < r8 ? x : r8) + i;
 }
 
+// 16-byte unit swizzle of token row n of a token-major B tile (see the top of the file).
+__device__ __forceinline__ int tm_swz(int n) { return ((n >> 1) & 7) ^ ((n & 1) << 2); }
+
 // Per-lane parts of the load offsets (the uniform parts go into the SGPR offset operand).
 struct LoadOffsets {
     uint32_t a;      // A tile: 16 * lane
     uint32_t m;      // metadata: 4 * (lane & 31) + (lane >> 5) * tiles * 128 (second tile of the pair)
-    uint32_t b[4];   // B row pair: (lane >> 5) * row pitch + 16 * swizzled chunk, by row & 3 >> 1 and row >> 3 & 1
+    // feature-major B row pair: (lane >> 5) * row pitch + 16 * swizzled chunk, by row & 3 >> 1 and
+    // row >> 3 & 1; token-major (b[0], b[1]): (lane >> 3) * row pitch + 16 * swizzled unit, by row >> 3 & 1
+    uint32_t b[4];
 };
 
+template <bool TM>
 __device__ __forceinline__ LoadOffsets load_offsets(const Args& a, int lane) {
     LoadOffsets o;
     const int tiles = (int)((a.K + BK - 1) / BK);
     o.a = 16 * lane;
     o.m = 4 * (lane & 31) + (lane >> 5) * tiles * 128;
-    const int pc = lane & 31;  // 16-byte slot in the LDS row
+    if constexpr (TM) {
+        // lane i of a load lands in token row 8h + i / 8 of the tile, 16-byte slot i % 8, and reads the
+        // unit that belongs there; only (row >> 3) & 1 = h & 1 changes the swizzle between loads
 #pragma unroll
-    for (int h = 0; h < 4; h++) {
-        // a row with the same (row & 3) and (row >> 3) & 1 as this lane's row of the pair
-        const int row = 2 * (h & 1) + (lane >> 5) + 8 * (h >> 1);
-        const int v = ((row & 3) << 1) | ((row >> 3) & 1);
-        const int lc = pc ^ (2 * v);  // 16-byte chunk of the X row
-        o.b[h] = (uint32_t)((lane >> 5) * a.ldx * 2 + 16 * lc);
+        for (int h = 0; h < 2; h++) {
+            const int row = 8 * h + (lane >> 3);
+            o.b[h] = (uint32_t)((lane >> 3) * a.ldx * 2 + 16 * ((lane & 7) ^ tm_swz(row)));
+        }
+        o.b[2] = o.b[3] = 0;
+    } else {
+        const int pc = lane & 31;  // 16-byte slot in the LDS row
+#pragma unroll
+        for (int h = 0; h < 4; h++) {
+            // a row with the same (row & 3) and (row >> 3) & 1 as this lane's row of the pair
+            const int row = 2 * (h & 1) + (lane >> 5) + 8 * (h >> 1);
+            const int v = ((row & 3) << 1) | ((row >> 3) & 1);
+            const int lc = pc ^ (2 * v);  // 16-byte chunk of the X row
+            o.b[h] = (uint32_t)((lane >> 5) * a.ldx * 2 + 16 * lc);
+        }
     }
     return o;
 }
@@ -143,6 +173,7 @@ __device__ __forceinline__ LoadOffsets load_offsets(const Args& a, int lane) {
 // block b at (b * tiles + s) * 1 KB of values and * 128 B of metadata). When td is not valid (past the
 // workgroup's last tile) the offsets get bit 31 set, past every record count, so the loads return
 // zeros without memory traffic (and X's record count is 0).
+template <bool TM>
 __device__ __forceinline__ void load_stage(uint32_t lds, const Args& a, const TileDesc& td, int s, int wave,
                                            const LoadOffsets& lo) {
     const int64_t k0 = (int64_t)s * BK;
@@ -160,26 +191,44 @@ __device__ __forceinline__ void load_stage(uint32_t lds, const Args& a, const Ti
         const int b = 4 * wave + 2 * h;
         dma4(lds + A_BYTES + b * 128, lo.m + (((uint32_t)(b * tiles + s) * 128u) | past), td.rM);
     }
-    // B: 64 rows x 512 B; this wave loads rows 16*wave .. +15, two rows per instruction (rows
-    // 16 wave + 2h + lane / 32: row & 3 = 2 (h & 1) + lane / 32, (row >> 3) & 1 = h >> 2).
-    // X's exact extent from this stage's corner ((K - 1) rows of pitch ldx plus N elements); make_rsrc
-    // rounds it up to whole dwords (the range check passes a dword only if all of it is in range)
-    const i32x4 rB =
-        make_rsrc(a.X + k0 * a.ldx + td.n0, td.valid ? ((a.K - 1 - k0) * a.ldx + a.N - td.n0) * 2 : 0);
+    if constexpr (TM) {
+        // B: 256 token rows x 128 B; this wave loads rows 64 wave .. +63, 8 rows per instruction.
+        // X's extent from this stage's corner: N - 1 - n0 rows of pitch ldx plus K - k0 elements, so
+        // token rows past N read zeros (K is a multiple of 64: no stage reaches past K)
+        const i32x4 rB =
+            make_rsrc(td.x + td.n0 * a.ldx + k0, td.valid ? ((a.N - 1 - td.n0) * a.ldx + a.K - k0) * 2 : 0);
 #pragma unroll
-    for (int h = 0; h < 8; h++) {
-        const int row = 16 * wave + 2 * h;
-        dma16(lds + A_BYTES + META_BYTES + row * B_ROW,
-              lo.b[(h & 1) | ((h >> 2) << 1)] + (uint32_t)(row * a.ldx * 2), rB);
+        for (int h = 0; h < 8; h++) {
+            const int row = 64 * wave + 8 * h;
+            dma16(lds + A_BYTES + META_BYTES + row * 128, lo.b[h & 1] + (uint32_t)(row * a.ldx * 2), rB);
+        }
+    } else {
+        // B: 64 rows x 512 B; this wave loads rows 16*wave .. +15, two rows per instruction (rows
+        // 16 wave + 2h + lane / 32: row & 3 = 2 (h & 1) + lane / 32, (row >> 3) & 1 = h >> 2).
+        // X's exact extent from this stage's corner ((K - 1) rows of pitch ldx plus N elements); make_rsrc
+        // rounds it up to whole dwords (the range check passes a dword only if all of it is in range)
+        const i32x4 rB =
+            make_rsrc(td.x + k0 * a.ldx + td.n0, td.valid ? ((a.K - 1 - k0) * a.ldx + a.N - td.n0) * 2 : 0);
+#pragma unroll
+        for (int h = 0; h < 8; h++) {
+            const int row = 16 * wave + 2 * h;
+            dma16(lds + A_BYTES + META_BYTES + row * B_ROW,
+                  lo.b[(h & 1) | ((h >> 2) << 1)] + (uint32_t)(row * a.ldx * 2), rB);
+        }
     }
 }
 
-// Tile descriptor of logical tile L (-1: none). Tiles are walked in groups of GROUP_M tile-rows,
-// column by column inside a group.
+// Tile descriptor of logical tile L (-1: none). Batch entries follow each other; inside one, tiles
+// are walked in groups of GROUP_M tile-rows, column by column inside a group.
+template <bool OUT_FP32>
 __device__ __forceinline__ TileDesc tile_desc(const Args& a, int L) {
     TileDesc td;
     td.valid = L >= 0;
-    const int Lc = L >= 0 ? L : 0;
+    const int per = a.tilesM * a.tilesN;
+    const int bt = L >= 0 ? L / per : 0;
+    const int Lc = L >= 0 ? L - bt * per : 0;
+    td.x = a.X + bt * a.sxb;
+    td.y = static_cast<char*>(a.Y) + bt * a.syb * (OUT_FP32 ? 4 : 2);
     const int gsize = GROUP_M * a.tilesN;
     const int g = Lc / gsize;
     const int first_m = g * GROUP_M;
@@ -199,14 +248,24 @@ __device__ __forceinline__ TileDesc tile_desc(const Args& a, int L) {
 struct LaneOffsets {
     int a;        // A fragment of block wm0/16: block * 1024 + lane * 16
     int m;        // metadata of block wm0/16: A_BYTES + block * 128 + lane * 2
-    int b[FN];    // B fragment j, first read (t = 0): row part + swizzled column part
+    int b[FN];    // B fragment j, first read (t = 0): row part + swizzled column part; token-major: the
+                  // two reads of fragment 0 (b[0], b[1]; fragment j adds 16 rows x 128 B)
 };
 
+template <bool TM>
 __device__ __forceinline__ LaneOffsets lane_offsets(int wm0, int wn0, int lane) {
     const int r = lane & 15, q = lane >> 4;
     LaneOffsets o;
     o.a = (wm0 >> 4) * 1024 + lane * 16;
     o.m = A_BYTES + (wm0 >> 4) * 128 + lane * 2;
+    if constexpr (TM) {
+        const int base = A_BYTES + META_BYTES + (wn0 + r) * 128, u = q ^ tm_swz(r);
+        o.b[0] = base + 16 * u;
+        o.b[1] = base + 16 * (u ^ 4);
+#pragma unroll
+        for (int j = 2; j < FN; j++) o.b[j] = 0;
+        return o;
+    }
     // read t of group q covers rows 8q + 4(t&1) + 32(t>>1) + r/4, which all have the row & 3 and
     // (row >> 3) & 1 of row0, so the unit swizzle is fixed per lane and t only adds immediates
     const int row0 = 8 * q + (r >> 2);
@@ -246,8 +305,18 @@ __device__ __forceinline__ void read_a(uint32_t buf, const LaneOffsets& o, AFrag
     }
 }
 
-// B fragment j (16 columns x 64 k) of the stage in buffer `buf`: four transposing reads.
+// B fragment j (16 columns x 64 k) of the stage in buffer `buf`: four transposing reads, or, token-
+// major, two 16-byte reads of the lane's token row.
+template <bool TM>
 __device__ __forceinline__ bf16x16 read_b(uint32_t buf, const LaneOffsets& o, int j) {
+    if constexpr (TM) {
+        typedef const __attribute__((address_space(3))) u32x4 lds_u32x4;
+        const lds_char* p0 = (const lds_char*)(size_t)stage_addr(buf, o.b[0]);
+        const lds_char* p1 = (const lds_char*)(size_t)stage_addr(buf, o.b[1]);
+        const u32x4 lo = *reinterpret_cast<lds_u32x4*>(p0 + j * 2048);
+        const u32x4 hi = *reinterpret_cast<lds_u32x4*>(p1 + j * 2048);
+        return __builtin_bit_cast(bf16x16, u32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+    }
     const lds_char* p = (const lds_char*)(size_t)stage_addr(buf, o.b[j]);
     u32x8 b;
 #pragma unroll
@@ -270,6 +339,7 @@ __device__ __forceinline__ void mfma_block(f32x4 (&acc)[FM][FN], const AFrags& f
 // One K stage (see the pipeline description in the kernel): stage s of the current tile, g-th stage of
 // the workgroup overall (selects the buffer). The loads it issues are those of stage s + 3 of the
 // current tile or, past its end, stage s + 3 - S of the next one. No branches.
+template <bool TM>
 __device__ __forceinline__ void stage(uint32_t l0, const Args& a, const TileDesc& cur_t, const TileDesc& next_t, int s,
                                       int S, int g, f32x4 (&acc)[FM][FN], AFrags& f, bf16x16 (&rb)[4],
                                       const LaneOffsets& o, int wave, const LoadOffsets& lo) {
@@ -278,7 +348,7 @@ __device__ __forceinline__ void stage(uint32_t l0, const Args& a, const TileDesc
     const uint32_t nxt = l0 + (cb == 2 ? 0 : cb + 1) * STAGE_BYTES;
 #pragma unroll
     for (int j = 0; j < 6; j++) {
-        rb[(j + 2) & 3] = read_b(cur, o, j + 2);
+        rb[(j + 2) & 3] = read_b<TM>(cur, o, j + 2);
         __builtin_amdgcn_sched_barrier(0);
         mfma_block(acc, f, rb[j & 3], j);
         __builtin_amdgcn_sched_barrier(0);
@@ -287,9 +357,9 @@ __device__ __forceinline__ void stage(uint32_t l0, const Args& a, const TileDesc
     wait_vmcnt<LOADS_PER_STAGE>();       // stage g+1 has landed (g+2 may still be in flight)
     __builtin_amdgcn_s_barrier();
     const bool here = s + 3 < S;
-    load_stage(cur, a, here ? cur_t : next_t, here ? s + 3 : s + 3 - S, wave, lo);
-    rb[0] = read_b(nxt, o, 0);
-    rb[1] = read_b(nxt, o, 1);
+    load_stage<TM>(cur, a, here ? cur_t : next_t, here ? s + 3 : s + 3 - S, wave, lo);
+    rb[0] = read_b<TM>(nxt, o, 0);
+    rb[1] = read_b<TM>(nxt, o, 1);
     __builtin_amdgcn_sched_barrier(0);
     mfma_block(acc, f, rb[2], 6);
     __builtin_amdgcn_sched_barrier(0);
@@ -307,25 +377,26 @@ __device__ __forceinline__ void stage(uint32_t l0, const Args& a, const TileDesc
 }
 
 // ---------------------------------------------------------------- epilogue
-// From registers, four fragments (64 columns) at a time: the quad transposes leave lane (q, 4a + b)
-// with row 4q + b, columns 4a .. 4a+3 of each fragment f; row_transpose4 then trades fragments for
-// row groups across the lane rows, so slot s holds row 4s + b, columns 4a .. 4a+3 of fragment q. Each
-// store instruction thus writes 4 rows x 64 consecutive columns -- whole 128-byte lines (bf16) or
-// pairs of them (fp32) -- so no line is ever cached half written (with power-of-two row pitches,
-// half-written lines were evicted and written back twice). The epilogue is bound by VALU issue (each
-// wave64 VALU instruction takes 4 cycles), so it keeps to cross-lane moves (DPP, permlane swaps) and
-// selects, without branches. No LDS is used, so the next tile's loads can land in the stage buffers
-// meanwhile.
+// From registers, four fragments (64 columns) at a time. The store path issues one request per lane
+// quad when the quad's 4 lanes fall in one 128-byte line and one per lane otherwise (measured: a
+// store instruction whose 64 lanes touch 16 rows costs about 3x one that touches 4), so each lane quad
+// is given one output row: the quad transposes of each fragment leave lane (q, 4a + b) with row 4q + b,
+// columns 4a .. 4a+3 of fragment f in slot f, and a quad transpose across the slots then gives lane
+// (q, 4a + x) row 4q + s, columns 16x + 4a .. +3 in slot s. A store of slot s thus writes 4 rows x 64
+// columns, whole 128-byte lines (a line is never cached half written, which with power-of-two row
+// pitches led to lines evicted and written back twice), one line per quad for bf16 and two for fp32.
+// No LDS is used, so the next tile's loads can land in the stage buffers meanwhile.
 // FULL: the wave's whole 128 x 128 block lies inside Y and vector stores are allowed (then the row
 // offsets of a lane quad fit 32 bits); otherwise every element is bounds-checked.
 template <bool OUT_FP32, bool FULL>
-__device__ __forceinline__ void store_tile(const f32x4 (&acc)[FM][FN], const Args& a, int64_t mw, int64_t nw,
+__device__ __forceinline__ void store_tile(const f32x4 (&acc)[FM][FN], const Args& a, char* y, int64_t mw, int64_t nw,
                                            int lane) {
     constexpr int W = OUT_FP32 ? 4 : 2, ES = OUT_FP32 ? 4 : 2;
-    const int q = lane >> 4, r = lane & 15, b = r & 3, c4 = r & ~3;
+    const int q = lane >> 4, r = lane & 15, b = r & 3, a4 = r >> 2;
     const uint32_t sel = half_sel(b);
-    char* const y0 = static_cast<char*>(a.Y) + (mw * a.ldy + nw) * ES;  // wave-uniform corner
-    const uint32_t lane_off = FULL ? (uint32_t)((b * a.ldy + 16 * q + c4) * ES) : 0u;
+    char* const y0 = y + (mw * a.ldy + nw) * ES;  // wave-uniform corner
+    // lane (q, 4 a4 + b) stores row 4q + s, columns 16 b + 4 a4 .. +3 of the 64-column group
+    const uint32_t lane_off = FULL ? (uint32_t)((4 * q * a.ldy + 16 * b + 4 * a4) * ES) : 0u;
 #pragma unroll
     for (int i = 0; i < FM; i++) {
 #pragma unroll
@@ -343,26 +414,26 @@ __device__ __forceinline__ void store_tile(const f32x4 (&acc)[FM][FN], const Arg
                     quad_transpose_bf16(e, v[f], b, sel);
                 }
             }
-            row_transpose4<W>(v);
+            slot_transpose4<W>(v, b);
 #pragma unroll
             for (int s = 0; s < 4; s++) {
                 if constexpr (FULL) {
-                    char* const p = y0 + ((16 * i + 4 * s) * a.ldy + 64 * jg) * ES + lane_off;
+                    char* const p = y0 + ((16 * i + s) * a.ldy + 64 * jg) * ES + lane_off;
                     if constexpr (OUT_FP32)
                         *reinterpret_cast<uint4*>(p) = make_uint4(v[s][0], v[s][1], v[s][2], v[s][3]);
                     else
                         *reinterpret_cast<uint2*>(p) = make_uint2(v[s][0], v[s][1]);
                 } else {
-                    const int64_t m = mw + 16 * i + 4 * s + b, n = nw + 16 * (4 * jg + q) + c4;
+                    const int64_t m = mw + 16 * i + 4 * q + s, n = nw + 64 * jg + 16 * b + 4 * a4;
                     if (m < a.M) {
 #pragma unroll
                         for (int k = 0; k < 4; k++) {
                             if (n + k >= a.N) continue;
                             const uint32_t w = v[s][OUT_FP32 ? k : k >> 1];
                             if constexpr (OUT_FP32)
-                                reinterpret_cast<uint32_t*>(a.Y)[m * a.ldy + n + k] = w;
+                                reinterpret_cast<uint32_t*>(y)[m * a.ldy + n + k] = w;
                             else
-                                reinterpret_cast<uint16_t*>(a.Y)[m * a.ldy + n + k] = (uint16_t)(k & 1 ? w >> 16 : w);
+                                reinterpret_cast<uint16_t*>(y)[m * a.ldy + n + k] = (uint16_t)(k & 1 ? w >> 16 : w);
                         }
                     }
                 }
@@ -372,7 +443,65 @@ __device__ __forceinline__ void store_tile(const f32x4 (&acc)[FM][FN], const Arg
     }
 }
 
-template <bool OUT_FP32>
+// Token-major epilogue: Y is N x M, and each accumulator (column n, rows 4q .. 4q+3 of M) is 4
+// consecutive elements of token row n. The lanes of a quad hold 4 different rows n, so a quad
+// transpose across four row fragments (slots i) gives lane (q, 4c + x) token row 4c + s, elements
+// 16x + 4q .. +3 of the 64 M-columns of the fragment group in slot s: each quad's stores then fall in
+// one 128-byte line (bf16) or two (fp32), and each store instruction covers 16 token rows x 64
+// elements, whole lines.
+template <bool OUT_FP32, bool FULL>
+__device__ __forceinline__ void store_tile_tm(const f32x4 (&acc)[FM][FN], const Args& a, char* y, int64_t mw,
+                                              int64_t nw, int lane) {
+    constexpr int ES = OUT_FP32 ? 4 : 2, W = OUT_FP32 ? 4 : 2;
+    const int q = lane >> 4, r = lane & 15, x = r & 3, c = r >> 2;
+    char* const y0 = y + (nw * a.ldy + mw) * ES;  // wave-uniform corner
+    const uint32_t lane_off = FULL ? (uint32_t)((4 * c * a.ldy + 16 * x + 4 * q) * ES) : 0u;
+#pragma unroll
+    for (int j = 0; j < FN; j++) {
+#pragma unroll
+        for (int ig = 0; ig < FM / 4; ig++) {
+            uint32_t v[4][W];
+#pragma unroll
+            for (int f = 0; f < 4; f++) {
+                const f32x4 e = acc[4 * ig + f][j];
+                if constexpr (OUT_FP32) {
+#pragma unroll
+                    for (int t = 0; t < 4; t++) v[f][t] = __float_as_uint(e[t]);
+                } else {
+                    v[f][0] = pack_bf16x2_rne(e[0], e[1]);
+                    v[f][1] = pack_bf16x2_rne(e[2], e[3]);
+                }
+            }
+            slot_transpose4<W>(v, x);
+#pragma unroll
+            for (int s = 0; s < 4; s++) {
+                if constexpr (FULL) {
+                    char* const p = y0 + ((16 * j + s) * a.ldy + 64 * ig) * ES + lane_off;
+                    if constexpr (OUT_FP32)
+                        *reinterpret_cast<uint4*>(p) = make_uint4(v[s][0], v[s][1], v[s][2], v[s][3]);
+                    else
+                        *reinterpret_cast<uint2*>(p) = make_uint2(v[s][0], v[s][1]);
+                } else {
+                    const int64_t n = nw + 16 * j + 4 * c + s, m = mw + 64 * ig + 16 * x + 4 * q;
+                    if (n < a.N) {
+#pragma unroll
+                        for (int t = 0; t < 4; t++) {
+                            if (m + t >= a.M) continue;
+                            const uint32_t w = v[s][OUT_FP32 ? t : t >> 1];
+                            if constexpr (OUT_FP32)
+                                reinterpret_cast<uint32_t*>(y)[n * a.ldy + m + t] = w;
+                            else
+                                reinterpret_cast<uint16_t*>(y)[n * a.ldy + m + t] = (uint16_t)(t & 1 ? w >> 16 : w);
+                        }
+                    }
+                }
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+template <bool OUT_FP32, bool TM>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_bf16_tiled_kernel(Args a) {
     __shared__ __attribute__((aligned(16))) char smem[3 * STAGE_BYTES];
     // LDS byte address of the first stage buffer (for the LDS-destination loads)
@@ -383,8 +512,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     if (L < 0) return;  // whole workgroup
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int wm0 = (wave >> 1) * WM, wn0 = (wave & 1) * WN;
-    const LaneOffsets o = lane_offsets(wm0, wn0, lane);
-    const LoadOffsets lo = load_offsets(a, lane);
+    const LaneOffsets o = lane_offsets<TM>(wm0, wn0, lane);
+    const LoadOffsets lo = load_offsets<TM>(a, lane);
     const int S = (int)((a.K + BK - 1) / BK);
 
     f32x4 acc[FM][FN];
@@ -403,29 +532,37 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     //    stage g run;
     //  - inside a stage, B fragment j+2 is read while fragment j is multiplied (ring of 4).
     // With fewer than 3 stages per tile every workgroup has one tile (see the launcher).
-    TileDesc cur_t = tile_desc(a, L);
-    TileDesc next_t = tile_desc(a, tile_of(a, p, 1));
-    load_stage(l0, a, S > 0 ? cur_t : next_t, 0, wave, lo);
-    load_stage(l0 + STAGE_BYTES, a, S > 1 ? cur_t : next_t, S > 1 ? 1 : 0, wave, lo);
+    TileDesc cur_t = tile_desc<OUT_FP32>(a, L);
+    TileDesc next_t = tile_desc<OUT_FP32>(a, tile_of(a, p, 1));
+    load_stage<TM>(l0, a, S > 0 ? cur_t : next_t, 0, wave, lo);
+    load_stage<TM>(l0 + STAGE_BYTES, a, S > 1 ? cur_t : next_t, S > 1 ? 1 : 0, wave, lo);
     wait_vmcnt<LOADS_PER_STAGE>();
     __builtin_amdgcn_s_barrier();
-    load_stage(l0 + 2 * STAGE_BYTES, a, S > 2 ? cur_t : next_t, S > 2 ? 2 : 0, wave, lo);
+    load_stage<TM>(l0 + 2 * STAGE_BYTES, a, S > 2 ? cur_t : next_t, S > 2 ? 2 : 0, wave, lo);
 
     AFrags fa;
     bf16x16 rb[4];
     read_a(l0, o, fa);
-    rb[0] = read_b(l0, o, 0);
-    rb[1] = read_b(l0, o, 1);
+    rb[0] = read_b<TM>(l0, o, 0);
+    rb[1] = read_b<TM>(l0, o, 1);
     int g = 0;
     for (int k = 1;; k++) {
-        for (int s = 0; s < S; s++, g++) stage(l0, a, cur_t, next_t, s, S, g, acc, fa, rb, o, wave, lo);
+        for (int s = 0; s < S; s++, g++) stage<TM>(l0, a, cur_t, next_t, s, S, g, acc, fa, rb, o, wave, lo);
         // epilogue from registers; the next tile's first stages are in flight meanwhile
         {
             const int64_t mw = cur_t.m0 + wm0, nw = cur_t.n0 + wn0;
-            if ((mw + WM <= a.M) && (nw + WN <= a.N) && a.y_vec)
-                store_tile<OUT_FP32, true>(acc, a, mw, nw, lane);
-            else
-                store_tile<OUT_FP32, false>(acc, a, mw, nw, lane);
+            const bool full = (mw + WM <= a.M) && (nw + WN <= a.N) && a.y_vec;
+            if constexpr (TM) {
+                if (full)
+                    store_tile_tm<OUT_FP32, true>(acc, a, cur_t.y, mw, nw, lane);
+                else
+                    store_tile_tm<OUT_FP32, false>(acc, a, cur_t.y, mw, nw, lane);
+            } else {
+                if (full)
+                    store_tile<OUT_FP32, true>(acc, a, cur_t.y, mw, nw, lane);
+                else
+                    store_tile<OUT_FP32, false>(acc, a, cur_t.y, mw, nw, lane);
+            }
         }
         if (!next_t.valid) break;
 #pragma unroll
@@ -433,18 +570,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
             for (int j = 0; j < FN; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
         cur_t = next_t;
-        next_t = tile_desc(a, tile_of(a, p, k + 1));
+        next_t = tile_desc<OUT_FP32>(a, tile_of(a, p, k + 1));
     }
     wait_vmcnt<0>();  // the zero-filling loads past the last tile have landed before the workgroup ends
 }
 
 }  // namespace tiled_bf16
 
-bool gemm_bf16_tiled_ok(int64_t M, int64_t K, int64_t N, int64_t ldx, const void* X) {
-    // 32-bit load offsets: 64 rows of X (64 * ldx * 2 < 2^31) and 16 row blocks of compressed tiles
-    // (16 * K / 64 * 1 KB < 2^31) stay below bit 31, which marks the loads past the last tile
-    return ldx % 8 == 0 && (reinterpret_cast<uintptr_t>(X) & 15) == 0 && N > 64 && ldx < ((int64_t)1 << 24) &&
-           K < ((int64_t)1 << 22) && ((M + 255) / 256) * ((N + 255) / 256) < (1 << 30);
+bool gemm_bf16_tiled_ok(const GemmArgs& g) {
+    // 32-bit load offsets stay below bit 31, which marks the loads past the last tile: 64 rows of X
+    // (64 * ldx * 2), token-major 256 rows (256 * ldx * 2), and 16 row blocks of compressed tiles
+    // (16 * K / 64 * 1 KB); 16-byte aligned rows of X in every batch entry
+    const bool x_ok = g.ldx % 8 == 0 && (reinterpret_cast<uintptr_t>(g.X) & 15) == 0 && (g.batch == 1 || g.sx % 8 == 0);
+    const bool tm_ok = !g.tm || (g.K % 64 == 0 && g.ldx < ((int64_t)1 << 22));
+    const int64_t tiles = ((g.M + 255) / 256) * ((g.N + 255) / 256) * g.batch;
+    return x_ok && tm_ok && g.N > 64 && g.ldx < ((int64_t)1 << 24) && g.K < ((int64_t)1 << 22) && tiles < (1 << 30);
 }
 
 // Number of compute units of the current device (cached per device).
@@ -460,25 +600,36 @@ static int device_cus() {
     return cached[dev];
 }
 
-hipError_t launch_gemm_bf16_tiled(const uint16_t* values, const uint8_t* meta, int64_t M, int64_t K, const uint16_t* X,
-                                  int64_t N, int64_t ldx, void* Y, bool out_fp32, int64_t ldy, hipStream_t s) {
+hipError_t launch_gemm_bf16_tiled(const GemmArgs& g, hipStream_t s) {
     tiled_bf16::Args a;
-    a.vals = values; a.meta = meta; a.X = X; a.Y = Y;
-    a.M = M; a.K = K; a.N = N; a.ldx = ldx; a.ldy = ldy;
-    a.tilesM = (int)((M + tiled_bf16::BM - 1) / tiled_bf16::BM);
-    a.tilesN = (int)((N + tiled_bf16::BN - 1) / tiled_bf16::BN);
-    a.y_vec = ((reinterpret_cast<uintptr_t>(Y) & 15) == 0) && ((ldy * (out_fp32 ? 4 : 2)) % 16 == 0) &&
-              ldy * (out_fp32 ? 4 : 2) * 4 < ((int64_t)1 << 31);
-    const int T = a.tilesM * a.tilesN;
-    const int S = (int)((K + tiled_bf16::BK - 1) / tiled_bf16::BK);
+    a.vals = static_cast<const uint16_t*>(g.values); a.meta = g.meta;
+    a.X = static_cast<const uint16_t*>(g.X); a.Y = g.Y;
+    a.M = g.M; a.K = g.K; a.N = g.N; a.ldx = g.ldx; a.ldy = g.ldy;
+    a.sxb = g.sx; a.syb = g.sy;
+    a.tilesM = (int)((g.M + tiled_bf16::BM - 1) / tiled_bf16::BM);
+    a.tilesN = (int)((g.N + tiled_bf16::BN - 1) / tiled_bf16::BN);
+    a.batch = (int)g.batch;
+    // vector stores: 16-byte aligned Y rows in every batch entry, and a lane quad's row offsets in 32 bits
+    const int64_t es = g.out_fp32 ? 4 : 2;
+    a.y_vec = ((reinterpret_cast<uintptr_t>(g.Y) & 15) == 0) && ((g.ldy * es) % 16 == 0) &&
+              (g.batch == 1 || (g.sy * es) % 16 == 0) && g.ldy * es * 16 < ((int64_t)1 << 31);
+    const int T = a.tilesM * a.tilesN * a.batch;
+    const int S = (int)((g.K + tiled_bf16::BK - 1) / tiled_bf16::BK);
     // one workgroup per compute unit walking several tiles; one tile each when a tile has fewer than
     // three stages (the cross-tile pipeline then has nothing to overlap)
     const int cus = device_cus();
     const unsigned grid = (unsigned)(S >= 3 && T > cus ? cus : T);
-    if (out_fp32)
-        hipLaunchKernelGGL(tiled_bf16::gemm_bf16_tiled_kernel<true>, dim3(grid), dim3(256), 0, s, a);
-    else
-        hipLaunchKernelGGL(tiled_bf16::gemm_bf16_tiled_kernel<false>, dim3(grid), dim3(256), 0, s, a);
+    if (g.tm) {
+        if (g.out_fp32)
+            hipLaunchKernelGGL((tiled_bf16::gemm_bf16_tiled_kernel<true, true>), dim3(grid), dim3(256), 0, s, a);
+        else
+            hipLaunchKernelGGL((tiled_bf16::gemm_bf16_tiled_kernel<false, true>), dim3(grid), dim3(256), 0, s, a);
+    } else {
+        if (g.out_fp32)
+            hipLaunchKernelGGL((tiled_bf16::gemm_bf16_tiled_kernel<true, false>), dim3(grid), dim3(256), 0, s, a);
+        else
+            hipLaunchKernelGGL((tiled_bf16::gemm_bf16_tiled_kernel<false, false>), dim3(grid), dim3(256), 0, s, a);
+    }
     return hipGetLastError();
 }
 

@@ -12,32 +12,44 @@
 //
 // The compressed weight is stored in that lane order (16-row x 128-column tiles, see include/sp24.h).
 // Direct kernel: each wave owns a 16 x (16*NF) tile, reads A (1 KB) and the index (256 B) of each
-// tile from global memory and gathers B element by element with bounds checks (any shape and row
-// pitch). The LDS-tiled kernel (gemm_i8_tiled.hip) takes over for N > 64 with 16-byte X rows.
+// tile from global memory and gathers B element by element with bounds checks through general element
+// strides (any shape, layout, batch and row pitch). The LDS-tiled kernel (gemm_i8_tiled.hip) takes
+// over for N > 64 with 16-byte X rows.
 #include "sp24_device.h"
 #include "sp24_launch.h"
 
 namespace sp24 {
 
+// Element strides: X[k, n] at k * sxk + n * sxn, Y[m, n] at m * sym + n * syn; batch blockIdx.z adds
+// z * sxb / z * syb.
+struct DirectArgsI8 {
+    const int8_t* vals;
+    const uint8_t* meta;
+    int64_t M, K, N;
+    const int8_t* X;
+    int64_t sxk, sxn, sxb;
+    const float* scale;
+    void* Y;
+    int64_t sym, syn, syb;
+};
+
 template <int NF>
-__global__ __launch_bounds__(256) void gemm_i8_direct(const int8_t* __restrict__ vals, const uint8_t* __restrict__ meta,
-                                                      int64_t M, int64_t K, const int8_t* __restrict__ X, int64_t N,
-                                                      int64_t ldx, const float* __restrict__ scale,
-                                                      void* __restrict__ Y, int64_t ldy) {
+__global__ __launch_bounds__(256) void gemm_i8_direct(DirectArgsI8 d) {
     const int lane = threadIdx.x & 63;
     const int r = lane & 15, q = lane >> 4;
     const int64_t m0 = ((int64_t)blockIdx.y * 4 + (threadIdx.x >> 6)) * 16;
     const int64_t n0 = (int64_t)blockIdx.x * 16 * NF;
-    if (m0 >= M) return;  // whole wave
+    if (m0 >= d.M) return;  // whole wave
+    const int8_t* __restrict__ X = d.X + (int64_t)blockIdx.z * d.sxb;
     i32x4 acc[NF];
 #pragma unroll
     for (int f = 0; f < NF; f++) acc[f] = i32x4{0, 0, 0, 0};
 
     // compressed tiles of this 16-row block: 1 KB of values and 256 B of metadata per 128 dense
     // columns, in lane order (padded rows/columns hold zeros and canonical metadata)
-    const int64_t tiles_per_row = (K + 127) / 128;
-    const u32x4* vt = reinterpret_cast<const u32x4*>(vals) + (m0 >> 4) * tiles_per_row * 64 + lane;
-    const uint32_t* mt = reinterpret_cast<const uint32_t*>(meta) + (m0 >> 4) * tiles_per_row * 64 + lane;
+    const int64_t tiles_per_row = (d.K + 127) / 128;
+    const u32x4* vt = reinterpret_cast<const u32x4*>(d.vals) + (m0 >> 4) * tiles_per_row * 64 + lane;
+    const uint32_t* mt = reinterpret_cast<const uint32_t*>(d.meta) + (m0 >> 4) * tiles_per_row * 64 + lane;
     for (int64_t t = 0; t < tiles_per_row; t++) {
         const int64_t k0 = 128 * t;
         const u32x4 a = vt[64 * t];
@@ -55,7 +67,7 @@ __global__ __launch_bounds__(256) void gemm_i8_direct(const int8_t* __restrict__
                     const int e = 4 * w + s;
                     const int64_t k = k0 + 16 * q + (e & 15) + 64 * (e >> 4);
                     uint32_t v = 0;
-                    if (n < N && k < K) v = (uint8_t)X[k * ldx + n];
+                    if (n < d.N && k < d.K) v = (uint8_t)X[k * d.sxk + n * d.sxn];
                     v4 |= v << (8 * s);
                 }
                 b[w] = v4;
@@ -64,34 +76,54 @@ __global__ __launch_bounds__(256) void gemm_i8_direct(const int8_t* __restrict__
             acc[f] = __builtin_amdgcn_smfmac_i32_16x16x128_i8(av, bv, acc[f], (int)idx, 0, 0);
         }
     }
+    char* const Y = static_cast<char*>(d.Y) + (int64_t)blockIdx.z * d.syb * 4;
 #pragma unroll
     for (int f = 0; f < NF; f++) {
         const int64_t n = n0 + 16 * f + r;
-        if (n >= N) continue;
+        if (n >= d.N) continue;
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             const int64_t m = m0 + 4 * q + i;
-            if (m >= M) continue;
-            if (scale)
-                reinterpret_cast<float*>(Y)[m * ldy + n] = __fmul_rn((float)acc[f][i], scale[m]);
+            if (m >= d.M) continue;
+            const int64_t o = m * d.sym + n * d.syn;
+            if (d.scale)
+                reinterpret_cast<float*>(Y)[o] = __fmul_rn((float)acc[f][i], d.scale[m]);
             else
-                reinterpret_cast<int32_t*>(Y)[m * ldy + n] = acc[f][i];
+                reinterpret_cast<int32_t*>(Y)[o] = acc[f][i];
         }
     }
 }
 
-hipError_t launch_gemm_i8(const int8_t* values, const uint8_t* meta, int64_t M, int64_t K, const int8_t* X, int64_t N,
-                          int64_t ldx, const float* scale, void* Y, int64_t ldy, hipStream_t s) {
-    if (gemm_i8_tiled_ok(M, K, N, ldx, X)) return launch_gemm_i8_tiled(values, meta, M, K, X, N, ldx, scale, Y, ldy, s);
-    const unsigned gy = (unsigned)((M + 63) / 64);
-    if (N <= 16) {
-        hipLaunchKernelGGL(gemm_i8_direct<1>, dim3((unsigned)((N + 15) / 16), gy), dim3(256), 0, s, values, meta, M, K,
-                           X, N, ldx, scale, Y, ldy);
-    } else {
-        hipLaunchKernelGGL(gemm_i8_direct<4>, dim3((unsigned)((N + 63) / 64), gy), dim3(256), 0, s, values, meta, M, K,
-                           X, N, ldx, scale, Y, ldy);
+hipError_t launch_gemm_i8(const GemmArgs& g, hipStream_t s) {
+    if (gemm_i8_tiled_ok(g)) return launch_gemm_i8_tiled(g, s);
+    DirectArgsI8 d;
+    d.vals = static_cast<const int8_t*>(g.values);
+    d.meta = g.meta;
+    d.M = g.M; d.K = g.K; d.N = g.N;
+    d.X = static_cast<const int8_t*>(g.X);
+    d.sxk = g.tm ? 1 : g.ldx;
+    d.sxn = g.tm ? g.ldx : 1;
+    d.sxb = g.sx;
+    d.scale = g.scale;
+    d.Y = g.Y;
+    d.sym = g.tm ? 1 : g.ldy;
+    d.syn = g.tm ? g.ldy : 1;
+    d.syb = g.sy;
+    const unsigned gy = (unsigned)((g.M + 63) / 64);
+    // grid z covers at most 65535 batch entries per launch
+    for (int64_t b0 = 0; b0 < g.batch; b0 += 65535) {
+        const unsigned gz = (unsigned)(g.batch - b0 < 65535 ? g.batch - b0 : 65535);
+        DirectArgsI8 e = d;
+        e.X = d.X + b0 * d.sxb;
+        e.Y = static_cast<char*>(d.Y) + b0 * d.syb * 4;
+        if (g.N <= 16)
+            hipLaunchKernelGGL(gemm_i8_direct<1>, dim3((unsigned)((g.N + 15) / 16), gy, gz), dim3(256), 0, s, e);
+        else
+            hipLaunchKernelGGL(gemm_i8_direct<4>, dim3((unsigned)((g.N + 63) / 64), gy, gz), dim3(256), 0, s, e);
+        const hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
     }
-    return hipGetLastError();
+    return hipSuccess;
 }
 
 }  // namespace sp24

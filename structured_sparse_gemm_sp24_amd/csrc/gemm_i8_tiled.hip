@@ -26,6 +26,13 @@
 // XCD at the same time, groups of 8 tile-rows) with the LDS pipeline continued across tiles; the
 // epilogue dequantizes in registers, transposes 4 x 4 blocks inside lane quads by DPP and stores 16
 // bytes per lane, so its stores drain while the next tile computes.
+//
+// Token-major X (N x K) and Y (N x M): the B tile is 256 token rows x 128 k (128 B per row), a lane's
+// operand two 16-byte runs of its token's row (k = 16q .. +15 and 64 + 16q .. +15), read with two
+// ds_read_b128 from units stored at unit ^ f(n), f(n) = ((n >> 1) & 7) ^ 4 (n & 1) (conflict-free, as
+// in the bf16 kernel); each accumulator's 4 consecutive rows of M are one 16-byte store of token row
+// n. K must be a multiple of 128 there. A batch of products sharing the weight adds the batch to the
+// tile index.
 #include "sp24_device.h"
 #include "sp24_launch.h"
 
@@ -80,13 +87,16 @@ struct Args {
     const float* scale;
     void* Y;
     int64_t M, K, N, ldx, ldy;
-    int tilesM, tilesN;
+    int64_t sxb, syb;  // batch strides (elements)
+    int tilesM, tilesN, batch;
     int y_vec;  // Y base and row pitch allow 16-byte stores, 4 rows < 2^31 bytes
 };
 
 // Corner and compressed-tile descriptors of one tile; `valid` is false past the workgroup's last tile.
 struct TileDesc {
     int64_t m0, n0;
+    const int8_t* x;  // X and Y of the tile's batch entry
+    char* y;
     i32x4 rA, rM;
     bool valid;
 };
@@ -96,7 +106,7 @@ struct TileDesc {
 // contiguous run of rem / 8 or rem / 8 + 1 of them, so a partial last turn still spreads its tiles,
 // and their output writes, over every XCD, and neighbouring tiles share an L2.
 __device__ __forceinline__ int tile_of(const Args& a, int p, int k) {
-    const int G = gridDim.x, T = a.tilesM * a.tilesN;
+    const int G = gridDim.x, T = a.tilesM * a.tilesN * a.batch;
     const int64_t base = (int64_t)k * G;
     if (base >= T) return -1;
     const int rem = (T - base) < G ? (int)(T - base) : G;
@@ -108,29 +118,46 @@ __device__ __forceinline__ int tile_of(const Args& a, int p, int k) {
 // Swizzle of the 16-byte units of B row k (see the header).
 __device__ __forceinline__ int bswz(int k) { return (k & 7) | (((k >> 4) & 1) << 3); }
 
+// 16-byte unit swizzle of token row n of a token-major B tile.
+__device__ __forceinline__ int tm_swz(int n) { return ((n >> 1) & 7) ^ ((n & 1) << 2); }
+
 // Per-lane parts of the load offsets.
 struct LoadOffsets {
     uint32_t a;      // A tile: 16 * lane
     uint32_t m;      // metadata: tile (lane / 16) of the wave's 4 blocks, 16 * (lane % 16) inside it
-    uint32_t b[8];   // B rows 4h + lane / 16 of the wave's 32 rows: row part + swizzled chunk
+    uint32_t b[8];   // B rows 4h + lane / 16 of the wave's 32 rows: row part + swizzled chunk;
+                     // token-major: rows 8h + lane / 8 of the wave's 64 (row part relative to the wave's first)
 };
 
+template <bool TM>
 __device__ __forceinline__ LoadOffsets load_offsets(const Args& a, int lane, int wave) {
     LoadOffsets o;
     const int tiles = (int)((a.K + BK - 1) / BK);
     o.a = 16 * lane;
     o.m = (uint32_t)((lane >> 4) * tiles * 256 + 16 * (lane & 15));
-    const int p = lane & 15;  // 16-byte slot in the LDS row
+    if constexpr (TM) {
+        // lane i of a load lands in token row 8h + i / 8 of the wave's rows, 16-byte slot i % 8, and
+        // reads the unit that belongs there
 #pragma unroll
-    for (int h = 0; h < 8; h++) {
-        const int row = 32 * wave + 4 * h + (lane >> 4);
-        o.b[h] = (uint32_t)(row * a.ldx + 16 * (p ^ bswz(row)));
+        for (int h = 0; h < 8; h++) {
+            const int row = 8 * h + (lane >> 3);
+            o.b[h] = (uint32_t)(row * a.ldx + 16 * ((lane & 7) ^ tm_swz(row)));
+        }
+        (void)wave;
+    } else {
+        const int p = lane & 15;  // 16-byte slot in the LDS row
+#pragma unroll
+        for (int h = 0; h < 8; h++) {
+            const int row = 32 * wave + 4 * h + (lane >> 4);
+            o.b[h] = (uint32_t)(row * a.ldx + 16 * (p ^ bswz(row)));
+        }
     }
     return o;
 }
 
 // This wave's share of the loads of stage s of tile td into the buffer at LDS address `lds`. When td
 // is not valid the offsets get bit 31 set (beyond every record count): zeros, no memory traffic.
+template <bool TM>
 __device__ __forceinline__ void load_stage(uint32_t lds, const Args& a, const TileDesc& td, int s, int wave,
                                            const LoadOffsets& lo) {
     const int64_t k0 = (int64_t)s * BK;
@@ -143,17 +170,31 @@ __device__ __forceinline__ void load_stage(uint32_t lds, const Args& a, const Ti
     }
     // metadata of blocks 4 wave .. 4 wave + 3 (one 256 B tile each) in one instruction
     dma16(lds + A_BYTES + 4 * wave * 256, lo.m + (((uint32_t)(4 * wave * tiles + s) * 256u) | past), td.rM);
-    // X's exact extent from this stage's corner, rounded up to whole dwords (see make_rsrc)
-    const i32x4 rB = make_rsrc(a.X + k0 * a.ldx + td.n0, td.valid ? (a.K - 1 - k0) * a.ldx + a.N - td.n0 : 0);
+    if constexpr (TM) {
+        // token rows 64 wave .. +63 of the tile, 8 per load; X's extent from the wave's first row:
+        // rows past N read zeros (K is a multiple of 128: no stage reaches past K)
+        const int64_t n1 = td.n0 + 64 * wave;
+        const i32x4 rB = make_rsrc(td.x + n1 * a.ldx + k0, td.valid ? (a.N - 1 - n1) * a.ldx + a.K - k0 : 0);
 #pragma unroll
-    for (int h = 0; h < 8; h++) dma16(lds + A_BYTES + META_BYTES + (32 * wave + 4 * h) * B_ROW, lo.b[h], rB);
+        for (int h = 0; h < 8; h++) dma16(lds + A_BYTES + META_BYTES + (64 * wave + 8 * h) * 128, lo.b[h], rB);
+    } else {
+        // X's exact extent from this stage's corner, rounded up to whole dwords (see make_rsrc)
+        const i32x4 rB = make_rsrc(td.x + k0 * a.ldx + td.n0, td.valid ? (a.K - 1 - k0) * a.ldx + a.N - td.n0 : 0);
+#pragma unroll
+        for (int h = 0; h < 8; h++) dma16(lds + A_BYTES + META_BYTES + (32 * wave + 4 * h) * B_ROW, lo.b[h], rB);
+    }
 }
 
-// Descriptor of logical tile L (-1: none); tiles walked in groups of GROUP_M tile-rows.
+// Descriptor of logical tile L (-1: none); batch entries follow each other, and inside one tiles are
+// walked in groups of GROUP_M tile-rows.
 __device__ __forceinline__ TileDesc tile_desc(const Args& a, int L) {
     TileDesc td;
     td.valid = L >= 0;
-    const int Lc = L >= 0 ? L : 0;
+    const int per = a.tilesM * a.tilesN;
+    const int bt = L >= 0 ? L / per : 0;
+    const int Lc = L >= 0 ? L - bt * per : 0;
+    td.x = a.X + bt * a.sxb;
+    td.y = static_cast<char*>(a.Y) + bt * a.syb * 4;
     const int gsize = GROUP_M * a.tilesN;
     const int g = Lc / gsize;
     const int first_m = g * GROUP_M;
@@ -172,14 +213,23 @@ __device__ __forceinline__ TileDesc tile_desc(const Args& a, int L) {
 struct LaneOffsets {
     int a;       // A fragment of block wm0/16: block * 1024 + lane * 16
     int m;       // metadata: A_BYTES + block * 256 + lane * 4
-    int b[FN];   // B fragment j, first read (t = 0)
+    int b[FN];   // B fragment j, first read (t = 0); token-major: the two reads of fragment 0
 };
 
+template <bool TM>
 __device__ __forceinline__ LaneOffsets lane_offsets(int wm0, int wn0, int lane) {
     const int r = lane & 15, q = lane >> 4;
     LaneOffsets o;
     o.a = (wm0 >> 4) * 1024 + lane * 16;
     o.m = A_BYTES + (wm0 >> 4) * 256 + lane * 4;
+    if constexpr (TM) {
+        const int base = A_BYTES + META_BYTES + (wn0 + r) * 128, u = q ^ tm_swz(r);
+        o.b[0] = base + 16 * u;
+        o.b[1] = base + 16 * (u ^ 4);
+#pragma unroll
+        for (int j = 2; j < FN; j++) o.b[j] = 0;
+        return o;
+    }
     // read t of group q covers rows 16q + 8(t&1) + 64(t>>1) + r/2, which share row & 7 and
     // (row >> 4) & 1 with row0, so the swizzle is fixed per lane and t only adds immediates
     const int row0 = 16 * q + (r >> 1);
@@ -219,8 +269,18 @@ __device__ __forceinline__ void read_a(uint32_t buf, const LaneOffsets& o, AFrag
 
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 
-// B fragment j (16 columns x 128 k): four transposing reads of 8 k each.
+// B fragment j (16 columns x 128 k): four transposing reads of 8 k each, or, token-major, two 16-byte
+// reads of the lane's token row.
+template <bool TM>
 __device__ __forceinline__ i32x8 read_b(uint32_t buf, const LaneOffsets& o, int j) {
+    if constexpr (TM) {
+        typedef const __attribute__((address_space(3))) i32x4 lds_i32x4;
+        const lds_char* p0 = (const lds_char*)(size_t)stage_addr(buf, o.b[0]);
+        const lds_char* p1 = (const lds_char*)(size_t)stage_addr(buf, o.b[1]);
+        const i32x4 lo = *reinterpret_cast<lds_i32x4*>(p0 + j * 2048);
+        const i32x4 hi = *reinterpret_cast<lds_i32x4*>(p1 + j * 2048);
+        return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
     const lds_char* p = (const lds_char*)(size_t)stage_addr(buf, o.b[j]);
     i32x8 b;
 #pragma unroll
@@ -243,6 +303,7 @@ __device__ __forceinline__ void mfma_block(i32x4 (&acc)[FM][FN], const AFrags& f
 // fragments are read two blocks ahead (ring of 4); before the last two blocks the barrier publishes
 // stage g+1 and the loads of stage s+3 of this tile (or s+3-S of the next) go into this buffer; the next
 // stage's A fragments are reloaded one by one inside the last block. No branches.
+template <bool TM>
 __device__ __forceinline__ void stage(uint32_t l0, const Args& a, const TileDesc& cur_t, const TileDesc& next_t, int s,
                                       int S, int g, i32x4 (&acc)[FM][FN], AFrags& f, i32x8 (&rb)[4],
                                       const LaneOffsets& o, int wave, const LoadOffsets& lo) {
@@ -251,7 +312,7 @@ __device__ __forceinline__ void stage(uint32_t l0, const Args& a, const TileDesc
     const uint32_t nxt = l0 + (cb == 2 ? 0 : cb + 1) * STAGE_BYTES;
 #pragma unroll
     for (int j = 0; j < 6; j++) {
-        rb[(j + 2) & 3] = read_b(cur, o, j + 2);
+        rb[(j + 2) & 3] = read_b<TM>(cur, o, j + 2);
         __builtin_amdgcn_sched_barrier(0);
         mfma_block(acc, f, rb[j & 3], j);
         __builtin_amdgcn_sched_barrier(0);
@@ -260,9 +321,9 @@ __device__ __forceinline__ void stage(uint32_t l0, const Args& a, const TileDesc
     wait_vmcnt<LOADS_PER_STAGE>();       // stage g+1 has landed
     __builtin_amdgcn_s_barrier();
     const bool here = s + 3 < S;
-    load_stage(cur, a, here ? cur_t : next_t, here ? s + 3 : s + 3 - S, wave, lo);
-    rb[0] = read_b(nxt, o, 0);
-    rb[1] = read_b(nxt, o, 1);
+    load_stage<TM>(cur, a, here ? cur_t : next_t, here ? s + 3 : s + 3 - S, wave, lo);
+    rb[0] = read_b<TM>(nxt, o, 0);
+    rb[1] = read_b<TM>(nxt, o, 1);
     __builtin_amdgcn_sched_barrier(0);
     mfma_block(acc, f, rb[2], 6);
     __builtin_amdgcn_sched_barrier(0);
@@ -278,19 +339,20 @@ __device__ __forceinline__ void stage(uint32_t l0, const Args& a, const TileDesc
 }
 
 // Epilogue from registers, four fragments (64 columns) at a time. The dequant -- fl32(fl32(acc) *
-// scale[m]), one rounding multiply -- is applied per accumulator row; the quad transposes leave lane
-// (q, 4a + b) with row 4q + b, columns 4a .. 4a+3 of each fragment f, and row_transpose4 trades
-// fragments for row groups across the lane rows, so slot s holds row 4s + b, columns 4a .. 4a+3 of
-// fragment q. Each 16-byte store instruction thus writes 4 rows x 256 bytes -- whole 128-byte lines,
-// never a half-written line that the cache could evict and write back twice (as happened with
-// power-of-two row pitches). No LDS is used.
+// scale[m]), one rounding multiply -- is applied per accumulator row; then, as in the bf16 kernel, the
+// quad transposes of each fragment and a quad transpose across the four fragments give lane
+// (q, 4a + x) row 4q + s, columns 16x + 4a .. +3 in slot s, so each lane quad stores into one row (two
+// 128-byte lines, one request each, instead of one request per lane) and each 16-byte store
+// instruction writes 4 rows x 256 bytes, whole lines (never a half-written line that the cache could
+// evict and write back twice, as happened with power-of-two row pitches). No LDS is used.
 // FULL: the wave's whole 128 x 128 block lies inside Y and 16-byte stores are allowed (then the row
 // offsets of a lane quad fit 32 bits); otherwise every element is bounds-checked.
 template <bool SCALE, bool FULL>
-__device__ __forceinline__ void store_tile(const i32x4 (&acc)[FM][FN], const Args& a, int64_t mw, int64_t nw, int lane) {
-    const int q = lane >> 4, r = lane & 15, b = r & 3, c4 = r & ~3;
-    char* const y0 = reinterpret_cast<char*>(a.Y) + (mw * a.ldy + nw) * 4;  // wave-uniform corner
-    const uint32_t lane_off = FULL ? (uint32_t)((b * a.ldy + 16 * q + c4) * 4) : 0u;
+__device__ __forceinline__ void store_tile(const i32x4 (&acc)[FM][FN], const Args& a, char* y, int64_t mw, int64_t nw,
+                                           int lane) {
+    const int q = lane >> 4, r = lane & 15, b = r & 3, a4 = r >> 2;
+    char* const y0 = y + (mw * a.ldy + nw) * 4;  // wave-uniform corner
+    const uint32_t lane_off = FULL ? (uint32_t)((4 * q * a.ldy + 16 * b + 4 * a4) * 4) : 0u;
 #pragma unroll
     for (int i = 0; i < FM; i++) {
         const int64_t mq = mw + 16 * i + 4 * q;  // accumulator rows mq .. mq+3
@@ -309,15 +371,15 @@ __device__ __forceinline__ void store_tile(const i32x4 (&acc)[FM][FN], const Arg
                 }
                 quad_transpose(v[f], b);
             }
-            row_transpose4<4>(v);
+            slot_transpose4<4>(v, b);
 #pragma unroll
             for (int s = 0; s < 4; s++) {
                 if constexpr (FULL) {
-                    char* const p = y0 + ((16 * i + 4 * s) * a.ldy + 64 * jg) * 4 + lane_off;
+                    char* const p = y0 + ((16 * i + s) * a.ldy + 64 * jg) * 4 + lane_off;
                     *reinterpret_cast<uint4*>(p) = make_uint4(v[s][0], v[s][1], v[s][2], v[s][3]);
                 } else {
-                    const int64_t m = mw + 16 * i + 4 * s + b, n = nw + 16 * (4 * jg + q) + c4;
-                    uint32_t* p = reinterpret_cast<uint32_t*>(a.Y) + m * a.ldy + n;
+                    const int64_t m = mw + 16 * i + 4 * q + s, n = nw + 64 * jg + 16 * b + 4 * a4;
+                    uint32_t* p = reinterpret_cast<uint32_t*>(y) + m * a.ldy + n;
                     if (m < a.M) {
 #pragma unroll
                         for (int k = 0; k < 4; k++)
@@ -330,7 +392,58 @@ __device__ __forceinline__ void store_tile(const i32x4 (&acc)[FM][FN], const Arg
     }
 }
 
-template <bool SCALE>
+// Token-major epilogue: Y is N x M; each accumulator (column n, rows 4q .. 4q+3 of M) is dequantized
+// per row and is 4 consecutive elements of token row n. As in the bf16 kernel, a quad transpose
+// across four row fragments gives each lane quad one token row (16x + 4q .. +3 of 64 M-columns in
+// lane 4c + x), so a quad's 16-byte stores fall in two 128-byte lines and each store instruction
+// covers 16 token rows x 256 bytes.
+template <bool SCALE, bool FULL>
+__device__ __forceinline__ void store_tile_tm(const i32x4 (&acc)[FM][FN], const Args& a, char* y, int64_t mw,
+                                              int64_t nw, int lane) {
+    const int q = lane >> 4, r = lane & 15, x = r & 3, c = r >> 2;
+    char* const y0 = y + (nw * a.ldy + mw) * 4;  // wave-uniform corner
+    const uint32_t lane_off = FULL ? (uint32_t)((4 * c * a.ldy + 16 * x + 4 * q) * 4) : 0u;
+    float sc[FM][4];
+#pragma unroll
+    for (int i = 0; i < FM; i++)
+#pragma unroll
+        for (int t = 0; t < 4; t++) {
+            const int64_t m = mw + 16 * i + 4 * q + t;
+            sc[i][t] = (SCALE && (FULL || m < a.M)) ? a.scale[m] : 0.f;
+        }
+#pragma unroll
+    for (int j = 0; j < FN; j++) {
+#pragma unroll
+        for (int ig = 0; ig < FM / 4; ig++) {
+            uint32_t v[4][4];
+#pragma unroll
+            for (int f = 0; f < 4; f++)
+#pragma unroll
+                for (int t = 0; t < 4; t++) {
+                    const int e = acc[4 * ig + f][j][t];
+                    v[f][t] = SCALE ? __float_as_uint(__fmul_rn((float)e, sc[4 * ig + f][t])) : (uint32_t)e;
+                }
+            slot_transpose4<4>(v, x);
+#pragma unroll
+            for (int s = 0; s < 4; s++) {
+                if constexpr (FULL) {
+                    char* const p = y0 + ((16 * j + s) * a.ldy + 64 * ig) * 4 + lane_off;
+                    *reinterpret_cast<uint4*>(p) = make_uint4(v[s][0], v[s][1], v[s][2], v[s][3]);
+                } else {
+                    const int64_t n = nw + 16 * j + 4 * c + s, m = mw + 64 * ig + 16 * x + 4 * q;
+                    if (n < a.N) {
+#pragma unroll
+                        for (int t = 0; t < 4; t++)
+                            if (m + t < a.M) reinterpret_cast<uint32_t*>(y)[n * a.ldy + m + t] = v[s][t];
+                    }
+                }
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+template <bool SCALE, bool TM>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_i8_tiled_kernel(Args a) {
     __shared__ __attribute__((aligned(16))) char smem[3 * STAGE_BYTES];
     const uint32_t l0 = (uint32_t)(size_t)(__attribute__((address_space(3))) char*)smem;
@@ -340,8 +453,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     if (L < 0) return;  // whole workgroup
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int wm0 = (wave >> 1) * WM, wn0 = (wave & 1) * WN;
-    const LaneOffsets o = lane_offsets(wm0, wn0, lane);
-    const LoadOffsets lo = load_offsets(a, lane, wave);
+    const LaneOffsets o = lane_offsets<TM>(wm0, wn0, lane);
+    const LoadOffsets lo = load_offsets<TM>(a, lane, wave);
     const int S = (int)((a.K + BK - 1) / BK);
 
     i32x4 acc[FM][FN];
@@ -354,26 +467,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // stages per tile every workgroup has one tile (see the launcher)
     TileDesc cur_t = tile_desc(a, L);
     TileDesc next_t = tile_desc(a, tile_of(a, p, 1));
-    load_stage(l0, a, S > 0 ? cur_t : next_t, 0, wave, lo);
-    load_stage(l0 + STAGE_BYTES, a, S > 1 ? cur_t : next_t, S > 1 ? 1 : 0, wave, lo);
+    load_stage<TM>(l0, a, S > 0 ? cur_t : next_t, 0, wave, lo);
+    load_stage<TM>(l0 + STAGE_BYTES, a, S > 1 ? cur_t : next_t, S > 1 ? 1 : 0, wave, lo);
     wait_vmcnt<LOADS_PER_STAGE>();
     __builtin_amdgcn_s_barrier();
-    load_stage(l0 + 2 * STAGE_BYTES, a, S > 2 ? cur_t : next_t, S > 2 ? 2 : 0, wave, lo);
+    load_stage<TM>(l0 + 2 * STAGE_BYTES, a, S > 2 ? cur_t : next_t, S > 2 ? 2 : 0, wave, lo);
 
     AFrags fa;
     i32x8 rb[4];
     read_a(l0, o, fa);
-    rb[0] = read_b(l0, o, 0);
-    rb[1] = read_b(l0, o, 1);
+    rb[0] = read_b<TM>(l0, o, 0);
+    rb[1] = read_b<TM>(l0, o, 1);
     int g = 0;
     for (int k = 1;; k++) {
-        for (int s = 0; s < S; s++, g++) stage(l0, a, cur_t, next_t, s, S, g, acc, fa, rb, o, wave, lo);
+        for (int s = 0; s < S; s++, g++) stage<TM>(l0, a, cur_t, next_t, s, S, g, acc, fa, rb, o, wave, lo);
         {
             const int64_t mw = cur_t.m0 + wm0, nw = cur_t.n0 + wn0;
-            if ((mw + WM <= a.M) && (nw + WN <= a.N) && a.y_vec)
-                store_tile<SCALE, true>(acc, a, mw, nw, lane);
-            else
-                store_tile<SCALE, false>(acc, a, mw, nw, lane);
+            const bool full = (mw + WM <= a.M) && (nw + WN <= a.N) && a.y_vec;
+            if constexpr (TM) {
+                if (full)
+                    store_tile_tm<SCALE, true>(acc, a, cur_t.y, mw, nw, lane);
+                else
+                    store_tile_tm<SCALE, false>(acc, a, cur_t.y, mw, nw, lane);
+            } else {
+                if (full)
+                    store_tile<SCALE, true>(acc, a, cur_t.y, mw, nw, lane);
+                else
+                    store_tile<SCALE, false>(acc, a, cur_t.y, mw, nw, lane);
+            }
         }
         if (!next_t.valid) break;
 #pragma unroll
@@ -388,24 +509,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
 }  // namespace tiled_i8
 
-bool gemm_i8_tiled_ok(int64_t M, int64_t K, int64_t N, int64_t ldx, const void* X) {
-    // 16-byte X rows; 32-bit load offsets: 128 rows of X (128 * ldx < 2^31) and 16 row blocks of
-    // compressed tiles (16 * K / 128 * 1 KB < 2^31) stay below bit 31, which marks the loads past the
-    // last stage
-    return ldx % 16 == 0 && (reinterpret_cast<uintptr_t>(X) & 15) == 0 && N > 64 && ldx < ((int64_t)1 << 24) &&
-           K < ((int64_t)1 << 22) && ((M + 255) / 256) * ((N + 255) / 256) < (1 << 30);
+bool gemm_i8_tiled_ok(const GemmArgs& g) {
+    // 16-byte X rows in every batch entry; 32-bit load offsets stay below bit 31, which marks the
+    // loads past the last stage: 128 rows of X (128 * ldx), token-major 64 rows from a wave's first,
+    // and 16 row blocks of compressed tiles (16 * K / 128 * 1 KB)
+    const bool x_ok = g.ldx % 16 == 0 && (reinterpret_cast<uintptr_t>(g.X) & 15) == 0 && (g.batch == 1 || g.sx % 16 == 0);
+    const bool tm_ok = !g.tm || g.K % 128 == 0;
+    const int64_t tiles = ((g.M + 255) / 256) * ((g.N + 255) / 256) * g.batch;
+    return x_ok && tm_ok && g.N > 64 && g.ldx < ((int64_t)1 << 24) && g.K < ((int64_t)1 << 22) && tiles < (1 << 30);
 }
 
-hipError_t launch_gemm_i8_tiled(const int8_t* values, const uint8_t* meta, int64_t M, int64_t K, const int8_t* X,
-                                int64_t N, int64_t ldx, const float* scale, void* Y, int64_t ldy, hipStream_t s) {
+hipError_t launch_gemm_i8_tiled(const GemmArgs& g, hipStream_t s) {
     tiled_i8::Args a;
-    a.vals = values; a.meta = meta; a.X = X; a.scale = scale; a.Y = Y;
-    a.M = M; a.K = K; a.N = N; a.ldx = ldx; a.ldy = ldy;
-    a.tilesM = (int)((M + tiled_i8::BM - 1) / tiled_i8::BM);
-    a.tilesN = (int)((N + tiled_i8::BN - 1) / tiled_i8::BN);
-    a.y_vec = ((reinterpret_cast<uintptr_t>(Y) & 15) == 0) && ((ldy * 4) % 16 == 0) && ldy * 16 < ((int64_t)1 << 31);
-    const int T = a.tilesM * a.tilesN;
-    const int S = (int)((K + tiled_i8::BK - 1) / tiled_i8::BK);
+    a.vals = static_cast<const int8_t*>(g.values); a.meta = g.meta;
+    a.X = static_cast<const int8_t*>(g.X); a.scale = g.scale; a.Y = g.Y;
+    a.M = g.M; a.K = g.K; a.N = g.N; a.ldx = g.ldx; a.ldy = g.ldy;
+    a.sxb = g.sx; a.syb = g.sy;
+    a.tilesM = (int)((g.M + tiled_i8::BM - 1) / tiled_i8::BM);
+    a.tilesN = (int)((g.N + tiled_i8::BN - 1) / tiled_i8::BN);
+    a.batch = (int)g.batch;
+    // vector stores: 16-byte aligned Y rows in every batch entry, and 16 rows' offsets in 32 bits
+    a.y_vec = ((reinterpret_cast<uintptr_t>(g.Y) & 15) == 0) && ((g.ldy * 4) % 16 == 0) &&
+              (g.batch == 1 || (g.sy * 4) % 16 == 0) && g.ldy * 64 < ((int64_t)1 << 31);
+    const int T = a.tilesM * a.tilesN * a.batch;
+    const int S = (int)((g.K + tiled_i8::BK - 1) / tiled_i8::BK);
     int cus = 0, dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
                                                  hipSuccess || cus <= 0)
@@ -413,10 +540,17 @@ hipError_t launch_gemm_i8_tiled(const int8_t* values, const uint8_t* meta, int64
     // one workgroup per compute unit walking several tiles; one tile each when a tile has fewer than
     // three stages (the cross-tile pipeline then has nothing to overlap)
     const unsigned grid = (unsigned)(S >= 3 && T > cus ? cus : T);
-    if (scale)
-        hipLaunchKernelGGL(tiled_i8::gemm_i8_tiled_kernel<true>, dim3(grid), dim3(256), 0, s, a);
-    else
-        hipLaunchKernelGGL(tiled_i8::gemm_i8_tiled_kernel<false>, dim3(grid), dim3(256), 0, s, a);
+    if (g.tm) {
+        if (g.scale)
+            hipLaunchKernelGGL((tiled_i8::gemm_i8_tiled_kernel<true, true>), dim3(grid), dim3(256), 0, s, a);
+        else
+            hipLaunchKernelGGL((tiled_i8::gemm_i8_tiled_kernel<false, true>), dim3(grid), dim3(256), 0, s, a);
+    } else {
+        if (g.scale)
+            hipLaunchKernelGGL((tiled_i8::gemm_i8_tiled_kernel<true, false>), dim3(grid), dim3(256), 0, s, a);
+        else
+            hipLaunchKernelGGL((tiled_i8::gemm_i8_tiled_kernel<false, false>), dim3(grid), dim3(256), 0, s, a);
+    }
     return hipGetLastError();
 }
 

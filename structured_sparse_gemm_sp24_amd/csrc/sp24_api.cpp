@@ -150,38 +150,86 @@ int sp24_decompress(const void* values, const uint8_t* meta, int dtype, int64_t 
         sp24::launch_decompress(values, meta, dtype, M, K, W_out, ldw, static_cast<hipStream_t>(stream)));
 }
 
-int sp24_gemm_bf16(const void* values, const uint8_t* meta, int64_t M, int64_t K, const void* X, int64_t N,
-                   int64_t ldx, void* Y, int out_dtype, int64_t ldy, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared validation of the GEMM operands (both dtypes); fills g on success. esx / esy: element sizes
+// of X and Y.
+int check_gemm(const void* values, const uint8_t* meta, int64_t M, int64_t K, const void* X, int64_t N, int64_t ldx,
+               int64_t sx, void* Y, int64_t ldy, int64_t sy, int64_t batch, int layout, int esx, int esy,
+               sp24::GemmArgs& g) {
     if (!values || !meta || !X || !Y) return SP24_ERR_NULL;
-    if (out_dtype != SP24_FP32 && out_dtype != SP24_BF16) return SP24_ERR_DTYPE;
-    if (M < 1 || N < 1) return SP24_ERR_SHAPE;
+    if (layout != SP24_FEATURE_MAJOR && layout != SP24_TOKEN_MAJOR) return SP24_ERR_ARG;
+    if (M < 1 || N < 1 || batch < 1) return SP24_ERR_SHAPE;
     int st = check_k(K);
     if (st != SP24_OK) return st;
-    if (ldx < N || ldy < N) return SP24_ERR_SHAPE;
+    const bool tm = layout == SP24_TOKEN_MAJOR;
+    // X rows hold N (feature-major) or K (token-major) elements, Y rows N or M
+    if (ldx < (tm ? K : N) || ldy < (tm ? M : N)) return SP24_ERR_SHAPE;
     if (M > kMaxRowsDirect || N > ((int64_t)1 << 31)) return SP24_ERR_SHAPE;
+    if (batch > 1) {
+        // batch entries of Y must not overlap (X may: it is only read)
+        const int64_t y_extent = tm ? (N - 1) * ldy + M : (M - 1) * ldy + N;
+        if (sx < 0 || sy < y_extent) return SP24_ERR_SHAPE;
+        if ((sx * esx) % 16 != 0 || (sy * esy) % 16 != 0) return SP24_ERR_ALIGN;
+    }
     if (!aligned16(values) || !aligned16(meta) || !aligned16(X) || !aligned16(Y)) return SP24_ERR_ALIGN;
+    g.values = values;
+    g.meta = meta;
+    g.M = M; g.K = K; g.N = N;
+    g.X = X; g.ldx = ldx; g.sx = batch > 1 ? sx : 0;
+    g.Y = Y; g.ldy = ldy; g.sy = batch > 1 ? sy : 0;
+    g.batch = batch;
+    g.tm = tm;
+    g.scale = nullptr;
+    g.out_fp32 = false;
+    return SP24_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sp24_gemm_bf16_ex(const void* values, const uint8_t* meta, int64_t M, int64_t K, const void* X, int64_t N,
+                      int64_t ldx, int64_t x_batch_stride, void* Y, int out_dtype, int64_t ldy, int64_t y_batch_stride,
+                      int64_t batch, int layout, void* stream) {
+    if (out_dtype != SP24_FP32 && out_dtype != SP24_BF16) {
+        if (!values || !meta || !X || !Y) return SP24_ERR_NULL;
+        return SP24_ERR_DTYPE;
+    }
+    sp24::GemmArgs g;
+    int st = check_gemm(values, meta, M, K, X, N, ldx, x_batch_stride, Y, ldy, y_batch_stride, batch, layout, 2,
+                        out_dtype == SP24_FP32 ? 4 : 2, g);
+    if (st != SP24_OK) return st;
+    g.out_fp32 = out_dtype == SP24_FP32;
     st = check_device();
     if (st != SP24_OK) return st;
-    return hip_status(sp24::launch_gemm_bf16(static_cast<const uint16_t*>(values), meta, M, K,
-                                             static_cast<const uint16_t*>(X), N, ldx, Y, out_dtype == SP24_FP32, ldy,
-                                             static_cast<hipStream_t>(stream)));
+    return hip_status(sp24::launch_gemm_bf16(g, static_cast<hipStream_t>(stream)));
+}
+
+int sp24_gemm_bf16(const void* values, const uint8_t* meta, int64_t M, int64_t K, const void* X, int64_t N,
+                   int64_t ldx, void* Y, int out_dtype, int64_t ldy, void* stream) {
+    return sp24_gemm_bf16_ex(values, meta, M, K, X, N, ldx, 0, Y, out_dtype, ldy, 0, 1, SP24_FEATURE_MAJOR, stream);
+}
+
+int sp24_gemm_i8_ex(const int8_t* values, const uint8_t* meta, int64_t M, int64_t K, const int8_t* X, int64_t N,
+                    int64_t ldx, int64_t x_batch_stride, const float* scale, void* Y, int64_t ldy,
+                    int64_t y_batch_stride, int64_t batch, int layout, void* stream) {
+    sp24::GemmArgs g;
+    int st = check_gemm(values, meta, M, K, X, N, ldx, x_batch_stride, Y, ldy, y_batch_stride, batch, layout, 1, 4, g);
+    if (st != SP24_OK) return st;
+    if (K > 262142) return SP24_ERR_SHAPE;  // keeps |acc| < 2^31 for any int8 inputs
+    if (scale && (reinterpret_cast<uintptr_t>(scale) & 3) != 0) return SP24_ERR_ALIGN;
+    g.scale = scale;
+    st = check_device();
+    if (st != SP24_OK) return st;
+    return hip_status(sp24::launch_gemm_i8(g, static_cast<hipStream_t>(stream)));
 }
 
 int sp24_gemm_i8(const int8_t* values, const uint8_t* meta, int64_t M, int64_t K, const int8_t* X, int64_t N,
                  int64_t ldx, const float* scale, void* Y, int64_t ldy, void* stream) {
-    if (!values || !meta || !X || !Y) return SP24_ERR_NULL;
-    if (M < 1 || N < 1) return SP24_ERR_SHAPE;
-    int st = check_k(K);
-    if (st != SP24_OK) return st;
-    if (K > 262142) return SP24_ERR_SHAPE;  // keeps |acc| < 2^31 for any int8 inputs
-    if (ldx < N || ldy < N) return SP24_ERR_SHAPE;
-    if (M > kMaxRowsDirect || N > ((int64_t)1 << 31)) return SP24_ERR_SHAPE;
-    if (!aligned16(values) || !aligned16(meta) || !aligned16(X) || !aligned16(Y)) return SP24_ERR_ALIGN;
-    if (scale && (reinterpret_cast<uintptr_t>(scale) & 3) != 0) return SP24_ERR_ALIGN;
-    st = check_device();
-    if (st != SP24_OK) return st;
-    return hip_status(
-        sp24::launch_gemm_i8(values, meta, M, K, X, N, ldx, scale, Y, ldy, static_cast<hipStream_t>(stream)));
+    return sp24_gemm_i8_ex(values, meta, M, K, X, N, ldx, 0, scale, Y, ldy, 0, 1, SP24_FEATURE_MAJOR, stream);
 }
 
 }  // extern "C"

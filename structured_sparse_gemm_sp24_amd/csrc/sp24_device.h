@@ -92,29 +92,18 @@ __device__ __forceinline__ void quad_transpose_bf16(const float (&f)[4], uint32_
     v[0] = __builtin_amdgcn_perm(dpp_xor1(x0), x0, sel);
     v[1] = __builtin_amdgcn_perm(dpp_xor1(x1), x1, sel);
 }
-// gfx950 lane-row swaps (a row is 16 lanes): swap32 trades lanes 32..63 of x for lanes 0..31 of y;
-// swap16 trades lanes 16..31 and 48..63 of x for lanes 0..15 and 32..47 of y.
-__device__ __forceinline__ void swap32(uint32_t& x, uint32_t& y) {
-    const auto r = __builtin_amdgcn_permlane32_swap(x, y, false, false);
-    x = r[0];
-    y = r[1];
-}
-__device__ __forceinline__ void swap16(uint32_t& x, uint32_t& y) {
-    const auto r = __builtin_amdgcn_permlane16_swap(x, y, false, false);
-    x = r[0];
-    y = r[1];
-}
-// Transpose of (lane row q = lane / 16, slot f) over four slots of W words: on entry lane row q holds
-// item (q, f) in slot f, on exit item (f, q). swap32 on slot pairs (0,2), (1,3) exchanges the 2 x 2
-// blocks across lane halves, swap16 on (0,1), (2,3) the elements inside them.
+// Quad transpose across four slots of W words: lane b of each quad takes slot f from lane f of its
+// quad, so (lane b, slot f) -> (lane f, slot b). Used to give the 4 lanes of a quad 4 pieces of one
+// output row: the memory pipeline merges a quad's stores into one request when they fall in one
+// 128-byte line, and otherwise issues one per lane.
 template <int W>
-__device__ __forceinline__ void row_transpose4(uint32_t (&v)[4][W]) {
+__device__ __forceinline__ void slot_transpose4(uint32_t (&v)[4][W], int b) {
 #pragma unroll
     for (int w = 0; w < W; w++) {
-        swap32(v[0][w], v[2][w]);
-        swap32(v[1][w], v[3][w]);
-        swap16(v[0][w], v[1][w]);
-        swap16(v[2][w], v[3][w]);
+        uint32_t u[4] = {v[0][w], v[1][w], v[2][w], v[3][w]};
+        quad_transpose(u, b);
+#pragma unroll
+        for (int t = 0; t < 4; t++) v[t][w] = u[t];
     }
 }
 

@@ -6,6 +6,25 @@
 
 namespace sp24 {
 
+// Operands of one sparse GEMM call, validated by the C ABI. Element strides are in elements of the
+// operand's type.
+//   feature-major (tm == false): X is K x N (X[k, n] at k * ldx + n), Y is M x N (Y[m, n] at m * ldy + n)
+//   token-major   (tm == true):  X is N x K (X[k, n] at n * ldx + k), Y is N x M (Y[m, n] at n * ldy + m)
+//   batch b (0 <= b < batch) adds b * sx to X and b * sy to Y; the weight is shared.
+struct GemmArgs {
+    const void* values;
+    const uint8_t* meta;
+    int64_t M, K, N;
+    const void* X;
+    int64_t ldx, sx;
+    void* Y;
+    int64_t ldy, sy;
+    int64_t batch;
+    bool tm;
+    const float* scale;  // int8 only: per-row dequant scale, or NULL for raw int32 output
+    bool out_fp32;       // bf16 only: fp32 output (else bf16)
+};
+
 hipError_t launch_col_norms(const uint16_t* X, int64_t K, int64_t N, int64_t ldx, float* norms, hipStream_t s);
 
 hipError_t launch_prune_compress(const void* W, int dtype, int64_t M, int64_t K, int64_t ldw, int score,
@@ -14,22 +33,16 @@ hipError_t launch_prune_compress(const void* W, int dtype, int64_t M, int64_t K,
 hipError_t launch_decompress(const void* values, const uint8_t* meta, int dtype, int64_t M, int64_t K,
                              void* W_out, int64_t ldw, hipStream_t s);
 
-hipError_t launch_gemm_bf16(const uint16_t* values, const uint8_t* meta, int64_t M, int64_t K, const uint16_t* X,
-                            int64_t N, int64_t ldx, void* Y, bool out_fp32, int64_t ldy, hipStream_t s);
+// bf16 GEMM: the kernel is chosen from the shape, layout and alignment (few tokens, LDS-tiled, direct).
+hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s);
+bool gemm_bf16_skinny_ok(const GemmArgs& g);
+hipError_t launch_gemm_bf16_skinny(const GemmArgs& g, hipStream_t s);
+bool gemm_bf16_tiled_ok(const GemmArgs& g);
+hipError_t launch_gemm_bf16_tiled(const GemmArgs& g, hipStream_t s);
 
-bool gemm_bf16_skinny_ok(int64_t K, int64_t N, int64_t ldx);
-hipError_t launch_gemm_bf16_skinny(const uint16_t* values, const uint8_t* meta, int64_t M, int64_t K, const uint16_t* X,
-                                   int64_t N, int64_t ldx, void* Y, bool out_fp32, int64_t ldy, hipStream_t s);
-
-bool gemm_bf16_tiled_ok(int64_t M, int64_t K, int64_t N, int64_t ldx, const void* X);
-hipError_t launch_gemm_bf16_tiled(const uint16_t* values, const uint8_t* meta, int64_t M, int64_t K, const uint16_t* X,
-                                  int64_t N, int64_t ldx, void* Y, bool out_fp32, int64_t ldy, hipStream_t s);
-
-bool gemm_i8_tiled_ok(int64_t M, int64_t K, int64_t N, int64_t ldx, const void* X);
-hipError_t launch_gemm_i8_tiled(const int8_t* values, const uint8_t* meta, int64_t M, int64_t K, const int8_t* X,
-                                int64_t N, int64_t ldx, const float* scale, void* Y, int64_t ldy, hipStream_t s);
-
-hipError_t launch_gemm_i8(const int8_t* values, const uint8_t* meta, int64_t M, int64_t K, const int8_t* X,
-                          int64_t N, int64_t ldx, const float* scale, void* Y, int64_t ldy, hipStream_t s);
+// int8 GEMM: LDS-tiled when it applies, else direct.
+hipError_t launch_gemm_i8(const GemmArgs& g, hipStream_t s);
+bool gemm_i8_tiled_ok(const GemmArgs& g);
+hipError_t launch_gemm_i8_tiled(const GemmArgs& g, hipStream_t s);
 
 }  // namespace sp24

@@ -128,6 +128,39 @@ def test_gemm_i8_validation(lib, args, expect):
     assert lib.sp24_gemm_i8(*args) == expect
 
 
+FM, TM = sp.SP24_FEATURE_MAJOR, sp.SP24_TOKEN_MAJOR
+
+
+@pytest.mark.parametrize("args,expect", [
+    # values, meta, M, K, X, N, ldx, x_batch_stride, Y, out_dtype, ldy, y_batch_stride, batch, layout, stream
+    ((A, B, 16, 16, C, 4, 4, 0, A, FP32, 4, 0, 1, 2, NULL), sp.SP24_ERR_ARG),      # unknown layout
+    ((A, B, 16, 16, C, 4, 4, 0, A, FP32, 4, 0, 0, FM, NULL), sp.SP24_ERR_SHAPE),   # batch 0
+    ((A, B, 16, 16, C, 4, 8, 0, A, FP32, 16, 0, 1, TM, NULL), sp.SP24_ERR_SHAPE),  # token-major ldx < K
+    ((A, B, 16, 16, C, 4, 16, 0, A, FP32, 8, 0, 1, TM, NULL), sp.SP24_ERR_SHAPE),  # token-major ldy < M
+    ((A, B, 16, 16, C, 4, 4, 64, A, FP32, 4, 32, 2, FM, NULL), sp.SP24_ERR_SHAPE),  # Y entries overlap
+    ((A, B, 16, 16, C, 4, 4, 64, A, FP32, 4, -64, 2, FM, NULL), sp.SP24_ERR_SHAPE),
+    ((A, B, 16, 16, C, 4, 4, -8, A, FP32, 4, 64, 2, FM, NULL), sp.SP24_ERR_SHAPE),  # negative X stride
+    ((A, B, 16, 16, C, 4, 4, 4, A, FP32, 4, 64, 2, FM, NULL), sp.SP24_ERR_ALIGN),   # X entry 8 bytes apart
+    ((A, B, 16, 16, C, 4, 4, 64, A, FP32, 4, 66, 2, FM, NULL), sp.SP24_ERR_ALIGN),  # Y entry misaligned
+    ((A, B, 16, 16, C, 4, 4, 0, A, I32, 4, 0, 1, FM, NULL), sp.SP24_ERR_DTYPE),
+    ((NULL, B, 16, 16, C, 4, 4, 0, A, FP32, 4, 0, 1, TM, NULL), sp.SP24_ERR_NULL),
+])
+def test_gemm_bf16_ex_validation(lib, args, expect):
+    assert lib.sp24_gemm_bf16_ex(*args) == expect
+
+
+@pytest.mark.parametrize("args,expect", [
+    # values, meta, M, K, X, N, ldx, x_batch_stride, scale, Y, ldy, y_batch_stride, batch, layout, stream
+    ((A, B, 16, 16, C, 4, 16, 0, NULL, A, 16, 0, 1, 7, NULL), sp.SP24_ERR_ARG),
+    ((A, B, 16, 16, C, 4, 8, 0, NULL, A, 16, 0, 1, TM, NULL), sp.SP24_ERR_SHAPE),
+    ((A, B, 16, 16, C, 4, 16, 0, NULL, A, 4, 0, 1, TM, NULL), sp.SP24_ERR_SHAPE),
+    ((A, B, 16, 16, C, 4, 4, 8, NULL, A, 4, 64, 2, FM, NULL), sp.SP24_ERR_ALIGN),
+    ((A, B, 16, 262144, C, 4, 262144, 0, NULL, A, 16, 0, 1, TM, NULL), sp.SP24_ERR_SHAPE),
+])
+def test_gemm_i8_ex_validation(lib, args, expect):
+    assert lib.sp24_gemm_i8_ex(*args) == expect
+
+
 def test_compressed_bytes(lib):
     vb, mb = ctypes.c_int64(), ctypes.c_int64()
     # rows padded to 16, columns to 128 / value size
@@ -152,6 +185,8 @@ def test_compressed_bytes_matches_oracle(lib):
 def test_valid_arguments_without_a_device_report_device_error(lib):
     # all host checks pass, then the device check fails: nothing is launched
     assert lib.sp24_gemm_bf16(A, B, 16, 16, C, 4, 4, A, FP32, 4, NULL) == sp.SP24_ERR_DEVICE
+    assert lib.sp24_gemm_bf16_ex(A, B, 16, 16, C, 4, 16, 64, A, FP32, 16, 64, 2, TM, NULL) == sp.SP24_ERR_DEVICE
+    assert lib.sp24_gemm_i8_ex(A, B, 16, 16, C, 4, 16, 64, NULL, A, 16, 64, 2, TM, NULL) == sp.SP24_ERR_DEVICE
     assert lib.sp24_col_norms(A, 16, 8, 8, B, NULL) == sp.SP24_ERR_DEVICE
 
 

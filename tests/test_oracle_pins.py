@@ -366,6 +366,35 @@ def test_gemm_i8_vs_numpy_integer_matmul_and_dequant():
     assert Y2 is None and np.array_equal(acc2, ref)
 
 
+@pytest.mark.parametrize("M,K,N", [(16, 16, 1), (37, 64, 29), (5, 128, 3)])
+def test_gemm_bf16_token_major_vs_numpy_matmul(M, K, N):
+    # a Linear layer's orientation: Y (N x M) = X (N x K) @ Wp^T, by numpy in that orientation
+    W, vals, meta = _rand_pruned(M * 7 + K + N, M, K)
+    X = synth.normal_bf16(N + 31, (N, K))
+    pos = top2_by_sort(np.abs(synth.bf16_bits_to_f32(W)))
+    Wp = synth.bf16_bits_to_f32(dense_from_positions(W, pos)).astype(np.float64)
+    ref = synth.bf16_bits_to_f32(X).astype(np.float64) @ Wp.T
+    Y = oracle.gemm_bf16(vals, meta, X, M, layout="token")
+    assert Y.shape == (N, M)
+    np.testing.assert_allclose(Y, ref, rtol=1e-12, atol=1e-12)
+    rows = np.array([M - 1, 0])
+    assert np.array_equal(oracle.gemm_bf16(vals, meta, X, M, rows=rows, layout="token"), Y[:, rows])
+
+
+def test_gemm_i8_token_major_vs_numpy_integer_matmul():
+    rng = np.random.default_rng(81)
+    M, K, N = 20, 64, 9
+    W = rng.integers(-127, 128, size=(M, K), dtype=np.int8)
+    X = rng.integers(-128, 128, size=(N, K), dtype=np.int8)
+    vals, meta = oracle.prune_compress(W, oracle.I8)
+    Wp = dense_from_positions(W, top2_by_sort(np.abs(W.astype(np.int32)))).astype(np.int64)
+    ref = X.astype(np.int64) @ Wp.T
+    scale = (rng.random(M) * 1e-3).astype(np.float32)
+    acc, Y = oracle.gemm_i8(vals, meta, X, M, scale, layout="token")
+    assert np.array_equal(acc, ref)
+    assert np.array_equal(Y, ref.astype(np.int32).astype(np.float32) * scale[None, :])
+
+
 def test_gemm_i8_overflow_is_reported():
     K = 270000 - 270000 % 16
     W = np.full((1, K), -128, np.int8)
