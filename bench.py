@@ -2,7 +2,9 @@
 
 One step = one pass of a workload's whole path over its synthetic batch. The default workload is the
 ViT-B/16 MLP fc1 layer: 2:4 magnitude prune + compress of W (3072 x 768 bf16), then the sparse GEMM
-Y = W_2:4 . X (X 768 x 6304 bf16, Y bf16). Other workloads (--workload, --n) cover the single 256 x 256
+of the layer's 6304 tokens (bf16 in and out). By default the activations are token-major, as a
+Linear layer holds them (X 6304 x 768, Y 6304 x 3072); --layout feature uses X 768 x 6304 and
+Y 3072 x 6304 instead (the same products). Other workloads (--workload, --n) cover the single 256 x 256
 Linear, the BERT-base int8 FFN pair, the LLM projections with Wanda scoring and the 28672 x 8192 FFN
 sweep. Inputs are resident in HBM before timing; steps rotate over enough copies of every buffer
 (> 2x the 256 MB Infinity Cache, when they fit) that each step reads its operands from HBM.
@@ -73,18 +75,23 @@ def gemm_sources(N):
 # Each builder returns: name, config, dtype, flops (dense-equivalent per step), copies, kernels (in
 # step order), dense_ref (optional: the dense GEMM of the same shape), cpu_sample(budget) -> (s, text).
 
-def _bf16_gemm_workload(name, W_host, X_host, score, Xcal_host, config, out=torch.bfloat16):
+def _bf16_gemm_workload(name, W_host, X_host, score, Xcal_host, config, layout, out=torch.bfloat16):
+    """X_host is K x N (feature-major); with layout 'token' the device copies hold X^T (N x K) and Y is
+    N x M."""
     M, K = W_host.shape
     N = X_host.shape[1]
+    tm = layout == "token"
+    config = dict(config, layout="token-major: X N x K, Y N x M" if tm else "feature-major: X K x N, Y M x N")
+    X_dev_host = np.ascontiguousarray(X_host.T) if tm else X_host
     vb, mb = sp.sp24_compressed_bytes(M, K, torch.bfloat16)
     ob = 2 if out == torch.bfloat16 else 4
     step_bytes = M * K * 2 + vb + mb + K * N * 2 + M * N * ob + (Xcal_host.size * 2 if Xcal_host is not None else 0)
     copies = []
     for _ in range(n_copies(step_bytes)):
-        c = dict(W=to_dev(W_host, "bf16"), X=to_dev(X_host, "bf16"),
+        c = dict(W=to_dev(W_host, "bf16"), X=to_dev(X_dev_host, "bf16"),
                  vals=torch.empty(vb // 2, dtype=torch.bfloat16, device="cuda"),
                  meta=torch.empty(mb, dtype=torch.uint8, device="cuda"),
-                 Y=torch.empty((M, N), dtype=out, device="cuda"))
+                 Y=torch.empty((N, M) if tm else (M, N), dtype=out, device="cuda"))
         if Xcal_host is not None:
             c["Xcal"] = to_dev(Xcal_host, "bf16")
             c["norms"] = torch.empty(K, dtype=torch.float32, device="cuda")
@@ -100,7 +107,9 @@ def _bf16_gemm_workload(name, W_host, X_host, score, Xcal_host, config, out=torc
         lambda c: sp.sp24_prune_compress(c["W"], score=score, norms=c["norms"] if wanda else None, values=c["vals"],
                                          meta=c["meta"]),
         M * K * 2 + (K * 4 if wanda else 0) + M * K * 9 // 8, sources=("prune.hip", "sp24_device.h")))
-    kernels.append(Kernel("gemm_bf16", lambda c: sp.sp24_gemm_bf16(c["vals"], c["meta"], M, c["X"], out=c["Y"]),
+    lay = "token" if tm else "feature"
+    kernels.append(Kernel("gemm_bf16",
+                          lambda c: sp.sp24_gemm_bf16_ex(c["vals"], c["meta"], M, c["X"], layout=lay, out=c["Y"]),
                           M * K * 9 // 8 + K * N * 2 + M * N * ob, float(M) * N * K, "bf16", gemm_sources(N)))
 
     def dense_ref():
@@ -108,6 +117,10 @@ def _bf16_gemm_workload(name, W_host, X_host, score, Xcal_host, config, out=torc
         for k in kernels:
             k.fn(c0)
         Wd = sp.sp24_decompress(c0["vals"], c0["meta"], M, K)
+        if tm:
+            Wt = Wd.t()  # X (N x K) @ W^T, the Linear layer's own product
+            Yd = torch.empty((N, M), dtype=torch.bfloat16, device="cuda")
+            return lambda c: torch.matmul(c["X"], Wt, out=Yd)
         Yd = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
         return lambda c: torch.matmul(Wd, c["X"], out=Yd)
 
@@ -121,11 +134,11 @@ def _bf16_gemm_workload(name, W_host, X_host, score, Xcal_host, config, out=torc
         t_fixed = time.perf_counter() - t0
         rows = min(M, 8)
         t0 = time.perf_counter()
-        oracle.gemm_bf16(v, m, X_host, M, rows=np.arange(rows))
+        oracle.gemm_bf16(v, m, X_dev_host, M, rows=np.arange(rows), layout=lay)
         t_small = time.perf_counter() - t0
         rows = int(min(M, max(8, rows * max(budget_s - t_fixed, 1.0) / max(t_small, 1e-6))))
         t0 = time.perf_counter()
-        oracle.gemm_bf16(v, m, X_host, M, rows=np.arange(rows))
+        oracle.gemm_bf16(v, m, X_dev_host, M, rows=np.arange(rows), layout=lay)
         t_rows = time.perf_counter() - t0
         what = ("column norms + " if norms is not None else "") + f"prune/compress of the full {M}x{K} W"
         return t_fixed + t_rows * M / rows, f"{what} + GEMM on {rows} of {M} rows (N = {N}), scaled to all rows"
@@ -141,7 +154,7 @@ def workload_vit(args):
     cfg = dict(workload="vit_b16_fc1", M=M, K=K, N=N, weight="bf16 N(0,0.02^2) seed 11",
                activations="bf16 N(0,1) seed 12, N = 32 images x 197 tokens", score="magnitude", out="bf16",
                step="prune_compress + gemm_bf16")
-    return _bf16_gemm_workload("vit_b16_fc1", d["W_bf16"], d["X_bf16"], sp.SP24_SCORE_MAGNITUDE, None, cfg)
+    return _bf16_gemm_workload("vit_b16_fc1", d["W_bf16"], d["X_bf16"], sp.SP24_SCORE_MAGNITUDE, None, cfg, args.layout)
 
 
 def workload_llm(M):
@@ -154,7 +167,8 @@ def workload_llm(M):
                    calibration="4096 x 2048 bf16, lognormal(0,1) channel scale x Student-t(3), seed 33",
                    activations="same law, seed 34, first N columns", score="wanda", out="bf16",
                    step="col_norms + prune_compress (Wanda) + gemm_bf16")
-        return _bf16_gemm_workload(f"llm_proj_{M}x4096_n{N}", d["W_bf16"], X, sp.SP24_SCORE_WANDA, d["Xcal_bf16"], cfg)
+        return _bf16_gemm_workload(f"llm_proj_{M}x4096_n{N}", d["W_bf16"], X, sp.SP24_SCORE_WANDA, d["Xcal_bf16"], cfg,
+                                   args.layout)
     return build
 
 
@@ -164,7 +178,8 @@ def workload_ffn(args):
     cfg = dict(workload="ffn_28672x8192", M=28672, K=8192, N=N, weight="bf16 N(0,0.02^2) seed 41",
                activations="bf16 N(0,1) seed 42, first N columns of an 8192-wide draw", score="magnitude",
                out="bf16", step="prune_compress + gemm_bf16")
-    return _bf16_gemm_workload(f"ffn_28672x8192_n{N}", d["W_bf16"], d["X_bf16"], sp.SP24_SCORE_MAGNITUDE, None, cfg)
+    return _bf16_gemm_workload(f"ffn_28672x8192_n{N}", d["W_bf16"], d["X_bf16"], sp.SP24_SCORE_MAGNITUDE, None, cfg,
+                               args.layout)
 
 
 def workload_single(args):
@@ -173,14 +188,17 @@ def workload_single(args):
     M, K = W.shape
     N = X.shape[1]
     vb, mb = sp.sp24_compressed_bytes(M, K, torch.bfloat16)
-    copies = [dict(W=to_dev(W), X=to_dev(X, "bf16"), vals=torch.empty(vb // 2, dtype=torch.bfloat16, device="cuda"),
+    tm = args.layout == "token"
+    Xdev = np.ascontiguousarray(X.T) if tm else X
+    copies = [dict(W=to_dev(W), X=to_dev(Xdev, "bf16"), vals=torch.empty(vb // 2, dtype=torch.bfloat16, device="cuda"),
                    meta=torch.empty(mb, dtype=torch.uint8, device="cuda"),
-                   Y=torch.empty((M, N), dtype=torch.float32, device="cuda")) for _ in range(8)]
+                   Y=torch.empty((N, M) if tm else (M, N), dtype=torch.float32, device="cuda")) for _ in range(8)]
     kernels = [
         Kernel("prune_compress", lambda c: sp.sp24_prune_compress(c["W"], val_dtype=torch.bfloat16, values=c["vals"],
                                                                   meta=c["meta"]),
                M * K * 4 + M * K * 9 // 8, sources=("prune.hip", "sp24_device.h")),
-        Kernel("gemm_bf16", lambda c: sp.sp24_gemm_bf16(c["vals"], c["meta"], M, c["X"], out=c["Y"]),
+        Kernel("gemm_bf16", lambda c: sp.sp24_gemm_bf16_ex(c["vals"], c["meta"], M, c["X"], layout=args.layout,
+                                                           out=c["Y"]),
                M * K * 9 // 8 + K * N * 2 + M * N * 4, float(M) * N * K, "bf16", gemm_sources(N))]
 
     def cpu_sample(budget_s):
@@ -192,7 +210,8 @@ def workload_single(args):
 
     cfg = dict(workload="single_linear_256", M=M, K=K, N=N, weight="fp32 N(0,1) seed 1, kept values rounded to bf16",
                activations="fp32 N(0,1) seed 2 rounded to bf16", score="magnitude", out="fp32",
-               step="prune_compress + gemm_bf16")
+               step="prune_compress + gemm_bf16",
+               layout="token-major: X N x K, Y N x M" if tm else "feature-major: X K x N, Y M x N")
     return dict(name="single_linear_256", dtype="bf16", unit="TFLOP/s", config=cfg, flops=2.0 * M * N * K,
                 copies=copies, kernels=kernels, dense_ref=None, cpu_sample=cpu_sample)
 
@@ -211,17 +230,19 @@ def workload_bert_int8(args):
         Wp = sp.sp24_decompress(v, m, M, K).cpu().numpy()
         q, s_w = synth.quantize_rows(Wp)
         xq, s_x = synth.quantize_tensor(d[xk])
-        layers.append(dict(M=M, K=K, N=xq.shape[1], q=q, xq=xq, scale=synth.dequant_scales(s_w, s_x)))
+        xdev = np.ascontiguousarray(xq.T) if args.layout == "token" else xq
+        layers.append(dict(M=M, K=K, N=xq.shape[1], q=q, xq=xq, xdev=xdev, scale=synth.dequant_scales(s_w, s_x)))
     step_bytes = sum(L["M"] * L["K"] * 2 + L["K"] * L["N"] + 4 * L["M"] * L["N"] for L in layers)
     copies = []
     for _ in range(n_copies(step_bytes)):
         c = {}
         for i, L in enumerate(layers):
             vb, mb = sp.sp24_compressed_bytes(L["M"], L["K"], torch.int8)
-            c[i] = dict(W=to_dev(L["q"]), X=to_dev(L["xq"]), scale=to_dev(L["scale"]),
+            ysh = (L["N"], L["M"]) if args.layout == "token" else (L["M"], L["N"])
+            c[i] = dict(W=to_dev(L["q"]), X=to_dev(L["xdev"]), scale=to_dev(L["scale"]),
                         vals=torch.empty(vb, dtype=torch.int8, device="cuda"),
                         meta=torch.empty(mb, dtype=torch.uint8, device="cuda"),
-                        Y=torch.empty((L["M"], L["N"]), dtype=torch.float32, device="cuda"))
+                        Y=torch.empty(ysh, dtype=torch.float32, device="cuda"))
         copies.append(c)
     kernels = []
     for i, L in enumerate(layers):
@@ -230,10 +251,11 @@ def workload_bert_int8(args):
                               lambda c, i=i: sp.sp24_prune_compress(c[i]["W"], values=c[i]["vals"], meta=c[i]["meta"]),
                               M * K + M * K * 5 // 8, sources=("prune.hip", "sp24_device.h")))
         kernels.append(Kernel(f"gemm_i8_w{i + 1}",
-                              lambda c, i=i, M=M: sp.sp24_gemm_i8(c[i]["vals"], c[i]["meta"], M, c[i]["X"],
-                                                                  scale=c[i]["scale"], out=c[i]["Y"]),
+                              lambda c, i=i, M=M: sp.sp24_gemm_i8_ex(c[i]["vals"], c[i]["meta"], M, c[i]["X"],
+                                                                     scale=c[i]["scale"], layout=args.layout,
+                                                                     out=c[i]["Y"]),
                               M * K * 5 // 8 + K * N + 4 * M * N + 4 * M, float(M) * N * K, "i8",
-                              ("gemm_i8.hip", "sp24_device.h")))
+                              ("gemm_i8_tiled.hip", "sp24_device.h")))
 
     def cpu_sample(budget_s):
         import oracle
@@ -256,7 +278,8 @@ def workload_bert_int8(args):
     cfg = dict(workload="bert_ffn_int8", W1="3072x768", W2="768x3072", N=8192,
                weights="fp32 N(0,0.02^2) seeds 21/22, 2:4 magnitude, per-row int8 at 99.99 % coverage",
                activations="fp32 N(0,1) seeds 23/24, per-tensor int8 at 99.99 % coverage (64 x 128 tokens)",
-               out="fp32 (int32 accumulate, per-channel dequant)", step="2 x (prune_compress int8 + gemm_i8)")
+               out="fp32 (int32 accumulate, per-channel dequant)", step="2 x (prune_compress int8 + gemm_i8)",
+               layout="token-major: X N x K, Y N x M" if args.layout == "token" else "feature-major: X K x N, Y M x N")
     flops = sum(2.0 * L["M"] * L["N"] * L["K"] for L in layers)
     return dict(name="bert_ffn_int8", dtype="i8", unit="TOP/s", config=cfg, flops=flops, copies=copies,
                 kernels=kernels, dense_ref=None, cpu_sample=cpu_sample)
@@ -385,6 +408,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="vit_b16_fc1", choices=sorted(WORKLOADS))
     ap.add_argument("--n", type=int, default=0, help="tokens N for the llm_proj_* and ffn_* workloads")
+    ap.add_argument("--layout", default="token", choices=("token", "feature"),
+                    help="activations token-major (X N x K, Y N x M, a Linear layer's layout) or feature-major")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense-ref", action="store_true", help="skip timing the dense bf16 GEMM of the same shape")
