@@ -255,7 +255,7 @@ def workload_bert_int8(args):
                                                                      scale=c[i]["scale"], layout=args.layout,
                                                                      out=c[i]["Y"]),
                               M * K * 5 // 8 + K * N + 4 * M * N + 4 * M, float(M) * N * K, "i8",
-                              ("gemm_i8_tiled.hip", "sp24_device.h")))
+                              ("gemm_i8_tiled_impl.h", "gemm_i8_tiled.hip", "sp24_device.h")))
 
     def cpu_sample(budget_s):
         import oracle

@@ -96,6 +96,9 @@ typedef enum { SP24_SCORE_MAGNITUDE = 0, SP24_SCORE_WANDA = 1 } sp24_score;
  *                      Y is N x M; row pitches ldx >= K and ldy >= M. */
 typedef enum { SP24_FEATURE_MAJOR = 0, SP24_TOKEN_MAJOR = 1 } sp24_layout;
 
+/* Activation of the fused int8 epilogue: none, or GELU(y) = y/2 (1 + erf(y / sqrt 2)). */
+typedef enum { SP24_ACT_NONE = 0, SP24_ACT_GELU = 1 } sp24_activation;
+
 /* Per-input-channel activation norms for Wanda scoring (zyxy.net Wanda lecture, section 2.1).
  *   norms[j] = sqrt( sum_{n<N} X[j*ldx + n]^2 ),  j < K.
  * X: bf16, K x N, any row pitch ldx >= N (16-byte aligned base). norms: fp32[K].
@@ -165,6 +168,22 @@ int sp24_gemm_bf16_ex(const void* values, const uint8_t* meta, int64_t M, int64_
 int sp24_gemm_i8_ex(const int8_t* values, const uint8_t* meta, int64_t M, int64_t K, const int8_t* X, int64_t N,
                     int64_t ldx, int64_t x_batch_stride, const float* scale, void* Y, int64_t ldy,
                     int64_t y_batch_stride, int64_t batch, int layout, void* stream);
+
+/* The int8 GEMM with its FFN epilogue fused (NVIDIA blog, quantization section: the sparse int8 BERT
+ * of the Sparse-QAT case keeps its FFN in int8 between layers; oeforum post: int8 and 2:4 combine).
+ * For every output element, in fp32 with one rounding per step:
+ *   y = fl32( fl32(acc[m, n]) * scale[m] );   y = fl32(y + bias[m]) when bias != NULL;
+ *   y = GELU(y) when activation == SP24_ACT_GELU (fp32, computed with the device erff: not bit-exact
+ *       across implementations; |error| <= 8 * 2^-24 * |y| against the exact GELU of the fp32 input);
+ *   stored as out_dtype: SP24_FP32; SP24_BF16 (round to nearest even); or SP24_I8, the requantized code
+ *       clamp( rne( fl32(y * inv) ), -127, 127 ) with inv = fl32(1 / out_scale), out_scale > 0 the next
+ *       layer's input scale (a multiply by the rounded reciprocal, not a division).
+ * scale (fp32[M]) is required; bias is fp32[M] or NULL. Operands, layout, batch and strides as
+ * sp24_gemm_i8_ex (Y's element size follows out_dtype). */
+int sp24_gemm_i8_fused(const int8_t* values, const uint8_t* meta, int64_t M, int64_t K, const int8_t* X, int64_t N,
+                       int64_t ldx, int64_t x_batch_stride, const float* scale, const float* bias, int activation,
+                       void* Y, int out_dtype, float out_scale, int64_t ldy, int64_t y_batch_stride, int64_t batch,
+                       int layout, void* stream);
 
 /* Static description of a status code. */
 const char* sp24_status_string(int status);

@@ -215,6 +215,41 @@ def gemm_i8(values: np.ndarray, meta: np.ndarray, X: np.ndarray, M: int, scale: 
     return acc, Y
 
 
+def gelu64(y) -> np.ndarray:
+    """GELU(y) = y/2 (1 + erf(y / sqrt 2)) in float64 (the exact erf form used by BERT's FFN)."""
+    from scipy.special import erf
+    y = np.asarray(y, np.float64)
+    return 0.5 * y * (1.0 + erf(y / np.sqrt(2.0)))
+
+
+def requant_i8(y, out_scale: float) -> np.ndarray:
+    """int8 code of y: clamp(rne(y * inv), -127, 127) with inv = fl32(1 / out_scale); fp32 inputs
+    multiply in fp32 (one rounding), float64 inputs in float64."""
+    y = np.asarray(y)
+    inv = np.float32(1) / np.float32(out_scale)
+    d = y * (inv if y.dtype == np.float32 else np.float64(inv))
+    return np.clip(np.rint(d), -127, 127).astype(np.int8)
+
+
+def gemm_i8_fused(values: np.ndarray, meta: np.ndarray, X: np.ndarray, M: int, scale: np.ndarray,
+                  bias: np.ndarray | None = None, gelu: bool = False, out_scale: float | None = None, rows=None,
+                  layout: str = "feature") -> dict:
+    """The int8 GEMM's fused FFN epilogue (NVIDIA blog, quantization section: the sparse int8 BERT keeps
+    its FFN in int8; oeforum post: int8 and 2:4 combine), step by step in the pages' order:
+      y32 = fl32(fl32(acc) * scale[m])      (gemm_i8)
+      y32 = fl32(y32 + bias[m])             (fp32 add, when bias is given)
+      y   = GELU(y32)                       (float64 reference, when gelu)
+      q   = clamp(rne(y * fl32(1/out_scale)))  (fp32 multiply without GELU; float64 with it)
+    Returns dict(y32=..., y=..., q=...) laid out as gemm_i8's results for the layout."""
+    _, y32 = gemm_i8(values, meta, X, M, scale, rows=rows, layout=layout)
+    if bias is not None:
+        b = np.asarray(bias, np.float32)[_rows_arg(rows, M)]
+        y32 = (y32 + (b[None, :] if layout == "token" else b[:, None])).astype(np.float32)
+    y = gelu64(y32) if gelu else y32
+    q = requant_i8(y, out_scale) if out_scale is not None else None
+    return dict(y32=y32, y=y, q=q)
+
+
 def fp32_to_bf16(x: float) -> int:
     return int(_load().oracle_fp32_to_bf16(float(x)))
 

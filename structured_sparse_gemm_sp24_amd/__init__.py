@@ -20,10 +20,11 @@ SP24_ERR_DTYPE, SP24_ERR_ARG, SP24_ERR_DEVICE, SP24_ERR_HIP = -4, -5, -6, -7
 SP24_BF16, SP24_FP16, SP24_FP32, SP24_I8, SP24_I32 = 0, 1, 2, 3, 4
 SP24_SCORE_MAGNITUDE, SP24_SCORE_WANDA = 0, 1
 SP24_FEATURE_MAJOR, SP24_TOKEN_MAJOR = 0, 1
+SP24_ACT_NONE, SP24_ACT_GELU = 0, 1
 
 # every symbol include/sp24.h declares
 EXPORTS = ("sp24_col_norms", "sp24_compressed_bytes", "sp24_prune_compress", "sp24_decompress", "sp24_gemm_bf16",
-           "sp24_gemm_i8", "sp24_gemm_bf16_ex", "sp24_gemm_i8_ex", "sp24_status_string")
+           "sp24_gemm_i8", "sp24_gemm_bf16_ex", "sp24_gemm_i8_ex", "sp24_gemm_i8_fused", "sp24_status_string")
 
 _TORCH_TO_SP24 = {torch.bfloat16: SP24_BF16, torch.float16: SP24_FP16, torch.float32: SP24_FP32,
                   torch.int8: SP24_I8, torch.int32: SP24_I32}
@@ -57,6 +58,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sp24_gemm_i8.argtypes = [P, P, I64, I64, P, I64, I64, P, P, I64, P]
     lib.sp24_gemm_bf16_ex.argtypes = [P, P, I64, I64, P, I64, I64, I64, P, I, I64, I64, I64, I, P]
     lib.sp24_gemm_i8_ex.argtypes = [P, P, I64, I64, P, I64, I64, I64, P, P, I64, I64, I64, I, P]
+    lib.sp24_gemm_i8_fused.argtypes = [P, P, I64, I64, P, I64, I64, I64, P, P, I, P, I, ctypes.c_float, I64, I64, I64,
+                                       I, P]
     for fn in EXPORTS[:-1]:
         getattr(lib, fn).restype = I
     lib.sp24_status_string.argtypes = [I]
@@ -246,4 +249,26 @@ def sp24_gemm_i8_ex(values: torch.Tensor, meta: torch.Tensor, M: int, X: torch.T
     st = load_library().sp24_gemm_i8_ex(_ptr(values), _ptr(meta), M, K, _ptr(X), N, ldx, sx, _ptr(scale), _ptr(out),
                                         ldy, sy, batch, lay, _stream(X))
     _check("sp24_gemm_i8_ex", st)
+    return out
+
+
+_ACT = {"none": SP24_ACT_NONE, "gelu": SP24_ACT_GELU, SP24_ACT_NONE: SP24_ACT_NONE, SP24_ACT_GELU: SP24_ACT_GELU}
+
+
+def sp24_gemm_i8_fused(values: torch.Tensor, meta: torch.Tensor, M: int, X: torch.Tensor, scale: torch.Tensor,
+                       bias: torch.Tensor | None = None, activation="none", out_dtype: torch.dtype = torch.float32,
+                       out_scale: float = 1.0, layout="feature", out: torch.Tensor | None = None) -> torch.Tensor:
+    """int8 sparse GEMM with the FFN epilogue fused: y = fl32(fl32(acc) * scale[m]) (+ bias[m]) (GELU),
+    stored as fp32, bf16, or int8 codes clamp(rne(y / out_scale), -127, 127). Layout and batching as
+    sp24_gemm_i8_ex."""
+    _dev_check(values, meta, X, scale, bias, out)
+    if scale is None:
+        raise ValueError("the fused epilogue needs the dequant scale")
+    lay = _layout(layout)
+    K, N, ldx, sx, batch, out, ldy, sy = _gemm_operands(X, M, lay, out, out_dtype)
+    _check_compressed(values, meta, M, K)
+    st = load_library().sp24_gemm_i8_fused(_ptr(values), _ptr(meta), M, K, _ptr(X), N, ldx, sx, _ptr(scale),
+                                           _ptr(bias), _ACT[activation], _ptr(out), _TORCH_TO_SP24[out.dtype],
+                                           float(out_scale), ldy, sy, batch, lay, _stream(X))
+    _check("sp24_gemm_i8_fused", st)
     return out

@@ -8,7 +8,8 @@
 //   index: 32 bits per lane (8 groups) -- 4 contiguous bytes of a row of `meta`;
 //   B (dense, 128 x 16): lane holds column r, element e at row k = 16q + (e & 15) + 64 (e >> 4);
 //   C/D (16 x 16 int32): lane holds column r, rows 4q .. 4q+3.
-// Epilogue: y = fl32( fl32(acc) * scale[m] ), a single rounding multiply.
+// Epilogue: y = fl32( fl32(acc) * scale[m] ), a single rounding multiply; optionally + bias[m] (one rounding
+// add) and GELU, stored as fp32, bf16 (round to nearest even) or int8 codes clamp(rne(y * inv_scale)).
 //
 // The compressed weight is stored in that lane order (16-row x 128-column tiles, see include/sp24.h).
 // Direct kernel: each wave owns a 16 x (16*NF) tile, reads A (1 KB) and the index (256 B) of each
@@ -29,6 +30,9 @@ struct DirectArgsI8 {
     const int8_t* X;
     int64_t sxk, sxn, sxb;
     const float* scale;
+    const float* bias;
+    int gelu, out_kind;
+    float inv_scale;
     void* Y;
     int64_t sym, syn, syb;
 };
@@ -76,7 +80,8 @@ __global__ __launch_bounds__(256) void gemm_i8_direct(DirectArgsI8 d) {
             acc[f] = __builtin_amdgcn_smfmac_i32_16x16x128_i8(av, bv, acc[f], (int)idx, 0, 0);
         }
     }
-    char* const Y = static_cast<char*>(d.Y) + (int64_t)blockIdx.z * d.syb * 4;
+    const int es = d.out_kind == OUT_BF16 ? 2 : (d.out_kind == OUT_I8 ? 1 : 4);
+    char* const Y = static_cast<char*>(d.Y) + (int64_t)blockIdx.z * d.syb * es;
 #pragma unroll
     for (int f = 0; f < NF; f++) {
         const int64_t n = n0 + 16 * f + r;
@@ -86,10 +91,17 @@ __global__ __launch_bounds__(256) void gemm_i8_direct(DirectArgsI8 d) {
             const int64_t m = m0 + 4 * q + i;
             if (m >= d.M) continue;
             const int64_t o = m * d.sym + n * d.syn;
-            if (d.scale)
-                reinterpret_cast<float*>(Y)[o] = __fmul_rn((float)acc[f][i], d.scale[m]);
-            else
+            if (d.out_kind == OUT_I32) {
                 reinterpret_cast<int32_t*>(Y)[o] = acc[f][i];
+                continue;
+            }
+            const float y = i8_value(acc[f][i], d.scale[m], d.bias ? d.bias[m] : 0.f, d.bias != nullptr, d.gelu != 0);
+            if (d.out_kind == OUT_F32)
+                reinterpret_cast<float*>(Y)[o] = y;
+            else if (d.out_kind == OUT_BF16)
+                reinterpret_cast<uint16_t*>(Y)[o] = f32_to_bf16_rne(y);
+            else
+                reinterpret_cast<uint8_t*>(Y)[o] = (uint8_t)quant_i8(y, d.inv_scale);
         }
     }
 }
@@ -105,6 +117,10 @@ hipError_t launch_gemm_i8(const GemmArgs& g, hipStream_t s) {
     d.sxn = g.tm ? g.ldx : 1;
     d.sxb = g.sx;
     d.scale = g.scale;
+    d.bias = g.bias;
+    d.gelu = g.gelu;
+    d.out_kind = g.out_kind;
+    d.inv_scale = g.inv_scale;
     d.Y = g.Y;
     d.sym = g.tm ? 1 : g.ldy;
     d.syn = g.tm ? g.ldy : 1;
@@ -115,7 +131,7 @@ hipError_t launch_gemm_i8(const GemmArgs& g, hipStream_t s) {
         const unsigned gz = (unsigned)(g.batch - b0 < 65535 ? g.batch - b0 : 65535);
         DirectArgsI8 e = d;
         e.X = d.X + b0 * d.sxb;
-        e.Y = static_cast<char*>(d.Y) + b0 * d.syb * 4;
+        e.Y = static_cast<char*>(d.Y) + b0 * d.syb * (g.out_kind == OUT_BF16 ? 2 : (g.out_kind == OUT_I8 ? 1 : 4));
         if (g.N <= 16)
             hipLaunchKernelGGL(gemm_i8_direct<1>, dim3((unsigned)((g.N + 15) / 16), gy, gz), dim3(256), 0, s, e);
         else

@@ -1,512 +1,14 @@
-// Tiled sparse x dense GEMM for large N, int8 in, exact int32 accumulation, per-output-channel fp32
-// dequant epilogue (oeforum post on sparse acceleration: int8 and 2:4 combine; Orin NN design,
-// Chapter 7, section 3.1 Step 4; NVIDIA blog on Ampere structured sparsity, Figure 1).
-//
-// Same organisation as the bf16 tiled kernel, with v_smfmac_i32_16x16x128_i8:
-// workgroup tile 256 (M) x 256 (N), 4 waves in a 2 x 2 grid, each wave 128 x 128 = 8 x 8 fragments
-// (256 int32 accumulators per lane, one wave per SIMD). K advances 128 dense columns per stage; three
-// stages are in flight through LDS (3 x 52 KB):
-//   A (compressed values): one 1 KB tile per 16-row block, already in the operand's lane order
-//     (lane l holds 16 kept int8 of row l % 16, dense columns [32 (l / 16), +32));
-//   metadata: one 256 B tile per block (lane l's 32-bit index at 4 l);
-//   B tile (X, 128 rows x 256 int8 = 256 B per row): row-major with the 16-byte units of row k
-//     stored at unit ^ f(k), f(k) = (k & 7) + 8 ((k >> 4) & 1). One ds_read_b64_tr_b8 takes 8 rows x
-//     16 bytes per 16-lane group, rows 16q + {0..7} (+8, +64) for q = 0..3; f puts those 32 rows in 16
-//     distinct 16-byte bank slots (two rows each, the minimum for 512 bytes), and stays the same for
-//     the +8 / +64 row offsets, so those are immediates. Every 4 consecutive lanes of a global load
-//     still read one aligned 64-byte run.
-// The B operand (lane = column, 32 k values: k = 16q + (e & 15) + 64 (e >> 4)) comes from four
-// ds_read_b64_tr_b8: in each 16-lane group, lane s points at row k0 + s/2, columns c0 + 8 (s % 2);
-// the instruction hands lane i the 8 consecutive k of column c0 + i.
-//
-// Loads are buffer loads with LDS destination whose whole byte offset is in the range-checked VGPR
-// operand: reads past this workgroup's row blocks, past K and past the end of X return zeros, and the
-// loads the pipeline issues past the workgroup's last tile are pushed out of range on purpose.
-// Persistent like the bf16 kernel: one workgroup per CU walks its tiles (neighbouring tiles on the same
-// XCD at the same time, groups of 8 tile-rows) with the LDS pipeline continued across tiles; the
-// epilogue dequantizes in registers, transposes 4 x 4 blocks inside lane quads by DPP and stores 16
-// bytes per lane, so its stores drain while the next tile computes.
-//
-// Token-major X (N x K) and Y (N x M): the B tile is 256 token rows x 128 k (128 B per row), a lane's
-// operand two 16-byte runs of its token's row (k = 16q .. +15 and 64 + 16q .. +15), read with two
-// ds_read_b128 from units stored at unit ^ f(n), f(n) = ((n >> 1) & 7) ^ 4 (n & 1) (conflict-free, as
-// in the bf16 kernel); each accumulator's 4 consecutive rows of M are one 16-byte store of token row
-// n. K must be a multiple of 128 there. A batch of products sharing the weight adds the batch to the
-// tile index.
-#include "sp24_device.h"
-#include "sp24_launch.h"
+// Tiled int8 sparse GEMM: the shape check and the dispatch over output kinds. The kernel is in
+// gemm_i8_tiled_impl.h; the int32 and fp32 outputs are instantiated here, bf16 and int8 in
+// gemm_i8_tiled_bf16.hip and gemm_i8_tiled_i8.hip (separate files compile in parallel).
+#include "gemm_i8_tiled_impl.h"
 
 namespace sp24 {
 namespace tiled_i8 {
-
-constexpr int BM = 256, BN = 256, BK = 128;
-constexpr int WM = 128, WN = 128;
-constexpr int FM = WM / 16, FN = WN / 16;
-constexpr int A_BYTES = BM * 64;          // 64 kept int8 per row per stage
-constexpr int META_BYTES = BM * 16;       // 64 kept values x 2 bits = 16 bytes per row
-constexpr int B_ROW = BN;                 // 256 bytes
-constexpr int B_BYTES = BK * B_ROW;
-constexpr int STAGE_BYTES = A_BYTES + META_BYTES + B_BYTES;
-constexpr int LOADS_PER_STAGE = 4 + 1 + 8;  // per wave: A, metadata, B
-constexpr int GROUP_M = 8;
-constexpr uint32_t RSRC_FLAGS = 0x00020000u;
-static_assert(3 * STAGE_BYTES <= 160 * 1024, "three stages fit in LDS");
-
-// Raw buffer descriptor over `bytes` bytes rounded up to whole dwords: the range check returns a
-// dword only when all of it is below the record count, and the rounding keeps the last partial dword
-// of the real data (that dword lies in the same page as the data it ends).
-__device__ __forceinline__ i32x4 make_rsrc(const void* base, int64_t bytes) {
-    const int64_t n = bytes <= 0 ? 0 : (bytes > 0xFFFFFFFCll ? 0xFFFFFFFCll : (bytes + 3) & ~(int64_t)3);
-    const uint64_t b = reinterpret_cast<uint64_t>(base);
-    i32x4 r;
-    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)b);
-    r[1] = __builtin_amdgcn_readfirstlane((int)((b >> 32) & 0xFFFFu));
-    r[2] = __builtin_amdgcn_readfirstlane((int)(uint32_t)n);
-    r[3] = (int)RSRC_FLAGS;
-    return r;
-}
-
-// Buffer load with LDS destination (lane i's 16 bytes land at lds + 16 i), from inline asm so the
-// compiler adds no waits of its own; ordered by explicit s_waitcnt vmcnt + s_barrier. No VGPR is
-// written. `lds` is wave-uniform; `voff` is the lane's whole byte offset (range-checked).
-__device__ __forceinline__ void dma16(uint32_t lds, uint32_t voff, i32x4 rsrc) {
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                 :: "s"(lds), "v"(voff), "s"(rsrc) : "memory");
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
-struct Args {
-    const int8_t* vals;
-    const uint8_t* meta;
-    const int8_t* X;
-    const float* scale;
-    void* Y;
-    int64_t M, K, N, ldx, ldy;
-    int64_t sxb, syb;  // batch strides (elements)
-    int tilesM, tilesN, batch;
-    int y_vec;  // Y base and row pitch allow 16-byte stores, 4 rows < 2^31 bytes
-};
-
-// Corner and compressed-tile descriptors of one tile; `valid` is false past the workgroup's last tile.
-struct TileDesc {
-    int64_t m0, n0;
-    const int8_t* x;  // X and Y of the tile's batch entry
-    char* y;
-    i32x4 rA, rM;
-    bool valid;
-};
-
-// Logical tile of workgroup p at its k-th turn, or -1. Turn k covers tiles [kG, kG + rem), rem =
-// min(G, T - kG), split evenly over the 8 XCDs (workgroup p runs on XCD p % 8): XCD x takes a
-// contiguous run of rem / 8 or rem / 8 + 1 of them, so a partial last turn still spreads its tiles,
-// and their output writes, over every XCD, and neighbouring tiles share an L2.
-__device__ __forceinline__ int tile_of(const Args& a, int p, int k) {
-    const int G = gridDim.x, T = a.tilesM * a.tilesN * a.batch;
-    const int64_t base = (int64_t)k * G;
-    if (base >= T) return -1;
-    const int rem = (T - base) < G ? (int)(T - base) : G;
-    const int x = p & 7, i = p >> 3, q8 = rem >> 3, r8 = rem & 7;
-    if (i >= q8 + (x < r8 ? 1 : 0)) return -1;
-    return (int)base + x * q8 + (x < r8 ? x : r8) + i;
-}
-
-// Swizzle of the 16-byte units of B row k (see the header).
-__device__ __forceinline__ int bswz(int k) { return (k & 7) | (((k >> 4) & 1) << 3); }
-
-// 16-byte unit swizzle of token row n of a token-major B tile.
-__device__ __forceinline__ int tm_swz(int n) { return ((n >> 1) & 7) ^ ((n & 1) << 2); }
-
-// Per-lane parts of the load offsets.
-struct LoadOffsets {
-    uint32_t a;      // A tile: 16 * lane
-    uint32_t m;      // metadata: tile (lane / 16) of the wave's 4 blocks, 16 * (lane % 16) inside it
-    uint32_t b[8];   // B rows 4h + lane / 16 of the wave's 32 rows: row part + swizzled chunk;
-                     // token-major: rows 8h + lane / 8 of the wave's 64 (row part relative to the wave's first)
-};
-
-template <bool TM>
-__device__ __forceinline__ LoadOffsets load_offsets(const Args& a, int lane, int wave) {
-    LoadOffsets o;
-    const int tiles = (int)((a.K + BK - 1) / BK);
-    o.a = 16 * lane;
-    o.m = (uint32_t)((lane >> 4) * tiles * 256 + 16 * (lane & 15));
-    if constexpr (TM) {
-        // lane i of a load lands in token row 8h + i / 8 of the wave's rows, 16-byte slot i % 8, and
-        // reads the unit that belongs there
-#pragma unroll
-        for (int h = 0; h < 8; h++) {
-            const int row = 8 * h + (lane >> 3);
-            o.b[h] = (uint32_t)(row * a.ldx + 16 * ((lane & 7) ^ tm_swz(row)));
-        }
-        (void)wave;
-    } else {
-        const int p = lane & 15;  // 16-byte slot in the LDS row
-#pragma unroll
-        for (int h = 0; h < 8; h++) {
-            const int row = 32 * wave + 4 * h + (lane >> 4);
-            o.b[h] = (uint32_t)(row * a.ldx + 16 * (p ^ bswz(row)));
-        }
-    }
-    return o;
-}
-
-// This wave's share of the loads of stage s of tile td into the buffer at LDS address `lds`. When td
-// is not valid the offsets get bit 31 set (beyond every record count): zeros, no memory traffic.
-template <bool TM>
-__device__ __forceinline__ void load_stage(uint32_t lds, const Args& a, const TileDesc& td, int s, int wave,
-                                           const LoadOffsets& lo) {
-    const int64_t k0 = (int64_t)s * BK;
-    const int tiles = (int)((a.K + BK - 1) / BK);
-    const uint32_t past = td.valid ? 0u : 0x80000000u;
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-        const int b = 4 * wave + j;
-        dma16(lds + b * 1024, lo.a + (((uint32_t)(b * tiles + s) * 1024u) | past), td.rA);
-    }
-    // metadata of blocks 4 wave .. 4 wave + 3 (one 256 B tile each) in one instruction
-    dma16(lds + A_BYTES + 4 * wave * 256, lo.m + (((uint32_t)(4 * wave * tiles + s) * 256u) | past), td.rM);
-    if constexpr (TM) {
-        // token rows 64 wave .. +63 of the tile, 8 per load; X's extent from the wave's first row:
-        // rows past N read zeros (K is a multiple of 128: no stage reaches past K)
-        const int64_t n1 = td.n0 + 64 * wave;
-        const i32x4 rB = make_rsrc(td.x + n1 * a.ldx + k0, td.valid ? (a.N - 1 - n1) * a.ldx + a.K - k0 : 0);
-#pragma unroll
-        for (int h = 0; h < 8; h++) dma16(lds + A_BYTES + META_BYTES + (64 * wave + 8 * h) * 128, lo.b[h], rB);
-    } else {
-        // X's exact extent from this stage's corner, rounded up to whole dwords (see make_rsrc)
-        const i32x4 rB = make_rsrc(td.x + k0 * a.ldx + td.n0, td.valid ? (a.K - 1 - k0) * a.ldx + a.N - td.n0 : 0);
-#pragma unroll
-        for (int h = 0; h < 8; h++) dma16(lds + A_BYTES + META_BYTES + (32 * wave + 4 * h) * B_ROW, lo.b[h], rB);
-    }
-}
-
-// Descriptor of logical tile L (-1: none); batch entries follow each other, and inside one tiles are
-// walked in groups of GROUP_M tile-rows.
-__device__ __forceinline__ TileDesc tile_desc(const Args& a, int L) {
-    TileDesc td;
-    td.valid = L >= 0;
-    const int per = a.tilesM * a.tilesN;
-    const int bt = L >= 0 ? L / per : 0;
-    const int Lc = L >= 0 ? L - bt * per : 0;
-    td.x = a.X + bt * a.sxb;
-    td.y = static_cast<char*>(a.Y) + bt * a.syb * 4;
-    const int gsize = GROUP_M * a.tilesN;
-    const int g = Lc / gsize;
-    const int first_m = g * GROUP_M;
-    const int gm = (a.tilesM - first_m) < GROUP_M ? (a.tilesM - first_m) : GROUP_M;
-    const int in_g = Lc - g * gsize;
-    const int tm = first_m + in_g % gm, tn = in_g / gm;
-    td.m0 = (int64_t)tm * BM;
-    td.n0 = (int64_t)tn * BN;
-    const int64_t tiles = (a.K + BK - 1) / BK, blocks_left = (a.M + 15) / 16 - td.m0 / 16;
-    const int64_t blocks = blocks_left < BM / 16 ? blocks_left : BM / 16;
-    td.rA = make_rsrc(reinterpret_cast<const char*>(a.vals) + (td.m0 / 16) * tiles * 1024, blocks * tiles * 1024);
-    td.rM = make_rsrc(a.meta + (td.m0 / 16) * tiles * 256, blocks * tiles * 256);
-    return td;
-}
-
-struct LaneOffsets {
-    int a;       // A fragment of block wm0/16: block * 1024 + lane * 16
-    int m;       // metadata: A_BYTES + block * 256 + lane * 4
-    int b[FN];   // B fragment j, first read (t = 0); token-major: the two reads of fragment 0
-};
-
-template <bool TM>
-__device__ __forceinline__ LaneOffsets lane_offsets(int wm0, int wn0, int lane) {
-    const int r = lane & 15, q = lane >> 4;
-    LaneOffsets o;
-    o.a = (wm0 >> 4) * 1024 + lane * 16;
-    o.m = A_BYTES + (wm0 >> 4) * 256 + lane * 4;
-    if constexpr (TM) {
-        const int base = A_BYTES + META_BYTES + (wn0 + r) * 128, u = q ^ tm_swz(r);
-        o.b[0] = base + 16 * u;
-        o.b[1] = base + 16 * (u ^ 4);
-#pragma unroll
-        for (int j = 2; j < FN; j++) o.b[j] = 0;
-        return o;
-    }
-    // read t of group q covers rows 16q + 8(t&1) + 64(t>>1) + r/2, which share row & 7 and
-    // (row >> 4) & 1 with row0, so the swizzle is fixed per lane and t only adds immediates
-    const int row0 = 16 * q + (r >> 1);
-    const int f = bswz(row0);
-#pragma unroll
-    for (int j = 0; j < FN; j++) {
-        const int unit = (wn0 >> 4) + j;  // 16 columns = one 16-byte unit
-        o.b[j] = A_BYTES + META_BYTES + row0 * B_ROW + ((unit ^ f) << 4) + 8 * (r & 1);
-    }
-    return o;
-}
-
-struct AFrags {
-    i32x4 a[FM];
-    uint32_t idx[FM];
-};
-
-typedef __attribute__((address_space(3))) char lds_char;
-
-// A lane's LDS address in this stage's buffer, opaque to the optimizer (keeps the immediates in the
-// reads instead of dozens of hoisted loop-invariant sums).
-__device__ __forceinline__ uint32_t stage_addr(uint32_t buf, int off) {
-    uint32_t v = buf + (uint32_t)off;
-    asm volatile("" : "+v"(v));
-    return v;
-}
-
-__device__ __forceinline__ void read_a(uint32_t buf, const LaneOffsets& o, AFrags& f) {
-    const lds_char* pa = (const lds_char*)(size_t)stage_addr(buf, o.a);
-    const lds_char* pm = (const lds_char*)(size_t)stage_addr(buf, o.m);
-#pragma unroll
-    for (int i = 0; i < FM; i++) {
-        f.a[i] = *reinterpret_cast<const __attribute__((address_space(3))) i32x4*>(pa + i * 1024);
-        f.idx[i] = *reinterpret_cast<const __attribute__((address_space(3))) uint32_t*>(pm + i * 256);
-    }
-}
-
-typedef int i32x2 __attribute__((ext_vector_type(2)));
-
-// B fragment j (16 columns x 128 k): four transposing reads of 8 k each, or, token-major, two 16-byte
-// reads of the lane's token row.
-template <bool TM>
-__device__ __forceinline__ i32x8 read_b(uint32_t buf, const LaneOffsets& o, int j) {
-    if constexpr (TM) {
-        typedef const __attribute__((address_space(3))) i32x4 lds_i32x4;
-        const lds_char* p0 = (const lds_char*)(size_t)stage_addr(buf, o.b[0]);
-        const lds_char* p1 = (const lds_char*)(size_t)stage_addr(buf, o.b[1]);
-        const i32x4 lo = *reinterpret_cast<lds_i32x4*>(p0 + j * 2048);
-        const i32x4 hi = *reinterpret_cast<lds_i32x4*>(p1 + j * 2048);
-        return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    }
-    const lds_char* p = (const lds_char*)(size_t)stage_addr(buf, o.b[j]);
-    i32x8 b;
-#pragma unroll
-    for (int t = 0; t < 4; t++) {
-        const int imm = ((t & 1) * 8 + (t >> 1) * 64) * B_ROW;
-        const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)(p + imm));
-        b[2 * t] = v[0];
-        b[2 * t + 1] = v[1];
-    }
-    return b;
-}
-
-__device__ __forceinline__ void mfma_block(i32x4 (&acc)[FM][FN], const AFrags& f, const i32x8& b, int j) {
-#pragma unroll
-    for (int i = 0; i < FM; i++)
-        acc[i][j] = __builtin_amdgcn_smfmac_i32_16x16x128_i8(f.a[i], b, acc[i][j], (int)f.idx[i], 0, 0);
-}
-
-// One K stage: stage s of the current tile, the workgroup's g-th stage (selects the buffer). B
-// fragments are read two blocks ahead (ring of 4); before the last two blocks the barrier publishes
-// stage g+1 and the loads of stage s+3 of this tile (or s+3-S of the next) go into this buffer; the next
-// stage's A fragments are reloaded one by one inside the last block. No branches.
-template <bool TM>
-__device__ __forceinline__ void stage(uint32_t l0, const Args& a, const TileDesc& cur_t, const TileDesc& next_t, int s,
-                                      int S, int g, i32x4 (&acc)[FM][FN], AFrags& f, i32x8 (&rb)[4],
-                                      const LaneOffsets& o, int wave, const LoadOffsets& lo) {
-    const int cb = g % 3;
-    const uint32_t cur = l0 + cb * STAGE_BYTES;
-    const uint32_t nxt = l0 + (cb == 2 ? 0 : cb + 1) * STAGE_BYTES;
-#pragma unroll
-    for (int j = 0; j < 6; j++) {
-        rb[(j + 2) & 3] = read_b<TM>(cur, o, j + 2);
-        __builtin_amdgcn_sched_barrier(0);
-        mfma_block(acc, f, rb[j & 3], j);
-        __builtin_amdgcn_sched_barrier(0);
-    }
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of stage g are done
-    wait_vmcnt<LOADS_PER_STAGE>();       // stage g+1 has landed
-    __builtin_amdgcn_s_barrier();
-    const bool here = s + 3 < S;
-    load_stage<TM>(cur, a, here ? cur_t : next_t, here ? s + 3 : s + 3 - S, wave, lo);
-    rb[0] = read_b<TM>(nxt, o, 0);
-    rb[1] = read_b<TM>(nxt, o, 1);
-    __builtin_amdgcn_sched_barrier(0);
-    mfma_block(acc, f, rb[2], 6);
-    __builtin_amdgcn_sched_barrier(0);
-    const lds_char* pa = (const lds_char*)(size_t)stage_addr(nxt, o.a);
-    const lds_char* pm = (const lds_char*)(size_t)stage_addr(nxt, o.m);
-#pragma unroll
-    for (int i = 0; i < FM; i++) {
-        acc[i][7] = __builtin_amdgcn_smfmac_i32_16x16x128_i8(f.a[i], rb[3], acc[i][7], (int)f.idx[i], 0, 0);
-        f.a[i] = *reinterpret_cast<const __attribute__((address_space(3))) i32x4*>(pa + i * 1024);
-        f.idx[i] = *reinterpret_cast<const __attribute__((address_space(3))) uint32_t*>(pm + i * 256);
-        __builtin_amdgcn_sched_barrier(0);
-    }
-}
-
-// Epilogue from registers, four fragments (64 columns) at a time. The dequant -- fl32(fl32(acc) *
-// scale[m]), one rounding multiply -- is applied per accumulator row; then, as in the bf16 kernel, the
-// quad transposes of each fragment and a quad transpose across the four fragments give lane
-// (q, 4a + x) row 4q + s, columns 16x + 4a .. +3 in slot s, so each lane quad stores into one row (two
-// 128-byte lines, one request each, instead of one request per lane) and each 16-byte store
-// instruction writes 4 rows x 256 bytes, whole lines (never a half-written line that the cache could
-// evict and write back twice, as happened with power-of-two row pitches). No LDS is used.
-// FULL: the wave's whole 128 x 128 block lies inside Y and 16-byte stores are allowed (then the row
-// offsets of a lane quad fit 32 bits); otherwise every element is bounds-checked.
-template <bool SCALE, bool FULL>
-__device__ __forceinline__ void store_tile(const i32x4 (&acc)[FM][FN], const Args& a, char* y, int64_t mw, int64_t nw,
-                                           int lane) {
-    const int q = lane >> 4, r = lane & 15, b = r & 3, a4 = r >> 2;
-    char* const y0 = y + (mw * a.ldy + nw) * 4;  // wave-uniform corner
-    const uint32_t lane_off = FULL ? (uint32_t)((4 * q * a.ldy + 16 * b + 4 * a4) * 4) : 0u;
-#pragma unroll
-    for (int i = 0; i < FM; i++) {
-        const int64_t mq = mw + 16 * i + 4 * q;  // accumulator rows mq .. mq+3
-        float sc[4];
-#pragma unroll
-        for (int t = 0; t < 4; t++) sc[t] = (SCALE && (FULL || mq + t < a.M)) ? a.scale[mq + t] : 0.f;
-#pragma unroll
-        for (int jg = 0; jg < FN / 4; jg++) {
-            uint32_t v[4][4];
-#pragma unroll
-            for (int f = 0; f < 4; f++) {
-#pragma unroll
-                for (int t = 0; t < 4; t++) {
-                    const int x = acc[i][4 * jg + f][t];
-                    v[f][t] = SCALE ? __float_as_uint(__fmul_rn((float)x, sc[t])) : (uint32_t)x;
-                }
-                quad_transpose(v[f], b);
-            }
-            slot_transpose4<4>(v, b);
-#pragma unroll
-            for (int s = 0; s < 4; s++) {
-                if constexpr (FULL) {
-                    char* const p = y0 + ((16 * i + s) * a.ldy + 64 * jg) * 4 + lane_off;
-                    *reinterpret_cast<uint4*>(p) = make_uint4(v[s][0], v[s][1], v[s][2], v[s][3]);
-                } else {
-                    const int64_t m = mw + 16 * i + 4 * q + s, n = nw + 64 * jg + 16 * b + 4 * a4;
-                    uint32_t* p = reinterpret_cast<uint32_t*>(y) + m * a.ldy + n;
-                    if (m < a.M) {
-#pragma unroll
-                        for (int k = 0; k < 4; k++)
-                            if (n + k < a.N) p[k] = v[s][k];
-                    }
-                }
-            }
-        }
-        __builtin_amdgcn_sched_barrier(0);  // one row block of fragments at a time
-    }
-}
-
-// Token-major epilogue: Y is N x M; each accumulator (column n, rows 4q .. 4q+3 of M) is dequantized
-// per row and is 4 consecutive elements of token row n. As in the bf16 kernel, a quad transpose
-// across four row fragments gives each lane quad one token row (16x + 4q .. +3 of 64 M-columns in
-// lane 4c + x), so a quad's 16-byte stores fall in two 128-byte lines and each store instruction
-// covers 16 token rows x 256 bytes.
-template <bool SCALE, bool FULL>
-__device__ __forceinline__ void store_tile_tm(const i32x4 (&acc)[FM][FN], const Args& a, char* y, int64_t mw,
-                                              int64_t nw, int lane) {
-    const int q = lane >> 4, r = lane & 15, x = r & 3, c = r >> 2;
-    char* const y0 = y + (nw * a.ldy + mw) * 4;  // wave-uniform corner
-    const uint32_t lane_off = FULL ? (uint32_t)((4 * c * a.ldy + 16 * x + 4 * q) * 4) : 0u;
-    float sc[FM][4];
-#pragma unroll
-    for (int i = 0; i < FM; i++)
-#pragma unroll
-        for (int t = 0; t < 4; t++) {
-            const int64_t m = mw + 16 * i + 4 * q + t;
-            sc[i][t] = (SCALE && (FULL || m < a.M)) ? a.scale[m] : 0.f;
-        }
-#pragma unroll
-    for (int j = 0; j < FN; j++) {
-#pragma unroll
-        for (int ig = 0; ig < FM / 4; ig++) {
-            uint32_t v[4][4];
-#pragma unroll
-            for (int f = 0; f < 4; f++)
-#pragma unroll
-                for (int t = 0; t < 4; t++) {
-                    const int e = acc[4 * ig + f][j][t];
-                    v[f][t] = SCALE ? __float_as_uint(__fmul_rn((float)e, sc[4 * ig + f][t])) : (uint32_t)e;
-                }
-            slot_transpose4<4>(v, x);
-#pragma unroll
-            for (int s = 0; s < 4; s++) {
-                if constexpr (FULL) {
-                    char* const p = y0 + ((16 * j + s) * a.ldy + 64 * ig) * 4 + lane_off;
-                    *reinterpret_cast<uint4*>(p) = make_uint4(v[s][0], v[s][1], v[s][2], v[s][3]);
-                } else {
-                    const int64_t n = nw + 16 * j + 4 * c + s, m = mw + 64 * ig + 16 * x + 4 * q;
-                    if (n < a.N) {
-#pragma unroll
-                        for (int t = 0; t < 4; t++)
-                            if (m + t < a.M) reinterpret_cast<uint32_t*>(y)[n * a.ldy + m + t] = v[s][t];
-                    }
-                }
-            }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-    }
-}
-
-template <bool SCALE, bool TM>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_i8_tiled_kernel(Args a) {
-    __shared__ __attribute__((aligned(16))) char smem[3 * STAGE_BYTES];
-    const uint32_t l0 = (uint32_t)(size_t)(__attribute__((address_space(3))) char*)smem;
-
-    const int p = blockIdx.x;
-    const int L = tile_of(a, p, 0);
-    if (L < 0) return;  // whole workgroup
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    const int wm0 = (wave >> 1) * WM, wn0 = (wave & 1) * WN;
-    const LaneOffsets o = lane_offsets<TM>(wm0, wn0, lane);
-    const LoadOffsets lo = load_offsets<TM>(a, lane, wave);
-    const int S = (int)((a.K + BK - 1) / BK);
-
-    i32x4 acc[FM][FN];
-#pragma unroll
-    for (int i = 0; i < FM; i++)
-#pragma unroll
-        for (int j = 0; j < FN; j++) acc[i][j] = i32x4{0, 0, 0, 0};
-
-    // three-stage pipeline continued across the workgroup's tiles (see stage()); with fewer than 3
-    // stages per tile every workgroup has one tile (see the launcher)
-    TileDesc cur_t = tile_desc(a, L);
-    TileDesc next_t = tile_desc(a, tile_of(a, p, 1));
-    load_stage<TM>(l0, a, S > 0 ? cur_t : next_t, 0, wave, lo);
-    load_stage<TM>(l0 + STAGE_BYTES, a, S > 1 ? cur_t : next_t, S > 1 ? 1 : 0, wave, lo);
-    wait_vmcnt<LOADS_PER_STAGE>();
-    __builtin_amdgcn_s_barrier();
-    load_stage<TM>(l0 + 2 * STAGE_BYTES, a, S > 2 ? cur_t : next_t, S > 2 ? 2 : 0, wave, lo);
-
-    AFrags fa;
-    i32x8 rb[4];
-    read_a(l0, o, fa);
-    rb[0] = read_b<TM>(l0, o, 0);
-    rb[1] = read_b<TM>(l0, o, 1);
-    int g = 0;
-    for (int k = 1;; k++) {
-        for (int s = 0; s < S; s++, g++) stage<TM>(l0, a, cur_t, next_t, s, S, g, acc, fa, rb, o, wave, lo);
-        {
-            const int64_t mw = cur_t.m0 + wm0, nw = cur_t.n0 + wn0;
-            const bool full = (mw + WM <= a.M) && (nw + WN <= a.N) && a.y_vec;
-            if constexpr (TM) {
-                if (full)
-                    store_tile_tm<SCALE, true>(acc, a, cur_t.y, mw, nw, lane);
-                else
-                    store_tile_tm<SCALE, false>(acc, a, cur_t.y, mw, nw, lane);
-            } else {
-                if (full)
-                    store_tile<SCALE, true>(acc, a, cur_t.y, mw, nw, lane);
-                else
-                    store_tile<SCALE, false>(acc, a, cur_t.y, mw, nw, lane);
-            }
-        }
-        if (!next_t.valid) break;
-#pragma unroll
-        for (int i = 0; i < FM; i++)
-#pragma unroll
-            for (int j = 0; j < FN; j++) acc[i][j] = i32x4{0, 0, 0, 0};
-        cur_t = next_t;
-        next_t = tile_desc(a, tile_of(a, p, k + 1));
-    }
-    wait_vmcnt<0>();  // the zero-filling loads past the last tile have landed before the workgroup ends
-}
-
+extern template hipError_t launch_out<OUT_BF16>(const GemmArgs&, hipStream_t);
+extern template hipError_t launch_out<OUT_I8>(const GemmArgs&, hipStream_t);
+template hipError_t launch_out<OUT_I32>(const GemmArgs&, hipStream_t);
+template hipError_t launch_out<OUT_F32>(const GemmArgs&, hipStream_t);
 }  // namespace tiled_i8
 
 bool gemm_i8_tiled_ok(const GemmArgs& g) {
@@ -520,38 +22,12 @@ bool gemm_i8_tiled_ok(const GemmArgs& g) {
 }
 
 hipError_t launch_gemm_i8_tiled(const GemmArgs& g, hipStream_t s) {
-    tiled_i8::Args a;
-    a.vals = static_cast<const int8_t*>(g.values); a.meta = g.meta;
-    a.X = static_cast<const int8_t*>(g.X); a.scale = g.scale; a.Y = g.Y;
-    a.M = g.M; a.K = g.K; a.N = g.N; a.ldx = g.ldx; a.ldy = g.ldy;
-    a.sxb = g.sx; a.syb = g.sy;
-    a.tilesM = (int)((g.M + tiled_i8::BM - 1) / tiled_i8::BM);
-    a.tilesN = (int)((g.N + tiled_i8::BN - 1) / tiled_i8::BN);
-    a.batch = (int)g.batch;
-    // vector stores: 16-byte aligned Y rows in every batch entry, and 16 rows' offsets in 32 bits
-    a.y_vec = ((reinterpret_cast<uintptr_t>(g.Y) & 15) == 0) && ((g.ldy * 4) % 16 == 0) &&
-              (g.batch == 1 || (g.sy * 4) % 16 == 0) && g.ldy * 64 < ((int64_t)1 << 31);
-    const int T = a.tilesM * a.tilesN * a.batch;
-    const int S = (int)((g.K + tiled_i8::BK - 1) / tiled_i8::BK);
-    int cus = 0, dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
-                                                 hipSuccess || cus <= 0)
-        cus = 256;
-    // one workgroup per compute unit walking several tiles; one tile each when a tile has fewer than
-    // three stages (the cross-tile pipeline then has nothing to overlap)
-    const unsigned grid = (unsigned)(S >= 3 && T > cus ? cus : T);
-    if (g.tm) {
-        if (g.scale)
-            hipLaunchKernelGGL((tiled_i8::gemm_i8_tiled_kernel<true, true>), dim3(grid), dim3(256), 0, s, a);
-        else
-            hipLaunchKernelGGL((tiled_i8::gemm_i8_tiled_kernel<false, true>), dim3(grid), dim3(256), 0, s, a);
-    } else {
-        if (g.scale)
-            hipLaunchKernelGGL((tiled_i8::gemm_i8_tiled_kernel<true, false>), dim3(grid), dim3(256), 0, s, a);
-        else
-            hipLaunchKernelGGL((tiled_i8::gemm_i8_tiled_kernel<false, false>), dim3(grid), dim3(256), 0, s, a);
+    switch (g.out_kind) {
+    case OUT_I32: return tiled_i8::launch_out<OUT_I32>(g, s);
+    case OUT_F32: return tiled_i8::launch_out<OUT_F32>(g, s);
+    case OUT_BF16: return tiled_i8::launch_out<OUT_BF16>(g, s);
+    default: return tiled_i8::launch_out<OUT_I8>(g, s);
     }
-    return hipGetLastError();
 }
 
 }  // namespace sp24

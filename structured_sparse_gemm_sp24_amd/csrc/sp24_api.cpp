@@ -184,6 +184,10 @@ int check_gemm(const void* values, const uint8_t* meta, int64_t M, int64_t K, co
     g.tm = tm;
     g.scale = nullptr;
     g.out_fp32 = false;
+    g.bias = nullptr;
+    g.gelu = 0;
+    g.out_kind = sp24::OUT_I32;
+    g.inv_scale = 1.f;
     return SP24_OK;
 }
 
@@ -222,6 +226,35 @@ int sp24_gemm_i8_ex(const int8_t* values, const uint8_t* meta, int64_t M, int64_
     if (K > 262142) return SP24_ERR_SHAPE;  // keeps |acc| < 2^31 for any int8 inputs
     if (scale && (reinterpret_cast<uintptr_t>(scale) & 3) != 0) return SP24_ERR_ALIGN;
     g.scale = scale;
+    g.out_kind = scale ? sp24::OUT_F32 : sp24::OUT_I32;
+    st = check_device();
+    if (st != SP24_OK) return st;
+    return hip_status(sp24::launch_gemm_i8(g, static_cast<hipStream_t>(stream)));
+}
+
+int sp24_gemm_i8_fused(const int8_t* values, const uint8_t* meta, int64_t M, int64_t K, const int8_t* X, int64_t N,
+                       int64_t ldx, int64_t x_batch_stride, const float* scale, const float* bias, int activation,
+                       void* Y, int out_dtype, float out_scale, int64_t ldy, int64_t y_batch_stride, int64_t batch,
+                       int layout, void* stream) {
+    if (!scale) return SP24_ERR_NULL;
+    if (out_dtype != SP24_FP32 && out_dtype != SP24_BF16 && out_dtype != SP24_I8) {
+        if (!values || !meta || !X || !Y) return SP24_ERR_NULL;
+        return SP24_ERR_DTYPE;
+    }
+    const int es = out_dtype == SP24_FP32 ? 4 : (out_dtype == SP24_BF16 ? 2 : 1);
+    sp24::GemmArgs g;
+    int st = check_gemm(values, meta, M, K, X, N, ldx, x_batch_stride, Y, ldy, y_batch_stride, batch, layout, 1, es, g);
+    if (st != SP24_OK) return st;
+    if (K > 262142) return SP24_ERR_SHAPE;  // keeps |acc| < 2^31 for any int8 inputs
+    if (activation != SP24_ACT_NONE && activation != SP24_ACT_GELU) return SP24_ERR_ARG;
+    if (out_dtype == SP24_I8 && !(out_scale > 0.f && out_scale < 3.4e38f)) return SP24_ERR_ARG;
+    if ((reinterpret_cast<uintptr_t>(scale) & 3) != 0 || (bias && (reinterpret_cast<uintptr_t>(bias) & 3) != 0))
+        return SP24_ERR_ALIGN;
+    g.scale = scale;
+    g.bias = bias;
+    g.gelu = activation == SP24_ACT_GELU;
+    g.out_kind = out_dtype == SP24_FP32 ? sp24::OUT_F32 : (out_dtype == SP24_BF16 ? sp24::OUT_BF16 : sp24::OUT_I8);
+    g.inv_scale = 1.0f / out_scale;  // IEEE single division, rounded once
     st = check_device();
     if (st != SP24_OK) return st;
     return hip_status(sp24::launch_gemm_i8(g, static_cast<hipStream_t>(stream)));

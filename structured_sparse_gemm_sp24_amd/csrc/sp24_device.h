@@ -107,6 +107,54 @@ __device__ __forceinline__ void slot_transpose4(uint32_t (&v)[4][W], int b) {
     }
 }
 
+// ---------------------------------------------------------------- int8 GEMM epilogue
+// GELU in fp32 from the device library's erff: 0.5 y (1 + erf(y / sqrt 2)), each step one rounding
+// (no contraction into fused multiply-adds).
+__device__ __forceinline__ float gelu_f32(float y) {
+#pragma clang fp contract(off)
+    const float t = erff(__fmul_rn(y, 0.70710678118654752f));
+    return __fmul_rn(__fmul_rn(0.5f, y), __fadd_rn(1.0f, t));
+}
+
+// Four GELUs as one out-of-line call: the tiled kernels' epilogues evaluate 256 per lane, and inlining
+// erff at every one of them makes the unrolled epilogue too large to unroll (the accumulators then
+// leave registers).
+__device__ __attribute__((noinline)) f32x4 gelu4_f32(f32x4 y) {
+    return f32x4{gelu_f32(y[0]), gelu_f32(y[1]), gelu_f32(y[2]), gelu_f32(y[3])};
+}
+
+// The int8 GEMM's value pipeline for one accumulator of output row m: dequant (one rounding multiply),
+// optional bias add (one rounding add), optional GELU.
+__device__ __forceinline__ float i8_dequant(int acc, float sc, float bias, bool has_bias) {
+#pragma clang fp contract(off)
+    float y = __fmul_rn((float)acc, sc);
+    if (has_bias) y = __fadd_rn(y, bias);
+    return y;
+}
+
+__device__ __forceinline__ float i8_value(int acc, float sc, float bias, bool has_bias, bool gelu) {
+    const float y = i8_dequant(acc, sc, bias, has_bias);
+    return gelu ? gelu_f32(y) : y;
+}
+
+// Requantization to int8: clamp(rne(fl32(y * inv_scale)), -127, 127), as the low byte; inv_scale is
+// fl32(1 / out_scale), computed once on the host.
+__device__ __forceinline__ uint32_t quant_i8(float y, float inv_scale) {
+    float q = rintf(__fmul_rn(y, inv_scale));
+    q = q > 127.f ? 127.f : (q < -127.f ? -127.f : q);
+    return (uint32_t)((int)q) & 0xFFu;
+}
+
+// 4 x 4 byte transpose inside each lane quad: byte t of lane b's word (row t of column b) goes to byte b
+// of lane t's word. Two exchanges: 16-bit halves with lane b ^ 2, then bytes with lane b ^ 1, each one
+// DPP move and one byte permute.
+__device__ __forceinline__ uint32_t quad_transpose_u8(uint32_t w, int b) {
+    const uint32_t r = dpp_xor2(w);
+    const uint32_t x = __builtin_amdgcn_perm(r, w, b < 2 ? 0x05040100u : 0x03020706u);
+    const uint32_t s = dpp_xor1(x);
+    return __builtin_amdgcn_perm(s, x, (b & 1) == 0 ? 0x06020400u : 0x03070105u);
+}
+
 // Wave-level sum of a double (64 lanes) by butterfly shuffles.
 __device__ __forceinline__ double wave_sum_f64(double v) {
 #pragma unroll

@@ -6,6 +6,9 @@
 
 namespace sp24 {
 
+// Output kinds of the int8 GEMM.
+enum OutKind { OUT_I32 = 0, OUT_F32 = 1, OUT_BF16 = 2, OUT_I8 = 3 };
+
 // Operands of one sparse GEMM call, validated by the C ABI. Element strides are in elements of the
 // operand's type.
 //   feature-major (tm == false): X is K x N (X[k, n] at k * ldx + n), Y is M x N (Y[m, n] at m * ldy + n)
@@ -23,6 +26,13 @@ struct GemmArgs {
     bool tm;
     const float* scale;  // int8 only: per-row dequant scale, or NULL for raw int32 output
     bool out_fp32;       // bf16 only: fp32 output (else bf16)
+    // int8 epilogue (with scale): y = fl32(fl32(acc) * scale[m]), + bias[m] when bias is set, GELU when
+    // gelu is set, then stored as out_kind (OUT_F32, OUT_BF16 round to nearest even, OUT_I8
+    // clamp(rne(fl32(y * inv_scale)), -127, 127)); without scale out_kind is OUT_I32 (raw accumulators)
+    const float* bias;
+    int gelu;
+    int out_kind;
+    float inv_scale;
 };
 
 hipError_t launch_col_norms(const uint16_t* X, int64_t K, int64_t N, int64_t ldx, float* norms, hipStream_t s);

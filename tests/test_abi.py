@@ -161,6 +161,21 @@ def test_gemm_i8_ex_validation(lib, args, expect):
     assert lib.sp24_gemm_i8_ex(*args) == expect
 
 
+@pytest.mark.parametrize("args,expect", [
+    # values, meta, M, K, X, N, ldx, xbs, scale, bias, act, Y, out_dtype, out_scale, ldy, ybs, batch, layout, stream
+    ((A, B, 16, 16, C, 4, 4, 0, NULL, NULL, 0, A, FP32, 1.0, 4, 0, 1, FM, NULL), sp.SP24_ERR_NULL),    # no scale
+    ((A, B, 16, 16, C, 4, 4, 0, B, NULL, 0, A, I32, 1.0, 4, 0, 1, FM, NULL), sp.SP24_ERR_DTYPE),
+    ((A, B, 16, 16, C, 4, 4, 0, B, NULL, 2, A, FP32, 1.0, 4, 0, 1, FM, NULL), sp.SP24_ERR_ARG),       # activation
+    ((A, B, 16, 16, C, 4, 4, 0, B, NULL, 1, A, I8, 0.0, 4, 0, 1, FM, NULL), sp.SP24_ERR_ARG),         # out_scale
+    ((A, B, 16, 16, C, 4, 4, 0, B, NULL, 1, A, I8, float("nan"), 4, 0, 1, FM, NULL), sp.SP24_ERR_ARG),
+    ((A, B, 16, 16, C, 4, 4, 0, B, ctypes.c_void_p(0x20002), 0, A, FP32, 1.0, 4, 0, 1, FM, NULL), sp.SP24_ERR_ALIGN),
+    ((A, B, 16, 16, C, 4, 4, 8, B, NULL, 0, A, I8, 1.0, 4, 64, 2, FM, NULL), sp.SP24_ERR_ALIGN),      # X stride
+    ((A, B, 16, 16, C, 4, 16, 0, B, NULL, 0, A, BF16, 1.0, 8, 0, 1, TM, NULL), sp.SP24_ERR_SHAPE),    # ldy < M
+])
+def test_gemm_i8_fused_validation(lib, args, expect):
+    assert lib.sp24_gemm_i8_fused(*args) == expect
+
+
 def test_compressed_bytes(lib):
     vb, mb = ctypes.c_int64(), ctypes.c_int64()
     # rows padded to 16, columns to 128 / value size
@@ -187,6 +202,8 @@ def test_valid_arguments_without_a_device_report_device_error(lib):
     assert lib.sp24_gemm_bf16(A, B, 16, 16, C, 4, 4, A, FP32, 4, NULL) == sp.SP24_ERR_DEVICE
     assert lib.sp24_gemm_bf16_ex(A, B, 16, 16, C, 4, 16, 64, A, FP32, 16, 64, 2, TM, NULL) == sp.SP24_ERR_DEVICE
     assert lib.sp24_gemm_i8_ex(A, B, 16, 16, C, 4, 16, 64, NULL, A, 16, 64, 2, TM, NULL) == sp.SP24_ERR_DEVICE
+    assert lib.sp24_gemm_i8_fused(A, B, 16, 16, C, 4, 16, 64, B, NULL, 1, A, I8, 0.5, 16, 64, 2, TM, NULL) == \
+        sp.SP24_ERR_DEVICE
     assert lib.sp24_col_norms(A, 16, 8, 8, B, NULL) == sp.SP24_ERR_DEVICE
 
 

@@ -395,6 +395,55 @@ def test_gemm_i8_token_major_vs_numpy_integer_matmul():
     assert np.array_equal(Y, ref.astype(np.int32).astype(np.float32) * scale[None, :])
 
 
+def test_gelu_reference_vs_torch_and_identities():
+    # the fused epilogue's GELU reference against torch's exact (erf) GELU in float64
+    x = np.concatenate([np.linspace(-12, 12, 2001), [0.0, 1e-30, -1e-30, 1e-8, -40.0, 40.0]])
+    ref = torch.nn.functional.gelu(torch.from_numpy(x), approximate="none").numpy()
+    # (1 + erf) cancels for large negative x in both: compare with an absolute floor there
+    np.testing.assert_allclose(oracle.gelu64(x), ref, rtol=1e-14, atol=1e-15)
+    # GELU(x) - GELU(-x) = x, GELU(0) = 0, GELU(x) -> x for large x
+    np.testing.assert_allclose(oracle.gelu64(x) - oracle.gelu64(-x), x, rtol=1e-14, atol=1e-15)
+    assert oracle.gelu64(0.0) == 0.0 and oracle.gelu64(40.0) == 40.0
+
+
+def test_requant_rule_examples():
+    # clamp(rne(y * fl32(1/s)), -127, 127): halfway cases to even, clamping at +-127 (never -128)
+    y = np.array([2.5, 3.5, -2.5, -3.5, 127.6, 126.5, -300.0, 0.49999997, -0.5, 0.0], np.float32)
+    assert oracle.requant_i8(y, 1.0).tolist() == [2, 4, -2, -4, 127, 126, -127, 0, 0, 0]
+    # the reciprocal is rounded to fp32 first: fl32(1/0.1f) = 10 exactly, fl32(0.25 * 10) = 2.5 -> 2
+    assert np.float32(1) / np.float32(0.1) == np.float32(10.0)
+    assert oracle.requant_i8(np.float32(0.25), 0.1).item() == 2
+    # fl32(1/3) = 0.33333334: 7.5 and 4.5 times it round to exactly 2.5 and 1.5 in fp32, then to even
+    assert oracle.requant_i8(np.array([7.5, 4.5], np.float32), 3.0).tolist() == [2, 2]
+    # in float64 the products stay above the halfway points: 2.5000000 + 5e-8 -> 3, 1.5 + 3e-8 -> 2
+    assert oracle.requant_i8(np.array([7.5, 4.5], np.float64), 3.0).tolist() == [3, 2]
+
+
+def test_gemm_i8_fused_closed_forms():
+    rng = np.random.default_rng(90)
+    M, K, N = 24, 64, 11
+    W = rng.integers(-3, 4, size=(M, K), dtype=np.int8)
+    X = rng.integers(-3, 4, size=(K, N), dtype=np.int8)
+    vals, meta = oracle.prune_compress(W, oracle.I8)
+    acc, _ = oracle.gemm_i8(vals, meta, X, M)
+    one = np.ones(M, np.float32)
+    bias = rng.integers(-20, 21, size=M).astype(np.float32)
+    # scale 1 and integer bias: every step is exact, y = acc + bias
+    r = oracle.gemm_i8_fused(vals, meta, X, M, one, bias, out_scale=1.0)
+    assert np.array_equal(r["y32"], (acc + bias[:, None]).astype(np.float32))
+    assert np.array_equal(r["q"], np.clip(acc + bias[:, None], -127, 127).astype(np.int8))
+    # GELU of exact integers against torch
+    g = oracle.gemm_i8_fused(vals, meta, X, M, one, bias, gelu=True)["y"]
+    ref = torch.nn.functional.gelu(torch.from_numpy((acc + bias[:, None]).astype(np.float64))).numpy()
+    np.testing.assert_allclose(g, ref, rtol=1e-14, atol=1e-300)
+    # no bias, no GELU: the plain dequantized GEMM
+    s = (rng.random(M) * 1e-2).astype(np.float32)
+    assert np.array_equal(oracle.gemm_i8_fused(vals, meta, X, M, s)["y"], oracle.gemm_i8(vals, meta, X, M, s)[1])
+    # token-major layout: the transpose
+    rt = oracle.gemm_i8_fused(vals, meta, np.ascontiguousarray(X.T), M, one, bias, out_scale=1.0, layout="token")
+    assert np.array_equal(rt["q"], r["q"].T)
+
+
 def test_gemm_i8_overflow_is_reported():
     K = 270000 - 270000 % 16
     W = np.full((1, K), -128, np.int8)
