@@ -173,8 +173,9 @@ int sp24_gemm_i8_ex(const int8_t* values, const uint8_t* meta, int64_t M, int64_
  * of the Sparse-QAT case keeps its FFN in int8 between layers; oeforum post: int8 and 2:4 combine).
  * For every output element, in fp32 with one rounding per step:
  *   y = fl32( fl32(acc[m, n]) * scale[m] );   y = fl32(y + bias[m]) when bias != NULL;
- *   y = GELU(y) when activation == SP24_ACT_GELU (fp32, computed with the device erff: not bit-exact
- *       across implementations; |error| <= 8 * 2^-24 * |y| against the exact GELU of the fp32 input);
+ *   y = GELU(y) = y/2 erfc(-y / sqrt 2) when activation == SP24_ACT_GELU, in fp32 with the erfc
+ *       formula of Numerical Recipes (section 6.2): not bit-exact across implementations; |error| <=
+ *       8 * 2^-24 * |y| against the exact GELU of the fp32 input;
  *   stored as out_dtype: SP24_FP32; SP24_BF16 (round to nearest even); or SP24_I8, the requantized code
  *       clamp( rne( fl32(y * inv) ), -127, 127 ) with inv = fl32(1 / out_scale), out_scale > 0 the next
  *       layer's input scale (a multiply by the rounded reciprocal, not a division).

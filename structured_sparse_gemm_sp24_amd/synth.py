@@ -129,6 +129,12 @@ def bert_ffn_int8_dense():
                 X1_f32=normal_f32(23, (768, 8192)), X2_f32=normal_f32(24, (3072, 8192)))
 
 
+def bert_ffn_biases():
+    """Biases of the BERT-base FFN pair for the fused chain: b1 (3072, seed 25), b2 (768, seed 26),
+    fp32 ~N(0, 0.02^2)."""
+    return dict(b1=normal_f32(25, (3072,), 0.02), b2=normal_f32(26, (768,), 0.02))
+
+
 def llm_proj(M: int):
     """LLM projection, Wanda scoring: W Mx4096 bf16 ~N(0, 0.02^2) (seed 31 for M=11008, 32 for 4096);
     calibration X 4096x2048 heavy-tailed (seed 33); GEMM activations 4096x4096 same law (seed 34),

@@ -119,3 +119,39 @@ def test_ffn_28672x8192():
     rows = _rows(28672, 5)[:24]
     for N in (8, 64, 512, 8192):
         _check_bf16(vd, md, rv, rm, 28672, np.ascontiguousarray(d["X_bf16"][:, :N]), rows)
+
+
+def test_bert_ffn_int8_fused_chain():
+    # the fused chain the bench times (token-major): H = int8(GELU(W1 X + b1)), Y = W2 H + b2
+    d = synth.bert_ffn_int8_dense()
+    bias = synth.bert_ffn_biases()
+    qs = []
+    for wk in ("W1_f32", "W2_f32"):
+        W = d[wk]
+        M, K = W.shape
+        _, _, rv, rm = _prune_bit_exact(W, oracle.FP32)
+        qs.append(synth.quantize_rows(oracle.decompress(rv, rm, oracle.FP32, M, K)))
+    (q1, s_w1), (q2, s_w2) = qs
+    xq, s_x = synth.quantize_tensor(d["X1_f32"])
+    Xt = np.ascontiguousarray(xq.T)  # 8192 tokens x 768
+    s1 = synth.dequant_scales(s_w1, s_x)
+    s_h = 0.01  # a fixed hidden scale (the codes' range is what matters here)
+    s2 = synth.dequant_scales(s_w2, np.float32(s_h))
+    say("full size: BERT FFN int8 fused chain, token-major, N = 8192")
+    v1, m1, rv1, rm1 = _prune_bit_exact(q1, oracle.I8)
+    v2, m2, rv2, rm2 = _prune_bit_exact(q2, oracle.I8)
+    H = sp.sp24_gemm_i8_fused(v1, m1, 3072, dev(Xt), dev(s1), bias=dev(bias["b1"]), activation="gelu",
+                              out_dtype=torch.int8, out_scale=s_h, layout="token")
+    Y = sp.sp24_gemm_i8_fused(v2, m2, 768, H, dev(s2), bias=dev(bias["b2"]), layout="token")
+    rows = _rows(3072, 6)
+    h = host_bits(H)
+    ref = oracle.gemm_i8_fused(rv1, rm1, Xt, 3072, s1, bias["b1"], gelu=True, out_scale=s_h, rows=rows,
+                               layout="token")
+    got = h[:, rows].astype(np.int32)
+    assert np.all(np.abs(got - ref["q"].astype(np.int32)) <= 1)
+    assert np.mean(got == ref["q"]) > 0.999
+    # GEMM 2 is bit-exact on the codes the GPU produced
+    rows2 = _rows(768, 7)
+    y = host_bits(Y)[:, rows2]
+    ref2 = oracle.gemm_i8_fused(rv2, rm2, h, 768, s2, bias["b2"], rows=rows2, layout="token")["y"]
+    assert np.array_equal(y.view(np.uint32), ref2.view(np.uint32))
