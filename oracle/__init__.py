@@ -61,6 +61,7 @@ def _load():
         lib.oracle_meta_offset.argtypes = [I64, I64, I64, I]
         lib.oracle_meta_offset.restype = I64
         lib.oracle_decompress.argtypes = [P, P, I, I64, I64, P, I64]
+        lib.oracle_prune_mask.argtypes = [P, I, I64, I64, I64, I, I, P, P, P, I64]
         lib.oracle_gemm_bf16.argtypes = [P, P, I64, I64, P, I64, I64, P, I64, P]
         lib.oracle_gemm_i8.argtypes = [P, P, I64, I64, P, I64, I64, P, P, I64, P, P]
         lib.oracle_fp32_to_bf16.argtypes = [ctypes.c_float]
@@ -129,6 +130,20 @@ def prune_compress(W: np.ndarray, dtype: int, score: int = MAGNITUDE, norms: np.
     _check(_load().oracle_prune_compress(_ptr(W), dtype, M, K, K, score, _ptr(norms), _ptr(values), val_dtype,
                                          _ptr(meta)))
     return values, meta
+
+
+def prune_mask(W: np.ndarray, dtype: int, keep: int, score: int = MAGNITUDE, norms: np.ndarray | None = None):
+    """k-of-4 mask (NVIDIA blog, progressive sparse training, Figure 4: keep 3 of 4, later 2 of 4).
+    Returns (mask, masked): mask M x K/8 bytes (nibble of group g at byte g/2, even g low, bit t set
+    when position t is kept) and the masked M x K weight (kept elements bit-copied, +0 elsewhere)."""
+    W = np.ascontiguousarray(_c(W, _DT_NP[dtype]))
+    M, K = W.shape
+    mask = np.zeros((M, K // 8), np.uint8)
+    out = np.zeros((M, K), _DT_NP[dtype])
+    if norms is not None:
+        norms = np.ascontiguousarray(_c(norms, np.float32))
+    _check(_load().oracle_prune_mask(_ptr(W), dtype, M, K, K, keep, score, _ptr(norms), _ptr(mask), _ptr(out), K))
+    return mask, out
 
 
 def meta_bad_nibbles(meta: np.ndarray, M: int, K: int, val_dtype: int) -> int:

@@ -279,6 +279,62 @@ int oracle_prune_compress(const void* W, int dtype, int64_t M, int64_t K, int64_
     return OR_OK;
 }
 
+/* ---------------------------------------------------------------- k-of-4 masks [NVBLOG progressive] */
+
+/* NVIDIA blog on Ampere structured sparsity, progressive sparse training section, Figure 4: the mask
+ * first keeps 3 of every 4 weights (25 % sparsity), later 2 of 4 (50 %). Element t of a group is kept
+ * when fewer than `keep` other elements beat it (u beats t if its score is larger, or equal with a lower
+ * index -- the rule of keep_two). Returns the mask nibble, bit t set when t is kept. */
+static int keep_mask(const double s[4], int keep) {
+    int nib = 0;
+    for (int t = 0; t < 4; t++) {
+        int beaten_by = 0;
+        for (int u = 0; u < 4; u++) {
+            if (u == t) continue;
+            if (s[u] > s[t] || (s[u] == s[t] && u < t)) beaten_by++;
+        }
+        if (beaten_by < keep) nib |= 1 << t;
+    }
+    return nib;
+}
+
+/* W: M x K (pitch ldw) of dtype in {BF16, FP16, FP32, I8}, K % 16 == 0, 1 <= keep <= 4. mask (or NULL):
+ * M x K/8 bytes, row-major, the nibble of group g at byte g/2 (even g low). W_out (or NULL): M x K
+ * (pitch ldo) with the kept elements bit-copied and +0 elsewhere. */
+int oracle_prune_mask(const void* W, int dtype, int64_t M, int64_t K, int64_t ldw, int keep, int score,
+                      const float* norms, uint8_t* mask, void* W_out, int64_t ldo) {
+    if (!W || (!mask && !W_out) || M < 0 || K < 0 || K % 16 != 0 || ldw < K || keep < 1 || keep > 4)
+        return OR_EARG;
+    if (W_out && ldo < K) return OR_EARG;
+    if (dtype != OR_BF16 && dtype != OR_FP16 && dtype != OR_FP32 && dtype != OR_I8) return OR_EARG;
+    if (score == OR_WANDA && (!norms || dtype == OR_I8)) return OR_EARG;
+    if (score != OR_WANDA && score != OR_MAGNITUDE) return OR_EARG;
+    const size_t isz = dtype_size(dtype);
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < M; i++) {
+        for (int64_t g = 0; g < K / 4; g++) {
+            size_t base = (size_t)i * (size_t)ldw + (size_t)(4 * g);
+            double s[4];
+            group_scores(W, dtype, base, score, norms, 4 * g, s);
+            int nib = keep_mask(s, keep);
+            if (mask) {
+                uint8_t* mb = mask + (size_t)i * (size_t)(K / 8) + (size_t)(g / 2);
+                *mb = (uint8_t)((*mb & (0xF0 >> (4 * (g % 2)))) | (nib << (4 * (g % 2))));
+            }
+            if (W_out) {
+                char* o = (char*)W_out + ((size_t)i * (size_t)ldo + (size_t)(4 * g)) * isz;
+                for (int t = 0; t < 4; t++) {
+                    if (nib & (1 << t))
+                        memcpy(o + t * isz, (const char*)W + (base + (size_t)t) * isz, isz);
+                    else
+                        memset(o + t * isz, 0, isz);
+                }
+            }
+        }
+    }
+    return OR_OK;
+}
+
 /* ---------------------------------------------------------------- metadata check [ORIN7 6.1] */
 
 /* Every nibble of the M x K region must name two distinct positions in ascending order. Returns

@@ -167,6 +167,68 @@ def test_bruteforce_int8_heavy_ties():
     assert np.array_equal(oracle.decompress(vflat, mflat, oracle.I8, 64, 256), dense_from_positions(W, pos))
 
 
+# ----------------------------------------------------------------- k-of-4 masks
+
+
+def topk_by_sort(scores: np.ndarray, k: int) -> np.ndarray:
+    """Mask nibbles of each group of 4 along the last axis: the first k of a stable sort by descending
+    score (equal scores keep index order, so the lower index wins)."""
+    s = scores.reshape(-1, 4)
+    order = np.argsort(-s, axis=1, kind="stable")[:, :k]
+    return (1 << order).sum(axis=1)
+
+
+def mask_nibbles(mask: np.ndarray, K: int) -> np.ndarray:
+    m = np.asarray(mask, np.uint8)
+    return np.stack([m & 0xF, m >> 4], axis=-1).reshape(m.shape[0], K // 4)
+
+
+@pytest.mark.parametrize("keep", [1, 2, 3, 4])
+def test_mask_bruteforce_every_group(keep):
+    """All 6^4 groups over {-2, -1, -0, +0, 1, 2}: the k-of-4 mask equals a stable top-k sort, the
+    masked weight keeps bit copies and writes +0 elsewhere."""
+    alphabet = np.array([-2.0, -1.0, -0.0, 0.0, 1.0, 2.0], dtype=np.float32)
+    groups = np.array(list(itertools.product(range(6), repeat=4)))
+    W = alphabet[groups].reshape(1, -1)
+    K = W.shape[1]
+    mask, out = oracle.prune_mask(W, oracle.FP32, keep)
+    nib = mask_nibbles(mask, K)[0]
+    assert np.array_equal(nib, topk_by_sort(np.abs(W), keep))
+    bits = (nib[:, None] >> np.arange(4)[None, :]) & 1
+    ref = np.where(bits.reshape(1, -1) == 1, W, np.float32(0.0))
+    assert np.array_equal(out.view(np.uint32), ref.view(np.uint32))
+    assert np.all([bin(n).count("1") == keep for n in nib])
+
+
+def test_mask_two_of_four_equals_compression_positions():
+    for dt in (oracle.BF16, oracle.I8):
+        W = (synth.normal_bf16(5, (37, 208)) if dt == oracle.BF16
+             else np.random.default_rng(5).integers(-128, 128, size=(37, 208), dtype=np.int8))
+        mask, _ = oracle.prune_mask(W, dt, 2)
+        vals, meta, _, _ = compress_rm(W, dt)
+        nib = meta_nibbles(meta, 208)
+        assert np.array_equal(mask_nibbles(mask, 208), (1 << (nib & 3)) | (1 << (nib >> 2)))
+
+
+@pytest.mark.parametrize("score", [oracle.MAGNITUDE, oracle.WANDA])
+def test_progressive_masks_equal_direct(score):
+    """NVIDIA blog, progressive sparse training (Figure 4): keep 3 of 4, then recompute on the remaining
+    weights to keep 2 of 4. Without tuning in between, that equals the direct 2 of 4 mask (the dropped
+    element scores 0 and stays last); so does every chain 4 -> 3 -> 2 -> 1."""
+    W = synth.normal_bf16(9, (48, 256))
+    W[:, ::7] = 0  # ties at zero
+    norms = None
+    if score == oracle.WANDA:
+        norms = np.abs(np.random.default_rng(3).standard_normal(256)).astype(np.float32)
+    cur = W
+    for keep in (3, 2, 1):
+        m_direct, out_direct = oracle.prune_mask(W, oracle.BF16, keep, score, norms)
+        m_chain, out_chain = oracle.prune_mask(cur, oracle.BF16, keep, score, norms)
+        assert np.array_equal(m_chain, m_direct), keep
+        assert np.array_equal(out_chain, out_direct)
+        cur = out_chain
+
+
 # ----------------------------------------------------------------- invariants on random data
 
 
