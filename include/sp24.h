@@ -119,6 +119,21 @@ int sp24_compressed_bytes(int64_t M, int64_t K, int val_dtype, int64_t* values_b
 int sp24_prune_compress(const void* W, int dtype, int64_t M, int64_t K, int64_t ldw, int score,
                         const float* norms, void* values, int val_dtype, uint8_t* meta, void* stream);
 
+/* k-of-4 mask (NVIDIA blog on Ampere structured sparsity, progressive sparse training section,
+ * Figure 4: the mask first keeps 3 of every 4 weights (25 % sparsity), is recomputed on the remaining
+ * weights after tuning to keep 2 of 4 (50 %); the tuning itself is outside this library).
+ *   In every group of 4 consecutive columns of a row of W (as sp24_prune_compress: dtype in {BF16, FP16,
+ *   FP32, I8}, pitch ldw with ldw*sizeof(dtype) % 16 == 0, MAGNITUDE or WANDA scores, lower index wins
+ *   ties), the `keep` elements (1 <= keep <= 4) beaten by fewer than `keep` others are kept.
+ *   mask (or NULL): M x K/8 bytes, row-major, the nibble of group g at byte g/2 of its row (even g in
+ *     the low nibble), bit t set when position t is kept.
+ *   W_out (or NULL; not both NULL): the masked weight, M x K of dtype, pitch ldo with
+ *     ldo*sizeof(dtype) % 16 == 0: kept elements bit-copied, +0 at the others.
+ * Recomputing a mask on a masked weight with a smaller keep gives the same mask as computing it on the
+ * original weight directly (the dropped elements score 0 and lose every comparison). */
+int sp24_prune_mask(const void* W, int dtype, int64_t M, int64_t K, int64_t ldw, int keep, int score,
+                    const float* norms, uint8_t* mask, void* W_out, int64_t ldo, void* stream);
+
 /* Inverse of the compression: W_out (M x K of dtype in {BF16, FP16, FP32, I8}, pitch ldw with
  * ldw*sizeof(dtype) % 16 == 0) gets every kept value at its original column and +0 (all-zero bits)
  * at the two pruned columns of every group. dtype is the values' dtype. */

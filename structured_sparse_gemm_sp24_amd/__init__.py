@@ -23,7 +23,8 @@ SP24_FEATURE_MAJOR, SP24_TOKEN_MAJOR = 0, 1
 SP24_ACT_NONE, SP24_ACT_GELU = 0, 1
 
 # every symbol include/sp24.h declares
-EXPORTS = ("sp24_col_norms", "sp24_compressed_bytes", "sp24_prune_compress", "sp24_decompress", "sp24_gemm_bf16",
+EXPORTS = ("sp24_col_norms", "sp24_compressed_bytes", "sp24_prune_compress", "sp24_prune_mask", "sp24_decompress",
+           "sp24_gemm_bf16",
            "sp24_gemm_i8", "sp24_gemm_bf16_ex", "sp24_gemm_i8_ex", "sp24_gemm_i8_fused", "sp24_status_string")
 
 _TORCH_TO_SP24 = {torch.bfloat16: SP24_BF16, torch.float16: SP24_FP16, torch.float32: SP24_FP32,
@@ -54,6 +55,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sp24_compressed_bytes.argtypes = [I64, I64, I, ctypes.POINTER(I64), ctypes.POINTER(I64)]
     lib.sp24_prune_compress.argtypes = [P, I, I64, I64, I64, I, P, P, I, P, P]
     lib.sp24_decompress.argtypes = [P, P, I, I64, I64, P, I64, P]
+    lib.sp24_prune_mask.argtypes = [P, I, I64, I64, I64, I, I, P, P, P, I64, P]
     lib.sp24_gemm_bf16.argtypes = [P, P, I64, I64, P, I64, I64, P, I, I64, P]
     lib.sp24_gemm_i8.argtypes = [P, P, I64, I64, P, I64, I64, P, P, I64, P]
     lib.sp24_gemm_bf16_ex.argtypes = [P, P, I64, I64, P, I64, I64, I64, P, I, I64, I64, I64, I, P]
@@ -148,6 +150,26 @@ def sp24_prune_compress(W: torch.Tensor, score: int = SP24_SCORE_MAGNITUDE, norm
                                             _ptr(norms), _ptr(values), _TORCH_TO_SP24[vdt], _ptr(meta), _stream(W))
     _check("sp24_prune_compress", st)
     return values, meta
+
+
+def sp24_prune_mask(W: torch.Tensor, keep: int, score: int = SP24_SCORE_MAGNITUDE, norms: torch.Tensor | None = None,
+                    mask: torch.Tensor | None = None, out: torch.Tensor | None = None, want_masked: bool = True):
+    """k-of-4 mask of W (M x K): returns (mask, masked W). mask is uint8 M x K/8 (nibble of group g at
+    byte g/2, bit t = position t kept); the masked weight keeps the selected elements and zeroes the
+    rest (None when want_masked is False and no out is given)."""
+    _dev_check(W, norms, mask, out)
+    M, K = W.shape
+    if mask is None:
+        mask = torch.empty((M, K // 8), dtype=torch.uint8, device=W.device)
+    if out is None and want_masked:
+        out = torch.empty((M, K), dtype=W.dtype, device=W.device)
+    if mask.dtype != torch.uint8 or tuple(mask.shape) != (M, K // 8) or not mask.is_contiguous():
+        raise ValueError(f"mask must be a contiguous uint8 tensor of shape {(M, K // 8)}")
+    st = load_library().sp24_prune_mask(_ptr(W), _TORCH_TO_SP24[W.dtype], M, K, _rows(W, "W"), int(keep), int(score),
+                                        _ptr(norms), _ptr(mask), _ptr(out), _rows(out, "out") if out is not None else K,
+                                        _stream(W))
+    _check("sp24_prune_mask", st)
+    return mask, out
 
 
 def sp24_decompress(values: torch.Tensor, meta: torch.Tensor, M: int, K: int,

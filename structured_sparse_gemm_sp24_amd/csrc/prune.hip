@@ -53,6 +53,24 @@ __device__ __forceinline__ void knockout_top2(const uint32_t k[4], int& lo, int&
 
 template <int DT> constexpr int esize() { return DT == DT_FP32 ? 4 : (DT == DT_I8 ? 1 : 2); }
 
+// Selection key of one element (bit pattern v of type DT): larger key = larger score. Magnitude: the
+// sign-cleared bits (IEEE) or |q| (int8); Wanda: the bits of fl32(|w|) * norm.
+template <int DT, bool WANDA, typename T>
+__device__ __forceinline__ uint32_t select_key(T v, float norm) {
+    if (WANDA) {
+        float a;
+        if (DT == DT_FP32) a = __uint_as_float((uint32_t)v & 0x7FFFFFFFu);
+        else if (DT == DT_FP16) a = f16_to_f32((uint16_t)(v & 0x7FFFu));
+        else a = bf16_to_f32((uint16_t)(v & 0x7FFFu));
+        return __float_as_uint(__fmul_rn(a, norm)) & 0x7FFFFFFFu;
+    } else if (DT == DT_I8) {
+        const int sv = (int)(int8_t)v;
+        return (uint32_t)(sv < 0 ? -sv : sv);
+    } else {
+        return (uint32_t)v & (DT == DT_FP32 ? 0x7FFFFFFFu : 0x7FFFu);
+    }
+}
+
 // Workgroup = 4 waves x TPW tiles of one 16-row block: wave w takes tiles t0 + w + 4 i, i < TPW.
 // Slots outside the M x K weight write the padding (values 0, metadata nibbles 0x4).
 template <int DT, int VOUT, bool WANDA, int TPW>
@@ -107,21 +125,7 @@ __global__ __launch_bounds__(256) void prune_compress_kernel(const void* __restr
             if (row_ok && c < K) {
                 uint32_t key[4];
 #pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    const T v = x[i][4 * g + e];
-                    if (WANDA) {
-                        float a;
-                        if (DT == DT_FP32) a = __uint_as_float((uint32_t)v & 0x7FFFFFFFu);
-                        else if (DT == DT_FP16) a = f16_to_f32((uint16_t)(v & 0x7FFFu));
-                        else a = bf16_to_f32((uint16_t)(v & 0x7FFFu));
-                        key[e] = __float_as_uint(__fmul_rn(a, norms[c + e])) & 0x7FFFFFFFu;
-                    } else if (DT == DT_I8) {
-                        const int sv = (int)(int8_t)v;
-                        key[e] = (uint32_t)(sv < 0 ? -sv : sv);
-                    } else {
-                        key[e] = (uint32_t)v & (DT == DT_FP32 ? 0x7FFFFFFFu : 0x7FFFu);
-                    }
-                }
+                for (int e = 0; e < 4; e++) key[e] = select_key<DT, WANDA>(x[i][4 * g + e], WANDA ? norms[c + e] : 0.f);
                 int lo, hi;
                 knockout_top2(key, lo, hi);
                 mbits |= (uint32_t)(lo | (hi << 2)) << (4 * g);
@@ -220,6 +224,99 @@ __global__ __launch_bounds__(256) void decompress_kernel(const void* __restrict_
             w[i] = out[4 * i] | (out[4 * i + 1] << 8) | (out[4 * i + 2] << 16) | (out[4 * i + 3] << 24);
         *reinterpret_cast<uint4*>(wp) = make_uint4(w[0], w[1], w[2], w[3]);
     }
+}
+
+// k-of-4 masks (NVIDIA blog, progressive sparse training, Figure 4: keep 3 of every 4, later 2 of 4).
+// One thread per 16-column chunk of a row: 4 groups; element t of a group is kept when fewer than
+// `keep` others beat it (the selection rule above: larger key, or equal key and lower index). Writes
+// the 4 mask nibbles (bit t = position t kept; 2 bytes of the row's K/8) and, when W_out is set, the
+// masked chunk (kept elements bit-copied, +0 elsewhere).
+template <int DT, bool WANDA>
+__global__ __launch_bounds__(256) void prune_mask_kernel(const void* __restrict__ W, int64_t ldw, uint32_t chunks_per_row,
+                                                         uint32_t total_chunks, int keep, const float* __restrict__ norms,
+                                                         uint8_t* __restrict__ mask, int64_t mask_ld, void* __restrict__ W_out,
+                                                         int64_t ldo) {
+    const uint32_t t = blockIdx.x * 256u + threadIdx.x;
+    if (t >= total_chunks) return;
+    const uint32_t row = t / chunks_per_row, c = t - row * chunks_per_row;
+    constexpr int isz = esize<DT>();
+    typedef typename Elem<DT>::T T;
+    const char* src = reinterpret_cast<const char*>(W) + ((int64_t)row * ldw + 16 * (int64_t)c) * isz;
+    uint32_t w[4 * isz];  // the chunk's 16 elements as 4 * isz words
+#pragma unroll
+    for (int h = 0; h < isz; h++) {
+        const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src) + h);
+#pragma unroll
+        for (int e = 0; e < 4; e++) w[4 * h + e] = v[e];
+    }
+    T x[16];
+#pragma unroll
+    for (int e = 0; e < 16; e++) {
+        if (isz == 4) x[e] = (T)w[e];
+        if (isz == 2) x[e] = (T)((w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+        if (isz == 1) x[e] = (T)((w[e >> 2] >> (8 * (e & 3))) & 0xFFu);
+    }
+    uint32_t bits = 0;
+#pragma unroll
+    for (int g = 0; g < 4; g++) {
+        uint32_t key[4];
+#pragma unroll
+        for (int e = 0; e < 4; e++) key[e] = select_key<DT, WANDA>(x[4 * g + e], WANDA ? norms[16 * c + 4 * g + e] : 0.f);
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            int beaten_by = 0;
+#pragma unroll
+            for (int u = 0; u < 4; u++)
+                if (u != e) beaten_by += (key[u] > key[e] || (key[u] == key[e] && u < e)) ? 1 : 0;
+            if (beaten_by < keep) bits |= 1u << (4 * g + e);
+        }
+    }
+    if (mask) *reinterpret_cast<uint16_t*>(mask + (int64_t)row * mask_ld + 2 * (int64_t)c) = (uint16_t)bits;
+    if (W_out) {
+        uint32_t o[4 * isz];
+#pragma unroll
+        for (int k = 0; k < 4 * isz; k++) o[k] = 0;
+#pragma unroll
+        for (int e = 0; e < 16; e++) {
+            const uint32_t v = (bits >> e) & 1 ? (uint32_t)x[e] : 0u;
+            if (isz == 4) o[e] = v;
+            if (isz == 2) o[e >> 1] |= v << (16 * (e & 1));
+            if (isz == 1) o[e >> 2] |= v << (8 * (e & 3));
+        }
+        uint4* dst = reinterpret_cast<uint4*>(reinterpret_cast<char*>(W_out) + ((int64_t)row * ldo + 16 * (int64_t)c) * isz);
+#pragma unroll
+        for (int h = 0; h < isz; h++) dst[h] = make_uint4(o[4 * h], o[4 * h + 1], o[4 * h + 2], o[4 * h + 3]);
+    }
+}
+
+template <int DT, bool WANDA>
+static hipError_t launch_mask(const void* W, int64_t M, int64_t K, int64_t ldw, int keep, const float* norms,
+                              uint8_t* mask, void* W_out, int64_t ldo, hipStream_t s) {
+    const uint32_t cpr = (uint32_t)(K / 16);
+    const uint32_t total = (uint32_t)(M * (K / 16));
+    const uint32_t blocks = (total + 255) / 256;
+    hipLaunchKernelGGL((prune_mask_kernel<DT, WANDA>), dim3(blocks), dim3(256), 0, s, W, ldw, cpr, total, keep, norms,
+                       mask, K / 8, W_out, ldo);
+    return hipGetLastError();
+}
+
+hipError_t launch_prune_mask(const void* W, int dtype, int64_t M, int64_t K, int64_t ldw, int keep, int score,
+                             const float* norms, uint8_t* mask, void* W_out, int64_t ldo, hipStream_t s) {
+    const bool wanda = score == 1;
+    switch (dtype) {
+    case DT_BF16:
+        return wanda ? launch_mask<DT_BF16, true>(W, M, K, ldw, keep, norms, mask, W_out, ldo, s)
+                     : launch_mask<DT_BF16, false>(W, M, K, ldw, keep, norms, mask, W_out, ldo, s);
+    case DT_FP16:
+        return wanda ? launch_mask<DT_FP16, true>(W, M, K, ldw, keep, norms, mask, W_out, ldo, s)
+                     : launch_mask<DT_FP16, false>(W, M, K, ldw, keep, norms, mask, W_out, ldo, s);
+    case DT_FP32:
+        return wanda ? launch_mask<DT_FP32, true>(W, M, K, ldw, keep, norms, mask, W_out, ldo, s)
+                     : launch_mask<DT_FP32, false>(W, M, K, ldw, keep, norms, mask, W_out, ldo, s);
+    case DT_I8:
+        return launch_mask<DT_I8, false>(W, M, K, ldw, keep, norms, mask, W_out, ldo, s);
+    }
+    return hipErrorInvalidValue;
 }
 
 // Padded sizes of the compressed form (values of `vsz` bytes): Mp, Kp, tiles per row.

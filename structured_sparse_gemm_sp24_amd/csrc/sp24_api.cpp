@@ -133,6 +133,34 @@ int sp24_prune_compress(const void* W, int dtype, int64_t M, int64_t K, int64_t 
                                                   static_cast<hipStream_t>(stream)));
 }
 
+int sp24_prune_mask(const void* W, int dtype, int64_t M, int64_t K, int64_t ldw, int keep, int score,
+                    const float* norms, uint8_t* mask, void* W_out, int64_t ldo, void* stream) {
+    if (!W || (!mask && !W_out)) return SP24_ERR_NULL;
+    if (dtype != SP24_BF16 && dtype != SP24_FP16 && dtype != SP24_FP32 && dtype != SP24_I8) return SP24_ERR_DTYPE;
+    if (keep < 1 || keep > 4) return SP24_ERR_ARG;
+    if (score != SP24_SCORE_MAGNITUDE && score != SP24_SCORE_WANDA) return SP24_ERR_ARG;
+    if (score == SP24_SCORE_WANDA) {
+        if (dtype == SP24_I8) return SP24_ERR_DTYPE;
+        if (!norms) return SP24_ERR_NULL;
+    } else if (norms) {
+        return SP24_ERR_ARG;
+    }
+    if (M < 1) return SP24_ERR_SHAPE;
+    int st = check_k(K);
+    if (st != SP24_OK) return st;
+    if (ldw < K || (W_out && ldo < K)) return SP24_ERR_SHAPE;
+    if (M * (K / 16) >= kMaxChunks) return SP24_ERR_SHAPE;
+    const int isz = elem_size(dtype);
+    if (!aligned16(W) || (ldw * isz) % 16 != 0) return SP24_ERR_ALIGN;
+    if (mask && !aligned16(mask)) return SP24_ERR_ALIGN;
+    if (W_out && (!aligned16(W_out) || (ldo * isz) % 16 != 0)) return SP24_ERR_ALIGN;
+    if (norms && !aligned16(norms)) return SP24_ERR_ALIGN;
+    st = check_device();
+    if (st != SP24_OK) return st;
+    return hip_status(sp24::launch_prune_mask(W, dtype, M, K, ldw, keep, score, norms, mask, W_out, ldo,
+                                              static_cast<hipStream_t>(stream)));
+}
+
 int sp24_decompress(const void* values, const uint8_t* meta, int dtype, int64_t M, int64_t K, void* W_out, int64_t ldw,
                     void* stream) {
     if (!values || !meta || !W_out) return SP24_ERR_NULL;

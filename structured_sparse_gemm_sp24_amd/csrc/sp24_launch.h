@@ -40,6 +40,9 @@ hipError_t launch_col_norms(const uint16_t* X, int64_t K, int64_t N, int64_t ldx
 hipError_t launch_prune_compress(const void* W, int dtype, int64_t M, int64_t K, int64_t ldw, int score,
                                  const float* norms, void* values, int val_dtype, uint8_t* meta, hipStream_t s);
 
+hipError_t launch_prune_mask(const void* W, int dtype, int64_t M, int64_t K, int64_t ldw, int keep, int score,
+                             const float* norms, uint8_t* mask, void* W_out, int64_t ldo, hipStream_t s);
+
 hipError_t launch_decompress(const void* values, const uint8_t* meta, int dtype, int64_t M, int64_t K,
                              void* W_out, int64_t ldw, hipStream_t s);
 

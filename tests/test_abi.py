@@ -176,6 +176,24 @@ def test_gemm_i8_fused_validation(lib, args, expect):
     assert lib.sp24_gemm_i8_fused(*args) == expect
 
 
+@pytest.mark.parametrize("args,expect", [
+    # W, dtype, M, K, ldw, keep, score, norms, mask, W_out, ldo, stream
+    ((NULL, BF16, 16, 16, 16, 2, 0, NULL, B, NULL, 16, NULL), sp.SP24_ERR_NULL),
+    ((A, BF16, 16, 16, 16, 2, 0, NULL, NULL, NULL, 16, NULL), sp.SP24_ERR_NULL),   # neither output
+    ((A, BF16, 16, 16, 16, 0, 0, NULL, B, NULL, 16, NULL), sp.SP24_ERR_ARG),       # keep 0
+    ((A, BF16, 16, 16, 16, 5, 0, NULL, B, NULL, 16, NULL), sp.SP24_ERR_ARG),       # keep 5
+    ((A, I32, 16, 16, 16, 2, 0, NULL, B, NULL, 16, NULL), sp.SP24_ERR_DTYPE),
+    ((A, I8, 16, 16, 16, 2, 1, C, B, NULL, 16, NULL), sp.SP24_ERR_DTYPE),          # Wanda on int8
+    ((A, BF16, 16, 16, 16, 2, 0, C, B, NULL, 16, NULL), sp.SP24_ERR_ARG),          # norms with magnitude
+    ((A, BF16, 16, 20, 24, 2, 0, NULL, B, NULL, 24, NULL), sp.SP24_ERR_SHAPE),     # K % 16
+    ((A, BF16, 16, 16, 16, 2, 0, NULL, NULL, C, 8, NULL), sp.SP24_ERR_SHAPE),      # ldo < K
+    ((A, BF16, 16, 16, 16, 2, 0, NULL, MIS, NULL, 16, NULL), sp.SP24_ERR_ALIGN),
+    ((A, BF16, 16, 16, 20, 2, 0, NULL, B, NULL, 16, NULL), sp.SP24_ERR_ALIGN),     # ldw*2 % 16
+])
+def test_prune_mask_validation(lib, args, expect):
+    assert lib.sp24_prune_mask(*args) == expect
+
+
 def test_compressed_bytes(lib):
     vb, mb = ctypes.c_int64(), ctypes.c_int64()
     # rows padded to 16, columns to 128 / value size
