@@ -62,6 +62,9 @@ def _load():
         lib.oracle_meta_offset.restype = I64
         lib.oracle_decompress.argtypes = [P, P, I, I64, I64, P, I64]
         lib.oracle_prune_mask.argtypes = [P, I, I64, I64, I64, I, I, P, P, P, I64]
+        lib.oracle_channel_permutation.argtypes = [P, I, I64, I64, I64, I, P, I, P]
+        lib.oracle_retained.argtypes = [P, I, I64, I64, I64, I, P, P]
+        lib.oracle_retained.restype = ctypes.c_double
         lib.oracle_gemm_bf16.argtypes = [P, P, I64, I64, P, I64, I64, P, I64, P]
         lib.oracle_gemm_i8.argtypes = [P, P, I64, I64, P, I64, I64, P, P, I64, P, P]
         lib.oracle_fp32_to_bf16.argtypes = [ctypes.c_float]
@@ -144,6 +147,32 @@ def prune_mask(W: np.ndarray, dtype: int, keep: int, score: int = MAGNITUDE, nor
         norms = np.ascontiguousarray(_c(norms, np.float32))
     _check(_load().oracle_prune_mask(_ptr(W), dtype, M, K, K, keep, score, _ptr(norms), _ptr(mask), _ptr(out), K))
     return mask, out
+
+
+def channel_permutation(W: np.ndarray, dtype: int, sweeps: int = 1, score: int = MAGNITUDE,
+                        norms: np.ndarray | None = None) -> np.ndarray:
+    """Input-channel permutation before pruning (Orin NN design, Chapter 7, section 3.1 Step 2 and
+    section 6.3): the round-robin pair re-partition search of sp24_oracle.c. Returns perm (int32[K]):
+    permuted column c is original column perm[c]."""
+    W = np.ascontiguousarray(_c(W, _DT_NP[dtype]))
+    M, K = W.shape
+    perm = np.zeros(K, np.int32)
+    if norms is not None:
+        norms = np.ascontiguousarray(_c(norms, np.float32))
+    _check(_load().oracle_channel_permutation(_ptr(W), dtype, M, K, K, score, _ptr(norms), sweeps, _ptr(perm)))
+    return perm
+
+
+def retained(W: np.ndarray, dtype: int, perm: np.ndarray | None = None, score: int = MAGNITUDE,
+             norms: np.ndarray | None = None) -> float:
+    """Sum over rows and groups of the two largest scores per group of the column order perm."""
+    W = np.ascontiguousarray(_c(W, _DT_NP[dtype]))
+    M, K = W.shape
+    if perm is not None:
+        perm = np.ascontiguousarray(np.asarray(perm, np.int32))
+    if norms is not None:
+        norms = np.ascontiguousarray(_c(norms, np.float32))
+    return float(_load().oracle_retained(_ptr(W), dtype, M, K, K, score, _ptr(norms), _ptr(perm)))
 
 
 def meta_bad_nibbles(meta: np.ndarray, M: int, K: int, val_dtype: int) -> int:

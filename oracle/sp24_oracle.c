@@ -335,6 +335,120 @@ int oracle_prune_mask(const void* W, int dtype, int64_t M, int64_t K, int64_t ld
     return OR_OK;
 }
 
+/* ---------------------------------------------------------------- channel permutation [ORIN7 3.1, 6.3] */
+
+/* Orin NN design, Chapter 7, section 3.1 Step 2 and section 6.3: before the mask is computed, permute
+ * the input channels (columns of W, with the matching rows of X) so that large weights share groups of
+ * four and 2:4 pruning keeps more of them; the product is unchanged. The pages name no search; this is
+ * the one the library defines (a reading, see the design notes):
+ *  - the objective of a column order is R = sum over rows m of the retained score in each group: the
+ *    sum of its two largest scores (|w|, or the Wanda fl32(|w|) * norm of the column's original
+ *    channel), accumulated in double precision row by row in increasing m;
+ *  - a sweep is G' - 1 rounds of a round-robin pairing of the G = K/4 groups (G' = G rounded up to
+ *    even; position 0 fixed, positions 1..G'-1 rotated by the round; a group paired with the dummy
+ *    G'-1 >= G sits out); in each round every pair (A = lower group, B = higher) re-partitions its 8
+ *    channels into two groups of four, choosing among the 35 partitions (the channel at A's first slot
+ *    stays in A; A's other 3 are a 3-subset of the remaining 7 slots, in lexicographic order, index 0
+ *    being the current arrangement) the one with the largest pair objective
+ *      S_P = sum_m ( T(A_P, m) + T(B_P, m) ),  T = top-2 sum (fl64(top1 + top2)),
+ *    the earliest index on ties (so nothing moves unless it strictly gains); channels keep their slot
+ *    order inside A_P and B_P;
+ *  - R never decreases.
+ * K must be a multiple of 4 (at least 8). perm_out[c] = original column of permuted column c. */
+static double top2_sum(const double v[4]) {
+    double a = v[0], b = v[1], c = v[2], d = v[3], t;
+    /* sort descending (insertion), then the two largest */
+    if (b > a) { t = a; a = b; b = t; }
+    if (c > b) { t = b; b = c; c = t; if (b > a) { t = a; a = b; b = t; } }
+    if (d > c) { t = c; c = d; d = t; if (c > b) { t = b; b = c; c = t; if (b > a) { t = a; a = b; b = t; } } }
+    return a + b;
+}
+
+static double col_score(const void* W, int dtype, int64_t ldw, int64_t m, int64_t col, int score, const float* norms) {
+    double a = fabs(elem_value(W, dtype, (size_t)m * (size_t)ldw + (size_t)col));
+    if (score == OR_WANDA) {
+        float prod = (float)a * norms[col];
+        return (double)prod;
+    }
+    return a;
+}
+
+/* the 35 partitions: 3-subsets of slots {1..7} in lexicographic order */
+static void partition_subsets(int subs[35][3]) {
+    int n = 0;
+    for (int x = 1; x <= 7; x++)
+        for (int y = x + 1; y <= 7; y++)
+            for (int z = y + 1; z <= 7; z++) { subs[n][0] = x; subs[n][1] = y; subs[n][2] = z; n++; }
+}
+
+int oracle_channel_permutation(const void* W, int dtype, int64_t M, int64_t K, int64_t ldw, int score,
+                               const float* norms, int sweeps, int32_t* perm_out) {
+    if (!W || !perm_out || M < 1 || K < 8 || K % 4 != 0 || ldw < K || sweeps < 0) return OR_EARG;
+    if (dtype != OR_BF16 && dtype != OR_FP16 && dtype != OR_FP32 && dtype != OR_I8) return OR_EARG;
+    if (score == OR_WANDA && (!norms || dtype == OR_I8)) return OR_EARG;
+    if (score != OR_WANDA && score != OR_MAGNITUDE) return OR_EARG;
+    const int G = (int)(K / 4), Ge = G + (G & 1);
+    int subs[35][3];
+    partition_subsets(subs);
+    for (int64_t c = 0; c < K; c++) perm_out[c] = (int32_t)c;
+    for (int sw = 0; sw < sweeps; sw++) {
+        for (int r = 0; r < Ge - 1; r++) {
+#pragma omp parallel for schedule(dynamic)
+            for (int p = 0; p < Ge / 2; p++) {
+                int pa = p, pb = Ge - 1 - p;
+                int ga = pa == 0 ? 0 : 1 + ((pa - 1 + r) % (Ge - 1));
+                int gb = pb == 0 ? 0 : 1 + ((pb - 1 + r) % (Ge - 1));
+                if (ga >= G || gb >= G) continue;
+                if (ga > gb) { int t = ga; ga = gb; gb = t; }
+                int64_t oc[8];
+                for (int i = 0; i < 4; i++) { oc[i] = perm_out[4 * ga + i]; oc[4 + i] = perm_out[4 * gb + i]; }
+                double S[35];
+                for (int t = 0; t < 35; t++) S[t] = 0.0;
+                for (int64_t m = 0; m < M; m++) {
+                    double v[8];
+                    for (int i = 0; i < 8; i++) v[i] = col_score(W, dtype, ldw, m, oc[i], score, norms);
+                    for (int t = 0; t < 35; t++) {
+                        double a[4], b[4];
+                        int inA[8] = {1, 0, 0, 0, 0, 0, 0, 0}, na = 1, nb = 0;
+                        inA[subs[t][0]] = inA[subs[t][1]] = inA[subs[t][2]] = 1;
+                        a[0] = v[0];
+                        for (int i = 1; i < 8; i++) { if (inA[i]) a[na++] = v[i]; else b[nb++] = v[i]; }
+                        S[t] += top2_sum(a) + top2_sum(b);
+                    }
+                }
+                int best = 0;
+                for (int t = 1; t < 35; t++) if (S[t] > S[best]) best = t;
+                if (best != 0) {
+                    int inA[8] = {1, 0, 0, 0, 0, 0, 0, 0}, na = 1, nb = 0;
+                    int64_t na_[4], nb_[4];
+                    inA[subs[best][0]] = inA[subs[best][1]] = inA[subs[best][2]] = 1;
+                    na_[0] = oc[0];
+                    for (int i = 1; i < 8; i++) { if (inA[i]) na_[na++] = oc[i]; else nb_[nb++] = oc[i]; }
+                    for (int i = 0; i < 4; i++) {
+                        perm_out[4 * ga + i] = (int32_t)na_[i];
+                        perm_out[4 * gb + i] = (int32_t)nb_[i];
+                    }
+                }
+            }
+        }
+    }
+    return OR_OK;
+}
+
+/* Retained objective R of a column order (see above), double precision, rows in increasing order and
+ * groups in increasing order within a row. */
+double oracle_retained(const void* W, int dtype, int64_t M, int64_t K, int64_t ldw, int score, const float* norms,
+                       const int32_t* perm) {
+    double R = 0.0;
+    for (int64_t m = 0; m < M; m++)
+        for (int64_t g = 0; g < K / 4; g++) {
+            double v[4];
+            for (int i = 0; i < 4; i++) v[i] = col_score(W, dtype, ldw, m, perm ? perm[4 * g + i] : 4 * g + i, score, norms);
+            R += top2_sum(v);
+        }
+    return R;
+}
+
 /* ---------------------------------------------------------------- metadata check [ORIN7 6.1] */
 
 /* Every nibble of the M x K region must name two distinct positions in ascending order. Returns

@@ -229,6 +229,84 @@ def test_progressive_masks_equal_direct(score):
         cur = out_chain
 
 
+# ----------------------------------------------------------------- channel permutation
+
+
+def _golden_floats(g, key):
+    return [float(x) for x in g[key].split()]
+
+
+def test_permutation_golden_principle():
+    g = read_golden("orin7_permutation.txt")
+    row = np.array(_golden_floats(g, "row"), np.float32)
+    W = np.tile(row, (3, 2))  # K is a multiple of 16: the 8-column row twice
+    r0 = oracle.retained(W, oracle.FP32)
+    perm = oracle.channel_permutation(W, oracle.FP32)
+    r1 = oracle.retained(W, oracle.FP32, perm)
+    f = float(np.float32(0.9)), float(np.float32(0.1))
+    assert r0 == pytest.approx(6 * (3 * f[0] + f[1]), rel=1e-15)
+    assert _golden_floats(g, "retained_before")[0] == pytest.approx(r0 / 6, rel=1e-6)
+    assert r1 == pytest.approx(6 * 4 * f[0], rel=1e-15)
+    assert _golden_floats(g, "retained_after")[0] == pytest.approx(r1 / 6, rel=1e-6)
+    assert sorted(perm.tolist()) == list(range(16))
+    # the page's one-group example keeps both large weights without any permutation
+    ex = np.array(_golden_floats(g, "page_example_row"), np.float32).reshape(1, 4)
+    pos = [int(x) for x in _golden_floats(g, "page_example_kept_positions")]
+    W16 = np.tile(ex, (1, 4))
+    vals, meta, _, _ = compress_rm(W16, oracle.FP32)
+    nib = meta_nibbles(meta, 16)[0, 0]
+    assert [nib & 3, nib >> 2] == pos
+
+
+def test_permutation_two_groups_is_best_partition():
+    """K = 8: one sweep is one round on the single pair, so the result must reach the best of all 35
+    partitions of the 8 channels into two groups of four (enumerated independently here)."""
+    rng = np.random.default_rng(21)
+    for trial in range(20):
+        W = rng.standard_normal((16, 8)).astype(np.float32)
+        a = np.abs(W.astype(np.float64))
+        best = -1.0
+        for A in itertools.combinations(range(8), 4):
+            B = [c for c in range(8) if c not in A]
+            tA = np.sort(a[:, list(A)], axis=1)[:, -2:].sum(axis=1)
+            tB = np.sort(a[:, B], axis=1)[:, -2:].sum(axis=1)
+            best = max(best, float((tA + tB).sum()))
+        perm = oracle.channel_permutation(W, oracle.FP32)
+        assert sorted(perm.tolist()) == list(range(8))
+        r = oracle.retained(W, oracle.FP32, perm)
+        assert r == pytest.approx(best, rel=1e-12), trial
+
+
+@pytest.mark.parametrize("score", [oracle.MAGNITUDE, oracle.WANDA])
+def test_permutation_invariants(score):
+    W = synth.normal_bf16(31, (64, 256))
+    norms = None
+    if score == oracle.WANDA:
+        norms = np.abs(np.random.default_rng(32).standard_normal(256)).astype(np.float32) + 0.1
+    r_prev = oracle.retained(W, oracle.BF16, None, score, norms)
+    for sweeps in (1, 2, 3):
+        perm = oracle.channel_permutation(W, oracle.BF16, sweeps, score, norms)
+        assert sorted(perm.tolist()) == list(range(256))
+        r = oracle.retained(W, oracle.BF16, perm, score, norms)
+        assert r >= r_prev
+        r_prev = r
+    assert r_prev > oracle.retained(W, oracle.BF16, None, score, norms)
+    # equal magnitudes: nothing strictly gains, the order stays
+    same = np.full((8, 64), 0x3F80, np.uint16)
+    assert np.array_equal(oracle.channel_permutation(same, oracle.BF16, 2), np.arange(64))
+
+
+def test_permutation_objective_equals_kept_magnitude():
+    # the magnitude objective is the sum of |kept values| of the 2:4 compression of the permuted W
+    W = synth.normal_bf16(41, (32, 128))
+    perm = oracle.channel_permutation(W, oracle.BF16, 2)
+    Wp = np.ascontiguousarray(W[:, perm])
+    vals, _, _, _ = compress_rm(Wp, oracle.BF16)
+    kept = np.abs(synth.bf16_bits_to_f32(vals).astype(np.float64)).sum()
+    assert oracle.retained(W, oracle.BF16, perm) == pytest.approx(kept, rel=1e-12)
+    assert oracle.retained(Wp, oracle.BF16) == pytest.approx(kept, rel=1e-12)
+
+
 # ----------------------------------------------------------------- invariants on random data
 
 
