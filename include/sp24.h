@@ -134,6 +134,21 @@ int sp24_prune_compress(const void* W, int dtype, int64_t M, int64_t K, int64_t 
 int sp24_prune_mask(const void* W, int dtype, int64_t M, int64_t K, int64_t ldw, int keep, int score,
                     const float* norms, uint8_t* mask, void* W_out, int64_t ldo, void* stream);
 
+/* Input-channel permutation before pruning (Orin NN design, Chapter 7, section 3.1 Step 2 "Channel
+ * Permutation" and section 6.3): writes perm (int32[K], device), an order of W's columns in which 2:4
+ * pruning keeps at least as much score: permuted column c is original column perm[c]. Prune
+ * W[:, perm]; the product is unchanged when X's rows (feature-major; token-major: X's columns) follow
+ * perm, which a model usually applies offline to the previous layer's output channels.
+ *   Objective: the sum over rows and groups of four of the two largest scores (|w|, or Wanda
+ *   fl32(|w|) * norms[original column]), in double precision. Search: `sweeps` sweeps (0..1000) of
+ *   round-robin rounds over pairs of groups; each pair moves to the best of its 35 splits into two
+ *   groups of four only when that strictly increases its objective, so the objective never decreases
+ *   and sweeps = 0 returns the identity. The result is deterministic (the same for any device).
+ *   W: M x K of dtype in {BF16, FP16, FP32, I8}, pitch ldw >= K, K a multiple of 4 (at least 8);
+ *   score/norms as sp24_prune_compress. Asynchronous: sweeps * (ceil(K/8)*2 - 1) launches on stream. */
+int sp24_channel_permutation(const void* W, int dtype, int64_t M, int64_t K, int64_t ldw, int score,
+                             const float* norms, int sweeps, int32_t* perm, void* stream);
+
 /* Inverse of the compression: W_out (M x K of dtype in {BF16, FP16, FP32, I8}, pitch ldw with
  * ldw*sizeof(dtype) % 16 == 0) gets every kept value at its original column and +0 (all-zero bits)
  * at the two pruned columns of every group. dtype is the values' dtype. */

@@ -23,7 +23,8 @@ SP24_FEATURE_MAJOR, SP24_TOKEN_MAJOR = 0, 1
 SP24_ACT_NONE, SP24_ACT_GELU = 0, 1
 
 # every symbol include/sp24.h declares
-EXPORTS = ("sp24_col_norms", "sp24_compressed_bytes", "sp24_prune_compress", "sp24_prune_mask", "sp24_decompress",
+EXPORTS = ("sp24_col_norms", "sp24_compressed_bytes", "sp24_prune_compress", "sp24_prune_mask",
+           "sp24_channel_permutation", "sp24_decompress",
            "sp24_gemm_bf16",
            "sp24_gemm_i8", "sp24_gemm_bf16_ex", "sp24_gemm_i8_ex", "sp24_gemm_i8_fused", "sp24_status_string")
 
@@ -56,6 +57,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sp24_prune_compress.argtypes = [P, I, I64, I64, I64, I, P, P, I, P, P]
     lib.sp24_decompress.argtypes = [P, P, I, I64, I64, P, I64, P]
     lib.sp24_prune_mask.argtypes = [P, I, I64, I64, I64, I, I, P, P, P, I64, P]
+    lib.sp24_channel_permutation.argtypes = [P, I, I64, I64, I64, I, P, I, P, P]
     lib.sp24_gemm_bf16.argtypes = [P, P, I64, I64, P, I64, I64, P, I, I64, P]
     lib.sp24_gemm_i8.argtypes = [P, P, I64, I64, P, I64, I64, P, P, I64, P]
     lib.sp24_gemm_bf16_ex.argtypes = [P, P, I64, I64, P, I64, I64, I64, P, I, I64, I64, I64, I, P]
@@ -170,6 +172,19 @@ def sp24_prune_mask(W: torch.Tensor, keep: int, score: int = SP24_SCORE_MAGNITUD
                                         _stream(W))
     _check("sp24_prune_mask", st)
     return mask, out
+
+
+def sp24_channel_permutation(W: torch.Tensor, sweeps: int = 1, score: int = SP24_SCORE_MAGNITUDE,
+                             norms: torch.Tensor | None = None, perm: torch.Tensor | None = None) -> torch.Tensor:
+    """Input-channel order (int32[K]) in which 2:4 pruning of W[:, perm] keeps at least as much score."""
+    _dev_check(W, norms, perm)
+    M, K = W.shape
+    if perm is None:
+        perm = torch.empty(K, dtype=torch.int32, device=W.device)
+    st = load_library().sp24_channel_permutation(_ptr(W), _TORCH_TO_SP24[W.dtype], M, K, _rows(W, "W"), int(score),
+                                                 _ptr(norms), int(sweeps), _ptr(perm), _stream(W))
+    _check("sp24_channel_permutation", st)
+    return perm
 
 
 def sp24_decompress(values: torch.Tensor, meta: torch.Tensor, M: int, K: int,

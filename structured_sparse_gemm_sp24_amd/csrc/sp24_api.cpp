@@ -161,6 +161,28 @@ int sp24_prune_mask(const void* W, int dtype, int64_t M, int64_t K, int64_t ldw,
                                               static_cast<hipStream_t>(stream)));
 }
 
+int sp24_channel_permutation(const void* W, int dtype, int64_t M, int64_t K, int64_t ldw, int score,
+                             const float* norms, int sweeps, int32_t* perm, void* stream) {
+    if (!W || !perm) return SP24_ERR_NULL;
+    if (dtype != SP24_BF16 && dtype != SP24_FP16 && dtype != SP24_FP32 && dtype != SP24_I8) return SP24_ERR_DTYPE;
+    if (score != SP24_SCORE_MAGNITUDE && score != SP24_SCORE_WANDA) return SP24_ERR_ARG;
+    if (score == SP24_SCORE_WANDA) {
+        if (dtype == SP24_I8) return SP24_ERR_DTYPE;
+        if (!norms) return SP24_ERR_NULL;
+    } else if (norms) {
+        return SP24_ERR_ARG;
+    }
+    if (sweeps < 0 || sweeps > 1000) return SP24_ERR_ARG;
+    if (M < 1 || K < 8 || K % 4 != 0 || ldw < K || K > ((int64_t)1 << 30)) return SP24_ERR_SHAPE;
+    const int isz = elem_size(dtype);
+    if ((reinterpret_cast<uintptr_t>(W) % isz) != 0 || (reinterpret_cast<uintptr_t>(perm) & 3) != 0) return SP24_ERR_ALIGN;
+    if (norms && (reinterpret_cast<uintptr_t>(norms) & 3) != 0) return SP24_ERR_ALIGN;
+    const int st = check_device();
+    if (st != SP24_OK) return st;
+    return hip_status(sp24::launch_channel_permutation(W, dtype, M, K, ldw, score, norms, sweeps, perm,
+                                                       static_cast<hipStream_t>(stream)));
+}
+
 int sp24_decompress(const void* values, const uint8_t* meta, int dtype, int64_t M, int64_t K, void* W_out, int64_t ldw,
                     void* stream) {
     if (!values || !meta || !W_out) return SP24_ERR_NULL;

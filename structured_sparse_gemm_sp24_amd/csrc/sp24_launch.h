@@ -43,6 +43,9 @@ hipError_t launch_prune_compress(const void* W, int dtype, int64_t M, int64_t K,
 hipError_t launch_prune_mask(const void* W, int dtype, int64_t M, int64_t K, int64_t ldw, int keep, int score,
                              const float* norms, uint8_t* mask, void* W_out, int64_t ldo, hipStream_t s);
 
+hipError_t launch_channel_permutation(const void* W, int dtype, int64_t M, int64_t K, int64_t ldw, int score,
+                                      const float* norms, int sweeps, int32_t* perm, hipStream_t s);
+
 hipError_t launch_decompress(const void* values, const uint8_t* meta, int dtype, int64_t M, int64_t K,
                              void* W_out, int64_t ldw, hipStream_t s);
 

@@ -194,6 +194,23 @@ def test_prune_mask_validation(lib, args, expect):
     assert lib.sp24_prune_mask(*args) == expect
 
 
+@pytest.mark.parametrize("args,expect", [
+    # W, dtype, M, K, ldw, score, norms, sweeps, perm, stream
+    ((NULL, BF16, 16, 16, 16, 0, NULL, 1, B, NULL), sp.SP24_ERR_NULL),
+    ((A, BF16, 16, 16, 16, 0, NULL, 1, NULL, NULL), sp.SP24_ERR_NULL),
+    ((A, I32, 16, 16, 16, 0, NULL, 1, B, NULL), sp.SP24_ERR_DTYPE),
+    ((A, BF16, 16, 16, 16, 0, NULL, -1, B, NULL), sp.SP24_ERR_ARG),
+    ((A, BF16, 16, 16, 16, 0, C, 1, B, NULL), sp.SP24_ERR_ARG),        # norms with magnitude
+    ((A, I8, 16, 16, 16, 1, C, 1, B, NULL), sp.SP24_ERR_DTYPE),        # Wanda on int8
+    ((A, BF16, 16, 6, 16, 0, NULL, 1, B, NULL), sp.SP24_ERR_SHAPE),    # K % 4
+    ((A, BF16, 16, 4, 16, 0, NULL, 1, B, NULL), sp.SP24_ERR_SHAPE),    # K < 8
+    ((A, BF16, 16, 16, 8, 0, NULL, 1, B, NULL), sp.SP24_ERR_SHAPE),    # ldw < K
+    ((A, BF16, 16, 16, 16, 0, NULL, 1, ctypes.c_void_p(0x20002), NULL), sp.SP24_ERR_ALIGN),
+])
+def test_channel_permutation_validation(lib, args, expect):
+    assert lib.sp24_channel_permutation(*args) == expect
+
+
 def test_compressed_bytes(lib):
     vb, mb = ctypes.c_int64(), ctypes.c_int64()
     # rows padded to 16, columns to 128 / value size
