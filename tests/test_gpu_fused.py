@@ -3,7 +3,7 @@ optional GELU, and fp32 / bf16 / int8 output, in both layouts and through the ti
 
 Bars: without GELU every step is a single IEEE rounding on both sides, so fp32 output and int8 codes
 are bit-exact and bf16 output is the nearest-even rounding of the oracle's fp32 value. With GELU the
-kernel uses the device erff: fp32 output within 8 * 2^-24 * |y| (+1e-30) of the float64 GELU of the same
+kernel uses the Abramowitz & Stegun 7.1.26 approximation (expanded in 1 - t): fp32 output within 8 * 2^-24 * |y| (+1e-30) of the float64 GELU of the same
 fp32 input; bf16 output equal to the nearest-even rounding of the same kernel's fp32 output; int8 codes
 within 1 of the reference everywhere and equal wherever the reference y / out_scale is farther than the
 error bound from a rounding boundary."""
