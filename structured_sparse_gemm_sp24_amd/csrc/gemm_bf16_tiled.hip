@@ -46,16 +46,27 @@
 namespace sp24 {
 namespace tiled_bf16 {
 
-constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int WM = 128, WN = 128;
-constexpr int FM = WM / 16, FN = WN / 16;
+constexpr int BM = 256, BK = 64;
+constexpr int WM = 128;
+constexpr int FM = WM / 16;
 constexpr int A_BYTES = BM * BK;          // BK/2 bf16 values per row = BK bytes
 constexpr int META_BYTES = BM * BK / 8;   // 4 bits per group of 4
-constexpr int B_BYTES = BK * BN * 2;
-constexpr int B_ROW = BN * 2;             // 512 bytes
-constexpr int STAGE_BYTES = A_BYTES + META_BYTES + B_BYTES;
-constexpr int LOADS_PER_STAGE = 4 + 2 + 8;  // per wave: A, metadata, B
 constexpr int GROUP_M = 8;
+
+// Tile width BN (N columns of a workgroup tile): 256 (waves of 128 x 128), or 128 for token-major X
+// (waves of 128 x 64), which halves a tile's work for shapes whose 256-wide tiles leave most compute
+// units idle in a last partial turn. The narrower stage (34 KB) leaves room for four LDS buffers.
+template <int BN_>
+struct Cfg {
+    static constexpr int BN = BN_, WN = BN_ / 2, FN = WN / 16;
+    static constexpr int B_BYTES = BK * BN * 2;
+    static constexpr int B_ROW = BN * 2;  // feature-major B tile row: 512 bytes
+    static constexpr int STAGE_BYTES = A_BYTES + META_BYTES + B_BYTES;
+    static constexpr int NBUF = BN == 256 ? 3 : 4;  // stage buffers (3 x 50 KB or 4 x 34 KB of LDS)
+    static constexpr int B_LOADS = BN / 32;          // per wave: token-major 8 rows per load, feature-major 2 rows
+    static constexpr int LOADS_PER_STAGE = 4 + 2 + B_LOADS;  // per wave: A, metadata, B
+};
+constexpr int BN = 256, WN = 128, FN = 8, B_ROW = 512;  // the feature-major (and default) tile
 constexpr uint32_t RSRC_FLAGS = 0x00020000u;
 
 // Raw buffer descriptor: base, stride 0, byte count rounded up to whole dwords, format word. The range
@@ -173,9 +184,11 @@ __device__ __forceinline__ LoadOffsets load_offsets(const Args& a, int lane) {
 // block b at (b * tiles + s) * 1 KB of values and * 128 B of metadata). When td is not valid (past the
 // workgroup's last tile) the offsets get bit 31 set, past every record count, so the loads return
 // zeros without memory traffic (and X's record count is 0).
-template <bool TM>
+template <bool TM, int BNT>
 __device__ __forceinline__ void load_stage(uint32_t lds, const Args& a, const TileDesc& td, int s, int wave,
                                            const LoadOffsets& lo) {
+    using C = Cfg<BNT>;
+    static_assert(TM || BNT == 256, "feature-major tiles are 256 wide");
     const int64_t k0 = (int64_t)s * BK;
     const int tiles = (int)((a.K + BK - 1) / BK);
     const uint32_t past = td.valid ? 0u : 0x80000000u;
@@ -192,14 +205,14 @@ __device__ __forceinline__ void load_stage(uint32_t lds, const Args& a, const Ti
         dma4(lds + A_BYTES + b * 128, lo.m + (((uint32_t)(b * tiles + s) * 128u) | past), td.rM);
     }
     if constexpr (TM) {
-        // B: 256 token rows x 128 B; this wave loads rows 64 wave .. +63, 8 rows per instruction.
+        // B: BNT token rows x 128 B; this wave loads rows BNT/4 * wave .. +BNT/4-1, 8 rows per instruction.
         // X's extent from this stage's corner: N - 1 - n0 rows of pitch ldx plus K - k0 elements, so
         // token rows past N read zeros (K is a multiple of 64: no stage reaches past K)
         const i32x4 rB =
             make_rsrc(td.x + td.n0 * a.ldx + k0, td.valid ? ((a.N - 1 - td.n0) * a.ldx + a.K - k0) * 2 : 0);
 #pragma unroll
-        for (int h = 0; h < 8; h++) {
-            const int row = 64 * wave + 8 * h;
+        for (int h = 0; h < C::B_LOADS; h++) {
+            const int row = (BNT / 4) * wave + 8 * h;
             dma16(lds + A_BYTES + META_BYTES + row * 128, lo.b[h & 1] + (uint32_t)(row * a.ldx * 2), rB);
         }
     } else {
@@ -220,7 +233,7 @@ __device__ __forceinline__ void load_stage(uint32_t lds, const Args& a, const Ti
 
 // Tile descriptor of logical tile L (-1: none). Batch entries follow each other; inside one, tiles
 // are walked in groups of GROUP_M tile-rows, column by column inside a group.
-template <bool OUT_FP32>
+template <bool OUT_FP32, int BNT>
 __device__ __forceinline__ TileDesc tile_desc(const Args& a, int L) {
     TileDesc td;
     td.valid = L >= 0;
@@ -236,7 +249,7 @@ __device__ __forceinline__ TileDesc tile_desc(const Args& a, int L) {
     const int in_g = Lc - g * gsize;
     const int tm = first_m + in_g % gm, tn = in_g / gm;
     td.m0 = (int64_t)tm * BM;
-    td.n0 = (int64_t)tn * BN;
+    td.n0 = (int64_t)tn * BNT;
     const int64_t tiles = (a.K + BK - 1) / BK, blocks_left = (a.M + 15) / 16 - td.m0 / 16;
     const int64_t blocks = blocks_left < BM / 16 ? blocks_left : BM / 16;
     td.rA = make_rsrc(reinterpret_cast<const char*>(a.vals) + (td.m0 / 16) * tiles * 1024, blocks * tiles * 1024);
@@ -245,17 +258,18 @@ __device__ __forceinline__ TileDesc tile_desc(const Args& a, int L) {
 }
 
 // Lane-dependent LDS byte offsets used by compute_stage (computed once per kernel).
+template <int FNT>
 struct LaneOffsets {
     int a;        // A fragment of block wm0/16: block * 1024 + lane * 16
     int m;        // metadata of block wm0/16: A_BYTES + block * 128 + lane * 2
-    int b[FN];    // B fragment j, first read (t = 0): row part + swizzled column part; token-major: the
+    int b[FNT];   // B fragment j, first read (t = 0): row part + swizzled column part; token-major: the
                   // two reads of fragment 0 (b[0], b[1]; fragment j adds 16 rows x 128 B)
 };
 
-template <bool TM>
-__device__ __forceinline__ LaneOffsets lane_offsets(int wm0, int wn0, int lane) {
+template <bool TM, int FNT>
+__device__ __forceinline__ LaneOffsets<FNT> lane_offsets(int wm0, int wn0, int lane) {
     const int r = lane & 15, q = lane >> 4;
-    LaneOffsets o;
+    LaneOffsets<FNT> o;
     o.a = (wm0 >> 4) * 1024 + lane * 16;
     o.m = A_BYTES + (wm0 >> 4) * 128 + lane * 2;
     if constexpr (TM) {
@@ -263,7 +277,7 @@ __device__ __forceinline__ LaneOffsets lane_offsets(int wm0, int wn0, int lane) 
         o.b[0] = base + 16 * u;
         o.b[1] = base + 16 * (u ^ 4);
 #pragma unroll
-        for (int j = 2; j < FN; j++) o.b[j] = 0;
+        for (int j = 2; j < FNT; j++) o.b[j] = 0;
         return o;
     }
     // read t of group q covers rows 8q + 4(t&1) + 32(t>>1) + r/4, which all have the row & 3 and
@@ -271,7 +285,7 @@ __device__ __forceinline__ LaneOffsets lane_offsets(int wm0, int wn0, int lane) 
     const int row0 = 8 * q + (r >> 2);
     const int v = ((row0 & 3) << 1) | ((row0 >> 3) & 1);
 #pragma unroll
-    for (int j = 0; j < FN; j++) {
+    for (int j = 0; j < FNT; j++) {
         const int col = wn0 + 16 * j + 4 * (r & 3);  // first of the 4 columns this lane points at
         o.b[j] = A_BYTES + META_BYTES + row0 * B_ROW + (((col >> 4) ^ v) << 5) + 2 * (col & 15);
     }
@@ -295,7 +309,8 @@ __device__ __forceinline__ uint32_t stage_addr(uint32_t buf, int off) {
     return v;
 }
 
-__device__ __forceinline__ void read_a(uint32_t buf, const LaneOffsets& o, AFrags& f) {
+template <int FNT>
+__device__ __forceinline__ void read_a(uint32_t buf, const LaneOffsets<FNT>& o, AFrags& f) {
     const lds_char* pa = (const lds_char*)(size_t)stage_addr(buf, o.a);
     const lds_char* pm = (const lds_char*)(size_t)stage_addr(buf, o.m);
 #pragma unroll
@@ -307,8 +322,8 @@ __device__ __forceinline__ void read_a(uint32_t buf, const LaneOffsets& o, AFrag
 
 // B fragment j (16 columns x 64 k) of the stage in buffer `buf`: four transposing reads, or, token-
 // major, two 16-byte reads of the lane's token row.
-template <bool TM>
-__device__ __forceinline__ bf16x16 read_b(uint32_t buf, const LaneOffsets& o, int j) {
+template <bool TM, int FNT>
+__device__ __forceinline__ bf16x16 read_b(uint32_t buf, const LaneOffsets<FNT>& o, int j) {
     if constexpr (TM) {
         typedef const __attribute__((address_space(3))) u32x4 lds_u32x4;
         const lds_char* p0 = (const lds_char*)(size_t)stage_addr(buf, o.b[0]);
@@ -330,38 +345,41 @@ __device__ __forceinline__ bf16x16 read_b(uint32_t buf, const LaneOffsets& o, in
     return __builtin_bit_cast(bf16x16, b);
 }
 
-__device__ __forceinline__ void mfma_block(f32x4 (&acc)[FM][FN], const AFrags& f, const bf16x16& b, int j) {
+template <int FNT>
+__device__ __forceinline__ void mfma_block(f32x4 (&acc)[FM][FNT], const AFrags& f, const bf16x16& b, int j) {
 #pragma unroll
     for (int i = 0; i < FM; i++)
         acc[i][j] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(f.a[i], b, acc[i][j], (int)f.idx[i], 0, 0);
 }
 
 // One K stage (see the pipeline description in the kernel): stage s of the current tile, g-th stage of
-// the workgroup overall (selects the buffer). The loads it issues are those of stage s + 3 of the
-// current tile or, past its end, stage s + 3 - S of the next one. No branches.
-template <bool TM>
+// the workgroup overall (selects the buffer). The loads it issues are those of stage s + NBUF of the
+// current tile or, past its end, stage s + NBUF - S of the next one. No branches.
+template <bool TM, int BNT>
 __device__ __forceinline__ void stage(uint32_t l0, const Args& a, const TileDesc& cur_t, const TileDesc& next_t, int s,
-                                      int S, int g, f32x4 (&acc)[FM][FN], AFrags& f, bf16x16 (&rb)[4],
-                                      const LaneOffsets& o, int wave, const LoadOffsets& lo) {
-    const int cb = g % 3;
-    const uint32_t cur = l0 + cb * STAGE_BYTES;
-    const uint32_t nxt = l0 + (cb == 2 ? 0 : cb + 1) * STAGE_BYTES;
+                                      int S, int g, f32x4 (&acc)[FM][Cfg<BNT>::FN], AFrags& f, bf16x16 (&rb)[4],
+                                      const LaneOffsets<Cfg<BNT>::FN>& o, int wave, const LoadOffsets& lo) {
+    using C = Cfg<BNT>;
+    constexpr int F = C::FN, NB = C::NBUF;
+    const int cb = g % NB;
+    const uint32_t cur = l0 + cb * C::STAGE_BYTES;
+    const uint32_t nxt = l0 + (cb == NB - 1 ? 0 : cb + 1) * C::STAGE_BYTES;
 #pragma unroll
-    for (int j = 0; j < 6; j++) {
+    for (int j = 0; j < F - 2; j++) {
         rb[(j + 2) & 3] = read_b<TM>(cur, o, j + 2);
         __builtin_amdgcn_sched_barrier(0);
         mfma_block(acc, f, rb[j & 3], j);
         __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of stage g are done
-    wait_vmcnt<LOADS_PER_STAGE>();       // stage g+1 has landed (g+2 may still be in flight)
+    __builtin_amdgcn_s_waitcnt(0xC07F);           // lgkmcnt(0): this wave's reads of stage g are done
+    wait_vmcnt<(NB - 2) * C::LOADS_PER_STAGE>();  // stage g+1 has landed (later ones may be in flight)
     __builtin_amdgcn_s_barrier();
-    const bool here = s + 3 < S;
-    load_stage<TM>(cur, a, here ? cur_t : next_t, here ? s + 3 : s + 3 - S, wave, lo);
+    const bool here = s + NB < S;
+    load_stage<TM, BNT>(cur, a, here ? cur_t : next_t, here ? s + NB : s + NB - S, wave, lo);
     rb[0] = read_b<TM>(nxt, o, 0);
     rb[1] = read_b<TM>(nxt, o, 1);
     __builtin_amdgcn_sched_barrier(0);
-    mfma_block(acc, f, rb[2], 6);
+    mfma_block(acc, f, rb[(F - 2) & 3], F - 2);
     __builtin_amdgcn_sched_barrier(0);
     // last block: once fragment i has been used for the last time, reload it (and its index) from the
     // next stage, so one A register set serves the whole pipeline
@@ -369,7 +387,8 @@ __device__ __forceinline__ void stage(uint32_t l0, const Args& a, const TileDesc
     const lds_char* pm = (const lds_char*)(size_t)stage_addr(nxt, o.m);
 #pragma unroll
     for (int i = 0; i < FM; i++) {
-        acc[i][7] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(f.a[i], rb[3], acc[i][7], (int)f.idx[i], 0, 0);
+        acc[i][F - 1] =
+            __builtin_amdgcn_smfmac_f32_16x16x64_bf16(f.a[i], rb[(F - 1) & 3], acc[i][F - 1], (int)f.idx[i], 0, 0);
         f.a[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(pa + i * 1024));
         f.idx[i] = *reinterpret_cast<const __attribute__((address_space(3))) uint16_t*>(pm + i * 128);
         __builtin_amdgcn_sched_barrier(0);
@@ -388,8 +407,8 @@ __device__ __forceinline__ void stage(uint32_t l0, const Args& a, const TileDesc
 // No LDS is used, so the next tile's loads can land in the stage buffers meanwhile.
 // FULL: the wave's whole 128 x 128 block lies inside Y and vector stores are allowed (then the row
 // offsets of a lane quad fit 32 bits); otherwise every element is bounds-checked.
-template <bool OUT_FP32, bool FULL>
-__device__ __forceinline__ void store_tile(const f32x4 (&acc)[FM][FN], const Args& a, char* y, int64_t mw, int64_t nw,
+template <bool OUT_FP32, bool FULL, int FNT>
+__device__ __forceinline__ void store_tile(const f32x4 (&acc)[FM][FNT], const Args& a, char* y, int64_t mw, int64_t nw,
                                            int lane) {
     constexpr int W = OUT_FP32 ? 4 : 2, ES = OUT_FP32 ? 4 : 2;
     const int q = lane >> 4, r = lane & 15, b = r & 3, a4 = r >> 2;
@@ -400,7 +419,7 @@ __device__ __forceinline__ void store_tile(const f32x4 (&acc)[FM][FN], const Arg
 #pragma unroll
     for (int i = 0; i < FM; i++) {
 #pragma unroll
-        for (int jg = 0; jg < FN / 4; jg++) {
+        for (int jg = 0; jg < FNT / 4; jg++) {
             uint32_t v[4][W];
 #pragma unroll
             for (int f = 0; f < 4; f++) {
@@ -449,15 +468,15 @@ __device__ __forceinline__ void store_tile(const f32x4 (&acc)[FM][FN], const Arg
 // 16x + 4q .. +3 of the 64 M-columns of the fragment group in slot s: each quad's stores then fall in
 // one 128-byte line (bf16) or two (fp32), and each store instruction covers 16 token rows x 64
 // elements, whole lines.
-template <bool OUT_FP32, bool FULL>
-__device__ __forceinline__ void store_tile_tm(const f32x4 (&acc)[FM][FN], const Args& a, char* y, int64_t mw,
+template <bool OUT_FP32, bool FULL, int FNT>
+__device__ __forceinline__ void store_tile_tm(const f32x4 (&acc)[FM][FNT], const Args& a, char* y, int64_t mw,
                                               int64_t nw, int lane) {
     constexpr int ES = OUT_FP32 ? 4 : 2, W = OUT_FP32 ? 4 : 2;
     const int q = lane >> 4, r = lane & 15, x = r & 3, c = r >> 2;
     char* const y0 = y + (nw * a.ldy + mw) * ES;  // wave-uniform corner
     const uint32_t lane_off = FULL ? (uint32_t)((4 * c * a.ldy + 16 * x + 4 * q) * ES) : 0u;
 #pragma unroll
-    for (int j = 0; j < FN; j++) {
+    for (int j = 0; j < FNT; j++) {
 #pragma unroll
         for (int ig = 0; ig < FM / 4; ig++) {
             uint32_t v[4][W];
@@ -501,9 +520,11 @@ __device__ __forceinline__ void store_tile_tm(const f32x4 (&acc)[FM][FN], const 
     }
 }
 
-template <bool OUT_FP32, bool TM>
+template <bool OUT_FP32, bool TM, int BNT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_bf16_tiled_kernel(Args a) {
-    __shared__ __attribute__((aligned(16))) char smem[3 * STAGE_BYTES];
+    using C = Cfg<BNT>;
+    constexpr int NB = C::NBUF, F = C::FN;
+    __shared__ __attribute__((aligned(16))) char smem[NB * C::STAGE_BYTES];
     // LDS byte address of the first stage buffer (for the LDS-destination loads)
     const uint32_t l0 = (uint32_t)(size_t)(__attribute__((address_space(3))) char*)smem;
 
@@ -511,34 +532,37 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     int L = tile_of(a, p, 0);
     if (L < 0) return;  // whole workgroup
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    const int wm0 = (wave >> 1) * WM, wn0 = (wave & 1) * WN;
-    const LaneOffsets o = lane_offsets<TM>(wm0, wn0, lane);
+    const int wm0 = (wave >> 1) * WM, wn0 = (wave & 1) * C::WN;
+    const LaneOffsets<F> o = lane_offsets<TM, F>(wm0, wn0, lane);
     const LoadOffsets lo = load_offsets<TM>(a, lane);
     const int S = (int)((a.K + BK - 1) / BK);
 
-    f32x4 acc[FM][FN];
+    f32x4 acc[FM][F];
 #pragma unroll
     for (int i = 0; i < FM; i++)
 #pragma unroll
-        for (int j = 0; j < FN; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < F; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // Software pipeline over K stages of 64 columns, three LDS buffers (the workgroup's g-th stage in
-    // buffer g % 3), continued across the workgroup's tiles:
-    //  - the loads of stage g+3 go out once every wave has finished reading stage g, i.e. at the
+    // Software pipeline over K stages of 64 columns, NB = 3 (256-wide tiles) or 4 (128-wide) LDS
+    // buffers (the workgroup's g-th stage in buffer g % NB), continued across the workgroup's tiles:
+    //  - the loads of stage g+NB go out once every wave has finished reading stage g, i.e. at the
     //    barrier placed before the last two fragment blocks of stage g, so each stage's loads have
-    //    about two stages of compute to land;
+    //    about NB - 1 stages of compute to land;
     //  - that barrier also publishes stage g+1 (each wave first waits for its own loads of it), so
     //    stage g+1's A fragments, indices and first B fragments are read while the last 16 smfmacs of
     //    stage g run;
     //  - inside a stage, B fragment j+2 is read while fragment j is multiplied (ring of 4).
-    // With fewer than 3 stages per tile every workgroup has one tile (see the launcher).
-    TileDesc cur_t = tile_desc<OUT_FP32>(a, L);
-    TileDesc next_t = tile_desc<OUT_FP32>(a, tile_of(a, p, 1));
-    load_stage<TM>(l0, a, S > 0 ? cur_t : next_t, 0, wave, lo);
-    load_stage<TM>(l0 + STAGE_BYTES, a, S > 1 ? cur_t : next_t, S > 1 ? 1 : 0, wave, lo);
-    wait_vmcnt<LOADS_PER_STAGE>();
+    // With fewer than NB stages per tile every workgroup has one tile (see the launcher), so the
+    // prologue's loads past the tile's stages (next_t invalid) only zero-fill.
+    TileDesc cur_t = tile_desc<OUT_FP32, BNT>(a, L);
+    TileDesc next_t = tile_desc<OUT_FP32, BNT>(a, tile_of(a, p, 1));
+#pragma unroll
+    for (int i = 0; i < NB - 1; i++)
+        load_stage<TM, BNT>(l0 + i * C::STAGE_BYTES, a, S > i ? cur_t : next_t, S > i ? i : 0, wave, lo);
+    wait_vmcnt<(NB - 2) * C::LOADS_PER_STAGE>();
     __builtin_amdgcn_s_barrier();
-    load_stage<TM>(l0 + 2 * STAGE_BYTES, a, S > 2 ? cur_t : next_t, S > 2 ? 2 : 0, wave, lo);
+    load_stage<TM, BNT>(l0 + (NB - 1) * C::STAGE_BYTES, a, S > NB - 1 ? cur_t : next_t, S > NB - 1 ? NB - 1 : 0, wave,
+                        lo);
 
     AFrags fa;
     bf16x16 rb[4];
@@ -547,11 +571,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     rb[1] = read_b<TM>(l0, o, 1);
     int g = 0;
     for (int k = 1;; k++) {
-        for (int s = 0; s < S; s++, g++) stage<TM>(l0, a, cur_t, next_t, s, S, g, acc, fa, rb, o, wave, lo);
+        for (int s = 0; s < S; s++, g++) stage<TM, BNT>(l0, a, cur_t, next_t, s, S, g, acc, fa, rb, o, wave, lo);
         // epilogue from registers; the next tile's first stages are in flight meanwhile
         {
             const int64_t mw = cur_t.m0 + wm0, nw = cur_t.n0 + wn0;
-            const bool full = (mw + WM <= a.M) && (nw + WN <= a.N) && a.y_vec;
+            const bool full = (mw + WM <= a.M) && (nw + C::WN <= a.N) && a.y_vec;
             if constexpr (TM) {
                 if (full)
                     store_tile_tm<OUT_FP32, true>(acc, a, cur_t.y, mw, nw, lane);
@@ -568,9 +592,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
         for (int i = 0; i < FM; i++)
 #pragma unroll
-            for (int j = 0; j < FN; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int j = 0; j < F; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
         cur_t = next_t;
-        next_t = tile_desc<OUT_FP32>(a, tile_of(a, p, k + 1));
+        next_t = tile_desc<OUT_FP32, BNT>(a, tile_of(a, p, k + 1));
     }
     wait_vmcnt<0>();  // the zero-filling loads past the last tile have landed before the workgroup ends
 }
@@ -583,7 +607,7 @@ bool gemm_bf16_tiled_ok(const GemmArgs& g) {
     // (16 * K / 64 * 1 KB); 16-byte aligned rows of X in every batch entry
     const bool x_ok = g.ldx % 8 == 0 && (reinterpret_cast<uintptr_t>(g.X) & 15) == 0 && (g.batch == 1 || g.sx % 8 == 0);
     const bool tm_ok = !g.tm || (g.K % 64 == 0 && g.ldx < ((int64_t)1 << 22));
-    const int64_t tiles = ((g.M + 255) / 256) * ((g.N + 255) / 256) * g.batch;
+    const int64_t tiles = ((g.M + 255) / 256) * ((g.N + 127) / 128) * g.batch;
     return x_ok && tm_ok && g.N > 64 && g.ldx < ((int64_t)1 << 24) && g.K < ((int64_t)1 << 22) && tiles < (1 << 30);
 }
 
@@ -600,14 +624,29 @@ static int device_cus() {
     return cached[dev];
 }
 
-hipError_t launch_gemm_bf16_tiled(const GemmArgs& g, hipStream_t s) {
+// Tile width for a launch. A 128-wide tile (token-major only) costs about C128 of a 256-wide one
+// (measured on MI355X), so it wins when the 256-wide tiles leave a last partial turn that the
+// 128-wide ones fill better: e.g. 3072 x 6304 has 300 tiles of 256 x 256 on 256 compute units (two
+// turns), and 600 of 256 x 128 (three turns of the cheaper tile).
+static int tiled_bn(const GemmArgs& g, int cus) {
+    if (!g.tm) return 256;
+    constexpr double C128 = 0.6;
+    const int64_t tm = (g.M + 255) / 256;
+    const int64_t t256 = tm * ((g.N + 255) / 256) * g.batch, t128 = tm * ((g.N + 127) / 128) * g.batch;
+    const double c256 = (double)((t256 + cus - 1) / cus), c128 = C128 * (double)((t128 + cus - 1) / cus);
+    return c128 < c256 ? 128 : 256;
+}
+
+template <int BNT>
+static hipError_t launch_bn(const GemmArgs& g, hipStream_t s) {
+    using C = tiled_bf16::Cfg<BNT>;
     tiled_bf16::Args a;
     a.vals = static_cast<const uint16_t*>(g.values); a.meta = g.meta;
     a.X = static_cast<const uint16_t*>(g.X); a.Y = g.Y;
     a.M = g.M; a.K = g.K; a.N = g.N; a.ldx = g.ldx; a.ldy = g.ldy;
     a.sxb = g.sx; a.syb = g.sy;
     a.tilesM = (int)((g.M + tiled_bf16::BM - 1) / tiled_bf16::BM);
-    a.tilesN = (int)((g.N + tiled_bf16::BN - 1) / tiled_bf16::BN);
+    a.tilesN = (int)((g.N + BNT - 1) / BNT);
     a.batch = (int)g.batch;
     // vector stores: 16-byte aligned Y rows in every batch entry, and a lane quad's row offsets in 32 bits
     const int64_t es = g.out_fp32 ? 4 : 2;
@@ -615,22 +654,31 @@ hipError_t launch_gemm_bf16_tiled(const GemmArgs& g, hipStream_t s) {
               (g.batch == 1 || (g.sy * es) % 16 == 0) && g.ldy * es * 16 < ((int64_t)1 << 31);
     const int T = a.tilesM * a.tilesN * a.batch;
     const int S = (int)((g.K + tiled_bf16::BK - 1) / tiled_bf16::BK);
-    // one workgroup per compute unit walking several tiles; one tile each when a tile has fewer than
-    // three stages (the cross-tile pipeline then has nothing to overlap)
+    // one workgroup per compute unit walking several tiles; one tile each when a tile has fewer stages
+    // than there are stage buffers (the cross-tile pipeline then has nothing to overlap)
     const int cus = device_cus();
-    const unsigned grid = (unsigned)(S >= 3 && T > cus ? cus : T);
-    if (g.tm) {
+    const unsigned grid = (unsigned)(S >= C::NBUF && T > cus ? cus : T);
+    if constexpr (BNT == 128) {
         if (g.out_fp32)
-            hipLaunchKernelGGL((tiled_bf16::gemm_bf16_tiled_kernel<true, true>), dim3(grid), dim3(256), 0, s, a);
+            hipLaunchKernelGGL((tiled_bf16::gemm_bf16_tiled_kernel<true, true, 128>), dim3(grid), dim3(256), 0, s, a);
         else
-            hipLaunchKernelGGL((tiled_bf16::gemm_bf16_tiled_kernel<false, true>), dim3(grid), dim3(256), 0, s, a);
+            hipLaunchKernelGGL((tiled_bf16::gemm_bf16_tiled_kernel<false, true, 128>), dim3(grid), dim3(256), 0, s, a);
+    } else if (g.tm) {
+        if (g.out_fp32)
+            hipLaunchKernelGGL((tiled_bf16::gemm_bf16_tiled_kernel<true, true, 256>), dim3(grid), dim3(256), 0, s, a);
+        else
+            hipLaunchKernelGGL((tiled_bf16::gemm_bf16_tiled_kernel<false, true, 256>), dim3(grid), dim3(256), 0, s, a);
     } else {
         if (g.out_fp32)
-            hipLaunchKernelGGL((tiled_bf16::gemm_bf16_tiled_kernel<true, false>), dim3(grid), dim3(256), 0, s, a);
+            hipLaunchKernelGGL((tiled_bf16::gemm_bf16_tiled_kernel<true, false, 256>), dim3(grid), dim3(256), 0, s, a);
         else
-            hipLaunchKernelGGL((tiled_bf16::gemm_bf16_tiled_kernel<false, false>), dim3(grid), dim3(256), 0, s, a);
+            hipLaunchKernelGGL((tiled_bf16::gemm_bf16_tiled_kernel<false, false, 256>), dim3(grid), dim3(256), 0, s, a);
     }
     return hipGetLastError();
+}
+
+hipError_t launch_gemm_bf16_tiled(const GemmArgs& g, hipStream_t s) {
+    return tiled_bn(g, device_cus()) == 128 ? launch_bn<128>(g, s) : launch_bn<256>(g, s);
 }
 
 }  // namespace sp24

@@ -46,17 +46,26 @@ def _prune_bit_exact(W_host, dt, score=oracle.MAGNITUDE, norms=None, val_dtype=N
 
 
 def _check_bf16(vd, md, rv, rm, M, X_host, rows):
+    """Both layouts against the oracle's sampled rows: feature-major (X K x N, Y M x N) and token-major
+    (X N x K, Y N x M: the sampled rows are columns of Y), the layout bench.py times by default."""
     K, N = X_host.shape
-    Xd = dev(X_host, "bf16")
     r = torch.from_numpy(rows).cuda()
-    Yf = host_bits(sp.sp24_gemm_bf16(vd, md, M, Xd, out_dtype=torch.float32)[r])
-    Yb = host_bits(sp.sp24_gemm_bf16(vd, md, M, Xd, out_dtype=torch.bfloat16)[r])
     Y64 = oracle.gemm_bf16(rv, rm, X_host, M, rows=rows)
     dense = bf16_to_f64(oracle.decompress(rv, rm, oracle.BF16, M, K)[rows])
     bound = fp32_sum_bound(np.abs(dense) @ np.abs(bf16_to_f64(X_host)), K)
-    assert np.all(np.abs(Yf.astype(np.float64) - Y64) <= bound)
-    assert frob_rel(Yf, Y64) <= 1e-3
-    assert np.array_equal(Yb, synth.f32_to_bf16_bits(Yf))
+    for layout in ("feature", "token"):
+        if layout == "feature":
+            Xd = dev(X_host, "bf16")
+            pick = lambda Y: Y[r]
+        else:
+            Xd = dev(np.ascontiguousarray(X_host.T), "bf16")
+            pick = lambda Y: Y[:, r].t().contiguous()
+        Yf = host_bits(pick(sp.sp24_gemm_bf16_ex(vd, md, M, Xd, layout=layout, out_dtype=torch.float32)))
+        Yb = host_bits(pick(sp.sp24_gemm_bf16_ex(vd, md, M, Xd, layout=layout, out_dtype=torch.bfloat16)))
+        assert np.all(np.abs(Yf.astype(np.float64) - Y64) <= bound), layout
+        assert frob_rel(Yf, Y64) <= 1e-3, layout
+        assert np.array_equal(Yb, synth.f32_to_bf16_bits(Yf)), layout
+        del Xd
 
 
 def test_single_linear_256():
