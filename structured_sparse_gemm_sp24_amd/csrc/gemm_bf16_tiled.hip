@@ -612,7 +612,7 @@ bool gemm_bf16_tiled_ok(const GemmArgs& g) {
 }
 
 // Number of compute units of the current device (cached per device).
-static int device_cus() {
+int device_cus() {
     static int cached[64] = {0};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
@@ -624,13 +624,14 @@ static int device_cus() {
     return cached[dev];
 }
 
-// Tile width for a launch. A 128-wide tile (token-major only) costs about C128 of a 256-wide one
-// (measured on MI355X), so it wins when the 256-wide tiles leave a last partial turn that the
-// 128-wide ones fill better: e.g. 3072 x 6304 has 300 tiles of 256 x 256 on 256 compute units (two
+// Tile width for a launch of either tiled GEMM. A 128-wide tile (token-major only) costs about C128 of
+// a 256-wide one (measured on MI355X), so it wins when the 256-wide tiles leave a last partial turn that
+// the 128-wide ones fill better: e.g. 3072 x 6304 has 300 tiles of 256 x 256 on 256 compute units (two
 // turns), and 600 of 256 x 128 (three turns of the cheaper tile).
-static int tiled_bn(const GemmArgs& g, int cus) {
+int tiled_tile_width(const GemmArgs& g) {
     if (!g.tm) return 256;
     constexpr double C128 = 0.6;
+    const int64_t cus = device_cus();
     const int64_t tm = (g.M + 255) / 256;
     const int64_t t256 = tm * ((g.N + 255) / 256) * g.batch, t128 = tm * ((g.N + 127) / 128) * g.batch;
     const double c256 = (double)((t256 + cus - 1) / cus), c128 = C128 * (double)((t128 + cus - 1) / cus);
@@ -678,7 +679,7 @@ static hipError_t launch_bn(const GemmArgs& g, hipStream_t s) {
 }
 
 hipError_t launch_gemm_bf16_tiled(const GemmArgs& g, hipStream_t s) {
-    return tiled_bn(g, device_cus()) == 128 ? launch_bn<128>(g, s) : launch_bn<256>(g, s);
+    return tiled_tile_width(g) == 128 ? launch_bn<128>(g, s) : launch_bn<256>(g, s);
 }
 
 }  // namespace sp24

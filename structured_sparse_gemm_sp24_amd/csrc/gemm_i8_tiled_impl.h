@@ -40,18 +40,27 @@
 namespace sp24 {
 namespace tiled_i8 {
 
-constexpr int BM = 256, BN = 256, BK = 128;
-constexpr int WM = 128, WN = 128;
-constexpr int FM = WM / 16, FN = WN / 16;
+constexpr int BM = 256, BK = 128;
+constexpr int WM = 128;
+constexpr int FM = WM / 16;
 constexpr int A_BYTES = BM * 64;          // 64 kept int8 per row per stage
 constexpr int META_BYTES = BM * 16;       // 64 kept values x 2 bits = 16 bytes per row
-constexpr int B_ROW = BN;                 // 256 bytes
-constexpr int B_BYTES = BK * B_ROW;
-constexpr int STAGE_BYTES = A_BYTES + META_BYTES + B_BYTES;
-constexpr int LOADS_PER_STAGE = 4 + 1 + 8;  // per wave: A, metadata, B
 constexpr int GROUP_M = 8;
 constexpr uint32_t RSRC_FLAGS = 0x00020000u;
-static_assert(3 * STAGE_BYTES <= 160 * 1024, "three stages fit in LDS");
+constexpr int B_ROW = 256;                // feature-major B tile row: 256 int8 columns
+
+// Tile width BN: 256 (waves of 128 x 128, three 52 KB stage buffers), or 128 for token-major X (waves
+// of 128 x 64, four 36 KB buffers), chosen per launch (tiled_tile_width).
+template <int BN_>
+struct Cfg {
+    static constexpr int BN = BN_, WN = BN_ / 2, FN = WN / 16;
+    static constexpr int B_BYTES = BK * BN;  // token-major: BN rows x 128 B; feature-major: 128 rows x BN B
+    static constexpr int STAGE_BYTES = A_BYTES + META_BYTES + B_BYTES;
+    static constexpr int NBUF = BN == 256 ? 3 : 4;
+    static constexpr int B_LOADS = BN / 32;  // per wave
+    static constexpr int LOADS_PER_STAGE = 4 + 1 + B_LOADS;  // per wave: A, metadata, B
+    static_assert(NBUF * STAGE_BYTES <= 160 * 1024, "the stage buffers fit in LDS");
+};
 
 // Raw buffer descriptor over `bytes` bytes rounded up to whole dwords: the range check returns a
 // dword only when all of it is below the record count, and the rounding keeps the last partial dword
@@ -162,9 +171,10 @@ __device__ __forceinline__ LoadOffsets load_offsets(const Args& a, int lane, int
 
 // This wave's share of the loads of stage s of tile td into the buffer at LDS address `lds`. When td
 // is not valid the offsets get bit 31 set (beyond every record count): zeros, no memory traffic.
-template <bool TM>
+template <bool TM, int BNT>
 __device__ __forceinline__ void load_stage(uint32_t lds, const Args& a, const TileDesc& td, int s, int wave,
                                            const LoadOffsets& lo) {
+    static_assert(TM || BNT == 256, "feature-major tiles are 256 wide");
     const int64_t k0 = (int64_t)s * BK;
     const int tiles = (int)((a.K + BK - 1) / BK);
     const uint32_t past = td.valid ? 0u : 0x80000000u;
@@ -176,12 +186,13 @@ __device__ __forceinline__ void load_stage(uint32_t lds, const Args& a, const Ti
     // metadata of blocks 4 wave .. 4 wave + 3 (one 256 B tile each) in one instruction
     dma16(lds + A_BYTES + 4 * wave * 256, lo.m + (((uint32_t)(4 * wave * tiles + s) * 256u) | past), td.rM);
     if constexpr (TM) {
-        // token rows 64 wave .. +63 of the tile, 8 per load; X's extent from the wave's first row:
-        // rows past N read zeros (K is a multiple of 128: no stage reaches past K)
-        const int64_t n1 = td.n0 + 64 * wave;
+        // token rows BNT/4 * wave .. +BNT/4-1 of the tile, 8 per load; X's extent from the wave's first
+        // row: rows past N read zeros (K is a multiple of 128: no stage reaches past K)
+        const int64_t n1 = td.n0 + (BNT / 4) * wave;
         const i32x4 rB = make_rsrc(td.x + n1 * a.ldx + k0, td.valid ? (a.N - 1 - n1) * a.ldx + a.K - k0 : 0);
 #pragma unroll
-        for (int h = 0; h < 8; h++) dma16(lds + A_BYTES + META_BYTES + (64 * wave + 8 * h) * 128, lo.b[h], rB);
+        for (int h = 0; h < Cfg<BNT>::B_LOADS; h++)
+            dma16(lds + A_BYTES + META_BYTES + ((BNT / 4) * wave + 8 * h) * 128, lo.b[h], rB);
     } else {
         // X's exact extent from this stage's corner, rounded up to whole dwords (see make_rsrc)
         const i32x4 rB = make_rsrc(td.x + k0 * a.ldx + td.n0, td.valid ? (a.K - 1 - k0) * a.ldx + a.N - td.n0 : 0);
@@ -192,6 +203,7 @@ __device__ __forceinline__ void load_stage(uint32_t lds, const Args& a, const Ti
 
 // Descriptor of logical tile L (-1: none); batch entries follow each other, and inside one tiles are
 // walked in groups of GROUP_M tile-rows.
+template <int BNT>
 __device__ __forceinline__ TileDesc tile_desc(const Args& a, int L) {
     TileDesc td;
     td.valid = L >= 0;
@@ -207,7 +219,7 @@ __device__ __forceinline__ TileDesc tile_desc(const Args& a, int L) {
     const int in_g = Lc - g * gsize;
     const int tm = first_m + in_g % gm, tn = in_g / gm;
     td.m0 = (int64_t)tm * BM;
-    td.n0 = (int64_t)tn * BN;
+    td.n0 = (int64_t)tn * BNT;
     const int64_t tiles = (a.K + BK - 1) / BK, blocks_left = (a.M + 15) / 16 - td.m0 / 16;
     const int64_t blocks = blocks_left < BM / 16 ? blocks_left : BM / 16;
     td.rA = make_rsrc(reinterpret_cast<const char*>(a.vals) + (td.m0 / 16) * tiles * 1024, blocks * tiles * 1024);
@@ -215,16 +227,17 @@ __device__ __forceinline__ TileDesc tile_desc(const Args& a, int L) {
     return td;
 }
 
+template <int FNT>
 struct LaneOffsets {
     int a;       // A fragment of block wm0/16: block * 1024 + lane * 16
     int m;       // metadata: A_BYTES + block * 256 + lane * 4
-    int b[FN];   // B fragment j, first read (t = 0); token-major: the two reads of fragment 0
+    int b[FNT];   // B fragment j, first read (t = 0); token-major: the two reads of fragment 0
 };
 
-template <bool TM>
-__device__ __forceinline__ LaneOffsets lane_offsets(int wm0, int wn0, int lane) {
+template <bool TM, int FNT>
+__device__ __forceinline__ LaneOffsets<FNT> lane_offsets(int wm0, int wn0, int lane) {
     const int r = lane & 15, q = lane >> 4;
-    LaneOffsets o;
+    LaneOffsets<FNT> o;
     o.a = (wm0 >> 4) * 1024 + lane * 16;
     o.m = A_BYTES + (wm0 >> 4) * 256 + lane * 4;
     if constexpr (TM) {
@@ -232,7 +245,7 @@ __device__ __forceinline__ LaneOffsets lane_offsets(int wm0, int wn0, int lane) 
         o.b[0] = base + 16 * u;
         o.b[1] = base + 16 * (u ^ 4);
 #pragma unroll
-        for (int j = 2; j < FN; j++) o.b[j] = 0;
+        for (int j = 2; j < FNT; j++) o.b[j] = 0;
         return o;
     }
     // read t of group q covers rows 16q + 8(t&1) + 64(t>>1) + r/2, which share row & 7 and
@@ -240,7 +253,7 @@ __device__ __forceinline__ LaneOffsets lane_offsets(int wm0, int wn0, int lane) 
     const int row0 = 16 * q + (r >> 1);
     const int f = bswz(row0);
 #pragma unroll
-    for (int j = 0; j < FN; j++) {
+    for (int j = 0; j < FNT; j++) {
         const int unit = (wn0 >> 4) + j;  // 16 columns = one 16-byte unit
         o.b[j] = A_BYTES + META_BYTES + row0 * B_ROW + ((unit ^ f) << 4) + 8 * (r & 1);
     }
@@ -262,7 +275,8 @@ __device__ __forceinline__ uint32_t stage_addr(uint32_t buf, int off) {
     return v;
 }
 
-__device__ __forceinline__ void read_a(uint32_t buf, const LaneOffsets& o, AFrags& f) {
+template <int FNT>
+__device__ __forceinline__ void read_a(uint32_t buf, const LaneOffsets<FNT>& o, AFrags& f) {
     const lds_char* pa = (const lds_char*)(size_t)stage_addr(buf, o.a);
     const lds_char* pm = (const lds_char*)(size_t)stage_addr(buf, o.m);
 #pragma unroll
@@ -276,8 +290,8 @@ typedef int i32x2 __attribute__((ext_vector_type(2)));
 
 // B fragment j (16 columns x 128 k): four transposing reads of 8 k each, or, token-major, two 16-byte
 // reads of the lane's token row.
-template <bool TM>
-__device__ __forceinline__ i32x8 read_b(uint32_t buf, const LaneOffsets& o, int j) {
+template <bool TM, int FNT>
+__device__ __forceinline__ i32x8 read_b(uint32_t buf, const LaneOffsets<FNT>& o, int j) {
     if constexpr (TM) {
         typedef const __attribute__((address_space(3))) i32x4 lds_i32x4;
         const lds_char* p0 = (const lds_char*)(size_t)stage_addr(buf, o.b[0]);
@@ -298,7 +312,8 @@ __device__ __forceinline__ i32x8 read_b(uint32_t buf, const LaneOffsets& o, int 
     return b;
 }
 
-__device__ __forceinline__ void mfma_block(i32x4 (&acc)[FM][FN], const AFrags& f, const i32x8& b, int j) {
+template <int FNT>
+__device__ __forceinline__ void mfma_block(i32x4 (&acc)[FM][FNT], const AFrags& f, const i32x8& b, int j) {
 #pragma unroll
     for (int i = 0; i < FM; i++)
         acc[i][j] = __builtin_amdgcn_smfmac_i32_16x16x128_i8(f.a[i], b, acc[i][j], (int)f.idx[i], 0, 0);
@@ -306,37 +321,40 @@ __device__ __forceinline__ void mfma_block(i32x4 (&acc)[FM][FN], const AFrags& f
 
 // One K stage: stage s of the current tile, the workgroup's g-th stage (selects the buffer). B
 // fragments are read two blocks ahead (ring of 4); before the last two blocks the barrier publishes
-// stage g+1 and the loads of stage s+3 of this tile (or s+3-S of the next) go into this buffer; the next
-// stage's A fragments are reloaded one by one inside the last block. No branches.
-template <bool TM>
+// stage g+1 and the loads of stage s+NBUF of this tile (or s+NBUF-S of the next) go into this buffer; the
+// next stage's A fragments are reloaded one by one inside the last block. No branches.
+template <bool TM, int BNT>
 __device__ __forceinline__ void stage(uint32_t l0, const Args& a, const TileDesc& cur_t, const TileDesc& next_t, int s,
-                                      int S, int g, i32x4 (&acc)[FM][FN], AFrags& f, i32x8 (&rb)[4],
-                                      const LaneOffsets& o, int wave, const LoadOffsets& lo) {
-    const int cb = g % 3;
-    const uint32_t cur = l0 + cb * STAGE_BYTES;
-    const uint32_t nxt = l0 + (cb == 2 ? 0 : cb + 1) * STAGE_BYTES;
+                                      int S, int g, i32x4 (&acc)[FM][Cfg<BNT>::FN], AFrags& f, i32x8 (&rb)[4],
+                                      const LaneOffsets<Cfg<BNT>::FN>& o, int wave, const LoadOffsets& lo) {
+    using C = Cfg<BNT>;
+    constexpr int F = C::FN, NB = C::NBUF;
+    const int cb = g % NB;
+    const uint32_t cur = l0 + cb * C::STAGE_BYTES;
+    const uint32_t nxt = l0 + (cb == NB - 1 ? 0 : cb + 1) * C::STAGE_BYTES;
 #pragma unroll
-    for (int j = 0; j < 6; j++) {
+    for (int j = 0; j < F - 2; j++) {
         rb[(j + 2) & 3] = read_b<TM>(cur, o, j + 2);
         __builtin_amdgcn_sched_barrier(0);
         mfma_block(acc, f, rb[j & 3], j);
         __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of stage g are done
-    wait_vmcnt<LOADS_PER_STAGE>();       // stage g+1 has landed
+    __builtin_amdgcn_s_waitcnt(0xC07F);           // lgkmcnt(0): this wave's reads of stage g are done
+    wait_vmcnt<(NB - 2) * C::LOADS_PER_STAGE>();  // stage g+1 has landed
     __builtin_amdgcn_s_barrier();
-    const bool here = s + 3 < S;
-    load_stage<TM>(cur, a, here ? cur_t : next_t, here ? s + 3 : s + 3 - S, wave, lo);
+    const bool here = s + NB < S;
+    load_stage<TM, BNT>(cur, a, here ? cur_t : next_t, here ? s + NB : s + NB - S, wave, lo);
     rb[0] = read_b<TM>(nxt, o, 0);
     rb[1] = read_b<TM>(nxt, o, 1);
     __builtin_amdgcn_sched_barrier(0);
-    mfma_block(acc, f, rb[2], 6);
+    mfma_block(acc, f, rb[(F - 2) & 3], F - 2);
     __builtin_amdgcn_sched_barrier(0);
     const lds_char* pa = (const lds_char*)(size_t)stage_addr(nxt, o.a);
     const lds_char* pm = (const lds_char*)(size_t)stage_addr(nxt, o.m);
 #pragma unroll
     for (int i = 0; i < FM; i++) {
-        acc[i][7] = __builtin_amdgcn_smfmac_i32_16x16x128_i8(f.a[i], rb[3], acc[i][7], (int)f.idx[i], 0, 0);
+        acc[i][F - 1] =
+            __builtin_amdgcn_smfmac_i32_16x16x128_i8(f.a[i], rb[(F - 1) & 3], acc[i][F - 1], (int)f.idx[i], 0, 0);
         f.a[i] = *reinterpret_cast<const __attribute__((address_space(3))) i32x4*>(pa + i * 1024);
         f.idx[i] = *reinterpret_cast<const __attribute__((address_space(3))) uint32_t*>(pm + i * 256);
         __builtin_amdgcn_sched_barrier(0);
@@ -420,8 +438,8 @@ __device__ __forceinline__ void row_params(const Args& a, int64_t m, bool full, 
 
 // FULL: the wave's whole 128 x 128 block lies inside Y and vector stores are allowed (then the row
 // offsets of a lane quad fit 32 bits); otherwise every element is bounds-checked.
-template <int OUT, int EPI, bool FULL>
-__device__ __forceinline__ void store_tile(const i32x4 (&acc)[FM][FN], const Args& a, char* y, int64_t mw, int64_t nw,
+template <int OUT, int EPI, bool FULL, int FNT>
+__device__ __forceinline__ void store_tile(const i32x4 (&acc)[FM][FNT], const Args& a, char* y, int64_t mw, int64_t nw,
                                            int lane) {
     constexpr int ES = OutTraits<OUT>::ES, W = OutTraits<OUT>::W;
     const int q = lane >> 4, r = lane & 15, b = r & 3, a4 = r >> 2;
@@ -434,7 +452,7 @@ __device__ __forceinline__ void store_tile(const i32x4 (&acc)[FM][FN], const Arg
         float sc[4], bi[4];
         row_params<OUT, EPI>(a, mw + 16 * i + 4 * q, FULL, sc, bi);  // accumulator rows 4q .. 4q+3
 #pragma unroll
-        for (int jg = 0; jg < FN / 4; jg++) {
+        for (int jg = 0; jg < FNT / 4; jg++) {
             uint32_t v[4][W];
 #pragma unroll
             for (int f = 0; f < 4; f++) {
@@ -478,8 +496,8 @@ __device__ __forceinline__ void store_tile(const i32x4 (&acc)[FM][FN], const Arg
 // value pipeline and is 4 consecutive elements of token row n. As in the bf16 kernel, a quad transpose
 // across four row fragments gives each lane quad one token row (elements 16x + 4q .. +3 of 64 M-columns
 // in lane 4c + x), so each store instruction covers 16 token rows x 64 elements.
-template <int OUT, int EPI, bool FULL>
-__device__ __forceinline__ void store_tile_tm(const i32x4 (&acc)[FM][FN], const Args& a, char* y, int64_t mw,
+template <int OUT, int EPI, bool FULL, int FNT>
+__device__ __forceinline__ void store_tile_tm(const i32x4 (&acc)[FM][FNT], const Args& a, char* y, int64_t mw,
                                               int64_t nw, int lane) {
     constexpr int ES = OutTraits<OUT>::ES, W = OutTraits<OUT>::W;
     const int q = lane >> 4, r = lane & 15, x = r & 3, c = r >> 2;
@@ -491,7 +509,7 @@ __device__ __forceinline__ void store_tile_tm(const i32x4 (&acc)[FM][FN], const 
 #pragma unroll
         for (int f = 0; f < 4; f++) row_params<OUT, EPI>(a, mw + 16 * (4 * ig + f) + 4 * q, FULL, sc[f], bi[f]);
 #pragma unroll
-        for (int j = 0; j < FN; j++) {
+        for (int j = 0; j < FNT; j++) {
             uint32_t v[4][W];
 #pragma unroll
             for (int f = 0; f < 4; f++) {
@@ -517,35 +535,40 @@ __device__ __forceinline__ void store_tile_tm(const i32x4 (&acc)[FM][FN], const 
     }
 }
 
-template <int OUT, bool TM, int EPI>
+template <int OUT, bool TM, int EPI, int BNT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_i8_tiled_kernel(Args a) {
-    __shared__ __attribute__((aligned(16))) char smem[3 * STAGE_BYTES];
+    using C = Cfg<BNT>;
+    constexpr int NB = C::NBUF, F = C::FN;
+    __shared__ __attribute__((aligned(16))) char smem[NB * C::STAGE_BYTES];
     const uint32_t l0 = (uint32_t)(size_t)(__attribute__((address_space(3))) char*)smem;
 
     const int p = blockIdx.x;
     const int L = tile_of(a, p, 0);
     if (L < 0) return;  // whole workgroup
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    const int wm0 = (wave >> 1) * WM, wn0 = (wave & 1) * WN;
-    const LaneOffsets o = lane_offsets<TM>(wm0, wn0, lane);
+    const int wm0 = (wave >> 1) * WM, wn0 = (wave & 1) * C::WN;
+    const LaneOffsets<F> o = lane_offsets<TM, F>(wm0, wn0, lane);
     const LoadOffsets lo = load_offsets<TM>(a, lane, wave);
     const int S = (int)((a.K + BK - 1) / BK);
 
-    i32x4 acc[FM][FN];
+    i32x4 acc[FM][F];
 #pragma unroll
     for (int i = 0; i < FM; i++)
 #pragma unroll
-        for (int j = 0; j < FN; j++) acc[i][j] = i32x4{0, 0, 0, 0};
+        for (int j = 0; j < F; j++) acc[i][j] = i32x4{0, 0, 0, 0};
 
-    // three-stage pipeline continued across the workgroup's tiles (see stage()); with fewer than 3
-    // stages per tile every workgroup has one tile (see the launcher)
-    TileDesc cur_t = tile_desc(a, L);
-    TileDesc next_t = tile_desc(a, tile_of(a, p, 1));
-    load_stage<TM>(l0, a, S > 0 ? cur_t : next_t, 0, wave, lo);
-    load_stage<TM>(l0 + STAGE_BYTES, a, S > 1 ? cur_t : next_t, S > 1 ? 1 : 0, wave, lo);
-    wait_vmcnt<LOADS_PER_STAGE>();
+    // NB-stage pipeline continued across the workgroup's tiles (see stage()); with fewer than NB
+    // stages per tile every workgroup has one tile (see the launcher), so the prologue's loads past
+    // the tile's stages (next_t invalid) only zero-fill
+    TileDesc cur_t = tile_desc<BNT>(a, L);
+    TileDesc next_t = tile_desc<BNT>(a, tile_of(a, p, 1));
+#pragma unroll
+    for (int i = 0; i < NB - 1; i++)
+        load_stage<TM, BNT>(l0 + i * C::STAGE_BYTES, a, S > i ? cur_t : next_t, S > i ? i : 0, wave, lo);
+    wait_vmcnt<(NB - 2) * C::LOADS_PER_STAGE>();
     __builtin_amdgcn_s_barrier();
-    load_stage<TM>(l0 + 2 * STAGE_BYTES, a, S > 2 ? cur_t : next_t, S > 2 ? 2 : 0, wave, lo);
+    load_stage<TM, BNT>(l0 + (NB - 1) * C::STAGE_BYTES, a, S > NB - 1 ? cur_t : next_t, S > NB - 1 ? NB - 1 : 0, wave,
+                        lo);
 
     AFrags fa;
     i32x8 rb[4];
@@ -554,10 +577,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     rb[1] = read_b<TM>(l0, o, 1);
     int g = 0;
     for (int k = 1;; k++) {
-        for (int s = 0; s < S; s++, g++) stage<TM>(l0, a, cur_t, next_t, s, S, g, acc, fa, rb, o, wave, lo);
+        for (int s = 0; s < S; s++, g++) stage<TM, BNT>(l0, a, cur_t, next_t, s, S, g, acc, fa, rb, o, wave, lo);
         {
             const int64_t mw = cur_t.m0 + wm0, nw = cur_t.n0 + wn0;
-            const bool full = (mw + WM <= a.M) && (nw + WN <= a.N) && a.y_vec;
+            const bool full = (mw + WM <= a.M) && (nw + C::WN <= a.N) && a.y_vec;
             if constexpr (TM) {
                 if (full)
                     store_tile_tm<OUT, EPI, true>(acc, a, cur_t.y, mw, nw, lane);
@@ -574,17 +597,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
         for (int i = 0; i < FM; i++)
 #pragma unroll
-            for (int j = 0; j < FN; j++) acc[i][j] = i32x4{0, 0, 0, 0};
+            for (int j = 0; j < F; j++) acc[i][j] = i32x4{0, 0, 0, 0};
         cur_t = next_t;
-        next_t = tile_desc(a, tile_of(a, p, k + 1));
+        next_t = tile_desc<BNT>(a, tile_of(a, p, k + 1));
     }
     wait_vmcnt<0>();  // the zero-filling loads past the last tile have landed before the workgroup ends
 }
 
-// Launch for one output kind (instantiated in gemm_i8_tiled*.hip, one output kind per file so they
-// compile in parallel): grid, arguments, and the layout x epilogue variant.
-template <int OUT>
-hipError_t launch_out(const GemmArgs& g, hipStream_t s) {
+template <int OUT, bool TMV, int BNT>
+void launch_epi(int epi, dim3 grid, dim3 block, hipStream_t s, const Args& a) {
+    switch (epi) {
+    case 0: hipLaunchKernelGGL((gemm_i8_tiled_kernel<OUT, TMV, 0, BNT>), grid, block, 0, s, a); break;
+    case 1: if constexpr (OUT != OUT_I32) hipLaunchKernelGGL((gemm_i8_tiled_kernel<OUT, TMV, 1, BNT>), grid, block, 0, s, a); break;
+    case 2: if constexpr (OUT != OUT_I32) hipLaunchKernelGGL((gemm_i8_tiled_kernel<OUT, TMV, 2, BNT>), grid, block, 0, s, a); break;
+    default: if constexpr (OUT != OUT_I32) hipLaunchKernelGGL((gemm_i8_tiled_kernel<OUT, TMV, 3, BNT>), grid, block, 0, s, a); break;
+    }
+}
+
+// Launch for one output kind and tile width (instantiated in gemm_i8_tiled*.hip, one output kind per
+// file so they compile in parallel): grid, arguments, and the layout x epilogue variant.
+template <int OUT, int BNT>
+hipError_t launch_bn(const GemmArgs& g, hipStream_t s) {
+    using C = Cfg<BNT>;
     Args a;
     a.vals = static_cast<const int8_t*>(g.values); a.meta = g.meta;
     a.X = static_cast<const int8_t*>(g.X); a.scale = g.scale; a.bias = g.bias; a.Y = g.Y;
@@ -592,7 +626,7 @@ hipError_t launch_out(const GemmArgs& g, hipStream_t s) {
     a.inv_scale = g.inv_scale; a.gelu = g.gelu;
     a.sxb = g.sx; a.syb = g.sy;
     a.tilesM = (int)((g.M + BM - 1) / BM);
-    a.tilesN = (int)((g.N + BN - 1) / BN);
+    a.tilesN = (int)((g.N + BNT - 1) / BNT);
     a.batch = (int)g.batch;
     constexpr int64_t es = OutTraits<OUT>::ES;
     a.es = (int)es;
@@ -601,34 +635,25 @@ hipError_t launch_out(const GemmArgs& g, hipStream_t s) {
               (g.batch == 1 || (g.sy * es) % 16 == 0) && g.ldy * es * 16 < ((int64_t)1 << 31);
     const int T = a.tilesM * a.tilesN * a.batch;
     const int S = (int)((g.K + BK - 1) / BK);
-    int cus = 0, dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
-                                                 hipSuccess || cus <= 0)
-        cus = 256;
-    // one workgroup per compute unit walking several tiles; one tile each when a tile has fewer than
-    // three stages (the cross-tile pipeline then has nothing to overlap)
-    const dim3 grid((unsigned)(S >= 3 && T > cus ? cus : T)), block(256);
-    // the epilogue variant (bias, GELU) is a compile-time choice: GELU's erff, and even a per-element
-    // bias select, would otherwise cost every epilogue
+    const int cus = device_cus();
+    // one workgroup per compute unit walking several tiles; one tile each when a tile has fewer stages
+    // than there are stage buffers (the cross-tile pipeline then has nothing to overlap)
+    const dim3 grid((unsigned)(S >= C::NBUF && T > cus ? cus : T)), block(256);
+    // the epilogue variant (bias, GELU) is a compile-time choice: GELU, and even a per-element bias
+    // select, would otherwise cost every epilogue
     const int epi = OUT == OUT_I32 ? 0 : ((g.bias ? 1 : 0) | (g.gelu ? 2 : 0));
-#define SP24_I8_LAUNCH(TMV, E) hipLaunchKernelGGL((gemm_i8_tiled_kernel<OUT, TMV, E>), grid, block, 0, s, a)
-    if (g.tm) {
-        switch (epi) {
-        case 0: SP24_I8_LAUNCH(true, 0); break;
-        case 1: if constexpr (OUT != OUT_I32) SP24_I8_LAUNCH(true, 1); break;
-        case 2: if constexpr (OUT != OUT_I32) SP24_I8_LAUNCH(true, 2); break;
-        default: if constexpr (OUT != OUT_I32) SP24_I8_LAUNCH(true, 3); break;
-        }
-    } else {
-        switch (epi) {
-        case 0: SP24_I8_LAUNCH(false, 0); break;
-        case 1: if constexpr (OUT != OUT_I32) SP24_I8_LAUNCH(false, 1); break;
-        case 2: if constexpr (OUT != OUT_I32) SP24_I8_LAUNCH(false, 2); break;
-        default: if constexpr (OUT != OUT_I32) SP24_I8_LAUNCH(false, 3); break;
-        }
-    }
-#undef SP24_I8_LAUNCH
+    if constexpr (BNT == 128)
+        launch_epi<OUT, true, BNT>(epi, grid, block, s, a);  // 128-wide tiles are token-major only
+    else if (g.tm)
+        launch_epi<OUT, true, BNT>(epi, grid, block, s, a);
+    else
+        launch_epi<OUT, false, BNT>(epi, grid, block, s, a);
     return hipGetLastError();
+}
+
+template <int OUT>
+hipError_t launch_out(const GemmArgs& g, hipStream_t s) {
+    return tiled_tile_width(g) == 128 ? launch_bn<OUT, 128>(g, s) : launch_bn<OUT, 256>(g, s);
 }
 
 }  // namespace tiled_i8

@@ -53,6 +53,10 @@ hipError_t launch_decompress(const void* values, const uint8_t* meta, int dtype,
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s);
 bool gemm_bf16_skinny_ok(const GemmArgs& g);
 hipError_t launch_gemm_bf16_skinny(const GemmArgs& g, hipStream_t s);
+// Compute units of the current device (cached per device; 256 if the query fails).
+int device_cus();
+// Workgroup tile width (256 or 128 columns of N) of a tiled GEMM launch.
+int tiled_tile_width(const GemmArgs& g);
 bool gemm_bf16_tiled_ok(const GemmArgs& g);
 hipError_t launch_gemm_bf16_tiled(const GemmArgs& g, hipStream_t s);
 

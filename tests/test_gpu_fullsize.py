@@ -105,6 +105,10 @@ def test_bert_ffn_int8():
         acc, Y = oracle.gemm_i8(rv8, rm8, xq, M, scale, rows=rows)
         assert np.array_equal(got_acc.astype(np.int64), acc)
         assert np.array_equal(got.view(np.uint32), Y.view(np.uint32))
+        # token-major (X N x K, Y N x M), the layout the bench times
+        Xt = dev(np.ascontiguousarray(xq.T))
+        got_tm = host_bits(sp.sp24_gemm_i8_ex(v8, m8, M, Xt, scale=dev(scale), layout="token")[:, r].t().contiguous())
+        assert np.array_equal(got_tm.view(np.uint32), Y.view(np.uint32))
 
 
 @pytest.mark.parametrize("M", [11008, 4096])

@@ -58,6 +58,7 @@ TM_SHAPES = [
     (257, 128, 513, 136, 260),
     (768, 1024, 1024, 1024, 768),
     (40, 192, 300, 192, 48),
+    (2304, 128, 4100, 136, 2304),  # 153 tiles of 256 x 256: the 256-wide tile (smaller shapes take 128)
     # direct kernel (K tail with N > 64, or unaligned rows)
     (200, 336, 100, 336, 200),
     (96, 256, 130, 259, 97),
@@ -133,6 +134,7 @@ def test_gemm_bf16_batched_broadcast_x():
 I8_TM_SHAPES = [
     # M, K, N, ldx (>= K), ldy (>= M): tiled (K % 128 == 0, 16-byte rows, N > 64) and direct
     (257, 512, 513, 528, 264),
+    (2304, 384, 4100, 400, 2312),  # 153 tiles of 256 x 256: the 256-wide tile (smaller shapes take 128)
     (40, 128, 65, 128, 48),
     (520, 1152, 1000, 1152, 520),
     (33, 48, 17, 48, 40),
