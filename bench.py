@@ -41,6 +41,7 @@ from structured_sparse_gemm_sp24_amd import synth  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
 DENSE_PEAK = {"bf16": 2516.6, "i8": 5033.2}   # TFLOP/s (bf16) and TOP/s (int8), dense MFMA
+SPEC_SCLK_MHZ = 2400.0                          # the clock those peaks are quoted at
 CACHE_BYTES = 256 << 20                      # MI355X Infinity Cache
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "structured_sparse_gemm_sp24_amd", "csrc")
@@ -507,6 +508,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense-ref", action="store_true", help="skip timing the dense bf16 GEMM of the same shape")
+    ap.add_argument("--no-sclk-probe", action="store_true", help="skip the shader-clock probe (sp24_probe_sclk)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain copy of MIB MiB (to scale FETCH_SIZE / WRITE_SIZE counter readings)")
     args = ap.parse_args()
@@ -536,6 +538,17 @@ def main():
         if k.flops:
             e["tflops_dense_equiv"] = round(2 * k.flops / t / 1e12, 1)
         kernels[k.name] = e
+
+    if not args.no_sclk_probe:
+        # the shader clock under sustained matrix-core load: the MFMA peak above assumes 2.4 GHz
+        pr = sp.sp24_probe_sclk()
+        roof["sclk_mhz"] = round(pr["sclk_mhz"], 1)
+        roof["cycles_per_smfmac"] = round(pr["cycles_per_smfmac"], 2)
+        k = by_name[dom]
+        if k.flops:
+            peak_sclk = DENSE_PEAK[k.dtype] * pr["sclk_mhz"] / SPEC_SCLK_MHZ
+            roof["mfma_peak_at_sclk"] = round(peak_sclk, 1)
+            roof["mfma_frac_at_sclk"] = round(k.flops / (per_kernel_ms[dom] * 1e-3) / 1e12 / peak_sclk, 4)
 
     if not args.no_dense_ref and w.get("dense_ref"):
         fn = w["dense_ref"]()

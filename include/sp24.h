@@ -203,9 +203,10 @@ int sp24_gemm_i8_ex(const int8_t* values, const uint8_t* meta, int64_t M, int64_
  * of the Sparse-QAT case keeps its FFN in int8 between layers; oeforum post: int8 and 2:4 combine).
  * For every output element, in fp32 with one rounding per step:
  *   y = fl32( fl32(acc[m, n]) * scale[m] );   y = fl32(y + bias[m]) when bias != NULL;
- *   y = GELU(y) = y/2 erfc(-y / sqrt 2) when activation == SP24_ACT_GELU, in fp32 with the erfc
- *       formula of Numerical Recipes (section 6.2): not bit-exact across implementations; |error| <=
- *       8 * 2^-24 * |y| against the exact GELU of the fp32 input;
+ *   y = GELU(y) = y/2 erfc(-y / sqrt 2) when activation == SP24_ACT_GELU, in fp32 with the rational
+ *       erfc approximation of Abramowitz & Stegun (Handbook of Mathematical Functions, formula 7.1.26):
+ *       not bit-exact across implementations; |error| <= 8 * 2^-24 * |y| against the exact GELU of the
+ *       fp32 input;
  *   stored as out_dtype: SP24_FP32; SP24_BF16 (round to nearest even); or SP24_I8, the requantized code
  *       clamp( rne( fl32(y * inv) ), -127, 127 ) with inv = fl32(1 / out_scale), out_scale > 0 the next
  *       layer's input scale (a multiply by the rounded reciprocal, not a division).
@@ -215,6 +216,17 @@ int sp24_gemm_i8_fused(const int8_t* values, const uint8_t* meta, int64_t M, int
                        int64_t ldx, int64_t x_batch_stride, const float* scale, const float* bias, int activation,
                        void* Y, int out_dtype, float out_scale, int64_t ldy, int64_t y_batch_stride, int64_t batch,
                        int layout, void* stream);
+
+/* Measurement support (no passage of the method: rates are quoted against the MI355X peaks, and this
+ * gives the clock those peaks scale with). Launches `blocks` workgroups of 4 waves, one workgroup per
+ * compute unit (each takes 96 KB of LDS), in which every wave issues iters x 16 independent
+ * v_smfmac_f32_16x16x64_bf16 back to back on register operands, and records for each wave the shader
+ * clock cycles (s_memtime) and the 100 MHz real-time ticks (s_memrealtime) of that loop:
+ *   out[2 w] = cycles, out[2 w + 1] = real-time ticks, for waves w = 0 .. 4 blocks - 1
+ * (device memory owned by the caller, 8 * blocks uint64). Cycles per smfmac = cycles / (16 iters); the
+ * sustained shader clock under matrix-core load = cycles / (ticks / 100 MHz). Errors: SP24_ERR_NULL,
+ * SP24_ERR_ARG (blocks < 1 or > 65535, iters < 1 or > 10^6). */
+int sp24_probe_sclk(int64_t blocks, int iters, uint64_t* out, void* stream);
 
 /* Static description of a status code. */
 const char* sp24_status_string(int status);

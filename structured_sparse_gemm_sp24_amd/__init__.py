@@ -26,7 +26,8 @@ SP24_ACT_NONE, SP24_ACT_GELU = 0, 1
 EXPORTS = ("sp24_col_norms", "sp24_compressed_bytes", "sp24_prune_compress", "sp24_prune_mask",
            "sp24_channel_permutation", "sp24_decompress",
            "sp24_gemm_bf16",
-           "sp24_gemm_i8", "sp24_gemm_bf16_ex", "sp24_gemm_i8_ex", "sp24_gemm_i8_fused", "sp24_status_string")
+           "sp24_gemm_i8", "sp24_gemm_bf16_ex", "sp24_gemm_i8_ex", "sp24_gemm_i8_fused", "sp24_probe_sclk",
+           "sp24_status_string")
 
 _TORCH_TO_SP24 = {torch.bfloat16: SP24_BF16, torch.float16: SP24_FP16, torch.float32: SP24_FP32,
                   torch.int8: SP24_I8, torch.int32: SP24_I32}
@@ -64,6 +65,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sp24_gemm_i8_ex.argtypes = [P, P, I64, I64, P, I64, I64, I64, P, P, I64, I64, I64, I, P]
     lib.sp24_gemm_i8_fused.argtypes = [P, P, I64, I64, P, I64, I64, I64, P, P, I, P, I, ctypes.c_float, I64, I64, I64,
                                        I, P]
+    lib.sp24_probe_sclk.argtypes = [I64, I, P, P]
     for fn in EXPORTS[:-1]:
         getattr(lib, fn).restype = I
     lib.sp24_status_string.argtypes = [I]
@@ -309,3 +311,20 @@ def sp24_gemm_i8_fused(values: torch.Tensor, meta: torch.Tensor, M: int, X: torc
                                            float(out_scale), ldy, sy, batch, lay, _stream(X))
     _check("sp24_gemm_i8_fused", st)
     return out
+
+
+def sp24_probe_sclk(blocks: int | None = None, iters: int = 4000, device: int | None = None) -> dict:
+    """Sustained shader clock under matrix-core load and the issue rate of back-to-back smfmacs, from
+    one probe launch (one workgroup of 4 waves per compute unit by default): per wave, shader-clock
+    cycles and 100 MHz real-time ticks of iters x 16 independent v_smfmac_f32_16x16x64_bf16."""
+    dev = torch.device("cuda", torch.cuda.current_device() if device is None else device)
+    if blocks is None:
+        blocks = torch.cuda.get_device_properties(dev).multi_processor_count
+    out = torch.zeros(8 * blocks, dtype=torch.int64, device=dev)
+    st = load_library().sp24_probe_sclk(int(blocks), int(iters), _ptr(out), ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream))
+    _check("sp24_probe_sclk", st)
+    h = out.view(-1, 2).cpu().double()
+    cycles, ticks = h[:, 0], h[:, 1]
+    n = 16.0 * iters
+    return {"sclk_mhz": float((cycles / (ticks / 100.0)).mean()), "cycles_per_smfmac": float((cycles / n).mean()),
+            "waves": int(h.shape[0])}

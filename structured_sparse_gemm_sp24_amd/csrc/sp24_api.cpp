@@ -315,4 +315,13 @@ int sp24_gemm_i8(const int8_t* values, const uint8_t* meta, int64_t M, int64_t K
     return sp24_gemm_i8_ex(values, meta, M, K, X, N, ldx, 0, scale, Y, ldy, 0, 1, SP24_FEATURE_MAJOR, stream);
 }
 
+int sp24_probe_sclk(int64_t blocks, int iters, uint64_t* out, void* stream) {
+    if (!out) return SP24_ERR_NULL;
+    if (blocks < 1 || blocks > 65535 || iters < 1 || iters > 1000000) return SP24_ERR_ARG;
+    if ((reinterpret_cast<uintptr_t>(out) & 7) != 0) return SP24_ERR_ALIGN;
+    const int st = check_device();
+    if (st != SP24_OK) return st;
+    return hip_status(sp24::launch_sclk_probe(blocks, iters, out, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -43,6 +43,8 @@ hipError_t launch_prune_compress(const void* W, int dtype, int64_t M, int64_t K,
 hipError_t launch_prune_mask(const void* W, int dtype, int64_t M, int64_t K, int64_t ldw, int keep, int score,
                              const float* norms, uint8_t* mask, void* W_out, int64_t ldo, hipStream_t s);
 
+// Shader-clock probe: `blocks` workgroups of 4 waves, cycles and real-time ticks per wave into out.
+hipError_t launch_sclk_probe(int64_t blocks, int iters, uint64_t* out, hipStream_t s);
 hipError_t launch_channel_permutation(const void* W, int dtype, int64_t M, int64_t K, int64_t ldw, int score,
                                       const float* norms, int sweeps, int32_t* perm, hipStream_t s);
 

@@ -211,6 +211,18 @@ def test_channel_permutation_validation(lib, args, expect):
     assert lib.sp24_channel_permutation(*args) == expect
 
 
+@pytest.mark.parametrize("args,expect", [
+    ((4, 10, NULL, NULL), sp.SP24_ERR_NULL),
+    ((0, 10, A, NULL), sp.SP24_ERR_ARG),
+    ((65536, 10, A, NULL), sp.SP24_ERR_ARG),
+    ((4, 0, A, NULL), sp.SP24_ERR_ARG),
+    ((4, 1000001, A, NULL), sp.SP24_ERR_ARG),
+    ((4, 10, ctypes.c_void_p(0x10004), NULL), sp.SP24_ERR_ALIGN),
+])
+def test_probe_sclk_validation(lib, args, expect):
+    assert lib.sp24_probe_sclk(*args) == expect
+
+
 def test_compressed_bytes(lib):
     vb, mb = ctypes.c_int64(), ctypes.c_int64()
     # rows padded to 16, columns to 128 / value size
