@@ -541,7 +541,7 @@ def main():
 
     if not args.no_sclk_probe:
         # the shader clock under sustained matrix-core load: the MFMA peak above assumes 2.4 GHz
-        pr = sp.sp24_probe_sclk()
+        pr = sp.sp24_probe_sclk(iters=16000)
         roof["sclk_mhz"] = round(pr["sclk_mhz"], 1)
         roof["cycles_per_smfmac"] = round(pr["cycles_per_smfmac"], 2)
         k = by_name[dom]
