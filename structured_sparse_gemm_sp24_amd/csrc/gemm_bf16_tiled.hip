@@ -15,11 +15,12 @@
 //     operand (16 rows x 64 dense columns), so each tile is one contiguous 64-lane copy, and a
 //     lane's ds_read_b128 of its operand is conflict-free.
 //   metadata: 128 B tiles in lane order; a lane reads its 16-bit index with ds_read_u16.
-//   B tile (X, 64 rows x 256 bf16 = 512 B per row): row-major with the 32-byte units of row k
-//     stored at unit ^ v(k), v(k) = 2 (k & 3) + ((k >> 3) & 1). One transposing read (below) takes
-//     16 rows x 32 bytes, rows 8q + {0..3} for q = 0..3; v puts them in 8 distinct 32-byte bank
-//     groups (two rows each, the minimum for 512 bytes). In global memory every 4 consecutive lanes
-//     of a load still read one aligned 64-byte run (v only swaps its two halves or moves it whole).
+//   B tile (X, 64 rows x 256 bf16 = 512 B per row; 128 bf16 = 256 B in the 128-wide tile): row-major
+//     with the 32-byte units of row k stored at unit ^ v(k), v(k) = 2 (k & 3) + ((k >> 3) & 1) (< 8,
+//     so a unit stays in its row for either width). One transposing read (below) takes 16 rows x 32
+//     bytes, rows 8q + {0..3} for q = 0..3; v puts them in 8 distinct 32-byte bank groups (two rows
+//     each, the minimum for 512 bytes). In global memory every 4 consecutive lanes of a load still
+//     read one aligned 64-byte run (v only swaps its two halves or moves it whole).
 // The B operand (lane = column, 16 k values in two halves of 8) comes from four ds_read_b64_tr_b16:
 // in each 16-lane group, lane s points at row k0 + s/4, columns c0 + 4(s%4); the instruction hands
 // lane i the four consecutive k of column c0 + i.
@@ -53,20 +54,19 @@ constexpr int A_BYTES = BM * BK;          // BK/2 bf16 values per row = BK bytes
 constexpr int META_BYTES = BM * BK / 8;   // 4 bits per group of 4
 constexpr int GROUP_M = 8;
 
-// Tile width BN (N columns of a workgroup tile): 256 (waves of 128 x 128), or 128 for token-major X
-// (waves of 128 x 64), which halves a tile's work for shapes whose 256-wide tiles leave most compute
-// units idle in a last partial turn. The narrower stage (34 KB) leaves room for four LDS buffers.
+// Tile width BN (N columns of a workgroup tile): 256 (waves of 128 x 128), or 128 (waves of 128 x 64),
+// which halves a tile's work for shapes whose 256-wide tiles leave most compute units idle in a last
+// partial turn. The narrower stage (34 KB) leaves room for four LDS buffers.
 template <int BN_>
 struct Cfg {
     static constexpr int BN = BN_, WN = BN_ / 2, FN = WN / 16;
     static constexpr int B_BYTES = BK * BN * 2;
-    static constexpr int B_ROW = BN * 2;  // feature-major B tile row: 512 bytes
+    static constexpr int B_ROW = BN * 2;  // feature-major B tile row: 512 or 256 bytes
     static constexpr int STAGE_BYTES = A_BYTES + META_BYTES + B_BYTES;
     static constexpr int NBUF = BN == 256 ? 3 : 4;  // stage buffers (3 x 50 KB or 4 x 34 KB of LDS)
-    static constexpr int B_LOADS = BN / 32;          // per wave: token-major 8 rows per load, feature-major 2 rows
+    static constexpr int B_LOADS = BN / 32;          // per wave: token-major 8 rows per load, feature-major 1 KB
     static constexpr int LOADS_PER_STAGE = 4 + 2 + B_LOADS;  // per wave: A, metadata, B
 };
-constexpr int BN = 256, WN = 128, FN = 8, B_ROW = 512;  // the feature-major (and default) tile
 constexpr uint32_t RSRC_FLAGS = 0x00020000u;
 
 // Raw buffer descriptor: base, stride 0, byte count rounded up to whole dwords, format word. The range
@@ -145,12 +145,13 @@ __device__ __forceinline__ int tm_swz(int n) { return ((n >> 1) & 7) ^ ((n & 1) 
 struct LoadOffsets {
     uint32_t a;      // A tile: 16 * lane
     uint32_t m;      // metadata: 4 * (lane & 31) + (lane >> 5) * tiles * 128 (second tile of the pair)
-    // feature-major B row pair: (lane >> 5) * row pitch + 16 * swizzled chunk, by row & 3 >> 1 and
+    // feature-major, 256 wide: row pair (lane >> 5) * row pitch + 16 * swizzled chunk, by row & 3 >> 1 and
+    // row >> 3 & 1; 128 wide (b[0], b[1]): row quad (lane >> 4) * row pitch + 16 * swizzled chunk, by
     // row >> 3 & 1; token-major (b[0], b[1]): (lane >> 3) * row pitch + 16 * swizzled unit, by row >> 3 & 1
     uint32_t b[4];
 };
 
-template <bool TM>
+template <bool TM, int BNT>
 __device__ __forceinline__ LoadOffsets load_offsets(const Args& a, int lane) {
     LoadOffsets o;
     const int tiles = (int)((a.K + BK - 1) / BK);
@@ -163,6 +164,17 @@ __device__ __forceinline__ LoadOffsets load_offsets(const Args& a, int lane) {
         for (int h = 0; h < 2; h++) {
             const int row = 8 * h + (lane >> 3);
             o.b[h] = (uint32_t)((lane >> 3) * a.ldx * 2 + 16 * ((lane & 7) ^ tm_swz(row)));
+        }
+        o.b[2] = o.b[3] = 0;
+    } else if constexpr (BNT == 128) {
+        // lane i of a load lands in row (i >> 4) of a quad of 256-byte rows, 16-byte slot i & 15; the
+        // quads of one wave's loads differ in (row >> 3) & 1 only (row & 3 = i >> 4 in each)
+        const int pc = lane & 15;
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+            const int row = (lane >> 4) + 8 * h;
+            const int v = ((row & 3) << 1) | ((row >> 3) & 1);
+            o.b[h] = (uint32_t)((lane >> 4) * a.ldx * 2 + 16 * (pc ^ (2 * v)));
         }
         o.b[2] = o.b[3] = 0;
     } else {
@@ -188,7 +200,6 @@ template <bool TM, int BNT>
 __device__ __forceinline__ void load_stage(uint32_t lds, const Args& a, const TileDesc& td, int s, int wave,
                                            const LoadOffsets& lo) {
     using C = Cfg<BNT>;
-    static_assert(TM || BNT == 256, "feature-major tiles are 256 wide");
     const int64_t k0 = (int64_t)s * BK;
     const int tiles = (int)((a.K + BK - 1) / BK);
     const uint32_t past = td.valid ? 0u : 0x80000000u;
@@ -215,6 +226,16 @@ __device__ __forceinline__ void load_stage(uint32_t lds, const Args& a, const Ti
             const int row = (BNT / 4) * wave + 8 * h;
             dma16(lds + A_BYTES + META_BYTES + row * 128, lo.b[h & 1] + (uint32_t)(row * a.ldx * 2), rB);
         }
+    } else if constexpr (BNT == 128) {
+        // B: 64 rows x 256 B; this wave loads rows 16 wave .. +15, four rows per instruction (rows
+        // 16 wave + 4h + lane / 16: row & 3 = lane / 16, (row >> 3) & 1 = h >> 1).
+        const i32x4 rB =
+            make_rsrc(td.x + k0 * a.ldx + td.n0, td.valid ? ((a.K - 1 - k0) * a.ldx + a.N - td.n0) * 2 : 0);
+#pragma unroll
+        for (int h = 0; h < 4; h++) {
+            const int row = 16 * wave + 4 * h;
+            dma16(lds + A_BYTES + META_BYTES + row * 256, lo.b[h >> 1] + (uint32_t)(row * a.ldx * 2), rB);
+        }
     } else {
         // B: 64 rows x 512 B; this wave loads rows 16*wave .. +15, two rows per instruction (rows
         // 16 wave + 2h + lane / 32: row & 3 = 2 (h & 1) + lane / 32, (row >> 3) & 1 = h >> 2).
@@ -225,7 +246,7 @@ __device__ __forceinline__ void load_stage(uint32_t lds, const Args& a, const Ti
 #pragma unroll
         for (int h = 0; h < 8; h++) {
             const int row = 16 * wave + 2 * h;
-            dma16(lds + A_BYTES + META_BYTES + row * B_ROW,
+            dma16(lds + A_BYTES + META_BYTES + row * 512,
                   lo.b[(h & 1) | ((h >> 2) << 1)] + (uint32_t)(row * a.ldx * 2), rB);
         }
     }
@@ -282,6 +303,7 @@ __device__ __forceinline__ LaneOffsets<FNT> lane_offsets(int wm0, int wn0, int l
     }
     // read t of group q covers rows 8q + 4(t&1) + 32(t>>1) + r/4, which all have the row & 3 and
     // (row >> 3) & 1 of row0, so the unit swizzle is fixed per lane and t only adds immediates
+    constexpr int B_ROW = 64 * FNT;  // bytes per row of the feature-major B tile
     const int row0 = 8 * q + (r >> 2);
     const int v = ((row0 & 3) << 1) | ((row0 >> 3) & 1);
 #pragma unroll
@@ -332,6 +354,7 @@ __device__ __forceinline__ bf16x16 read_b(uint32_t buf, const LaneOffsets<FNT>& 
         const u32x4 hi = *reinterpret_cast<lds_u32x4*>(p1 + j * 2048);
         return __builtin_bit_cast(bf16x16, u32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
     }
+    constexpr int B_ROW = 64 * FNT;  // bytes per row of the feature-major B tile
     const lds_char* p = (const lds_char*)(size_t)stage_addr(buf, o.b[j]);
     u32x8 b;
 #pragma unroll
@@ -534,7 +557,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int wm0 = (wave >> 1) * WM, wn0 = (wave & 1) * C::WN;
     const LaneOffsets<F> o = lane_offsets<TM, F>(wm0, wn0, lane);
-    const LoadOffsets lo = load_offsets<TM>(a, lane);
+    const LoadOffsets lo = load_offsets<TM, BNT>(a, lane);
     const int S = (int)((a.K + BK - 1) / BK);
 
     f32x4 acc[FM][F];
@@ -624,12 +647,12 @@ int device_cus() {
     return cached[dev];
 }
 
-// Tile width for a launch of either tiled GEMM. A 128-wide tile (token-major only) costs about C128 of
+// Tile width for a launch of either tiled GEMM. A 128-wide tile (the int8 kernel: token-major only) costs about C128 of
 // a 256-wide one (measured on MI355X), so it wins when the 256-wide tiles leave a last partial turn that
 // the 128-wide ones fill better: e.g. 3072 x 6304 has 300 tiles of 256 x 256 on 256 compute units (two
 // turns), and 600 of 256 x 128 (three turns of the cheaper tile).
-int tiled_tile_width(const GemmArgs& g) {
-    if (!g.tm) return 256;
+int tiled_tile_width(const GemmArgs& g, bool feature_major_128) {
+    if (!g.tm && !feature_major_128) return 256;
     constexpr double C128 = 0.6;
     const int64_t cus = device_cus();
     const int64_t tm = (g.M + 255) / 256;
@@ -659,27 +682,22 @@ static hipError_t launch_bn(const GemmArgs& g, hipStream_t s) {
     // than there are stage buffers (the cross-tile pipeline then has nothing to overlap)
     const int cus = device_cus();
     const unsigned grid = (unsigned)(S >= C::NBUF && T > cus ? cus : T);
-    if constexpr (BNT == 128) {
+    if (g.tm) {
         if (g.out_fp32)
-            hipLaunchKernelGGL((tiled_bf16::gemm_bf16_tiled_kernel<true, true, 128>), dim3(grid), dim3(256), 0, s, a);
+            hipLaunchKernelGGL((tiled_bf16::gemm_bf16_tiled_kernel<true, true, BNT>), dim3(grid), dim3(256), 0, s, a);
         else
-            hipLaunchKernelGGL((tiled_bf16::gemm_bf16_tiled_kernel<false, true, 128>), dim3(grid), dim3(256), 0, s, a);
-    } else if (g.tm) {
-        if (g.out_fp32)
-            hipLaunchKernelGGL((tiled_bf16::gemm_bf16_tiled_kernel<true, true, 256>), dim3(grid), dim3(256), 0, s, a);
-        else
-            hipLaunchKernelGGL((tiled_bf16::gemm_bf16_tiled_kernel<false, true, 256>), dim3(grid), dim3(256), 0, s, a);
+            hipLaunchKernelGGL((tiled_bf16::gemm_bf16_tiled_kernel<false, true, BNT>), dim3(grid), dim3(256), 0, s, a);
     } else {
         if (g.out_fp32)
-            hipLaunchKernelGGL((tiled_bf16::gemm_bf16_tiled_kernel<true, false, 256>), dim3(grid), dim3(256), 0, s, a);
+            hipLaunchKernelGGL((tiled_bf16::gemm_bf16_tiled_kernel<true, false, BNT>), dim3(grid), dim3(256), 0, s, a);
         else
-            hipLaunchKernelGGL((tiled_bf16::gemm_bf16_tiled_kernel<false, false, 256>), dim3(grid), dim3(256), 0, s, a);
+            hipLaunchKernelGGL((tiled_bf16::gemm_bf16_tiled_kernel<false, false, BNT>), dim3(grid), dim3(256), 0, s, a);
     }
     return hipGetLastError();
 }
 
 hipError_t launch_gemm_bf16_tiled(const GemmArgs& g, hipStream_t s) {
-    return tiled_tile_width(g) == 128 ? launch_bn<128>(g, s) : launch_bn<256>(g, s);
+    return tiled_tile_width(g, true) == 128 ? launch_bn<128>(g, s) : launch_bn<256>(g, s);
 }
 
 }  // namespace sp24

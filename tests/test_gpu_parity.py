@@ -76,9 +76,14 @@ def wanda_norms(seed, K):
 @pytest.mark.parametrize("score", ["magnitude", "wanda"])
 @pytest.mark.parametrize("M,K,ld", [(1, 16, 16), (37, 48, 64), (200, 336, 352), (3, 1024, 1024)])
 def test_prune_compress_bit_exact(dt, score, M, K, ld):
-    if dt == "i8" and score == "wanda":
-        pytest.skip("Wanda scoring takes float weights")
     Wf = weights_f32(M * 7 + K, M, K)
+    if dt == "i8" and score == "wanda":
+        # Wanda scores float weights; the library refuses int8 with it, before any launch
+        W8 = np.clip(np.rint(Wf * 50), -127, 127).astype(np.int8)
+        with pytest.raises(sp.Sp24Error) as e:
+            sp.sp24_prune_compress(dev(W8), score=sp.SP24_SCORE_WANDA, norms=dev(wanda_norms(K, K)))
+        assert e.value.status == sp.SP24_ERR_DTYPE
+        return
     W, odt, kind = as_dtype(Wf, dt)
     vdt = oracle.BF16 if dt == "fp32->bf16" else odt
     norms = wanda_norms(K, K) if score == "wanda" else None
@@ -181,6 +186,8 @@ GEMM_SHAPES = [
     (257, 128, 513, 520, 516),
     (768, 1024, 1024, 1024, 1024),
     (40, 192, 300, 304, 300),
+    # 153 tiles of 256 x 256: the 256-wide tile (the shapes above take the 128-wide one)
+    (2304, 128, 4100, 4104, 4100),
 ]
 
 
