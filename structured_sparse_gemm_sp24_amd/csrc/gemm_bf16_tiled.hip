@@ -1,9 +1,13 @@
 // Tiled sparse x dense GEMM for large N, bf16 in, fp32 accumulate (NVIDIA blog on Ampere structured
 // sparsity, Figure 1; Orin NN design, Chapter 7, section 2.1 Step 3).
 //
-// Workgroup tile 256 (M) x 256 (N), 4 waves in a 2 x 2 grid, each wave 128 x 128 = 8 x 8
-// v_smfmac_f32_16x16x64_bf16 fragments (256 fp32 accumulators per lane, one wave per SIMD).
-// K advances 64 dense columns per stage; three stages are in flight through LDS (3 x 50 KB).
+// Workgroup tile 256 (M) x BN (N), 4 waves in a 2 x 2 grid, each wave 128 x BN/2 = 8 x BN/32
+// v_smfmac_f32_16x16x64_bf16 fragments. K advances 64 dense columns per stage through LDS stage buffers.
+// Two configurations are launched (see the launcher): BN = 128 with two workgroups per compute unit
+// (two waves per SIMD, 128 fp32 accumulators per lane, at most 256 registers per wave), each with two
+// 34 KB stage buffers -- while one workgroup waits at its barrier or for its loads, the other's smfmacs
+// keep the SIMD busy -- and BN = 256 with one workgroup per CU (256 accumulators per lane, three 50 KB
+// buffers). The template also builds BN = 128 with one workgroup per CU and four 34 KB buffers.
 //
 // Global -> LDS uses buffer loads with LDS destination (no VGPR staging). The whole byte offset of
 // each load is in its VGPR operand, which the buffer range check covers (the SGPR offset is not
@@ -35,7 +39,7 @@
 //
 // A batch of products sharing the weight (1x1 conv over B images) adds the batch to the tile index.
 //
-// Persistent: one workgroup per CU walks its tiles (p, p + G, p + 2G, ... in a numbering where the
+// Persistent: each workgroup (one or two per CU) walks its tiles (p, p + G, p + 2G, ... in a numbering where the
 // workgroups of one XCD -- workgroup p runs on XCD p % 8 -- hold neighbouring tiles at the same time,
 // walked in groups of 8 tile-rows, so A and B tiles are re-read from that XCD's L2). The three-stage
 // LDS pipeline runs across tile boundaries: the last stages of a tile load the first stages of the
@@ -57,13 +61,17 @@ constexpr int GROUP_M = 8;
 // Tile width BN (N columns of a workgroup tile): 256 (waves of 128 x 128), or 128 (waves of 128 x 64),
 // which halves a tile's work for shapes whose 256-wide tiles leave most compute units idle in a last
 // partial turn. The narrower stage (34 KB) leaves room for four LDS buffers.
-template <int BN_>
+// OCC_ = 2: two workgroups per compute unit (two waves per SIMD, at most 256 registers each), with
+// two stage buffers each (2 x 2 x 34 KB of LDS), for the 128-wide tile only: one workgroup's smfmacs can
+// run while the other waits at its barrier or for its loads.
+template <int BN_, int OCC_ = 1>
 struct Cfg {
+    static_assert(OCC_ == 1 || BN_ == 128, "two workgroups per CU only with the 128-wide tile");
     static constexpr int BN = BN_, WN = BN_ / 2, FN = WN / 16;
     static constexpr int B_BYTES = BK * BN * 2;
     static constexpr int B_ROW = BN * 2;  // feature-major B tile row: 512 or 256 bytes
     static constexpr int STAGE_BYTES = A_BYTES + META_BYTES + B_BYTES;
-    static constexpr int NBUF = BN == 256 ? 3 : 4;  // stage buffers (3 x 50 KB or 4 x 34 KB of LDS)
+    static constexpr int NBUF = OCC_ == 2 ? 2 : (BN == 256 ? 3 : 4);  // stage buffers (3 x 50 KB, 4 x 34 KB, 2 x 34 KB)
     static constexpr int B_LOADS = BN / 32;          // per wave: token-major 8 rows per load, feature-major 1 KB
     static constexpr int LOADS_PER_STAGE = 4 + 2 + B_LOADS;  // per wave: A, metadata, B
 };
@@ -378,11 +386,11 @@ __device__ __forceinline__ void mfma_block(f32x4 (&acc)[FM][FNT], const AFrags& 
 // One K stage (see the pipeline description in the kernel): stage s of the current tile, g-th stage of
 // the workgroup overall (selects the buffer). The loads it issues are those of stage s + NBUF of the
 // current tile or, past its end, stage s + NBUF - S of the next one. No branches.
-template <bool TM, int BNT>
+template <bool TM, int BNT, int OCC>
 __device__ __forceinline__ void stage(uint32_t l0, const Args& a, const TileDesc& cur_t, const TileDesc& next_t, int s,
                                       int S, int g, f32x4 (&acc)[FM][Cfg<BNT>::FN], AFrags& f, bf16x16 (&rb)[4],
                                       const LaneOffsets<Cfg<BNT>::FN>& o, int wave, const LoadOffsets& lo) {
-    using C = Cfg<BNT>;
+    using C = Cfg<BNT, OCC>;
     constexpr int F = C::FN, NB = C::NBUF;
     const int cb = g % NB;
     const uint32_t cur = l0 + cb * C::STAGE_BYTES;
@@ -543,9 +551,9 @@ __device__ __forceinline__ void store_tile_tm(const f32x4 (&acc)[FM][FNT], const
     }
 }
 
-template <bool OUT_FP32, bool TM, int BNT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_bf16_tiled_kernel(Args a) {
-    using C = Cfg<BNT>;
+template <bool OUT_FP32, bool TM, int BNT, int OCC>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void gemm_bf16_tiled_kernel(Args a) {
+    using C = Cfg<BNT, OCC>;
     constexpr int NB = C::NBUF, F = C::FN;
     __shared__ __attribute__((aligned(16))) char smem[NB * C::STAGE_BYTES];
     // LDS byte address of the first stage buffer (for the LDS-destination loads)
@@ -566,8 +574,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
         for (int j = 0; j < F; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // Software pipeline over K stages of 64 columns, NB = 3 (256-wide tiles) or 4 (128-wide) LDS
-    // buffers (the workgroup's g-th stage in buffer g % NB), continued across the workgroup's tiles:
+    // Software pipeline over K stages of 64 columns, NB LDS buffers (2 with two workgroups per CU, else
+    // 3 for 256-wide tiles and 4 for 128-wide; the workgroup's g-th stage in buffer g % NB), continued
+    // across the workgroup's tiles:
     //  - the loads of stage g+NB go out once every wave has finished reading stage g, i.e. at the
     //    barrier placed before the last two fragment blocks of stage g, so each stage's loads have
     //    about NB - 1 stages of compute to land;
@@ -594,7 +603,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     rb[1] = read_b<TM>(l0, o, 1);
     int g = 0;
     for (int k = 1;; k++) {
-        for (int s = 0; s < S; s++, g++) stage<TM, BNT>(l0, a, cur_t, next_t, s, S, g, acc, fa, rb, o, wave, lo);
+        for (int s = 0; s < S; s++, g++) stage<TM, BNT, OCC>(l0, a, cur_t, next_t, s, S, g, acc, fa, rb, o, wave, lo);
         // epilogue from registers; the next tile's first stages are in flight meanwhile
         {
             const int64_t mw = cur_t.m0 + wm0, nw = cur_t.n0 + wn0;
@@ -647,12 +656,12 @@ int device_cus() {
     return cached[dev];
 }
 
-// Tile width for a launch of either tiled GEMM. A 128-wide tile (the int8 kernel: token-major only) costs about C128 of
+// Tile width for a launch of the tiled int8 GEMM. A 128-wide tile (token-major only) costs about C128 of
 // a 256-wide one (measured on MI355X), so it wins when the 256-wide tiles leave a last partial turn that
-// the 128-wide ones fill better: e.g. 3072 x 6304 has 300 tiles of 256 x 256 on 256 compute units (two
-// turns), and 600 of 256 x 128 (three turns of the cheaper tile).
-int tiled_tile_width(const GemmArgs& g, bool feature_major_128) {
-    if (!g.tm && !feature_major_128) return 256;
+// the 128-wide ones fill better: e.g. 3072 x 8192 has 384 tiles of 256 x 256 on 256 compute units (two
+// turns), and 768 of 256 x 128 (three turns of the cheaper tile).
+int tiled_tile_width(const GemmArgs& g) {
+    if (!g.tm) return 256;
     constexpr double C128 = 0.6;
     const int64_t cus = device_cus();
     const int64_t tm = (g.M + 255) / 256;
@@ -661,9 +670,9 @@ int tiled_tile_width(const GemmArgs& g, bool feature_major_128) {
     return c128 < c256 ? 128 : 256;
 }
 
-template <int BNT>
+template <int BNT, int OCC>
 static hipError_t launch_bn(const GemmArgs& g, hipStream_t s) {
-    using C = tiled_bf16::Cfg<BNT>;
+    using C = tiled_bf16::Cfg<BNT, OCC>;
     tiled_bf16::Args a;
     a.vals = static_cast<const uint16_t*>(g.values); a.meta = g.meta;
     a.X = static_cast<const uint16_t*>(g.X); a.Y = g.Y;
@@ -678,26 +687,33 @@ static hipError_t launch_bn(const GemmArgs& g, hipStream_t s) {
               (g.batch == 1 || (g.sy * es) % 16 == 0) && g.ldy * es * 16 < ((int64_t)1 << 31);
     const int T = a.tilesM * a.tilesN * a.batch;
     const int S = (int)((g.K + tiled_bf16::BK - 1) / tiled_bf16::BK);
-    // one workgroup per compute unit walking several tiles; one tile each when a tile has fewer stages
+    // OCC workgroups per compute unit walking several tiles; one tile each when a tile has fewer stages
     // than there are stage buffers (the cross-tile pipeline then has nothing to overlap)
-    const int cus = device_cus();
-    const unsigned grid = (unsigned)(S >= C::NBUF && T > cus ? cus : T);
+    const int slots = device_cus() * OCC;
+    const unsigned grid = (unsigned)(S >= C::NBUF && T > slots ? slots : T);
     if (g.tm) {
         if (g.out_fp32)
-            hipLaunchKernelGGL((tiled_bf16::gemm_bf16_tiled_kernel<true, true, BNT>), dim3(grid), dim3(256), 0, s, a);
+            hipLaunchKernelGGL((tiled_bf16::gemm_bf16_tiled_kernel<true, true, BNT, OCC>), dim3(grid), dim3(256), 0, s, a);
         else
-            hipLaunchKernelGGL((tiled_bf16::gemm_bf16_tiled_kernel<false, true, BNT>), dim3(grid), dim3(256), 0, s, a);
+            hipLaunchKernelGGL((tiled_bf16::gemm_bf16_tiled_kernel<false, true, BNT, OCC>), dim3(grid), dim3(256), 0, s, a);
     } else {
         if (g.out_fp32)
-            hipLaunchKernelGGL((tiled_bf16::gemm_bf16_tiled_kernel<true, false, BNT>), dim3(grid), dim3(256), 0, s, a);
+            hipLaunchKernelGGL((tiled_bf16::gemm_bf16_tiled_kernel<true, false, BNT, OCC>), dim3(grid), dim3(256), 0, s, a);
         else
-            hipLaunchKernelGGL((tiled_bf16::gemm_bf16_tiled_kernel<false, false, BNT>), dim3(grid), dim3(256), 0, s, a);
+            hipLaunchKernelGGL((tiled_bf16::gemm_bf16_tiled_kernel<false, false, BNT, OCC>), dim3(grid), dim3(256), 0, s, a);
     }
     return hipGetLastError();
 }
 
+// Configuration of a bf16 launch, measured on MI355X against one workgroup per CU with 256 x 256 or
+// 256 x 128 tiles (bit-identical results: the K order inside a tile does not depend on the tile shape):
+// 256 x 128 tiles with two workgroups per compute unit win by far when the 256-wide tiles need at most two
+// turns of the compute units (3072 x 768 x 6304 token-major: 48.4 / 41.9 -> 34.5 us; 768 x 3072 x 8192:
+// 61.9 / 41.0 -> 40.6 us) and tie on one to three turns of large tiles (4096^3, 11008 x 4096 x 4096); with
+// many turns the 256 x 256 tile keeps its edge in re-use (28672 x 8192 x 8192: 1977 against 2068 us).
 hipError_t launch_gemm_bf16_tiled(const GemmArgs& g, hipStream_t s) {
-    return tiled_tile_width(g, true) == 128 ? launch_bn<128>(g, s) : launch_bn<256>(g, s);
+    const int64_t t256 = ((g.M + 255) / 256) * ((g.N + 255) / 256) * g.batch;
+    return t256 <= 2 * (int64_t)device_cus() ? launch_bn<128, 2>(g, s) : launch_bn<256, 1>(g, s);
 }
 
 }  // namespace sp24

@@ -653,7 +653,7 @@ hipError_t launch_bn(const GemmArgs& g, hipStream_t s) {
 
 template <int OUT>
 hipError_t launch_out(const GemmArgs& g, hipStream_t s) {
-    return tiled_tile_width(g, false) == 128 ? launch_bn<OUT, 128>(g, s) : launch_bn<OUT, 256>(g, s);
+    return tiled_tile_width(g) == 128 ? launch_bn<OUT, 128>(g, s) : launch_bn<OUT, 256>(g, s);
 }
 
 }  // namespace tiled_i8

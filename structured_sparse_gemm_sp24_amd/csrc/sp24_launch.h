@@ -57,9 +57,8 @@ bool gemm_bf16_skinny_ok(const GemmArgs& g);
 hipError_t launch_gemm_bf16_skinny(const GemmArgs& g, hipStream_t s);
 // Compute units of the current device (cached per device; 256 if the query fails).
 int device_cus();
-// Workgroup tile width (256 or 128 columns of N) of a tiled GEMM launch; 128 only for token-major X
-// unless the kernel also has a 128-wide feature-major tile.
-int tiled_tile_width(const GemmArgs& g, bool feature_major_128);
+// Workgroup tile width (256, or 128 for token-major X) of a tiled int8 GEMM launch.
+int tiled_tile_width(const GemmArgs& g);
 bool gemm_bf16_tiled_ok(const GemmArgs& g);
 hipError_t launch_gemm_bf16_tiled(const GemmArgs& g, hipStream_t s);
 

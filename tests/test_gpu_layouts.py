@@ -58,7 +58,7 @@ TM_SHAPES = [
     (257, 128, 513, 136, 260),
     (768, 1024, 1024, 1024, 768),
     (40, 192, 300, 192, 48),
-    (2304, 128, 4100, 136, 2304),  # 153 tiles of 256 x 256: the 256-wide tile (smaller shapes take 128)
+    (2304, 128, 4100, 136, 2304),  # 153 tiles of 256 x 256: several turns of 256 x 128 tiles, two per CU
     # direct kernel (K tail with N > 64, or unaligned rows)
     (200, 336, 100, 336, 200),
     (96, 256, 130, 259, 97),
@@ -178,3 +178,29 @@ def test_gemm_i8_batched(B, M, K, N, layout):
     for b in range(B):
         _, ref = oracle.gemm_i8(v, m, xs[b], M, scale, layout=layout)
         assert np.array_equal(Y[b].view(np.uint32), ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("layout", ["feature", "token"])
+def test_gemm_bf16_many_tiles_sampled(layout):
+    # 18 x 31 = 558 tiles of 256 x 256 (more than two turns of the compute units: the 256-wide tile with
+    # one workgroup per CU), ragged in M and N; the oracle computes a sample of rows
+    M, K, N = 4360, 192, 7900
+    W = synth.normal_bf16(91, (M, K), 0.02)
+    X = synth.normal_bf16(92, (K, N))
+    v, m = oracle.prune_compress(W, oracle.BF16)
+    rows = np.unique(np.concatenate([np.random.default_rng(93).choice(M, 40, replace=False), [0, 255, 256, M - 1]]))
+    say(f"gemm_bf16_ex many tiles {layout} M={M} K={K} N={N}")
+    vd, md = dev(v, "bf16"), dev(m)
+    r = torch.from_numpy(rows).cuda()
+    if layout == "feature":
+        Xd, pick = dev(X, "bf16"), (lambda Y: Y[r])
+    else:
+        Xd, pick = dev(np.ascontiguousarray(X.T), "bf16"), (lambda Y: Y[:, r].t().contiguous())
+    Yf = host_bits(pick(sp.sp24_gemm_bf16_ex(vd, md, M, Xd, layout=layout, out_dtype=torch.float32)))
+    Yb = host_bits(pick(sp.sp24_gemm_bf16_ex(vd, md, M, Xd, layout=layout, out_dtype=torch.bfloat16)))
+    Y64 = oracle.gemm_bf16(v, m, X, M, rows=rows)
+    dense = bf16_to_f64(oracle.decompress(v, m, oracle.BF16, M, K)[rows])
+    bound = fp32_sum_bound(np.abs(dense) @ np.abs(bf16_to_f64(X)), K)
+    assert np.all(np.abs(Yf.astype(np.float64) - Y64) <= bound)
+    assert frob_rel(Yf, Y64) <= 1e-3
+    assert np.array_equal(Yb, synth.f32_to_bf16_bits(Yf))

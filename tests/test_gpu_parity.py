@@ -186,7 +186,7 @@ GEMM_SHAPES = [
     (257, 128, 513, 520, 516),
     (768, 1024, 1024, 1024, 1024),
     (40, 192, 300, 304, 300),
-    # 153 tiles of 256 x 256: the 256-wide tile (the shapes above take the 128-wide one)
+    # 153 tiles of 256 x 256: several turns of 256 x 128 tiles, two workgroups per CU
     (2304, 128, 4100, 4104, 4100),
 ]
 
