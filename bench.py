@@ -55,9 +55,11 @@ def to_dev(a, kind=None):
     return torch.from_numpy(a).cuda()
 
 
-def n_copies(step_bytes: int, budget: int = 24 << 30) -> int:
-    n = int(np.ceil(2 * CACHE_BYTES / max(step_bytes, 1)))
-    return max(1, min(64, n, budget // max(step_bytes, 1)))
+def n_copies(step_bytes: int, kernel_bytes: int, budget: int = 8 << 30) -> int:
+    """Buffer copies to rotate so that every kernel's launches cycle over more than twice the Infinity
+    Cache (kernel_bytes: the smallest bytes one kernel of the step touches), within a memory budget."""
+    n = int(np.ceil(2 * CACHE_BYTES / max(kernel_bytes, 1))) + 1
+    return max(2, min(64, n, budget // max(step_bytes, 1)))
 
 
 class Kernel:
@@ -87,8 +89,10 @@ def _bf16_gemm_workload(name, W_host, X_host, score, Xcal_host, config, layout, 
     vb, mb = sp.sp24_compressed_bytes(M, K, torch.bfloat16)
     ob = 2 if out == torch.bfloat16 else 4
     step_bytes = M * K * 2 + vb + mb + K * N * 2 + M * N * ob + (Xcal_host.size * 2 if Xcal_host is not None else 0)
+    kernel_bytes = min(M * K * 2 + vb + mb, vb + mb + K * N * 2 + M * N * ob,
+                       Xcal_host.size * 2 if Xcal_host is not None else step_bytes)
     copies = []
-    for _ in range(n_copies(step_bytes)):
+    for _ in range(n_copies(step_bytes, kernel_bytes)):
         c = dict(W=to_dev(W_host, "bf16"), X=to_dev(X_dev_host, "bf16"),
                  vals=torch.empty(vb // 2, dtype=torch.bfloat16, device="cuda"),
                  meta=torch.empty(mb, dtype=torch.uint8, device="cuda"),
@@ -234,8 +238,10 @@ def workload_bert_int8(args):
         xdev = np.ascontiguousarray(xq.T) if args.layout == "token" else xq
         layers.append(dict(M=M, K=K, N=xq.shape[1], q=q, xq=xq, xdev=xdev, scale=synth.dequant_scales(s_w, s_x)))
     step_bytes = sum(L["M"] * L["K"] * 2 + L["K"] * L["N"] + 4 * L["M"] * L["N"] for L in layers)
+    # the smallest kernel: an int8 prune/compress (M K read, 5/8 M K written)
+    kernel_bytes = min(L["M"] * L["K"] * 13 // 8 for L in layers)
     copies = []
-    for _ in range(n_copies(step_bytes)):
+    for _ in range(n_copies(step_bytes, kernel_bytes)):
         c = {}
         for i, L in enumerate(layers):
             vb, mb = sp.sp24_compressed_bytes(L["M"], L["K"], torch.int8)
@@ -320,8 +326,9 @@ def workload_bert_int8_fused(args):
     hsh = (N, M1) if tm else (M1, N)
     ysh = (N, M2) if tm else (M2, N)
     step_bytes = M1 * K1 * 2 + M2 * K2 * 2 + K1 * N + 2 * M1 * N + 4 * M2 * N
+    kernel_bytes = min(M1 * K1 * 13 // 8, M2 * K2 * 13 // 8)
     copies = []
-    for _ in range(n_copies(step_bytes)):
+    for _ in range(n_copies(step_bytes, kernel_bytes)):
         c = dict(W1=to_dev(q1), W2=to_dev(q2), X=to_dev(xdev), s1=to_dev(scale1), s2=to_dev(scale2),
                  b1=to_dev(bias["b1"]), b2=to_dev(bias["b2"]),
                  H=torch.empty(hsh, dtype=torch.int8, device="cuda"),

@@ -131,6 +131,7 @@ static hipError_t launch_gemm_bf16_direct(const GemmArgs& g, hipStream_t s) {
 }
 
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s) {
+    if (gemm_bf16_fewtok_ok(g)) return launch_gemm_bf16_fewtok(g, s);
     if (gemm_bf16_skinny_ok(g)) return launch_gemm_bf16_skinny(g, s);
     if (gemm_bf16_tiled_ok(g)) return launch_gemm_bf16_tiled(g, s);
     return launch_gemm_bf16_direct(g, s);

@@ -59,6 +59,9 @@ hipError_t launch_gemm_bf16_skinny(const GemmArgs& g, hipStream_t s);
 int device_cus();
 // Workgroup tile width (256, or 128 for token-major X) of a tiled int8 GEMM launch.
 int tiled_tile_width(const GemmArgs& g);
+// Few-token GEMM in the Linear layout (token-major, N <= 16) with the weight streamed through LDS.
+bool gemm_bf16_fewtok_ok(const GemmArgs& g);
+hipError_t launch_gemm_bf16_fewtok(const GemmArgs& g, hipStream_t s);
 bool gemm_bf16_tiled_ok(const GemmArgs& g);
 hipError_t launch_gemm_bf16_tiled(const GemmArgs& g, hipStream_t s);
 

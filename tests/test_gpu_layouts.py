@@ -52,6 +52,16 @@ TM_SHAPES = [
     (600, 208, 16, 208, 600),
     (300, 320, 8, 321, 304),
     (1040, 1088, 64, 1088, 1040),
+    # few-token kernel with the weight streamed through LDS (N <= 2, or N <= 8 below 1024 row blocks;
+    # 16-byte rows): 4, 8 and 16 waves, 2- and 8-row X tiles, K tails (80, 208, 240), one K tile per
+    # wave or several; and N = 9 .. 16 on the register-pipelined kernel
+    (9000, 192, 16, 200, 9000),
+    (4000, 320, 12, 320, 4000),
+    (3100, 256, 3, 264, 3100),
+    (2050, 240, 9, 248, 2056),
+    (5000, 4096, 1, 4096, 5000),
+    (1000, 256, 7, 256, 1000),
+    (1000, 240, 2, 248, 1008),
     # LDS-tiled kernel (K % 64 == 0, N > 64): ragged M and N, padded pitches
     (1000, 512, 777, 512, 1000),
     (64, 64, 65, 72, 64),
@@ -90,6 +100,8 @@ BATCH_SHAPES = [
     (2, 128, 256, 100, "token"),
     (3, 48, 64, 20, "token"),
     (2, 300, 208, 90, "token"),
+    (3, 200, 320, 12, "token"),
+    (2, 200, 320, 6, "token"),
 ]
 
 
