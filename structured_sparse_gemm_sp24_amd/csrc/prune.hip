@@ -124,8 +124,15 @@ __global__ __launch_bounds__(256) void prune_compress_kernel(const void* __restr
             const int64_t c = c0 + 4 * g;
             if (row_ok && c < K) {
                 uint32_t key[4];
+                float nv[4] = {0.f, 0.f, 0.f, 0.f};
+                if constexpr (WANDA) {
+                    // c is a multiple of 4, the group lies inside K and norms is 16-byte aligned (checked
+                    // on the host): one 16-byte load
+                    const f32x4 n4 = *reinterpret_cast<const f32x4*>(norms + c);
+                    nv[0] = n4[0]; nv[1] = n4[1]; nv[2] = n4[2]; nv[3] = n4[3];
+                }
 #pragma unroll
-                for (int e = 0; e < 4; e++) key[e] = select_key<DT, WANDA>(x[i][4 * g + e], WANDA ? norms[c + e] : 0.f);
+                for (int e = 0; e < 4; e++) key[e] = select_key<DT, WANDA>(x[i][4 * g + e], nv[e]);
                 int lo, hi;
                 knockout_top2(key, lo, hi);
                 mbits |= (uint32_t)(lo | (hi << 2)) << (4 * g);

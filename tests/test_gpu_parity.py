@@ -72,6 +72,18 @@ def wanda_norms(seed, K):
 
 # ----------------------------------------------------------------------------- prune / compress
 
+
+def test_prune_wanda_norms_must_be_16_byte_aligned():
+    # the kernel reads the norms of a group of four as one 16-byte load: other alignments are refused
+    M, K = 48, 320
+    W, _, kind = as_dtype(weights_f32(7, M, K), "bf16")
+    say("prune_compress wanda norms one float into their buffer")
+    nbuf = dev(np.concatenate([[np.float32(1.0)], wanda_norms(K + 1, K)]).astype(np.float32))
+    with pytest.raises(sp.Sp24Error) as e:
+        sp.sp24_prune_compress(dev(W, kind), score=sp.SP24_SCORE_WANDA, norms=nbuf[1:])
+    assert e.value.status == sp.SP24_ERR_ALIGN
+
+
 @pytest.mark.parametrize("dt", ["bf16", "fp16", "fp32", "fp32->bf16", "i8"])
 @pytest.mark.parametrize("score", ["magnitude", "wanda"])
 @pytest.mark.parametrize("M,K,ld", [(1, 16, 16), (37, 48, 64), (200, 336, 352), (3, 1024, 1024)])
