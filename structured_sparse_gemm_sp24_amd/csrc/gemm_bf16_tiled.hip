@@ -3,11 +3,12 @@
 //
 // Workgroup tile 256 (M) x BN (N), 4 waves in a 2 x 2 grid, each wave 128 x BN/2 = 8 x BN/32
 // v_smfmac_f32_16x16x64_bf16 fragments. K advances 64 dense columns per stage through LDS stage buffers.
-// Two configurations are launched (see the launcher): BN = 128 with two workgroups per compute unit
+// Three configurations are launched (see the launcher): BN = 128 with two workgroups per compute unit
 // (two waves per SIMD, 128 fp32 accumulators per lane, at most 256 registers per wave), each with two
 // 34 KB stage buffers -- while one workgroup waits at its barrier or for its loads, the other's smfmacs
-// keep the SIMD busy -- and BN = 256 with one workgroup per CU (256 accumulators per lane, three 50 KB
-// buffers). The template also builds BN = 128 with one workgroup per CU and four 34 KB buffers.
+// keep the SIMD busy; BN = 256 with eight waves (two per SIMD, each 128 x 64, 128 accumulators), three
+// 50 KB buffers, token-major; and BN = 256 with four waves (256 accumulators per lane), three 50 KB
+// buffers. The template also builds BN = 128 with one workgroup per CU and four 34 KB buffers.
 //
 // Global -> LDS uses buffer loads with LDS destination (no VGPR staging). The whole byte offset of
 // each load is in its VGPR operand, which the buffer range check covers (the SGPR offset is not
@@ -64,16 +65,20 @@ constexpr int GROUP_M = 8;
 // OCC_ = 2: two workgroups per compute unit (two waves per SIMD, at most 256 registers each), with
 // two stage buffers each (2 x 2 x 34 KB of LDS), for the 128-wide tile only: one workgroup's smfmacs can
 // run while the other waits at its barrier or for its loads.
-template <int BN_, int OCC_ = 1>
+// WAVES_ = 8: one workgroup of eight waves (two per SIMD, a 2 x 4 grid of 128 x BN/4 wave tiles) shares the
+// 256-wide tile's loads, for two waves per SIMD without halving the tile.
+template <int BN_, int OCC_ = 1, int WAVES_ = 4>
 struct Cfg {
-    static_assert(OCC_ == 1 || BN_ == 128, "two workgroups per CU only with the 128-wide tile");
-    static constexpr int BN = BN_, WN = BN_ / 2, FN = WN / 16;
+    static_assert((WAVES_ == 4 && (OCC_ == 1 || BN_ == 128)) || (WAVES_ == 8 && OCC_ == 2 && BN_ == 256),
+                  "supported configurations");
+    static constexpr int WAVES = WAVES_;
+    static constexpr int BN = BN_, WN = BN_ / (WAVES_ / 2), FN = WN / 16;
     static constexpr int B_BYTES = BK * BN * 2;
     static constexpr int B_ROW = BN * 2;  // feature-major B tile row: 512 or 256 bytes
     static constexpr int STAGE_BYTES = A_BYTES + META_BYTES + B_BYTES;
-    static constexpr int NBUF = OCC_ == 2 ? 2 : (BN == 256 ? 3 : 4);  // stage buffers (3 x 50 KB, 4 x 34 KB, 2 x 34 KB)
+    static constexpr int NBUF = (OCC_ == 2 && WAVES_ == 4) ? 2 : (BN == 256 ? 3 : 4);  // 3 x 50 KB, 4 x 34 KB, 2 x 34 KB
     static constexpr int B_LOADS = BN / 32;          // per wave: token-major 8 rows per load, feature-major 1 KB
-    static constexpr int LOADS_PER_STAGE = 4 + 2 + B_LOADS;  // per wave: A, metadata, B
+    static constexpr int LOADS_PER_STAGE = (4 + 2 + B_LOADS) / (WAVES_ / 4);  // per wave: A, metadata, B
 };
 constexpr uint32_t RSRC_FLAGS = 0x00020000u;
 
@@ -204,22 +209,27 @@ __device__ __forceinline__ LoadOffsets load_offsets(const Args& a, int lane) {
 // block b at (b * tiles + s) * 1 KB of values and * 128 B of metadata). When td is not valid (past the
 // workgroup's last tile) the offsets get bit 31 set, past every record count, so the loads return
 // zeros without memory traffic (and X's record count is 0).
-template <bool TM, int BNT>
-__device__ __forceinline__ void load_stage(uint32_t lds, const Args& a, const TileDesc& td, int s, int wave,
+template <bool TM, int BNT, int WAVES>
+__device__ __forceinline__ void load_stage(uint32_t lds, const Args& a, const TileDesc& td, int s, int wave_,
                                            const LoadOffsets& lo) {
     using C = Cfg<BNT>;
+    // with eight waves, wave w issues half (part w & 1) of the loads wave w / 2 issues with four
+    constexpr int PARTS = WAVES / 4;
+    const int wave = wave_ / PARTS, part = wave_ % PARTS;
     const int64_t k0 = (int64_t)s * BK;
     const int tiles = (int)((a.K + BK - 1) / BK);
     const uint32_t past = td.valid ? 0u : 0x80000000u;
     // A: one 1 KB tile per 16-row block, copied as is (it is already in lane order)
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
+    for (int jj = 0; jj < 4 / PARTS; jj++) {
+        const int j = part * (4 / PARTS) + jj;
         const int b = 4 * wave + j;
         dma16(lds + b * 1024, lo.a + (((uint32_t)(b * tiles + s) * 1024u) | past), td.rA);
     }
     // metadata: one 128 B tile per block; 4 blocks per wave, two per dword instruction
 #pragma unroll
-    for (int h = 0; h < 2; h++) {
+    for (int hh = 0; hh < 2 / PARTS; hh++) {
+        const int h = part * (2 / PARTS) + hh;
         const int b = 4 * wave + 2 * h;
         dma4(lds + A_BYTES + b * 128, lo.m + (((uint32_t)(b * tiles + s) * 128u) | past), td.rM);
     }
@@ -230,7 +240,8 @@ __device__ __forceinline__ void load_stage(uint32_t lds, const Args& a, const Ti
         const i32x4 rB =
             make_rsrc(td.x + td.n0 * a.ldx + k0, td.valid ? ((a.N - 1 - td.n0) * a.ldx + a.K - k0) * 2 : 0);
 #pragma unroll
-        for (int h = 0; h < C::B_LOADS; h++) {
+        for (int hh = 0; hh < C::B_LOADS / PARTS; hh++) {
+            const int h = part * (C::B_LOADS / PARTS) + hh;
             const int row = (BNT / 4) * wave + 8 * h;
             dma16(lds + A_BYTES + META_BYTES + row * 128, lo.b[h & 1] + (uint32_t)(row * a.ldx * 2), rB);
         }
@@ -240,7 +251,8 @@ __device__ __forceinline__ void load_stage(uint32_t lds, const Args& a, const Ti
         const i32x4 rB =
             make_rsrc(td.x + k0 * a.ldx + td.n0, td.valid ? ((a.K - 1 - k0) * a.ldx + a.N - td.n0) * 2 : 0);
 #pragma unroll
-        for (int h = 0; h < 4; h++) {
+        for (int hh = 0; hh < 4 / PARTS; hh++) {
+            const int h = part * (4 / PARTS) + hh;
             const int row = 16 * wave + 4 * h;
             dma16(lds + A_BYTES + META_BYTES + row * 256, lo.b[h >> 1] + (uint32_t)(row * a.ldx * 2), rB);
         }
@@ -252,7 +264,8 @@ __device__ __forceinline__ void load_stage(uint32_t lds, const Args& a, const Ti
         const i32x4 rB =
             make_rsrc(td.x + k0 * a.ldx + td.n0, td.valid ? ((a.K - 1 - k0) * a.ldx + a.N - td.n0) * 2 : 0);
 #pragma unroll
-        for (int h = 0; h < 8; h++) {
+        for (int hh = 0; hh < 8 / PARTS; hh++) {
+            const int h = part * (8 / PARTS) + hh;
             const int row = 16 * wave + 2 * h;
             dma16(lds + A_BYTES + META_BYTES + row * 512,
                   lo.b[(h & 1) | ((h >> 2) << 1)] + (uint32_t)(row * a.ldx * 2), rB);
@@ -287,7 +300,7 @@ __device__ __forceinline__ TileDesc tile_desc(const Args& a, int L) {
 }
 
 // Lane-dependent LDS byte offsets used by compute_stage (computed once per kernel).
-template <int FNT>
+template <int FNT, int BROW>  // fragments per wave, bytes per row of the feature-major B tile
 struct LaneOffsets {
     int a;        // A fragment of block wm0/16: block * 1024 + lane * 16
     int m;        // metadata of block wm0/16: A_BYTES + block * 128 + lane * 2
@@ -295,10 +308,10 @@ struct LaneOffsets {
                   // two reads of fragment 0 (b[0], b[1]; fragment j adds 16 rows x 128 B)
 };
 
-template <bool TM, int FNT>
-__device__ __forceinline__ LaneOffsets<FNT> lane_offsets(int wm0, int wn0, int lane) {
+template <bool TM, int FNT, int BROW>
+__device__ __forceinline__ LaneOffsets<FNT, BROW> lane_offsets(int wm0, int wn0, int lane) {
     const int r = lane & 15, q = lane >> 4;
-    LaneOffsets<FNT> o;
+    LaneOffsets<FNT, BROW> o;
     o.a = (wm0 >> 4) * 1024 + lane * 16;
     o.m = A_BYTES + (wm0 >> 4) * 128 + lane * 2;
     if constexpr (TM) {
@@ -311,7 +324,7 @@ __device__ __forceinline__ LaneOffsets<FNT> lane_offsets(int wm0, int wn0, int l
     }
     // read t of group q covers rows 8q + 4(t&1) + 32(t>>1) + r/4, which all have the row & 3 and
     // (row >> 3) & 1 of row0, so the unit swizzle is fixed per lane and t only adds immediates
-    constexpr int B_ROW = 64 * FNT;  // bytes per row of the feature-major B tile
+    constexpr int B_ROW = BROW;
     const int row0 = 8 * q + (r >> 2);
     const int v = ((row0 & 3) << 1) | ((row0 >> 3) & 1);
 #pragma unroll
@@ -339,8 +352,8 @@ __device__ __forceinline__ uint32_t stage_addr(uint32_t buf, int off) {
     return v;
 }
 
-template <int FNT>
-__device__ __forceinline__ void read_a(uint32_t buf, const LaneOffsets<FNT>& o, AFrags& f) {
+template <int FNT, int BROW>
+__device__ __forceinline__ void read_a(uint32_t buf, const LaneOffsets<FNT, BROW>& o, AFrags& f) {
     const lds_char* pa = (const lds_char*)(size_t)stage_addr(buf, o.a);
     const lds_char* pm = (const lds_char*)(size_t)stage_addr(buf, o.m);
 #pragma unroll
@@ -352,8 +365,8 @@ __device__ __forceinline__ void read_a(uint32_t buf, const LaneOffsets<FNT>& o, 
 
 // B fragment j (16 columns x 64 k) of the stage in buffer `buf`: four transposing reads, or, token-
 // major, two 16-byte reads of the lane's token row.
-template <bool TM, int FNT>
-__device__ __forceinline__ bf16x16 read_b(uint32_t buf, const LaneOffsets<FNT>& o, int j) {
+template <bool TM, int FNT, int BROW>
+__device__ __forceinline__ bf16x16 read_b(uint32_t buf, const LaneOffsets<FNT, BROW>& o, int j) {
     if constexpr (TM) {
         typedef const __attribute__((address_space(3))) u32x4 lds_u32x4;
         const lds_char* p0 = (const lds_char*)(size_t)stage_addr(buf, o.b[0]);
@@ -362,7 +375,7 @@ __device__ __forceinline__ bf16x16 read_b(uint32_t buf, const LaneOffsets<FNT>& 
         const u32x4 hi = *reinterpret_cast<lds_u32x4*>(p1 + j * 2048);
         return __builtin_bit_cast(bf16x16, u32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
     }
-    constexpr int B_ROW = 64 * FNT;  // bytes per row of the feature-major B tile
+    constexpr int B_ROW = BROW;
     const lds_char* p = (const lds_char*)(size_t)stage_addr(buf, o.b[j]);
     u32x8 b;
 #pragma unroll
@@ -386,11 +399,13 @@ __device__ __forceinline__ void mfma_block(f32x4 (&acc)[FM][FNT], const AFrags& 
 // One K stage (see the pipeline description in the kernel): stage s of the current tile, g-th stage of
 // the workgroup overall (selects the buffer). The loads it issues are those of stage s + NBUF of the
 // current tile or, past its end, stage s + NBUF - S of the next one. No branches.
-template <bool TM, int BNT, int OCC>
+template <bool TM, int BNT, int OCC, int WAVES>
 __device__ __forceinline__ void stage(uint32_t l0, const Args& a, const TileDesc& cur_t, const TileDesc& next_t, int s,
-                                      int S, int g, f32x4 (&acc)[FM][Cfg<BNT>::FN], AFrags& f, bf16x16 (&rb)[4],
-                                      const LaneOffsets<Cfg<BNT>::FN>& o, int wave, const LoadOffsets& lo) {
-    using C = Cfg<BNT, OCC>;
+                                      int S, int g, f32x4 (&acc)[FM][Cfg<BNT, OCC, WAVES>::FN], AFrags& f,
+                                      bf16x16 (&rb)[4],
+                                      const LaneOffsets<Cfg<BNT, OCC, WAVES>::FN, Cfg<BNT>::B_ROW>& o, int wave,
+                                      const LoadOffsets& lo) {
+    using C = Cfg<BNT, OCC, WAVES>;
     constexpr int F = C::FN, NB = C::NBUF;
     const int cb = g % NB;
     const uint32_t cur = l0 + cb * C::STAGE_BYTES;
@@ -406,7 +421,7 @@ __device__ __forceinline__ void stage(uint32_t l0, const Args& a, const TileDesc
     wait_vmcnt<(NB - 2) * C::LOADS_PER_STAGE>();  // stage g+1 has landed (later ones may be in flight)
     __builtin_amdgcn_s_barrier();
     const bool here = s + NB < S;
-    load_stage<TM, BNT>(cur, a, here ? cur_t : next_t, here ? s + NB : s + NB - S, wave, lo);
+    load_stage<TM, BNT, WAVES>(cur, a, here ? cur_t : next_t, here ? s + NB : s + NB - S, wave, lo);
     rb[0] = read_b<TM>(nxt, o, 0);
     rb[1] = read_b<TM>(nxt, o, 1);
     __builtin_amdgcn_sched_barrier(0);
@@ -551,9 +566,10 @@ __device__ __forceinline__ void store_tile_tm(const f32x4 (&acc)[FM][FNT], const
     }
 }
 
-template <bool OUT_FP32, bool TM, int BNT, int OCC>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void gemm_bf16_tiled_kernel(Args a) {
-    using C = Cfg<BNT, OCC>;
+template <bool OUT_FP32, bool TM, int BNT, int OCC, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void gemm_bf16_tiled_kernel(
+    Args a) {
+    using C = Cfg<BNT, OCC, WAVES>;
     constexpr int NB = C::NBUF, F = C::FN;
     __shared__ __attribute__((aligned(16))) char smem[NB * C::STAGE_BYTES];
     // LDS byte address of the first stage buffer (for the LDS-destination loads)
@@ -563,8 +579,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
     int L = tile_of(a, p, 0);
     if (L < 0) return;  // whole workgroup
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    const int wm0 = (wave >> 1) * WM, wn0 = (wave & 1) * C::WN;
-    const LaneOffsets<F> o = lane_offsets<TM, F>(wm0, wn0, lane);
+    const int wm0 = (wave / (WAVES / 2)) * WM, wn0 = (wave % (WAVES / 2)) * C::WN;
+    const LaneOffsets<F, C::B_ROW> o = lane_offsets<TM, F, C::B_ROW>(wm0, wn0, lane);
     const LoadOffsets lo = load_offsets<TM, BNT>(a, lane);
     const int S = (int)((a.K + BK - 1) / BK);
 
@@ -590,11 +606,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
     TileDesc next_t = tile_desc<OUT_FP32, BNT>(a, tile_of(a, p, 1));
 #pragma unroll
     for (int i = 0; i < NB - 1; i++)
-        load_stage<TM, BNT>(l0 + i * C::STAGE_BYTES, a, S > i ? cur_t : next_t, S > i ? i : 0, wave, lo);
+        load_stage<TM, BNT, WAVES>(l0 + i * C::STAGE_BYTES, a, S > i ? cur_t : next_t, S > i ? i : 0, wave, lo);
     wait_vmcnt<(NB - 2) * C::LOADS_PER_STAGE>();
     __builtin_amdgcn_s_barrier();
-    load_stage<TM, BNT>(l0 + (NB - 1) * C::STAGE_BYTES, a, S > NB - 1 ? cur_t : next_t, S > NB - 1 ? NB - 1 : 0, wave,
-                        lo);
+    load_stage<TM, BNT, WAVES>(l0 + (NB - 1) * C::STAGE_BYTES, a, S > NB - 1 ? cur_t : next_t, S > NB - 1 ? NB - 1 : 0,
+                               wave, lo);
 
     AFrags fa;
     bf16x16 rb[4];
@@ -603,7 +619,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
     rb[1] = read_b<TM>(l0, o, 1);
     int g = 0;
     for (int k = 1;; k++) {
-        for (int s = 0; s < S; s++, g++) stage<TM, BNT, OCC>(l0, a, cur_t, next_t, s, S, g, acc, fa, rb, o, wave, lo);
+        for (int s = 0; s < S; s++, g++)
+            stage<TM, BNT, OCC, WAVES>(l0, a, cur_t, next_t, s, S, g, acc, fa, rb, o, wave, lo);
         // epilogue from registers; the next tile's first stages are in flight meanwhile
         {
             const int64_t mw = cur_t.m0 + wm0, nw = cur_t.n0 + wn0;
@@ -670,9 +687,9 @@ int tiled_tile_width(const GemmArgs& g) {
     return c128 < c256 ? 128 : 256;
 }
 
-template <int BNT, int OCC>
+template <int BNT, int OCC, int WAVES = 4>
 static hipError_t launch_bn(const GemmArgs& g, hipStream_t s) {
-    using C = tiled_bf16::Cfg<BNT, OCC>;
+    using C = tiled_bf16::Cfg<BNT, OCC, WAVES>;
     tiled_bf16::Args a;
     a.vals = static_cast<const uint16_t*>(g.values); a.meta = g.meta;
     a.X = static_cast<const uint16_t*>(g.X); a.Y = g.Y;
@@ -687,33 +704,37 @@ static hipError_t launch_bn(const GemmArgs& g, hipStream_t s) {
               (g.batch == 1 || (g.sy * es) % 16 == 0) && g.ldy * es * 16 < ((int64_t)1 << 31);
     const int T = a.tilesM * a.tilesN * a.batch;
     const int S = (int)((g.K + tiled_bf16::BK - 1) / tiled_bf16::BK);
-    // OCC workgroups per compute unit walking several tiles; one tile each when a tile has fewer stages
-    // than there are stage buffers (the cross-tile pipeline then has nothing to overlap)
-    const int slots = device_cus() * OCC;
+    // OCC / (WAVES / 4) workgroups per compute unit walking several tiles; one tile each when a tile has
+    // fewer stages than there are stage buffers (the cross-tile pipeline then has nothing to overlap)
+    const int slots = device_cus() * OCC / (WAVES / 4);
     const unsigned grid = (unsigned)(S >= C::NBUF && T > slots ? slots : T);
-    if (g.tm) {
+    if (WAVES == 8 || g.tm) {  // eight waves: token-major only (the launcher's choice)
         if (g.out_fp32)
-            hipLaunchKernelGGL((tiled_bf16::gemm_bf16_tiled_kernel<true, true, BNT, OCC>), dim3(grid), dim3(256), 0, s, a);
+            hipLaunchKernelGGL((tiled_bf16::gemm_bf16_tiled_kernel<true, true, BNT, OCC, WAVES>), dim3(grid), dim3(64 * WAVES), 0, s, a);
         else
-            hipLaunchKernelGGL((tiled_bf16::gemm_bf16_tiled_kernel<false, true, BNT, OCC>), dim3(grid), dim3(256), 0, s, a);
-    } else {
+            hipLaunchKernelGGL((tiled_bf16::gemm_bf16_tiled_kernel<false, true, BNT, OCC, WAVES>), dim3(grid), dim3(64 * WAVES), 0, s, a);
+    } else if constexpr (WAVES == 4) {
         if (g.out_fp32)
-            hipLaunchKernelGGL((tiled_bf16::gemm_bf16_tiled_kernel<true, false, BNT, OCC>), dim3(grid), dim3(256), 0, s, a);
+            hipLaunchKernelGGL((tiled_bf16::gemm_bf16_tiled_kernel<true, false, BNT, OCC, WAVES>), dim3(grid), dim3(64 * WAVES), 0, s, a);
         else
-            hipLaunchKernelGGL((tiled_bf16::gemm_bf16_tiled_kernel<false, false, BNT, OCC>), dim3(grid), dim3(256), 0, s, a);
+            hipLaunchKernelGGL((tiled_bf16::gemm_bf16_tiled_kernel<false, false, BNT, OCC, WAVES>), dim3(grid), dim3(64 * WAVES), 0, s, a);
     }
     return hipGetLastError();
 }
 
-// Configuration of a bf16 launch, measured on MI355X against one workgroup per CU with 256 x 256 or
-// 256 x 128 tiles (bit-identical results: the K order inside a tile does not depend on the tile shape):
-// 256 x 128 tiles with two workgroups per compute unit win by far when the 256-wide tiles need at most two
-// turns of the compute units (3072 x 768 x 6304 token-major: 48.4 / 41.9 -> 34.5 us; 768 x 3072 x 8192:
-// 61.9 / 41.0 -> 40.6 us) and tie on one to three turns of large tiles (4096^3, 11008 x 4096 x 4096); with
-// many turns the 256 x 256 tile keeps its edge in re-use (28672 x 8192 x 8192: 1977 against 2068 us).
+// Configuration of a bf16 launch, measured on MI355X against one workgroup of four waves per CU with 256 x 256
+// tiles (bit-identical results: the K order inside a tile does not depend on the tile shape):
+//  - up to two turns of the compute units with 256 x 256 tiles: 256 x 128 tiles with two workgroups per
+//    CU, which fill the last turn better and keep a second wave per SIMD (3072 x 768 x 6304 token-major:
+//    48.0 -> 34.3 us; 768 x 3072 x 8192: 62.8 -> 38.8 us; 4096^3, one turn: 84.5 against 90.5 us);
+//  - more turns, token-major: 256 x 256 tiles with eight waves per workgroup, two per SIMD, so the big
+//    tile's re-use stays and a second wave covers each one's barrier and load waits (11008 x 4096 x 4096:
+//    235.4 -> 212.2 us; 28672 x 8192 x 8192: 2115 -> 1986 us); feature-major keeps four waves (its
+//    eight-wave build spills registers).
 hipError_t launch_gemm_bf16_tiled(const GemmArgs& g, hipStream_t s) {
     const int64_t t256 = ((g.M + 255) / 256) * ((g.N + 255) / 256) * g.batch;
-    return t256 <= 2 * (int64_t)device_cus() ? launch_bn<128, 2>(g, s) : launch_bn<256, 1>(g, s);
+    if (t256 <= 2 * (int64_t)device_cus()) return launch_bn<128, 2>(g, s);
+    return g.tm ? launch_bn<256, 2, 8>(g, s) : launch_bn<256, 1>(g, s);
 }
 
 }  // namespace sp24
