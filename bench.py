@@ -6,8 +6,10 @@ of the layer's 6304 tokens (bf16 in and out). By default the activations are tok
 Linear layer holds them (X 6304 x 768, Y 6304 x 3072); --layout feature uses X 768 x 6304 and
 Y 3072 x 6304 instead (the same products). Other workloads (--workload, --n) cover the single 256 x 256
 Linear, the BERT-base int8 FFN pair, the LLM projections with Wanda scoring and the 28672 x 8192 FFN
-sweep. Inputs are resident in HBM before timing; steps rotate over enough copies of every buffer
-(> 2x the 256 MB Infinity Cache, when they fit) that each step reads its operands from HBM.
+sweep, and the BERT FFN as one fused int8 chain. Inputs are resident in HBM before timing; steps rotate
+over enough copies of every buffer that each kernel's launches cycle over more than twice the 256 MB
+Infinity Cache (within a memory budget), so each launch reads its operands from HBM. The roofline also
+carries the sustained shader clock under matrix-core load (sp24_probe_sclk) and the MFMA peak scaled to it.
 
 Prints ONE JSON line: the step's dense-equivalent throughput (2*M*N*K per GEMM), the dominant
 kernel's roofline (its average duration from HIP events on the launch stream; algorithmic bytes or
