@@ -345,15 +345,15 @@ static hipError_t launch_pc_tpw(const void* W, int64_t M, int64_t K, int64_t ldw
     return hipGetLastError();
 }
 
-// Four tiles per wave (4 x 32-64 bytes of loads in flight per lane) when that still leaves a few
-// thousand workgroups; one otherwise, so small weights spread over the whole chip.
+// One tile per wave: measured on MI355X against 2, 4 and 8 tiles per wave (more loads in flight per lane,
+// fewer workgroups), one was the fastest at every size (28672 x 8192 bf16: 127.6 us against 142.8 us with
+// four, 72 % of HBM; 11008 x 4096: 27.1 against 30.0 us; Wanda 146 against 150 us), the hardware keeping
+// more, smaller workgroups in flight.
 template <int DT, int VOUT, bool WANDA>
 static hipError_t launch_pc(const void* W, int64_t M, int64_t K, int64_t ldw, const float* norms, void* values,
                             uint8_t* meta, hipStream_t s) {
     int64_t Mp, Kp, tiles;
     padded_dims(M, K, esize<VOUT>(), Mp, Kp, tiles);
-    if ((Mp / 16) * ((tiles + 15) / 16) >= 2048)
-        return launch_pc_tpw<DT, VOUT, WANDA, 4>(W, M, K, ldw, norms, values, meta, Mp, tiles, s);
     return launch_pc_tpw<DT, VOUT, WANDA, 1>(W, M, K, ldw, norms, values, meta, Mp, tiles, s);
 }
 
