@@ -8,7 +8,7 @@
 // 34 KB stage buffers -- while one workgroup waits at its barrier or for its loads, the other's smfmacs
 // keep the SIMD busy; BN = 256 with eight waves (two per SIMD, each 128 x 64, 128 accumulators), three
 // 50 KB buffers, token-major; and BN = 256 with four waves (256 accumulators per lane), three 50 KB
-// buffers. The template also builds BN = 128 with one workgroup per CU and four 34 KB buffers.
+// buffers, feature-major. The template also takes BN = 128 with one workgroup per CU and four 34 KB buffers.
 //
 // Global -> LDS uses buffer loads with LDS destination (no VGPR staging). The whole byte offset of
 // each load is in its VGPR operand, which the buffer range check covers (the SGPR offset is not
@@ -687,7 +687,7 @@ int tiled_tile_width(const GemmArgs& g) {
     return c128 < c256 ? 128 : 256;
 }
 
-template <int BNT, int OCC, int WAVES = 4>
+template <bool TM, int BNT, int OCC, int WAVES = 4>
 static hipError_t launch_bn(const GemmArgs& g, hipStream_t s) {
     using C = tiled_bf16::Cfg<BNT, OCC, WAVES>;
     tiled_bf16::Args a;
@@ -708,17 +708,10 @@ static hipError_t launch_bn(const GemmArgs& g, hipStream_t s) {
     // fewer stages than there are stage buffers (the cross-tile pipeline then has nothing to overlap)
     const int slots = device_cus() * OCC / (WAVES / 4);
     const unsigned grid = (unsigned)(S >= C::NBUF && T > slots ? slots : T);
-    if (WAVES == 8 || g.tm) {  // eight waves: token-major only (the launcher's choice)
-        if (g.out_fp32)
-            hipLaunchKernelGGL((tiled_bf16::gemm_bf16_tiled_kernel<true, true, BNT, OCC, WAVES>), dim3(grid), dim3(64 * WAVES), 0, s, a);
-        else
-            hipLaunchKernelGGL((tiled_bf16::gemm_bf16_tiled_kernel<false, true, BNT, OCC, WAVES>), dim3(grid), dim3(64 * WAVES), 0, s, a);
-    } else if constexpr (WAVES == 4) {
-        if (g.out_fp32)
-            hipLaunchKernelGGL((tiled_bf16::gemm_bf16_tiled_kernel<true, false, BNT, OCC, WAVES>), dim3(grid), dim3(64 * WAVES), 0, s, a);
-        else
-            hipLaunchKernelGGL((tiled_bf16::gemm_bf16_tiled_kernel<false, false, BNT, OCC, WAVES>), dim3(grid), dim3(64 * WAVES), 0, s, a);
-    }
+    if (g.out_fp32)
+        hipLaunchKernelGGL((tiled_bf16::gemm_bf16_tiled_kernel<true, TM, BNT, OCC, WAVES>), dim3(grid), dim3(64 * WAVES), 0, s, a);
+    else
+        hipLaunchKernelGGL((tiled_bf16::gemm_bf16_tiled_kernel<false, TM, BNT, OCC, WAVES>), dim3(grid), dim3(64 * WAVES), 0, s, a);
     return hipGetLastError();
 }
 
@@ -733,8 +726,8 @@ static hipError_t launch_bn(const GemmArgs& g, hipStream_t s) {
 //    eight-wave build spills registers).
 hipError_t launch_gemm_bf16_tiled(const GemmArgs& g, hipStream_t s) {
     const int64_t t256 = ((g.M + 255) / 256) * ((g.N + 255) / 256) * g.batch;
-    if (t256 <= 2 * (int64_t)device_cus()) return launch_bn<128, 2>(g, s);
-    return g.tm ? launch_bn<256, 2, 8>(g, s) : launch_bn<256, 1>(g, s);
+    if (t256 <= 2 * (int64_t)device_cus()) return g.tm ? launch_bn<true, 128, 2>(g, s) : launch_bn<false, 128, 2>(g, s);
+    return g.tm ? launch_bn<true, 256, 2, 8>(g, s) : launch_bn<false, 256, 1>(g, s);
 }
 
 }  // namespace sp24
