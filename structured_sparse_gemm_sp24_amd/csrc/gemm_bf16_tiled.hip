@@ -79,6 +79,15 @@ struct Cfg {
     static constexpr int NBUF = (OCC_ == 2 && WAVES_ == 4) ? 2 : (BN == 256 ? 3 : 4);  // 3 x 50 KB, 4 x 34 KB, 2 x 34 KB
     static constexpr int B_LOADS = BN / 32;          // per wave: token-major 8 rows per load, feature-major 1 KB
     static constexpr int LOADS_PER_STAGE = (4 + 2 + B_LOADS) / (WAVES_ / 4);  // per wave: A, metadata, B
+    // How a wave issues a stage's loads once the barrier has freed its buffer (measured on MI355X):
+    //  0: in one burst (two workgroups per CU: interleaving cost 3-4 %);
+    //  1: interleaved with the smfmacs of the last two fragment blocks (eight waves: even with the burst
+    //     on large N, and carrying some into the next stage was 5-7 % slower);
+    //  2: LPRE of them interleaved with the first FN - 2 blocks of the next stage, in proportion to the
+    //     smfmac slots there, the rest with the last two blocks (four waves of 256 accumulators, eight
+    //     fragment blocks per stage: 7-8 % faster than the burst on 11008 x 4096 x 4096 feature-major).
+    static constexpr int SPREAD = (OCC_ == 2 && WAVES_ == 4) ? 0 : (WAVES_ == 8 ? 1 : 2);
+    static constexpr int LPRE = SPREAD == 2 ? LOADS_PER_STAGE - (2 * LOADS_PER_STAGE + FN / 2) / FN : 0;
 };
 constexpr uint32_t RSRC_FLAGS = 0x00020000u;
 
@@ -204,73 +213,80 @@ __device__ __forceinline__ LoadOffsets load_offsets(const Args& a, int lane) {
     return o;
 }
 
-// Issue this wave's share of the loads of stage `s` of tile `td` into the stage buffer at LDS address
-// `lds`. td.rA / td.rM cover the compressed tiles of the tile's row blocks (at most 16; tile (b, s) of
+// The loads of one stage (wave-uniform): the stage buffer, the three buffer descriptors and the stage's
+// index. td.rA / td.rM cover the compressed tiles of the tile's row blocks (at most 16; tile (b, s) of
 // block b at (b * tiles + s) * 1 KB of values and * 128 B of metadata). When td is not valid (past the
 // workgroup's last tile) the offsets get bit 31 set, past every record count, so the loads return
 // zeros without memory traffic (and X's record count is 0).
-template <bool TM, int BNT, int WAVES>
-__device__ __forceinline__ void load_stage(uint32_t lds, const Args& a, const TileDesc& td, int s, int wave_,
-                                           const LoadOffsets& lo) {
-    using C = Cfg<BNT>;
-    // with eight waves, wave w issues half (part w & 1) of the loads wave w / 2 issues with four
-    constexpr int PARTS = WAVES / 4;
-    const int wave = wave_ / PARTS, part = wave_ % PARTS;
+struct StageLoads {
+    i32x4 rA, rM, rB;
+    uint32_t lds, past;
+    int s, tiles;
+};
+
+template <bool TM>
+__device__ __forceinline__ StageLoads plan_stage(uint32_t lds, const Args& a, const TileDesc& td, int s) {
+    StageLoads p;
     const int64_t k0 = (int64_t)s * BK;
-    const int tiles = (int)((a.K + BK - 1) / BK);
-    const uint32_t past = td.valid ? 0u : 0x80000000u;
-    // A: one 1 KB tile per 16-row block, copied as is (it is already in lane order)
-#pragma unroll
-    for (int jj = 0; jj < 4 / PARTS; jj++) {
-        const int j = part * (4 / PARTS) + jj;
-        const int b = 4 * wave + j;
-        dma16(lds + b * 1024, lo.a + (((uint32_t)(b * tiles + s) * 1024u) | past), td.rA);
-    }
-    // metadata: one 128 B tile per block; 4 blocks per wave, two per dword instruction
-#pragma unroll
-    for (int hh = 0; hh < 2 / PARTS; hh++) {
-        const int h = part * (2 / PARTS) + hh;
-        const int b = 4 * wave + 2 * h;
-        dma4(lds + A_BYTES + b * 128, lo.m + (((uint32_t)(b * tiles + s) * 128u) | past), td.rM);
-    }
+    p.lds = lds;
+    p.past = td.valid ? 0u : 0x80000000u;
+    p.s = s;
+    p.tiles = (int)((a.K + BK - 1) / BK);
+    p.rA = td.rA;
+    p.rM = td.rM;
     if constexpr (TM) {
-        // B: BNT token rows x 128 B; this wave loads rows BNT/4 * wave .. +BNT/4-1, 8 rows per instruction.
         // X's extent from this stage's corner: N - 1 - n0 rows of pitch ldx plus K - k0 elements, so
         // token rows past N read zeros (K is a multiple of 64: no stage reaches past K)
-        const i32x4 rB =
-            make_rsrc(td.x + td.n0 * a.ldx + k0, td.valid ? ((a.N - 1 - td.n0) * a.ldx + a.K - k0) * 2 : 0);
-#pragma unroll
-        for (int hh = 0; hh < C::B_LOADS / PARTS; hh++) {
-            const int h = part * (C::B_LOADS / PARTS) + hh;
-            const int row = (BNT / 4) * wave + 8 * h;
-            dma16(lds + A_BYTES + META_BYTES + row * 128, lo.b[h & 1] + (uint32_t)(row * a.ldx * 2), rB);
-        }
-    } else if constexpr (BNT == 128) {
-        // B: 64 rows x 256 B; this wave loads rows 16 wave .. +15, four rows per instruction (rows
-        // 16 wave + 4h + lane / 16: row & 3 = lane / 16, (row >> 3) & 1 = h >> 1).
-        const i32x4 rB =
-            make_rsrc(td.x + k0 * a.ldx + td.n0, td.valid ? ((a.K - 1 - k0) * a.ldx + a.N - td.n0) * 2 : 0);
-#pragma unroll
-        for (int hh = 0; hh < 4 / PARTS; hh++) {
-            const int h = part * (4 / PARTS) + hh;
-            const int row = 16 * wave + 4 * h;
-            dma16(lds + A_BYTES + META_BYTES + row * 256, lo.b[h >> 1] + (uint32_t)(row * a.ldx * 2), rB);
-        }
+        p.rB = make_rsrc(td.x + td.n0 * a.ldx + k0, td.valid ? ((a.N - 1 - td.n0) * a.ldx + a.K - k0) * 2 : 0);
     } else {
-        // B: 64 rows x 512 B; this wave loads rows 16*wave .. +15, two rows per instruction (rows
-        // 16 wave + 2h + lane / 32: row & 3 = 2 (h & 1) + lane / 32, (row >> 3) & 1 = h >> 2).
         // X's exact extent from this stage's corner ((K - 1) rows of pitch ldx plus N elements); make_rsrc
         // rounds it up to whole dwords (the range check passes a dword only if all of it is in range)
-        const i32x4 rB =
-            make_rsrc(td.x + k0 * a.ldx + td.n0, td.valid ? ((a.K - 1 - k0) * a.ldx + a.N - td.n0) * 2 : 0);
-#pragma unroll
-        for (int hh = 0; hh < 8 / PARTS; hh++) {
-            const int h = part * (8 / PARTS) + hh;
-            const int row = 16 * wave + 2 * h;
-            dma16(lds + A_BYTES + META_BYTES + row * 512,
-                  lo.b[(h & 1) | ((h >> 2) << 1)] + (uint32_t)(row * a.ldx * 2), rB);
-        }
+        p.rB = make_rsrc(td.x + k0 * a.ldx + td.n0, td.valid ? ((a.K - 1 - k0) * a.ldx + a.N - td.n0) * 2 : 0);
     }
+    return p;
+}
+
+// Load number `ord` (0 .. LOADS_PER_STAGE - 1) of this wave's share of a stage: first the A tiles, then
+// the metadata, then the B rows. With eight waves, wave w issues half (part w & 1) of the loads wave w / 2
+// issues with four.
+template <bool TM, int BNT, int WAVES>
+__device__ __forceinline__ void issue_load(const StageLoads& p, const Args& a, int ord, int wave_, const LoadOffsets& lo) {
+    constexpr int PARTS = WAVES / 4, NA = 4 / PARTS, NM = 2 / PARTS;
+    const int wave = wave_ / PARTS, part = wave_ % PARTS;
+    if (ord < NA) {
+        // A: one 1 KB tile per 16-row block, copied as is (it is already in lane order)
+        const int b = 4 * wave + part * NA + ord;
+        dma16(p.lds + b * 1024, lo.a + (((uint32_t)(b * p.tiles + p.s) * 1024u) | p.past), p.rA);
+    } else if (ord < NA + NM) {
+        // metadata: one 128 B tile per block; 4 blocks per wave, two per dword instruction
+        const int b = 4 * wave + 2 * (part * NM + ord - NA);
+        dma4(p.lds + A_BYTES + b * 128, lo.m + (((uint32_t)(b * p.tiles + p.s) * 128u) | p.past), p.rM);
+    } else if constexpr (TM) {
+        // B: BNT token rows x 128 B; wave w / PARTS loads rows BNT/4 * (w / PARTS) .., 8 rows per load
+        const int h = part * (Cfg<BNT>::B_LOADS / PARTS) + ord - NA - NM;
+        const int row = (BNT / 4) * wave + 8 * h;
+        dma16(p.lds + A_BYTES + META_BYTES + row * 128, lo.b[h & 1] + (uint32_t)(row * a.ldx * 2), p.rB);
+    } else if constexpr (BNT == 128) {
+        // B: 64 rows x 256 B; rows 16 wave .. +15, four rows per load (rows 16 wave + 4h + lane / 16:
+        // row & 3 = lane / 16, (row >> 3) & 1 = h >> 1)
+        const int h = part * (4 / PARTS) + ord - NA - NM;
+        const int row = 16 * wave + 4 * h;
+        dma16(p.lds + A_BYTES + META_BYTES + row * 256, lo.b[h >> 1] + (uint32_t)(row * a.ldx * 2), p.rB);
+    } else {
+        // B: 64 rows x 512 B; rows 16 wave .. +15, two rows per load (rows 16 wave + 2h + lane / 32:
+        // row & 3 = 2 (h & 1) + lane / 32, (row >> 3) & 1 = h >> 2)
+        const int h = part * (8 / PARTS) + ord - NA - NM;
+        const int row = 16 * wave + 2 * h;
+        dma16(p.lds + A_BYTES + META_BYTES + row * 512, lo.b[(h & 1) | ((h >> 2) << 1)] + (uint32_t)(row * a.ldx * 2),
+              p.rB);
+    }
+}
+
+// Loads [O0, O1) of a stage, back to back.
+template <bool TM, int BNT, int WAVES, int O0, int O1>
+__device__ __forceinline__ void issue_loads(const StageLoads& p, const Args& a, int wave, const LoadOffsets& lo) {
+#pragma unroll
+    for (int k = O0; k < O1; k++) issue_load<TM, BNT, WAVES>(p, a, k, wave, lo);
 }
 
 // Tile descriptor of logical tile L (-1: none). Batch entries follow each other; inside one, tiles
@@ -389,43 +405,71 @@ __device__ __forceinline__ bf16x16 read_b(uint32_t buf, const LaneOffsets<FNT, B
     return __builtin_bit_cast(bf16x16, b);
 }
 
-template <int FNT>
-__device__ __forceinline__ void mfma_block(f32x4 (&acc)[FM][FNT], const AFrags& f, const bf16x16& b, int j) {
+// Loads still to be issued for an earlier stage: this wave issues a stage's loads partly after the barrier
+// that frees its buffer and partly during the first fragment blocks of the next stage (see `stage`).
+// nxt: the loads belong to the tile after the current one; s: their stage index in that tile.
+struct Pending {
+    bool nxt;
+    int s;
+};
+
+// Fragment block j (FM smfmacs), with loads O0 + k, k < N, of `p` interleaved: a region of R smfmac slots
+// starting at slot `first` of this block takes load k after its slot (k * R) / N, so the wave never
+// queues more than a load or two at the texture unit while it has smfmacs to issue.
+template <bool TM, int BNT, int WAVES, int FNT, int N, int R, int O0>
+__device__ __forceinline__ void mfma_block(f32x4 (&acc)[FM][FNT], const AFrags& f, const bf16x16& b, int j, int first,
+                                           const StageLoads& p, const Args& a, int wave, const LoadOffsets& lo) {
 #pragma unroll
-    for (int i = 0; i < FM; i++)
+    for (int i = 0; i < FM; i++) {
         acc[i][j] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(f.a[i], b, acc[i][j], (int)f.idx[i], 0, 0);
+#pragma unroll
+        for (int k = 0; k < N; k++)
+            if ((k * R) / N == first + i) issue_load<TM, BNT, WAVES>(p, a, O0 + k, wave, lo);
+        if constexpr (N > 0) __builtin_amdgcn_sched_barrier(0);
+    }
 }
 
-// One K stage (see the pipeline description in the kernel): stage s of the current tile, g-th stage of
-// the workgroup overall (selects the buffer). The loads it issues are those of stage s + NBUF of the
-// current tile or, past its end, stage s + NBUF - S of the next one. No branches.
+// One K stage: stage s of the current tile, g-th stage of the workgroup overall (selects the buffer).
+// The loads of stage s + NBUF of the current tile (or, past its end, stage s + NBUF - S of the next) go
+// into this stage's buffer once the barrier has freed it, in one of the patterns Cfg::SPREAD selects;
+// in pattern 2 the last LPRE of them are issued during the first F - 2 blocks of the next stage (the
+// `pend` loads; three buffers). The vmcnt wait is the same in every pattern: at the barrier of stage g
+// the newest LOADS_PER_STAGE loads are exactly those of stage g + NBUF - 1. No branches.
 template <bool TM, int BNT, int OCC, int WAVES>
 __device__ __forceinline__ void stage(uint32_t l0, const Args& a, const TileDesc& cur_t, const TileDesc& next_t, int s,
                                       int S, int g, f32x4 (&acc)[FM][Cfg<BNT, OCC, WAVES>::FN], AFrags& f,
                                       bf16x16 (&rb)[4],
                                       const LaneOffsets<Cfg<BNT, OCC, WAVES>::FN, Cfg<BNT>::B_ROW>& o, int wave,
-                                      const LoadOffsets& lo) {
+                                      const LoadOffsets& lo, Pending& pend) {
     using C = Cfg<BNT, OCC, WAVES>;
-    constexpr int F = C::FN, NB = C::NBUF;
+    constexpr int F = C::FN, NB = C::NBUF, L = C::LOADS_PER_STAGE;
+    constexpr int LPRE = C::LPRE, LPOST = L - LPRE;
     const int cb = g % NB;
     const uint32_t cur = l0 + cb * C::STAGE_BYTES;
     const uint32_t nxt = l0 + (cb == NB - 1 ? 0 : cb + 1) * C::STAGE_BYTES;
+    StageLoads pp;
+    if constexpr (LPRE > 0)
+        pp = plan_stage<TM>(l0 + (cb == 0 ? NB - 1 : cb - 1) * C::STAGE_BYTES, a, pend.nxt ? next_t : cur_t, pend.s);
 #pragma unroll
     for (int j = 0; j < F - 2; j++) {
         rb[(j + 2) & 3] = read_b<TM>(cur, o, j + 2);
         __builtin_amdgcn_sched_barrier(0);
-        mfma_block(acc, f, rb[j & 3], j);
+        mfma_block<TM, BNT, WAVES, F, LPRE, (F - 2) * FM, LPOST>(acc, f, rb[j & 3], j, j * FM, pp, a, wave, lo);
         __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);           // lgkmcnt(0): this wave's reads of stage g are done
-    wait_vmcnt<(NB - 2) * C::LOADS_PER_STAGE>();  // stage g+1 has landed (later ones may be in flight)
+    wait_vmcnt<(NB - 2) * L>();                   // stage g+1 has landed (later ones may be in flight)
     __builtin_amdgcn_s_barrier();
     const bool here = s + NB < S;
-    load_stage<TM, BNT, WAVES>(cur, a, here ? cur_t : next_t, here ? s + NB : s + NB - S, wave, lo);
+    pend.nxt = !here;
+    pend.s = here ? s + NB : s + NB - S;
+    const StageLoads np = plan_stage<TM>(cur, a, here ? cur_t : next_t, pend.s);
+    if constexpr (C::SPREAD == 0) issue_loads<TM, BNT, WAVES, 0, L>(np, a, wave, lo);
+    constexpr int LI = C::SPREAD == 0 ? 0 : LPOST;  // loads interleaved with the last two blocks
     rb[0] = read_b<TM>(nxt, o, 0);
     rb[1] = read_b<TM>(nxt, o, 1);
     __builtin_amdgcn_sched_barrier(0);
-    mfma_block(acc, f, rb[(F - 2) & 3], F - 2);
+    mfma_block<TM, BNT, WAVES, F, LI, 2 * FM, 0>(acc, f, rb[(F - 2) & 3], F - 2, 0, np, a, wave, lo);
     __builtin_amdgcn_sched_barrier(0);
     // last block: once fragment i has been used for the last time, reload it (and its index) from the
     // next stage, so one A register set serves the whole pipeline
@@ -437,6 +481,9 @@ __device__ __forceinline__ void stage(uint32_t l0, const Args& a, const TileDesc
             __builtin_amdgcn_smfmac_f32_16x16x64_bf16(f.a[i], rb[(F - 1) & 3], acc[i][F - 1], (int)f.idx[i], 0, 0);
         f.a[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(pa + i * 1024));
         f.idx[i] = *reinterpret_cast<const __attribute__((address_space(3))) uint16_t*>(pm + i * 128);
+#pragma unroll
+        for (int k = 0; k < LI; k++)
+            if ((k * 2 * FM) / LI == FM + i) issue_load<TM, BNT, WAVES>(np, a, k, wave, lo);
         __builtin_amdgcn_sched_barrier(0);
     }
 }
@@ -606,11 +653,14 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(OCC,
     TileDesc next_t = tile_desc<OUT_FP32, BNT>(a, tile_of(a, p, 1));
 #pragma unroll
     for (int i = 0; i < NB - 1; i++)
-        load_stage<TM, BNT, WAVES>(l0 + i * C::STAGE_BYTES, a, S > i ? cur_t : next_t, S > i ? i : 0, wave, lo);
+        issue_loads<TM, BNT, WAVES, 0, C::LOADS_PER_STAGE>(
+            plan_stage<TM>(l0 + i * C::STAGE_BYTES, a, S > i ? cur_t : next_t, S > i ? i : 0), a, wave, lo);
     wait_vmcnt<(NB - 2) * C::LOADS_PER_STAGE>();
     __builtin_amdgcn_s_barrier();
-    load_stage<TM, BNT, WAVES>(l0 + (NB - 1) * C::STAGE_BYTES, a, S > NB - 1 ? cur_t : next_t, S > NB - 1 ? NB - 1 : 0,
-                               wave, lo);
+    // stage NB - 1: the loads a stage issues after its barrier; the first stage issues the rest
+    Pending pend{S <= NB - 1, S > NB - 1 ? NB - 1 : 0};
+    issue_loads<TM, BNT, WAVES, 0, C::LOADS_PER_STAGE - C::LPRE>(
+        plan_stage<TM>(l0 + (NB - 1) * C::STAGE_BYTES, a, pend.nxt ? next_t : cur_t, pend.s), a, wave, lo);
 
     AFrags fa;
     bf16x16 rb[4];
@@ -620,7 +670,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(OCC,
     int g = 0;
     for (int k = 1;; k++) {
         for (int s = 0; s < S; s++, g++)
-            stage<TM, BNT, OCC, WAVES>(l0, a, cur_t, next_t, s, S, g, acc, fa, rb, o, wave, lo);
+            stage<TM, BNT, OCC, WAVES>(l0, a, cur_t, next_t, s, S, g, acc, fa, rb, o, wave, lo, pend);
         // epilogue from registers; the next tile's first stages are in flight meanwhile
         {
             const int64_t mw = cur_t.m0 + wm0, nw = cur_t.n0 + wn0;
@@ -643,6 +693,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(OCC,
 #pragma unroll
             for (int j = 0; j < F; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
         cur_t = next_t;
+        pend.nxt = false;  // the pending loads' tile (the next one) is now the current one
         next_t = tile_desc<OUT_FP32, BNT>(a, tile_of(a, p, k + 1));
     }
     wait_vmcnt<0>();  // the zero-filling loads past the last tile have landed before the workgroup ends
