@@ -766,18 +766,28 @@ static hipError_t launch_bn(const GemmArgs& g, hipStream_t s) {
     return hipGetLastError();
 }
 
-// Configuration of a bf16 launch, measured on MI355X against one workgroup of four waves per CU with 256 x 256
-// tiles (bit-identical results: the K order inside a tile does not depend on the tile shape):
-//  - up to two turns of the compute units with 256 x 256 tiles: 256 x 128 tiles with two workgroups per
-//    CU, which fill the last turn better and keep a second wave per SIMD (3072 x 768 x 6304 token-major:
-//    48.0 -> 34.3 us; 768 x 3072 x 8192: 62.8 -> 38.8 us; 4096^3, one turn: 84.5 against 90.5 us);
-//  - more turns, token-major: 256 x 256 tiles with eight waves per workgroup, two per SIMD, so the big
-//    tile's re-use stays and a second wave covers each one's barrier and load waits (11008 x 4096 x 4096:
-//    235.4 -> 212.2 us; 28672 x 8192 x 8192: 2115 -> 1986 us); feature-major keeps four waves (its
-//    eight-wave build spills registers).
+// Configuration of a bf16 launch, measured on MI355X (bit-identical results: the K order inside a tile does
+// not depend on the tile shape):
+//  - 256 x 128 tiles with two workgroups per CU fill the CUs better when there are fewer 256 x 256 tiles
+//    than CUs, and fill a partial last turn better: their last turn's tiles run one per CU, at about 0.6
+//    of a paired turn, while a full turn of 256 x 256 tiles costs about 0.92 of one (3072 x 768 x 6304
+//    token-major: 33.8 us against 37.0 with 256 x 256; 3072 x 4096 x 6304: 122 against 130; 768 x 3072 x
+//    8192: 42.9 against 48.4);
+//  - 256 x 256 tiles otherwise (a full first turn, or more than two turns): token-major with eight waves per
+//    workgroup, two per SIMD, so the big tile's re-use stays and a second wave covers each one's barrier
+//    and load waits (11008 x 4096 x 4096: 235.4 -> 212.2 us against four waves; 28672 x 8192 x 8192:
+//    2115 -> 1986 us; against 256 x 128 two per CU: 4096^3 90.8 -> 83.7 us, 4096 x 4096 x 8192 160 -> 152,
+//    4096 x 2048 x 8192 101 -> 91); feature-major with four waves (its eight-wave build spills registers;
+//    4096^3 82.4 -> 77.7 us).
 hipError_t launch_gemm_bf16_tiled(const GemmArgs& g, hipStream_t s) {
-    const int64_t t256 = ((g.M + 255) / 256) * ((g.N + 255) / 256) * g.batch;
-    if (t256 <= 2 * (int64_t)device_cus()) return g.tm ? launch_bn<true, 128, 2>(g, s) : launch_bn<false, 128, 2>(g, s);
+    const int64_t tm = ((g.M + 255) / 256) * g.batch, cus = device_cus();
+    const int64_t t256 = tm * ((g.N + 255) / 256), t128 = tm * ((g.N + 127) / 128);
+    // turns of each tiling in units of a paired 256 x 128 turn
+    const double c256 = 0.92 * (double)((t256 + cus - 1) / cus);
+    const int64_t rem = t128 % (2 * cus);
+    const double c128 = (double)(t128 / (2 * cus)) + (rem == 0 ? 0.0 : rem <= cus ? 0.6 : 1.0);
+    if (t256 < cus || (t256 <= 2 * cus && c128 <= c256))
+        return g.tm ? launch_bn<true, 128, 2>(g, s) : launch_bn<false, 128, 2>(g, s);
     return g.tm ? launch_bn<true, 256, 2, 8>(g, s) : launch_bn<false, 256, 1>(g, s);
 }
 
