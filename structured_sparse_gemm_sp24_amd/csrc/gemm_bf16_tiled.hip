@@ -499,7 +499,10 @@ __device__ __forceinline__ void stage(uint32_t l0, const Args& a, const TileDesc
 // pitches led to lines evicted and written back twice), one line per quad for bf16 and two for fp32.
 // No LDS is used, so the next tile's loads can land in the stage buffers meanwhile.
 // FULL: the wave's whole 128 x 128 block lies inside Y and vector stores are allowed (then the row
-// offsets of a lane quad fit 32 bits); otherwise every element is bounds-checked.
+// offsets of a lane quad fit 32 bits); otherwise every element is bounds-checked. The vector stores carry
+// the non-temporal hint: Y is not read again by this kernel, and streaming its lines out instead of
+// leaving them dirty in L2 shortens the drain after the last tiles (measured: 3072 x 768 x 6304
+// token-major 33.7 -> 32.2 us, 4096^3 87.6 -> 82.5 us).
 template <bool OUT_FP32, bool FULL, int FNT>
 __device__ __forceinline__ void store_tile(const f32x4 (&acc)[FM][FNT], const Args& a, char* y, int64_t mw, int64_t nw,
                                            int lane) {
@@ -532,9 +535,9 @@ __device__ __forceinline__ void store_tile(const f32x4 (&acc)[FM][FNT], const Ar
                 if constexpr (FULL) {
                     char* const p = y0 + ((16 * i + s) * a.ldy + 64 * jg) * ES + lane_off;
                     if constexpr (OUT_FP32)
-                        *reinterpret_cast<uint4*>(p) = make_uint4(v[s][0], v[s][1], v[s][2], v[s][3]);
+                        __builtin_nontemporal_store(u32x4{v[s][0], v[s][1], v[s][2], v[s][3]}, reinterpret_cast<u32x4*>(p));
                     else
-                        *reinterpret_cast<uint2*>(p) = make_uint2(v[s][0], v[s][1]);
+                        __builtin_nontemporal_store(u32x2{v[s][0], v[s][1]}, reinterpret_cast<u32x2*>(p));
                 } else {
                     const int64_t m = mw + 16 * i + 4 * q + s, n = nw + 64 * jg + 16 * b + 4 * a4;
                     if (m < a.M) {
@@ -590,9 +593,9 @@ __device__ __forceinline__ void store_tile_tm(const f32x4 (&acc)[FM][FNT], const
                 if constexpr (FULL) {
                     char* const p = y0 + ((16 * j + s) * a.ldy + 64 * ig) * ES + lane_off;
                     if constexpr (OUT_FP32)
-                        *reinterpret_cast<uint4*>(p) = make_uint4(v[s][0], v[s][1], v[s][2], v[s][3]);
+                        __builtin_nontemporal_store(u32x4{v[s][0], v[s][1], v[s][2], v[s][3]}, reinterpret_cast<u32x4*>(p));
                     else
-                        *reinterpret_cast<uint2*>(p) = make_uint2(v[s][0], v[s][1]);
+                        __builtin_nontemporal_store(u32x2{v[s][0], v[s][1]}, reinterpret_cast<u32x2*>(p));
                 } else {
                     const int64_t n = nw + 16 * j + 4 * c + s, m = mw + 64 * ig + 16 * x + 4 * q;
                     if (n < a.N) {

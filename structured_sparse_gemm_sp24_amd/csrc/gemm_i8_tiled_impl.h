@@ -390,11 +390,13 @@ __device__ __forceinline__ void store_elem(char* y, int64_t idx, uint32_t bits) 
     else reinterpret_cast<uint32_t*>(y)[idx] = bits;
 }
 
+// One lane's group of output elements, with the non-temporal hint (the output is not read again here;
+// streaming it out shortens the drain after the last tiles: 768 x 3072 x 8192 fp32 out 26.3 -> 24.8 us).
 template <int OUT>
 __device__ __forceinline__ void store_group(char* p, const uint32_t* v) {
-    if constexpr (OutTraits<OUT>::W == 4) *reinterpret_cast<uint4*>(p) = make_uint4(v[0], v[1], v[2], v[3]);
-    else if constexpr (OutTraits<OUT>::W == 2) *reinterpret_cast<uint2*>(p) = make_uint2(v[0], v[1]);
-    else *reinterpret_cast<uint32_t*>(p) = v[0];
+    if constexpr (OutTraits<OUT>::W == 4) __builtin_nontemporal_store(u32x4{v[0], v[1], v[2], v[3]}, reinterpret_cast<u32x4*>(p));
+    else if constexpr (OutTraits<OUT>::W == 2) __builtin_nontemporal_store(u32x2{v[0], v[1]}, reinterpret_cast<u32x2*>(p));
+    else __builtin_nontemporal_store(v[0], reinterpret_cast<uint32_t*>(p));
 }
 
 // The 4 accumulators of one lane and fragment (rows m .. m+3 of one column, or, token-major, 4
