@@ -170,16 +170,24 @@ __global__ __launch_bounds__(256) void prune_compress_kernel(const void* __restr
     }
 }
 
-// One thread per 16-column chunk of the M x K weight.
+// One thread per 16-column chunk of the M x K weight, numbered in the order of the compressed tiles: the 16
+// rows of a row block first, then the chunk's place in the tile's 64-byte rows, then the tile. The lanes
+// of a wave then read whole 1 KB value tiles and their metadata in address order, and (bf16) write 16
+// full 128-byte row segments; numbered row by row, neighbouring lanes read 16 bytes 256 bytes apart
+// (28672 x 8192 bf16: 223 us, 40 % of HBM).
 template <int DT>
 __global__ __launch_bounds__(256) void decompress_kernel(const void* __restrict__ values,
-                                                         const uint8_t* __restrict__ meta, uint32_t chunks_per_row,
-                                                         uint32_t total_chunks, int64_t tiles_per_row,
-                                                         void* __restrict__ W, int64_t ldw) {
+                                                         const uint8_t* __restrict__ meta, uint32_t M,
+                                                         uint32_t chunks_per_row, uint32_t total_threads,
+                                                         int64_t tiles_per_row, void* __restrict__ W, int64_t ldw) {
     const uint32_t t = blockIdx.x * 256u + threadIdx.x;
-    if (t >= total_chunks) return;
-    const uint32_t row = t / chunks_per_row, c = t - row * chunks_per_row;
+    if (t >= total_threads) return;
     constexpr int isz = esize<DT>();
+    constexpr uint32_t CPT = 8 / isz;  // 16-column chunks per 64-byte tile row
+    const uint32_t rest = t >> 4, cq = rest % CPT, tl = rest / CPT;
+    const uint32_t blk = tl / (uint32_t)tiles_per_row, tt = tl - blk * (uint32_t)tiles_per_row;
+    const uint32_t row = 16 * blk + (t & 15), c = tt * CPT + cq;
+    if (row >= M || c >= chunks_per_row) return;
     constexpr int TM = 16 / isz;
     const char* vbase = reinterpret_cast<const char*>(values);
     const int64_t vb = 8 * isz * (int64_t)c;
@@ -385,9 +393,10 @@ static hipError_t launch_dc(const void* values, const uint8_t* meta, int64_t M, 
     int64_t Mp, Kp, tiles;
     padded_dims(M, K, esize<DT>(), Mp, Kp, tiles);
     const uint32_t cpr = (uint32_t)(K / 16);
-    const uint32_t total = (uint32_t)(M * (K / 16));
+    const uint32_t total = (uint32_t)(Mp * tiles * (8 / esize<DT>()));  // one thread per chunk of the padded tiles
     const uint32_t blocks = (total + 255) / 256;
-    hipLaunchKernelGGL(decompress_kernel<DT>, dim3(blocks), dim3(256), 0, s, values, meta, cpr, total, tiles, W_out, ldw);
+    hipLaunchKernelGGL(decompress_kernel<DT>, dim3(blocks), dim3(256), 0, s, values, meta, (uint32_t)M, cpr, total,
+                       tiles, W_out, ldw);
     return hipGetLastError();
 }
 

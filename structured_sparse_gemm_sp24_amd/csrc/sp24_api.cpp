@@ -191,7 +191,7 @@ int sp24_decompress(const void* values, const uint8_t* meta, int dtype, int64_t 
     int st = check_k(K);
     if (st != SP24_OK) return st;
     if (ldw < K) return SP24_ERR_SHAPE;
-    if (M * (K / 16) >= kMaxChunks) return SP24_ERR_SHAPE;
+    if (padded_m(M) * (padded_k(K, elem_size(dtype)) / 16) >= kMaxChunks) return SP24_ERR_SHAPE;  // one thread per padded chunk
     const int isz = elem_size(dtype);
     if (!aligned16(values) || !aligned16(meta) || !aligned16(W_out) || (ldw * isz) % 16 != 0) return SP24_ERR_ALIGN;
     st = check_device();
