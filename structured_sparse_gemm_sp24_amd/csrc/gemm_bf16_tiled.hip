@@ -727,12 +727,11 @@ int device_cus() {
     return cached[dev];
 }
 
-// Tile width for a launch of the tiled int8 GEMM. A 128-wide tile (token-major only) costs about C128 of
+// Tile width for a launch of the tiled int8 GEMM (either layout). A 128-wide tile costs about C128 of
 // a 256-wide one (measured on MI355X), so it wins when the 256-wide tiles leave a last partial turn that
 // the 128-wide ones fill better: e.g. 3072 x 8192 has 384 tiles of 256 x 256 on 256 compute units (two
 // turns), and 768 of 256 x 128 (three turns of the cheaper tile).
 int tiled_tile_width(const GemmArgs& g) {
-    if (!g.tm) return 256;
     constexpr double C128 = 0.6;
     const int64_t cus = device_cus();
     const int64_t tm = (g.M + 255) / 256;

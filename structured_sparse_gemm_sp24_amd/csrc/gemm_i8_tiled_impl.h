@@ -47,10 +47,9 @@ constexpr int A_BYTES = BM * 64;          // 64 kept int8 per row per stage
 constexpr int META_BYTES = BM * 16;       // 64 kept values x 2 bits = 16 bytes per row
 constexpr int GROUP_M = 8;
 constexpr uint32_t RSRC_FLAGS = 0x00020000u;
-constexpr int B_ROW = 256;                // feature-major B tile row: 256 int8 columns
 
-// Tile width BN: 256 (waves of 128 x 128, three 52 KB stage buffers), or 128 for token-major X (waves
-// of 128 x 64, four 36 KB buffers), chosen per launch (tiled_tile_width).
+// Tile width BN: 256 (waves of 128 x 128, three 52 KB stage buffers), or 128 (waves of 128 x 64, four
+// 36 KB buffers), chosen per launch (tiled_tile_width). A feature-major B tile row is BN bytes.
 template <int BN_>
 struct Cfg {
     static constexpr int BN = BN_, WN = BN_ / 2, FN = WN / 16;
@@ -131,6 +130,12 @@ __device__ __forceinline__ int tile_of(const Args& a, int p, int k) {
 
 // Swizzle of the 16-byte units of B row k (see the header).
 __device__ __forceinline__ int bswz(int k) { return (k & 7) | (((k >> 4) & 1) << 3); }
+// The same for the 128-byte rows of the 128-wide feature-major tile (8 units): g(k) = ((k >> 1) & 3) +
+// 4 ((k >> 4) & 1). A read's rows 16q + {0..7} then take bank slots 8 (k & 1) + (u ^ g(k)): groups q and
+// q + 1 together fill all 16 slots once, so each slot serves two rows (the minimum for 512 bytes); g is
+// unchanged by the +8 / +64 row offsets of the reads, and XOR with g keeps each 4-lane group of a
+// global load on one aligned 64-byte run.
+__device__ __forceinline__ int bswz128(int k) { return ((k >> 1) & 3) | (((k >> 4) & 1) << 2); }
 
 // 16-byte unit swizzle of token row n of a token-major B tile.
 __device__ __forceinline__ int tm_swz(int n) { return ((n >> 1) & 7) ^ ((n & 1) << 2); }
@@ -143,7 +148,7 @@ struct LoadOffsets {
                      // token-major: rows 8h + lane / 8 of the wave's 64 (row part relative to the wave's first)
 };
 
-template <bool TM>
+template <bool TM, int BNT>
 __device__ __forceinline__ LoadOffsets load_offsets(const Args& a, int lane, int wave) {
     LoadOffsets o;
     const int tiles = (int)((a.K + BK - 1) / BK);
@@ -158,13 +163,23 @@ __device__ __forceinline__ LoadOffsets load_offsets(const Args& a, int lane, int
             o.b[h] = (uint32_t)(row * a.ldx + 16 * ((lane & 7) ^ tm_swz(row)));
         }
         (void)wave;
-    } else {
+    } else if constexpr (BNT == 256) {
         const int p = lane & 15;  // 16-byte slot in the LDS row
 #pragma unroll
         for (int h = 0; h < 8; h++) {
             const int row = 32 * wave + 4 * h + (lane >> 4);
             o.b[h] = (uint32_t)(row * a.ldx + 16 * (p ^ bswz(row)));
         }
+    } else {
+        // 128-byte rows: lane i of load h lands in row 32 wave + 8h + i / 8, slot i % 8
+        const int p = lane & 7;
+#pragma unroll
+        for (int h = 0; h < 4; h++) {
+            const int row = 32 * wave + 8 * h + (lane >> 3);
+            o.b[h] = (uint32_t)(row * a.ldx + 16 * (p ^ bswz128(row)));
+        }
+#pragma unroll
+        for (int h = 4; h < 8; h++) o.b[h] = 0;
     }
     return o;
 }
@@ -174,7 +189,6 @@ __device__ __forceinline__ LoadOffsets load_offsets(const Args& a, int lane, int
 template <bool TM, int BNT>
 __device__ __forceinline__ void load_stage(uint32_t lds, const Args& a, const TileDesc& td, int s, int wave,
                                            const LoadOffsets& lo) {
-    static_assert(TM || BNT == 256, "feature-major tiles are 256 wide");
     const int64_t k0 = (int64_t)s * BK;
     const int tiles = (int)((a.K + BK - 1) / BK);
     const uint32_t past = td.valid ? 0u : 0x80000000u;
@@ -196,8 +210,10 @@ __device__ __forceinline__ void load_stage(uint32_t lds, const Args& a, const Ti
     } else {
         // X's exact extent from this stage's corner, rounded up to whole dwords (see make_rsrc)
         const i32x4 rB = make_rsrc(td.x + k0 * a.ldx + td.n0, td.valid ? (a.K - 1 - k0) * a.ldx + a.N - td.n0 : 0);
+        // this wave's 32 rows: 4 per load with 256-byte rows, 8 per load with 128-byte rows
+        constexpr int RPL = 1024 / BNT;
 #pragma unroll
-        for (int h = 0; h < 8; h++) dma16(lds + A_BYTES + META_BYTES + (32 * wave + 4 * h) * B_ROW, lo.b[h], rB);
+        for (int h = 0; h < 32 / RPL; h++) dma16(lds + A_BYTES + META_BYTES + (32 * wave + RPL * h) * BNT, lo.b[h], rB);
     }
 }
 
@@ -250,8 +266,9 @@ __device__ __forceinline__ LaneOffsets<FNT> lane_offsets(int wm0, int wn0, int l
     }
     // read t of group q covers rows 16q + 8(t&1) + 64(t>>1) + r/2, which share row & 7 and
     // (row >> 4) & 1 with row0, so the swizzle is fixed per lane and t only adds immediates
+    constexpr int B_ROW = 32 * FNT;  // the tile width in bytes
     const int row0 = 16 * q + (r >> 1);
-    const int f = bswz(row0);
+    const int f = B_ROW == 256 ? bswz(row0) : bswz128(row0);
 #pragma unroll
     for (int j = 0; j < FNT; j++) {
         const int unit = (wn0 >> 4) + j;  // 16 columns = one 16-byte unit
@@ -300,6 +317,7 @@ __device__ __forceinline__ i32x8 read_b(uint32_t buf, const LaneOffsets<FNT>& o,
         const i32x4 hi = *reinterpret_cast<lds_i32x4*>(p1 + j * 2048);
         return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
+    constexpr int B_ROW = 32 * FNT;
     const lds_char* p = (const lds_char*)(size_t)stage_addr(buf, o.b[j]);
     i32x8 b;
 #pragma unroll
@@ -550,7 +568,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int wm0 = (wave >> 1) * WM, wn0 = (wave & 1) * C::WN;
     const LaneOffsets<F> o = lane_offsets<TM, F>(wm0, wn0, lane);
-    const LoadOffsets lo = load_offsets<TM>(a, lane, wave);
+    const LoadOffsets lo = load_offsets<TM, BNT>(a, lane, wave);
     const int S = (int)((a.K + BK - 1) / BK);
 
     i32x4 acc[FM][F];
@@ -644,9 +662,7 @@ hipError_t launch_bn(const GemmArgs& g, hipStream_t s) {
     // the epilogue variant (bias, GELU) is a compile-time choice: GELU, and even a per-element bias
     // select, would otherwise cost every epilogue
     const int epi = OUT == OUT_I32 ? 0 : ((g.bias ? 1 : 0) | (g.gelu ? 2 : 0));
-    if constexpr (BNT == 128)
-        launch_epi<OUT, true, BNT>(epi, grid, block, s, a);  // 128-wide tiles are token-major only
-    else if (g.tm)
+    if (g.tm)
         launch_epi<OUT, true, BNT>(epi, grid, block, s, a);
     else
         launch_epi<OUT, false, BNT>(epi, grid, block, s, a);

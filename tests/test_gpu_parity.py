@@ -292,3 +292,25 @@ def test_gemm_i8_bit_exact(M, K, N, ldx):
     got_y = host_bits(sp.sp24_gemm_i8(vd, md, M, Xd, scale=dev(scale)))
     assert np.array_equal(got_acc.astype(np.int64), acc)
     assert np.array_equal(got_y.view(np.uint32), Y.view(np.uint32))
+
+
+@pytest.mark.parametrize("M,K,N", [(4000, 256, 4000), (3000, 640, 7000)])
+def test_gemm_i8_feature_major_tile_widths_sampled(M, K, N):
+    # Feature-major launches at both int8 tile widths, ragged in M and N, compared bit for bit on sampled
+    # rows: 4000 x 4000 has 16 x 16 = 256 tiles of 256 x 256 (one full turn: the 256-wide tile), and
+    # 3000 x 7000 has 12 x 28 = 336 of them, where 12 x 55 = 660 tiles of 256 x 128 fill three turns of
+    # the cheaper tile better than two turns of 256 x 256 (the 128-wide tile, 128-byte B rows).
+    rng = np.random.default_rng(M + K + N)
+    W = rng.integers(-128, 128, size=(M, K), dtype=np.int8)
+    X = rng.integers(-128, 128, size=(K, N), dtype=np.int8)
+    scale = (rng.random(M) * 1e-3 + 1e-5).astype(np.float32)
+    v, m = oracle.prune_compress(W, oracle.I8)
+    rows = np.unique(np.concatenate([rng.choice(M, 24, replace=False), [0, 255, 256, M - 1]]))
+    acc, Y = oracle.gemm_i8(v, m, X, M, scale, rows=rows)
+    say(f"gemm_i8 feature-major tile widths M={M} K={K} N={N}")
+    vd, md, Xd = dev(v), dev(m), dev(X)
+    r = torch.from_numpy(rows).cuda()
+    got_acc = host_bits(sp.sp24_gemm_i8(vd, md, M, Xd)[r])
+    got_y = host_bits(sp.sp24_gemm_i8(vd, md, M, Xd, scale=dev(scale))[r])
+    assert np.array_equal(got_acc.astype(np.int64), acc)
+    assert np.array_equal(got_y.view(np.uint32), Y.view(np.uint32))
