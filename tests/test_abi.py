@@ -96,6 +96,10 @@ def test_prune_compress_validation(lib, args, expect):
     ((A, B, BF16, 4, 16, C, 8, NULL), sp.SP24_ERR_SHAPE),
     ((A, B, FP32, 4, 16, C, 18, NULL), sp.SP24_ERR_ALIGN),
     ((A, MIS, BF16, 4, 16, C, 16, NULL), sp.SP24_ERR_ALIGN),
+    # one thread per 16-column chunk of the padded tiles must fit 32 bits: 2^20 x 2^16 is 2^32 chunks, and
+    # 2^20 - 1 rows pad to 2^20 (the unpadded count alone would pass)
+    ((A, B, BF16, 1 << 20, 1 << 16, C, 1 << 16, NULL), sp.SP24_ERR_SHAPE),
+    ((A, B, BF16, (1 << 20) - 1, 1 << 16, C, 1 << 16, NULL), sp.SP24_ERR_SHAPE),
 ])
 def test_decompress_validation(lib, args, expect):
     assert lib.sp24_decompress(*args) == expect
