@@ -92,12 +92,23 @@ __global__ __launch_bounds__(256) void prune_compress_kernel(const void* __restr
     const bool row_ok = row < M;
     const char* wrow = reinterpret_cast<const char*>(W) + row * ldw * isz;
 
-    // load every tile first (TPW x SPAN elements per lane)
+    // load every tile first (TPW x SPAN elements per lane), and with Wanda the norms of the lane's span in
+    // the same round: loaded inside the group loop instead, they cost a second memory round trip per wave
+    // (11008 x 4096 bf16 Wanda: 33.4 us against 29.4 for magnitude)
     T x[TPW][SPAN];
+    f32x4 nrm[TPW][WANDA ? NG : 1];
 #pragma unroll
     for (int i = 0; i < TPW; i++) {
         const int64_t t = tx * 4 * TPW + wave + 4 * i;
         const int64_t c0 = t * KT + SPAN * qq;
+        if constexpr (WANDA) {
+            // the span starts at a multiple of SPAN (8 or 16, which divides K), so when it starts inside K all
+            // of it is inside K; norms is 16-byte aligned (checked on the host): NG 16-byte loads
+#pragma unroll
+            for (int g = 0; g < NG; g++)
+                nrm[i][g] = (t < tiles && c0 < K) ? *reinterpret_cast<const f32x4*>(norms + c0 + 4 * g)
+                                                  : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
 #pragma unroll
         for (int h = 0; h < (SPAN * isz) / 16; h++) {  // 16-byte pieces of the lane's span
             constexpr int PER = 16 / isz;                // elements per piece
@@ -126,10 +137,7 @@ __global__ __launch_bounds__(256) void prune_compress_kernel(const void* __restr
                 uint32_t key[4];
                 float nv[4] = {0.f, 0.f, 0.f, 0.f};
                 if constexpr (WANDA) {
-                    // c is a multiple of 4, the group lies inside K and norms is 16-byte aligned (checked
-                    // on the host): one 16-byte load
-                    const f32x4 n4 = *reinterpret_cast<const f32x4*>(norms + c);
-                    nv[0] = n4[0]; nv[1] = n4[1]; nv[2] = n4[2]; nv[3] = n4[3];
+                    nv[0] = nrm[i][g][0]; nv[1] = nrm[i][g][1]; nv[2] = nrm[i][g][2]; nv[3] = nrm[i][g][3];
                 }
 #pragma unroll
                 for (int e = 0; e < 4; e++) key[e] = select_key<DT, WANDA>(x[i][4 * g + e], nv[e]);
