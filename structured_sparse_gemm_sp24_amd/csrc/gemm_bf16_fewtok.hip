@@ -1,4 +1,4 @@
-// Sparse x dense GEMM for a few tokens in the Linear layout (token-major X, N <= 8), bf16 in, fp32
+// Sparse x dense GEMM for a few tokens in the Linear layout (token-major X, N <= 16), bf16 in, fp32
 // accumulate (NVIDIA blog on Ampere structured sparsity, Figure 1; Orin NN design, Chapter 7, section 2.1
 // Step 3).
 //
@@ -231,15 +231,16 @@ hipError_t launch(const GemmArgs& g, hipStream_t s) {
 // Where this kernel is used: measured against the register-pipelined few-token kernel on MI355X (HIP
 // graph replays, weight copies rotated beyond the Infinity Cache), it is faster for N <= 2 (28672 x 8192
 // at N = 1: 44.9 against 48.7 us) and for N <= 8 on weights of fewer than 1024 row blocks (11008 x 4096 at
-// N = 8: 12.2 against 14.1 us); with 16-row X tiles the ring holds too few weight bytes (28672 x 8192 at
-// N = 16: 59.3 against 50.2 us), so those shapes stay with the other kernel.
+// N = 8: 12.2 against 14.1 us). With 16-row X tiles (9 to 16 tokens) the ring holds fewer weight bytes:
+// slower on large weights (28672 x 8192 at N = 16: 59.3 against 50.2 us), even on 11008 x 4096, and
+// faster below 512 row blocks (4096 x 4096 at N = 9 / 12 / 16: 7.0 / 6.9 / 7.1 against 7.6 / 7.2 / 7.9 us).
 bool gemm_bf16_fewtok_ok(const GemmArgs& g) {
     // token-major, rows of X 16-byte aligned in every batch entry; 32-bit load offsets below bit 31
     // (which marks the loads past a wave's range): 16 X rows plus K, the value tiles of one row block
     // (16 K bytes)
     const bool aligned = g.ldx % 8 == 0 && (reinterpret_cast<uintptr_t>(g.X) & 15) == 0 && (g.batch == 1 || g.sx % 8 == 0);
     const int64_t nb = (g.M + 15) / 16;
-    const bool pays = g.N <= 2 || (g.N <= 8 && nb < 1024);
+    const bool pays = g.N <= 2 || (g.N <= 8 && nb < 1024) || (g.N <= 16 && nb < 512);
     return g.tm && g.N >= 1 && pays && aligned && (16 * g.ldx + g.K) * 2 < ((int64_t)1 << 31) &&
            g.K < ((int64_t)1 << 26) && nb < ((int64_t)1 << 31);
 }
@@ -252,6 +253,10 @@ hipError_t launch_gemm_bf16_fewtok(const GemmArgs& g, hipStream_t s) {
         if (nb >= 512) return fewtok::launch<4, 8, 2>(g, s);   // 48 KB per workgroup, three per CU
         if (nb >= 192) return fewtok::launch<8, 8, 2>(g, s);   // 96 KB
         return fewtok::launch<16, 6, 2>(g, s);                 // 144 KB
+    }
+    if (g.N > 8) {  // 16 token rows per unit, below 512 row blocks (the only place it was faster)
+        if (nb >= 192) return fewtok::launch<8, 3, 16>(g, s);  // 78 KB
+        return fewtok::launch<16, 2, 16>(g, s);                // 104 KB
     }
     if (nb >= 512) return fewtok::launch<4, 5, 8>(g, s);       // 46 KB
     if (nb >= 192) return fewtok::launch<8, 5, 8>(g, s);       // 92 KB
