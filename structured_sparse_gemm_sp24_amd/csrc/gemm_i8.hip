@@ -107,6 +107,7 @@ __global__ __launch_bounds__(256) void gemm_i8_direct(DirectArgsI8 d) {
 }
 
 hipError_t launch_gemm_i8(const GemmArgs& g, hipStream_t s) {
+    if (gemm_i8_fewtok_ok(g)) return launch_gemm_i8_fewtok(g, s);
     if (gemm_i8_tiled_ok(g)) return launch_gemm_i8_tiled(g, s);
     DirectArgsI8 d;
     d.vals = static_cast<const int8_t*>(g.values);

@@ -67,6 +67,8 @@ hipError_t launch_gemm_bf16_tiled(const GemmArgs& g, hipStream_t s);
 
 // int8 GEMM: LDS-tiled when it applies, else direct.
 hipError_t launch_gemm_i8(const GemmArgs& g, hipStream_t s);
+bool gemm_i8_fewtok_ok(const GemmArgs& g);
+hipError_t launch_gemm_i8_fewtok(const GemmArgs& g, hipStream_t s);
 bool gemm_i8_tiled_ok(const GemmArgs& g);
 hipError_t launch_gemm_i8_tiled(const GemmArgs& g, hipStream_t s);
 

@@ -152,6 +152,14 @@ I8_TM_SHAPES = [
     (33, 48, 17, 48, 40),
     (200, 336, 100, 336, 200),
     (96, 256, 130, 260, 97),
+    # few-token int8 kernel (N <= 64, K % 128 == 0, 16-byte rows): ragged M, every fragment count
+    (700, 384, 1, 384, 704),
+    (1000, 256, 5, 272, 1000),
+    (517, 512, 16, 512, 520),
+    (300, 1024, 17, 1040, 300),
+    (96, 128, 33, 144, 100),
+    (33, 128, 48, 128, 36),
+    (2050, 640, 64, 640, 2056),
 ]
 
 
@@ -177,7 +185,7 @@ def test_gemm_i8_token_major(M, K, N, ldx, ldy):
 
 
 @pytest.mark.parametrize("B,M,K,N,layout", [(3, 64, 256, 100, "feature"), (2, 96, 384, 80, "token"),
-                                            (2, 40, 48, 30, "feature")])
+                                            (2, 40, 48, 30, "feature"), (3, 200, 256, 12, "token")])
 def test_gemm_i8_batched(B, M, K, N, layout):
     rng = np.random.default_rng(B * M + K + N)
     W = rng.integers(-128, 128, size=(M, K), dtype=np.int8)
