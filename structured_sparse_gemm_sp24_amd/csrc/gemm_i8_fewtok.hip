@@ -5,7 +5,7 @@
 //
 // With N this small the product streams the compressed int8 weight (0.625 bytes per dense weight) from
 // HBM once, and X (N rows of K bytes) stays in L2. A workgroup owns R consecutive 16-row blocks and all N
-// tokens (NF fragments of 16); its 8 waves split the K tiles (128 dense columns each) into contiguous
+// tokens (NF fragments of 16); its S waves split the K tiles (128 dense columns each) into contiguous
 // ranges. A wave requests U tiles' operands at a time before their smfmacs:
 //  - per lane and block, the 16-byte run of its slot in the compressed value tile and its 32-bit index
 //    (both already in v_smfmac_i32_16x16x128_i8 operand order);
@@ -22,7 +22,6 @@ namespace sp24 {
 namespace fewtok_i8 {
 
 constexpr int KT = 128;  // dense K per compressed tile
-constexpr int S = 8;     // waves per workgroup
 constexpr uint32_t OOR = 0x80000000u;  // a byte offset past every record count: the load returns zeros
 
 struct Args {
@@ -41,7 +40,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, 0x00020000);
 }
 
-template <int NF, int R, int U, bool SCALE>
+template <int NF, int R, int U, int S, bool SCALE>
 __global__ __launch_bounds__(64 * S) void gemm_i8_fewtok_kernel(Args a) {
     __shared__ i32x4 red[(S - 1) * R * NF * 64];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -153,7 +152,7 @@ __global__ __launch_bounds__(64 * S) void gemm_i8_fewtok_kernel(Args a) {
     }
 }
 
-template <int NF, int R, int U>
+template <int NF, int R, int U, int S>
 static hipError_t launch(const GemmArgs& g, hipStream_t s) {
     Args a;
     a.vals = static_cast<const int8_t*>(g.values);
@@ -171,9 +170,9 @@ static hipError_t launch(const GemmArgs& g, hipStream_t s) {
         e.X = a.X + e0 * a.sxb;
         e.Y = static_cast<char*>(a.Y) + e0 * a.syb * 4;
         if (g.scale)
-            hipLaunchKernelGGL((gemm_i8_fewtok_kernel<NF, R, U, true>), dim3(grid, gb), dim3(64 * S), 0, s, e);
+            hipLaunchKernelGGL((gemm_i8_fewtok_kernel<NF, R, U, S, true>), dim3(grid, gb), dim3(64 * S), 0, s, e);
         else
-            hipLaunchKernelGGL((gemm_i8_fewtok_kernel<NF, R, U, false>), dim3(grid, gb), dim3(64 * S), 0, s, e);
+            hipLaunchKernelGGL((gemm_i8_fewtok_kernel<NF, R, U, S, false>), dim3(grid, gb), dim3(64 * S), 0, s, e);
         const hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
@@ -191,15 +190,17 @@ bool gemm_i8_fewtok_ok(const GemmArgs& g) {
            (g.N - 1) * g.ldx + g.K + 128 < ((int64_t)1 << 31) && 4 * (g.K / fewtok_i8::KT) * 1024 < ((int64_t)1 << 31);
 }
 
-// Row blocks per workgroup (R) and tiles per request round (U) by the number of 16-token fragments: the
-// largest R and U whose operands fit next to the accumulators in registers, and whose partial sums fit
-// in LDS for the reduction.
+// Row blocks per workgroup (R), tiles per request round (U) and waves (S) by the number of 16-token
+// fragments, measured on MI355X (HIP graph replays, weight copies rotated beyond the Infinity Cache) over
+// R in {1, 2, 4, 8}, U in {1, 2, 4, 8}, S in {4, 8, 16}: one fragment, R = 2, U = 4, S = 8 (4096 x 4096 /
+// 11008 x 4096 / 28672 x 8192 at N = 1: 6.8 / 10.3 / 28.5 us, against 11.5 / 13.2 / 31.3 with R = 4);
+// four fragments, R = 2, U = 4, S = 4 (N = 64: 13.0 / 21.8 / 69.9 us).
 hipError_t launch_gemm_i8_fewtok(const GemmArgs& g, hipStream_t s) {
     switch ((g.N + 15) / 16) {
-    case 1: return fewtok_i8::launch<1, 4, 4>(g, s);
-    case 2: return fewtok_i8::launch<2, 4, 2>(g, s);
-    case 3: return fewtok_i8::launch<3, 2, 2>(g, s);
-    default: return fewtok_i8::launch<4, 2, 2>(g, s);
+    case 1: return fewtok_i8::launch<1, 2, 4, 8>(g, s);
+    case 2: return fewtok_i8::launch<2, 2, 4, 8>(g, s);
+    case 3: return fewtok_i8::launch<3, 2, 4, 4>(g, s);
+    default: return fewtok_i8::launch<4, 2, 4, 4>(g, s);
     }
 }
 
