@@ -1,7 +1,8 @@
 // Sparse x dense int8 GEMM for a few tokens in the Linear layout (token-major X, N <= 64), exact int32
-// accumulation and the optional per-output-channel fp32 dequant (oeforum post on sparse acceleration:
-// int8 and 2:4 combine; NVIDIA blog on Ampere structured sparsity, Figure 1; Orin NN design, Chapter 7,
-// section 3.1 Step 4).
+// accumulation, the optional per-output-channel fp32 dequant and the fused FFN epilogue (bias, GELU, bf16
+// or requantized int8 output) (oeforum post on sparse acceleration: int8 and 2:4 combine; NVIDIA blog on
+// Ampere structured sparsity, Figure 1 and its quantization section; Orin NN design, Chapter 7, section
+// 3.1 Step 4).
 //
 // With N this small the product streams the compressed int8 weight (0.625 bytes per dense weight) from
 // HBM once, and X (N rows of K bytes) stays in L2. A workgroup owns R consecutive 16-row blocks and all N
@@ -13,8 +14,9 @@
 //    B operand's two halves, lane = token).
 // Every read goes through a buffer descriptor: blocks past M, tokens past N and the tiles past a wave's
 // range read zeros, and nothing else is read. The waves' int32 partial sums are added through LDS (exact
-// in any order), then wave 0 dequantizes (y = fl32(fl32(acc) * scale[m]), one multiply) and stores, per
-// lane, four consecutive output channels of one token.
+// in any order), then wave 0 runs the epilogue value pipeline of the tiled int8 kernel on each accumulator
+// (y = fl32(fl32(acc) * scale[m]), then fl32(y + bias[m]), then GELU, then the output conversion; each step
+// one rounding) and stores, per lane, four consecutive output channels of one token.
 #include "sp24_device.h"
 #include "sp24_launch.h"
 
@@ -29,6 +31,8 @@ struct Args {
     const uint8_t* meta;
     const int8_t* X;
     const float* scale;
+    const float* bias;
+    float inv_scale;  // int8 output: fl32(1 / out_scale)
     void* Y;
     int64_t M, K, N, ldx, sxb, ldy, syb;
     int y_vec;  // 16-byte output stores allowed (aligned Y, row pitch and batch stride multiples of 4)
@@ -40,7 +44,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, 0x00020000);
 }
 
-template <int NF, int R, int U, int S, bool SCALE>
+// OUT: OUT_I32 (raw accumulators), OUT_F32, OUT_BF16, OUT_I8; EPI: bias (1) | GELU (2).
+template <int NF, int R, int U, int S, int OUT, int EPI>
 __global__ __launch_bounds__(64 * S) void gemm_i8_fewtok_kernel(Args a) {
     __shared__ i32x4 red[(S - 1) * R * NF * 64];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -116,39 +121,60 @@ __global__ __launch_bounds__(64 * S) void gemm_i8_fewtok_kernel(Args a) {
             for (int f = 0; f < NF; f++) acc[i][f] += red[(((w - 1) * R + i) * NF + f) * 64 + lane];
 
     // lane (q, r): output channels 16 b + 4q .. +3 of token 16 f + r (the accumulator's four rows)
-    char* const Y = static_cast<char*>(a.Y) + (int64_t)blockIdx.y * a.syb * 4;
+    constexpr int ES = OUT == OUT_BF16 ? 2 : (OUT == OUT_I8 ? 1 : 4);
+    constexpr bool BIAS = (EPI & 1) != 0, GELU = (EPI & 2) != 0;
+    char* const Y = static_cast<char*>(a.Y) + (int64_t)blockIdx.y * a.syb * ES;
 #pragma unroll
     for (int i = 0; i < R; i++) {
         const int64_t m0 = 16 * (b0 + i) + 4 * q;
         if (m0 >= a.M) continue;
-        float sc[4] = {1.f, 1.f, 1.f, 1.f};
-        if constexpr (SCALE) {
+        float sc[4] = {1.f, 1.f, 1.f, 1.f}, bi[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int j = 0; j < 4; j++) sc[j] = m0 + j < a.M ? a.scale[m0 + j] : 0.f;
+        for (int j = 0; j < 4; j++) {
+            if constexpr (OUT != OUT_I32) sc[j] = m0 + j < a.M ? a.scale[m0 + j] : 0.f;
+            if constexpr (BIAS) bi[j] = m0 + j < a.M ? a.bias[m0 + j] : 0.f;
         }
 #pragma unroll
         for (int f = 0; f < NF; f++) {
             const int64_t n = 16 * f + r;
             if (n >= a.N) continue;
-            uint32_t v[4];
+            uint32_t e[4];  // the four output elements' bits
 #pragma unroll
             for (int j = 0; j < 4; j++) {
-                if constexpr (SCALE) {
-#pragma clang fp contract(off)
-                    v[j] = __float_as_uint(__fmul_rn((float)acc[i][f][j], sc[j]));
+                if constexpr (OUT == OUT_I32) {
+                    e[j] = (uint32_t)acc[i][f][j];
                 } else {
-                    v[j] = (uint32_t)acc[i][f][j];
+                    const float y = i8_value(acc[i][f][j], sc[j], bi[j], BIAS, GELU);
+                    if constexpr (OUT == OUT_F32) e[j] = __float_as_uint(y);
+                    else if constexpr (OUT == OUT_BF16) e[j] = f32_to_bf16_rne(y);
+                    else e[j] = quant_i8(y, a.inv_scale);
                 }
             }
-            char* const p = Y + (n * a.ldy + m0) * 4;
+            char* const p = Y + (n * a.ldy + m0) * ES;
             if (a.y_vec && m0 + 3 < a.M) {
-                *reinterpret_cast<u32x4*>(p) = u32x4{v[0], v[1], v[2], v[3]};
+                if constexpr (ES == 4) *reinterpret_cast<u32x4*>(p) = u32x4{e[0], e[1], e[2], e[3]};
+                else if constexpr (ES == 2) *reinterpret_cast<u32x2*>(p) = u32x2{e[0] | (e[1] << 16), e[2] | (e[3] << 16)};
+                else *reinterpret_cast<uint32_t*>(p) = e[0] | (e[1] << 8) | (e[2] << 16) | (e[3] << 24);
             } else {
 #pragma unroll
-                for (int j = 0; j < 4; j++)
-                    if (m0 + j < a.M) reinterpret_cast<uint32_t*>(p)[j] = v[j];
+                for (int j = 0; j < 4; j++) {
+                    if (m0 + j >= a.M) continue;
+                    if constexpr (ES == 4) reinterpret_cast<uint32_t*>(p)[j] = e[j];
+                    else if constexpr (ES == 2) reinterpret_cast<uint16_t*>(p)[j] = (uint16_t)e[j];
+                    else reinterpret_cast<uint8_t*>(p)[j] = (uint8_t)e[j];
+                }
             }
         }
+    }
+}
+
+template <int NF, int R, int U, int S, int OUT>
+static void launch_epi(int epi, dim3 grd, dim3 blk, hipStream_t s, const Args& e) {
+    switch (epi) {
+    case 0: hipLaunchKernelGGL((gemm_i8_fewtok_kernel<NF, R, U, S, OUT, 0>), grd, blk, 0, s, e); break;
+    case 1: hipLaunchKernelGGL((gemm_i8_fewtok_kernel<NF, R, U, S, OUT, 1>), grd, blk, 0, s, e); break;
+    case 2: hipLaunchKernelGGL((gemm_i8_fewtok_kernel<NF, R, U, S, OUT, 2>), grd, blk, 0, s, e); break;
+    default: hipLaunchKernelGGL((gemm_i8_fewtok_kernel<NF, R, U, S, OUT, 3>), grd, blk, 0, s, e); break;
     }
 }
 
@@ -159,20 +185,27 @@ static hipError_t launch(const GemmArgs& g, hipStream_t s) {
     a.meta = g.meta;
     a.X = static_cast<const int8_t*>(g.X);
     a.scale = g.scale;
+    a.bias = g.bias;
+    a.inv_scale = g.inv_scale;
     a.Y = g.Y;
     a.M = g.M; a.K = g.K; a.N = g.N; a.ldx = g.ldx; a.sxb = g.sx; a.ldy = g.ldy; a.syb = g.sy;
     a.y_vec = ((reinterpret_cast<uintptr_t>(g.Y) & 15) == 0) && g.ldy % 4 == 0 && (g.batch == 1 || g.sy % 4 == 0);
     const unsigned grid = (unsigned)(((g.M + 15) / 16 + R - 1) / R);
     // grid y covers at most 65535 batch entries per launch
+    const int es = g.out_kind == OUT_BF16 ? 2 : (g.out_kind == OUT_I8 ? 1 : 4);
+    const int epi = (g.bias ? 1 : 0) | (g.gelu ? 2 : 0);
     for (int64_t e0 = 0; e0 < g.batch; e0 += 65535) {
         const unsigned gb = (unsigned)(g.batch - e0 < 65535 ? g.batch - e0 : 65535);
         Args e = a;
         e.X = a.X + e0 * a.sxb;
-        e.Y = static_cast<char*>(a.Y) + e0 * a.syb * 4;
-        if (g.scale)
-            hipLaunchKernelGGL((gemm_i8_fewtok_kernel<NF, R, U, S, true>), dim3(grid, gb), dim3(64 * S), 0, s, e);
-        else
-            hipLaunchKernelGGL((gemm_i8_fewtok_kernel<NF, R, U, S, false>), dim3(grid, gb), dim3(64 * S), 0, s, e);
+        e.Y = static_cast<char*>(a.Y) + e0 * a.syb * es;
+        const dim3 grd(grid, gb), blk(64 * S);
+        switch (g.out_kind) {
+        case OUT_I32: hipLaunchKernelGGL((gemm_i8_fewtok_kernel<NF, R, U, S, OUT_I32, 0>), grd, blk, 0, s, e); break;
+        case OUT_F32: launch_epi<NF, R, U, S, OUT_F32>(epi, grd, blk, s, e); break;
+        case OUT_BF16: launch_epi<NF, R, U, S, OUT_BF16>(epi, grd, blk, s, e); break;
+        default: launch_epi<NF, R, U, S, OUT_I8>(epi, grd, blk, s, e); break;
+        }
         const hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
@@ -182,11 +215,11 @@ static hipError_t launch(const GemmArgs& g, hipStream_t s) {
 }  // namespace fewtok_i8
 
 bool gemm_i8_fewtok_ok(const GemmArgs& g) {
-    // the plain epilogue (int32 accumulators, or fp32 with the dequant scale); 16-byte aligned rows of X in
-    // every batch entry; whole 128-column tiles; 32-bit byte offsets for X and for R = 4 row blocks' tiles
-    const bool plain = !g.bias && !g.gelu && (g.scale ? g.out_kind == OUT_F32 : g.out_kind == OUT_I32);
+    // raw int32 accumulators without a scale, every epilogue with one; 16-byte aligned rows of X in every
+    // batch entry; whole 128-column tiles; 32-bit byte offsets for X and for R = 4 row blocks' tiles
+    const bool epi_ok = g.scale ? true : (g.out_kind == OUT_I32 && !g.bias && !g.gelu);
     const bool aligned = g.ldx % 16 == 0 && (reinterpret_cast<uintptr_t>(g.X) & 15) == 0 && (g.batch == 1 || g.sx % 16 == 0);
-    return g.tm && plain && aligned && g.N >= 1 && g.N <= 64 && g.K >= fewtok_i8::KT && g.K % fewtok_i8::KT == 0 &&
+    return g.tm && epi_ok && aligned && g.N >= 1 && g.N <= 64 && g.K >= fewtok_i8::KT && g.K % fewtok_i8::KT == 0 &&
            (g.N - 1) * g.ldx + g.K + 128 < ((int64_t)1 << 31) && 4 * (g.K / fewtok_i8::KT) * 1024 < ((int64_t)1 << 31);
 }
 

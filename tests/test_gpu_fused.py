@@ -33,6 +33,8 @@ SHAPES = [
     (96, 256, 130, "feature"),
     (33, 48, 17, "token"),
     (40, 208, 90, "feature"),
+    (200, 256, 12, "token"),   # few-token kernel: one fragment
+    (150, 384, 40, "token"),   # few-token kernel: three fragments
     (520, 1152, 1000, "token"),
 ]
 
