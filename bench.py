@@ -388,10 +388,66 @@ def workload_bert_int8_fused(args):
                 kernels=kernels, dense_ref=None, cpu_sample=cpu_sample)
 
 
+def workload_llm_int8(args):
+    """An LLM projection decoding a few tokens in int8: W 11008x4096 magnitude-pruned 2:4 in fp32, then
+    per-row symmetric int8 (99.99 % coverage); N tokens (default 16, at most 64) per-tensor int8. The step
+    prunes/compresses the int8 weight on the GPU and runs the int8 GEMM (int32 accumulate, fp32 dequant),
+    token-major, which for N <= 64 streams the 28 MB compressed weight once."""
+    N = args.n or 16
+    if not 1 <= N <= 64:
+        raise SystemExit("llm_proj_11008x4096_int8: --n must be in 1..64")
+    d = synth.llm_proj_int8_dense()
+    Wf = d["W_f32"]
+    M, K = Wf.shape
+    # host data prep (untimed): prune the fp32 weight with the library itself, then quantize
+    v, m = sp.sp24_prune_compress(to_dev(Wf))
+    q, s_w = synth.quantize_rows(sp.sp24_decompress(v, m, M, K).cpu().numpy())
+    xq, s_x = synth.quantize_tensor(np.ascontiguousarray(d["X_f32"][:, :N]))
+    scale = synth.dequant_scales(s_w, s_x)
+    xt = np.ascontiguousarray(xq.T)
+    step_bytes = M * K * 2 + K * N + 4 * M * N
+    kernel_bytes = M * K * 5 // 8 + K * N + 4 * M * N + 4 * M
+    copies = []
+    for _ in range(n_copies(step_bytes, kernel_bytes)):
+        vb, mb = sp.sp24_compressed_bytes(M, K, torch.int8)
+        copies.append(dict(W=to_dev(q), X=to_dev(xt), scale=to_dev(scale),
+                           vals=torch.empty(vb, dtype=torch.int8, device="cuda"),
+                           meta=torch.empty(mb, dtype=torch.uint8, device="cuda"),
+                           Y=torch.empty((N, M), dtype=torch.float32, device="cuda")))
+    kernels = [Kernel("prune_compress_i8", lambda c: sp.sp24_prune_compress(c["W"], values=c["vals"], meta=c["meta"]),
+                      M * K + M * K * 5 // 8, sources=("prune.hip", "sp24_device.h")),
+               Kernel("gemm_i8", lambda c: sp.sp24_gemm_i8_ex(c["vals"], c["meta"], M, c["X"], scale=c["scale"],
+                                                              layout="token", out=c["Y"]),
+                      kernel_bytes, float(M) * N * K, "i8", ("gemm_i8_fewtok.hip", "sp24_device.h"))]
+
+    def cpu_sample(budget_s):
+        import oracle
+        t0 = time.perf_counter()
+        v8, m8 = oracle.prune_compress(q, oracle.I8)
+        t_fixed = time.perf_counter() - t0
+        rows = 64
+        t0 = time.perf_counter()
+        oracle.gemm_i8(v8, m8, xq, M, scale, rows=np.arange(rows))
+        t_small = time.perf_counter() - t0
+        rows = int(min(M, max(64, rows * max(budget_s - t_fixed, 0.5) / max(t_small, 1e-6))))
+        t0 = time.perf_counter()
+        oracle.gemm_i8(v8, m8, xq, M, scale, rows=np.arange(rows))
+        total = t_fixed + (time.perf_counter() - t0) * M / rows
+        return total, f"int8 prune/compress of the full {M}x{K} weight + GEMM on {rows} of {M} rows, scaled to all rows"
+
+    cfg = dict(workload="llm_proj_11008x4096_int8", M=M, K=K, N=N,
+               weight="fp32 N(0,0.02^2) seed 37, 2:4 magnitude, per-row int8 at 99.99 % coverage",
+               activations=f"fp32 N(0,1) seed 38, first {N} columns, per-tensor int8 at 99.99 % coverage",
+               out="fp32 (int32 accumulate, per-channel dequant)", step="prune_compress int8 + gemm_i8",
+               layout="token-major: X N x K, Y N x M")
+    return dict(name=f"llm_proj_11008x4096_int8_n{N}", dtype="i8", unit="TOP/s", config=cfg,
+                flops=2.0 * M * N * K, copies=copies, kernels=kernels, dense_ref=None, cpu_sample=cpu_sample)
+
+
 WORKLOADS = {"vit_b16_fc1": workload_vit, "single_linear_256": workload_single, "bert_ffn_int8": workload_bert_int8,
              "bert_ffn_int8_fused": workload_bert_int8_fused,
              "llm_proj_11008x4096": workload_llm(11008), "llm_proj_4096x4096": workload_llm(4096),
-             "ffn_28672x8192": workload_ffn}
+             "ffn_28672x8192": workload_ffn, "llm_proj_11008x4096_int8": workload_llm_int8}
 
 
 # ----------------------------------------------------------------------------- HBM traffic

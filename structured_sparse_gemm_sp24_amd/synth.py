@@ -129,6 +129,12 @@ def bert_ffn_int8_dense():
                 X1_f32=normal_f32(23, (768, 8192)), X2_f32=normal_f32(24, (3072, 8192)))
 
 
+def llm_proj_int8_dense():
+    """LLM projection for int8 decoding, before pruning/quantization: W 11008x4096 fp32 ~N(0, 0.02^2)
+    (seed 37); X 4096x64 fp32 ~N(0,1) (seed 38), of which the first N columns (tokens) are used."""
+    return dict(W_f32=normal_f32(37, (11008, 4096), 0.02), X_f32=normal_f32(38, (4096, 64)))
+
+
 def bert_ffn_biases():
     """Biases of the BERT-base FFN pair for the fused chain: b1 (3072, seed 25), b2 (768, seed 26),
     fp32 ~N(0, 0.02^2)."""

@@ -111,6 +111,30 @@ def test_bert_ffn_int8():
         assert np.array_equal(got_tm.view(np.uint32), Y.view(np.uint32))
 
 
+def test_llm_projection_int8_few_tokens():
+    # the int8 decode workload: fp32 prune (bit-exact), host int8 preparation from the oracle's pruned
+    # weight, int8 prune/compress (bit-exact), then the few-token int8 GEMM token-major (bit-exact on
+    # sampled rows, int32 and fp32 output) at N = 1, 16 and 64
+    d = synth.llm_proj_int8_dense()
+    W = d["W_f32"]
+    M, K = W.shape
+    say(f"full size: LLM projection int8 {M} x {K}, N in 1, 16, 64")
+    _, _, rv, rm = _prune_bit_exact(W, oracle.FP32)
+    q, s_w = synth.quantize_rows(oracle.decompress(rv, rm, oracle.FP32, M, K))
+    v8, m8, rv8, rm8 = _prune_bit_exact(q, oracle.I8)
+    rows = _rows(M, 6)
+    r = torch.from_numpy(rows).cuda()
+    for N in (1, 16, 64):
+        xq, s_x = synth.quantize_tensor(np.ascontiguousarray(d["X_f32"][:, :N]))
+        scale = synth.dequant_scales(s_w, s_x)
+        acc, Y = oracle.gemm_i8(rv8, rm8, xq, M, scale, rows=rows)
+        Xt = dev(np.ascontiguousarray(xq.T))
+        got = host_bits(sp.sp24_gemm_i8_ex(v8, m8, M, Xt, scale=dev(scale), layout="token")[:, r].t().contiguous())
+        got_acc = host_bits(sp.sp24_gemm_i8_ex(v8, m8, M, Xt, layout="token")[:, r].t().contiguous())
+        assert np.array_equal(got_acc.astype(np.int64), acc)
+        assert np.array_equal(got.view(np.uint32), Y.view(np.uint32))
+
+
 @pytest.mark.parametrize("M", [11008, 4096])
 def test_llm_projection_wanda(M):
     d = synth.llm_proj(M)
