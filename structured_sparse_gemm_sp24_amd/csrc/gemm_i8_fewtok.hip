@@ -225,15 +225,20 @@ bool gemm_i8_fewtok_ok(const GemmArgs& g) {
 
 // Row blocks per workgroup (R), tiles per request round (U) and waves (S) by the number of 16-token
 // fragments, measured on MI355X (HIP graph replays, weight copies rotated beyond the Infinity Cache) over
-// R in {1, 2, 4, 8}, U in {1, 2, 4, 8}, S in {4, 8, 16}: one fragment, R = 2, U = 4, S = 8 (4096 x 4096 /
-// 11008 x 4096 / 28672 x 8192 at N = 1: 6.8 / 10.3 / 28.5 us, against 11.5 / 13.2 / 31.3 with R = 4);
-// four fragments, R = 2, U = 4, S = 4 (N = 64: 13.0 / 21.8 / 69.9 us).
+// R in {1, 2, 4, 8}, U in {1, 2, 4, 8}, S in {4, 8, 16}: U = 4, S = 8 up to two fragments and S = 4 beyond.
+// R = 2 where it still gives over 256 workgroups (4096 x 4096 / 11008 x 4096 / 28672 x 8192 at N = 64:
+// 12.8 / 21.5 / 69.6 us, against 12.1 / 27.7 / 69.6 with R = 1); R = 1 below that, and for one fragment
+// up to 1024 row blocks, where the wider grid keeps more requests in flight (N = 1: 5.4 / 8.4 / 28.4 us,
+// against 6.7 / 9.9 / 28.5 with R = 2).
 hipError_t launch_gemm_i8_fewtok(const GemmArgs& g, hipStream_t s) {
-    switch ((g.N + 15) / 16) {
-    case 1: return fewtok_i8::launch<1, 2, 4, 8>(g, s);
-    case 2: return fewtok_i8::launch<2, 2, 4, 8>(g, s);
-    case 3: return fewtok_i8::launch<3, 2, 4, 4>(g, s);
-    default: return fewtok_i8::launch<4, 2, 4, 4>(g, s);
+    const int64_t nb = (g.M + 15) / 16;
+    const int nf = (int)((g.N + 15) / 16);
+    const bool r1 = nb <= 512 || (nf == 1 && nb <= 1024);
+    switch (nf) {
+    case 1: return r1 ? fewtok_i8::launch<1, 1, 4, 8>(g, s) : fewtok_i8::launch<1, 2, 4, 8>(g, s);
+    case 2: return r1 ? fewtok_i8::launch<2, 1, 4, 8>(g, s) : fewtok_i8::launch<2, 2, 4, 8>(g, s);
+    case 3: return r1 ? fewtok_i8::launch<3, 1, 4, 4>(g, s) : fewtok_i8::launch<3, 2, 4, 4>(g, s);
+    default: return r1 ? fewtok_i8::launch<4, 1, 4, 4>(g, s) : fewtok_i8::launch<4, 2, 4, 4>(g, s);
     }
 }
 
