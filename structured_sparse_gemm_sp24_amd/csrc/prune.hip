@@ -178,6 +178,69 @@ __global__ __launch_bounds__(256) void prune_compress_kernel(const void* __restr
     }
 }
 
+// int8 magnitude selection a group at a time, the group's four weights being one 32-bit word. Each byte
+// becomes |q| without crossing into its neighbour (for q < 0, ~q + 1 <= 0x80), and the key
+// (|q| << 2) | (3 - e) is unique within the group and orders as |q| with the lower position first on ties,
+// so the kept pair is the largest and second largest key: the second largest of four is the larger of the
+// median of the first three and the smaller of their maximum and the fourth.
+__device__ __forceinline__ void top2_i8(uint32_t w, uint32_t& lo, uint32_t& hi) {
+    const uint32_t sgn = (w >> 7) & 0x01010101u;
+    const uint32_t a = (w ^ (sgn * 0xFFu)) + sgn;
+    const uint32_t k0 = ((a & 0xFFu) << 2) | 3u, k1 = (((a >> 8) & 0xFFu) << 2) | 2u;
+    const uint32_t k2 = (((a >> 16) & 0xFFu) << 2) | 1u, k3 = (a >> 24) << 2;
+    const uint32_t m3 = max(max(k0, k1), k2);
+    const uint32_t med = max(min(k0, k1), min(max(k0, k1), k2));
+    const uint32_t first = max(m3, k3), second = max(med, min(m3, k3));
+    const uint32_t pf = first & 3u, ps = second & 3u;  // 3 - position
+    lo = 3u - max(pf, ps);
+    hi = 3u - min(pf, ps);
+}
+
+// The int8 magnitude prune on the same grid as prune_compress_kernel: lane (r, qq) of wave w holds 32
+// columns of row 16 b + r in tile t as two 16-byte words; each pair of groups yields 4 value bytes, gathered
+// by one byte permute (selector 0-3: bytes of the even group's word, 4-7: of the odd one's), and 8 index bits.
+template <int TPW>
+__global__ __launch_bounds__(256) void prune_compress_i8_kernel(const void* __restrict__ W, int64_t ldw, int64_t M,
+                                                                int64_t K, int64_t tiles, int64_t groups_x,
+                                                                int8_t* __restrict__ values, uint8_t* __restrict__ meta) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r = lane & 15, qq = lane >> 4;
+    const int64_t b = blockIdx.x / groups_x;
+    const int64_t tx = blockIdx.x - b * groups_x;
+    const int64_t row = 16 * b + r;
+    const bool row_ok = row < M;
+    const char* wrow = reinterpret_cast<const char*>(W) + row * ldw;
+    u32x4 x[TPW][2];
+#pragma unroll
+    for (int i = 0; i < TPW; i++) {
+        const int64_t t = tx * 4 * TPW + wave + 4 * i;
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+            const int64_t c = t * 128 + 32 * qq + 16 * h;  // K is a multiple of 16: a piece is all in or all out
+            x[i][h] = u32x4{0, 0, 0, 0};
+            if (row_ok && t < tiles && c < K) x[i][h] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wrow + c));
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < TPW; i++) {
+        const int64_t t = tx * 4 * TPW + wave + 4 * i;
+        if (t >= tiles) break;
+        // zero words (past M or K) select positions 0 and 1 with zero values: the padding encoding
+        uint32_t out[4], mbits = 0;
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            const uint32_t w0 = x[i][k >> 1][2 * (k & 1)], w1 = x[i][k >> 1][2 * (k & 1) + 1];
+            uint32_t lo0, hi0, lo1, hi1;
+            top2_i8(w0, lo0, hi0);
+            top2_i8(w1, lo1, hi1);
+            out[k] = __builtin_amdgcn_perm(w1, w0, lo0 | (hi0 << 8) | ((lo1 + 4u) << 16) | ((hi1 + 4u) << 24));
+            mbits |= (lo0 | (hi0 << 2) | (lo1 << 4) | (hi1 << 6)) << (8 * k);
+        }
+        *reinterpret_cast<u32x4*>(values + (b * tiles + t) * 1024 + 16 * lane) = u32x4{out[0], out[1], out[2], out[3]};
+        *reinterpret_cast<uint32_t*>(meta + (b * tiles + t) * 256 + 4 * lane) = mbits;
+    }
+}
+
 // One thread per 16-column chunk of the M x K weight, numbered in the order of the compressed tiles: the 16
 // rows of a row block first, then the chunk's place in the tile's 64-byte rows, then the tile. The lanes
 // of a wave then read whole 1 KB value tiles and their metadata in address order, and (bf16) write 16
@@ -356,15 +419,20 @@ static hipError_t launch_pc_tpw(const void* W, int64_t M, int64_t K, int64_t ldw
     const int64_t groups_x = (tiles + 4 * TPW - 1) / (4 * TPW);
     const int64_t blocks = (Mp / 16) * groups_x;
     if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((prune_compress_kernel<DT, VOUT, WANDA, TPW>), dim3((unsigned)blocks), dim3(256), 0, s, W, ldw, M,
-                       K, tiles, groups_x, norms, values, meta);
+    if constexpr (DT == DT_I8)
+        hipLaunchKernelGGL((prune_compress_i8_kernel<TPW>), dim3((unsigned)blocks), dim3(256), 0, s, W, ldw, M, K, tiles,
+                           groups_x, static_cast<int8_t*>(values), meta);
+    else
+        hipLaunchKernelGGL((prune_compress_kernel<DT, VOUT, WANDA, TPW>), dim3((unsigned)blocks), dim3(256), 0, s, W,
+                           ldw, M, K, tiles, groups_x, norms, values, meta);
     return hipGetLastError();
 }
 
 // One tile per wave: measured on MI355X against 2, 4 and 8 tiles per wave (more loads in flight per lane,
 // fewer workgroups), one was the fastest at every size (28672 x 8192 bf16: 127.6 us against 142.8 us with
 // four, 72 % of HBM; 11008 x 4096: 27.1 against 30.0 us; Wanda 146 against 150 us), the hardware keeping
-// more, smaller workgroups in flight.
+// more, smaller workgroups in flight. The int8 kernel likewise (28672 x 8192: 86.6-89.0 us against 87.0-87.4
+// with two).
 template <int DT, int VOUT, bool WANDA>
 static hipError_t launch_pc(const void* W, int64_t M, int64_t K, int64_t ldw, const float* norms, void* values,
                             uint8_t* meta, hipStream_t s) {
