@@ -64,6 +64,8 @@ def _load():
         lib.oracle_prune_mask.argtypes = [P, I, I64, I64, I64, I, I, P, P, P, I64]
         lib.oracle_channel_permutation.argtypes = [P, I, I64, I64, I64, I, P, I, P]
         lib.oracle_retained.argtypes = [P, I, I64, I64, I64, I, P, P]
+        lib.oracle_perm_pair.argtypes = [I, I, I, ctypes.POINTER(I), ctypes.POINTER(I)]
+        lib.oracle_perm_pair.restype = I
         lib.oracle_retained.restype = ctypes.c_double
         lib.oracle_gemm_bf16.argtypes = [P, P, I64, I64, P, I64, I64, P, I64, P]
         lib.oracle_gemm_i8.argtypes = [P, P, I64, I64, P, I64, I64, P, P, I64, P, P]
@@ -161,6 +163,15 @@ def channel_permutation(W: np.ndarray, dtype: int, sweeps: int = 1, score: int =
         norms = np.ascontiguousarray(_c(norms, np.float32))
     _check(_load().oracle_channel_permutation(_ptr(W), dtype, M, K, K, score, _ptr(norms), sweeps, _ptr(perm)))
     return perm
+
+
+def perm_pair(G: int, r: int, p: int):
+    """The pair of groups (ga < gb) that pair p of round r of a permutation sweep over G groups
+    re-partitions, or None when one of the two positions is the dummy of an odd G."""
+    a, b = ctypes.c_int(), ctypes.c_int()
+    if not _load().oracle_perm_pair(int(G), int(r), int(p), ctypes.byref(a), ctypes.byref(b)):
+        return None
+    return a.value, b.value
 
 
 def retained(W: np.ndarray, dtype: int, perm: np.ndarray | None = None, score: int = MAGNITUDE,

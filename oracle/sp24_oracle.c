@@ -381,6 +381,22 @@ static void partition_subsets(int subs[35][3]) {
             for (int z = y + 1; z <= 7; z++) { subs[n][0] = x; subs[n][1] = y; subs[n][2] = z; n++; }
 }
 
+/* The round-robin schedule: in round r (0 <= r < G' - 1) pair p (0 <= p < G'/2) joins the groups at
+ * positions p and G' - 1 - p of the circle in which position 0 is fixed and positions 1 .. G' - 1 hold
+ * the groups rotated by r. Returns 1 and the pair (*ga < *gb) when both are real groups, 0 when one is
+ * the dummy G' - 1 >= G (that group sits the round out). */
+int oracle_perm_pair(int G, int r, int p, int* ga, int* gb) {
+    const int Ge = G + (G & 1);
+    const int pa = p, pb = Ge - 1 - p;
+    int a = pa == 0 ? 0 : 1 + ((pa - 1 + r) % (Ge - 1));
+    int b = pb == 0 ? 0 : 1 + ((pb - 1 + r) % (Ge - 1));
+    if (a >= G || b >= G) return 0;
+    if (a > b) { int t = a; a = b; b = t; }
+    *ga = a;
+    *gb = b;
+    return 1;
+}
+
 int oracle_channel_permutation(const void* W, int dtype, int64_t M, int64_t K, int64_t ldw, int score,
                                const float* norms, int sweeps, int32_t* perm_out) {
     if (!W || !perm_out || M < 1 || K < 8 || K % 4 != 0 || ldw < K || sweeps < 0) return OR_EARG;
@@ -395,11 +411,8 @@ int oracle_channel_permutation(const void* W, int dtype, int64_t M, int64_t K, i
         for (int r = 0; r < Ge - 1; r++) {
 #pragma omp parallel for schedule(dynamic)
             for (int p = 0; p < Ge / 2; p++) {
-                int pa = p, pb = Ge - 1 - p;
-                int ga = pa == 0 ? 0 : 1 + ((pa - 1 + r) % (Ge - 1));
-                int gb = pb == 0 ? 0 : 1 + ((pb - 1 + r) % (Ge - 1));
-                if (ga >= G || gb >= G) continue;
-                if (ga > gb) { int t = ga; ga = gb; gb = t; }
+                int ga, gb;
+                if (!oracle_perm_pair(G, r, p, &ga, &gb)) continue;
                 int64_t oc[8];
                 for (int i = 0; i < 4; i++) { oc[i] = perm_out[4 * ga + i]; oc[4 + i] = perm_out[4 * gb + i]; }
                 double S[35];

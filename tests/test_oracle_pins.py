@@ -277,6 +277,100 @@ def test_permutation_two_groups_is_best_partition():
         assert r == pytest.approx(best, rel=1e-12), trial
 
 
+def test_permutation_schedule_meets_every_pair_once():
+    """One sweep is G' - 1 rounds of G'/2 pairs (G' = G rounded up to even). Enumerated here from the
+    oracle's own schedule: inside a round no group is in two pairs (the pairs of a round are
+    independent), and over the sweep every two of the G groups meet exactly once, odd G included (the
+    group drawn against the dummy sits the round out)."""
+    for G in range(2, 41):
+        Ge = G + (G & 1)
+        seen = []
+        for r in range(Ge - 1):
+            pairs = [oracle.perm_pair(G, r, p) for p in range(Ge // 2)]
+            pairs = [pr for pr in pairs if pr is not None]
+            assert len(pairs) == G // 2, (G, r)  # every real group plays, except one when G is odd
+            groups = [g for pr in pairs for g in pr]
+            assert len(set(groups)) == len(groups), (G, r)
+            assert all(0 <= a < b < G for a, b in pairs), (G, r)
+            seen += pairs
+        assert sorted(seen) == list(itertools.combinations(range(G), 2)), G
+
+
+def _one_improvable_pair(G, a, b):
+    """Two rows of 4G channels in which only groups a and b (a < b) can gain by re-partitioning:
+    a = [9 9 9 0] keeps 18 of 27, b = [9 0 0 0] keeps 9; every other group is [20 20 0 0] and already
+    keeps its two largest, and any pair that includes one of them holds at most four values that a
+    split could keep, which it keeps already. The best split of (a, b) keeps 36."""
+    W = np.tile(np.array([20, 20, 0, 0], np.float32), (2, G))
+    W[:, 4 * a:4 * a + 4] = [9, 9, 9, 0]
+    W[:, 4 * b:4 * b + 4] = [9, 0, 0, 0]
+    W[1] = -W[1]  # the score is the magnitude
+    return W
+
+
+def test_permutation_one_sweep_reaches_every_pair():
+    """The effect of the schedule on crafted weights: for every pair of groups (all pairs up to 16
+    groups, a seeded sample above), a weight in which only that pair can gain is fixed by one sweep;
+    a schedule that skipped the pair would leave the objective at its start."""
+    rng = np.random.default_rng(5)
+    for G in list(range(2, 17)) + [17, 24, 33, 40]:
+        pairs = list(itertools.combinations(range(G), 2))
+        if G > 16:
+            pick = rng.choice(len(pairs), size=24, replace=False)
+            pairs = sorted(set([pairs[i] for i in pick] + [(0, G - 1), (G - 2, G - 1), (0, 1)]))
+        for a, b in pairs:
+            W = _one_improvable_pair(G, a, b)
+            before = oracle.retained(W, oracle.FP32)
+            assert before == 2 * (27 + 40 * (G - 2))
+            perm = oracle.channel_permutation(W, oracle.FP32, 1)
+            assert sorted(perm.tolist()) == list(range(4 * G))
+            assert oracle.retained(W, oracle.FP32, perm) == 2 * (36 + 40 * (G - 2)), (G, a, b)
+
+
+def _pair_gain_left(S, perm):
+    """Largest strict gain any pair of groups could still make by re-partitioning its 8 channels
+    (numpy, exact for integer scores): S is M x K scores, perm the column order."""
+    P = S[:, perm]
+    G = P.shape[1] // 4
+    worst = 0.0
+    for a, b in itertools.combinations(range(G), 2):
+        ch = np.concatenate([P[:, 4 * a:4 * a + 4], P[:, 4 * b:4 * b + 4]], axis=1)
+        cur = (np.sort(ch[:, :4], axis=1)[:, -2:].sum() + np.sort(ch[:, 4:], axis=1)[:, -2:].sum())
+        for A in itertools.combinations(range(8), 4):
+            if 0 not in A:
+                continue
+            B = [c for c in range(8) if c not in A]
+            v = np.sort(ch[:, list(A)], axis=1)[:, -2:].sum() + np.sort(ch[:, B], axis=1)[:, -2:].sum()
+            worst = max(worst, float(v - cur))
+    return worst
+
+
+@pytest.mark.parametrize("K,score", [(48, oracle.MAGNITUDE), (44, oracle.MAGNITUDE), (40, oracle.WANDA)])
+def test_permutation_fixed_point_has_no_improving_pair(K, score):
+    """Sweeps until one changes nothing; then no pair of groups (every pair, enumerated in numpy) has a
+    split among its 35 that keeps strictly more. Integer weights and power-of-two norms keep every
+    sum exact, so the comparison has no rounding."""
+    rng = np.random.default_rng(K)
+    W = rng.integers(-40, 41, size=(24, K)).astype(np.float32)
+    norms = None
+    S = np.abs(W.astype(np.float64))
+    if score == oracle.WANDA:
+        norms = (2.0 ** rng.integers(-2, 3, size=K)).astype(np.float32)
+        S = S * norms.astype(np.float64)
+    prev = oracle.channel_permutation(W, oracle.FP32, 0, score, norms)
+    assert np.array_equal(prev, np.arange(K))
+    for sweeps in range(1, 60):
+        perm = oracle.channel_permutation(W, oracle.FP32, sweeps, score, norms)
+        if np.array_equal(perm, prev):
+            break
+        prev = perm
+    else:
+        raise AssertionError("no fixed point within 60 sweeps")
+    assert sweeps > 1  # the random start was improvable
+    assert _pair_gain_left(S, perm) == 0.0
+    assert _pair_gain_left(S, np.arange(K)) > 0.0  # the check does see gains where there are some
+
+
 @pytest.mark.parametrize("score", [oracle.MAGNITUDE, oracle.WANDA])
 def test_permutation_invariants(score):
     W = synth.normal_bf16(31, (64, 256))
