@@ -66,6 +66,8 @@ def _load():
         lib.oracle_retained.argtypes = [P, I, I64, I64, I64, I, P, P]
         lib.oracle_perm_pair.argtypes = [I, I, I, ctypes.POINTER(I), ctypes.POINTER(I)]
         lib.oracle_perm_pair.restype = I
+        lib.oracle_threads.argtypes = []
+        lib.oracle_threads.restype = I
         lib.oracle_retained.restype = ctypes.c_double
         lib.oracle_gemm_bf16.argtypes = [P, P, I64, I64, P, I64, I64, P, I64, P]
         lib.oracle_gemm_i8.argtypes = [P, P, I64, I64, P, I64, I64, P, P, I64, P, P]
@@ -163,6 +165,11 @@ def channel_permutation(W: np.ndarray, dtype: int, sweeps: int = 1, score: int =
         norms = np.ascontiguousarray(_c(norms, np.float32))
     _check(_load().oracle_channel_permutation(_ptr(W), dtype, M, K, K, score, _ptr(norms), sweeps, _ptr(perm)))
     return perm
+
+
+def threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(_load().oracle_threads())
 
 
 def perm_pair(G: int, r: int, p: int):

@@ -40,6 +40,9 @@
 #include <stddef.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 enum { OR_BF16 = 0, OR_FP16 = 1, OR_FP32 = 2, OR_I8 = 3, OR_I32 = 4 };
 enum { OR_MAGNITUDE = 0, OR_WANDA = 1 };
@@ -333,6 +336,15 @@ int oracle_prune_mask(const void* W, int dtype, int64_t M, int64_t K, int64_t ld
         }
     }
     return OR_OK;
+}
+
+/* Threads the OpenMP loops of this file use (1 without OpenMP): reported beside oracle timings. */
+int oracle_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
 }
 
 /* ---------------------------------------------------------------- channel permutation [ORIN7 3.1, 6.3] */

@@ -16,10 +16,11 @@ import oracle
 import structured_sparse_gemm_sp24_amd as sp
 from structured_sparse_gemm_sp24_amd import synth
 from tests.gpu_util import bf16_to_f64, dev, fp32_sum_bound, frob_rel, host_bits, require_gpu, say
+from tests.layout_ref import to_row_major
 
 pytestmark = pytest.mark.gpu
 
-ROWS = 48  # sampled output rows per GEMM
+ROWS = 48  # random output rows per GEMM, on top of one row in every 256-row block
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -28,9 +29,14 @@ def _gpu():
 
 
 def _rows(M, seed):
+    """Seeded sample of output rows: one in every 256-row block (a seeded offset inside it), so that every
+    row block of the tiled kernels' 256-row tiles is checked across all N columns (hence every tile), plus
+    ROWS random rows and the first and last row."""
     rng = np.random.default_rng(seed)
     r = np.sort(rng.choice(M, size=min(ROWS, M), replace=False))
-    return np.unique(np.concatenate([r, [0, M - 1]]))
+    starts = np.arange(0, M, 256)
+    per_block = np.minimum(starts + rng.integers(0, 256, size=len(starts)), M - 1)
+    return np.unique(np.concatenate([r, per_block, [0, M - 1]]))
 
 
 def _prune_bit_exact(W_host, dt, score=oracle.MAGNITUDE, norms=None, val_dtype=None):
@@ -149,11 +155,55 @@ def test_llm_projection_wanda(M):
         _check_bf16(vd, md, rv, rm, M, np.ascontiguousarray(d["X_bf16"][:, :N]), rows)
 
 
+def _nibbles(values, meta, M, K):
+    """Row-major group nibbles (M x K/4) of a bf16 compressed weight."""
+    _, m = to_row_major(values, meta, M, K, 2)
+    m = m.astype(np.uint8)
+    return np.stack([m & 0xF, m >> 4], axis=2).reshape(M, K // 4)
+
+
+@pytest.mark.parametrize("M", [11008, 4096])
+def test_llm_projection_wanda_chain(M):
+    """The chain bench.py times, GPU column norms then GPU Wanda prune, against the oracle's chain (oracle
+    norms, oracle prune). Given the same norms the prune is bit-exact; the GPU norms may differ from the
+    oracle's in the last bits (within 1e-5 relative), so a group may keep a different pair only where a kept
+    and a dropped score lie within that tolerance of each other. Such groups are counted and bounded."""
+    d = synth.llm_proj(M)
+    W, Xcal = d["W_bf16"], d["Xcal_bf16"]
+    K = W.shape[1]
+    say(f"full size: Wanda chain {M} x {K}, GPU norms -> GPU prune against the oracle chain")
+    gn = host_bits(sp.sp24_col_norms(dev(Xcal, "bf16")))
+    on = oracle.col_norms(Xcal)
+    rel = np.abs(gn.astype(np.float64) - on) / on
+    assert np.max(rel) <= 1e-5
+    v_g, m_g = sp.sp24_prune_compress(dev(W, "bf16"), score=sp.SP24_SCORE_WANDA, norms=dev(gn))
+    v_g, m_g = host_bits(v_g), host_bits(m_g)
+    # the GPU prune with the GPU norms is the oracle's prune with the same norms, bit for bit
+    rv_gn, rm_gn = oracle.prune_compress(W, oracle.BF16, oracle.WANDA, gn)
+    assert np.array_equal(m_g, rm_gn) and np.array_equal(v_g, rv_gn)
+    # against the oracle's whole chain
+    rv, rm = oracle.prune_compress(W, oracle.BF16, oracle.WANDA, on)
+    ng, no = _nibbles(v_g, m_g, M, K), _nibbles(rv, rm, M, K)
+    diff = np.argwhere(ng != no)
+    # scores under the oracle's norms: fl32(fl32(|w|) * norm)
+    a = np.abs(bf16_to_f64(W).astype(np.float32))
+    for i, g in diff:
+        s = (a[i, 4 * g:4 * g + 4] * on[4 * g:4 * g + 4]).astype(np.float64)
+        kg = {int(ng[i, g]) & 3, int(ng[i, g]) >> 2}
+        ko = {int(no[i, g]) & 3, int(no[i, g]) >> 2}
+        (x,), (y,) = kg - ko, ko - kg  # kept only by the GPU chain, kept only by the oracle chain
+        assert abs(s[x] - s[y]) <= 3e-5 * max(s[x], s[y]), (i, g, s)
+    frac = len(diff) / (M * K / 4)
+    say(f"Wanda chain {M} x {K}: {len(diff)} of {M * K // 4} groups differ (near-ties of the norms), {frac:.2e}")
+    assert frac <= 1e-4
+
+
 def test_ffn_28672x8192():
     d = synth.ffn_28672x8192(8192)
     say("full size: FFN 28672 x 8192, N in 8, 64, 512, 8192")
     vd, md, rv, rm = _prune_bit_exact(d["W_bf16"], oracle.BF16)
-    rows = _rows(28672, 5)[:24]
+    rows = _rows(28672, 5)
+    assert len(np.unique(rows // 256)) == 112  # every 256-row tile row
     for N in (8, 64, 512, 8192):
         _check_bf16(vd, md, rv, rm, 28672, np.ascontiguousarray(d["X_bf16"][:, :N]), rows)
 

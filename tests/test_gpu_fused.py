@@ -36,6 +36,7 @@ SHAPES = [
     (200, 256, 12, "token"),   # few-token kernel: one fragment
     (150, 384, 40, "token"),   # few-token kernel: three fragments
     (520, 1152, 1000, "token"),
+    (16400, 256, 20, "token"),  # few-token kernel, two row blocks per workgroup, odd block count (1025)
 ]
 
 
@@ -116,3 +117,27 @@ def test_fused_batched_token_major_int8_chain():
         # the second layer is bit-exact on the codes the GPU produced
         ref_y = oracle.gemm_i8_fused(v2, m2, h[b], 64, s2, layout="token")["y"]
         assert np.array_equal(Y[b].view(np.uint32), ref_y.view(np.uint32))
+
+
+@pytest.mark.parametrize("N", [1, 40])
+def test_fused_batched_two_blocks_per_workgroup(N):
+    # the few-token kernel's R = 2 launch (1025 row blocks) over a batch of 3 token-major inputs, with bias,
+    # GELU and int8 output
+    rng = np.random.default_rng(90 + N)
+    B, M, K = 3, 16400, 256
+    W = rng.integers(-128, 128, size=(M, K), dtype=np.int8)
+    X = rng.integers(-128, 128, size=(B, N, K), dtype=np.int8)
+    scale = (rng.random(M) * 2e-4 + 1e-5).astype(np.float32)
+    bias = rng.standard_normal(M).astype(np.float32)
+    v, m = oracle.prune_compress(W, oracle.I8)
+    out_scale = 0.02
+    say(f"gemm_i8_fused batched R=2 M={M} K={K} N={N} B={B}")
+    q = host_bits(sp.sp24_gemm_i8_fused(dev(v), dev(m), M, dev(X), dev(scale), bias=dev(bias), activation="gelu",
+                                        out_dtype=torch.int8, out_scale=out_scale, layout="token")).astype(np.int32)
+    y = host_bits(sp.sp24_gemm_i8_fused(dev(v), dev(m), M, dev(X), dev(scale), bias=dev(bias), layout="token"))
+    for b in range(B):
+        ref = oracle.gemm_i8_fused(v, m, X[b], M, scale, bias, gelu=True, out_scale=out_scale, layout="token")
+        assert np.all(np.abs(q[b] - ref["q"].astype(np.int32)) <= 1)
+        assert np.mean(q[b] == ref["q"]) > 0.98
+        ref_nb = oracle.gemm_i8_fused(v, m, X[b], M, scale, bias, layout="token")["y32"]
+        assert np.array_equal(y[b].view(np.uint32), ref_nb.view(np.uint32))

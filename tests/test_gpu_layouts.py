@@ -158,6 +158,13 @@ I8_TM_SHAPES = [
     (517, 512, 16, 512, 520),
     (300, 1024, 17, 1040, 300),
     (96, 128, 33, 144, 100),
+    # few-token int8 kernel with two row blocks per workgroup (more than 1024 row blocks, or more than 512
+    # with two or more fragments) and an odd block count, so the last workgroup holds one block
+    (16400, 256, 1, 256, 16400),
+    (16400, 256, 20, 272, 16408),
+    (16400, 256, 40, 256, 16400),
+    (16400, 256, 64, 256, 16416),
+    (8200, 256, 33, 256, 8200),
     (33, 128, 48, 128, 36),
     (2050, 640, 64, 640, 2056),
 ]
