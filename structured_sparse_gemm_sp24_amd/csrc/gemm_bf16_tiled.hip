@@ -1,21 +1,22 @@
 // Tiled sparse x dense GEMM for large N, bf16 in, fp32 accumulate (NVIDIA blog on Ampere structured
 // sparsity, Figure 1; Orin NN design, Chapter 7, section 2.1 Step 3).
 //
-// Workgroup tile 256 (M) x BN (N), 4 waves in a 2 x 2 grid, each wave 128 x BN/2 = 8 x BN/32
-// v_smfmac_f32_16x16x64_bf16 fragments. K advances 64 dense columns per stage through LDS stage buffers.
-// Three configurations are launched (see the launcher): BN = 128 with two workgroups per compute unit
-// (two waves per SIMD, 128 fp32 accumulators per lane, at most 256 registers per wave), each with two
-// 34 KB stage buffers -- while one workgroup waits at its barrier or for its loads, the other's smfmacs
-// keep the SIMD busy; BN = 256 with eight waves (two per SIMD, each 128 x 64, 128 accumulators), three
-// 50 KB buffers, token-major; and BN = 256 with four waves (256 accumulators per lane), three 50 KB
-// buffers, feature-major. The template also takes BN = 128 with one workgroup per CU and four 34 KB buffers.
+// Workgroup tile 256 (M) x BN (N); waves of 128 x WN hold 8 x WN/16 v_smfmac_f32_16x16x64_bf16 fragments.
+// K advances 64 dense columns per stage through LDS stage buffers. Two main loops:
+//  - token-major X (N x K, a Linear layer's input; gemm_bf16_tm_kernel): waves of 128 x 64, two per SIMD --
+//    BN = 256 with eight waves and three 50 KB stage buffers, or BN = 128 with four waves, two 34 KB buffers
+//    and two workgroups per compute unit. Its per-stage instruction stream is kept short (about 100
+//    instructions per wave per stage, 32 of them smfmacs): buffer descriptors are made once per tile, the
+//    lane part of every load offset once per kernel, and the stage's advance along K rides in the loads'
+//    SGPR offset;
+//  - feature-major X (K x N; gemm_bf16_tiled_kernel): BN = 256 with four waves of 128 x 128 (256
+//    accumulators per lane), or BN = 128 with two workgroups per compute unit.
 //
-// Global -> LDS uses buffer loads with LDS destination (no VGPR staging). The whole byte offset of
-// each load is in its VGPR operand, which the buffer range check covers (the SGPR offset is not
-// checked), so reads past this workgroup's row blocks and past the end of X return zeros without
-// touching memory: M/N tails need no branches in the main loop (columns past N only feed output
-// columns that are never stored), and the loads the pipeline issues past the last stage are pushed
-// out of range on purpose.
+// Global -> LDS uses buffer loads with LDS destination (no VGPR staging). The range-checked part of each
+// load's byte offset is its VGPR operand (the SGPR offset is outside the check): reads past this
+// workgroup's row blocks and past the end of X return zeros without touching memory, so M/N tails need no
+// branches in the main loop (columns past N only feed output columns that are never stored), and the loads
+// the pipeline issues past the last tile are pushed out of range on purpose.
 //   A (compressed values): the weight is stored as 1 KB tiles in the lane order of the smfmac A
 //     operand (16 rows x 64 dense columns), so each tile is one contiguous 64-lane copy, and a
 //     lane's ds_read_b128 of its operand is conflict-free.
@@ -69,24 +70,21 @@ constexpr int GROUP_M = 8;
 // 256-wide tile's loads, for two waves per SIMD without halving the tile.
 template <int BN_, int OCC_ = 1, int WAVES_ = 4>
 struct Cfg {
-    static_assert((WAVES_ == 4 && (OCC_ == 1 || BN_ == 128)) || (WAVES_ == 8 && OCC_ == 2 && BN_ == 256),
-                  "supported configurations");
+    static_assert(WAVES_ == 4 && (OCC_ == 1 || BN_ == 128), "supported configurations");
     static constexpr int WAVES = WAVES_;
     static constexpr int BN = BN_, WN = BN_ / (WAVES_ / 2), FN = WN / 16;
     static constexpr int B_BYTES = BK * BN * 2;
     static constexpr int B_ROW = BN * 2;  // feature-major B tile row: 512 or 256 bytes
     static constexpr int STAGE_BYTES = A_BYTES + META_BYTES + B_BYTES;
-    static constexpr int NBUF = (OCC_ == 2 && WAVES_ == 4) ? 2 : (BN == 256 ? 3 : 4);  // 3 x 50 KB, 4 x 34 KB, 2 x 34 KB
-    static constexpr int B_LOADS = BN / 32;          // per wave: token-major 8 rows per load, feature-major 1 KB
-    static constexpr int LOADS_PER_STAGE = (4 + 2 + B_LOADS) / (WAVES_ / 4);  // per wave: A, metadata, B
+    static constexpr int NBUF = OCC_ == 2 ? 2 : (BN == 256 ? 3 : 4);  // 3 x 50 KB, 4 x 34 KB, 2 x 34 KB
+    static constexpr int B_LOADS = BN / 32;          // per wave: 1 KB of the B tile per load
+    static constexpr int LOADS_PER_STAGE = 4 + 2 + B_LOADS;  // per wave: A, metadata, B
     // How a wave issues a stage's loads once the barrier has freed its buffer (measured on MI355X):
     //  0: in one burst (two workgroups per CU: interleaving cost 3-4 %);
-    //  1: interleaved with the smfmacs of the last two fragment blocks (eight waves: even with the burst
-    //     on large N, and carrying some into the next stage was 5-7 % slower);
     //  2: LPRE of them interleaved with the first FN - 2 blocks of the next stage, in proportion to the
     //     smfmac slots there, the rest with the last two blocks (four waves of 256 accumulators, eight
     //     fragment blocks per stage: 7-8 % faster than the burst on 11008 x 4096 x 4096 feature-major).
-    static constexpr int SPREAD = (OCC_ == 2 && WAVES_ == 4) ? 0 : (WAVES_ == 8 ? 1 : 2);
+    static constexpr int SPREAD = OCC_ == 2 ? 0 : 2;
     static constexpr int LPRE = SPREAD == 2 ? LOADS_PER_STAGE - (2 * LOADS_PER_STAGE + FN / 2) / FN : 0;
 };
 constexpr uint32_t RSRC_FLAGS = 0x00020000u;
@@ -224,7 +222,6 @@ struct StageLoads {
     int s, tiles;
 };
 
-template <bool TM>
 __device__ __forceinline__ StageLoads plan_stage(uint32_t lds, const Args& a, const TileDesc& td, int s) {
     StageLoads p;
     const int64_t k0 = (int64_t)s * BK;
@@ -234,48 +231,35 @@ __device__ __forceinline__ StageLoads plan_stage(uint32_t lds, const Args& a, co
     p.tiles = (int)((a.K + BK - 1) / BK);
     p.rA = td.rA;
     p.rM = td.rM;
-    if constexpr (TM) {
-        // X's extent from this stage's corner: N - 1 - n0 rows of pitch ldx plus K - k0 elements, so
-        // token rows past N read zeros (K is a multiple of 64: no stage reaches past K)
-        p.rB = make_rsrc(td.x + td.n0 * a.ldx + k0, td.valid ? ((a.N - 1 - td.n0) * a.ldx + a.K - k0) * 2 : 0);
-    } else {
-        // X's exact extent from this stage's corner ((K - 1) rows of pitch ldx plus N elements); make_rsrc
-        // rounds it up to whole dwords (the range check passes a dword only if all of it is in range)
-        p.rB = make_rsrc(td.x + k0 * a.ldx + td.n0, td.valid ? ((a.K - 1 - k0) * a.ldx + a.N - td.n0) * 2 : 0);
-    }
+    // X's exact extent from this stage's corner ((K - 1) rows of pitch ldx plus N elements); make_rsrc
+    // rounds it up to whole dwords (the range check passes a dword only if all of it is in range)
+    p.rB = make_rsrc(td.x + k0 * a.ldx + td.n0, td.valid ? ((a.K - 1 - k0) * a.ldx + a.N - td.n0) * 2 : 0);
     return p;
 }
 
 // Load number `ord` (0 .. LOADS_PER_STAGE - 1) of this wave's share of a stage: first the A tiles, then
-// the metadata, then the B rows. With eight waves, wave w issues half (part w & 1) of the loads wave w / 2
-// issues with four.
-template <bool TM, int BNT, int WAVES>
-__device__ __forceinline__ void issue_load(const StageLoads& p, const Args& a, int ord, int wave_, const LoadOffsets& lo) {
-    constexpr int PARTS = WAVES / 4, NA = 4 / PARTS, NM = 2 / PARTS;
-    const int wave = wave_ / PARTS, part = wave_ % PARTS;
+// the metadata, then the B rows (feature-major X).
+template <int BNT>
+__device__ __forceinline__ void issue_load(const StageLoads& p, const Args& a, int ord, int wave, const LoadOffsets& lo) {
+    constexpr int NA = 4, NM = 2;
     if (ord < NA) {
         // A: one 1 KB tile per 16-row block, copied as is (it is already in lane order)
-        const int b = 4 * wave + part * NA + ord;
+        const int b = 4 * wave + ord;
         dma16(p.lds + b * 1024, lo.a + (((uint32_t)(b * p.tiles + p.s) * 1024u) | p.past), p.rA);
     } else if (ord < NA + NM) {
         // metadata: one 128 B tile per block; 4 blocks per wave, two per dword instruction
-        const int b = 4 * wave + 2 * (part * NM + ord - NA);
+        const int b = 4 * wave + 2 * (ord - NA);
         dma4(p.lds + A_BYTES + b * 128, lo.m + (((uint32_t)(b * p.tiles + p.s) * 128u) | p.past), p.rM);
-    } else if constexpr (TM) {
-        // B: BNT token rows x 128 B; wave w / PARTS loads rows BNT/4 * (w / PARTS) .., 8 rows per load
-        const int h = part * (Cfg<BNT>::B_LOADS / PARTS) + ord - NA - NM;
-        const int row = (BNT / 4) * wave + 8 * h;
-        dma16(p.lds + A_BYTES + META_BYTES + row * 128, lo.b[h & 1] + (uint32_t)(row * a.ldx * 2), p.rB);
     } else if constexpr (BNT == 128) {
         // B: 64 rows x 256 B; rows 16 wave .. +15, four rows per load (rows 16 wave + 4h + lane / 16:
         // row & 3 = lane / 16, (row >> 3) & 1 = h >> 1)
-        const int h = part * (4 / PARTS) + ord - NA - NM;
+        const int h = ord - NA - NM;
         const int row = 16 * wave + 4 * h;
         dma16(p.lds + A_BYTES + META_BYTES + row * 256, lo.b[h >> 1] + (uint32_t)(row * a.ldx * 2), p.rB);
     } else {
         // B: 64 rows x 512 B; rows 16 wave .. +15, two rows per load (rows 16 wave + 2h + lane / 32:
         // row & 3 = 2 (h & 1) + lane / 32, (row >> 3) & 1 = h >> 2)
-        const int h = part * (8 / PARTS) + ord - NA - NM;
+        const int h = ord - NA - NM;
         const int row = 16 * wave + 2 * h;
         dma16(p.lds + A_BYTES + META_BYTES + row * 512, lo.b[(h & 1) | ((h >> 2) << 1)] + (uint32_t)(row * a.ldx * 2),
               p.rB);
@@ -283,10 +267,10 @@ __device__ __forceinline__ void issue_load(const StageLoads& p, const Args& a, i
 }
 
 // Loads [O0, O1) of a stage, back to back.
-template <bool TM, int BNT, int WAVES, int O0, int O1>
+template <int BNT, int O0, int O1>
 __device__ __forceinline__ void issue_loads(const StageLoads& p, const Args& a, int wave, const LoadOffsets& lo) {
 #pragma unroll
-    for (int k = O0; k < O1; k++) issue_load<TM, BNT, WAVES>(p, a, k, wave, lo);
+    for (int k = O0; k < O1; k++) issue_load<BNT>(p, a, k, wave, lo);
 }
 
 // Tile descriptor of logical tile L (-1: none). Batch entries follow each other; inside one, tiles
@@ -416,7 +400,7 @@ struct Pending {
 // Fragment block j (FM smfmacs), with loads O0 + k, k < N, of `p` interleaved: a region of R smfmac slots
 // starting at slot `first` of this block takes load k after its slot (k * R) / N, so the wave never
 // queues more than a load or two at the texture unit while it has smfmacs to issue.
-template <bool TM, int BNT, int WAVES, int FNT, int N, int R, int O0>
+template <int BNT, int FNT, int N, int R, int O0>
 __device__ __forceinline__ void mfma_block(f32x4 (&acc)[FM][FNT], const AFrags& f, const bf16x16& b, int j, int first,
                                            const StageLoads& p, const Args& a, int wave, const LoadOffsets& lo) {
 #pragma unroll
@@ -424,24 +408,24 @@ __device__ __forceinline__ void mfma_block(f32x4 (&acc)[FM][FNT], const AFrags& 
         acc[i][j] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(f.a[i], b, acc[i][j], (int)f.idx[i], 0, 0);
 #pragma unroll
         for (int k = 0; k < N; k++)
-            if ((k * R) / N == first + i) issue_load<TM, BNT, WAVES>(p, a, O0 + k, wave, lo);
+            if ((k * R) / N == first + i) issue_load<BNT>(p, a, O0 + k, wave, lo);
         if constexpr (N > 0) __builtin_amdgcn_sched_barrier(0);
     }
 }
 
-// One K stage: stage s of the current tile, g-th stage of the workgroup overall (selects the buffer).
+// One K stage of the feature-major loop: stage s of the current tile, g-th stage of the workgroup overall
+// (selects the buffer).
 // The loads of stage s + NBUF of the current tile (or, past its end, stage s + NBUF - S of the next) go
 // into this stage's buffer once the barrier has freed it, in one of the patterns Cfg::SPREAD selects;
 // in pattern 2 the last LPRE of them are issued during the first F - 2 blocks of the next stage (the
 // `pend` loads; three buffers). The vmcnt wait is the same in every pattern: at the barrier of stage g
 // the newest LOADS_PER_STAGE loads are exactly those of stage g + NBUF - 1. No branches.
-template <bool TM, int BNT, int OCC, int WAVES>
+template <int BNT, int OCC>
 __device__ __forceinline__ void stage(uint32_t l0, const Args& a, const TileDesc& cur_t, const TileDesc& next_t, int s,
-                                      int S, int g, f32x4 (&acc)[FM][Cfg<BNT, OCC, WAVES>::FN], AFrags& f,
-                                      bf16x16 (&rb)[4],
-                                      const LaneOffsets<Cfg<BNT, OCC, WAVES>::FN, Cfg<BNT>::B_ROW>& o, int wave,
+                                      int S, int g, f32x4 (&acc)[FM][Cfg<BNT, OCC>::FN], AFrags& f, bf16x16 (&rb)[4],
+                                      const LaneOffsets<Cfg<BNT, OCC>::FN, Cfg<BNT>::B_ROW>& o, int wave,
                                       const LoadOffsets& lo, Pending& pend) {
-    using C = Cfg<BNT, OCC, WAVES>;
+    using C = Cfg<BNT, OCC>;
     constexpr int F = C::FN, NB = C::NBUF, L = C::LOADS_PER_STAGE;
     constexpr int LPRE = C::LPRE, LPOST = L - LPRE;
     const int cb = g % NB;
@@ -449,12 +433,12 @@ __device__ __forceinline__ void stage(uint32_t l0, const Args& a, const TileDesc
     const uint32_t nxt = l0 + (cb == NB - 1 ? 0 : cb + 1) * C::STAGE_BYTES;
     StageLoads pp;
     if constexpr (LPRE > 0)
-        pp = plan_stage<TM>(l0 + (cb == 0 ? NB - 1 : cb - 1) * C::STAGE_BYTES, a, pend.nxt ? next_t : cur_t, pend.s);
+        pp = plan_stage(l0 + (cb == 0 ? NB - 1 : cb - 1) * C::STAGE_BYTES, a, pend.nxt ? next_t : cur_t, pend.s);
 #pragma unroll
     for (int j = 0; j < F - 2; j++) {
-        rb[(j + 2) & 3] = read_b<TM>(cur, o, j + 2);
+        rb[(j + 2) & 3] = read_b<false>(cur, o, j + 2);
         __builtin_amdgcn_sched_barrier(0);
-        mfma_block<TM, BNT, WAVES, F, LPRE, (F - 2) * FM, LPOST>(acc, f, rb[j & 3], j, j * FM, pp, a, wave, lo);
+        mfma_block<BNT, F, LPRE, (F - 2) * FM, LPOST>(acc, f, rb[j & 3], j, j * FM, pp, a, wave, lo);
         __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);           // lgkmcnt(0): this wave's reads of stage g are done
@@ -463,13 +447,13 @@ __device__ __forceinline__ void stage(uint32_t l0, const Args& a, const TileDesc
     const bool here = s + NB < S;
     pend.nxt = !here;
     pend.s = here ? s + NB : s + NB - S;
-    const StageLoads np = plan_stage<TM>(cur, a, here ? cur_t : next_t, pend.s);
-    if constexpr (C::SPREAD == 0) issue_loads<TM, BNT, WAVES, 0, L>(np, a, wave, lo);
+    const StageLoads np = plan_stage(cur, a, here ? cur_t : next_t, pend.s);
+    if constexpr (C::SPREAD == 0) issue_loads<BNT, 0, L>(np, a, wave, lo);
     constexpr int LI = C::SPREAD == 0 ? 0 : LPOST;  // loads interleaved with the last two blocks
-    rb[0] = read_b<TM>(nxt, o, 0);
-    rb[1] = read_b<TM>(nxt, o, 1);
+    rb[0] = read_b<false>(nxt, o, 0);
+    rb[1] = read_b<false>(nxt, o, 1);
     __builtin_amdgcn_sched_barrier(0);
-    mfma_block<TM, BNT, WAVES, F, LI, 2 * FM, 0>(acc, f, rb[(F - 2) & 3], F - 2, 0, np, a, wave, lo);
+    mfma_block<BNT, F, LI, 2 * FM, 0>(acc, f, rb[(F - 2) & 3], F - 2, 0, np, a, wave, lo);
     __builtin_amdgcn_sched_barrier(0);
     // last block: once fragment i has been used for the last time, reload it (and its index) from the
     // next stage, so one A register set serves the whole pipeline
@@ -483,7 +467,7 @@ __device__ __forceinline__ void stage(uint32_t l0, const Args& a, const TileDesc
         f.idx[i] = *reinterpret_cast<const __attribute__((address_space(3))) uint16_t*>(pm + i * 128);
 #pragma unroll
         for (int k = 0; k < LI; k++)
-            if ((k * 2 * FM) / LI == FM + i) issue_load<TM, BNT, WAVES>(np, a, k, wave, lo);
+            if ((k * 2 * FM) / LI == FM + i) issue_load<BNT>(np, a, k, wave, lo);
         __builtin_amdgcn_sched_barrier(0);
     }
 }
@@ -616,10 +600,11 @@ __device__ __forceinline__ void store_tile_tm(const f32x4 (&acc)[FM][FNT], const
     }
 }
 
-template <bool OUT_FP32, bool TM, int BNT, int OCC, int WAVES>
-__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void gemm_bf16_tiled_kernel(
-    Args a) {
-    using C = Cfg<BNT, OCC, WAVES>;
+// The feature-major loop (X K x N): 256 x 256 tiles with four waves of 128 x 128, or 256 x 128 tiles with two
+// workgroups per compute unit.
+template <bool OUT_FP32, int BNT, int OCC>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void gemm_bf16_tiled_kernel(Args a) {
+    using C = Cfg<BNT, OCC>;
     constexpr int NB = C::NBUF, F = C::FN;
     __shared__ __attribute__((aligned(16))) char smem[NB * C::STAGE_BYTES];
     // LDS byte address of the first stage buffer (for the LDS-destination loads)
@@ -629,9 +614,9 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(OCC,
     int L = tile_of(a, p, 0);
     if (L < 0) return;  // whole workgroup
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    const int wm0 = (wave / (WAVES / 2)) * WM, wn0 = (wave % (WAVES / 2)) * C::WN;
-    const LaneOffsets<F, C::B_ROW> o = lane_offsets<TM, F, C::B_ROW>(wm0, wn0, lane);
-    const LoadOffsets lo = load_offsets<TM, BNT>(a, lane);
+    const int wm0 = (wave / 2) * WM, wn0 = (wave % 2) * C::WN;
+    const LaneOffsets<F, C::B_ROW> o = lane_offsets<false, F, C::B_ROW>(wm0, wn0, lane);
+    const LoadOffsets lo = load_offsets<false, BNT>(a, lane);
     const int S = (int)((a.K + BK - 1) / BK);
 
     f32x4 acc[FM][F];
@@ -656,39 +641,31 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(OCC,
     TileDesc next_t = tile_desc<OUT_FP32, BNT>(a, tile_of(a, p, 1));
 #pragma unroll
     for (int i = 0; i < NB - 1; i++)
-        issue_loads<TM, BNT, WAVES, 0, C::LOADS_PER_STAGE>(
-            plan_stage<TM>(l0 + i * C::STAGE_BYTES, a, S > i ? cur_t : next_t, S > i ? i : 0), a, wave, lo);
+        issue_loads<BNT, 0, C::LOADS_PER_STAGE>(
+            plan_stage(l0 + i * C::STAGE_BYTES, a, S > i ? cur_t : next_t, S > i ? i : 0), a, wave, lo);
     wait_vmcnt<(NB - 2) * C::LOADS_PER_STAGE>();
     __builtin_amdgcn_s_barrier();
     // stage NB - 1: the loads a stage issues after its barrier; the first stage issues the rest
     Pending pend{S <= NB - 1, S > NB - 1 ? NB - 1 : 0};
-    issue_loads<TM, BNT, WAVES, 0, C::LOADS_PER_STAGE - C::LPRE>(
-        plan_stage<TM>(l0 + (NB - 1) * C::STAGE_BYTES, a, pend.nxt ? next_t : cur_t, pend.s), a, wave, lo);
+    issue_loads<BNT, 0, C::LOADS_PER_STAGE - C::LPRE>(
+        plan_stage(l0 + (NB - 1) * C::STAGE_BYTES, a, pend.nxt ? next_t : cur_t, pend.s), a, wave, lo);
 
     AFrags fa;
     bf16x16 rb[4];
     read_a(l0, o, fa);
-    rb[0] = read_b<TM>(l0, o, 0);
-    rb[1] = read_b<TM>(l0, o, 1);
+    rb[0] = read_b<false>(l0, o, 0);
+    rb[1] = read_b<false>(l0, o, 1);
     int g = 0;
     for (int k = 1;; k++) {
         for (int s = 0; s < S; s++, g++)
-            stage<TM, BNT, OCC, WAVES>(l0, a, cur_t, next_t, s, S, g, acc, fa, rb, o, wave, lo, pend);
+            stage<BNT, OCC>(l0, a, cur_t, next_t, s, S, g, acc, fa, rb, o, wave, lo, pend);
         // epilogue from registers; the next tile's first stages are in flight meanwhile
         {
             const int64_t mw = cur_t.m0 + wm0, nw = cur_t.n0 + wn0;
-            const bool full = (mw + WM <= a.M) && (nw + C::WN <= a.N) && a.y_vec;
-            if constexpr (TM) {
-                if (full)
-                    store_tile_tm<OUT_FP32, true>(acc, a, cur_t.y, mw, nw, lane);
-                else
-                    store_tile_tm<OUT_FP32, false>(acc, a, cur_t.y, mw, nw, lane);
-            } else {
-                if (full)
-                    store_tile<OUT_FP32, true>(acc, a, cur_t.y, mw, nw, lane);
-                else
-                    store_tile<OUT_FP32, false>(acc, a, cur_t.y, mw, nw, lane);
-            }
+            if ((mw + WM <= a.M) && (nw + C::WN <= a.N) && a.y_vec)
+                store_tile<OUT_FP32, true>(acc, a, cur_t.y, mw, nw, lane);
+            else
+                store_tile<OUT_FP32, false>(acc, a, cur_t.y, mw, nw, lane);
         }
         if (!next_t.valid) break;
 #pragma unroll
@@ -700,6 +677,214 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(OCC,
         next_t = tile_desc<OUT_FP32, BNT>(a, tile_of(a, p, k + 1));
     }
     wait_vmcnt<0>();  // the zero-filling loads past the last tile have landed before the workgroup ends
+}
+
+// ---------------------------------------------------------------- token-major main loop
+// Token-major X (N x K) with waves of 128 x 64 (two per SIMD): 256-wide tiles with eight waves and three stage
+// buffers, or 128-wide tiles with four waves, two stage buffers and two workgroups per compute unit. Per-stage
+// scalar work is kept to the stage's soffsets and buffer rotation: the buffer descriptors are made once per tile
+// (record count 0 for a tile past the last one), the lane-dependent part of every load offset (the part the range
+// check covers: the row block of A and metadata, the token row of X) is fixed per kernel, and the stage's advance
+// along K (s * 1 KB of A tiles, s * 128 B of metadata and of each X row) goes into the SGPR offset operand.
+__device__ __forceinline__ void dma16s(uint32_t lds, uint32_t voff, i32x4 rsrc, uint32_t soff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
+                 : "memory");
+}
+__device__ __forceinline__ void dma4s(uint32_t lds, uint32_t voff, i32x4 rsrc, uint32_t soff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds" ::"s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
+                 : "memory");
+}
+
+template <int BN>
+struct TmCfg {
+    static constexpr int WAVES = BN / 32;  // 8 or 4: two waves per SIMD either way (one or two workgroups per CU)
+    static constexpr int WN = 64, FN = 4;
+    static constexpr int STAGE_BYTES = A_BYTES + META_BYTES + BK * BN * 2;
+    static constexpr int NBUF = BN == 256 ? 3 : 2;
+    static constexpr int NA = 16 / WAVES, NM = 8 / WAVES, NBL = BN / 8 / WAVES;  // loads per wave per stage
+    static constexpr int L = NA + NM + NBL;
+};
+
+struct TmTile {
+    int64_t m0, n0;
+    char* y;
+    i32x4 rA, rM, rB;
+    bool valid;
+};
+
+template <bool OUT_FP32, int BNT>
+__device__ __forceinline__ TmTile tm_tile(const Args& a, int L) {
+    const TileDesc d = tile_desc<OUT_FP32, BNT>(a, L);
+    TmTile t;
+    t.m0 = d.m0;
+    t.n0 = d.n0;
+    t.y = d.y;
+    t.valid = d.valid;
+    t.rA = d.rA;
+    t.rM = d.rM;
+    t.rB = make_rsrc(d.x + d.n0 * a.ldx, ((a.N - 1 - d.n0) * a.ldx + a.K) * 2);
+    if (!d.valid) {
+        t.rA[2] = 0;
+        t.rM[2] = 0;
+        t.rB[2] = 0;
+    }
+    return t;
+}
+
+// Load k (compile-time) of this wave's share of one stage into the buffer at byte offset buf.
+template <int BN, int k>
+__device__ __forceinline__ void tm_load(uint32_t buf, const TmTile& t, uint32_t soffA, uint32_t soffMB, int wave,
+                                        uint32_t tiles, uint32_t ldx2, const LoadOffsets& lo) {
+    using C = TmCfg<BN>;
+    if constexpr (k < C::NA) {
+        const uint32_t b = C::NA * wave + k;
+        dma16s(buf + b * 1024, lo.a + b * tiles * 1024u, t.rA, soffA);
+    } else if constexpr (k < C::NA + C::NM) {
+        const uint32_t b = 2 * (C::NM * wave + (k - C::NA));
+        dma4s(buf + A_BYTES + b * 128, lo.m + b * tiles * 128u, t.rM, soffMB);
+    } else {
+        constexpr int h = k - C::NA - C::NM;
+        const uint32_t r0 = 8 * (C::NBL * wave + h);
+        dma16s(buf + A_BYTES + META_BYTES + r0 * 128, lo.b[h & 1] + r0 * ldx2, t.rB, soffMB);
+    }
+}
+
+template <int BN, int k0, int k1>
+__device__ __forceinline__ void tm_loads(uint32_t buf, const TmTile& t, uint32_t soffA, uint32_t soffMB, int wave,
+                                         uint32_t tiles, uint32_t ldx2, const LoadOffsets& lo) {
+    if constexpr (k0 < k1) {
+        tm_load<BN, k0>(buf, t, soffA, soffMB, wave, tiles, ldx2, lo);
+        tm_loads<BN, k0 + 1, k1>(buf, t, soffA, soffMB, wave, tiles, ldx2, lo);
+    }
+}
+
+// Loads interleaved with smfmac slot `slot` (0 .. 2 FM - 1) of the last two fragment blocks: load k after slot
+// (k * 2 FM) / L.
+template <int BN, int k>
+__device__ __forceinline__ void tm_loads_at(int slot, uint32_t buf, const TmTile& t, uint32_t soffA, uint32_t soffMB,
+                                            int wave, uint32_t tiles, uint32_t ldx2, const LoadOffsets& lo) {
+    if constexpr (k < TmCfg<BN>::L) {
+        if ((k * 2 * FM) / TmCfg<BN>::L == slot) tm_load<BN, k>(buf, t, soffA, soffMB, wave, tiles, ldx2, lo);
+        tm_loads_at<BN, k + 1>(slot, buf, t, soffA, soffMB, wave, tiles, ldx2, lo);
+    }
+}
+
+// One K stage: the current buffer `cur` (this stage), `nxt` (the next stage, published by this stage's barrier).
+// After the barrier the loads of stage `ls` of tile `lt` go into `cur`.
+template <int BN>
+__device__ __forceinline__ void tm_stage(uint32_t l0, uint32_t cur, uint32_t nxt, const TmTile& lt, uint32_t ls,
+                                         f32x4 (&acc)[FM][4], AFrags& f, bf16x16 (&rb)[4],
+                                         const LaneOffsets<4, 256>& o, int wave, uint32_t tiles, uint32_t ldx2,
+                                         const LoadOffsets& lo) {
+    using C = TmCfg<BN>;
+    constexpr int F = 4, NB = C::NBUF, L = C::L;
+    const uint32_t cb = l0 + cur, nb = l0 + nxt;
+#pragma unroll
+    for (int j = 0; j < F - 2; j++) {
+        rb[(j + 2) & 3] = read_b<true>(cb, o, j + 2);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < FM; i++)
+            acc[i][j] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(f.a[i], rb[j & 3], acc[i][j], (int)f.idx[i], 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of the stage are done
+    wait_vmcnt<(NB - 2) * L>();          // the next stage has landed
+    __builtin_amdgcn_s_barrier();
+    const uint32_t soffA = ls * 1024u, soffMB = ls * 128u;
+    rb[0] = read_b<true>(nb, o, 0);
+    rb[1] = read_b<true>(nb, o, 1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < FM; i++) {
+        acc[i][F - 2] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(f.a[i], rb[(F - 2) & 3], acc[i][F - 2], (int)f.idx[i], 0, 0);
+        tm_loads_at<BN, 0>(i, cb, lt, soffA, soffMB, wave, tiles, ldx2, lo);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    const lds_char* pa = (const lds_char*)(size_t)stage_addr(nb, o.a);
+    const lds_char* pm = (const lds_char*)(size_t)stage_addr(nb, o.m);
+#pragma unroll
+    for (int i = 0; i < FM; i++) {
+        acc[i][F - 1] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(f.a[i], rb[(F - 1) & 3], acc[i][F - 1], (int)f.idx[i], 0, 0);
+        f.a[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(pa + i * 1024));
+        f.idx[i] = *reinterpret_cast<const __attribute__((address_space(3))) uint16_t*>(pm + i * 128);
+        tm_loads_at<BN, 0>(FM + i, cb, lt, soffA, soffMB, wave, tiles, ldx2, lo);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+template <bool OUT_FP32, int BN>
+__global__ __launch_bounds__(64 * TmCfg<BN>::WAVES) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_bf16_tm_kernel(
+    Args a) {
+    using C = TmCfg<BN>;
+    constexpr int NB = C::NBUF, W = C::WAVES, L = C::L, SB = C::STAGE_BYTES;
+    __shared__ __attribute__((aligned(16))) char smem[NB * SB];
+    const uint32_t l0 = (uint32_t)(size_t)(__attribute__((address_space(3))) char*)smem;
+    const int p = blockIdx.x;
+    int Lt = tile_of(a, p, 0);
+    if (Lt < 0) return;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int wm0 = (wave / (W / 2)) * WM, wn0 = (wave % (W / 2)) * C::WN;
+    const LaneOffsets<4, 256> o = lane_offsets<true, 4, 256>(wm0, wn0, lane);
+    const LoadOffsets lo = load_offsets<true, BN>(a, lane);
+    const int S = (int)(a.K / BK);
+    const uint32_t tiles = (uint32_t)S, ldx2 = (uint32_t)(a.ldx * 2);
+
+    f32x4 acc[FM][4];
+#pragma unroll
+    for (int i = 0; i < FM; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    TmTile cur_t = tm_tile<OUT_FP32, BN>(a, Lt);
+    TmTile nxt_t = tm_tile<OUT_FP32, BN>(a, tile_of(a, p, 1));
+    // prologue: stages 0 .. NB - 1 (past the tile's stages: the next tile's first ones)
+#pragma unroll
+    for (int i = 0; i < NB; i++) {
+        const bool here = i < S;
+        const uint32_t ls = here ? i : i - S;
+        if (i == NB - 1) {
+            wait_vmcnt<(NB - 2) * L>();
+            __builtin_amdgcn_s_barrier();
+        }
+        tm_loads<BN, 0, L>(i * SB, here ? cur_t : nxt_t, ls * 1024u, ls * 128u, wave, tiles, ldx2, lo);
+    }
+    AFrags fa;
+    bf16x16 rb[4];
+    read_a(l0, o, fa);
+    rb[0] = read_b<true>(l0, o, 0);
+    rb[1] = read_b<true>(l0, o, 1);
+    uint32_t cur = 0;
+    for (int k = 1;; k++) {
+        int s = 0;
+        // stages whose barrier-time loads are this tile's stage s + NB
+        for (; s < S - NB; s++) {
+            const uint32_t nxt = cur == (NB - 1) * SB ? 0u : cur + SB;
+            tm_stage<BN>(l0, cur, nxt, cur_t, (uint32_t)(s + NB), acc, fa, rb, o, wave, tiles, ldx2, lo);
+            cur = nxt;
+        }
+        // the last NB stages load the next tile's first stages
+        for (; s < S; s++) {
+            const uint32_t nxt = cur == (NB - 1) * SB ? 0u : cur + SB;
+            tm_stage<BN>(l0, cur, nxt, nxt_t, (uint32_t)(s + NB - S), acc, fa, rb, o, wave, tiles, ldx2, lo);
+            cur = nxt;
+        }
+        {
+            const int64_t mw = cur_t.m0 + wm0, nw = cur_t.n0 + wn0;
+            if ((mw + WM <= a.M) && (nw + C::WN <= a.N) && a.y_vec)
+                store_tile_tm<OUT_FP32, true>(acc, a, cur_t.y, mw, nw, lane);
+            else
+                store_tile_tm<OUT_FP32, false>(acc, a, cur_t.y, mw, nw, lane);
+        }
+        if (!nxt_t.valid) break;
+#pragma unroll
+        for (int i = 0; i < FM; i++)
+#pragma unroll
+            for (int j = 0; j < 4; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        cur_t = nxt_t;
+        nxt_t = tm_tile<OUT_FP32, BN>(a, tile_of(a, p, k + 1));
+    }
+    wait_vmcnt<0>();
 }
 
 }  // namespace tiled_bf16
@@ -740,9 +925,8 @@ int tiled_tile_width(const GemmArgs& g) {
     return c128 < c256 ? 128 : 256;
 }
 
-template <bool TM, int BNT, int OCC, int WAVES = 4>
+template <bool TM, int BNT, int OCC>
 static hipError_t launch_bn(const GemmArgs& g, hipStream_t s) {
-    using C = tiled_bf16::Cfg<BNT, OCC, WAVES>;
     tiled_bf16::Args a;
     a.vals = static_cast<const uint16_t*>(g.values); a.meta = g.meta;
     a.X = static_cast<const uint16_t*>(g.X); a.Y = g.Y;
@@ -757,14 +941,26 @@ static hipError_t launch_bn(const GemmArgs& g, hipStream_t s) {
               (g.batch == 1 || (g.sy * es) % 16 == 0) && g.ldy * es * 16 < ((int64_t)1 << 31);
     const int T = a.tilesM * a.tilesN * a.batch;
     const int S = (int)((g.K + tiled_bf16::BK - 1) / tiled_bf16::BK);
-    // OCC / (WAVES / 4) workgroups per compute unit walking several tiles; one tile each when a tile has
-    // fewer stages than there are stage buffers (the cross-tile pipeline then has nothing to overlap)
-    const int slots = device_cus() * OCC / (WAVES / 4);
-    const unsigned grid = (unsigned)(S >= C::NBUF && T > slots ? slots : T);
-    if (g.out_fp32)
-        hipLaunchKernelGGL((tiled_bf16::gemm_bf16_tiled_kernel<true, TM, BNT, OCC, WAVES>), dim3(grid), dim3(64 * WAVES), 0, s, a);
-    else
-        hipLaunchKernelGGL((tiled_bf16::gemm_bf16_tiled_kernel<false, TM, BNT, OCC, WAVES>), dim3(grid), dim3(64 * WAVES), 0, s, a);
+    // workgroups walking several tiles, OCC per compute unit (the eight-wave token-major workgroup fills a CU
+    // alone); one tile each when a tile has fewer stages than there are stage buffers (the cross-tile pipeline
+    // then has nothing to overlap)
+    if constexpr (TM) {
+        using C = tiled_bf16::TmCfg<BNT>;
+        const int slots = device_cus() * (BNT == 256 ? 1 : 2);
+        const unsigned grid = (unsigned)(S >= C::NBUF && T > slots ? slots : T);
+        if (g.out_fp32)
+            hipLaunchKernelGGL((tiled_bf16::gemm_bf16_tm_kernel<true, BNT>), dim3(grid), dim3(64 * C::WAVES), 0, s, a);
+        else
+            hipLaunchKernelGGL((tiled_bf16::gemm_bf16_tm_kernel<false, BNT>), dim3(grid), dim3(64 * C::WAVES), 0, s, a);
+    } else {
+        using C = tiled_bf16::Cfg<BNT, OCC>;
+        const int slots = device_cus() * OCC;
+        const unsigned grid = (unsigned)(S >= C::NBUF && T > slots ? slots : T);
+        if (g.out_fp32)
+            hipLaunchKernelGGL((tiled_bf16::gemm_bf16_tiled_kernel<true, BNT, OCC>), dim3(grid), dim3(256), 0, s, a);
+        else
+            hipLaunchKernelGGL((tiled_bf16::gemm_bf16_tiled_kernel<false, BNT, OCC>), dim3(grid), dim3(256), 0, s, a);
+    }
     return hipGetLastError();
 }
 
@@ -790,7 +986,7 @@ hipError_t launch_gemm_bf16_tiled(const GemmArgs& g, hipStream_t s) {
     const double c128 = (double)(t128 / (2 * cus)) + (rem == 0 ? 0.0 : rem <= cus ? 0.6 : 1.0);
     if (t256 < cus || (t256 <= 2 * cus && c128 <= c256))
         return g.tm ? launch_bn<true, 128, 2>(g, s) : launch_bn<false, 128, 2>(g, s);
-    return g.tm ? launch_bn<true, 256, 2, 8>(g, s) : launch_bn<false, 256, 1>(g, s);
+    return g.tm ? launch_bn<true, 256, 1>(g, s) : launch_bn<false, 256, 1>(g, s);
 }
 
 }  // namespace sp24
