@@ -758,57 +758,64 @@ __device__ __forceinline__ void tm_loads(uint32_t buf, const TmTile& t, uint32_t
     }
 }
 
-// Loads interleaved with smfmac slot `slot` (0 .. 2 FM - 1) of the last two fragment blocks: load k after slot
-// (k * 2 FM) / L.
+// Loads interleaved with smfmac slot `slot` (0 .. 3 FM - 1) of the last three fragment blocks: load k after slot
+// (k * 3 FM) / L.
 template <int BN, int k>
 __device__ __forceinline__ void tm_loads_at(int slot, uint32_t buf, const TmTile& t, uint32_t soffA, uint32_t soffMB,
                                             int wave, uint32_t tiles, uint32_t ldx2, const LoadOffsets& lo) {
     if constexpr (k < TmCfg<BN>::L) {
-        if ((k * 2 * FM) / TmCfg<BN>::L == slot) tm_load<BN, k>(buf, t, soffA, soffMB, wave, tiles, ldx2, lo);
+        if ((k * 3 * FM) / TmCfg<BN>::L == slot) tm_load<BN, k>(buf, t, soffA, soffMB, wave, tiles, ldx2, lo);
         tm_loads_at<BN, k + 1>(slot, buf, t, soffA, soffMB, wave, tiles, ldx2, lo);
     }
 }
 
 // One K stage: the current buffer `cur` (this stage), `nxt` (the next stage, published by this stage's barrier).
-// After the barrier the loads of stage `ls` of tile `lt` go into `cur`.
+// The barrier sits after the first fragment block: B fragments 2 and 3 are read before it, so the rest of the
+// stage's operand traffic (the next stage's B fragments 0 and 1, A fragments and indices, and this wave's
+// loads of stage `ls` of tile `lt` into `cur`) spreads over the last three blocks.
 template <int BN>
 __device__ __forceinline__ void tm_stage(uint32_t l0, uint32_t cur, uint32_t nxt, const TmTile& lt, uint32_t ls,
                                          f32x4 (&acc)[FM][4], AFrags& f, bf16x16 (&rb)[4],
                                          const LaneOffsets<4, 256>& o, int wave, uint32_t tiles, uint32_t ldx2,
                                          const LoadOffsets& lo) {
     using C = TmCfg<BN>;
-    constexpr int F = 4, NB = C::NBUF, L = C::L;
+    constexpr int NB = C::NBUF, L = C::L;
     const uint32_t cb = l0 + cur, nb = l0 + nxt;
+    rb[2] = read_b<true>(cb, o, 2);
+    rb[3] = read_b<true>(cb, o, 3);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int j = 0; j < F - 2; j++) {
-        rb[(j + 2) & 3] = read_b<true>(cb, o, j + 2);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int i = 0; i < FM; i++)
-            acc[i][j] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(f.a[i], rb[j & 3], acc[i][j], (int)f.idx[i], 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-    }
+    for (int i = 0; i < FM; i++)
+        acc[i][0] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(f.a[i], rb[0], acc[i][0], (int)f.idx[i], 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of the stage are done
     wait_vmcnt<(NB - 2) * L>();          // the next stage has landed
     __builtin_amdgcn_s_barrier();
     const uint32_t soffA = ls * 1024u, soffMB = ls * 128u;
     rb[0] = read_b<true>(nb, o, 0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < FM; i++) {
+        acc[i][1] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(f.a[i], rb[1], acc[i][1], (int)f.idx[i], 0, 0);
+        tm_loads_at<BN, 0>(i, cb, lt, soffA, soffMB, wave, tiles, ldx2, lo);
+        __builtin_amdgcn_sched_barrier(0);
+    }
     rb[1] = read_b<true>(nb, o, 1);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < FM; i++) {
-        acc[i][F - 2] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(f.a[i], rb[(F - 2) & 3], acc[i][F - 2], (int)f.idx[i], 0, 0);
-        tm_loads_at<BN, 0>(i, cb, lt, soffA, soffMB, wave, tiles, ldx2, lo);
+        acc[i][2] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(f.a[i], rb[2], acc[i][2], (int)f.idx[i], 0, 0);
+        tm_loads_at<BN, 0>(FM + i, cb, lt, soffA, soffMB, wave, tiles, ldx2, lo);
         __builtin_amdgcn_sched_barrier(0);
     }
     const lds_char* pa = (const lds_char*)(size_t)stage_addr(nb, o.a);
     const lds_char* pm = (const lds_char*)(size_t)stage_addr(nb, o.m);
 #pragma unroll
     for (int i = 0; i < FM; i++) {
-        acc[i][F - 1] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(f.a[i], rb[(F - 1) & 3], acc[i][F - 1], (int)f.idx[i], 0, 0);
+        acc[i][3] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(f.a[i], rb[3], acc[i][3], (int)f.idx[i], 0, 0);
         f.a[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(pa + i * 1024));
         f.idx[i] = *reinterpret_cast<const __attribute__((address_space(3))) uint16_t*>(pm + i * 128);
-        tm_loads_at<BN, 0>(FM + i, cb, lt, soffA, soffMB, wave, tiles, ldx2, lo);
+        tm_loads_at<BN, 0>(2 * FM + i, cb, lt, soffA, soffMB, wave, tiles, ldx2, lo);
         __builtin_amdgcn_sched_barrier(0);
     }
 }
@@ -886,6 +893,209 @@ __global__ __launch_bounds__(64 * TmCfg<BN>::WAVES) __attribute__((amdgpu_waves_
     }
     wait_vmcnt<0>();
 }
+
+// ---------------------------------------------------------------- dense reference (measurement only)
+// A dense bf16 GEMM on v_mfma_f32_16x16x32_bf16 with the token-major sparse loop's tiling -- 256 x 256 workgroup
+// tiles in the same persistent XCD-aware walk, eight waves of 128 x 64, 32 MFMAs per wave per stage, the barrier
+// after the first fragment block, the same loads with an SGPR stage offset and the same epilogue -- so that its
+// time against the sparse kernel's isolates what 2:4 sparsity changes (a 16 x 16 x 64 block is one smfmac
+// instead of two MFMAs). K advances 32 per stage (one MFMA's depth) through four 32 KB stage buffers, about the
+// bytes in flight of the sparse loop's three 50 KB ones. The weight is a dense copy in MFMA operand order: tiles
+// of 16 rows x 32 columns (1 KB), byte range [16 l, 16 l + 16) = lane l's A operand (row l % 16, columns
+// 8 (l / 16) .. +7), stored row block by row block and along K inside a block.
+namespace dense_ref {
+constexpr int BKD = 32, NB = 4, WAVES = 8, BN = 256;
+constexpr int A_TILE = BM * BKD * 2;             // 16 KB
+constexpr int STAGE_BYTES = A_TILE + BN * BKD * 2;  // + 256 token rows x 64 B
+constexpr int NA = 2, NBL = 2, L = NA + NBL;     // loads per wave per stage (1 KB each)
+
+// The B tile holds 64 B per token row; the 16-byte unit u of row n sits at u ^ ((n >> 2) & 3), so the 16 rows
+// of one read group (one unit each) start in 16 distinct 4-bank groups.
+struct Tile {
+    int64_t m0, n0;
+    char* y;
+    i32x4 rA, rB;
+    bool valid;
+};
+
+template <bool OUT_FP32>
+__device__ __forceinline__ Tile tile(const Args& a, int L) {
+    const TileDesc d = tile_desc<OUT_FP32, BN>(a, L);
+    Tile t;
+    t.m0 = d.m0;
+    t.n0 = d.n0;
+    t.y = d.y;
+    t.valid = d.valid;
+    const int64_t kt = a.K / BKD, blocks_left = (a.M + 15) / 16 - d.m0 / 16;
+    const int64_t blocks = blocks_left < BM / 16 ? blocks_left : BM / 16;
+    t.rA = make_rsrc(reinterpret_cast<const char*>(a.vals) + (d.m0 / 16) * kt * 1024, d.valid ? blocks * kt * 1024 : 0);
+    t.rB = make_rsrc(d.x + d.n0 * a.ldx, d.valid ? ((a.N - 1 - d.n0) * a.ldx + a.K) * 2 : 0);
+    return t;
+}
+
+template <int k>
+__device__ __forceinline__ void load(uint32_t buf, const Tile& t, uint32_t soffA, uint32_t soffB, int wave, uint32_t kt,
+                                     uint32_t ldx2, uint32_t la, uint32_t lb) {
+    if constexpr (k < NA) {
+        const uint32_t b = NA * wave + k;
+        dma16s(buf + b * 1024, la + b * kt * 1024u, t.rA, soffA);
+    } else {
+        const uint32_t r0 = 16 * (NBL * wave + (k - NA));
+        dma16s(buf + A_TILE + r0 * 64, lb + r0 * ldx2, t.rB, soffB);
+    }
+}
+
+template <int k>
+__device__ __forceinline__ void loads_at(int slot, uint32_t buf, const Tile& t, uint32_t soffA, uint32_t soffB, int wave,
+                                         uint32_t kt, uint32_t ldx2, uint32_t la, uint32_t lb) {
+    if constexpr (k < L) {
+        if ((k * 3 * FM) / L == slot) load<k>(buf, t, soffA, soffB, wave, kt, ldx2, la, lb);
+        loads_at<k + 1>(slot, buf, t, soffA, soffB, wave, kt, ldx2, la, lb);
+    }
+}
+
+__device__ __forceinline__ bf16x8 read16(uint32_t addr) {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+                                          (const lds_char*)(size_t)stage_addr(addr, 0)));
+}
+
+__device__ __forceinline__ void stage(uint32_t l0, uint32_t cur, uint32_t nxt, const Tile& lt, uint32_t ls,
+                                      f32x4 (&acc)[FM][4], bf16x8 (&fa)[FM], bf16x8 (&rb)[4], uint32_t oa, uint32_t ob,
+                                      int wave, uint32_t kt, uint32_t ldx2, uint32_t la, uint32_t lb) {
+    const uint32_t cb = l0 + cur, nb = l0 + nxt;
+    rb[2] = read16(cb + ob + 2 * 1024);
+    rb[3] = read16(cb + ob + 3 * 1024);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < FM; i++) acc[i][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], rb[0], acc[i][0], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    wait_vmcnt<(NB - 2) * L>();
+    __builtin_amdgcn_s_barrier();
+    const uint32_t soffA = ls * 1024u, soffB = ls * 64u;
+    rb[0] = read16(nb + ob);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < FM; i++) {
+        acc[i][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], rb[1], acc[i][1], 0, 0, 0);
+        loads_at<0>(i, cb, lt, soffA, soffB, wave, kt, ldx2, la, lb);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    rb[1] = read16(nb + ob + 1024);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < FM; i++) {
+        acc[i][2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], rb[2], acc[i][2], 0, 0, 0);
+        loads_at<0>(FM + i, cb, lt, soffA, soffB, wave, kt, ldx2, la, lb);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    const lds_char* pa = (const lds_char*)(size_t)stage_addr(nb, oa);
+#pragma unroll
+    for (int i = 0; i < FM; i++) {
+        acc[i][3] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], rb[3], acc[i][3], 0, 0, 0);
+        fa[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(pa + i * 1024));
+        loads_at<0>(2 * FM + i, cb, lt, soffA, soffB, wave, kt, ldx2, la, lb);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+template <bool OUT_FP32>
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_dense_kernel(Args a) {
+    constexpr int SB = STAGE_BYTES;
+    __shared__ __attribute__((aligned(16))) char smem[NB * SB];
+    const uint32_t l0 = (uint32_t)(size_t)(__attribute__((address_space(3))) char*)smem;
+    const int p = blockIdx.x;
+    int Lt = tile_of(a, p, 0);
+    if (Lt < 0) return;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int wm0 = (wave / (WAVES / 2)) * WM, wn0 = (wave % (WAVES / 2)) * 64;
+    const int r = lane & 15, q = lane >> 4;
+    // LDS read offsets: A fragment i of the wave at (wm0 / 16 + i) KB + 16 lane; B fragment j at token row
+    // wn0 + 16 j + r, unit q (swizzled)
+    const uint32_t oa = (uint32_t)((wm0 >> 4) * 1024 + lane * 16);
+    const uint32_t ob = (uint32_t)(A_TILE + (wn0 + r) * 64 + 16 * (q ^ ((r >> 2) & 3)));
+    // load offsets (the range-checked lane part): A 16 lane; B row lane / 4 of a 16-row group, unit lane % 4 of
+    // that row's swizzled order
+    const uint32_t la = (uint32_t)(16 * lane);
+    const uint32_t lb = (uint32_t)((lane >> 2) * a.ldx * 2 + 16 * ((lane & 3) ^ ((lane >> 4) & 3)));
+    const int S = (int)(a.K / BKD);
+    const uint32_t kt = (uint32_t)S, ldx2 = (uint32_t)(a.ldx * 2);
+
+    f32x4 acc[FM][4];
+#pragma unroll
+    for (int i = 0; i < FM; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    Tile cur_t = tile<OUT_FP32>(a, Lt);
+    Tile nxt_t = tile<OUT_FP32>(a, tile_of(a, p, 1));
+#pragma unroll
+    for (int i = 0; i < NB; i++) {
+        const bool here = i < S;
+        const uint32_t ls = here ? i : i - S;
+        if (i == NB - 1) {
+            wait_vmcnt<(NB - 2) * L>();
+            __builtin_amdgcn_s_barrier();
+        }
+#pragma unroll
+        for (int k = 0; k < L; k++) {
+            const Tile& t = here ? cur_t : nxt_t;
+            if (k == 0) load<0>(i * SB, t, ls * 1024u, ls * 64u, wave, kt, ldx2, la, lb);
+            if (k == 1) load<1>(i * SB, t, ls * 1024u, ls * 64u, wave, kt, ldx2, la, lb);
+            if (k == 2) load<2>(i * SB, t, ls * 1024u, ls * 64u, wave, kt, ldx2, la, lb);
+            if (k == 3) load<3>(i * SB, t, ls * 1024u, ls * 64u, wave, kt, ldx2, la, lb);
+        }
+    }
+    bf16x8 fa[FM], rb[4];
+#pragma unroll
+    for (int i = 0; i < FM; i++) fa[i] = read16(l0 + oa + i * 1024);
+    rb[0] = read16(l0 + ob);
+    rb[1] = read16(l0 + ob + 1024);
+    uint32_t cur = 0;
+    for (int k = 1;; k++) {
+        int s = 0;
+        for (; s < S - NB; s++) {
+            const uint32_t nxt = cur == (NB - 1) * SB ? 0u : cur + SB;
+            stage(l0, cur, nxt, cur_t, (uint32_t)(s + NB), acc, fa, rb, oa, ob, wave, kt, ldx2, la, lb);
+            cur = nxt;
+        }
+        for (; s < S; s++) {
+            const uint32_t nxt = cur == (NB - 1) * SB ? 0u : cur + SB;
+            stage(l0, cur, nxt, nxt_t, (uint32_t)(s + NB - S), acc, fa, rb, oa, ob, wave, kt, ldx2, la, lb);
+            cur = nxt;
+        }
+        {
+            const int64_t mw = cur_t.m0 + wm0, nw = cur_t.n0 + wn0;
+            if ((mw + WM <= a.M) && (nw + 64 <= a.N) && a.y_vec)
+                store_tile_tm<OUT_FP32, true>(acc, a, cur_t.y, mw, nw, lane);
+            else
+                store_tile_tm<OUT_FP32, false>(acc, a, cur_t.y, mw, nw, lane);
+        }
+        if (!nxt_t.valid) break;
+#pragma unroll
+        for (int i = 0; i < FM; i++)
+#pragma unroll
+            for (int j = 0; j < 4; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        cur_t = nxt_t;
+        nxt_t = tile<OUT_FP32>(a, tile_of(a, p, k + 1));
+    }
+    wait_vmcnt<0>();
+}
+
+// Dense M x K bf16 (row pitch ldw) -> the tiled operand order above; rows past M padded with zeros. One thread
+// per 16-byte chunk of the output.
+__global__ __launch_bounds__(256) void dense_tile_kernel(const uint16_t* __restrict__ W, int64_t M, int64_t K, int64_t ldw,
+                                                         u32x4* __restrict__ out, int64_t chunks) {
+    const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (c >= chunks) return;
+    const int64_t kt = K / BKD;
+    const int l = (int)(c & 63);
+    const int64_t t = (c >> 6) % kt, b = (c >> 6) / kt;
+    const int64_t m = 16 * b + (l & 15), k = BKD * t + 8 * (l >> 4);
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (m < M) v = *reinterpret_cast<const u32x4*>(W + m * ldw + k);
+    out[c] = v;
+}
+}  // namespace dense_ref
 
 }  // namespace tiled_bf16
 
@@ -987,6 +1197,41 @@ hipError_t launch_gemm_bf16_tiled(const GemmArgs& g, hipStream_t s) {
     if (t256 < cus || (t256 <= 2 * cus && c128 <= c256))
         return g.tm ? launch_bn<true, 128, 2>(g, s) : launch_bn<false, 128, 2>(g, s);
     return g.tm ? launch_bn<true, 256, 1>(g, s) : launch_bn<false, 256, 1>(g, s);
+}
+
+}  // namespace sp24
+
+namespace sp24 {
+
+// Host side of the dense reference (measurement only; arguments validated by the C ABI).
+hipError_t launch_dense_tile(const void* W, int64_t M, int64_t K, int64_t ldw, void* Wt, hipStream_t s) {
+    const int64_t chunks = (M + 15) / 16 * (K / tiled_bf16::dense_ref::BKD) * 64;
+    hipLaunchKernelGGL(tiled_bf16::dense_ref::dense_tile_kernel, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, s,
+                       static_cast<const uint16_t*>(W), M, K, ldw, static_cast<u32x4*>(Wt), chunks);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_dense_ref(const GemmArgs& g, hipStream_t s) {
+    namespace D = tiled_bf16::dense_ref;
+    tiled_bf16::Args a;
+    a.vals = static_cast<const uint16_t*>(g.values); a.meta = nullptr;
+    a.X = static_cast<const uint16_t*>(g.X); a.Y = g.Y;
+    a.M = g.M; a.K = g.K; a.N = g.N; a.ldx = g.ldx; a.ldy = g.ldy;
+    a.sxb = 0; a.syb = 0;
+    a.tilesM = (int)((g.M + tiled_bf16::BM - 1) / tiled_bf16::BM);
+    a.tilesN = (int)((g.N + D::BN - 1) / D::BN);
+    a.batch = 1;
+    const int64_t es = g.out_fp32 ? 4 : 2;
+    a.y_vec = ((reinterpret_cast<uintptr_t>(g.Y) & 15) == 0) && ((g.ldy * es) % 16 == 0) && g.ldy * es * 16 < ((int64_t)1 << 31);
+    const int T = a.tilesM * a.tilesN;
+    const int S = (int)(g.K / D::BKD);
+    const int slots = device_cus();
+    const unsigned grid = (unsigned)(S >= D::NB && T > slots ? slots : T);
+    if (g.out_fp32)
+        hipLaunchKernelGGL((D::gemm_dense_kernel<true>), dim3(grid), dim3(64 * D::WAVES), 0, s, a);
+    else
+        hipLaunchKernelGGL((D::gemm_dense_kernel<false>), dim3(grid), dim3(64 * D::WAVES), 0, s, a);
+    return hipGetLastError();
 }
 
 }  // namespace sp24
