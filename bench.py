@@ -182,16 +182,25 @@ def _bf16_gemm_workload(name, W_host, X_host, score, Xcal_host, config, layout, 
                           M * K * 9 // 8 + K * N * 2 + M * N * ob, float(M) * N * K, "bf16", gemm_sources(N)))
 
     def dense_ref():
+        """Dense bf16 GEMMs of the same shape on the decompressed (pruned) weight: hipBLASLt through
+        torch.matmul, and (token-major, K % 64 == 0) the library's dense reference with the sparse tiled
+        kernel's tiling (include/sp24_bench.h)."""
         c0 = copies[0]
         for k in kernels:
             k.fn(c0)
         Wd = sp.sp24_decompress(c0["vals"], c0["meta"], M, K)
+        out = {}
         if tm:
-            Wt = Wd.t()  # X (N x K) @ W^T, the Linear layer's own product
+            Wtr = Wd.t()  # X (N x K) @ W^T, the Linear layer's own product
             Yd = torch.empty((N, M), dtype=torch.bfloat16, device="cuda")
-            return lambda c: torch.matmul(c["X"], Wt, out=Yd)
-        Yd = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
-        return lambda c: torch.matmul(Wd, c["X"], out=Yd)
+            out["dense_bf16_matmul_same_shape"] = lambda c: torch.matmul(c["X"], Wtr, out=Yd)
+            if K % 64 == 0 and N >= TILED_MIN_N:
+                Wtiled = sp.sp24_bench_dense_tile(Wd)
+                out["dense_bf16_same_tiling"] = lambda c: sp.sp24_bench_gemm_dense_bf16(Wtiled, M, c["X"], out=Yd)
+        else:
+            Yd = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+            out["dense_bf16_matmul_same_shape"] = lambda c: torch.matmul(Wd, c["X"], out=Yd)
+        return out
 
     def cpu_sample(budget_s):
         """The oracle per function: column norms, prune/compress and decompress of the whole weight (median
@@ -720,10 +729,11 @@ def main():
             roof["mfma_frac_at_sclk"] = round(k.flops / (per_kernel_ms[dom] * 1e-3) / 1e12 / peak_sclk, 4)
 
     if not args.no_dense_ref and w.get("dense_ref"):
-        fn = w["dense_ref"]()
-        t_dense = kernel_time_ms(fn, w["copies"], args.steps, args.warmup)
-        kernels["dense_bf16_matmul_same_shape"] = dict(avg_us=round(t_dense * 1e3, 2))
-        kernels["gemm_bf16"]["speedup_vs_dense"] = round(t_dense / per_kernel_ms["gemm_bf16"], 3)
+        for name, fn in w["dense_ref"]().items():
+            t_dense = kernel_time_ms(fn, w["copies"], args.steps, args.warmup)
+            kernels[name] = dict(avg_us=round(t_dense * 1e3, 2))
+            key = "speedup_vs_dense" if name == "dense_bf16_matmul_same_shape" else "speedup_vs_dense_same_tiling"
+            kernels["gemm_bf16"][key] = round(t_dense / per_kernel_ms["gemm_bf16"], 3)
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -27,6 +27,7 @@ EXPORTS = ("sp24_col_norms", "sp24_compressed_bytes", "sp24_prune_compress", "sp
            "sp24_channel_permutation", "sp24_decompress",
            "sp24_gemm_bf16",
            "sp24_gemm_i8", "sp24_gemm_bf16_ex", "sp24_gemm_i8_ex", "sp24_gemm_i8_fused", "sp24_probe_sclk",
+           "sp24_bench_dense_tiled_bytes", "sp24_bench_dense_tile", "sp24_bench_gemm_dense_bf16",
            "sp24_status_string")
 
 _TORCH_TO_SP24 = {torch.bfloat16: SP24_BF16, torch.float16: SP24_FP16, torch.float32: SP24_FP32,
@@ -66,6 +67,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sp24_gemm_i8_fused.argtypes = [P, P, I64, I64, P, I64, I64, I64, P, P, I, P, I, ctypes.c_float, I64, I64, I64,
                                        I, P]
     lib.sp24_probe_sclk.argtypes = [I64, I, P, P]
+    lib.sp24_bench_dense_tiled_bytes.argtypes = [I64, I64, ctypes.POINTER(I64)]
+    lib.sp24_bench_dense_tile.argtypes = [P, I64, I64, I64, P, P]
+    lib.sp24_bench_gemm_dense_bf16.argtypes = [P, I64, I64, P, I64, I64, P, I, I64, P]
     for fn in EXPORTS[:-1]:
         getattr(lib, fn).restype = I
     lib.sp24_status_string.argtypes = [I]
@@ -328,3 +332,42 @@ def sp24_probe_sclk(blocks: int | None = None, iters: int = 4000, device: int | 
     n = 16.0 * iters
     return {"sclk_mhz": float((cycles / (ticks / 100.0)).mean()), "cycles_per_smfmac": float((cycles / n).mean()),
             "waves": int(h.shape[0])}
+
+
+# ----------------------------------------------------------------------------- measurement support
+# (include/sp24_bench.h): a dense reference GEMM with the token-major sparse kernel's tiling.
+
+def sp24_bench_dense_tiled_bytes(M: int, K: int) -> int:
+    """Bytes of the dense tiled copy of an M x K bf16 weight."""
+    b = ctypes.c_int64()
+    _check("sp24_bench_dense_tiled_bytes", load_library().sp24_bench_dense_tiled_bytes(M, K, ctypes.byref(b)))
+    return b.value
+
+
+def sp24_bench_dense_tile(W: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Dense bf16 W (M x K) -> its copy in v_mfma_f32_16x16x32_bf16 operand order (1-D bf16 buffer)."""
+    _dev_check(W, out)
+    M, K = W.shape
+    nb = sp24_bench_dense_tiled_bytes(M, K)
+    if out is None:
+        out = torch.empty(nb // 2, dtype=torch.bfloat16, device=W.device)
+    if out.numel() * 2 != nb or not out.is_contiguous():
+        raise ValueError(f"the tiled copy needs a contiguous buffer of {nb} bytes")
+    _check("sp24_bench_dense_tile", load_library().sp24_bench_dense_tile(_ptr(W), M, K, _rows(W, "W"), _ptr(out),
+                                                                         _stream(W)))
+    return out
+
+
+def sp24_bench_gemm_dense_bf16(W_tiled: torch.Tensor, M: int, X: torch.Tensor, out_dtype: torch.dtype = torch.float32,
+                               out: torch.Tensor | None = None) -> torch.Tensor:
+    """Dense token-major GEMM Y (N x M) = X (N x K) . W^T with the sparse tiled kernel's tiling (measurement only)."""
+    _dev_check(W_tiled, X, out)
+    N, K = X.shape
+    if W_tiled.numel() * 2 != sp24_bench_dense_tiled_bytes(M, K):
+        raise ValueError("W_tiled does not hold an M x K weight")
+    if out is None:
+        out = torch.empty((N, M), dtype=out_dtype, device=X.device)
+    st = load_library().sp24_bench_gemm_dense_bf16(_ptr(W_tiled), M, K, _ptr(X), N, _rows(X, "X"), _ptr(out),
+                                                   _TORCH_TO_SP24[out.dtype], _rows(out, "out"), _stream(X))
+    _check("sp24_bench_gemm_dense_bf16", st)
+    return out

@@ -1,6 +1,7 @@
 // C ABI of the sp24 library: argument validation (host only, before any HIP call), the device check,
 // and dispatch to the kernels. Declarations and the contract live in include/sp24.h.
 #include "../../include/sp24.h"
+#include "../../include/sp24_bench.h"
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -324,4 +325,45 @@ int sp24_probe_sclk(int64_t blocks, int iters, uint64_t* out, void* stream) {
     return hip_status(sp24::launch_sclk_probe(blocks, iters, out, static_cast<hipStream_t>(stream)));
 }
 
+
+/* ---- measurement support: the dense reference with the token-major tiled kernel's tiling ---- */
+
+int sp24_bench_dense_tiled_bytes(int64_t M, int64_t K, int64_t* bytes) {
+    if (!bytes) return SP24_ERR_NULL;
+    if (M < 1 || K < 64 || K % 64 != 0) return SP24_ERR_SHAPE;
+    *bytes = padded_m(M) * K * 2;
+    return SP24_OK;
+}
+
+int sp24_bench_dense_tile(const void* W, int64_t M, int64_t K, int64_t ldw, void* W_tiled, void* stream) {
+    if (!W || !W_tiled) return SP24_ERR_NULL;
+    if (M < 1 || K < 64 || K % 64 != 0 || ldw < K) return SP24_ERR_SHAPE;
+    if (!aligned16(W) || !aligned16(W_tiled) || (ldw * 2) % 16 != 0) return SP24_ERR_ALIGN;
+    if (padded_m(M) / 16 * (K / 32) * 64 >= kMaxChunks) return SP24_ERR_SHAPE;
+    const int st = check_device();
+    if (st != SP24_OK) return st;
+    return hip_status(sp24::launch_dense_tile(W, M, K, ldw, W_tiled, static_cast<hipStream_t>(stream)));
+}
+
+int sp24_bench_gemm_dense_bf16(const void* W_tiled, int64_t M, int64_t K, const void* X, int64_t N, int64_t ldx, void* Y,
+                               int out_dtype, int64_t ldy, void* stream) {
+    if (!W_tiled || !X || !Y) return SP24_ERR_NULL;
+    if (out_dtype != SP24_FP32 && out_dtype != SP24_BF16) return SP24_ERR_DTYPE;
+    if (M < 1 || N < 1 || K < 64 || K % 64 != 0 || ldx < K || ldy < M) return SP24_ERR_SHAPE;
+    if (K >= ((int64_t)1 << 22) || ldx >= ((int64_t)1 << 22) || ldy >= ((int64_t)1 << 31)) return SP24_ERR_SHAPE;
+    if (((M + 255) / 256) * ((N + 255) / 256) >= ((int64_t)1 << 30)) return SP24_ERR_SHAPE;
+    if (!aligned16(W_tiled) || !aligned16(X) || ldx % 8 != 0 || !aligned16(Y)) return SP24_ERR_ALIGN;
+    const int st = check_device();
+    if (st != SP24_OK) return st;
+    sp24::GemmArgs g = {};
+    g.values = W_tiled;
+    g.meta = nullptr;
+    g.M = M; g.K = K; g.N = N;
+    g.X = X; g.ldx = ldx; g.sx = 0;
+    g.Y = Y; g.ldy = ldy; g.sy = 0;
+    g.batch = 1;
+    g.tm = true;
+    g.out_fp32 = out_dtype == SP24_FP32;
+    return hip_status(sp24::launch_gemm_dense_ref(g, static_cast<hipStream_t>(stream)));
+}
 }  // extern "C"

@@ -65,6 +65,11 @@ hipError_t launch_gemm_bf16_fewtok(const GemmArgs& g, hipStream_t s);
 bool gemm_bf16_tiled_ok(const GemmArgs& g);
 hipError_t launch_gemm_bf16_tiled(const GemmArgs& g, hipStream_t s);
 
+// Dense reference with the token-major tiled kernel's tiling (measurement only): the weight converted to the
+// MFMA operand order, and the GEMM (token-major X, batch 1; values = the converted weight).
+hipError_t launch_dense_tile(const void* W, int64_t M, int64_t K, int64_t ldw, void* Wt, hipStream_t s);
+hipError_t launch_gemm_dense_ref(const GemmArgs& g, hipStream_t s);
+
 // int8 GEMM: LDS-tiled when it applies, else direct.
 hipError_t launch_gemm_i8(const GemmArgs& g, hipStream_t s);
 bool gemm_i8_fewtok_ok(const GemmArgs& g);

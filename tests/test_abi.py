@@ -1,5 +1,5 @@
 """Host-side checks of the C-ABI library (no GPU needed, no kernel launched):
-the library loads, exports every symbol include/sp24.h declares, and rejects invalid arguments on
+the library loads, exports every symbol include/*.h declares, and rejects invalid arguments on
 the host before any HIP call."""
 import ctypes
 import os
@@ -14,7 +14,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def _declared_functions():
-    txt = open(os.path.join(ROOT, "include", "sp24.h")).read()
+    inc = os.path.join(ROOT, "include")
+    txt = "".join(open(os.path.join(inc, f)).read() for f in sorted(os.listdir(inc)) if f.endswith(".h"))
     txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
     return sorted(set(re.findall(r"\b(sp24_[a-z0-9_]+)\s*\(", txt)))
 
@@ -261,3 +262,24 @@ def test_valid_arguments_without_a_device_report_device_error(lib):
 def test_binding_refuses_host_tensors(lib):
     with pytest.raises(ValueError):
         sp.sp24_col_norms(torch.zeros((4, 4), dtype=torch.bfloat16))
+
+
+def test_bench_dense_reference_validation(lib):
+    P, I64 = ctypes.c_void_p, ctypes.c_int64
+    b = I64()
+    assert lib.sp24_bench_dense_tiled_bytes(40, 128, ctypes.byref(b)) == 0 and b.value == 48 * 128 * 2
+    assert lib.sp24_bench_dense_tiled_bytes(40, 96, ctypes.byref(b)) == sp.SP24_ERR_SHAPE
+    assert lib.sp24_bench_dense_tiled_bytes(40, 128, None) == sp.SP24_ERR_NULL
+    p = P(4096)
+    assert lib.sp24_bench_dense_tile(None, 16, 64, 64, p, None) == sp.SP24_ERR_NULL
+    assert lib.sp24_bench_dense_tile(p, 16, 96, 96, p, None) == sp.SP24_ERR_SHAPE
+    assert lib.sp24_bench_dense_tile(p, 16, 64, 60, p, None) == sp.SP24_ERR_SHAPE
+    assert lib.sp24_bench_dense_tile(p, 16, 64, 68, p, None) == sp.SP24_ERR_ALIGN
+    assert lib.sp24_bench_dense_tile(P(4098), 16, 64, 64, p, None) == sp.SP24_ERR_ALIGN
+    g = lib.sp24_bench_gemm_dense_bf16
+    assert g(p, 16, 64, None, 8, 64, p, sp.SP24_FP32, 16, None) == sp.SP24_ERR_NULL
+    assert g(p, 16, 64, p, 8, 64, p, sp.SP24_I8, 16, None) == sp.SP24_ERR_DTYPE
+    assert g(p, 16, 80, p, 8, 80, p, sp.SP24_FP32, 16, None) == sp.SP24_ERR_SHAPE
+    assert g(p, 16, 64, p, 0, 64, p, sp.SP24_FP32, 16, None) == sp.SP24_ERR_SHAPE
+    assert g(p, 16, 64, p, 8, 64, p, sp.SP24_FP32, 15, None) == sp.SP24_ERR_SHAPE
+    assert g(p, 16, 64, p, 8, 68, p, sp.SP24_FP32, 16, None) == sp.SP24_ERR_ALIGN
