@@ -615,6 +615,20 @@ def launch_stats_us(fn, copies, steps):
     return float(np.median(t)), float(np.percentile(t, 10)), float(np.percentile(t, 90))
 
 
+def stream_floor_us(nbytes: int, steps: int):
+    """The achievable floor for a kernel that must read nbytes once: a plain streaming read of exactly that many
+    bytes (sp24_bench_stream_read), rotated over enough buffer copies that the launches cycle over more than
+    twice the Infinity Cache, as the kernels are. Returns (average us, copies)."""
+    nb = (int(nbytes) + 15) // 16 * 16
+    n = max(2, min(64, int(np.ceil(2 * CACHE_BYTES / nb)) + 1))
+    bufs = [dict(src=torch.empty(nb, dtype=torch.uint8, device="cuda").fill_(1)) for _ in range(n)]
+    sink = sp.sp24_bench_stream_read(bufs[0]["src"])
+    t = kernel_time_ms(lambda c: sp.sp24_bench_stream_read(c["src"], nb, sink), bufs, steps, 2) * 1e3
+    del bufs
+    torch.cuda.empty_cache()
+    return t, n
+
+
 def cpu_model() -> str:
     try:
         for line in open("/proc/cpuinfo"):
@@ -714,6 +728,17 @@ def main():
         # warm: the same launch repeated on one copy, so whatever fits stays in the caches (labelled as such)
         e["warm_avg_us"] = round(kernel_time_ms(k.fn, w["copies"][:1], args.steps, 1) * 1e3, 2)
         kernels[k.name] = e
+    # HBM-bound GEMMs (few tokens) and an HBM-bound dominant kernel: the measured streaming-read floor of the same
+    # bytes beside the spec peak
+    for k in w["kernels"]:
+        kr = roofline(k, per_kernel_ms[k.name] * 1e-3, w["name"])
+        if kr["bound"] == "hbm" and (k.flops or k.name == dom):
+            f_us, n = stream_floor_us(k.nbytes, args.steps)
+            e = kernels[k.name]
+            e.update(floor_us=round(f_us, 2), floor_gbs=round(k.nbytes / f_us / 1e3, 1),
+                     frac_of_floor=round(f_us / e["avg_us"], 4), hbm_frac=round(k.nbytes / e["avg_us"] / 1e3 / HBM_PEAK_GBS, 4))
+            if k.name == dom:
+                roof.update(floor_us=e["floor_us"], floor_gbs=e["floor_gbs"], frac_of_floor=e["frac_of_floor"])
     roof["median_us"] = kernels[dom]["median_us"]
     roof["p10_us"], roof["p90_us"] = kernels[dom]["p10_us"], kernels[dom]["p90_us"]
 

@@ -39,6 +39,14 @@ int sp24_bench_dense_tile(const void* W, int64_t M, int64_t K, int64_t ldw, void
 int sp24_bench_gemm_dense_bf16(const void* W_tiled, int64_t M, int64_t K, const void* X, int64_t N, int64_t ldx,
                                void* Y, int out_dtype, int64_t ldy, void* stream);
 
+/* A plain streaming read of `bytes` (a multiple of 16) from src: the achievable floor for a kernel that must read
+ * that many bytes once, launch ramp and tail included, against which the few-token GEMMs (bound by streaming
+ * their compressed weight) are reported. Every 16-byte word is loaded once; workgroup b writes the XOR of the
+ * words it read to sink[b] (16 bytes each; sp24_bench_stream_read_blocks gives the count, so the caller sizes
+ * sink and can check that every word was read). 16-byte aligned pointers. */
+int sp24_bench_stream_read_blocks(int64_t bytes, int64_t* blocks);
+int sp24_bench_stream_read(const void* src, int64_t bytes, void* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

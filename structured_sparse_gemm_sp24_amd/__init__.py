@@ -28,6 +28,7 @@ EXPORTS = ("sp24_col_norms", "sp24_compressed_bytes", "sp24_prune_compress", "sp
            "sp24_gemm_bf16",
            "sp24_gemm_i8", "sp24_gemm_bf16_ex", "sp24_gemm_i8_ex", "sp24_gemm_i8_fused", "sp24_probe_sclk",
            "sp24_bench_dense_tiled_bytes", "sp24_bench_dense_tile", "sp24_bench_gemm_dense_bf16",
+           "sp24_bench_stream_read_blocks", "sp24_bench_stream_read",
            "sp24_status_string")
 
 _TORCH_TO_SP24 = {torch.bfloat16: SP24_BF16, torch.float16: SP24_FP16, torch.float32: SP24_FP32,
@@ -70,6 +71,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sp24_bench_dense_tiled_bytes.argtypes = [I64, I64, ctypes.POINTER(I64)]
     lib.sp24_bench_dense_tile.argtypes = [P, I64, I64, I64, P, P]
     lib.sp24_bench_gemm_dense_bf16.argtypes = [P, I64, I64, P, I64, I64, P, I, I64, P]
+    lib.sp24_bench_stream_read_blocks.argtypes = [I64, ctypes.POINTER(I64)]
+    lib.sp24_bench_stream_read.argtypes = [P, I64, P, P]
     for fn in EXPORTS[:-1]:
         getattr(lib, fn).restype = I
     lib.sp24_status_string.argtypes = [I]
@@ -371,3 +374,21 @@ def sp24_bench_gemm_dense_bf16(W_tiled: torch.Tensor, M: int, X: torch.Tensor, o
                                                    _TORCH_TO_SP24[out.dtype], _rows(out, "out"), _stream(X))
     _check("sp24_bench_gemm_dense_bf16", st)
     return out
+
+
+def sp24_bench_stream_read(src: torch.Tensor, nbytes: int | None = None, sink: torch.Tensor | None = None) -> torch.Tensor:
+    """Streaming read of the first nbytes of src (measurement only); returns the per-workgroup XOR words
+    (uint32, 4 per workgroup)."""
+    _dev_check(src, sink)
+    nb = src.numel() * src.element_size() if nbytes is None else int(nbytes)
+    if nb > src.numel() * src.element_size() or not src.is_contiguous():
+        raise ValueError("nbytes exceeds the contiguous source")
+    lib = load_library()
+    blocks = ctypes.c_int64()
+    _check("sp24_bench_stream_read_blocks", lib.sp24_bench_stream_read_blocks(nb, ctypes.byref(blocks)))
+    if sink is None:
+        sink = torch.empty(4 * blocks.value, dtype=torch.int32, device=src.device)
+    if sink.numel() * sink.element_size() < 16 * blocks.value:
+        raise ValueError("sink too small")
+    _check("sp24_bench_stream_read", lib.sp24_bench_stream_read(_ptr(src), nb, _ptr(sink), _stream(src)))
+    return sink

@@ -366,4 +366,22 @@ int sp24_bench_gemm_dense_bf16(const void* W_tiled, int64_t M, int64_t K, const 
     g.out_fp32 = out_dtype == SP24_FP32;
     return hip_status(sp24::launch_gemm_dense_ref(g, static_cast<hipStream_t>(stream)));
 }
+
+int sp24_bench_stream_read_blocks(int64_t bytes, int64_t* blocks) {
+    if (!blocks) return SP24_ERR_NULL;
+    if (bytes < 16 || bytes % 16 != 0) return SP24_ERR_SHAPE;
+    const int st = check_device();
+    if (st != SP24_OK) return st;
+    *blocks = sp24::stream_read_blocks(bytes);
+    return SP24_OK;
+}
+
+int sp24_bench_stream_read(const void* src, int64_t bytes, void* sink, void* stream) {
+    if (!src || !sink) return SP24_ERR_NULL;
+    if (bytes < 16 || bytes % 16 != 0) return SP24_ERR_SHAPE;
+    if (!aligned16(src) || !aligned16(sink)) return SP24_ERR_ALIGN;
+    const int st = check_device();
+    if (st != SP24_OK) return st;
+    return hip_status(sp24::launch_stream_read(src, bytes, sink, static_cast<hipStream_t>(stream)));
+}
 }  // extern "C"

@@ -70,6 +70,10 @@ hipError_t launch_gemm_bf16_tiled(const GemmArgs& g, hipStream_t s);
 hipError_t launch_dense_tile(const void* W, int64_t M, int64_t K, int64_t ldw, void* Wt, hipStream_t s);
 hipError_t launch_gemm_dense_ref(const GemmArgs& g, hipStream_t s);
 
+// Streaming read (measurement only): workgroups used for `bytes`, and the launch.
+int stream_read_blocks(int64_t bytes);
+hipError_t launch_stream_read(const void* src, int64_t bytes, void* sink, hipStream_t s);
+
 // int8 GEMM: LDS-tiled when it applies, else direct.
 hipError_t launch_gemm_i8(const GemmArgs& g, hipStream_t s);
 bool gemm_i8_fewtok_ok(const GemmArgs& g);

@@ -283,3 +283,13 @@ def test_bench_dense_reference_validation(lib):
     assert g(p, 16, 64, p, 0, 64, p, sp.SP24_FP32, 16, None) == sp.SP24_ERR_SHAPE
     assert g(p, 16, 64, p, 8, 64, p, sp.SP24_FP32, 15, None) == sp.SP24_ERR_SHAPE
     assert g(p, 16, 64, p, 8, 68, p, sp.SP24_FP32, 16, None) == sp.SP24_ERR_ALIGN
+
+
+def test_bench_stream_read_validation(lib):
+    P, I64 = ctypes.c_void_p, ctypes.c_int64
+    b = I64()
+    assert lib.sp24_bench_stream_read_blocks(100, ctypes.byref(b)) == sp.SP24_ERR_SHAPE
+    assert lib.sp24_bench_stream_read_blocks(64, None) == sp.SP24_ERR_NULL
+    assert lib.sp24_bench_stream_read(None, 64, P(4096), None) == sp.SP24_ERR_NULL
+    assert lib.sp24_bench_stream_read(P(4096), 8, P(4096), None) == sp.SP24_ERR_SHAPE
+    assert lib.sp24_bench_stream_read(P(4104), 64, P(4096), None) == sp.SP24_ERR_ALIGN

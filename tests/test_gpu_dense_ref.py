@@ -54,3 +54,16 @@ def test_dense_reference(M, K, N, ldx):
     assert np.all(np.abs(yf.astype(np.float64) - Y64) <= bound)
     assert frob_rel(yf, Y64) <= 1e-3
     assert np.array_equal(host_bits(Yb), synth.f32_to_bf16_bits(host_bits(Yf)))
+
+
+@pytest.mark.parametrize("nbytes", [16, 4096, 1000000 * 16 + 48, 19 * (1 << 20)])
+def test_stream_read_reads_every_word(nbytes):
+    # the floor kernel bench.py times: the XOR of its per-workgroup words is the XOR of every 16-byte word
+    rng = np.random.default_rng(nbytes % 1000)
+    words = rng.integers(0, 2 ** 32, size=nbytes // 4, dtype=np.uint32)
+    say(f"stream read {nbytes} bytes")
+    src = dev(words.view(np.int32))
+    sink = host_bits(sp.sp24_bench_stream_read(src)).view(np.uint32).reshape(-1, 4)
+    x = np.bitwise_xor.reduce(sink, axis=0)
+    want = np.bitwise_xor.reduce(words.reshape(-1, 4), axis=0)
+    assert np.array_equal(x, want)
