@@ -227,8 +227,8 @@ def _bf16_gemm_workload(name, W_host, X_host, score, Xcal_host, config, layout, 
         gemm_what = f"GEMM on the first {rows} of {M} rows (N = {N}), scaled to all rows" if extra else f"GEMM on all {M} rows"
         return total, f"{what} + {gemm_what}", per
 
-    return dict(name=name, dtype="bf16", unit="TFLOP/s", config=config, flops=2.0 * M * N * K, copies=copies,
-                kernels=kernels, dense_ref=dense_ref, cpu_sample=cpu_sample)
+    return dict(name=name if tm else name + "_feature", dtype="bf16", unit="TFLOP/s", config=config,
+                flops=2.0 * M * N * K, copies=copies, kernels=kernels, dense_ref=dense_ref, cpu_sample=cpu_sample)
 
 
 def workload_vit(args):
@@ -371,7 +371,8 @@ def workload_bert_int8(args):
                out="fp32 (int32 accumulate, per-channel dequant)", step="2 x (prune_compress int8 + gemm_i8)",
                layout="token-major: X N x K, Y N x M" if args.layout == "token" else "feature-major: X K x N, Y M x N")
     flops = sum(2.0 * L["M"] * L["N"] * L["K"] for L in layers)
-    return dict(name="bert_ffn_int8", dtype="i8", unit="TOP/s", config=cfg, flops=flops, copies=copies,
+    return dict(name="bert_ffn_int8" + ("" if args.layout == "token" else "_feature"), dtype="i8", unit="TOP/s",
+                config=cfg, flops=flops, copies=copies,
                 kernels=kernels, dense_ref=None, cpu_sample=cpu_sample)
 
 
@@ -462,7 +463,8 @@ def workload_bert_int8_fused(args):
                                        "fused GEMM 2 (bias, fp32 out)",
                layout="token-major: X N x K, Y N x M" if tm else "feature-major: X K x N, Y M x N")
     flops = 2.0 * M1 * N * K1 + 2.0 * M2 * N * K2
-    return dict(name="bert_ffn_int8_fused", dtype="i8", unit="TOP/s", config=cfg, flops=flops, copies=copies,
+    return dict(name="bert_ffn_int8_fused" + ("" if tm else "_feature"), dtype="i8", unit="TOP/s", config=cfg,
+                flops=flops, copies=copies,
                 kernels=kernels, dense_ref=None, cpu_sample=cpu_sample)
 
 
@@ -728,11 +730,10 @@ def main():
         # warm: the same launch repeated on one copy, so whatever fits stays in the caches (labelled as such)
         e["warm_avg_us"] = round(kernel_time_ms(k.fn, w["copies"][:1], args.steps, 1) * 1e3, 2)
         kernels[k.name] = e
-    # HBM-bound GEMMs (few tokens) and an HBM-bound dominant kernel: the measured streaming-read floor of the same
-    # bytes beside the spec peak
+    # GEMMs that stream their weight (few tokens: at most 64 flop per byte, reads dominate): the measured
+    # streaming-read floor of the same bytes beside the spec peak
     for k in w["kernels"]:
-        kr = roofline(k, per_kernel_ms[k.name] * 1e-3, w["name"])
-        if kr["bound"] == "hbm" and (k.flops or k.name == dom):
+        if k.flops and k.flops / k.nbytes <= 64:
             f_us, n = stream_floor_us(k.nbytes, args.steps)
             e = kernels[k.name]
             e.update(floor_us=round(f_us, 2), floor_gbs=round(k.nbytes / f_us / 1e3, 1),
