@@ -56,6 +56,11 @@ TM_SHAPES = [
     # 16-byte rows): 4, 8 and 16 waves, 2- and 8-row X tiles, K tails (80, 208, 240), one K tile per
     # wave or several; and N = 9 .. 16 on the register-pipelined kernel
     (9000, 192, 16, 200, 9000),
+    # few-token units of two row blocks sharing one X tile (9 to 16 tokens, 512 row blocks and more): odd
+    # block counts (a last workgroup with one block), a K tail, both ring configurations
+    (16400, 240, 13, 248, 16400),
+    (8200, 4096, 16, 4096, 8200),
+    (6150, 320, 11, 320, 6150),
     (4000, 320, 12, 320, 4000),
     (3100, 256, 3, 264, 3100),
     (2050, 240, 9, 248, 2056),
@@ -100,6 +105,7 @@ BATCH_SHAPES = [
     (2, 128, 256, 100, "token"),
     (3, 48, 64, 20, "token"),
     (2, 300, 208, 90, "token"),
+    (2, 8200, 128, 10, "token"),
     (3, 200, 320, 12, "token"),
     (2, 200, 320, 6, "token"),
 ]
