@@ -20,9 +20,9 @@
 //   A (compressed values): the weight is stored as 1 KB tiles in the lane order of the smfmac A
 //     operand (16 rows x 64 dense columns), so each tile is one contiguous 64-lane copy, and a
 //     lane's ds_read_b128 of its operand is conflict-free.
-//   metadata: 128 B tiles in lane order; a lane reads its 16-bit index with ds_read_u16. The token-major loop
-//     reads four fragments' indices at once with ds_read_b64_tr_b16 (16 lanes x 4 tiles transposed, so a lane
-//     gets its own index from each tile, two to a register) and selects the half with the smfmac's abid field.
+//   metadata: 128 B tiles in lane order; a lane reads four fragments' 16-bit indices at once with
+//     ds_read_b64_tr_b16 (16 lanes x 4 tiles transposed, so a lane gets its own index from each tile, two
+//     to a register) and the smfmac's abid field selects the half.
 //   B tile (X, 64 rows x 256 bf16 = 512 B per row; 128 bf16 = 256 B in the 128-wide tile): row-major
 //     with the 32-byte units of row k stored at unit ^ v(k), v(k) = 2 (k & 3) + ((k >> 3) & 1) (< 8,
 //     so a unit stays in its row for either width). One transposing read (below) takes 16 rows x 32
@@ -305,9 +305,8 @@ __device__ __forceinline__ TileDesc tile_desc(const Args& a, int L) {
 template <int FNT, int BROW>  // fragments per wave, bytes per row of the feature-major B tile
 struct LaneOffsets {
     int a;        // A fragment of block wm0/16: block * 1024 + lane * 16
-    int m;        // metadata of block wm0/16: A_BYTES + block * 128 + lane * 2; token-major: the transposing
-                  // read of blocks wm0/16 .. +3, A_BYTES + block * 128 + 128 ((lane & 15) >> 2) + 32 (lane >> 4)
-                  // + 8 (lane & 3) (+512: the next four blocks)
+    int m;        // metadata: the transposing read of blocks wm0/16 .. +3, A_BYTES + (wm0 / 16) * 128 +
+                  // 128 ((lane & 15) >> 2) + 32 (lane >> 4) + 8 (lane & 3) (+512: the next four blocks)
     int b[FNT];   // B fragment j, first read (t = 0): row part + swizzled column part; token-major: the
                   // two reads of fragment 0 (b[0], b[1]; fragment j adds 16 rows x 128 B)
 };
@@ -317,9 +316,8 @@ __device__ __forceinline__ LaneOffsets<FNT, BROW> lane_offsets(int wm0, int wn0,
     const int r = lane & 15, q = lane >> 4;
     LaneOffsets<FNT, BROW> o;
     o.a = (wm0 >> 4) * 1024 + lane * 16;
-    o.m = A_BYTES + (wm0 >> 4) * 128 + lane * 2;
+    o.m = A_BYTES + (wm0 >> 4) * 128 + 128 * (r >> 2) + 32 * q + 8 * (r & 3);
     if constexpr (TM) {
-        o.m += 128 * (r >> 2) + 32 * q + 8 * (r & 3) - lane * 2;
         const int base = A_BYTES + META_BYTES + (wn0 + r) * 128, u = q ^ tm_swz(r);
         o.b[0] = base + 16 * u;
         o.b[1] = base + 16 * (u ^ 4);
@@ -340,11 +338,11 @@ __device__ __forceinline__ LaneOffsets<FNT, BROW> lane_offsets(int wm0, int wn0,
     return o;
 }
 
-// Operands of one stage held in registers: the 8 A fragments and their indices (token-major: packed two to a
-// register, fragment i in half i & 1 of idx[i / 2]).
+// Operands of one stage held in registers: the 8 A fragments and their indices, packed two to a register
+// (fragment i in half i & 1 of idx[i / 2]).
 struct AFrags {
     bf16x8 a[FM];
-    uint32_t idx[FM];
+    uint32_t idx[FM / 2];
 };
 
 typedef __attribute__((address_space(3))) char lds_char;
@@ -357,7 +355,7 @@ __device__ __forceinline__ u32x2 read_idx4(const lds_char* p) {
 }
 
 // smfmac of fragment i (unrolled, so the branch folds) with its index from the packed registers.
-__device__ __forceinline__ f32x4 smfmac_tm(const AFrags& f, int i, const bf16x16& b, const f32x4& c) {
+__device__ __forceinline__ f32x4 smfmac_p(const AFrags& f, int i, const bf16x16& b, const f32x4& c) {
     return (i & 1) ? __builtin_amdgcn_smfmac_f32_16x16x64_bf16(f.a[i], b, c, (int)f.idx[i >> 1], 0, 1)
                    : __builtin_amdgcn_smfmac_f32_16x16x64_bf16(f.a[i], b, c, (int)f.idx[i >> 1], 0, 0);
 }
@@ -371,22 +369,18 @@ __device__ __forceinline__ uint32_t stage_addr(uint32_t buf, int off) {
     return v;
 }
 
-template <bool TM, int FNT, int BROW>
+template <int FNT, int BROW>
 __device__ __forceinline__ void read_a(uint32_t buf, const LaneOffsets<FNT, BROW>& o, AFrags& f) {
     const lds_char* pa = (const lds_char*)(size_t)stage_addr(buf, o.a);
     const lds_char* pm = (const lds_char*)(size_t)stage_addr(buf, o.m);
 #pragma unroll
-    for (int i = 0; i < FM; i++) {
+    for (int i = 0; i < FM; i++)
         f.a[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(pa + i * 1024));
-        if constexpr (!TM) f.idx[i] = *reinterpret_cast<const __attribute__((address_space(3))) uint16_t*>(pm + i * 128);
-    }
-    if constexpr (TM) {
-        const u32x2 m0 = read_idx4(pm), m1 = read_idx4(pm + 512);
-        f.idx[0] = m0[0];
-        f.idx[1] = m0[1];
-        f.idx[2] = m1[0];
-        f.idx[3] = m1[1];
-    }
+    const u32x2 m0 = read_idx4(pm), m1 = read_idx4(pm + 512);
+    f.idx[0] = m0[0];
+    f.idx[1] = m0[1];
+    f.idx[2] = m1[0];
+    f.idx[3] = m1[1];
 }
 
 // B fragment j (16 columns x 64 k) of the stage in buffer `buf`: four transposing reads, or, token-
@@ -431,7 +425,7 @@ __device__ __forceinline__ void mfma_block(f32x4 (&acc)[FM][FNT], const AFrags& 
                                            const StageLoads& p, const Args& a, int wave, const LoadOffsets& lo) {
 #pragma unroll
     for (int i = 0; i < FM; i++) {
-        acc[i][j] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(f.a[i], b, acc[i][j], (int)f.idx[i], 0, 0);
+        acc[i][j] = smfmac_p(f, i, b, acc[i][j]);
 #pragma unroll
         for (int k = 0; k < N; k++)
             if ((k * R) / N == first + i) issue_load<BNT>(p, a, O0 + k, wave, lo);
@@ -485,17 +479,22 @@ __device__ __forceinline__ void stage(uint32_t l0, const Args& a, const TileDesc
     // next stage, so one A register set serves the whole pipeline
     const lds_char* pa = (const lds_char*)(size_t)stage_addr(nxt, o.a);
     const lds_char* pm = (const lds_char*)(size_t)stage_addr(nxt, o.m);
+    u32x2 m0, m1;  // the next stage's indices of fragments 0-3 and 4-7, read once this block has used the old ones
 #pragma unroll
     for (int i = 0; i < FM; i++) {
-        acc[i][F - 1] =
-            __builtin_amdgcn_smfmac_f32_16x16x64_bf16(f.a[i], rb[(F - 1) & 3], acc[i][F - 1], (int)f.idx[i], 0, 0);
+        acc[i][F - 1] = smfmac_p(f, i, rb[(F - 1) & 3], acc[i][F - 1]);
         f.a[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(pa + i * 1024));
-        f.idx[i] = *reinterpret_cast<const __attribute__((address_space(3))) uint16_t*>(pm + i * 128);
+        if (i == 3) m0 = read_idx4(pm);
+        if (i == FM - 1) m1 = read_idx4(pm + 512);
 #pragma unroll
         for (int k = 0; k < LI; k++)
             if ((k * 2 * FM) / LI == FM + i) issue_load<BNT>(np, a, k, wave, lo);
         __builtin_amdgcn_sched_barrier(0);
     }
+    f.idx[0] = m0[0];
+    f.idx[1] = m0[1];
+    f.idx[2] = m1[0];
+    f.idx[3] = m1[1];
 }
 
 // ---------------------------------------------------------------- epilogue
@@ -678,7 +677,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 
     AFrags fa;
     bf16x16 rb[4];
-    read_a<false>(l0, o, fa);
+    read_a(l0, o, fa);
     rb[0] = read_b<false>(l0, o, 0);
     rb[1] = read_b<false>(l0, o, 1);
     int g = 0;
@@ -812,7 +811,7 @@ __device__ __forceinline__ void tm_stage(uint32_t l0, uint32_t cur, uint32_t nxt
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < FM; i++)
-        acc[i][0] = smfmac_tm(f, i, rb[0], acc[i][0]);
+        acc[i][0] = smfmac_p(f, i, rb[0], acc[i][0]);
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of the stage are done
     wait_vmcnt<(NB - 2) * L>();          // the next stage has landed
@@ -822,7 +821,7 @@ __device__ __forceinline__ void tm_stage(uint32_t l0, uint32_t cur, uint32_t nxt
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < FM; i++) {
-        acc[i][1] = smfmac_tm(f, i, rb[1], acc[i][1]);
+        acc[i][1] = smfmac_p(f, i, rb[1], acc[i][1]);
         tm_loads_at<BN, 0>(i, cb, lt, soffA, soffMB, wave, tiles, ldx2, lo);
         __builtin_amdgcn_sched_barrier(0);
     }
@@ -830,7 +829,7 @@ __device__ __forceinline__ void tm_stage(uint32_t l0, uint32_t cur, uint32_t nxt
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < FM; i++) {
-        acc[i][2] = smfmac_tm(f, i, rb[2], acc[i][2]);
+        acc[i][2] = smfmac_p(f, i, rb[2], acc[i][2]);
         tm_loads_at<BN, 0>(FM + i, cb, lt, soffA, soffMB, wave, tiles, ldx2, lo);
         __builtin_amdgcn_sched_barrier(0);
     }
@@ -839,7 +838,7 @@ __device__ __forceinline__ void tm_stage(uint32_t l0, uint32_t cur, uint32_t nxt
     u32x2 m0, m1;  // the next stage's indices of fragments 0-3 and 4-7, read once this block has used the old ones
 #pragma unroll
     for (int i = 0; i < FM; i++) {
-        acc[i][3] = smfmac_tm(f, i, rb[3], acc[i][3]);
+        acc[i][3] = smfmac_p(f, i, rb[3], acc[i][3]);
         f.a[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(pa + i * 1024));
         if (i == 3) m0 = read_idx4(pm);
         if (i == FM - 1) m1 = read_idx4(pm + 512);
@@ -890,7 +889,7 @@ __global__ __launch_bounds__(64 * TmCfg<BN>::WAVES) __attribute__((amdgpu_waves_
     }
     AFrags fa;
     bf16x16 rb[4];
-    read_a<true>(l0, o, fa);
+    read_a(l0, o, fa);
     rb[0] = read_b<true>(l0, o, 0);
     rb[1] = read_b<true>(l0, o, 1);
     uint32_t cur = 0;
