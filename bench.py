@@ -75,7 +75,10 @@ class Kernel:
 
 
 def gemm_sources(N):
-    return ("gemm_bf16_tiled.hip", "sp24_device.h") if N >= TILED_MIN_N else ("gemm_bf16_skinny.hip", "sp24_device.h")
+    """Sources of the bf16 GEMM kernels that can run at N tokens (the library picks among them by shape)."""
+    if N >= TILED_MIN_N:
+        return ("gemm_bf16_tiled.hip", "sp24_device.h")
+    return ("gemm_bf16_fewtok.hip", "gemm_bf16_skinny.hip", "sp24_device.h")
 
 
 # ----------------------------------------------------------------------------- oracle timing helpers

@@ -1207,11 +1207,15 @@ static hipError_t launch_bn(const GemmArgs& g, hipStream_t s) {
 
 // Configuration of a bf16 launch, measured on MI355X (bit-identical results: the K order inside a tile does
 // not depend on the tile shape):
-//  - 256 x 128 tiles with two workgroups per CU fill the CUs better when there are fewer 256 x 256 tiles
+//  - from 32 stages (K >= 2048) 256 x 256 tiles, unless they would leave more than three quarters of the CUs
+//    idle: a workgroup of 256 x 128 alone on its CU runs its single wave per SIMD latency-bound, and two of
+//    them share the loads of a 256 x 256 tile less well (token-major, against the rule below: 28672 x 8192 x
+//    512 144.8 -> 128.0 us, 11008 x 4096 x 1024 58.0 -> 53.1, 3072 x 4096 x 6304 106.5 -> 100.3, 16384 x 8192
+//    x 512 113.7 -> 108.6, 768 x 3072 x 8192 32.9 either way; feature-major 28672 x 8192 x 512 146.2 -> 143.7);
+//  - below that, 256 x 128 tiles with two workgroups per CU fill the CUs better when there are fewer 256 x 256 tiles
 //    than CUs, and fill a partial last turn better: their last turn's tiles run one per CU, at about 0.6
 //    of a paired turn, while a full turn of 256 x 256 tiles costs about 0.92 of one (3072 x 768 x 6304
-//    token-major: 33.8 us against 37.0 with 256 x 256; 3072 x 4096 x 6304: 122 against 130; 768 x 3072 x
-//    8192: 42.9 against 48.4);
+//    token-major: 26.4 us against 30.8 with 256 x 256);
 //  - 256 x 256 tiles otherwise (a full first turn, or more than two turns): token-major with eight waves per
 //    workgroup, two per SIMD, so the big tile's re-use stays and a second wave covers each one's barrier
 //    and load waits (11008 x 4096 x 4096: 235.4 -> 212.2 us against four waves; 28672 x 8192 x 8192:
@@ -1225,6 +1229,9 @@ hipError_t launch_gemm_bf16_tiled(const GemmArgs& g, hipStream_t s) {
     const double c256 = 0.92 * (double)((t256 + cus - 1) / cus);
     const int64_t rem = t128 % (2 * cus);
     const double c128 = (double)(t128 / (2 * cus)) + (rem == 0 ? 0.0 : rem <= cus ? 0.6 : 1.0);
+    const int64_t stages = (g.K + tiled_bf16::BK - 1) / tiled_bf16::BK;
+    if (stages >= 32 && 4 * t256 >= cus)
+        return g.tm ? launch_bn<true, 256, 1>(g, s) : launch_bn<false, 256, 1>(g, s);
     if (t256 < cus || (t256 <= 2 * cus && c128 <= c256))
         return g.tm ? launch_bn<true, 128, 2>(g, s) : launch_bn<false, 128, 2>(g, s);
     return g.tm ? launch_bn<true, 256, 1>(g, s) : launch_bn<false, 256, 1>(g, s);
