@@ -166,11 +166,15 @@ I8_TM_SHAPES = [
     (96, 128, 33, 144, 100),
     # few-token int8 kernel with two row blocks per workgroup (more than 1024 row blocks, or more than 512
     # with two or more fragments) and an odd block count, so the last workgroup holds one block
-    (16400, 256, 1, 256, 16400),
+    (16400, 256, 1, 256, 16400),  # also the LDS-ring loop (one or two tokens from 1024 row blocks)
     (16400, 256, 20, 272, 16408),
     (16400, 256, 40, 256, 16400),
     (16400, 256, 64, 256, 16416),
     (8200, 256, 33, 256, 8200),
+    # the LDS-ring loop at 3-16 tokens below 1024 row blocks: four-wave workgroups from 512 blocks, odd counts
+    (8200, 256, 7, 272, 8200),
+    (10000, 384, 13, 384, 10008),
+    (6000, 256, 3, 256, 6000),
     (33, 128, 48, 128, 36),
     (2050, 640, 64, 640, 2056),
 ]
