@@ -269,11 +269,14 @@ bool gemm_bf16_fewtok_ok(const GemmArgs& g) {
 }
 
 // Waves per workgroup (S) and ring depth (D) by the number of 16-row blocks: enough workgroups that
-// all of them are resident at once, and as many LDS slots in flight per compute unit as that allows.
+// all of them are resident at once, and as many LDS slots in flight per compute unit as that allows. Above
+// 256 blocks the 4-wave workgroups (three per CU) keep every workgroup in one round; the 8-wave ones (one
+// per CU) would run a second round (cold caches: 6144 x 4096 at N = 1 / 4 / 8 9.1 / 9.9 / 10.6 -> 7.9 / 8.2 /
+// 8.9 us; 8000 x 4096 at N = 8 11.6 -> 9.3 us).
 hipError_t launch_gemm_bf16_fewtok(const GemmArgs& g, hipStream_t s) {
     const int64_t nb = (g.M + 15) / 16;
     if (g.N <= 2) {
-        if (nb >= 512) return fewtok::launch<4, 8, 2>(g, s);   // 48 KB per workgroup, three per CU
+        if (nb > 256) return fewtok::launch<4, 8, 2>(g, s);    // 48 KB per workgroup, three per CU
         if (nb >= 192) return fewtok::launch<8, 8, 2>(g, s);   // 96 KB
         return fewtok::launch<16, 6, 2>(g, s);                 // 144 KB
     }
@@ -283,7 +286,7 @@ hipError_t launch_gemm_bf16_fewtok(const GemmArgs& g, hipStream_t s) {
         if (nb >= 192) return fewtok::launch<8, 3, 16>(g, s);      // 78 KB
         return fewtok::launch<16, 2, 16>(g, s);                // 104 KB
     }
-    if (nb >= 512) return fewtok::launch<4, 5, 8>(g, s);       // 46 KB
+    if (nb > 256) return fewtok::launch<4, 5, 8>(g, s);        // 46 KB
     if (nb >= 192) return fewtok::launch<8, 5, 8>(g, s);       // 92 KB
     return fewtok::launch<16, 4, 8>(g, s);                     // 147 KB
 }

@@ -399,14 +399,13 @@ bool gemm_i8_fewtok_ok(const GemmArgs& g) {
 hipError_t launch_gemm_i8_fewtok(const GemmArgs& g, hipStream_t s) {
     const int64_t nb = (g.M + 15) / 16;
     const int nf = (int)((g.N + 15) / 16);
-    // the LDS ring: one or two tokens on weights of 1024 row blocks and more, 3 to 16 tokens below that
-    // (8 rotated copies: 28672 x 8192 at N = 1 28.0 -> 26.5 us; 11008 x 4096 at N = 8 / 12 / 16 8.0 / 8.5 /
-    // 9.4 -> 7.4 / 7.7 / 7.8 us; 4096 x 4096 at N = 16 5.3 -> 4.8 us; the register path stays faster for
-    // N = 1 below 1024 blocks, 11008 x 4096 6.8 against 7.3 us, and for N = 16 from 1024, 28672 x 8192 32.7
-    // against 35.4 us). Workgroups of 4 waves (three per CU) from 512 blocks, of 8 below.
-    if (g.N <= 2 && nb >= 1024) return fewtok_i8::launch_ring<4, 8, 2>(g, s);                   // 48 KB
-    if (g.N > 2 && g.N <= 8 && nb < 1024)
-        return nb >= 512 ? fewtok_i8::launch_ring<4, 5, 8>(g, s) : fewtok_i8::launch_ring<8, 5, 8>(g, s);    // 45 / 90 KB
+    // the LDS ring: one or two tokens on weights of 1024 row blocks and more, 9 to 16 tokens below that
+    // (24 rotated copies, beyond the Infinity Cache: 16400 x 4096 at N = 1 11.9 -> 11.0 us; 11008 x 4096 at
+    // N = 16 10.6 -> 9.9 us; 4096 x 4096 at N = 16 5.5 -> 4.9 us; 6144 x 4096 at N = 12 7.4 -> 7.2 us). The
+    // register loop stays for 3 to 8 tokens (11008 x 4096 at N = 3 / 4 / 6 / 8: 8.0 / 7.9 / 8.6 / 9.2 against
+    // 8.5 / 8.2 / 8.7 / 8.9 us), for N <= 2 below 1024 blocks and for N > 8 from 1024 (28672 x 8192 at N = 16:
+    // 32.7 against 35.4 us). Workgroups of 4 waves (three per CU) from 512 blocks, of 8 (two per CU) below.
+    if (g.N <= 2 && nb >= 1024) return fewtok_i8::launch_ring<4, 8, 2>(g, s);  // 48 KB
     if (g.N > 8 && g.N <= 16 && nb < 1024)
         return nb >= 512 ? fewtok_i8::launch_ring<4, 4, 16>(g, s) : fewtok_i8::launch_ring<8, 3, 16>(g, s);  // 52 / 78 KB
     const bool r1 = nb <= 512 || (nf == 1 && nb <= 1024);

@@ -37,7 +37,7 @@ SHAPES = [
     (150, 384, 40, "token"),   # few-token kernel: three fragments
     (520, 1152, 1000, "token"),
     (16400, 256, 20, "token"),  # few-token kernel, two row blocks per workgroup, odd block count (1025)
-    (8200, 256, 7, "token"),    # few-token LDS ring, four-wave workgroups (513 row blocks)
+    (8200, 256, 10, "token"),   # few-token LDS ring, four-wave workgroups (513 row blocks)
     (16400, 128, 2, "token"),   # few-token LDS ring for one or two tokens (1025 row blocks)
 ]
 

@@ -61,6 +61,7 @@ TM_SHAPES = [
     (16400, 240, 13, 248, 16400),
     (8200, 4096, 16, 4096, 8200),
     (6150, 320, 11, 320, 6150),
+    (6150, 320, 5, 328, 6150),  # 2-8 tokens, 4-wave ring workgroups above 256 row blocks, K tail
     (4000, 320, 12, 320, 4000),
     (3100, 256, 3, 264, 3100),
     (2050, 240, 9, 248, 2056),
@@ -171,10 +172,11 @@ I8_TM_SHAPES = [
     (16400, 256, 40, 256, 16400),
     (16400, 256, 64, 256, 16416),
     (8200, 256, 33, 256, 8200),
-    # the LDS-ring loop at 3-16 tokens below 1024 row blocks: four-wave workgroups from 512 blocks, odd counts
-    (8200, 256, 7, 272, 8200),
+    # the LDS-ring loop at 9-16 tokens below 1024 row blocks: four-wave workgroups from 512 blocks (odd count),
+    # eight-wave below
     (10000, 384, 13, 384, 10008),
-    (6000, 256, 3, 256, 6000),
+    (6000, 256, 11, 256, 6000),
+    (8200, 256, 7, 272, 8200),
     (33, 128, 48, 128, 36),
     (2050, 640, 64, 640, 2056),
 ]
