@@ -333,6 +333,26 @@ bool gemm_bf16_skinny_ok(const GemmArgs& g) {
 // more workgroups, R as large as that allows (each X fragment is then shared by more weight tiles);
 // the unit-vector case reads its X fragment cheaply and prefers more, smaller workgroups. Chosen by
 // measurement on MI355X over R in {1, 2, 4}, S in {4, 8, 16}, U in {1, 2, 4}.
+// Token-major X with 17 or more tokens (and 3-16 tokens from 1024 row blocks, where the LDS-ring kernel
+// is not used): measured again over R in {1, 2, 4, 8}, S in {4, 8, 16}, U in {1, 2} with weight copies
+// rotated beyond the Infinity Cache. There the best R is the smallest power of two that fits the grid in
+// one round of at most 256 workgroups: 28672 x 8192 at N = 64 / 32 / 16 85.8 / 63.7 / 50.2 -> 66.2 / 49.9 /
+// 45.4 us, 11008 x 4096 at N = 64 / 32 38.6 / 25.3 -> 25.3 / 16.8 us, 6144 x 4096 at N = 24 18.1 -> 11.2
+// us, 16384 x 4096 at N = 16 17.8 -> 16.1 us (that one-fragment grid fits two workgroups of 4 waves per CU).
+static hipError_t launch_skinny_tm(const GemmArgs& g, hipStream_t s, int64_t nb) {
+    if (g.N <= 16) return nb >= 1536 ? skinny::launch<1, 8, 8, 1>(g, s) : skinny::launch<1, 2, 4, 1>(g, s);
+    if (g.N <= 32) {
+        if (nb > 1024) return skinny::launch<2, 8, 8, 1>(g, s);
+        if (nb > 512) return skinny::launch<2, 4, 8, 1>(g, s);
+        if (nb > 256) return skinny::launch<2, 2, 8, 1>(g, s);
+        return nb >= 192 ? skinny::launch<2, 1, 8, 1>(g, s) : skinny::launch<2, 1, 16, 1>(g, s);
+    }
+    if (nb > 1024) return skinny::launch<4, 8, 4, 1>(g, s);
+    if (nb > 512) return skinny::launch<4, 4, 4, 1>(g, s);
+    if (nb > 256) return skinny::launch<4, 2, 8, 1>(g, s);
+    return skinny::launch<4, 1, 8, 1>(g, s);
+}
+
 hipError_t launch_gemm_bf16_skinny(const GemmArgs& g, hipStream_t s) {
     const int64_t nb = (g.M + 15) / 16;
     const bool vec1 = g.N == 1 && (g.tm || g.ldx == 1);  // one token: X is a contiguous K-vector
@@ -341,6 +361,7 @@ hipError_t launch_gemm_bf16_skinny(const GemmArgs& g, hipStream_t s) {
         if (nb >= 512) return skinny::launch<1, 2, 4, 2>(g, s);
         return skinny::launch<1, 1, 8, 4>(g, s);
     }
+    if (g.tm && (g.N > 16 || nb >= 1024)) return launch_skinny_tm(g, s, nb);
     if (g.N <= 16) {
         if (nb >= 512) return skinny::launch<1, 4, 16, 1>(g, s);
         return skinny::launch<1, 1, 16, 2>(g, s);

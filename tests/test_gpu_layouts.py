@@ -62,6 +62,17 @@ TM_SHAPES = [
     (8200, 4096, 16, 4096, 8200),
     (6150, 320, 11, 320, 6150),
     (6150, 320, 5, 328, 6150),  # 2-8 tokens, 4-wave ring workgroups above 256 row blocks, K tail
+    # the register-pipelined few-token kernel, token-major, one workgroup per grid slot at most 256 (R = the
+    # smallest power of two that fits): every configuration, ragged block counts, a K tail
+    (25000, 128, 12, 128, 25000),
+    (17000, 208, 16, 216, 17000),
+    (20000, 128, 30, 128, 20000),
+    (12000, 256, 20, 264, 12000),
+    (6000, 128, 24, 128, 6000),
+    (3500, 128, 17, 136, 3500),
+    (20000, 128, 40, 128, 20000),
+    (12000, 128, 64, 128, 12000),
+    (6000, 208, 48, 216, 6000),
     (4000, 320, 12, 320, 4000),
     (3100, 256, 3, 264, 3100),
     (2050, 240, 9, 248, 2056),
