@@ -382,20 +382,20 @@ static hipError_t launch_ring(const GemmArgs& g, hipStream_t s) {
 
 bool gemm_i8_fewtok_ok(const GemmArgs& g) {
     // raw int32 accumulators without a scale, every epilogue with one; 16-byte aligned rows of X in every
-    // batch entry; whole 128-column tiles; 32-bit byte offsets for X and for R = 4 row blocks' tiles
+    // batch entry; whole 128-column tiles; 32-bit byte offsets for X and for R = 8 row blocks' tiles
     const bool epi_ok = g.scale ? true : (g.out_kind == OUT_I32 && !g.bias && !g.gelu);
     const bool aligned = g.ldx % 16 == 0 && (reinterpret_cast<uintptr_t>(g.X) & 15) == 0 && (g.batch == 1 || g.sx % 16 == 0);
     return g.tm && epi_ok && aligned && g.N >= 1 && g.N <= 64 && g.K >= fewtok_i8::KT && g.K % fewtok_i8::KT == 0 &&
-           (g.N - 1) * g.ldx + g.K + 128 < ((int64_t)1 << 31) && 4 * (g.K / fewtok_i8::KT) * 1024 < ((int64_t)1 << 31);
+           (g.N - 1) * g.ldx + g.K + 128 < ((int64_t)1 << 31) && 8 * (g.K / fewtok_i8::KT) * 1024 < ((int64_t)1 << 31);
 }
 
-// Row blocks per workgroup (R), tiles per request round (U) and waves (S) by the number of 16-token
-// fragments, measured on MI355X (HIP graph replays, weight copies rotated beyond the Infinity Cache) over
-// R in {1, 2, 4, 8}, U in {1, 2, 4, 8}, S in {4, 8, 16}: U = 4, S = 8 up to two fragments and S = 4 beyond.
-// R = 2 where it still gives over 256 workgroups (4096 x 4096 / 11008 x 4096 / 28672 x 8192 at N = 64:
-// 12.8 / 21.5 / 69.6 us, against 12.1 / 27.7 / 69.6 with R = 1); R = 1 below that, and for one fragment
-// up to 1024 row blocks, where the wider grid keeps more requests in flight (N = 1: 5.4 / 8.4 / 28.4 us,
-// against 6.7 / 9.9 / 28.5 with R = 2).
+// Register loop: row blocks per workgroup (R), tiles per request round (U) and waves (S) by the number of 16-token
+// fragments and of row blocks, measured on MI355X with weight copies rotated beyond the Infinity Cache over
+// R in {1, 2, 4, 8}, U in {1, 2, 4}, S in {4, 8}. More row blocks per workgroup share each X fragment; the best
+// grid is about one round of workgroups (28672 x 8192 at N = 64 / 32: 69.4 / 43.8 -> 47.8 / 35.7 us with R = 4 /
+// 8; 11008 x 4096 at N = 64 / 32: 21.2 / 15.0 -> 18.2 / 12.4 us with R = 4; 6144 x 4096 at N = 64 19.4 -> 12.9
+// us with R = 2), and two tiles per round beat four at one fragment below 1024 blocks (11008 x 4096 at N = 8:
+// 8.9 -> 8.2 us; 4096 x 4096 at N = 8 5.0 -> 4.8 us).
 hipError_t launch_gemm_i8_fewtok(const GemmArgs& g, hipStream_t s) {
     const int64_t nb = (g.M + 15) / 16;
     const int nf = (int)((g.N + 15) / 16);
@@ -408,13 +408,27 @@ hipError_t launch_gemm_i8_fewtok(const GemmArgs& g, hipStream_t s) {
     if (g.N <= 2 && nb >= 1024) return fewtok_i8::launch_ring<4, 8, 2>(g, s);  // 48 KB
     if (g.N > 8 && g.N <= 16 && nb < 1024)
         return nb >= 512 ? fewtok_i8::launch_ring<4, 4, 16>(g, s) : fewtok_i8::launch_ring<8, 3, 16>(g, s);  // 52 / 78 KB
-    const bool r1 = nb <= 512 || (nf == 1 && nb <= 1024);
-    switch (nf) {
-    case 1: return r1 ? fewtok_i8::launch<1, 1, 4, 8>(g, s) : fewtok_i8::launch<1, 2, 4, 8>(g, s);
-    case 2: return r1 ? fewtok_i8::launch<2, 1, 4, 8>(g, s) : fewtok_i8::launch<2, 2, 4, 8>(g, s);
-    case 3: return r1 ? fewtok_i8::launch<3, 1, 4, 4>(g, s) : fewtok_i8::launch<3, 2, 4, 4>(g, s);
-    default: return r1 ? fewtok_i8::launch<4, 1, 4, 4>(g, s) : fewtok_i8::launch<4, 2, 4, 4>(g, s);
+    using namespace fewtok_i8;
+    if (nf == 1) {
+        if (nb >= 1024) return g.N > 8 ? launch<1, 8, 4, 8>(g, s) : launch<1, 2, 4, 8>(g, s);
+        return nb >= 512 ? launch<1, 1, 2, 4>(g, s) : launch<1, 1, 2, 8>(g, s);
     }
+    if (nf == 2) {
+        if (nb > 1024) return launch<2, 8, 2, 8>(g, s);
+        if (nb > 512) return launch<2, 4, 2, 4>(g, s);
+        if (nb > 256) return launch<2, 2, 2, 8>(g, s);
+        return launch<2, 1, 2, 4>(g, s);
+    }
+    if (nf == 3) {
+        if (nb > 1024) return launch<3, 4, 4, 4>(g, s);
+        if (nb > 512) return launch<3, 4, 2, 8>(g, s);
+        if (nb > 256) return launch<3, 2, 4, 4>(g, s);
+        return launch<3, 1, 2, 4>(g, s);
+    }
+    if (nb > 1024) return launch<4, 4, 4, 4>(g, s);
+    if (nb > 512) return launch<4, 4, 2, 8>(g, s);
+    if (nb > 256) return launch<4, 2, 4, 4>(g, s);
+    return launch<4, 1, 2, 4>(g, s);
 }
 
 }  // namespace sp24

@@ -188,6 +188,14 @@ I8_TM_SHAPES = [
     (10000, 384, 13, 384, 10008),
     (6000, 256, 11, 256, 6000),
     (8200, 256, 7, 272, 8200),
+    # the register loop's grid sizes: more row blocks per workgroup as the weight grows (ragged block counts)
+    (16400, 256, 12, 256, 16400),
+    (16400, 256, 5, 256, 16408),
+    (8200, 256, 24, 256, 8200),
+    (6000, 256, 30, 272, 6000),
+    (5000, 256, 36, 256, 5000),
+    (9000, 256, 64, 256, 9000),
+    (4500, 256, 50, 256, 4504),
     (33, 128, 48, 128, 36),
     (2050, 640, 64, 640, 2056),
 ]
