@@ -6,13 +6,12 @@
 // and the time is set by how many of those bytes are in flight: HBM latency under load is a couple of
 // microseconds, so a compute unit needs tens of KB outstanding. Here they wait in LDS, not in
 // registers:
-//  - a workgroup owns RB = 1 or 2 16-row blocks of the weight and all N tokens; its S waves split the
-//    blocks' K tiles (64 dense columns each) into S contiguous ranges;
-//  - each wave keeps a private ring of D units in LDS. A unit is one K tile: the RB 1 KB compressed value
-//    tiles (already in smfmac lane order), their 128-byte index tiles, and the X tile (XR = 2, 8 or 16 token
-//    rows x 128 bytes, 16-byte units of row n at unit ^ f(n) as in the tiled kernel's token-major B tile),
-//    each fetched with LDS-destination buffer loads, so no VGPRs hold data in flight. With RB = 2 the two
-//    blocks share the X tile: with 16 token rows X is otherwise twice the weight bytes of a unit;
+//  - a workgroup owns one 16-row block of the weight and all N tokens; its S waves split the block's
+//    K tiles (64 dense columns each) into S contiguous ranges;
+//  - each wave keeps a private ring of D units in LDS. A unit is one K tile: the 1 KB compressed value
+//    tile (already in smfmac lane order), its 128-byte index tile, and the X tile (XR = 2, 8 or 16 token
+//    rows x 128 bytes, 16-byte units of row n at unit ^ f(n) as in the tiled kernel's token-major B
+//    tile), each fetched with LDS-destination buffer loads, so no VGPRs hold data in flight;
 //  - the wave issues unit i + D - 1 into the slot that unit i - 1 has just left, waits (vmcnt) until
 //    unit i has landed, and multiplies it: D - 1 units stay in flight, every unit issues the same
 //    number of loads (units past the range are pushed out of the descriptor's range: zeros, no memory
@@ -20,7 +19,7 @@
 //  - token rows past N come back as zeros from the buffer range check (they only feed output columns
 //    that are never stored); a partial last K tile is multiplied outside the ring with its X elements
 //    read one by one, so nothing at k >= K (the next token's row, or row padding) is ever used;
-//  - at the end the S partial 16 x 16 accumulators of each block are summed through LDS in wave order
+//  - at the end the S partial 16 x 16 accumulators are summed through LDS in wave order
 //    (deterministic), rounded if the output is bf16, and stored into Y (N x M) with bounds checks.
 // A batch of products sharing the weight is grid dimension y.
 #include "sp24_device.h"
@@ -77,16 +76,14 @@ __device__ __forceinline__ int tm_swz(int n) { return ((n >> 1) & 7) ^ ((n & 1) 
 typedef __attribute__((address_space(3))) char lds_char;
 typedef const __attribute__((address_space(3))) u32x4 lds_u32x4;
 
-template <int S, int D, int XR, int RB>
+template <int S, int D, int XR>
 __global__ __launch_bounds__(64 * S) void gemm_bf16_fewtok(Args g) {
     static_assert(XR == 2 || XR == 8 || XR == 16, "X tile rows");
-    static_assert(RB == 1 || RB == 2, "row blocks per workgroup");
     constexpr int NXI = XR == 16 ? 2 : 1;           // X loads per unit (one dword load for 2 rows)
-    constexpr int XOFF = RB * 1024 + 256;           // value tiles, index tiles (one dword load), X tile
-    constexpr int UNIT = XOFF + 128 * XR;
+    constexpr int UNIT = 1024 + 256 + 128 * XR;     // value tile, index tile (128 B used), X tile
     constexpr int RING = D * UNIT;                  // per wave
-    constexpr int LPU = RB + 1 + NXI;               // loads per unit
-    constexpr int RED = S * RB * 256 * 4;
+    constexpr int LPU = 2 + NXI;                    // loads per unit
+    constexpr int RED = S * 256 * 4;
     static_assert((D - 1) * LPU < 64, "vmcnt range");
     __shared__ __attribute__((aligned(16))) char smem[S * RING > RED ? S * RING : RED];
     const uint32_t l0 = (uint32_t)(size_t)(__attribute__((address_space(3))) char*)smem;
@@ -94,24 +91,22 @@ __global__ __launch_bounds__(64 * S) void gemm_bf16_fewtok(Args g) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int r = lane & 15, q = lane >> 4;
     const int64_t M = g.M, K = g.K, N = g.N, ldx = g.ldx;
-    const int64_t b = (int64_t)blockIdx.x * RB;   // first row block
-    const int64_t nbl = ((M + 15) / 16 - b) < RB ? (M + 15) / 16 - b : RB;  // row blocks of this workgroup
+    const int64_t b = blockIdx.x;
     const uint16_t* const X = g.X + (int64_t)blockIdx.y * g.sxb;
     const int64_t T = (K + 63) / 64, Tf = K / 64;  // tiles per row block; full ones
     const int64_t t0 = T * wave / S, t1 = T * (wave + 1) / S;
     const int64_t tf = t1 < Tf ? t1 : Tf;         // the ring takes the full tiles [t0, tf)
     const int n = (int)(tf > t0 ? tf - t0 : 0);
 
-    const i32x4 rA = make_rsrc(g.vals + b * T * 1024, nbl * T * 1024);
-    const i32x4 rM = make_rsrc(g.meta + b * T * 128, nbl * T * 128);
+    const i32x4 rA = make_rsrc(g.vals + b * T * 1024, T * 1024);
+    const i32x4 rM = make_rsrc(g.meta + b * T * 128, T * 128);
     const i32x4 rX = make_rsrc(X, ((N - 1) * ldx + K) * 2);
-    // per-lane load offsets: value tile 16 * lane; index tiles 4 * (lane % 32) of the first block for lanes
-    // < 32 and of the second for the others (with one block the other half of the dword load is pushed out
-    // of range); X: 16-byte loads put lane i in row 8h + i / 8, unit
+    // per-lane load offsets: value tile 16 * lane; index tile 4 * lane for lanes < 32 (the other half
+    // of the dword load is pushed out of range); X: 16-byte loads put lane i in row 8h + i / 8, unit
     // slot i % 8, which holds unit (i % 8) ^ f(row); the dword load (XR = 2) puts lane i in row i / 32,
     // dword i % 32 of the row, i.e. dword i % 4 of unit slot (i % 32) / 4
     const uint32_t oA = 16u * (uint32_t)lane;
-    const uint32_t oM = lane < 32 ? 4u * (uint32_t)lane : (RB == 2 ? (uint32_t)(T * 128) + 4u * (uint32_t)(lane - 32) : 0x80000000u);
+    const uint32_t oM = lane < 32 ? 4u * (uint32_t)lane : 0x80000000u;
     uint32_t oX[NXI];
     if constexpr (XR == 2) {
         const int row = lane >> 5, slot = (lane & 31) >> 2;
@@ -130,25 +125,22 @@ __global__ __launch_bounds__(64 * S) void gemm_bf16_fewtok(Args g) {
     auto issue = [&](int i) {
         const uint32_t t = (uint32_t)(t0 + i), past = i < n ? 0u : 0x80000000u;
         const uint32_t slot = ring + (uint32_t)((i % D) * UNIT);
-#pragma unroll
-        for (int j = 0; j < RB; j++) dma16(slot + 1024 * j, (oA + (j * (uint32_t)T + t) * 1024u) | past, rA);
-        dma4(slot + RB * 1024, (oM + t * 128u) | past, rM);
+        dma16(slot, (oA + t * 1024u) | past, rA);
+        dma4(slot + 1024, (oM + t * 128u) | past, rM);
         if constexpr (XR == 2) {
-            dma4(slot + XOFF, (oX[0] + t * 128u) | past, rX);
+            dma4(slot + 1280, (oX[0] + t * 128u) | past, rX);
         } else {
 #pragma unroll
-            for (int h = 0; h < NXI; h++) dma16(slot + XOFF + 1024 * h, (oX[h] + t * 128u) | past, rX);
+            for (int h = 0; h < NXI; h++) dma16(slot + 1280 + 1024 * h, (oX[h] + t * 128u) | past, rX);
         }
     };
 
-    // lane (r, q) reads: value operand at 16 * lane, index at 2 * lane (block j: + 1024 j and + 128 j), X row r
-    // (rows past the tile's XR feed only output columns >= XR > N - 1, never stored: any row of the tile will do)
+    // lane (r, q) reads: value operand at 16 * lane, index at 2 * lane, X row r (rows past the tile's
+    // XR feed only output columns >= XR > N - 1, never stored: any row of the tile will do)
     const int xr = r & (XR - 1);
-    const int xo0 = XOFF + xr * 128 + 16 * (q ^ tm_swz(xr)), xo1 = XOFF + xr * 128 + 16 * ((q ^ tm_swz(xr)) ^ 4);
+    const int xo0 = 1280 + xr * 128 + 16 * (q ^ tm_swz(xr)), xo1 = 1280 + xr * 128 + 16 * ((q ^ tm_swz(xr)) ^ 4);
 
-    f32x4 acc[RB];
-#pragma unroll
-    for (int j = 0; j < RB; j++) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < D - 1; i++) issue(i);
     for (int i = 0; i < n; i++) {
@@ -156,16 +148,12 @@ __global__ __launch_bounds__(64 * S) void gemm_bf16_fewtok(Args g) {
         wait_vmcnt<(D - 1) * LPU>();  // unit i has landed
         asm volatile("" ::: "memory");  // and the reads of it stay below the wait
         const lds_char* p = (const lds_char*)(size_t)(ring + (uint32_t)((i % D) * UNIT));
+        const u32x4 av = *reinterpret_cast<lds_u32x4*>(p + 16 * lane);
+        const uint32_t idx = *reinterpret_cast<const __attribute__((address_space(3))) uint16_t*>(p + 1024 + 2 * lane);
         const u32x4 lo = *reinterpret_cast<lds_u32x4*>(p + xo0);
         const u32x4 hi = *reinterpret_cast<lds_u32x4*>(p + xo1);
         const bf16x16 bx = __builtin_bit_cast(bf16x16, u32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
-#pragma unroll
-        for (int j = 0; j < RB; j++) {
-            const u32x4 av = *reinterpret_cast<lds_u32x4*>(p + 1024 * j + 16 * lane);
-            const uint32_t idx =
-                *reinterpret_cast<const __attribute__((address_space(3))) uint16_t*>(p + RB * 1024 + 128 * j + 2 * lane);
-            acc[j] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, av), bx, acc[j], (int)idx, 0, 0);
-        }
+        acc = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, av), bx, acc, (int)idx, 0, 0);
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this unit's reads are done before its slot is refilled
     }
     wait_vmcnt<0>();  // every load (including the zero-filling ones) has landed before LDS is reused
@@ -173,6 +161,8 @@ __global__ __launch_bounds__(64 * S) void gemm_bf16_fewtok(Args g) {
     // the partial last K tile (K % 64 != 0): operands read directly, X elements at k >= K as zero
     if (t1 > tf && Tf < T) {
         const int64_t t = Tf;
+        const u32x4 av = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(g.vals + (b * T + t) * 1024) + lane);
+        const uint32_t idx = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(g.meta + (b * T + t) * 128) + lane);
         u32x8 bw = {0, 0, 0, 0, 0, 0, 0, 0};
         if (r < N) {
             const uint16_t* xrow = X + (int64_t)r * ldx;
@@ -184,33 +174,23 @@ __global__ __launch_bounds__(64 * S) void gemm_bf16_fewtok(Args g) {
                 bw[e >> 1] = v0 | (v1 << 16);
             }
         }
-#pragma unroll
-        for (int j = 0; j < RB; j++) {
-            if (j < nbl) {
-                const int64_t tb = (b + j) * T + t;
-                const u32x4 av = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(g.vals + tb * 1024) + lane);
-                const uint32_t idx = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(g.meta + tb * 128) + lane);
-                acc[j] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, av),
-                                                                   __builtin_bit_cast(bf16x16, bw), acc[j], (int)idx, 0, 0);
-            }
-        }
+        acc = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x16, bw),
+                                                        acc, (int)idx, 0, 0);
     }
 
-    // sum the S partial tiles in wave order: lane (r, q) holds column r, rows 4q .. 4q+3 of each block
+    // sum the S partial tiles in wave order: lane (r, q) holds column r, rows 4q .. 4q+3 of the block
     __syncthreads();  // every wave is done with its ring
     float* const red = reinterpret_cast<float*>(smem);
 #pragma unroll
-    for (int j = 0; j < RB; j++)
-#pragma unroll
-        for (int i = 0; i < 4; i++) red[(wave * RB + j) * 256 + (4 * q + i) * 16 + r] = acc[j][i];
+    for (int i = 0; i < 4; i++) red[wave * 256 + (4 * q + i) * 16 + r] = acc[i];
     __syncthreads();
     char* const Y = static_cast<char*>(g.Y) + (int64_t)blockIdx.y * g.syb * (g.out_fp32 ? 4 : 2);
-    for (int e = threadIdx.x; e < 256 * RB; e += 64 * S) {
+    for (int e = threadIdx.x; e < 256; e += 64 * S) {
         // consecutive threads take consecutive rows m of one token row of Y (N x M)
-        const int row = e % (16 * RB), col = e / (16 * RB), j = row >> 4;
+        const int row = e % 16, col = e / 16;
         float s = 0.f;
 #pragma unroll
-        for (int w = 0; w < S; w++) s += red[(w * RB + j) * 256 + (row & 15) * 16 + col];
+        for (int w = 0; w < S; w++) s += red[w * 256 + row * 16 + col];
         const int64_t m = b * 16 + row;
         if (m < M && col < N) {
             const int64_t o = (int64_t)col * g.ldy + m;
@@ -222,7 +202,7 @@ __global__ __launch_bounds__(64 * S) void gemm_bf16_fewtok(Args g) {
     }
 }
 
-template <int S, int D, int XR, int RB = 1>
+template <int S, int D, int XR>
 hipError_t launch(const GemmArgs& g, hipStream_t s) {
     Args a;
     a.vals = static_cast<const uint8_t*>(g.values);
@@ -233,13 +213,13 @@ hipError_t launch(const GemmArgs& g, hipStream_t s) {
     a.Y = g.Y;
     a.ldy = g.ldy; a.syb = g.sy;
     a.out_fp32 = g.out_fp32;
-    const unsigned grid = (unsigned)(((g.M + 15) / 16 + RB - 1) / RB);
+    const unsigned grid = (unsigned)((g.M + 15) / 16);
     for (int64_t b0 = 0; b0 < g.batch; b0 += 65535) {
         const unsigned gb = (unsigned)(g.batch - b0 < 65535 ? g.batch - b0 : 65535);
         Args e = a;
         e.X = a.X + b0 * a.sxb;
         e.Y = static_cast<char*>(a.Y) + b0 * a.syb * (g.out_fp32 ? 4 : 2);
-        hipLaunchKernelGGL((gemm_bf16_fewtok<S, D, XR, RB>), dim3(grid, gb), dim3(64 * S), 0, s, e);
+        hipLaunchKernelGGL((gemm_bf16_fewtok<S, D, XR>), dim3(grid, gb), dim3(64 * S), 0, s, e);
         const hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
@@ -249,21 +229,19 @@ hipError_t launch(const GemmArgs& g, hipStream_t s) {
 }  // namespace fewtok
 
 // Where this kernel is used: measured against the register-pipelined few-token kernel on MI355X (HIP
-// graph replays, weight copies rotated beyond the Infinity Cache), it is faster for N <= 2 (28672 x 8192
-// at N = 1: 44.9 against 48.7 us) and for N <= 8 on weights of fewer than 1024 row blocks (11008 x 4096 at
-// N = 8: 12.2 against 14.1 us). With 16-row X tiles (9 to 16 tokens) and one row block per unit the ring
-// holds fewer weight bytes; two row blocks per unit (RB = 2) halve the X bytes per weight byte and are
-// faster from 384 to 1023 row blocks (16 tokens, 16 rotated copies: 11008 x 4096 15.7 -> 15.0 us, 8192 x
-// 4096 13.4 -> 9.5 us, 6144 x 4096 10.9 -> 9.6 us; 12 tokens on 11008 x 4096 15.0 -> 14.2 us); from 1024
-// row blocks the register-pipelined kernel stays faster (28672 x 8192 at N = 16: 51.4 against 54.8 us), and
-// below 384 one row block per unit keeps more workgroups (4096 x 4096 at N = 16: 7.0 against 8.8 us).
+// graph replays, weight copies rotated beyond the Infinity Cache): for N <= 2 (28672 x 8192 at N = 1: 44.9
+// against 48.7 us), for N <= 8 below 1024 row blocks (11008 x 4096 at N = 8: 12.2 against 14.1 us), and for
+// 9 to 16 tokens below 384 row blocks (4096 x 4096 at N = 9 / 12 / 16: 7.0 / 6.9 / 7.1 against 7.6 / 7.2 /
+// 7.9 us). With 16-row X tiles a unit carries twice the X bytes of its weight bytes, and above 384 blocks the
+// register kernel, whose workgroups share each X fragment among up to 8 row blocks, is faster (11008 x 4096 at
+// N = 16: 13.9 against 14.7 us; 8192 x 4096: 9.8 against 10.1 us).
 bool gemm_bf16_fewtok_ok(const GemmArgs& g) {
     // token-major, rows of X 16-byte aligned in every batch entry; 32-bit load offsets below bit 31
-    // (which marks the loads past a wave's range): 16 X rows plus K, the value tiles of two row blocks
-    // (32 K bytes)
+    // (which marks the loads past a wave's range): 16 X rows plus K, the value tiles of one row block
+    // (16 K bytes)
     const bool aligned = g.ldx % 8 == 0 && (reinterpret_cast<uintptr_t>(g.X) & 15) == 0 && (g.batch == 1 || g.sx % 8 == 0);
     const int64_t nb = (g.M + 15) / 16;
-    const bool pays = g.N <= 2 || (g.N <= 16 && nb < 1024);
+    const bool pays = g.N <= 2 || (g.N <= 8 && nb < 1024) || (g.N <= 16 && nb < 384);
     return g.tm && g.N >= 1 && pays && aligned && (16 * g.ldx + g.K) * 2 < ((int64_t)1 << 31) &&
            g.K < ((int64_t)1 << 26) && nb < ((int64_t)1 << 31);
 }
@@ -280,10 +258,8 @@ hipError_t launch_gemm_bf16_fewtok(const GemmArgs& g, hipStream_t s) {
         if (nb >= 192) return fewtok::launch<8, 8, 2>(g, s);   // 96 KB
         return fewtok::launch<16, 6, 2>(g, s);                 // 144 KB
     }
-    if (g.N > 8) {  // 16 token rows per unit; two row blocks share it once that still leaves ~192 workgroups
-        if (nb >= 512) return fewtok::launch<4, 4, 16, 2>(g, s);   // 68 KB, two per CU
-        if (nb >= 384) return fewtok::launch<8, 3, 16, 2>(g, s);   // 102 KB
-        if (nb >= 192) return fewtok::launch<8, 3, 16>(g, s);      // 78 KB
+    if (g.N > 8) {  // 16 token rows per unit, below 384 row blocks
+        if (nb >= 192) return fewtok::launch<8, 3, 16>(g, s);  // 78 KB
         return fewtok::launch<16, 2, 16>(g, s);                // 104 KB
     }
     if (nb > 256) return fewtok::launch<4, 5, 8>(g, s);        // 46 KB

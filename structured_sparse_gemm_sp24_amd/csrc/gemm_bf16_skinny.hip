@@ -338,9 +338,15 @@ bool gemm_bf16_skinny_ok(const GemmArgs& g) {
 // rotated beyond the Infinity Cache. There the best R is the smallest power of two that fits the grid in
 // one round of at most 256 workgroups: 28672 x 8192 at N = 64 / 32 / 16 85.8 / 63.7 / 50.2 -> 66.2 / 49.9 /
 // 45.4 us, 11008 x 4096 at N = 64 / 32 38.6 / 25.3 -> 25.3 / 16.8 us, 6144 x 4096 at N = 24 18.1 -> 11.2
-// us, 16384 x 4096 at N = 16 17.8 -> 16.1 us (that one-fragment grid fits two workgroups of 4 waves per CU).
+// us, 16384 x 4096 at N = 16 17.8 -> 16.1 us (that one-fragment grid fits two workgroups of 4 waves per CU);
+// from 384 row blocks also 9-16 tokens (11008 x 4096 at N = 16: 13.9 us, 8192 x 4096: 9.8 us, against 14.7 and
+// 10.1 us in the LDS-ring kernel's two-block units).
 static hipError_t launch_skinny_tm(const GemmArgs& g, hipStream_t s, int64_t nb) {
-    if (g.N <= 16) return nb >= 1536 ? skinny::launch<1, 8, 8, 1>(g, s) : skinny::launch<1, 2, 4, 1>(g, s);
+    if (g.N <= 16) {
+        if (nb > 1536) return skinny::launch<1, 8, 8, 1>(g, s);
+        if (nb >= 1024) return skinny::launch<1, 2, 4, 1>(g, s);
+        return nb > 512 ? skinny::launch<1, 4, 4, 2>(g, s) : skinny::launch<1, 2, 8, 2>(g, s);
+    }
     if (g.N <= 32) {
         if (nb > 1024) return skinny::launch<2, 8, 8, 1>(g, s);
         if (nb > 512) return skinny::launch<2, 4, 8, 1>(g, s);
@@ -361,7 +367,7 @@ hipError_t launch_gemm_bf16_skinny(const GemmArgs& g, hipStream_t s) {
         if (nb >= 512) return skinny::launch<1, 2, 4, 2>(g, s);
         return skinny::launch<1, 1, 8, 4>(g, s);
     }
-    if (g.tm && (g.N > 16 || nb >= 1024)) return launch_skinny_tm(g, s, nb);
+    if (g.tm && (g.N > 16 || nb >= 384)) return launch_skinny_tm(g, s, nb);
     if (g.N <= 16) {
         if (nb >= 512) return skinny::launch<1, 4, 16, 1>(g, s);
         return skinny::launch<1, 1, 16, 2>(g, s);

@@ -56,8 +56,8 @@ TM_SHAPES = [
     # 16-byte rows): 4, 8 and 16 waves, 2- and 8-row X tiles, K tails (80, 208, 240), one K tile per
     # wave or several; and N = 9 .. 16 on the register-pipelined kernel
     (9000, 192, 16, 200, 9000),
-    # few-token units of two row blocks sharing one X tile (9 to 16 tokens, 512 row blocks and more): odd
-    # block counts (a last workgroup with one block), a K tail, both ring configurations
+    # 9 to 16 tokens from 384 row blocks (the register kernel with 2, 4 or 8 row blocks per workgroup): odd
+    # block counts (a last workgroup with fewer blocks), a K tail
     (16400, 240, 13, 248, 16400),
     (8200, 4096, 16, 4096, 8200),
     (6150, 320, 11, 320, 6150),
