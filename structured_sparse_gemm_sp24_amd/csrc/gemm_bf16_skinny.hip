@@ -340,7 +340,7 @@ bool gemm_bf16_skinny_ok(const GemmArgs& g) {
 // 45.4 us, 11008 x 4096 at N = 64 / 32 38.6 / 25.3 -> 25.3 / 16.8 us, 6144 x 4096 at N = 24 18.1 -> 11.2
 // us, 16384 x 4096 at N = 16 17.8 -> 16.1 us (that one-fragment grid fits two workgroups of 4 waves per CU);
 // from 384 row blocks also 9-16 tokens (11008 x 4096 at N = 16: 13.9 us, 8192 x 4096: 9.8 us, against 14.7 and
-// 10.1 us in the LDS-ring kernel's two-block units).
+// 10.1 us for LDS-ring units that carried two row blocks each).
 static hipError_t launch_skinny_tm(const GemmArgs& g, hipStream_t s, int64_t nb) {
     if (g.N <= 16) {
         if (nb > 1536) return skinny::launch<1, 8, 8, 1>(g, s);
