@@ -22,10 +22,11 @@
 // Loads are buffer loads with LDS destination whose whole byte offset is in the range-checked VGPR
 // operand: reads past this workgroup's row blocks, past K and past the end of X return zeros, and the
 // loads the pipeline issues past the workgroup's last tile are pushed out of range on purpose.
-// Persistent like the bf16 kernel: one workgroup per CU walks its tiles (neighbouring tiles on the same
-// XCD at the same time, groups of 8 tile-rows) with the LDS pipeline continued across tiles; the
-// epilogue dequantizes in registers, transposes 4 x 4 blocks inside lane quads by DPP and stores 16
-// bytes per lane, so its stores drain while the next tile computes.
+// Persistent like the bf16 kernel: one workgroup per CU (two for token-major 128-wide tiles, see Cfg)
+// walks its tiles (neighbouring tiles on the same XCD at the same time, groups of 8 tile-rows) with the
+// LDS pipeline continued across tiles; the epilogue dequantizes in registers, transposes 4 x 4 blocks
+// inside lane quads by DPP and stores 16 bytes per lane, so its stores drain while the next tile
+// computes.
 //
 // Token-major X (N x K) and Y (N x M): the B tile is 256 token rows x 128 k (128 B per row), a lane's
 // operand two 16-byte runs of its token's row (k = 16q .. +15 and 64 + 16q .. +15), read with two
@@ -50,15 +51,20 @@ constexpr uint32_t RSRC_FLAGS = 0x00020000u;
 
 // Tile width BN: 256 (waves of 128 x 128, three 52 KB stage buffers), or 128 (waves of 128 x 64, four
 // 36 KB buffers), chosen per launch (tiled_tile_width). A feature-major B tile row is BN bytes.
-template <int BN_>
+// PAIR (token-major, BN = 128 only): two workgroups per compute unit, each with two stage buffers and
+// at most 256 registers per lane, so that one workgroup's epilogue (VALU work and the tile's store burst)
+// runs beside the other's main loop instead of leaving the matrix cores idle.
+template <int BN_, bool PAIR_ = false>
 struct Cfg {
     static constexpr int BN = BN_, WN = BN_ / 2, FN = WN / 16;
+    static constexpr bool PAIR = PAIR_;
     static constexpr int B_BYTES = BK * BN;  // token-major: BN rows x 128 B; feature-major: 128 rows x BN B
     static constexpr int STAGE_BYTES = A_BYTES + META_BYTES + B_BYTES;
-    static constexpr int NBUF = BN == 256 ? 3 : 4;
+    static constexpr int NBUF = PAIR ? 2 : (BN == 256 ? 3 : 4);
     static constexpr int B_LOADS = BN / 32;  // per wave
     static constexpr int LOADS_PER_STAGE = 4 + 1 + B_LOADS;  // per wave: A, metadata, B
-    static_assert(NBUF * STAGE_BYTES <= 160 * 1024, "the stage buffers fit in LDS");
+    static_assert(!PAIR || BN == 128, "two workgroups per compute unit only with 128-wide tiles");
+    static_assert((PAIR ? 2 : 1) * NBUF * STAGE_BYTES <= 160 * 1024, "the stage buffers fit in LDS");
 };
 
 // Raw buffer descriptor over `bytes` bytes rounded up to whole dwords: the range check returns a
@@ -186,19 +192,27 @@ __device__ __forceinline__ LoadOffsets load_offsets(const Args& a, int lane, int
 
 // This wave's share of the loads of stage s of tile td into the buffer at LDS address `lds`. When td
 // is not valid the offsets get bit 31 set (beyond every record count): zeros, no memory traffic.
+// The descriptor in scalar registers (the loads take it there): a no-op where the compiler already holds
+// it there, a readfirstlane per word where register pressure made it keep the uniform words in VGPRs.
+__device__ __forceinline__ i32x4 uniform_rsrc(const i32x4& r) {
+    return i32x4{__builtin_amdgcn_readfirstlane(r[0]), __builtin_amdgcn_readfirstlane(r[1]),
+                 __builtin_amdgcn_readfirstlane(r[2]), __builtin_amdgcn_readfirstlane(r[3])};
+}
+
 template <bool TM, int BNT>
 __device__ __forceinline__ void load_stage(uint32_t lds, const Args& a, const TileDesc& td, int s, int wave,
                                            const LoadOffsets& lo) {
     const int64_t k0 = (int64_t)s * BK;
     const int tiles = (int)((a.K + BK - 1) / BK);
     const uint32_t past = td.valid ? 0u : 0x80000000u;
+    const i32x4 rA = uniform_rsrc(td.rA), rM = uniform_rsrc(td.rM);
 #pragma unroll
     for (int j = 0; j < 4; j++) {
         const int b = 4 * wave + j;
-        dma16(lds + b * 1024, lo.a + (((uint32_t)(b * tiles + s) * 1024u) | past), td.rA);
+        dma16(lds + b * 1024, lo.a + (((uint32_t)(b * tiles + s) * 1024u) | past), rA);
     }
     // metadata of blocks 4 wave .. 4 wave + 3 (one 256 B tile each) in one instruction
-    dma16(lds + A_BYTES + 4 * wave * 256, lo.m + (((uint32_t)(4 * wave * tiles + s) * 256u) | past), td.rM);
+    dma16(lds + A_BYTES + 4 * wave * 256, lo.m + (((uint32_t)(4 * wave * tiles + s) * 256u) | past), rM);
     if constexpr (TM) {
         // token rows BNT/4 * wave .. +BNT/4-1 of the tile, 8 per load; X's extent from the wave's first
         // row: rows past N read zeros (K is a multiple of 128: no stage reaches past K)
@@ -340,12 +354,14 @@ __device__ __forceinline__ void mfma_block(i32x4 (&acc)[FM][FNT], const AFrags& 
 // One K stage: stage s of the current tile, the workgroup's g-th stage (selects the buffer). B
 // fragments are read two blocks ahead (ring of 4); before the last two blocks the barrier publishes
 // stage g+1 and the loads of stage s+NBUF of this tile (or s+NBUF-S of the next) go into this buffer; the
-// next stage's A fragments are reloaded one by one inside the last block. No branches.
-template <bool TM, int BNT>
+// next stage's A fragments are reloaded one by one inside the last block. No branches. NEXT = false
+// (a tile's last stage with two workgroups per compute unit) leaves the next stage's operands unread,
+// so they do not occupy registers through the epilogue; the kernel reads them after it.
+template <bool TM, int BNT, bool PAIR, bool NEXT>
 __device__ __forceinline__ void stage(uint32_t l0, const Args& a, const TileDesc& cur_t, const TileDesc& next_t, int s,
                                       int S, int g, i32x4 (&acc)[FM][Cfg<BNT>::FN], AFrags& f, i32x8 (&rb)[4],
                                       const LaneOffsets<Cfg<BNT>::FN>& o, int wave, const LoadOffsets& lo) {
-    using C = Cfg<BNT>;
+    using C = Cfg<BNT, PAIR>;
     constexpr int F = C::FN, NB = C::NBUF;
     const int cb = g % NB;
     const uint32_t cur = l0 + cb * C::STAGE_BYTES;
@@ -362,6 +378,11 @@ __device__ __forceinline__ void stage(uint32_t l0, const Args& a, const TileDesc
     __builtin_amdgcn_s_barrier();
     const bool here = s + NB < S;
     load_stage<TM, BNT>(cur, a, here ? cur_t : next_t, here ? s + NB : s + NB - S, wave, lo);
+    if constexpr (!NEXT) {
+        mfma_block(acc, f, rb[(F - 2) & 3], F - 2);
+        mfma_block(acc, f, rb[(F - 1) & 3], F - 1);
+        return;
+    }
     rb[0] = read_b<TM>(nxt, o, 0);
     rb[1] = read_b<TM>(nxt, o, 1);
     __builtin_amdgcn_sched_barrier(0);
@@ -555,9 +576,10 @@ __device__ __forceinline__ void store_tile_tm(const i32x4 (&acc)[FM][FNT], const
     }
 }
 
-template <int OUT, bool TM, int EPI, int BNT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_i8_tiled_kernel(Args a) {
-    using C = Cfg<BNT>;
+template <int OUT, bool TM, int EPI, int BNT, bool PAIR>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PAIR ? 2 : 1, PAIR ? 2 : 1)))
+void gemm_i8_tiled_kernel(Args a) {
+    using C = Cfg<BNT, PAIR>;
     constexpr int NB = C::NBUF, F = C::FN;
     __shared__ __attribute__((aligned(16))) char smem[NB * C::STAGE_BYTES];
     const uint32_t l0 = (uint32_t)(size_t)(__attribute__((address_space(3))) char*)smem;
@@ -597,7 +619,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     rb[1] = read_b<TM>(l0, o, 1);
     int g = 0;
     for (int k = 1;; k++) {
-        for (int s = 0; s < S; s++, g++) stage<TM, BNT>(l0, a, cur_t, next_t, s, S, g, acc, fa, rb, o, wave, lo);
+        if constexpr (PAIR) {
+            for (int s = 0; s < S - 1; s++, g++)
+                stage<TM, BNT, PAIR, true>(l0, a, cur_t, next_t, s, S, g, acc, fa, rb, o, wave, lo);
+            stage<TM, BNT, PAIR, false>(l0, a, cur_t, next_t, S - 1, S, g, acc, fa, rb, o, wave, lo);
+            g++;
+        } else {
+            for (int s = 0; s < S; s++, g++)
+                stage<TM, BNT, PAIR, true>(l0, a, cur_t, next_t, s, S, g, acc, fa, rb, o, wave, lo);
+        }
         {
             const int64_t mw = cur_t.m0 + wm0, nw = cur_t.n0 + wn0;
             const bool full = (mw + WM <= a.M) && (nw + C::WN <= a.N) && a.y_vec;
@@ -620,19 +650,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             for (int j = 0; j < F; j++) acc[i][j] = i32x4{0, 0, 0, 0};
         cur_t = next_t;
         next_t = tile_desc<BNT>(a, tile_of(a, p, k + 1));
+        if constexpr (PAIR) {
+            // the next tile's first stage landed before the last stage's barrier, and its buffer is
+            // refilled only after the next barrier
+            const uint32_t buf = l0 + (g % NB) * C::STAGE_BYTES;
+            read_a(buf, o, fa);
+            rb[0] = read_b<TM>(buf, o, 0);
+            rb[1] = read_b<TM>(buf, o, 1);
+        }
     }
     wait_vmcnt<0>();  // the zero-filling loads past the last tile have landed before the workgroup ends
 }
 
-template <int OUT, bool TMV, int BNT>
+template <int OUT, bool TMV, int BNT, bool PAIR>
 void launch_epi(int epi, dim3 grid, dim3 block, hipStream_t s, const Args& a) {
     switch (epi) {
-    case 0: hipLaunchKernelGGL((gemm_i8_tiled_kernel<OUT, TMV, 0, BNT>), grid, block, 0, s, a); break;
-    case 1: if constexpr (OUT != OUT_I32) hipLaunchKernelGGL((gemm_i8_tiled_kernel<OUT, TMV, 1, BNT>), grid, block, 0, s, a); break;
-    case 2: if constexpr (OUT != OUT_I32) hipLaunchKernelGGL((gemm_i8_tiled_kernel<OUT, TMV, 2, BNT>), grid, block, 0, s, a); break;
-    default: if constexpr (OUT != OUT_I32) hipLaunchKernelGGL((gemm_i8_tiled_kernel<OUT, TMV, 3, BNT>), grid, block, 0, s, a); break;
+    case 0: hipLaunchKernelGGL((gemm_i8_tiled_kernel<OUT, TMV, 0, BNT, PAIR>), grid, block, 0, s, a); break;
+    case 1: if constexpr (OUT != OUT_I32) hipLaunchKernelGGL((gemm_i8_tiled_kernel<OUT, TMV, 1, BNT, PAIR>), grid, block, 0, s, a); break;
+    case 2: if constexpr (OUT != OUT_I32) hipLaunchKernelGGL((gemm_i8_tiled_kernel<OUT, TMV, 2, BNT, PAIR>), grid, block, 0, s, a); break;
+    default: if constexpr (OUT != OUT_I32) hipLaunchKernelGGL((gemm_i8_tiled_kernel<OUT, TMV, 3, BNT, PAIR>), grid, block, 0, s, a); break;
     }
 }
+
+// Whether a token-major launch of T 128-wide tiles of S stages runs two workgroups per compute unit.
+inline bool tiled_i8_pair(int T, int S, int cus) { return T > cus && S >= 2; }
 
 // Launch for one output kind and tile width (instantiated in gemm_i8_tiled*.hip, one output kind per
 // file so they compile in parallel): grid, arguments, and the layout x epilogue variant.
@@ -656,21 +697,35 @@ hipError_t launch_bn(const GemmArgs& g, hipStream_t s) {
     const int T = a.tilesM * a.tilesN * a.batch;
     const int S = (int)((g.K + BK - 1) / BK);
     const int cus = device_cus();
-    // one workgroup per compute unit walking several tiles; one tile each when a tile has fewer stages
-    // than there are stage buffers (the cross-tile pipeline then has nothing to overlap)
-    const dim3 grid((unsigned)(S >= C::NBUF && T > cus ? cus : T)), block(256);
     // the epilogue variant (bias, GELU) is a compile-time choice: GELU, and even a per-element bias
     // select, would otherwise cost every epilogue
     const int epi = OUT == OUT_I32 ? 0 : ((g.bias ? 1 : 0) | (g.gelu ? 2 : 0));
+    const dim3 block(256);
+    if constexpr (BNT == 128) {
+        // two workgroups per compute unit when every one of them gets a tile and each has its two stages
+        if (g.tm && tiled_i8_pair(T, S, cus)) {
+            launch_epi<OUT, true, BNT, true>(epi, dim3((unsigned)(T > 2 * cus ? 2 * cus : T)), block, s, a);
+            return hipGetLastError();
+        }
+    }
+    // one workgroup per compute unit walking several tiles; one tile each when a tile has fewer stages
+    // than there are stage buffers (the cross-tile pipeline then has nothing to overlap)
+    const dim3 grid((unsigned)(S >= C::NBUF && T > cus ? cus : T));
     if (g.tm)
-        launch_epi<OUT, true, BNT>(epi, grid, block, s, a);
+        launch_epi<OUT, true, BNT, false>(epi, grid, block, s, a);
     else
-        launch_epi<OUT, false, BNT>(epi, grid, block, s, a);
+        launch_epi<OUT, false, BNT, false>(epi, grid, block, s, a);
     return hipGetLastError();
 }
 
+// Tile width: token-major products with at least two 128-wide tiles per compute unit take them, two
+// workgroups per compute unit (faster than 256-wide tiles on every such shape measured: 4096^3 52.4 ->
+// 49.7 us, 11008 x 4096 x 4096 146.5 -> 142.5, 3072 x 768 x 16384 58.9 -> 52.8, 8192^3 352 -> 349.5);
+// the rest follow the turn-cost rule shared with the bf16 kernel.
 template <int OUT>
 hipError_t launch_out(const GemmArgs& g, hipStream_t s) {
+    const int64_t t128 = ((g.M + BM - 1) / BM) * ((g.N + 127) / 128) * g.batch;
+    if (g.tm && t128 >= 2 * (int64_t)device_cus() && g.K > BK) return launch_bn<OUT, 128>(g, s);
     return tiled_tile_width(g) == 128 ? launch_bn<OUT, 128>(g, s) : launch_bn<OUT, 256>(g, s);
 }
 

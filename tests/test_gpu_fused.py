@@ -39,6 +39,7 @@ SHAPES = [
     (16400, 256, 20, "token"),  # few-token kernel, two row blocks per workgroup, odd block count (1025)
     (8200, 256, 10, "token"),   # few-token LDS ring, four-wave workgroups (513 row blocks)
     (16400, 128, 2, "token"),   # few-token LDS ring for one or two tokens (1025 row blocks)
+    (2300, 256, 8200, "token"),  # 128-wide tiles, two workgroups per compute unit (585 tiles, ragged)
 ]
 
 

@@ -198,6 +198,10 @@ I8_TM_SHAPES = [
     (4500, 256, 50, 256, 4504),
     (33, 128, 48, 128, 36),
     (2050, 640, 64, 640, 2056),
+    # 128-wide tiles with two workgroups per compute unit (token-major, more tiles than compute units):
+    # 585 tiles over 512 workgroups, two stages per tile; 645 tiles, three stages; ragged M and N
+    (2300, 256, 8200, 272, 2312),
+    (1100, 384, 16500, 384, 1104),
 ]
 
 
@@ -223,7 +227,8 @@ def test_gemm_i8_token_major(M, K, N, ldx, ldy):
 
 
 @pytest.mark.parametrize("B,M,K,N,layout", [(3, 64, 256, 100, "feature"), (2, 96, 384, 80, "token"),
-                                            (2, 40, 48, 30, "feature"), (3, 200, 256, 12, "token")])
+                                            (2, 40, 48, 30, "feature"), (3, 200, 256, 12, "token"),
+                                            (2, 1100, 256, 8200, "token")])  # two workgroups per compute unit
 def test_gemm_i8_batched(B, M, K, N, layout):
     rng = np.random.default_rng(B * M + K + N)
     W = rng.integers(-128, 128, size=(M, K), dtype=np.int8)
