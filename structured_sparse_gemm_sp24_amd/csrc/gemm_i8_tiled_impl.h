@@ -460,8 +460,7 @@ __device__ __forceinline__ void to_out(const i32x4& c, const float (&sc)[4], con
             w[0] = pack_bf16x2_rne(y[0], y[1]);
             w[1] = pack_bf16x2_rne(y[2], y[3]);
         } else {
-            w[0] = quant_i8(y[0], a.inv_scale) | (quant_i8(y[1], a.inv_scale) << 8) |
-                   (quant_i8(y[2], a.inv_scale) << 16) | (quant_i8(y[3], a.inv_scale) << 24);
+            w[0] = quant_i8x4(y, a.inv_scale);
         }
     }
 }

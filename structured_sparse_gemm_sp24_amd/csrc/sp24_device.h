@@ -172,10 +172,30 @@ __device__ __forceinline__ float i8_value(int acc, float sc, float bias, bool ha
 }
 
 // Requantization to int8: clamp(rne(fl32(y * inv_scale)), -127, 127), as the low byte; inv_scale is
-// fl32(1 / out_scale), computed once on the host.
+// fl32(1 / out_scale), computed once on the host. Computed as fl32(t + B) with B = 1.5 * 2^23, clamped to
+// [B - 127, B + 127]: for |t| < 2^22 the sum lies in [2^23, 2^24), where the float spacing is 1, so the one
+// rounding of the add is rne(t) (B is even, so ties go to the even code), and the code sits in the low
+// mantissa bits as a two's complement byte; beyond that range the clamp decides either way. Three
+// instructions and no conversion; the byte is taken straight from the float's bits.
+__device__ __forceinline__ float quant_i8_biased(float y, float inv_scale) {
+#pragma clang fp contract(off)
+    constexpr float B = 12582912.0f;
+    const float t = __fmul_rn(y, inv_scale);
+    return __builtin_amdgcn_fmed3f(__fadd_rn(t, B), B - 127.0f, B + 127.0f);
+}
+
 __device__ __forceinline__ uint32_t quant_i8(float y, float inv_scale) {
-    const float q = __builtin_amdgcn_fmed3f(rintf(__fmul_rn(y, inv_scale)), -127.f, 127.f);
-    return (uint32_t)((int)q) & 0xFFu;
+    return __float_as_uint(quant_i8_biased(y, inv_scale)) & 0xFFu;
+}
+
+// Four codes packed into one word (element t in byte t): two byte permutes and an or.
+__device__ __forceinline__ uint32_t quant_i8x4(const f32x4& y, float inv_scale) {
+    const uint32_t q0 = __float_as_uint(quant_i8_biased(y[0], inv_scale));
+    const uint32_t q1 = __float_as_uint(quant_i8_biased(y[1], inv_scale));
+    const uint32_t q2 = __float_as_uint(quant_i8_biased(y[2], inv_scale));
+    const uint32_t q3 = __float_as_uint(quant_i8_biased(y[3], inv_scale));
+    // selector bytes 0-3 pick the second operand's bytes, 4-7 the first's, 0x0c gives zero
+    return __builtin_amdgcn_perm(q1, q0, 0x0c0c0400u) | __builtin_amdgcn_perm(q3, q2, 0x04000c0cu);
 }
 
 // 4 x 4 byte transpose inside each lane quad: byte t of lane b's word (row t of column b) goes to byte b
