@@ -333,28 +333,49 @@ bool gemm_bf16_skinny_ok(const GemmArgs& g) {
 // more workgroups, R as large as that allows (each X fragment is then shared by more weight tiles);
 // the unit-vector case reads its X fragment cheaply and prefers more, smaller workgroups. Chosen by
 // measurement on MI355X over R in {1, 2, 4}, S in {4, 8, 16}, U in {1, 2, 4}.
-// Token-major X with 17 or more tokens (and 3-16 tokens from 1024 row blocks, where the LDS-ring kernel
-// is not used): measured again over R in {1, 2, 4, 8}, S in {4, 8, 16}, U in {1, 2} with weight copies
-// rotated beyond the Infinity Cache. There the best R is the smallest power of two that fits the grid in
-// one round of at most 256 workgroups: 28672 x 8192 at N = 64 / 32 / 16 85.8 / 63.7 / 50.2 -> 66.2 / 49.9 /
-// 45.4 us, 11008 x 4096 at N = 64 / 32 38.6 / 25.3 -> 25.3 / 16.8 us, 6144 x 4096 at N = 24 18.1 -> 11.2
-// us, 16384 x 4096 at N = 16 17.8 -> 16.1 us (that one-fragment grid fits two workgroups of 4 waves per CU);
-// from 384 row blocks also 9-16 tokens (11008 x 4096 at N = 16: 13.9 us, 8192 x 4096: 9.8 us, against 14.7 and
-// 10.1 us for LDS-ring units that carried two row blocks each).
+// Token-major X with 17 or more tokens (and 9-16 tokens from 384 row blocks, where the LDS-ring kernel
+// is not used): measured over R in {1, ..., 8}, S in {4, 8, 16}, U in {1, 2} with weight copies rotated
+// beyond the Infinity Cache. The best grid is one round that loads every CU alike: past 512 row blocks, R =
+// ceil(blocks / CUs), which gives each CU R or R - 1 blocks (a power of two R left up to a quarter of the CUs
+// idle: 11008 x 4096 at N = 16 / 32 / 64 13.9 / 16.8 / 25.4 -> 12.2 / 14.8 / 23.8 us with R = 3 instead of 4,
+// 8200 x 4096 at N = 16 / 48 12.8 / 22.9 -> 11.7 / 21.0, 28672 x 8192 at N = 32 / 64 53.3 / 70.4 -> 49.8 /
+// 66.4 with R = 7 instead of 8; at N = 16 that weight streams at its read floor either way). For one
+// fragment from 1024 row blocks, workgroups of two blocks and four waves, several per CU, are kept where
+// they load the CUs as evenly (16384 x 4096: 16.0 us against 18.0 with R = 4; 20480 x 4096, 640 of them:
+// 20.7 against 19.6 with R = 5).
+template <int NF, int S, int U>
+static hipError_t launch_r(const GemmArgs& g, hipStream_t s, int64_t r) {
+    switch (r) {
+    case 1: return skinny::launch<NF, 1, S, U>(g, s);
+    case 2: return skinny::launch<NF, 2, S, U>(g, s);
+    case 3: return skinny::launch<NF, 3, S, U>(g, s);
+    case 4: return skinny::launch<NF, 4, S, U>(g, s);
+    case 5: return skinny::launch<NF, 5, S, U>(g, s);
+    case 6: return skinny::launch<NF, 6, S, U>(g, s);
+    case 7: return skinny::launch<NF, 7, S, U>(g, s);
+    default: return skinny::launch<NF, 8, S, U>(g, s);
+    }
+}
+
 static hipError_t launch_skinny_tm(const GemmArgs& g, hipStream_t s, int64_t nb) {
+    const int64_t cus = device_cus();
+    const int64_t r = (nb + cus - 1) / cus;  // blocks per workgroup for a one-round grid (R <= 8 below)
     if (g.N <= 16) {
-        if (nb > 1536) return skinny::launch<1, 8, 8, 1>(g, s);
-        if (nb >= 1024) return skinny::launch<1, 2, 4, 1>(g, s);
-        return nb > 512 ? skinny::launch<1, 4, 4, 2>(g, s) : skinny::launch<1, 2, 8, 2>(g, s);
+        if (nb > 8 * cus) return skinny::launch<1, 8, 8, 1>(g, s);
+        if (nb > 6 * cus) return launch_r<1, 8, 1>(g, s, r);
+        if (nb >= 1024) {
+            // workgroups of two blocks: the most blocks a CU gets is 2 ceil(ceil(nb / 2) / CUs)
+            const int64_t pairs = 2 * (((nb + 1) / 2 + cus - 1) / cus);
+            return pairs <= r ? skinny::launch<1, 2, 4, 1>(g, s) : launch_r<1, 4, 1>(g, s, r);
+        }
+        return nb > 512 ? launch_r<1, 4, 2>(g, s, r) : skinny::launch<1, 2, 8, 2>(g, s);
     }
     if (g.N <= 32) {
-        if (nb > 1024) return skinny::launch<2, 8, 8, 1>(g, s);
-        if (nb > 512) return skinny::launch<2, 4, 8, 1>(g, s);
+        if (nb > 512) return r <= 8 ? launch_r<2, 8, 1>(g, s, r) : skinny::launch<2, 8, 8, 1>(g, s);
         if (nb > 256) return skinny::launch<2, 2, 8, 1>(g, s);
         return nb >= 192 ? skinny::launch<2, 1, 8, 1>(g, s) : skinny::launch<2, 1, 16, 1>(g, s);
     }
-    if (nb > 1024) return skinny::launch<4, 8, 4, 1>(g, s);
-    if (nb > 512) return skinny::launch<4, 4, 4, 1>(g, s);
+    if (nb > 512) return r <= 8 ? launch_r<4, 4, 1>(g, s, r) : skinny::launch<4, 8, 4, 1>(g, s);
     if (nb > 256) return skinny::launch<4, 2, 8, 1>(g, s);
     return skinny::launch<4, 1, 8, 1>(g, s);
 }

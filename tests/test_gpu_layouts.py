@@ -62,9 +62,12 @@ TM_SHAPES = [
     (8200, 4096, 16, 4096, 8200),
     (6150, 320, 11, 320, 6150),
     (6150, 320, 5, 328, 6150),  # 2-8 tokens, 4-wave ring workgroups above 256 row blocks, K tail
-    # the register-pipelined few-token kernel, token-major, one workgroup per grid slot at most 256 (R = the
-    # smallest power of two that fits): every configuration, ragged block counts, a K tail
+    # the register-pipelined few-token kernel, token-major, one round of at most one workgroup per CU (R =
+    # ceil(blocks / CUs): 3, 5, 6 and 7 here, with a last workgroup holding fewer blocks), the two-block
+    # workgroups several per CU, ragged block counts, a K tail
     (25000, 128, 12, 128, 25000),
+    (24000, 128, 28, 136, 24000),
+    (20480, 128, 16, 128, 20480),
     (17000, 208, 16, 216, 17000),
     (20000, 128, 30, 128, 20000),
     (12000, 256, 20, 264, 12000),
