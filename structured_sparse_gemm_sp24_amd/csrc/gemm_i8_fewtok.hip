@@ -389,6 +389,17 @@ bool gemm_i8_fewtok_ok(const GemmArgs& g) {
            (g.N - 1) * g.ldx + g.K + 128 < ((int64_t)1 << 31) && 8 * (g.K / fewtok_i8::KT) * 1024 < ((int64_t)1 << 31);
 }
 
+// The register loop with R = r row blocks per workgroup for r in [RMIN, RMAX] (RMAX otherwise).
+template <int NF, int U, int S, int RMIN, int RMAX>
+static hipError_t launch_r(const GemmArgs& g, hipStream_t s, int64_t r) {
+    if constexpr (RMIN <= 3 && RMAX >= 3) if (r == 3) return fewtok_i8::launch<NF, 3, U, S>(g, s);
+    if constexpr (RMIN <= 4 && RMAX > 4) if (r == 4) return fewtok_i8::launch<NF, 4, U, S>(g, s);
+    if constexpr (RMIN <= 5 && RMAX > 5) if (r == 5) return fewtok_i8::launch<NF, 5, U, S>(g, s);
+    if constexpr (RMIN <= 6 && RMAX > 6) if (r == 6) return fewtok_i8::launch<NF, 6, U, S>(g, s);
+    if constexpr (RMIN <= 7 && RMAX > 7) if (r == 7) return fewtok_i8::launch<NF, 7, U, S>(g, s);
+    return fewtok_i8::launch<NF, RMAX, U, S>(g, s);
+}
+
 // Register loop: row blocks per workgroup (R), tiles per request round (U) and waves (S) by the number of 16-token
 // fragments and of row blocks, measured on MI355X with weight copies rotated beyond the Infinity Cache over
 // R in {1, 2, 4, 8}, U in {1, 2, 4}, S in {4, 8}. More row blocks per workgroup share each X fragment; the best
@@ -409,24 +420,34 @@ hipError_t launch_gemm_i8_fewtok(const GemmArgs& g, hipStream_t s) {
     if (g.N > 8 && g.N <= 16 && nb < 1024)
         return nb >= 512 ? fewtok_i8::launch_ring<4, 4, 16>(g, s) : fewtok_i8::launch_ring<8, 3, 16>(g, s);  // 52 / 78 KB
     using namespace fewtok_i8;
+    // register loop: R row blocks per workgroup. From 512 to 1024 row blocks (and 17 to 32 tokens beyond),
+    // R = ceil(blocks / CUs) loads every CU alike in one round (bit-identical; 11008 x 4096 at N = 24 / 40 /
+    // 64 11.9 / 15.4 / 18.2 -> 11.5 / 14.1 / 16.9 us with R = 3 instead of 4, 8200 x 4096 at N = 64 17.7 ->
+    // 16.4, 16384 x 4096 at N = 12 17.2 -> 15.3 with R = 4 instead of 8, 28672 x 8192 at N = 32 36.3 -> 35.2
+    // with R = 7). On 28672 x 8192 at one or three to four fragments the earlier grids stream faster (N = 16:
+    // 32.8 against 39.9 us with R = 7; N = 64: 49.0 against 58.3) and stay.
+    const int64_t cus = device_cus(), r = (nb + cus - 1) / cus;
     if (nf == 1) {
-        if (nb >= 1024) return g.N > 8 ? launch<1, 8, 4, 8>(g, s) : launch<1, 2, 4, 8>(g, s);
+        if (nb >= 1024) {
+            if (g.N <= 8) return launch<1, 2, 4, 8>(g, s);
+            return r == 4 ? launch<1, 4, 4, 8>(g, s) : launch<1, 8, 4, 8>(g, s);
+        }
         return nb >= 512 ? launch<1, 1, 2, 4>(g, s) : launch<1, 1, 2, 8>(g, s);
     }
     if (nf == 2) {
-        if (nb > 1024) return launch<2, 8, 2, 8>(g, s);
-        if (nb > 512) return launch<2, 4, 2, 4>(g, s);
+        if (nb > 1024) return r <= 8 ? launch_r<2, 2, 8, 5, 8>(g, s, r) : launch<2, 8, 2, 8>(g, s);
+        if (nb > 512) return launch_r<2, 2, 4, 3, 4>(g, s, r);
         if (nb > 256) return launch<2, 2, 2, 8>(g, s);
         return launch<2, 1, 2, 4>(g, s);
     }
     if (nf == 3) {
         if (nb > 1024) return launch<3, 4, 4, 4>(g, s);
-        if (nb > 512) return launch<3, 4, 2, 8>(g, s);
+        if (nb > 512) return launch_r<3, 2, 8, 3, 4>(g, s, r);
         if (nb > 256) return launch<3, 2, 4, 4>(g, s);
         return launch<3, 1, 2, 4>(g, s);
     }
     if (nb > 1024) return launch<4, 4, 4, 4>(g, s);
-    if (nb > 512) return launch<4, 4, 2, 8>(g, s);
+    if (nb > 512) return launch_r<4, 2, 8, 3, 4>(g, s, r);
     if (nb > 256) return launch<4, 2, 4, 4>(g, s);
     return launch<4, 1, 2, 4>(g, s);
 }

@@ -199,6 +199,10 @@ I8_TM_SHAPES = [
     (5000, 256, 36, 256, 5000),
     (9000, 256, 64, 256, 9000),
     (4500, 256, 50, 256, 4504),
+    # one round of workgroups with R = ceil(blocks / CUs): four blocks at one fragment (1024 blocks), three
+    # at three fragments (688 blocks)
+    (16384, 256, 12, 256, 16384),
+    (11008, 256, 40, 256, 11008),
     (33, 128, 48, 128, 36),
     (2050, 640, 64, 640, 2056),
     # 128-wide tiles with two workgroups per compute unit (token-major, more tiles than compute units):
