@@ -178,22 +178,42 @@ __global__ __launch_bounds__(256) void prune_compress_kernel(const void* __restr
     }
 }
 
-// int8 magnitude selection a group at a time, the group's four weights being one 32-bit word. Each byte
-// becomes |q| without crossing into its neighbour (for q < 0, ~q + 1 <= 0x80), and the key
-// (|q| << 2) | (3 - e) is unique within the group and orders as |q| with the lower position first on ties,
-// so the kept pair is the largest and second largest key: the second largest of four is the larger of the
-// median of the first three and the smaller of their maximum and the fourth.
-__device__ __forceinline__ void top2_i8(uint32_t w, uint32_t& lo, uint32_t& hi) {
-    const uint32_t sgn = (w >> 7) & 0x01010101u;
-    const uint32_t a = (w ^ (sgn * 0xFFu)) + sgn;
-    const uint32_t k0 = ((a & 0xFFu) << 2) | 3u, k1 = (((a >> 8) & 0xFFu) << 2) | 2u;
-    const uint32_t k2 = (((a >> 16) & 0xFFu) << 2) | 1u, k3 = (a >> 24) << 2;
-    const uint32_t m3 = max(max(k0, k1), k2);
-    const uint32_t med = max(min(k0, k1), min(max(k0, k1), k2));
-    const uint32_t first = max(m3, k3), second = max(med, min(m3, k3));
-    const uint32_t pf = first & 3u, ps = second & 3u;  // 3 - position
-    lo = 3u - max(pf, ps);
-    hi = 3u - min(pf, ps);
+// int8 magnitude selection, two groups at a time, the group's four weights being one 32-bit word. Each byte
+// becomes |q| without crossing into its neighbour (for q < 0, ~q + 1 <= 0x80). The key of position e,
+// (|q| << 2) | (3 - e), is unique within the group and orders as |q| with the lower position first on ties;
+// the two groups' keys of one position share a word, one per 16-bit half, and the packed 16-bit max / min
+// take both groups' comparisons at once. The kept pair is the largest and second largest key: the second
+// largest of four is the larger of the median of the first three and the smaller of their maximum and the
+// fourth. Returns, per half, the lower (lo) and higher (hi) kept position.
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t max_u16x2(uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a), __builtin_bit_cast(u16x2, b)));
+}
+__device__ __forceinline__ uint32_t min_u16x2(uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(u16x2, a), __builtin_bit_cast(u16x2, b)));
+}
+
+__device__ __forceinline__ uint32_t abs_i8x4(uint32_t w) {
+    const uint32_t hb = w & 0x80808080u, sgn = hb >> 7;
+    return (w ^ ((hb << 1) - sgn)) + sgn;  // (hb << 1) - sgn: 0xFF in each negative byte
+}
+
+__device__ __forceinline__ void top2_i8_pair(uint32_t w0, uint32_t w1, uint32_t& lo, uint32_t& hi) {
+    const uint32_t a0 = abs_i8x4(w0), a1 = abs_i8x4(w1);
+    // byte e of a0 into the low half, of a1 into the high half (selector bytes 0-3: a0, 4-7: a1, 0x0c: zero);
+    // |q| <= 0x80, so the shift stays inside each half
+    const uint32_t k0 = (__builtin_amdgcn_perm(a1, a0, 0x0c040c00u) << 2) | 0x00030003u;
+    const uint32_t k1 = (__builtin_amdgcn_perm(a1, a0, 0x0c050c01u) << 2) | 0x00020002u;
+    const uint32_t k2 = (__builtin_amdgcn_perm(a1, a0, 0x0c060c02u) << 2) | 0x00010001u;
+    const uint32_t k3 = __builtin_amdgcn_perm(a1, a0, 0x0c070c03u) << 2;
+    const uint32_t m01 = max_u16x2(k0, k1);
+    const uint32_t m3 = max_u16x2(m01, k2);
+    const uint32_t med = max_u16x2(min_u16x2(k0, k1), min_u16x2(m01, k2));
+    const uint32_t first = max_u16x2(m3, k3), second = max_u16x2(med, min_u16x2(m3, k3));
+    const uint32_t pf = first & 0x00030003u, ps = second & 0x00030003u;  // 3 - position
+    lo = max_u16x2(pf, ps) ^ 0x00030003u;
+    hi = min_u16x2(pf, ps) ^ 0x00030003u;
 }
 
 // The int8 magnitude prune on the same grid as prune_compress_kernel: lane (r, qq) of wave w holds 32
@@ -230,11 +250,13 @@ __global__ __launch_bounds__(256) void prune_compress_i8_kernel(const void* __re
 #pragma unroll
         for (int k = 0; k < 4; k++) {
             const uint32_t w0 = x[i][k >> 1][2 * (k & 1)], w1 = x[i][k >> 1][2 * (k & 1) + 1];
-            uint32_t lo0, hi0, lo1, hi1;
-            top2_i8(w0, lo0, hi0);
-            top2_i8(w1, lo1, hi1);
-            out[k] = __builtin_amdgcn_perm(w1, w0, lo0 | (hi0 << 8) | ((lo1 + 4u) << 16) | ((hi1 + 4u) << 24));
-            mbits |= (lo0 | (hi0 << 2) | (lo1 << 4) | (hi1 << 6)) << (8 * k);
+            uint32_t lo, hi;  // w0's positions in the low halves, w1's in the high halves
+            top2_i8_pair(w0, w1, lo, hi);
+            // selector lo0, hi0 (bytes of w0), lo1 + 4, hi1 + 4 (bytes of w1)
+            out[k] = __builtin_amdgcn_perm(w1, w0, lo | (hi << 8) | 0x04040000u);
+            // index bits lo0 | hi0 << 2 | lo1 << 4 | hi1 << 6
+            const uint32_t e = lo | (hi << 2);
+            mbits |= ((e | (e >> 12)) & 0xFFu) << (8 * k);
         }
         *reinterpret_cast<u32x4*>(values + (b * tiles + t) * 1024 + 16 * lane) = u32x4{out[0], out[1], out[2], out[3]};
         *reinterpret_cast<uint32_t*>(meta + (b * tiles + t) * 256 + 4 * lane) = mbits;
