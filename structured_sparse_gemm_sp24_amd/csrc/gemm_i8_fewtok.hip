@@ -154,12 +154,13 @@ __device__ __forceinline__ int x_swz(int n) { return ((n >> 1) & 7) ^ ((n & 1) <
 // i + D - 1 into the slot unit i - 1 has left, waits (vmcnt) until unit i has landed and multiplies it, so D - 1
 // units stay in flight and no wave waits for another until the final reduction. Units past the wave's range
 // read zeros without memory traffic (offset bit 31); tokens past N read zeros from the descriptor's range.
-template <int S, int D, int XR, int OUT, int EPI>
+template <int S, int D, int XR, int R, int OUT, int EPI>
 __global__ __launch_bounds__(64 * S) void gemm_i8_fewtok_ring(Args a) {
     static_assert(XR == 2 || XR == 8 || XR == 16, "X tile rows");
     constexpr int NXI = XR == 16 ? 2 : 1;  // X loads per unit (XR = 2: one dword load for both rows)
-    constexpr int XOFF = 1024 + 256, UNIT = XOFF + 128 * XR, RING = D * UNIT, LPU = 2 + NXI;
-    constexpr int RED = (S - 1) * 64 * 16;
+    // a unit: the K tile's R value tiles, their R index tiles, then the X tile all R blocks share
+    constexpr int MOFF = 1024 * R, XOFF = 1280 * R, UNIT = XOFF + 128 * XR, RING = D * UNIT, LPU = 2 * R + NXI;
+    constexpr int RED = (S - 1) * R * 64 * 16;
     static_assert((D - 1) * LPU < 64, "vmcnt range");
     __shared__ __attribute__((aligned(16))) char smem[S * RING > RED ? S * RING : RED];
     typedef __attribute__((address_space(3))) char lds_char;
@@ -167,12 +168,14 @@ __global__ __launch_bounds__(64 * S) void gemm_i8_fewtok_ring(Args a) {
     const uint32_t l0 = (uint32_t)(size_t)(lds_char*)smem;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int r = lane & 15, q = lane >> 4;
-    const int64_t b0 = blockIdx.x;
+    const int64_t b0 = (int64_t)blockIdx.x * R, nblk = (a.M + 15) / 16;
     const int T = (int)(a.K / KT);
     const int per = (T + S - 1) / S, t0 = wave * per, t1 = t0 + per < T ? t0 + per : T;
     const int n = t1 > t0 ? t1 - t0 : 0;
-    const i32x4 rA = rsrc4(a.vals + b0 * T * 1024, (int64_t)T * 1024);
-    const i32x4 rM = rsrc4(a.meta + b0 * T * 256, (int64_t)T * 256);
+    // the workgroup's blocks (fewer in the last one: blocks past the weight read zeros)
+    const int64_t nb = nblk - b0 < R ? nblk - b0 : R;
+    const i32x4 rA = rsrc4(a.vals + b0 * T * 1024, nb * T * 1024);
+    const i32x4 rM = rsrc4(a.meta + b0 * T * 256, nb * T * 256);
     const int8_t* X = a.X + (int64_t)blockIdx.y * a.sxb;
     const i32x4 rX = rsrc4(X, (a.N - 1) * a.ldx + a.K);
     // per-lane load offsets: value tile 16 * lane, index tile 4 * lane; X: 16-byte loads put lane i in row
@@ -194,8 +197,12 @@ __global__ __launch_bounds__(64 * S) void gemm_i8_fewtok_ring(Args a) {
     auto issue = [&](int i) {
         const uint32_t t = (uint32_t)(t0 + i), past = i < n ? 0u : OOR;
         const uint32_t slot = ring + (uint32_t)((i % D) * UNIT);
-        dma16(slot, (oA + t * 1024u) | past, rA);
-        dma4(slot + 1024, (oM + t * 256u) | past, rM);
+#pragma unroll
+        for (int j = 0; j < R; j++) {
+            const uint32_t tj = (uint32_t)(j * T) + t;
+            dma16(slot + 1024 * j, (oA + tj * 1024u) | past, rA);
+            dma4(slot + MOFF + 256 * j, (oM + tj * 256u) | past, rM);
+        }
         if constexpr (XR == 2) {
             dma4(slot + XOFF, (oX[0] + t * (uint32_t)KT) | past, rX);
         } else {
@@ -207,7 +214,9 @@ __global__ __launch_bounds__(64 * S) void gemm_i8_fewtok_ring(Args a) {
     // XR feed only tokens >= XR > N - 1, never stored: any row of the tile will do)
     const int xr = r & (XR - 1);
     const int xo0 = XOFF + xr * 128 + 16 * (q ^ x_swz(xr)), xo1 = XOFF + xr * 128 + 16 * ((q ^ x_swz(xr)) ^ 4);
-    i32x4 acc[1][1] = {{i32x4{0, 0, 0, 0}}};
+    i32x4 acc[R][1];
+#pragma unroll
+    for (int j = 0; j < R; j++) acc[j][0] = i32x4{0, 0, 0, 0};
 #pragma unroll
     for (int i = 0; i < D - 1; i++) issue(i);
     for (int i = 0; i < n; i++) {
@@ -215,16 +224,19 @@ __global__ __launch_bounds__(64 * S) void gemm_i8_fewtok_ring(Args a) {
         wait_vmcnt<(D - 1) * LPU>();  // unit i has landed
         asm volatile("" ::: "memory");
         const lds_char* p = (const lds_char*)(size_t)(ring + (uint32_t)((i % D) * UNIT));
-        const i32x4 av = *reinterpret_cast<lds_i32x4*>(p + 16 * lane);
-        const int iv = *reinterpret_cast<const __attribute__((address_space(3))) int*>(p + 1024 + 4 * lane);
         const i32x4 lo = *reinterpret_cast<lds_i32x4*>(p + xo0), hi = *reinterpret_cast<lds_i32x4*>(p + xo1);
-        acc[0][0] = __builtin_amdgcn_smfmac_i32_16x16x128_i8(av, i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]},
-                                                             acc[0][0], iv, 0, 0);
+        const i32x8 bx = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+        for (int j = 0; j < R; j++) {
+            const i32x4 av = *reinterpret_cast<lds_i32x4*>(p + 1024 * j + 16 * lane);
+            const int iv = *reinterpret_cast<const __attribute__((address_space(3))) int*>(p + MOFF + 256 * j + 4 * lane);
+            acc[j][0] = __builtin_amdgcn_smfmac_i32_16x16x128_i8(av, bx, acc[j][0], iv, 0, 0);
+        }
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this unit's reads are done before its slot is refilled
     }
     wait_vmcnt<0>();  // every load (the zero-filling ones included) has landed before LDS is reused
     __syncthreads();  // every wave is done with its ring
-    finish<1, 1, S, OUT, EPI>(acc, a, reinterpret_cast<i32x4*>(smem), b0, wave, lane);
+    finish<1, R, S, OUT, EPI>(acc, a, reinterpret_cast<i32x4*>(smem), b0, wave, lane);
 }
 
 // OUT: OUT_I32 (raw accumulators), OUT_F32, OUT_BF16, OUT_I8; EPI: bias (1) | GELU (2).
@@ -334,18 +346,18 @@ static hipError_t launch(const GemmArgs& g, hipStream_t s) {
     return hipSuccess;
 }
 
-template <int S, int D, int XR, int OUT>
+template <int S, int D, int XR, int R, int OUT>
 static void launch_ring_epi(int epi, dim3 grd, dim3 blk, hipStream_t s, const Args& e) {
     switch (epi) {
-    case 0: hipLaunchKernelGGL((gemm_i8_fewtok_ring<S, D, XR, OUT, 0>), grd, blk, 0, s, e); break;
-    case 1: hipLaunchKernelGGL((gemm_i8_fewtok_ring<S, D, XR, OUT, 1>), grd, blk, 0, s, e); break;
-    case 2: hipLaunchKernelGGL((gemm_i8_fewtok_ring<S, D, XR, OUT, 2>), grd, blk, 0, s, e); break;
-    default: hipLaunchKernelGGL((gemm_i8_fewtok_ring<S, D, XR, OUT, 3>), grd, blk, 0, s, e); break;
+    case 0: hipLaunchKernelGGL((gemm_i8_fewtok_ring<S, D, XR, R, OUT, 0>), grd, blk, 0, s, e); break;
+    case 1: hipLaunchKernelGGL((gemm_i8_fewtok_ring<S, D, XR, R, OUT, 1>), grd, blk, 0, s, e); break;
+    case 2: hipLaunchKernelGGL((gemm_i8_fewtok_ring<S, D, XR, R, OUT, 2>), grd, blk, 0, s, e); break;
+    default: hipLaunchKernelGGL((gemm_i8_fewtok_ring<S, D, XR, R, OUT, 3>), grd, blk, 0, s, e); break;
     }
 }
 
-// The LDS-ring kernel (N <= XR <= 16): one 16-row block per workgroup.
-template <int S, int D, int XR>
+// The LDS-ring kernel (N <= XR <= 16): R 16-row blocks per workgroup.
+template <int S, int D, int XR, int R = 1>
 static hipError_t launch_ring(const GemmArgs& g, hipStream_t s) {
     Args a;
     a.vals = static_cast<const int8_t*>(g.values);
@@ -357,7 +369,7 @@ static hipError_t launch_ring(const GemmArgs& g, hipStream_t s) {
     a.Y = g.Y;
     a.M = g.M; a.K = g.K; a.N = g.N; a.ldx = g.ldx; a.sxb = g.sx; a.ldy = g.ldy; a.syb = g.sy;
     a.y_vec = ((reinterpret_cast<uintptr_t>(g.Y) & 15) == 0) && g.ldy % 4 == 0 && (g.batch == 1 || g.sy % 4 == 0);
-    const unsigned grid = (unsigned)((g.M + 15) / 16);
+    const unsigned grid = (unsigned)(((g.M + 15) / 16 + R - 1) / R);
     const int es = g.out_kind == OUT_BF16 ? 2 : (g.out_kind == OUT_I8 ? 1 : 4);
     const int epi = (g.bias ? 1 : 0) | (g.gelu ? 2 : 0);
     for (int64_t e0 = 0; e0 < g.batch; e0 += 65535) {
@@ -367,10 +379,10 @@ static hipError_t launch_ring(const GemmArgs& g, hipStream_t s) {
         e.Y = static_cast<char*>(a.Y) + e0 * a.syb * es;
         const dim3 grd(grid, gb), blk(64 * S);
         switch (g.out_kind) {
-        case OUT_I32: hipLaunchKernelGGL((gemm_i8_fewtok_ring<S, D, XR, OUT_I32, 0>), grd, blk, 0, s, e); break;
-        case OUT_F32: launch_ring_epi<S, D, XR, OUT_F32>(epi, grd, blk, s, e); break;
-        case OUT_BF16: launch_ring_epi<S, D, XR, OUT_BF16>(epi, grd, blk, s, e); break;
-        default: launch_ring_epi<S, D, XR, OUT_I8>(epi, grd, blk, s, e); break;
+        case OUT_I32: hipLaunchKernelGGL((gemm_i8_fewtok_ring<S, D, XR, R, OUT_I32, 0>), grd, blk, 0, s, e); break;
+        case OUT_F32: launch_ring_epi<S, D, XR, R, OUT_F32>(epi, grd, blk, s, e); break;
+        case OUT_BF16: launch_ring_epi<S, D, XR, R, OUT_BF16>(epi, grd, blk, s, e); break;
+        default: launch_ring_epi<S, D, XR, R, OUT_I8>(epi, grd, blk, s, e); break;
         }
         const hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
@@ -417,8 +429,16 @@ hipError_t launch_gemm_i8_fewtok(const GemmArgs& g, hipStream_t s) {
     // 8.5 / 8.2 / 8.7 / 8.9 us), for N <= 2 below 1024 blocks and for N > 8 from 1024 (28672 x 8192 at N = 16:
     // 32.7 against 35.4 us). Workgroups of 4 waves (three per CU) from 512 blocks, of 8 (two per CU) below.
     if (g.N <= 2 && nb >= 1024) return fewtok_i8::launch_ring<4, 8, 2>(g, s);  // 48 KB
-    if (g.N > 8 && g.N <= 16 && nb < 1024)
+    if (g.N > 8 && g.N <= 16 && nb < 1024) {
+        // three or four row blocks per unit, sharing its X tile, where that makes a round of at least 7/8 of
+        // the CUs (bit-identical; 11008 x 4096 at N = 16 / 12 9.84 / 9.74 -> 9.28 / 9.22 us with three, 16000 x
+        // 4096 and 14336 x 4096 at N = 16 12.97 / 12.0 -> 12.32 / 11.5 with four; 12290 x 4096, 193 workgroups
+        // of four, 9.96 -> 10.38, so not there): one 94 / 115 KB workgroup per CU
+        const int64_t cus = device_cus();
+        if (nb > 2 * cus && 8 * ((nb + 2) / 3) >= 7 * cus && nb <= 3 * cus) return fewtok_i8::launch_ring<4, 4, 16, 3>(g, s);
+        if (8 * ((nb + 3) / 4) >= 7 * cus && nb <= 4 * cus) return fewtok_i8::launch_ring<4, 4, 16, 4>(g, s);
         return nb >= 512 ? fewtok_i8::launch_ring<4, 4, 16>(g, s) : fewtok_i8::launch_ring<8, 3, 16>(g, s);  // 52 / 78 KB
+    }
     using namespace fewtok_i8;
     // register loop: R row blocks per workgroup. From 512 to 1024 row blocks (and 17 to 32 tokens beyond),
     // R = ceil(blocks / CUs) loads every CU alike in one round (bit-identical; 11008 x 4096 at N = 24 / 40 /

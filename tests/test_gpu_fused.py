@@ -40,6 +40,7 @@ SHAPES = [
     (8200, 256, 10, "token"),   # few-token LDS ring, four-wave workgroups (513 row blocks)
     (16400, 128, 2, "token"),   # few-token LDS ring for one or two tokens (1025 row blocks)
     (2300, 256, 8200, "token"),  # 128-wide tiles, two workgroups per compute unit (585 tiles, ragged)
+    (11008, 256, 12, "token"),  # few-token LDS ring, units of three row blocks
 ]
 
 

@@ -189,6 +189,10 @@ I8_TM_SHAPES = [
     # the LDS-ring loop at 9-16 tokens below 1024 row blocks: four-wave workgroups from 512 blocks (odd count),
     # eight-wave below
     (10000, 384, 13, 384, 10008),
+    # LDS-ring units of three (688 row blocks) and four (894: a last workgroup of two) row blocks
+    (11008, 384, 13, 384, 11016),
+    (14300, 128, 9, 128, 14300),
+    (16000, 256, 16, 272, 16000),
     (6000, 256, 11, 256, 6000),
     (8200, 256, 7, 272, 8200),
     # the register loop's grid sizes: more row blocks per workgroup as the weight grows (ragged block counts)
