@@ -23,7 +23,9 @@ microsecond kernels are timed without the Python binding's per-call overhead bet
 Roofline conventions: a 2:4 GEMM executes M*N*K/2 multiply-adds, i.e. M*N*K algorithmic flops, which
 are priced against the dense MFMA peak of the dtype (bf16 2516.6 TFLOP/s, int8 5033.2 TOP/s); this
 fraction equals the dense-equivalent rate 2*M*N*K/t over the sparse-MFMA peak. HBM-bound kernels are
-priced as algorithmic bytes / t against 8 TB/s.
+priced as algorithmic bytes / t against 8 TB/s. A kernel whose epilogue's VALU work outweighs both (the fused
+int8 GEMM with GELU) is priced as its VALU lane-instruction slots / t against the issue rate
+256 x 4 x 16 x 2.4 GHz = 39.3 Tslot/s.
 """
 from __future__ import annotations
 
@@ -45,6 +47,13 @@ from structured_sparse_gemm_sp24_amd import synth  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
 DENSE_PEAK = {"bf16": 2516.6, "i8": 5033.2}   # TFLOP/s (bf16) and TOP/s (int8), dense MFMA
+# VALU issue rate in lane-instruction slots per second: 256 CUs x 4 SIMDs x 16 lanes per clock x 2.4 GHz
+# (unpacked fp32; a transcendental takes 4 slots)
+VALU_PEAK_TSLOTS = 256 * 4 * 16 * 2.4e9 / 1e12
+# slots per output of the fused int8 epilogue with GELU and int8 output: dequant (convert, scale, bias: 3),
+# GELU by Abramowitz & Stegun 7.1.26 (13 full-rate + reciprocal and exp2 at 4 slots each: 21), requantization
+# (scale, round by adding 1.5 * 2^23, clamp: 3), one slot for packing four codes
+GELU_I8_SLOTS_PER_OUTPUT = 28
 SPEC_SCLK_MHZ = 2400.0                          # the clock those peaks are quoted at
 CACHE_BYTES = 256 << 20                      # MI355X Infinity Cache
 PROFILES = os.path.join(ROOT, "profiles")
@@ -70,8 +79,9 @@ class Kernel:
     """One launch of the step: fn(copy), algorithmic bytes and flops per launch, the dtype of its
     arithmetic, and the source files whose digest keys its counter-measured traffic."""
 
-    def __init__(self, name, fn, nbytes, flops=0.0, dtype="bf16", sources=()):
+    def __init__(self, name, fn, nbytes, flops=0.0, dtype="bf16", sources=(), valu_slots=0.0):
         self.name, self.fn, self.nbytes, self.flops, self.dtype, self.sources = name, fn, nbytes, flops, dtype, sources
+        self.valu_slots = valu_slots  # VALU lane-instruction slots the epilogue's definition takes (0: none)
 
 
 def gemm_sources(N):
@@ -434,7 +444,8 @@ def workload_bert_int8_fused(args):
         Kernel("gemm_i8_w1_gelu_i8out",
                lambda c: sp.sp24_gemm_i8_fused(c["v0"], c["m0"], M1, c["X"], c["s1"], bias=c["b1"], activation="gelu",
                                                out_dtype=torch.int8, out_scale=s_h, layout=lay, out=c["H"]),
-               M1 * K1 * 5 // 8 + K1 * N + M1 * N + 8 * M1, float(M1) * N * K1, "i8", srcs),
+               M1 * K1 * 5 // 8 + K1 * N + M1 * N + 8 * M1, float(M1) * N * K1, "i8", srcs,
+               valu_slots=float(GELU_I8_SLOTS_PER_OUTPUT) * M1 * N),
         Kernel("gemm_i8_w2_bias_f32out",
                lambda c: sp.sp24_gemm_i8_fused(c["v1"], c["m1"], M2, c["H"], c["s2"], bias=c["b2"], layout=lay,
                                                out=c["Y"]),
@@ -671,7 +682,14 @@ def roofline(k: Kernel, t_s: float, workload: str):
     gbs = k.nbytes / t_s / 1e9
     peak_tf = DENSE_PEAK[k.dtype]
     tf = k.flops / t_s / 1e12
-    if k.flops == 0 or k.nbytes / (HBM_PEAK_GBS * 1e9) >= k.flops / (peak_tf * 1e12):
+    t_hbm = k.nbytes / (HBM_PEAK_GBS * 1e9)
+    t_mfma = k.flops / (peak_tf * 1e12)
+    t_alu = k.valu_slots / (VALU_PEAK_TSLOTS * 1e12)
+    if t_alu > max(t_hbm, t_mfma):
+        ts = k.valu_slots / t_s / 1e12
+        r = dict(bound="alu", achieved=round(ts, 2), peak=round(VALU_PEAK_TSLOTS, 2), unit="Tslot/s",
+                 frac=round(ts / VALU_PEAK_TSLOTS, 4))
+    elif k.flops == 0 or t_hbm >= t_mfma:
         r = dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s", frac=round(gbs / HBM_PEAK_GBS, 4))
     else:
         r = dict(bound="mfma", achieved=round(tf, 1), peak=peak_tf, unit="TOP/s" if k.dtype == "i8" else "TFLOP/s",
@@ -683,6 +701,9 @@ def roofline(k: Kernel, t_s: float, workload: str):
         r["algorithmic_flops"] = k.flops
         r["mfma_frac"] = round(tf / peak_tf, 4)
     r["hbm_frac"] = round(gbs / HBM_PEAK_GBS, 4)
+    if k.valu_slots:
+        r["valu_slots"] = k.valu_slots
+        r["alu_frac"] = round(k.valu_slots / t_s / 1e12 / VALU_PEAK_TSLOTS, 4)
     return r
 
 

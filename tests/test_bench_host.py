@@ -1,0 +1,28 @@
+"""Host checks of bench.py's roofline choice (no GPU: the function only prices given bytes, flops and slots)."""
+import os
+import sys
+
+sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+import bench  # noqa: E402
+
+
+def _k(nbytes, flops, dtype="bf16", slots=0.0):
+    return bench.Kernel("k", None, nbytes, flops, dtype, (), valu_slots=slots)
+
+
+def test_roofline_picks_the_binding_roof():
+    # 28672 x 8192 x 8192 bf16: MFMA-bound; 1550 us is 49.3 % of the dense bf16 peak
+    M, K, N = 28672, 8192, 8192
+    r = bench.roofline(_k(M * K * 9 // 8 + 2 * K * N + 2 * M * N, float(M) * N * K), 1550e-6, "none")
+    assert r["bound"] == "mfma" and abs(r["frac"] - M * N * K / 1550e-6 / 2516.6e12) < 1e-4
+    # 11008 x 4096 at N = 16: HBM-bound
+    M, K, N = 11008, 4096, 16
+    r = bench.roofline(_k(M * K * 9 // 8 + 2 * K * N + 2 * M * N, float(M) * N * K), 13e-6, "none")
+    assert r["bound"] == "hbm" and r["unit"] == "GB/s"
+    # the fused int8 epilogue with GELU: VALU slots outweigh bytes and flops
+    M, K, N = 3072, 768, 8192
+    slots = float(bench.GELU_I8_SLOTS_PER_OUTPUT) * M * N
+    r = bench.roofline(_k(M * K * 5 // 8 + K * N + M * N + 8 * M, float(M) * N * K, "i8", slots), 33.2e-6, "none")
+    assert r["bound"] == "alu" and r["unit"] == "Tslot/s"
+    assert abs(bench.VALU_PEAK_TSLOTS - 39.3216) < 1e-6
+    assert abs(r["frac"] - slots / 33.2e-6 / 1e12 / bench.VALU_PEAK_TSLOTS) < 1e-4
