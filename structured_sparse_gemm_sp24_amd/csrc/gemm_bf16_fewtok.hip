@@ -231,17 +231,19 @@ hipError_t launch(const GemmArgs& g, hipStream_t s) {
 // Where this kernel is used: measured against the register-pipelined few-token kernel on MI355X (HIP
 // graph replays, weight copies rotated beyond the Infinity Cache): for N <= 2 (28672 x 8192 at N = 1: 44.9
 // against 48.7 us), for N <= 8 below 1024 row blocks (11008 x 4096 at N = 8: 12.2 against 14.1 us), and for
-// 9 to 16 tokens below 384 row blocks (4096 x 4096 at N = 9 / 12 / 16: 7.0 / 6.9 / 7.1 against 7.6 / 7.2 /
-// 7.9 us). With 16-row X tiles a unit carries twice the X bytes of its weight bytes, and above 384 blocks the
-// register kernel, whose workgroups share each X fragment among up to 8 row blocks, is faster (11008 x 4096 at
-// N = 16: 13.9 against 14.7 us; 8192 x 4096: 9.8 against 10.1 us).
+// 9 to 16 tokens up to 256 row blocks, one workgroup per CU (4096 x 4096 at N = 9 / 12 / 16: 7.0 / 6.9 / 7.1
+// against 7.6 / 7.2 / 7.9 us). With 16-row X tiles a unit carries twice the X bytes of its weight bytes, and
+// past 256 blocks the register kernel, whose workgroups share each X fragment among several row blocks and
+// fit one round, is faster (cold: 5000 x 4096 at N = 16 10.6 -> 9.0 us, 6000 x 4096 at N = 12 10.1 -> 8.5,
+// 4400 x 4096 at N = 16 10.4 -> 8.8, 5600 x 2048 at N = 10 6.5 -> 5.8; 11008 x 4096 at N = 16 13.9 against
+// 14.7).
 bool gemm_bf16_fewtok_ok(const GemmArgs& g) {
     // token-major, rows of X 16-byte aligned in every batch entry; 32-bit load offsets below bit 31
     // (which marks the loads past a wave's range): 16 X rows plus K, the value tiles of one row block
     // (16 K bytes)
     const bool aligned = g.ldx % 8 == 0 && (reinterpret_cast<uintptr_t>(g.X) & 15) == 0 && (g.batch == 1 || g.sx % 8 == 0);
     const int64_t nb = (g.M + 15) / 16;
-    const bool pays = g.N <= 2 || (g.N <= 8 && nb < 1024) || (g.N <= 16 && nb < 384);
+    const bool pays = g.N <= 2 || (g.N <= 8 && nb < 1024) || (g.N <= 16 && nb <= 256);
     return g.tm && g.N >= 1 && pays && aligned && (16 * g.ldx + g.K) * 2 < ((int64_t)1 << 31) &&
            g.K < ((int64_t)1 << 26) && nb < ((int64_t)1 << 31);
 }
@@ -258,7 +260,7 @@ hipError_t launch_gemm_bf16_fewtok(const GemmArgs& g, hipStream_t s) {
         if (nb >= 192) return fewtok::launch<8, 8, 2>(g, s);   // 96 KB
         return fewtok::launch<16, 6, 2>(g, s);                 // 144 KB
     }
-    if (g.N > 8) {  // 16 token rows per unit, below 384 row blocks
+    if (g.N > 8) {  // 16 token rows per unit, at most 256 row blocks
         if (nb >= 192) return fewtok::launch<8, 3, 16>(g, s);  // 78 KB
         return fewtok::launch<16, 2, 16>(g, s);                // 104 KB
     }

@@ -333,7 +333,7 @@ bool gemm_bf16_skinny_ok(const GemmArgs& g) {
 // more workgroups, R as large as that allows (each X fragment is then shared by more weight tiles);
 // the unit-vector case reads its X fragment cheaply and prefers more, smaller workgroups. Chosen by
 // measurement on MI355X over R in {1, 2, 4}, S in {4, 8, 16}, U in {1, 2, 4}.
-// Token-major X with 17 or more tokens (and 9-16 tokens from 384 row blocks, where the LDS-ring kernel
+// Token-major X with 17 or more tokens (and 9-16 tokens past 256 row blocks, where the LDS-ring kernel
 // is not used): measured over R in {1, ..., 8}, S in {4, 8, 16}, U in {1, 2} with weight copies rotated
 // beyond the Infinity Cache. The best grid is one round that loads every CU alike: past 512 row blocks, R =
 // ceil(blocks / CUs), which gives each CU R or R - 1 blocks (a power of two R left up to a quarter of the CUs
@@ -388,7 +388,7 @@ hipError_t launch_gemm_bf16_skinny(const GemmArgs& g, hipStream_t s) {
         if (nb >= 512) return skinny::launch<1, 2, 4, 2>(g, s);
         return skinny::launch<1, 1, 8, 4>(g, s);
     }
-    if (g.tm && (g.N > 16 || nb >= 384)) return launch_skinny_tm(g, s, nb);
+    if (g.tm && (g.N > 16 || nb > 256)) return launch_skinny_tm(g, s, nb);
     if (g.N <= 16) {
         if (nb >= 512) return skinny::launch<1, 4, 16, 1>(g, s);
         return skinny::launch<1, 1, 16, 2>(g, s);

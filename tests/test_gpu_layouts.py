@@ -61,6 +61,8 @@ TM_SHAPES = [
     (16400, 240, 13, 248, 16400),
     (8200, 4096, 16, 4096, 8200),
     (6150, 320, 11, 320, 6150),
+    (4400, 256, 16, 264, 4400),   # 275 row blocks: the register kernel, two blocks per workgroup
+    (4096, 128, 13, 136, 4096),   # 256 row blocks: the LDS ring, one workgroup per CU
     (6150, 320, 5, 328, 6150),  # 2-8 tokens, 4-wave ring workgroups above 256 row blocks, K tail
     # the register-pipelined few-token kernel, token-major, one round of at most one workgroup per CU (R =
     # ceil(blocks / CUs): 3, 5, 6 and 7 here, with a last workgroup holding fewer blocks), the two-block
