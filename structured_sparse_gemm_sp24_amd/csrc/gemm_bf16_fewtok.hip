@@ -230,7 +230,10 @@ hipError_t launch(const GemmArgs& g, hipStream_t s) {
 
 // Where this kernel is used: measured against the register-pipelined few-token kernel on MI355X (HIP
 // graph replays, weight copies rotated beyond the Infinity Cache): for N <= 2 (28672 x 8192 at N = 1: 44.9
-// against 48.7 us), for N <= 8 below 1024 row blocks (11008 x 4096 at N = 8: 12.2 against 14.1 us), and for
+// against 48.7 us), for 3 to 8 tokens up to 256 and from 513 to 1023 row blocks (11008 x 4096 at N = 4 / 8:
+// 11.4 / 12.2 against 11.9 / 12.0 us, 16000 x 4096 at N = 8 16.0 against 17.2; in between the register
+// kernel's two-block workgroups fit one round and win: 5000 x 4096 at N = 8 8.6 -> 7.6 us, 7000 x 4096 at
+// N = 4 8.5 -> 7.8, 6000 x 4096 at N = 6 8.8 -> 8.1, 4400 x 4096 at N = 3 7.6 -> 6.8), and for
 // 9 to 16 tokens up to 256 row blocks, one workgroup per CU (4096 x 4096 at N = 9 / 12 / 16: 7.0 / 6.9 / 7.1
 // against 7.6 / 7.2 / 7.9 us). With 16-row X tiles a unit carries twice the X bytes of its weight bytes, and
 // past 256 blocks the register kernel, whose workgroups share each X fragment among several row blocks and
@@ -243,7 +246,7 @@ bool gemm_bf16_fewtok_ok(const GemmArgs& g) {
     // (16 K bytes)
     const bool aligned = g.ldx % 8 == 0 && (reinterpret_cast<uintptr_t>(g.X) & 15) == 0 && (g.batch == 1 || g.sx % 8 == 0);
     const int64_t nb = (g.M + 15) / 16;
-    const bool pays = g.N <= 2 || (g.N <= 8 && nb < 1024) || (g.N <= 16 && nb <= 256);
+    const bool pays = g.N <= 2 || (g.N <= 8 && nb < 1024 && (nb <= 256 || nb > 512)) || (g.N <= 16 && nb <= 256);
     return g.tm && g.N >= 1 && pays && aligned && (16 * g.ldx + g.K) * 2 < ((int64_t)1 << 31) &&
            g.K < ((int64_t)1 << 26) && nb < ((int64_t)1 << 31);
 }

@@ -63,7 +63,8 @@ TM_SHAPES = [
     (6150, 320, 11, 320, 6150),
     (4400, 256, 16, 264, 4400),   # 275 row blocks: the register kernel, two blocks per workgroup
     (4096, 128, 13, 136, 4096),   # 256 row blocks: the LDS ring, one workgroup per CU
-    (6150, 320, 5, 328, 6150),  # 2-8 tokens, 4-wave ring workgroups above 256 row blocks, K tail
+    (6150, 320, 5, 328, 6150),  # 3-8 tokens at 257-512 row blocks: the register kernel, K tail
+    (9000, 256, 6, 264, 9000),  # 3-8 tokens from 513 row blocks: 4-wave ring workgroups
     # the register-pipelined few-token kernel, token-major, one round of at most one workgroup per CU (R =
     # ceil(blocks / CUs): 3, 5, 6 and 7 here, with a last workgroup holding fewer blocks), the two-block
     # workgroups several per CU, ragged block counts, a K tail
