@@ -63,6 +63,11 @@ int hip_status(hipError_t e) { return e == hipSuccess ? SP24_OK : SP24_ERR_HIP; 
 // Launch-size limits of the kernels (one thread per 16-column chunk, 32-bit chunk counter; the
 // direct GEMMs put 64 rows per workgroup in grid.y).
 constexpr int64_t kMaxChunks = (int64_t)1 << 32;
+
+// rows * per_row >= kMaxChunks, without forming the product (no signed overflow for any int64 sizes)
+bool chunks_exceed(int64_t rows, int64_t per_row) {
+    return per_row > 0 && rows > (kMaxChunks - 1) / per_row;
+}
 constexpr int64_t kMaxRowsDirect = (int64_t)65535 * 64;
 
 }  // namespace
@@ -124,7 +129,7 @@ int sp24_prune_compress(const void* W, int dtype, int64_t M, int64_t K, int64_t 
     int st = check_k(K);
     if (st != SP24_OK) return st;
     if (ldw < K) return SP24_ERR_SHAPE;
-    if (padded_m(M) * (padded_k(K, elem_size(val_dtype)) / 16) >= kMaxChunks) return SP24_ERR_SHAPE;
+    if (chunks_exceed(padded_m(M), padded_k(K, elem_size(val_dtype)) / 16)) return SP24_ERR_SHAPE;
     const int isz = elem_size(dtype);
     if (!aligned16(W) || !aligned16(values) || !aligned16(meta) || (ldw * isz) % 16 != 0) return SP24_ERR_ALIGN;
     if (norms && !aligned16(norms)) return SP24_ERR_ALIGN;
@@ -150,7 +155,7 @@ int sp24_prune_mask(const void* W, int dtype, int64_t M, int64_t K, int64_t ldw,
     int st = check_k(K);
     if (st != SP24_OK) return st;
     if (ldw < K || (W_out && ldo < K)) return SP24_ERR_SHAPE;
-    if (M * (K / 16) >= kMaxChunks) return SP24_ERR_SHAPE;
+    if (chunks_exceed(M, K / 16)) return SP24_ERR_SHAPE;
     const int isz = elem_size(dtype);
     if (!aligned16(W) || (ldw * isz) % 16 != 0) return SP24_ERR_ALIGN;
     if (mask && !aligned16(mask)) return SP24_ERR_ALIGN;
@@ -192,7 +197,7 @@ int sp24_decompress(const void* values, const uint8_t* meta, int dtype, int64_t 
     int st = check_k(K);
     if (st != SP24_OK) return st;
     if (ldw < K) return SP24_ERR_SHAPE;
-    if (padded_m(M) * (padded_k(K, elem_size(dtype)) / 16) >= kMaxChunks) return SP24_ERR_SHAPE;  // one thread per padded chunk
+    if (chunks_exceed(padded_m(M), padded_k(K, elem_size(dtype)) / 16)) return SP24_ERR_SHAPE;  // one thread per padded chunk
     const int isz = elem_size(dtype);
     if (!aligned16(values) || !aligned16(meta) || !aligned16(W_out) || (ldw * isz) % 16 != 0) return SP24_ERR_ALIGN;
     st = check_device();
@@ -339,7 +344,7 @@ int sp24_bench_dense_tile(const void* W, int64_t M, int64_t K, int64_t ldw, void
     if (!W || !W_tiled) return SP24_ERR_NULL;
     if (M < 1 || K < 64 || K % 64 != 0 || ldw < K) return SP24_ERR_SHAPE;
     if (!aligned16(W) || !aligned16(W_tiled) || (ldw * 2) % 16 != 0) return SP24_ERR_ALIGN;
-    if (padded_m(M) / 16 * (K / 32) * 64 >= kMaxChunks) return SP24_ERR_SHAPE;
+    if (chunks_exceed(padded_m(M) / 16, (K / 32) * 64)) return SP24_ERR_SHAPE;
     const int st = check_device();
     if (st != SP24_OK) return st;
     return hip_status(sp24::launch_dense_tile(W, M, K, ldw, W_tiled, static_cast<hipStream_t>(stream)));

@@ -85,6 +85,8 @@ MAG, WANDA = sp.SP24_SCORE_MAGNITUDE, sp.SP24_SCORE_WANDA
     ((MIS, BF16, 4, 16, 16, MAG, NULL, B, BF16, C, NULL), sp.SP24_ERR_ALIGN),
     ((A, FP32, 4, 16, 16, WANDA, MIS, B, BF16, C, NULL), sp.SP24_ERR_ALIGN),
     ((A, I8, 4, 16, 24, MAG, NULL, B, I8, C, NULL), sp.SP24_ERR_ALIGN),
+    # rows x chunks per row past 2^63 (the check must not overflow into a small product)
+    ((A, BF16, 1 << 61, 1 << 20, 1 << 20, MAG, NULL, B, BF16, C, NULL), sp.SP24_ERR_SHAPE),
 ])
 def test_prune_compress_validation(lib, args, expect):
     assert lib.sp24_prune_compress(*args) == expect
@@ -101,6 +103,7 @@ def test_prune_compress_validation(lib, args, expect):
     # 2^20 - 1 rows pad to 2^20 (the unpadded count alone would pass)
     ((A, B, BF16, 1 << 20, 1 << 16, C, 1 << 16, NULL), sp.SP24_ERR_SHAPE),
     ((A, B, BF16, (1 << 20) - 1, 1 << 16, C, 1 << 16, NULL), sp.SP24_ERR_SHAPE),
+    ((A, B, BF16, 1 << 61, 1 << 20, C, 1 << 20, NULL), sp.SP24_ERR_SHAPE),  # product past 2^63
 ])
 def test_decompress_validation(lib, args, expect):
     assert lib.sp24_decompress(*args) == expect
@@ -194,6 +197,7 @@ def test_gemm_i8_fused_validation(lib, args, expect):
     ((A, BF16, 16, 16, 16, 2, 0, NULL, NULL, C, 8, NULL), sp.SP24_ERR_SHAPE),      # ldo < K
     ((A, BF16, 16, 16, 16, 2, 0, NULL, MIS, NULL, 16, NULL), sp.SP24_ERR_ALIGN),
     ((A, BF16, 16, 16, 20, 2, 0, NULL, B, NULL, 16, NULL), sp.SP24_ERR_ALIGN),     # ldw*2 % 16
+    ((A, BF16, 1 << 61, 1 << 20, 1 << 20, 2, 0, NULL, B, NULL, 1 << 20, NULL), sp.SP24_ERR_SHAPE),  # past 2^63
 ])
 def test_prune_mask_validation(lib, args, expect):
     assert lib.sp24_prune_mask(*args) == expect
