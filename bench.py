@@ -70,9 +70,10 @@ def to_dev(a, kind=None):
 
 def n_copies(step_bytes: int, kernel_bytes: int, budget: int = 8 << 30) -> int:
     """Buffer copies to rotate so that every kernel's launches cycle over more than twice the Infinity
-    Cache (kernel_bytes: the smallest bytes one kernel of the step touches), within a memory budget."""
+    Cache (kernel_bytes: the smallest bytes one kernel of the step touches), within a memory budget, and
+    never fewer than three (each launch then follows launches on two other copies)."""
     n = int(np.ceil(2 * CACHE_BYTES / max(kernel_bytes, 1))) + 1
-    return max(2, min(64, n, budget // max(step_bytes, 1)))
+    return max(3, min(64, n, budget // max(step_bytes, 1)))
 
 
 class Kernel:

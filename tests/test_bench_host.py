@@ -26,3 +26,13 @@ def test_roofline_picks_the_binding_roof():
     assert r["bound"] == "alu" and r["unit"] == "Tslot/s"
     assert abs(bench.VALU_PEAK_TSLOTS - 39.3216) < 1e-6
     assert abs(r["frac"] - slots / 33.2e-6 / 1e12 / bench.VALU_PEAK_TSLOTS) < 1e-4
+
+
+def test_buffer_rotation_covers_the_infinity_cache():
+    MB = 1 << 20
+    # the FFN step (about 1.34 GB) rotates three copies; a 51 MB kernel cycles over more than 512 MB
+    assert bench.n_copies(1340 * MB, 868 * MB) == 3
+    n = bench.n_copies(60 * MB, 51 * MB)
+    assert n * 51 * MB > 2 * bench.CACHE_BYTES and n <= 64
+    # never fewer than three, whatever the budget
+    assert bench.n_copies(10 << 30, 5 << 30) == 3

@@ -202,8 +202,13 @@ def test_ffn_28672x8192():
     d = synth.ffn_28672x8192(8192)
     say("full size: FFN 28672 x 8192, N in 8, 64, 512, 8192")
     vd, md, rv, rm = _prune_bit_exact(d["W_bf16"], oracle.BF16)
-    rows = _rows(28672, 5)
-    assert len(np.unique(rows // 256)) == 112  # every 256-row tile row
+    # the first 1024 rows whole (the slice the CPU baseline times) and 256 more: one in every 256-row
+    # tile row, the rest at random
+    rng = np.random.default_rng(5)
+    per_block = np.arange(0, 28672, 256) + rng.integers(0, 256, size=112)
+    extra = rng.choice(np.arange(1024, 28672), size=256, replace=False)
+    rows = np.unique(np.concatenate([np.arange(1024), per_block, extra, [28671]]))
+    assert len(np.unique(rows // 256)) == 112 and np.all(rows[:1024] == np.arange(1024))  # every tile row
     for N in (8, 64, 512, 8192):
         _check_bf16(vd, md, rv, rm, 28672, np.ascontiguousarray(d["X_bf16"][:, :N]), rows)
 
