@@ -755,10 +755,10 @@ def main():
         # warm: the same launch repeated on one copy, so whatever fits stays in the caches (labelled as such)
         e["warm_avg_us"] = round(kernel_time_ms(k.fn, w["copies"][:1], args.steps, 1) * 1e3, 2)
         kernels[k.name] = e
-    # GEMMs that stream their weight (few tokens: at most 64 flop per byte, reads dominate): the measured
-    # streaming-read floor of the same bytes beside the spec peak
+    # GEMMs that stream their weight (few tokens: at most 64 flop per byte, reads dominate) and the column
+    # norms (a pure read of X): the measured streaming-read floor of the same bytes beside the spec peak
     for k in w["kernels"]:
-        if k.flops and k.flops / k.nbytes <= 64:
+        if (k.flops and k.flops / k.nbytes <= 64) or k.name == "col_norms":
             f_us, n = stream_floor_us(k.nbytes, args.steps)
             e = kernels[k.name]
             e.update(floor_us=round(f_us, 2), floor_gbs=round(k.nbytes / f_us / 1e3, 1),
