@@ -255,6 +255,18 @@ def workload_vit(args):
     return _bf16_gemm_workload("vit_b16_fc1", d["W_bf16"], d["X_bf16"], sp.SP24_SCORE_MAGNITUDE, None, cfg, args.layout)
 
 
+def shard_rows(W, args, cfg, name):
+    """--shard-m G: one GPU's share of the layer split by output channels over G GPUs (rows [0, M/G) rounded up
+    to whole 16-row blocks); every GPU of such a split streams its own rows with no exchange."""
+    G = args.shard_m
+    if G == 1:
+        return W, cfg, name
+    M = W.shape[0]
+    Mg = -(-M // G // 16) * 16 if M % (16 * G) else M // G
+    cfg = dict(cfg, M=Mg, shard=f"rows [0, {Mg}) of {M}: one GPU's share of an output-channel split over {G} GPUs")
+    return np.ascontiguousarray(W[:Mg]), cfg, f"{name}_mshard{G}"
+
+
 def workload_llm(M):
     def build(args):
         N = args.n or 4096
@@ -265,8 +277,8 @@ def workload_llm(M):
                    calibration="4096 x 2048 bf16, lognormal(0,1) channel scale x Student-t(3), seed 33",
                    activations="same law, seed 34, first N columns", score="wanda", out="bf16",
                    step="col_norms + prune_compress (Wanda) + gemm_bf16")
-        return _bf16_gemm_workload(f"llm_proj_{M}x4096_n{N}", d["W_bf16"], X, sp.SP24_SCORE_WANDA, d["Xcal_bf16"], cfg,
-                                   args.layout)
+        W, cfg, name = shard_rows(d["W_bf16"], args, cfg, f"llm_proj_{M}x4096_n{N}")
+        return _bf16_gemm_workload(name, W, X, sp.SP24_SCORE_WANDA, d["Xcal_bf16"], cfg, args.layout)
     return build
 
 
@@ -276,8 +288,8 @@ def workload_ffn(args):
     cfg = dict(workload="ffn_28672x8192", M=28672, K=8192, N=N, weight="bf16 N(0,0.02^2) seed 41",
                activations="bf16 N(0,1) seed 42, first N columns of an 8192-wide draw", score="magnitude",
                out="bf16", step="prune_compress + gemm_bf16")
-    return _bf16_gemm_workload(f"ffn_28672x8192_n{N}", d["W_bf16"], d["X_bf16"], sp.SP24_SCORE_MAGNITUDE, None, cfg,
-                               args.layout)
+    W, cfg, name = shard_rows(d["W_bf16"], args, cfg, f"ffn_28672x8192_n{N}")
+    return _bf16_gemm_workload(name, W, d["X_bf16"], sp.SP24_SCORE_MAGNITUDE, None, cfg, args.layout)
 
 
 def workload_single(args):
@@ -717,6 +729,9 @@ def main():
     ap.add_argument("--n", type=int, default=0, help="tokens N for the llm_proj_* and ffn_* workloads (ffn default 8192)")
     ap.add_argument("--layout", default="token", choices=("token", "feature"),
                     help="activations token-major (X N x K, Y N x M, a Linear layer's layout) or feature-major")
+    ap.add_argument("--shard-m", type=int, default=1, metavar="G",
+                    help="ffn_* / llm_proj_* (bf16): time one GPU's share of the layer split by output channels over G "
+                         "GPUs (rows [0, M/G)); the other GPUs' shares are the same kernel on other rows")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense-ref", action="store_true", help="skip timing the dense bf16 GEMM of the same shape")
@@ -727,6 +742,10 @@ def main():
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path shards with no "
               "communication: by tokens or by output channels)", file=sys.stderr)
+        sys.exit(2)
+    if args.shard_m < 1 or (args.shard_m > 1 and not (args.workload.startswith("ffn_") or
+                                                       args.workload in ("llm_proj_11008x4096", "llm_proj_4096x4096"))):
+        print("--shard-m applies to the bf16 ffn_* and llm_proj_* workloads, with G >= 1", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)

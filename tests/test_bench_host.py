@@ -36,3 +36,15 @@ def test_buffer_rotation_covers_the_infinity_cache():
     assert n * 51 * MB > 2 * bench.CACHE_BYTES and n <= 64
     # never fewer than three, whatever the budget
     assert bench.n_copies(10 << 30, 5 << 30) == 3
+
+
+def test_shard_rows_takes_one_gpus_share():
+    import argparse
+    import numpy as np
+    W = np.arange(28672 * 4, dtype=np.uint16).reshape(28672, 4)
+    Ws, cfg, name = bench.shard_rows(W, argparse.Namespace(shard_m=8), dict(M=28672), "ffn")
+    assert Ws.shape == (3584, 4) and np.array_equal(Ws, W[:3584]) and cfg["M"] == 3584 and name == "ffn_mshard8"
+    # shares round up to whole 16-row blocks; G = 1 is the whole layer
+    Ws, cfg, _ = bench.shard_rows(W[:11008], argparse.Namespace(shard_m=3), dict(M=11008), "llm")
+    assert Ws.shape[0] == 3680 and 3 * 3680 >= 11008
+    assert bench.shard_rows(W, argparse.Namespace(shard_m=1), {}, "x")[0] is W

@@ -213,6 +213,19 @@ def test_ffn_28672x8192():
         _check_bf16(vd, md, rv, rm, 28672, np.ascontiguousarray(d["X_bf16"][:, :N]), rows)
 
 
+def test_ffn_one_gpu_share():
+    """Rows [0, 3584) of the FFN weight: one GPU's share of an output-channel split over eight GPUs, the shape
+    `bench.py --shard-m 8` times (other kernels' launch configurations than the whole layer at N = 8)."""
+    d = synth.ffn_28672x8192(8192)
+    W = np.ascontiguousarray(d["W_bf16"][:3584])
+    say("full size: FFN one-GPU share 3584 x 8192, N in 8, 8192")
+    vd, md, rv, rm = _prune_bit_exact(W, oracle.BF16)
+    rows = _rows(3584, 8)
+    assert len(np.unique(rows // 256)) == 14
+    for N in (8, 8192):
+        _check_bf16(vd, md, rv, rm, 3584, np.ascontiguousarray(d["X_bf16"][:, :N]), rows)
+
+
 def test_bert_ffn_int8_fused_chain():
     # the fused chain the bench times (token-major): H = int8(GELU(W1 X + b1)), Y = W2 H + b2
     d = synth.bert_ffn_int8_dense()
